@@ -1,0 +1,94 @@
+"""CPU oracle of the fused RMSNorm+MatMul path -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (``tensor_program_amd``)
+never does, and the two share no code.
+
+``rmm_oracle.c`` is the plain unfused program in fp64 (see its header for the
+passages it follows); this module marshals numpy arrays to it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "rmm_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+CFLAGS = ["-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+          "-Wall"]
+_lib = None
+
+
+def build(force: bool = False, src: str = _SRC, out: str = _LIB, extra=()) -> str:
+    """Compile the oracle with gcc."""
+    if force or not os.path.exists(out):
+        tmp = out + ".tmp"
+        subprocess.check_call(["gcc", *CFLAGS, *extra, "-o", tmp, src, "-lm"])
+        os.replace(tmp, out)
+    return out
+
+
+def load(path: str = _LIB):
+    """Load an oracle build (the default one, or another build of the same source)."""
+    lib = ctypes.CDLL(path)
+    vp, dbl, i64 = ctypes.c_void_p, ctypes.c_double, ctypes.c_int64
+    lib.rmm_oracle_rmsnorm_matmul_f64.argtypes = [vp, vp, vp, dbl, i64, i64, i64, vp]
+    lib.rmm_oracle_rmsnorm_matmul_f64.restype = ctypes.c_int
+    lib.rmm_oracle_rmsnorm_gated_mlp_f64.argtypes = [vp, vp, vp, vp, dbl, i64, i64, i64, vp]
+    lib.rmm_oracle_rmsnorm_gated_mlp_f64.restype = ctypes.c_int
+    return lib
+
+
+def _default():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        _lib = load(_LIB)
+    return _lib
+
+
+def _d(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _p(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def rmsnorm_matmul(X, g, W, eps, lib=None) -> np.ndarray:
+    """Y = RMSNorm(X; g, eps) @ W in fp64.  X: [M,K], g: [K], W: [K,N]."""
+    lib = lib or _default()
+    X, g, W = _d(X), _d(g), _d(W)
+    M, K = X.shape
+    K2, N = W.shape
+    assert K2 == K and g.shape == (K,)
+    Y = np.empty((M, N), np.float64)
+    rc = lib.rmm_oracle_rmsnorm_matmul_f64(_p(X), _p(g), _p(W), float(eps), M, N, K, _p(Y))
+    if rc != 0:
+        raise ValueError(f"oracle error {rc}")
+    return Y
+
+
+def rmsnorm_gated_mlp(X, g, W1, W3, eps, lib=None) -> np.ndarray:
+    """Y = silu(RMSNorm(X) @ W1) * (RMSNorm(X) @ W3) in fp64."""
+    lib = lib or _default()
+    X, g, W1, W3 = _d(X), _d(g), _d(W1), _d(W3)
+    M, K = X.shape
+    K2, N = W1.shape
+    assert K2 == K and W3.shape == W1.shape and g.shape == (K,)
+    Y = np.empty((M, N), np.float64)
+    rc = lib.rmm_oracle_rmsnorm_gated_mlp_f64(_p(X), _p(g), _p(W1), _p(W3), float(eps), M, N,
+                                              K, _p(Y))
+    if rc != 0:
+        raise ValueError(f"oracle error {rc}")
+    return Y
+
+
+def eps_as_passed(eps: float) -> float:
+    """The eps the kernels see: the float32 value, widened exactly to double."""
+    return float(np.float32(eps))

@@ -1,0 +1,122 @@
+/*
+ * CPU oracle for the fused RMSNorm+MatMul path -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+ * load this library.  It shares no code, header or constant with the HIP
+ * library: it is the plain, slow, unfused program in double precision.
+ *
+ * What it computes.  The Mirage paper review ("Mirage: A Multi-Level
+ * Superoptimizer for Tensor Programs", section "核心概念 / μGraph示例")
+ * takes RMSNorm followed by MatMul as its worked example: existing systems
+ * run the two as separate kernels, Mirage fuses them so the normalised
+ * tensor is never materialised.  The same page's abstract expression
+ * (section "核心公式 / 抽象表达式") is E(O) = sum(k, div(mul(I1, I2), I3)):
+ * a k-sum of a product divided by a per-row quantity that does not depend
+ * on k.  The oracle is the unfused program those sections describe:
+ *
+ *   1. per row m:  S[m] = (sum_k X[m,k]^2) / K,  r[m] = sqrt(S[m] + eps)
+ *   2. per (m,k):  Nrm[m,k] = (X[m,k] / r[m]) * g[k]     -- materialised
+ *   3. per (m,n):  Y[m,n] = sum_k Nrm[m,k] * W[k,n]        -- i-k-j loops
+ *
+ * RMSNorm itself is not written out on the pages; the reading used is the
+ * conventional one: root-mean-square over the contraction dimension K
+ * (divide by K), eps added inside the square root, gain g applied per k.
+ * The matmul is the plain broadcast-multiply-then-sum-over-k definition
+ * (the Luminal talk page describes matmul the same way).
+ *
+ * Gated MLP (paper review, section "五、实验结果", the GatedMLP benchmark row;
+ * the page does not define it, the reading is SwiGLU):
+ *   Z1 = Nrm * W1,  Z3 = Nrm * W3,  Y = Z1 / (1 + exp(-Z1)) * Z3.
+ *
+ * Build: gcc -O2 -fopenmp -ffp-contract=off (no fast-math).  OpenMP splits
+ * rows across threads only for timing; each output element is computed by
+ * one thread in the same order as the serial program.
+ *
+ * Parity pins live in tests/test_oracle_pins.py (closed forms, invariants,
+ * special cases that reduce to a library matmul, brute force on tiny
+ * shapes).  No function here is "parity unpinned".
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+/* Step 1: r[m] = sqrt(mean_k X[m,k]^2 + eps). */
+static void row_rms(const double* X, int64_t M, int64_t K, double eps, double* r) {
+#pragma omp parallel for schedule(static)
+  for (int64_t m = 0; m < M; ++m) {
+    double ss = 0.0;
+    for (int64_t k = 0; k < K; ++k) ss += X[m * K + k] * X[m * K + k];
+    r[m] = sqrt(ss / (double)K + eps);
+  }
+}
+
+/* Step 2: the normalised, gained activations (the tensor fusion avoids). */
+static void normalise(const double* X, const double* g, const double* r, int64_t M,
+                      int64_t K, double* Nrm) {
+#pragma omp parallel for schedule(static)
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t k = 0; k < K; ++k) Nrm[m * K + k] = (X[m * K + k] / r[m]) * g[k];
+}
+
+/* Step 3: Y = A * B, A: M x K, B: K x N (B[k*N + n]), i-k-j order. */
+static void matmul(const double* A, const double* B, int64_t M, int64_t N, int64_t K,
+                   double* Y) {
+#pragma omp parallel for schedule(static)
+  for (int64_t m = 0; m < M; ++m) {
+    double* y = Y + m * N;
+    for (int64_t n = 0; n < N; ++n) y[n] = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+      const double a = A[m * K + k];
+      const double* b = B + k * N;
+      for (int64_t n = 0; n < N; ++n) y[n] += a * b[n];
+    }
+  }
+}
+
+/* Returns 0 on success, 1 on bad shape, 2 on allocation failure. */
+int rmm_oracle_rmsnorm_matmul_f64(const double* X, const double* g, const double* W,
+                                  double eps, int64_t M, int64_t N, int64_t K, double* Y) {
+  if (M < 0 || N < 0 || K <= 0) return 1;
+  double* r = (double*)malloc(sizeof(double) * (size_t)(M > 0 ? M : 1));
+  double* Nrm = (double*)malloc(sizeof(double) * (size_t)(M > 0 ? M * K : 1));
+  if (!r || !Nrm) {
+    free(r);
+    free(Nrm);
+    return 2;
+  }
+  row_rms(X, M, K, eps, r);
+  normalise(X, g, r, M, K, Nrm);
+  matmul(Nrm, W, M, N, K, Y);
+  free(r);
+  free(Nrm);
+  return 0;
+}
+
+int rmm_oracle_rmsnorm_gated_mlp_f64(const double* X, const double* g, const double* W1,
+                                     const double* W3, double eps, int64_t M, int64_t N,
+                                     int64_t K, double* Y) {
+  if (M < 0 || N < 0 || K <= 0) return 1;
+  size_t mn = (size_t)(M * N > 0 ? M * N : 1);
+  double* r = (double*)malloc(sizeof(double) * (size_t)(M > 0 ? M : 1));
+  double* Nrm = (double*)malloc(sizeof(double) * (size_t)(M > 0 ? M * K : 1));
+  double* Z3 = (double*)malloc(sizeof(double) * mn);
+  if (!r || !Nrm || !Z3) {
+    free(r);
+    free(Nrm);
+    free(Z3);
+    return 2;
+  }
+  row_rms(X, M, K, eps, r);
+  normalise(X, g, r, M, K, Nrm);
+  matmul(Nrm, W1, M, N, K, Y); /* Y holds Z1 until the gate below */
+  matmul(Nrm, W3, M, N, K, Z3);
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < M * N; ++i) {
+    const double z1 = Y[i];
+    Y[i] = z1 / (1.0 + exp(-z1)) * Z3[i];
+  }
+  free(r);
+  free(Nrm);
+  free(Z3);
+  return 0;
+}

@@ -1,0 +1,57 @@
+"""The five synthetic workloads of the fused RMSNorm+MatMul path.
+
+Shapes and value distributions (all seed 0, one generator stream per tensor):
+  X ~ N(0,1) (optionally row-scaled), g ~ 1 + 0.1 N(0,1), W ~ N(0, 1/K).
+The pages give no shapes; these stand in for their (unnamed) benchmarks.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    dtype: str          # "f32" or "bf16": X, g, W*, Y all stored in this type
+    M: int
+    K: int
+    N: int
+    eps: float
+    gated: bool
+    row_scale: str | None   # None, "pick_x100" (1% of rows x100) or "loguniform"
+
+    @property
+    def n_weights(self) -> int:
+        return 2 if self.gated else 1
+
+    @property
+    def elem_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    def flops(self) -> int:
+        """Algorithmic flops: 2*M*N*K per contraction."""
+        return 2 * self.M * self.N * self.K * self.n_weights
+
+    def algo_bytes(self) -> int:
+        """Algorithmic HBM bytes: every input once and Y once."""
+        return (self.M * self.K + self.K + self.n_weights * self.K * self.N
+                + self.M * self.N) * self.elem_bytes
+
+
+WORKLOADS = {
+    w.name: w for w in (
+        Workload("f32_m8_k1024_n1024", "f32", 8, 1024, 1024, 1e-6, False, None),
+        Workload("decode_m16_k4096_n6144", "bf16", 16, 4096, 6144, 1e-6, False, None),
+        Workload("prefill_m4096_k4096_n4096", "bf16", 4096, 4096, 4096, 1e-6, False,
+                 "pick_x100"),
+        Workload("gated_m64_k4096_n14336", "bf16", 64, 4096, 14336, 1e-6, True, None),
+        Workload("large_m8192_k8192_n28672", "bf16", 8192, 8192, 28672, 1e-5, False,
+                 "loguniform"),
+    )
+}
+
+ORDER = list(WORKLOADS)
+
+
+def get_workload(name: str) -> Workload:
+    return WORKLOADS[name]

@@ -1,0 +1,230 @@
+"""Pins of the CPU oracle: checks against things other than the oracle itself.
+
+Each ``pin_*`` takes an oracle library handle (``oracle.load(path)``) so the
+same checks can be run on deliberately broken builds of the oracle
+(tests/test_oracle_mutants.py) to show that they catch plausible mistakes.
+
+What the pins rest on (the pages print no numbers for a worked example, so
+every expected value below is a closed form or a property of the definition):
+  * hand arithmetic on 2x2 examples;
+  * special cases that reduce to a library matmul (rows of unit RMS, eps = 0);
+  * the closed form of a constant row, c / sqrt(c^2 + eps);
+  * the normalised rows' mean square, S / (S + eps), when W = I;
+  * invariants: scale law, gain folding, linearity, permutations;
+  * exact rational / 50-digit brute force on tiny shapes;
+  * the gate's closed forms at z = +-ln 3 (sigmoid = 3/4 and 1/4 exactly).
+"""
+from __future__ import annotations
+
+import math
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+import numpy as np
+
+import oracle
+
+
+def _mm(lib, X, g, W, eps):
+    return oracle.rmsnorm_matmul(X, g, W, eps, lib=lib)
+
+
+def _gated(lib, X, g, W1, W3, eps):
+    return oracle.rmsnorm_gated_mlp(X, g, W1, W3, eps, lib=lib)
+
+
+def _close(a, b, rtol=1e-12, atol=1e-14):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    assert a.shape == b.shape, (a.shape, b.shape)
+    err = np.abs(a - b)
+    lim = atol + rtol * np.abs(b)
+    assert np.all(err <= lim), f"max err {err.max():.3e} (worst at {np.unravel_index(np.argmax(err - lim), err.shape)})"
+
+
+def pin_worked_example(lib):
+    # X = [3, 4]: mean square (9 + 16) / 2 = 12.5; with eps = 12.5 the RMS is
+    # sqrt(25) = 5, so the normalised row is [0.6, 0.8] and with g = [1, 2]
+    # the gained row is [0.6, 1.6].
+    X = np.array([[3.0, 4.0]])
+    g = np.array([1.0, 2.0])
+    _close(_mm(lib, X, g, np.eye(2), 12.5), [[0.6, 1.6]])
+    # W rows are indexed by k: Y = [0.6*1 + 1.6*3, 0.6*2 + 1.6*4] = [5.4, 7.6].
+    W = np.array([[1.0, 2.0], [3.0, 4.0]])
+    _close(_mm(lib, X, g, W, 12.5), [[5.4, 7.6]])
+
+
+def pin_library_matmul(lib):
+    # Rows of +-1 (any sign pattern) have mean square exactly 1; with eps = 0
+    # the RMS is 1 and the path reduces to (X * g) @ W, a library matmul.
+    # Non-square, non-symmetric shapes catch a transposed operand or a gain
+    # indexed by the wrong axis.
+    rng = np.random.default_rng(11)
+    for (M, K, N) in ((3, 5, 7), (4, 9, 2), (1, 1, 3), (6, 4, 4)):
+        X = rng.choice([-1.0, 1.0], size=(M, K))
+        g = rng.normal(1.0, 0.3, size=K)
+        W = rng.normal(size=(K, N))
+        _close(_mm(lib, X, g, W, 0.0), (X * g[None, :]) @ W)
+        # Rows of constant magnitude c_m: the RMS is c_m, so X / RMS = sign(X).
+        c = rng.uniform(0.1, 10.0, size=(M, 1))
+        _close(_mm(lib, X * c, g, W, 0.0), (X * g[None, :]) @ W)
+
+
+def pin_identity_weight(lib):
+    # W = I, g = 1: Y is RMSNorm(X) itself; every output row has mean square
+    # S / (S + eps) where S is the input row's mean square.
+    rng = np.random.default_rng(12)
+    M, K = 5, 8
+    X = rng.normal(size=(M, K)) * rng.uniform(0.1, 3.0, size=(M, 1))
+    for eps in (0.0, 0.3, 2.0):
+        Y = _mm(lib, X, np.ones(K), np.eye(K), eps)
+        S = np.mean(X * X, axis=1)
+        _close(np.mean(Y * Y, axis=1), S / (S + eps))
+        # and each output row is a positive multiple of its input row
+        ratio = Y / X
+        _close(ratio, np.repeat(ratio[:, :1], K, axis=1))
+        assert np.all(ratio[:, 0] > 0)
+
+
+def pin_constant_row(lib):
+    # A row of constant value c has mean square c^2 for any K, so every
+    # output is c / sqrt(c^2 + eps) * sum_k g_k W[k, n].
+    rng = np.random.default_rng(13)
+    K, N = 6, 5
+    g = rng.normal(1.0, 0.1, size=K)
+    W = rng.normal(size=(K, N))
+    for c, eps, factor in ((1e-3, 1e-6, 1.0 / math.sqrt(2.0)),
+                           (2.0, 0.0, 1.0),
+                           (0.01, 1e-5, 0.9534625892455924),
+                           (-0.5, 0.75, -0.5)):
+        X = np.full((2, K), c)
+        _close(_mm(lib, X, g, W, eps), np.repeat((factor * (g @ W))[None, :], 2, axis=0))
+
+
+def pin_scale_law(lib):
+    # Scaling a row by alpha and eps by alpha^2 leaves Y unchanged.
+    rng = np.random.default_rng(14)
+    M, K, N = 4, 7, 3
+    X = rng.normal(size=(M, K))
+    g = rng.normal(1.0, 0.1, size=K)
+    W = rng.normal(size=(K, N))
+    base = _mm(lib, X, g, W, 0.25)
+    for alpha in (3.7, 1e-3, 256.0):
+        _close(_mm(lib, alpha * X, g, W, 0.25 * alpha * alpha), base, rtol=1e-11)
+    # With eps = 0 a per-row positive scale drops out; a negative one flips the row.
+    s = rng.uniform(0.01, 100.0, size=(M, 1))
+    _close(_mm(lib, s * X, g, W, 0.0), _mm(lib, X, g, W, 0.0), rtol=1e-11)
+    _close(_mm(lib, -X, g, W, 0.0), -_mm(lib, X, g, W, 0.0), rtol=1e-11)
+
+
+def pin_gain_fold(lib):
+    # sum_k X g W = X (diag(g) W): the gain can move from the activation to W.
+    rng = np.random.default_rng(15)
+    M, K, N = 3, 6, 4
+    X = rng.normal(size=(M, K))
+    g = rng.normal(1.0, 0.5, size=K)
+    W = rng.normal(size=(K, N))
+    _close(_mm(lib, X, g, W, 0.1), _mm(lib, X, np.ones(K), g[:, None] * W, 0.1))
+
+
+def pin_structure(lib):
+    rng = np.random.default_rng(16)
+    M, K, N = 5, 6, 4
+    X = rng.normal(size=(M, K))
+    g = rng.normal(1.0, 0.2, size=K)
+    W1 = rng.normal(size=(K, N))
+    W2 = rng.normal(size=(K, N))
+    eps = 0.05
+    # linear in W
+    _close(_mm(lib, X, g, 2.0 * W1 - 3.0 * W2, eps),
+           2.0 * _mm(lib, X, g, W1, eps) - 3.0 * _mm(lib, X, g, W2, eps), rtol=1e-11, atol=1e-12)
+    # permuting rows of X permutes rows of Y
+    p = rng.permutation(M)
+    _close(_mm(lib, X[p], g, W1, eps), _mm(lib, X, g, W1, eps)[p])
+    # a common permutation of k in X, g and W changes nothing
+    q = rng.permutation(K)
+    _close(_mm(lib, X[:, q], g[q], W1[q], eps), _mm(lib, X, g, W1, eps))
+    # rows are independent: a single row gives the same result as in the batch
+    _close(_mm(lib, X[2:3], g, W1, eps), _mm(lib, X, g, W1, eps)[2:3])
+    # permuting columns of W permutes columns of Y
+    r = rng.permutation(N)
+    _close(_mm(lib, X, g, W1[:, r], eps), _mm(lib, X, g, W1, eps)[:, r])
+
+
+def pin_zero_row(lib):
+    rng = np.random.default_rng(17)
+    K, N = 5, 3
+    X = rng.normal(size=(3, K))
+    X[1] = 0.0
+    Y = _mm(lib, X, rng.normal(size=K), rng.normal(size=(K, N)), 1e-6)
+    assert np.all(Y[1] == 0.0)
+    assert np.all(np.isfinite(Y))
+
+
+def _brute(X, g, W, eps):
+    """Exact rationals for the k-sums and the mean square, 50-digit sqrt."""
+    getcontext().prec = 50
+    M, K = len(X), len(X[0])
+    N = len(W[0])
+    out = []
+    for m in range(M):
+        S = sum(Fraction(X[m][k]) ** 2 for k in range(K)) / K + Fraction(eps)
+        rms = Decimal(S.numerator).sqrt() / Decimal(S.denominator).sqrt()
+        row = []
+        for n in range(N):
+            num = sum(Fraction(X[m][k]) * Fraction(g[k]) * Fraction(W[k][n]) for k in range(K))
+            row.append(float(Decimal(num.numerator) / Decimal(num.denominator) / rms))
+        out.append(row)
+    return np.array(out)
+
+
+def pin_brute_force(lib):
+    rng = np.random.default_rng(18)
+    for _ in range(12):
+        M, K, N = (int(v) for v in rng.integers(1, 6, size=3))
+        X = rng.normal(size=(M, K))
+        g = rng.normal(1.0, 0.3, size=K)
+        W = rng.normal(size=(K, N))
+        eps = float(rng.choice([0.0, 1e-6, 0.5]))
+        X[0, 0] += 0.1  # keep row 0 away from zero
+        _close(_mm(lib, X, g, W, eps), _brute(X.tolist(), g.tolist(), W.tolist(), eps),
+               rtol=1e-13, atol=1e-15)
+
+
+def pin_gated_closed_forms(lib):
+    # X = [1, 1], g = 1, eps = 0: the normalised row is [1, 1] and each output
+    # column's pre-activation is the column sum of the weight.
+    ln3 = math.log(3.0)
+    X = np.array([[1.0, 1.0]])
+    g = np.ones(2)
+    W1 = np.array([[ln3 / 2, 0.0, -ln3 / 2, 20.0], [ln3 / 2, 0.0, -ln3 / 2, 20.0]])
+    W3 = np.array([[1.0, 2.5, 0.5, 0.25], [1.0, 2.5, 0.5, 0.25]])
+    # z1 = [ln3, 0, -ln3, 40], z3 = [2, 5, 1, 0.5]; sigmoid(ln3) = 3/4,
+    # sigmoid(-ln3) = 1/4, sigmoid(40) = 1 to double precision.
+    want = [[0.75 * ln3 * 2.0, 0.0, -0.25 * ln3 * 1.0, 40.0 * 0.5]]
+    _close(_gated(lib, X, g, W1, W3, 0.0), want)
+    # W3 = W1: y = z^2 sigmoid(z)
+    _close(_gated(lib, X, g, W1[:, :3], W1[:, :3], 0.0),
+           [[0.75 * ln3 * ln3, 0.0, 0.25 * ln3 * ln3]])
+    # The worked example of pin_worked_example gated with W3 = I:
+    # z1 = [5.4, 7.6], z3 = [0.6, 1.6].
+    Xw = np.array([[3.0, 4.0]])
+    gw = np.array([1.0, 2.0])
+    Ww = np.array([[1.0, 2.0], [3.0, 4.0]])
+    _close(_gated(lib, Xw, gw, Ww, np.eye(2), 12.5),
+           [[3.225432074958551, 12.153917554537914]], rtol=1e-13)
+    # The gate uses the same normalised activations as the plain path.
+    rng = np.random.default_rng(19)
+    Xr = rng.normal(size=(3, 5))
+    gr = rng.normal(1.0, 0.1, size=5)
+    Wa = rng.normal(size=(5, 4))
+    z = _mm(lib, Xr, gr, Wa, 1e-3)
+    ones = np.zeros((5, 4))
+    ones[0] = 1.0  # z3 = Nrm[:, 0] (first normalised column)
+    y = _gated(lib, Xr, gr, Wa, ones, 1e-3)
+    nrm0 = _mm(lib, Xr, gr, np.eye(5)[:, :1], 1e-3)
+    _close(y, z / (1.0 + np.exp(-z)) * nrm0, rtol=1e-12)
+
+
+ALL_PINS = [pin_worked_example, pin_library_matmul, pin_identity_weight, pin_constant_row,
+            pin_scale_law, pin_gain_fold, pin_structure, pin_zero_row, pin_brute_force,
+            pin_gated_closed_forms]

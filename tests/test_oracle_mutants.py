@@ -1,0 +1,63 @@
+"""The pins catch plausible mistakes: each mutant below is the oracle source
+with one planted error (a dropped term, a wrong index, a transposed operand,
+a wrong sign ...), built on the CPU; at least one pin must fail on every one.
+Every mutant keeps all memory accesses in bounds."""
+import os
+
+import pytest
+
+import oracle
+from tests import pins
+
+MUTANTS = {
+    "mean_over_k_minus_1": ("ss / (double)K + eps", "ss / (double)(K > 1 ? K - 1 : 1) + eps"),
+    "eps_outside_sqrt": ("sqrt(ss / (double)K + eps)", "(sqrt(ss / (double)K) + eps)"),
+    "eps_dropped": ("sqrt(ss / (double)K + eps)", "sqrt(ss / (double)K)"),
+    "sqrt_dropped": ("sqrt(ss / (double)K + eps)", "(ss / (double)K + eps)"),
+    "multiply_by_rms": ("(X[m * K + k] / r[m]) * g[k]", "(X[m * K + k] * r[m]) * g[k]"),
+    "gain_dropped": ("(X[m * K + k] / r[m]) * g[k]", "(X[m * K + k] / r[m])"),
+    "gain_wrong_index": ("(X[m * K + k] / r[m]) * g[k]", "(X[m * K + k] / r[m]) * g[m % K]"),
+    "abs_not_square": ("ss += X[m * K + k] * X[m * K + k]", "ss += fabs(X[m * K + k])"),
+    "k_loop_short": ("for (int64_t k = 0; k < K; ++k) ss +=",
+                     "for (int64_t k = 0; k < K - 1; ++k) ss +="),
+    "transposed_weight": ("y[n] += a * b[n];", "y[n] += a * B[(n * K + k) % (K * N)];"),
+    "weight_row_off_by_one": ("const double* b = B + k * N;",
+                              "const double* b = B + ((k + 1) % K) * N;"),
+    "gate_sign": ("z1 / (1.0 + exp(-z1)) * Z3[i]", "z1 / (1.0 + exp(z1)) * Z3[i]"),
+    "gate_swapped": ("z1 / (1.0 + exp(-z1)) * Z3[i]", "Z3[i] / (1.0 + exp(-Z3[i])) * z1"),
+    "gate_no_silu": ("z1 / (1.0 + exp(-z1)) * Z3[i]", "z1 * Z3[i]"),
+    "gate_both_w1": ("matmul(Nrm, W3, M, N, K, Z3);", "matmul(Nrm, W1, M, N, K, Z3);"),
+}
+
+
+def _build(tmp_path, name, src_text):
+    src = os.path.join(tmp_path, f"{name}.c")
+    with open(src, "w") as f:
+        f.write(src_text)
+    return oracle.load(oracle.build(force=True, src=src, out=os.path.join(tmp_path, f"lib{name}.so")))
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(oracle._SRC) as f:
+        return f.read()
+
+
+def test_unmutated_copy_passes(tmp_path, source):
+    lib = _build(str(tmp_path), "copy", source)
+    for pin in pins.ALL_PINS:
+        pin(lib)
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(tmp_path, source, name):
+    old, new = MUTANTS[name]
+    assert source.count(old) == 1, f"mutation site for {name} not unique/found"
+    lib = _build(str(tmp_path), name, source.replace(old, new))
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(lib)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches mutant {name}"

@@ -1,0 +1,262 @@
+"""Benchmark of the fused RMSNorm+MatMul hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+
+A step is one call of the library on one batch (one input set), i.e. one pass
+of the whole hot path.  Inputs are seeded synthetic tensors already resident
+in HBM.  R input sets are rotated so that each timed pass touches >= 1 GiB,
+more than the 256 MB Infinity Cache, so W really streams from HBM.  The R
+calls are captured once in a HIP graph (no allocation or memset inside) and
+replayed; HIP events on the launch stream bracket the K timed steps.
+
+Prints one JSON line.  `value` is the algorithmic HBM throughput (every input
+byte once + Y once, per second) for bandwidth-bound workloads, or TFLOP/s for
+matrix-core-bound ones.  `roofline` relates the dominant kernel to the MI355X
+peak; `cpu_baseline` times the CPU oracle on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused RMSNorm+MatMul TFLOP/s and HBM GB/s (% of MI355X roofline)"
+DEFAULT_WORKLOAD = "decode_m16_k4096_n6144"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2516.6      # dense bf16 MFMA, 256 CU x 4096 flop/clk x 2.4 GHz
+F32_VALU_PEAK_TFLOPS = 78.6    # fp32 FMA on the vector ALUs without packed math
+RIDGE = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+ROTATE_BYTES = 1 << 30
+KERNEL_SOURCES = {"decode": "rmm_decode.hip", "generic": "rmm_generic.hip",
+                  "prefill": "rmm_prefill.hip"}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_hash(variant: str) -> str | None:
+    path = os.path.join(ROOT, "tensor_program_amd", "csrc", KERNEL_SOURCES.get(variant, ""))
+    if not os.path.isfile(path):
+        return None
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_traffic(workload: str, variant: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.isfile(path):
+        return None
+    with open(path) as f:
+        table = json.load(f)
+    rec = table.get(f"{workload}/{variant}")
+    if not rec or rec.get("kernel_source_sha256_16") != source_hash(variant):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, inp, budget_s: float):
+    """The oracle, as it stands, on the host cores: whole workload if it fits
+    the time budget, else a leading block of rows (rows are independent)."""
+    import numpy as np
+    import oracle
+
+    eps = oracle.eps_as_passed(wl.eps)
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    # Probe on a small block of rows, then size the sample to the budget.
+    rows = min(wl.M, max(1, threads))
+    X = inp.X[:rows]
+
+    def once(Xs):
+        t0 = time.perf_counter()
+        if wl.gated:
+            oracle.rmsnorm_gated_mlp(Xs, inp.g, inp.W1, inp.W3, eps)
+        else:
+            oracle.rmsnorm_matmul(Xs, inp.g, inp.W1, eps)
+        return time.perf_counter() - t0
+
+    t_probe = once(X)
+    per_row = t_probe / rows
+    rows_budget = int(budget_s / max(per_row, 1e-9))
+    if rows_budget >= wl.M:
+        reps = max(1, int(budget_s / max(per_row * wl.M, 1e-9)))
+        reps = min(reps, 50)
+        t = sum(once(inp.X) for _ in range(reps)) / reps
+        sample = f"full workload ({wl.M} rows), mean of {reps} runs"
+        frac = 1.0
+    else:
+        rows = max(rows, (rows_budget // threads) * threads)
+        t = once(inp.X[:rows])
+        frac = rows / wl.M
+        sample = f"first {rows} of {wl.M} rows (rows are independent); time scaled x{wl.M / rows:.1f}"
+    t_full = t / frac
+    bound = "hbm" if wl.flops() / wl.algo_bytes() < RIDGE else "mfma"
+    if bound == "hbm":
+        value, unit = wl.algo_bytes() / t_full / 1e9, "GB/s"
+    else:
+        value, unit = wl.flops() / t_full / 1e12, "TFLOP/s"
+    used = min(threads, rows)
+    return {"value": value, "unit": unit, "cores": used, "kind": "oracle", "sample": sample,
+            "seconds_full_workload": t_full}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--variant", default="auto")
+    ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--no-graph", action="store_true", help="plain launches instead of a graph")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds for the oracle leg")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the fused RMSNorm+MatMul path has no "
+              "multi-GPU component in this build (--gpus must be 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import tensor_program_amd as tpa
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    tpa.load_library()  # fail loudly if the HIP library is not built
+    wl = synth.get_workload(args.workload)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    log(f"workload {wl.name}: generating inputs")
+    inp = synth.make_inputs(wl)
+
+    def dev_tensor(name):
+        a = inp.device_array(name)
+        if wl.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+
+    base = {n: dev_tensor(n) for n in (["X", "g", "W1"] + (["W3"] if wl.gated else []))}
+    per_set = wl.algo_bytes()
+    free = torch.cuda.mem_get_info(dev)[0]
+    R = max(1, math.ceil(ROTATE_BYTES / per_set))
+    R = max(1, min(R, int(0.6 * free // max(per_set, 1))))
+    sets = []
+    for r in range(R):
+        s = {n: (t if r == 0 else t.clone()) for n, t in base.items()}
+        s["Y"] = torch.empty((wl.M, wl.N), dtype=s["X"].dtype, device=dev)
+        sets.append(s)
+    st, variant, splits = tpa.plan(wl.M, wl.N, wl.K, dtype=sets[0]["X"].dtype, gated=wl.gated,
+                                   variant=args.variant, splits=args.splits)
+    if st != 0:
+        raise SystemExit(f"plan failed with status {st}")
+    log(f"variant {variant}, splits {splits}, {R} rotating input sets "
+        f"({R * per_set / 2**20:.0f} MiB)")
+    stream = torch.cuda.Stream(dev)
+    nbytes = tpa._binding.workspace_bytes(tpa._DTYPES[sets[0]["X"].dtype], wl.M, wl.N, wl.K,
+                                          wl.gated, args.variant, args.splits)
+    ws = tpa.Workspace(nbytes, dev) if nbytes > 0 else None
+    torch.cuda.synchronize()
+
+    def call(s):
+        if wl.gated:
+            tpa.rmsnorm_gated_mlp(s["X"], s["g"], s["W1"], s["W3"], wl.eps, out=s["Y"],
+                                  variant=args.variant, splits=args.splits, workspace=ws)
+        else:
+            tpa.rmsnorm_matmul(s["X"], s["g"], s["W1"], wl.eps, out=s["Y"],
+                               variant=args.variant, splits=args.splits, workspace=ws)
+
+    with torch.cuda.stream(stream):
+        for s in sets:  # eager warm-up of every set (also loads the code objects)
+            call(s)
+    torch.cuda.synchronize()
+
+    graph = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for s in sets:
+                call(s)
+        torch.cuda.synchronize()
+
+    def run_steps(n):
+        """n steps = n calls, rotating through the sets."""
+        with torch.cuda.stream(stream):
+            if graph is not None:
+                reps = n // R
+                for _ in range(reps):
+                    graph.replay()
+                for i in range(n - reps * R):
+                    call(sets[i])
+            else:
+                for i in range(n):
+                    call(sets[i % R])
+
+    steps = max(R, (args.steps // R) * R)
+    warm = max(R, (args.warmup // R) * R) if args.warmup > 0 else 0
+    log(f"warmup {warm} steps")
+    run_steps(warm)
+    torch.cuda.synchronize()
+    log(f"timing {steps} steps")
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        start.record(stream)
+    run_steps(steps)
+    with torch.cuda.stream(stream):
+        end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end)
+    per_launch_s = ms / 1e3 / steps
+    log(f"{ms:.3f} ms for {steps} steps: {per_launch_s * 1e6:.2f} us/step")
+
+    gbs = per_set / per_launch_s / 1e9
+    tflops = wl.flops() / per_launch_s / 1e12
+    bound = "hbm" if wl.flops() / per_set < RIDGE else "mfma"
+    if bound == "hbm":
+        value, unit = gbs, "GB/s"
+        roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": gbs / HBM_PEAK_GBS}
+    else:
+        peak = BF16_PEAK_TFLOPS if wl.dtype == "bf16" else F32_VALU_PEAK_TFLOPS
+        value, unit = tflops, "TFLOP/s"
+        roof = {"bound": "mfma" if wl.dtype == "bf16" else "alu", "achieved": tflops,
+                "peak": peak, "unit": "TFLOP/s", "frac": tflops / peak}
+    roof["traffic"] = stored_traffic(wl.name, variant)
+    roof["kernel"] = f"{variant}_kernel"
+    roof["algorithmic_bytes_per_launch"] = per_set
+    roof["algorithmic_flops_per_launch"] = wl.flops()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        cpu = cpu_baseline(wl, inp, args.cpu_budget)
+
+    line = {
+        "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": steps,
+        "warmup": warm, "ms_per_step": ms / steps, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": wl.name, "M": wl.M, "K": wl.K, "N": wl.N, "gated": wl.gated,
+                   "eps": wl.eps, "variant": variant, "splits": splits,
+                   "rotating_input_sets": R, "hip_graph": graph is not None},
+        "tflops": tflops, "hbm_gbs_algorithmic": gbs,
+        "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

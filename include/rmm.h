@@ -1,0 +1,154 @@
+/*
+ * rmm.h -- C ABI of the fused RMSNorm+MatMul library for MI355X (gfx950).
+ *
+ * The operation is the worked example of the Mirage paper review ("Mirage: A
+ * Multi-Level Superoptimizer for Tensor Programs", section "核心概念 /
+ * μGraph示例"): RMSNorm followed by MatMul, computed by one kernel that never
+ * writes the normalised activations to memory.  The same page's abstract
+ * expression (section "核心公式 / 抽象表达式"),
+ *     E(O) = sum(k, div(mul(I1, I2), I3)),
+ * is a k-sum of a product divided by a per-row value that does not depend on
+ * k, so the division can be applied once, after the k-sum:
+ *
+ *     Y[m,n] = ( sum_k X[m,k] * g[k] * W[k,n] ) / sqrt( sum_k X[m,k]^2 / K + eps )
+ *
+ * The pages name RMSNorm without defining it; the reading used is the usual
+ * one (RMS over the contraction dimension K, eps inside the square root, a
+ * per-k gain g).  The gated variant follows the GatedMLP benchmark row of
+ * the same page (section "五、实验结果"), read as SwiGLU:
+ *
+ *     Y = silu(norm(X) W1) * (norm(X) W3),   silu(z) = z / (1 + exp(-z))
+ *
+ * Layouts (all row-major, packed, no strides):
+ *   X  : M x K   (X[m*K + k])
+ *   g  : K
+ *   W, W1, W3 : K x N   (W[k*N + n]; rows indexed by k)
+ *   Y  : M x N   (Y[m*N + n])
+ * dtype selects the storage type of X, g, W*, Y together; products are summed
+ * in fp32 whatever the dtype.  With RMM_DTYPE_BF16 the operand X[m,k]*g[k] is
+ * formed in fp32 and rounded once (round to nearest even) to bf16 before the
+ * matrix-core product; Y is rounded once from fp32 to bf16 (nearest even).
+ *
+ * Ownership and ordering.  Every data pointer is a DEVICE pointer owned by the
+ * caller; the library keeps none after it returns, allocates nothing and
+ * never synchronises.  Calls are stream ordered: they validate on the host,
+ * enqueue on `stream` (NULL = the default stream) and return; Y is valid once
+ * the stream has reached that point.
+ *
+ * Workspace.  The decode (split-K) variant combines partial k-sums across
+ * workgroups through a caller-owned workspace.  `ws` may be NULL: the library
+ * then picks a variant that needs none (correct, slower).  A non-NULL `ws` must
+ * be zero-filled before its first use; the kernels leave it zeroed again
+ * (their arrival counters reset themselves), so it can be reused by later
+ * calls on the same stream without clearing.  One workspace must not be used
+ * by two calls that may run at the same time.  ws_bytes below
+ * rmm_workspace_bytes*() returns RMM_ERR_WORKSPACE.
+ *
+ * Errors.  Validation happens on the host before any HIP call, in this order:
+ *   RMM_ERR_NULL      a NULL data pointer (when M*N > 0)
+ *   RMM_ERR_SHAPE     M < 0, N < 0, K <= 0 (the mean over an empty row is
+ *                     undefined), or an element count that overflows int64
+ *   RMM_ERR_EPS       eps negative or not finite (eps = 0 is allowed)
+ *   RMM_ERR_DTYPE     unknown dtype
+ *   RMM_ERR_ALIAS     Y's byte range overlaps an input or the workspace
+ *   RMM_ERR_VARIANT   a forced variant/split count cannot run this call
+ *   RMM_ERR_WORKSPACE ws non-NULL and ws_bytes too small
+ * M == 0 or N == 0 is a no-op returning RMM_OK.  A failed launch returns
+ * RMM_ERR_HIP; rmm_last_hip_error() gives the hipError_t (thread local).
+ * Input values are not checked: NaN/Inf propagate (with eps = 0 an all-zero
+ * row gives 0 * inf = NaN).  No C++ exception crosses this interface.
+ */
+#ifndef RMM_H
+#define RMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RMM_ABI_VERSION 1
+
+typedef enum { RMM_DTYPE_F32 = 0, RMM_DTYPE_BF16 = 1 } rmm_dtype;
+
+typedef enum {
+  RMM_OK = 0,
+  RMM_ERR_NULL = 1,
+  RMM_ERR_SHAPE = 2,
+  RMM_ERR_EPS = 3,
+  RMM_ERR_DTYPE = 4,
+  RMM_ERR_ALIAS = 5,
+  RMM_ERR_WORKSPACE = 6,
+  RMM_ERR_HIP = 7,
+  RMM_ERR_VARIANT = 8
+} rmm_status;
+
+/* Kernel variants.  AUTO picks by shape; the others force one (tests, bench).
+ *   GENERIC : any shape, alignment and dtype; VALU fp32 products.
+ *   DECODE  : bf16, M <= 64, K % 8 == 0, N % 8 == 0, 16-byte aligned
+ *             pointers; streams W once with split-K across workgroups and
+ *             bf16 matrix-core (MFMA) products.  Bandwidth-bound shapes.
+ *   PREFILL : bf16, K % 8 == 0, N % 8 == 0, 16-byte aligned pointers;
+ *             LDS-tiled MFMA GEMM with the row sum of squares fused into
+ *             its k-loop.  Matrix-core-bound shapes.                        */
+typedef enum {
+  RMM_VARIANT_AUTO = 0,
+  RMM_VARIANT_GENERIC = 1,
+  RMM_VARIANT_DECODE = 2,
+  RMM_VARIANT_PREFILL = 3
+} rmm_variant;
+
+/* Y = RMSNorm(X; g, eps) W  (see the header comment for the definition).
+ * X, g, W: inputs; Y: output, must not overlap any input.  eps is used as
+ * given (fp32).  ws/ws_bytes: optional workspace (see above). */
+rmm_status rmsnorm_matmul(const void* X, const void* g, const void* W, void* Y, float eps,
+                          int64_t M, int64_t N, int64_t K, rmm_dtype dtype, void* ws,
+                          size_t ws_bytes, hipStream_t stream);
+
+/* Y = silu(RMSNorm(X) W1) * (RMSNorm(X) W3); W1 and W3 are both K x N and the
+ * 1/RMS scale is applied to both products before the SiLU. */
+rmm_status rmsnorm_gated_mlp(const void* X, const void* g, const void* W1, const void* W3,
+                             void* Y, float eps, int64_t M, int64_t N, int64_t K,
+                             rmm_dtype dtype, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* As above with a forced variant.  splits: number of K chunks the DECODE
+ * variant combines across workgroups (0 = chosen by the library, 1 = no
+ * cross-workgroup combine, so no workspace is needed); must be 0 for the
+ * other variants. */
+rmm_status rmsnorm_matmul_ex(const void* X, const void* g, const void* W, void* Y, float eps,
+                             int64_t M, int64_t N, int64_t K, rmm_dtype dtype,
+                             rmm_variant variant, int splits, void* ws, size_t ws_bytes,
+                             hipStream_t stream);
+rmm_status rmsnorm_gated_mlp_ex(const void* X, const void* g, const void* W1, const void* W3,
+                                void* Y, float eps, int64_t M, int64_t N, int64_t K,
+                                rmm_dtype dtype, rmm_variant variant, int splits, void* ws,
+                                size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes the call with these arguments would use (0 if none).  The
+ * plain entry points use variant = AUTO, splits = 0.  Returns 0 for
+ * arguments that would fail validation. */
+size_t rmm_workspace_bytes(rmm_dtype dtype, int64_t M, int64_t N, int64_t K, int gated);
+size_t rmm_workspace_bytes_ex(rmm_dtype dtype, int64_t M, int64_t N, int64_t K, int gated,
+                              rmm_variant variant, int splits);
+
+/* Host-only planning, no HIP call: validates the arguments exactly as the
+ * entry points do (pointer values are only compared, never dereferenced) and
+ * reports the variant and split count that would run.  *variant_out and
+ * *splits_out may be NULL. */
+rmm_status rmm_plan(const void* X, const void* g, const void* W1, const void* W3, const void* Y,
+                    float eps, int64_t M, int64_t N, int64_t K, rmm_dtype dtype, int gated,
+                    rmm_variant variant, int splits, const void* ws, size_t ws_bytes,
+                    rmm_variant* variant_out, int* splits_out);
+
+const char* rmm_status_string(rmm_status s);
+int rmm_last_hip_error(void);
+int rmm_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RMM_H */

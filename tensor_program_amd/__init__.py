@@ -1,0 +1,128 @@
+"""Fused RMSNorm+MatMul for MI355X (gfx950): Python front end of librmm.so.
+
+    import tensor_program_amd as tpa
+    y = tpa.rmsnorm_matmul(x, g, w, eps)             # Y = RMSNorm(x; g, eps) @ w
+    y = tpa.rmsnorm_gated_mlp(x, g, w1, w3, eps)     # silu(norm(x) @ w1) * (norm(x) @ w3)
+
+x: [M, K], g: [K], w/w1/w3: [K, N], all contiguous, on one GPU, all float32 or
+all bfloat16.  The work is enqueued on torch's current stream; this module
+only marshals arguments (see include/rmm.h for the contract).
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _binding
+from ._binding import RmmError, load_library  # noqa: F401
+
+__all__ = ["rmsnorm_matmul", "rmsnorm_gated_mlp", "RmmError", "load_library", "Workspace"]
+
+_DTYPES = {torch.float32: _binding.DTYPE_F32, torch.bfloat16: _binding.DTYPE_BF16}
+
+
+class Workspace:
+    """A zero-filled device workspace for the split-K variant.
+
+    The kernels leave it zeroed after every call, so one workspace serves any
+    number of calls on one stream.  Calls that may overlap (different streams)
+    need different workspaces.
+    """
+
+    def __init__(self, nbytes: int, device):
+        self.nbytes = int(nbytes)
+        self.tensor = torch.zeros(max(self.nbytes, 1), dtype=torch.uint8, device=device)
+
+    @property
+    def ptr(self) -> int:
+        return self.tensor.data_ptr()
+
+
+_workspaces: dict = {}
+
+
+def _workspace_for(device, stream_handle: int, nbytes: int) -> Workspace:
+    key = (str(device), stream_handle)
+    ws = _workspaces.get(key)
+    if ws is None or ws.nbytes < nbytes:
+        ws = Workspace(nbytes, device)
+        _workspaces[key] = ws
+    return ws
+
+
+def _check_operands(tensors, names):
+    t0 = tensors[0]
+    if t0.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {t0.dtype}; use float32 or bfloat16")
+    for t, n in zip(tensors, names):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{n} must be a torch.Tensor")
+        if t.dtype != t0.dtype:
+            raise TypeError(f"{n} has dtype {t.dtype}, expected {t0.dtype}")
+        if t.device != t0.device or t.device.type != "cuda":
+            raise ValueError(f"{n} must be on the same GPU as the others")
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+
+
+def _call(x, g, w1, w3, eps, out, variant, splits, workspace):
+    gated = w3 is not None
+    tensors = [x, g, w1] + ([w3] if gated else [])
+    names = ["x", "g", "w1", "w3"] if gated else ["x", "g", "w"]
+    _check_operands(tensors, names)
+    if x.dim() != 2 or g.dim() != 1 or w1.dim() != 2:
+        raise ValueError("expected x: [M, K], g: [K], w: [K, N]")
+    M, K = x.shape
+    K2, N = w1.shape
+    if K2 != K or g.shape[0] != K or (gated and tuple(w3.shape) != (K, N)):
+        raise ValueError(f"shape mismatch: x {tuple(x.shape)}, g {tuple(g.shape)}, "
+                         f"w {tuple(w1.shape)}")
+    if out is None:
+        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    else:
+        _check_operands([x, out], ["x", "out"])
+        if tuple(out.shape) != (M, N):
+            raise ValueError(f"out has shape {tuple(out.shape)}, expected {(M, N)}")
+    lib = load_library()
+    dtype = _DTYPES[x.dtype]
+    stream = torch.cuda.current_stream(x.device).cuda_stream
+    need = _binding.workspace_bytes(dtype, M, N, K, gated, variant, splits)
+    if workspace is None and need > 0:
+        workspace = _workspace_for(x.device, stream, need)
+    ws_ptr = workspace.ptr if workspace is not None else None
+    ws_bytes = workspace.nbytes if workspace is not None else 0
+    v = _binding.VARIANTS[variant]
+    if gated:
+        st = lib.rmsnorm_gated_mlp_ex(x.data_ptr(), g.data_ptr(), w1.data_ptr(), w3.data_ptr(),
+                                      out.data_ptr(), float(eps), M, N, K, dtype, v, splits,
+                                      ws_ptr, ws_bytes, stream)
+    else:
+        st = lib.rmsnorm_matmul_ex(x.data_ptr(), g.data_ptr(), w1.data_ptr(), out.data_ptr(),
+                                   float(eps), M, N, K, dtype, v, splits, ws_ptr, ws_bytes, stream)
+    _binding.check(st)
+    return out
+
+
+def rmsnorm_matmul(x, g, w, eps: float, out=None, variant: str = "auto", splits: int = 0,
+                   workspace: Workspace | None = None):
+    """Y = RMSNorm(x; g, eps) @ w, fused (the normalised x is never stored)."""
+    return _call(x, g, w, None, eps, out, variant, splits, workspace)
+
+
+def rmsnorm_gated_mlp(x, g, w1, w3, eps: float, out=None, variant: str = "auto",
+                      splits: int = 0, workspace: Workspace | None = None):
+    """Y = silu(RMSNorm(x) @ w1) * (RMSNorm(x) @ w3), fused."""
+    return _call(x, g, w1, w3, eps, out, variant, splits, workspace)
+
+
+def plan(M, N, K, dtype=torch.bfloat16, gated=False, variant="auto", splits=0,
+         with_workspace=True):
+    """Which variant and split count a call of this shape would run (host only)."""
+    # Distinct, 16-byte aligned stand-in addresses; rmm_plan never dereferences them.
+    base = 1 << 40
+    span = 1 << 36
+    ptrs = [base + i * span for i in range(6)]
+    d = _DTYPES[dtype]
+    ws = ptrs[5] if with_workspace else None
+    nb = _binding.workspace_bytes(d, M, N, K, gated, variant, splits) if with_workspace else 0
+    return _binding.plan(ptrs[0], ptrs[1], ptrs[2], ptrs[3] if gated else None, ptrs[4], 1e-6,
+                         M, N, K, d, gated, variant, splits, ws, nb)

@@ -1,0 +1,97 @@
+"""ctypes binding of librmm.so: argument marshalling only.
+
+Every step of the computation runs in the HIP kernels behind the C ABI
+(include/rmm.h).  PyTorch provides device memory and the current stream.
+If the library is missing this module raises; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librmm.so")
+
+DTYPE_F32, DTYPE_BF16 = 0, 1
+VARIANTS = {"auto": 0, "generic": 1, "decode": 2, "prefill": 3}
+VARIANT_NAMES = {v: k for k, v in VARIANTS.items()}
+STATUS_OK = 0
+
+# Exported symbols of include/rmm.h.
+SYMBOLS = ("rmsnorm_matmul", "rmsnorm_gated_mlp", "rmsnorm_matmul_ex", "rmsnorm_gated_mlp_ex",
+           "rmm_workspace_bytes", "rmm_workspace_bytes_ex", "rmm_plan", "rmm_status_string",
+           "rmm_last_hip_error", "rmm_abi_version")
+
+_lib = None
+
+
+class RmmError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH):
+    """Load librmm.so and declare its signatures.  Raises if it is not built."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python -m tensor_program_amd.build` "
+                          "(there is no non-HIP fallback)")
+    lib = ctypes.CDLL(path)
+    vp, f32, i64, i32, sz = (ctypes.c_void_p, ctypes.c_float, ctypes.c_int64, ctypes.c_int,
+                             ctypes.c_size_t)
+    lib.rmsnorm_matmul.argtypes = [vp, vp, vp, vp, f32, i64, i64, i64, i32, vp, sz, vp]
+    lib.rmsnorm_gated_mlp.argtypes = [vp, vp, vp, vp, vp, f32, i64, i64, i64, i32, vp, sz, vp]
+    lib.rmsnorm_matmul_ex.argtypes = [vp, vp, vp, vp, f32, i64, i64, i64, i32, i32, i32, vp, sz,
+                                      vp]
+    lib.rmsnorm_gated_mlp_ex.argtypes = [vp, vp, vp, vp, vp, f32, i64, i64, i64, i32, i32, i32,
+                                         vp, sz, vp]
+    for f in ("rmsnorm_matmul", "rmsnorm_gated_mlp", "rmsnorm_matmul_ex", "rmsnorm_gated_mlp_ex"):
+        getattr(lib, f).restype = i32
+    lib.rmm_workspace_bytes.argtypes = [i32, i64, i64, i64, i32]
+    lib.rmm_workspace_bytes.restype = sz
+    lib.rmm_workspace_bytes_ex.argtypes = [i32, i64, i64, i64, i32, i32, i32]
+    lib.rmm_workspace_bytes_ex.restype = sz
+    lib.rmm_plan.argtypes = [vp, vp, vp, vp, vp, f32, i64, i64, i64, i32, i32, i32, i32, vp, sz,
+                             ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.rmm_plan.restype = i32
+    lib.rmm_status_string.argtypes = [i32]
+    lib.rmm_status_string.restype = ctypes.c_char_p
+    lib.rmm_last_hip_error.argtypes = []
+    lib.rmm_last_hip_error.restype = i32
+    lib.rmm_abi_version.argtypes = []
+    lib.rmm_abi_version.restype = i32
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().rmm_status_string(status).decode()
+
+
+def check(status: int):
+    if status != STATUS_OK:
+        msg = status_string(status)
+        if status == 7:
+            msg += f" (hipError_t {load_library().rmm_last_hip_error()})"
+        raise RmmError(status, msg)
+
+
+def workspace_bytes(dtype: int, M: int, N: int, K: int, gated: bool, variant: str = "auto",
+                    splits: int = 0) -> int:
+    return int(load_library().rmm_workspace_bytes_ex(dtype, M, N, K, int(gated),
+                                                     VARIANTS[variant], splits))
+
+
+def plan(X, g, W1, W3, Y, eps, M, N, K, dtype, gated, variant="auto", splits=0, ws=None,
+         ws_bytes=0):
+    """Host-only planning through rmm_plan: (status, variant name, splits)."""
+    v = ctypes.c_int(-1)
+    s = ctypes.c_int(-1)
+    st = load_library().rmm_plan(X, g, W1, W3, Y, eps, M, N, K, dtype, int(gated),
+                                 VARIANTS[variant], splits, ws, ws_bytes, ctypes.byref(v),
+                                 ctypes.byref(s))
+    return st, VARIANT_NAMES.get(v.value), s.value

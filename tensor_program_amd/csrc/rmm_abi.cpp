@@ -1,0 +1,221 @@
+// C ABI of the fused RMSNorm+MatMul library: host-side validation, variant
+// selection and launch.  Validation runs before any HIP call, so every error
+// path can be exercised on a machine without a GPU.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/rmm.h"
+#include "rmm_device.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+struct Plan {
+  rmm_variant variant;
+  int splits;
+  size_t ws_bytes;
+  DecodePlan dec;
+};
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
+  if (!a || !b || an == 0 || bn == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + bn && b0 < a0 + an;
+}
+
+// Decode: few rows; the split count aims at ~3 workgroups per CU (256 CUs).
+constexpr int64_t kDecodeMaxM = 32;
+constexpr int64_t kDecodeMaxMGated = 16;
+constexpr int64_t kTargetWorkgroups = 768;
+
+int auto_decode_splits(int64_t N, int64_t K) {
+  const int64_t tiles = (N + 127) / 128;
+  if (tiles < 1) return 1;
+  int64_t s = (kTargetWorkgroups + tiles / 2) / tiles;
+  const int64_t kgran = (K + 127) / 128;
+  if (s < 1) s = 1;
+  if (s > kgran) s = kgran;
+  return (int)s;
+}
+
+// Shape/variant part of the plan; `aligned` says whether every pointer is
+// 16-byte aligned, `have_ws` whether a workspace was passed.
+rmm_status plan_shape(int64_t M, int64_t N, int64_t K, rmm_dtype dtype, int gated,
+                      rmm_variant variant, int splits, bool aligned, bool have_ws, Plan* out) {
+  if (variant < RMM_VARIANT_AUTO || variant > RMM_VARIANT_PREFILL) return RMM_ERR_VARIANT;
+  if (splits < 0) return RMM_ERR_VARIANT;
+  if (splits != 0 && variant != RMM_VARIANT_DECODE) return RMM_ERR_VARIANT;
+  if (M == 0 || N == 0) {  // nothing to compute, nothing launched
+    out->variant = variant == RMM_VARIANT_AUTO ? RMM_VARIANT_GENERIC : variant;
+    out->splits = 1;
+    out->ws_bytes = 0;
+    return RMM_OK;
+  }
+  const bool fast_layout = dtype == RMM_DTYPE_BF16 && K % 8 == 0 && N % 8 == 0 && aligned;
+  const bool decode_ok = fast_layout && M <= (gated ? kDecodeMaxMGated : kDecodeMaxM);
+  rmm_variant v = variant;
+  if (v == RMM_VARIANT_AUTO) v = decode_ok ? RMM_VARIANT_DECODE : RMM_VARIANT_GENERIC;
+  if (v == RMM_VARIANT_DECODE && !decode_ok) return RMM_ERR_VARIANT;
+  if (v == RMM_VARIANT_PREFILL) return RMM_ERR_VARIANT;  // not built yet
+  out->variant = v;
+  out->splits = 1;
+  out->ws_bytes = 0;
+  if (v == RMM_VARIANT_DECODE) {
+    int s = splits;
+    if (s == 0) s = have_ws ? auto_decode_splits(N, K) : 1;
+    if (s > (K + 127) / 128) return RMM_ERR_VARIANT;
+    if (s > 1 && !have_ws) return RMM_ERR_WORKSPACE;  // a forced split count needs one
+    rmm_decode_plan(M, N, K, gated, s, 2, &out->dec);
+    out->splits = out->dec.splits;
+    out->ws_bytes = out->dec.ws_bytes;
+  }
+  return RMM_OK;
+}
+
+rmm_status plan_call(const void* X, const void* g, const void* W1, const void* W3, const void* Y,
+                     float eps, int64_t M, int64_t N, int64_t K, rmm_dtype dtype, int gated,
+                     rmm_variant variant, int splits, const void* ws, size_t ws_bytes, Plan* out) {
+  // 1. pointers
+  const bool empty = (M == 0 || N == 0);
+  if (!empty && (!X || !g || !W1 || !Y || (gated && !W3))) return RMM_ERR_NULL;
+  // 2. shape
+  if (M < 0 || N < 0 || K <= 0) return RMM_ERR_SHAPE;
+  int64_t mk, kn, mn, tmp;
+  if (__builtin_mul_overflow(M, K, &mk) || __builtin_mul_overflow(K, N, &kn) ||
+      __builtin_mul_overflow(M, N, &mn) || __builtin_mul_overflow(mk, (int64_t)4, &tmp) ||
+      __builtin_mul_overflow(kn, (int64_t)4, &tmp) || __builtin_mul_overflow(mn, (int64_t)4, &tmp))
+    return RMM_ERR_SHAPE;
+  // 3. eps
+  if (!isfinite(eps) || eps < 0.0f) return RMM_ERR_EPS;
+  // 4. dtype
+  if (dtype != RMM_DTYPE_F32 && dtype != RMM_DTYPE_BF16) return RMM_ERR_DTYPE;
+  const size_t es = dtype == RMM_DTYPE_F32 ? 4 : 2;
+  // 5. aliasing of the output with the inputs and the workspace
+  if (!empty) {
+    const size_t yb = (size_t)mn * es;
+    if (overlaps(Y, yb, X, (size_t)mk * es) || overlaps(Y, yb, g, (size_t)K * es) ||
+        overlaps(Y, yb, W1, (size_t)kn * es) || (gated && overlaps(Y, yb, W3, (size_t)kn * es)) ||
+        overlaps(Y, yb, ws, ws ? ws_bytes : 0))
+      return RMM_ERR_ALIAS;
+  }
+  // 6. variant (and the split count it would use)
+  const bool aligned = empty || (aligned16(X) && aligned16(g) && aligned16(W1) &&
+                                 (!gated || aligned16(W3)) && aligned16(Y));
+  rmm_status st = plan_shape(M, N, K, dtype, gated, variant, splits, aligned, ws != nullptr, out);
+  if (st != RMM_OK) return st;
+  // 7. workspace
+  if (ws && ws_bytes < out->ws_bytes) return RMM_ERR_WORKSPACE;
+  return RMM_OK;
+}
+
+rmm_status run(const void* X, const void* g, const void* W1, const void* W3, void* Y, float eps,
+               int64_t M, int64_t N, int64_t K, rmm_dtype dtype, int gated, rmm_variant variant,
+               int splits, void* ws, size_t ws_bytes, hipStream_t stream) {
+  Plan plan;
+  rmm_status st =
+      plan_call(X, g, W1, W3, Y, eps, M, N, K, dtype, gated, variant, splits, ws, ws_bytes, &plan);
+  if (st != RMM_OK) return st;
+  if (M == 0 || N == 0) return RMM_OK;
+  RmmArgs a{X, g, W1, gated ? W3 : nullptr, Y, eps, M, N, K, gated, stream};
+  hipError_t err = hipSuccess;
+  switch (plan.variant) {
+    case RMM_VARIANT_GENERIC:
+      err = rmm_launch_generic(a, dtype == RMM_DTYPE_BF16);
+      break;
+    case RMM_VARIANT_DECODE:
+      err = rmm_launch_decode(a, plan.dec, plan.dec.splits > 1 ? ws : nullptr);
+      break;
+    default:
+      return RMM_ERR_VARIANT;
+  }
+  if (err != hipSuccess) {
+    g_last_hip_error = (int)err;
+    return RMM_ERR_HIP;
+  }
+  return RMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+rmm_status rmsnorm_matmul(const void* X, const void* g, const void* W, void* Y, float eps,
+                          int64_t M, int64_t N, int64_t K, rmm_dtype dtype, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+  return run(X, g, W, nullptr, Y, eps, M, N, K, dtype, 0, RMM_VARIANT_AUTO, 0, ws, ws_bytes,
+             stream);
+}
+
+rmm_status rmsnorm_gated_mlp(const void* X, const void* g, const void* W1, const void* W3,
+                             void* Y, float eps, int64_t M, int64_t N, int64_t K,
+                             rmm_dtype dtype, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return run(X, g, W1, W3, Y, eps, M, N, K, dtype, 1, RMM_VARIANT_AUTO, 0, ws, ws_bytes, stream);
+}
+
+rmm_status rmsnorm_matmul_ex(const void* X, const void* g, const void* W, void* Y, float eps,
+                             int64_t M, int64_t N, int64_t K, rmm_dtype dtype,
+                             rmm_variant variant, int splits, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
+  return run(X, g, W, nullptr, Y, eps, M, N, K, dtype, 0, variant, splits, ws, ws_bytes, stream);
+}
+
+rmm_status rmsnorm_gated_mlp_ex(const void* X, const void* g, const void* W1, const void* W3,
+                                void* Y, float eps, int64_t M, int64_t N, int64_t K,
+                                rmm_dtype dtype, rmm_variant variant, int splits, void* ws,
+                                size_t ws_bytes, hipStream_t stream) {
+  return run(X, g, W1, W3, Y, eps, M, N, K, dtype, 1, variant, splits, ws, ws_bytes, stream);
+}
+
+size_t rmm_workspace_bytes_ex(rmm_dtype dtype, int64_t M, int64_t N, int64_t K, int gated,
+                              rmm_variant variant, int splits) {
+  // Sizes only: aligned pointers and a workspace are assumed to be present.
+  if (M < 0 || N < 0 || K <= 0) return 0;
+  if (dtype != RMM_DTYPE_F32 && dtype != RMM_DTYPE_BF16) return 0;
+  Plan plan;
+  if (plan_shape(M, N, K, dtype, gated ? 1 : 0, variant, splits, true, true, &plan) != RMM_OK)
+    return 0;
+  return plan.ws_bytes;
+}
+
+size_t rmm_workspace_bytes(rmm_dtype dtype, int64_t M, int64_t N, int64_t K, int gated) {
+  return rmm_workspace_bytes_ex(dtype, M, N, K, gated, RMM_VARIANT_AUTO, 0);
+}
+
+rmm_status rmm_plan(const void* X, const void* g, const void* W1, const void* W3, const void* Y,
+                    float eps, int64_t M, int64_t N, int64_t K, rmm_dtype dtype, int gated,
+                    rmm_variant variant, int splits, const void* ws, size_t ws_bytes,
+                    rmm_variant* variant_out, int* splits_out) {
+  Plan plan;
+  rmm_status st = plan_call(X, g, W1, W3, Y, eps, M, N, K, dtype, gated ? 1 : 0, variant, splits,
+                            ws, ws_bytes, &plan);
+  if (st == RMM_OK) {
+    if (variant_out) *variant_out = plan.variant;
+    if (splits_out) *splits_out = plan.splits;
+  }
+  return st;
+}
+
+const char* rmm_status_string(rmm_status s) {
+  switch (s) {
+    case RMM_OK: return "RMM_OK";
+    case RMM_ERR_NULL: return "RMM_ERR_NULL: a required pointer is NULL";
+    case RMM_ERR_SHAPE: return "RMM_ERR_SHAPE: M < 0, N < 0, K <= 0 or size overflow";
+    case RMM_ERR_EPS: return "RMM_ERR_EPS: eps must be finite and >= 0";
+    case RMM_ERR_DTYPE: return "RMM_ERR_DTYPE: unknown dtype";
+    case RMM_ERR_ALIAS: return "RMM_ERR_ALIAS: Y overlaps an input or the workspace";
+    case RMM_ERR_WORKSPACE: return "RMM_ERR_WORKSPACE: workspace too small";
+    case RMM_ERR_HIP: return "RMM_ERR_HIP: kernel launch failed";
+    case RMM_ERR_VARIANT: return "RMM_ERR_VARIANT: variant/splits cannot run this call";
+  }
+  return "unknown rmm_status";
+}
+
+int rmm_last_hip_error(void) { return g_last_hip_error; }
+
+int rmm_abi_version(void) { return RMM_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,77 @@
+// Device-side helpers shared by the gfx950 kernels of the RMSNorm+MatMul
+// library: storage types, bf16 conversion, vector types, launcher prototypes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rmm {
+
+typedef uint16_t bf16_t;  // bf16 storage (bit pattern)
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// bf16 bits -> fp32 (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(bf16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (gfx950 v_cvt_pk_bf16_f32).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  __bf16 b = (__bf16)f;
+  return __builtin_bit_cast(bf16_t, b);
+}
+// Two fp32 -> packed bf16 pair (lo, hi), round to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// Load/store of one element of the storage type as fp32.
+__device__ __forceinline__ float load_f32(const float* p) { return *p; }
+__device__ __forceinline__ float load_f32(const bf16_t* p) { return bf16_to_f32(*p); }
+__device__ __forceinline__ void store_f32(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store_f32(bf16_t* p, float v) { *p = f32_to_bf16(v); }
+
+// silu(z) * z3 for the gated epilogue.
+__device__ __forceinline__ float silu_gate(float z1, float z3) {
+  return z1 / (1.0f + expf(-z1)) * z3;
+}
+
+// 1 / sqrt(ss / K + eps) with IEEE division and square root, so that
+// exact inputs (ss = K * 4^j, eps = 0) give an exact power of two.
+__device__ __forceinline__ float inv_rms(float ss, int64_t K, float eps) {
+  return 1.0f / __fsqrt_rn(__fdiv_rn(ss, (float)K) + eps);
+}
+
+}  // namespace rmm
+
+// Host-side launchers (return hipSuccess or the launch error).
+struct RmmArgs {
+  const void* X;
+  const void* g;
+  const void* W1;
+  const void* W3;  // NULL unless gated
+  void* Y;
+  float eps;
+  int64_t M, N, K;
+  int gated;
+  hipStream_t stream;
+};
+
+hipError_t rmm_launch_generic(const RmmArgs& a, bool bf16);
+
+struct DecodePlan {
+  int mb;          // 16-row blocks (1..4)
+  int nbw;         // 32-deep k-blocks per wave per step
+  int splits;      // K chunks combined across workgroups
+  int64_t kchunk;  // K per chunk (multiple of 128)
+  int64_t tiles;   // 128-column tiles
+  size_t ws_cnt_off, ws_ssq_off, ws_part_off, ws_bytes;
+};
+void rmm_decode_plan(int64_t M, int64_t N, int64_t K, int gated, int splits, int nbw,
+                     DecodePlan* p);
+hipError_t rmm_launch_decode(const RmmArgs& a, const DecodePlan& p, void* ws);

@@ -1,0 +1,137 @@
+// Generic fused RMSNorm+MatMul kernel: any M, N, K, any alignment, fp32 or
+// bf16 storage.  fp32 products on the vector ALUs.
+//
+// Fusion as in the Mirage example (paper review, "μGraph示例" and the
+// abstract expression E(O) = sum(k, div(mul(I1,I2), I3)) of "核心公式"): the
+// k-sum of X*g*W and the row sum of squares are accumulated separately, and
+// the division by the row RMS is applied once to the finished sum.
+//
+// Workgroup tile: 64 columns x 8 rows, 256 threads = 64 columns x 4 k-slices.
+// Thread (c, s) owns column c of the tile and k = s, s+4, s+8, ... of each
+// 64-deep chunk; the four k-slices are summed through LDS at the end.  A
+// chunk of X*g (8 x 64, fp32) is staged in LDS and read as broadcasts.
+#include "rmm_device.h"
+
+namespace rmm {
+
+constexpr int GEN_COLS = 64;
+constexpr int GEN_ROWS = 8;
+constexpr int GEN_KC = 64;
+constexpr int GEN_THREADS = 256;
+
+template <typename T, bool GATED>
+__global__ __launch_bounds__(GEN_THREADS) void generic_kernel(
+    const T* __restrict__ X, const T* __restrict__ g, const T* __restrict__ W1,
+    const T* __restrict__ W3, T* __restrict__ Y, float eps, int64_t M, int64_t N, int64_t K) {
+  __shared__ float a_s[GEN_ROWS][GEN_KC];
+  __shared__ float red[GATED ? 2 : 1][4][GEN_ROWS][GEN_COLS];
+  __shared__ float ss_s[GEN_ROWS][32];
+  __shared__ float inv_s[GEN_ROWS];
+
+  const int tid = threadIdx.x;
+  const int64_t n0 = (int64_t)blockIdx.x * GEN_COLS;
+  const int64_t m0 = (int64_t)blockIdx.y * GEN_ROWS;
+
+  // Row sums of squares of raw X (32 threads per row).
+  {
+    const int r = tid / 32, j = tid % 32;
+    float ss = 0.0f;
+    if (m0 + r < M) {
+      const T* xr = X + (m0 + r) * K;
+      for (int64_t k = j; k < K; k += 32) {
+        float x = load_f32(xr + k);
+        ss += x * x;
+      }
+    }
+    ss_s[r][j] = ss;
+  }
+  __syncthreads();
+  if (tid < GEN_ROWS) {
+    float ss = 0.0f;
+    for (int j = 0; j < 32; ++j) ss += ss_s[tid][j];
+    inv_s[tid] = inv_rms(ss, K, eps);
+  }
+
+  const int c = tid % GEN_COLS, s = tid / GEN_COLS;
+  const int64_t n = n0 + c;
+  const bool col_ok = n < N;
+  float acc1[GEN_ROWS], acc3[GEN_ROWS];
+#pragma unroll
+  for (int i = 0; i < GEN_ROWS; ++i) acc1[i] = acc3[i] = 0.0f;
+
+  for (int64_t k0 = 0; k0 < K; k0 += GEN_KC) {
+    __syncthreads();
+    // Stage X*g for the chunk (fp32, no rounding).
+    for (int e = tid; e < GEN_ROWS * GEN_KC; e += GEN_THREADS) {
+      const int r = e / GEN_KC, kk = e % GEN_KC;
+      const int64_t m = m0 + r, k = k0 + kk;
+      a_s[r][kk] = (m < M && k < K) ? load_f32(X + m * K + k) * load_f32(g + k) : 0.0f;
+    }
+    __syncthreads();
+    if (col_ok) {
+      const int64_t kend = (K - k0 < GEN_KC) ? (K - k0) : GEN_KC;
+      for (int kk = s; kk < kend; kk += 4) {
+        const float w1 = load_f32(W1 + (k0 + kk) * N + n);
+        float w3 = 0.0f;
+        if (GATED) w3 = load_f32(W3 + (k0 + kk) * N + n);
+#pragma unroll
+        for (int i = 0; i < GEN_ROWS; ++i) {
+          acc1[i] += a_s[i][kk] * w1;
+          if (GATED) acc3[i] += a_s[i][kk] * w3;
+        }
+      }
+    }
+  }
+
+  // Sum the four k-slices, then scale by 1/RMS (after the k-sum) and store.
+#pragma unroll
+  for (int i = 0; i < GEN_ROWS; ++i) {
+    red[0][s][i][c] = acc1[i];
+    if (GATED) red[GATED ? 1 : 0][s][i][c] = acc3[i];
+  }
+  __syncthreads();
+  for (int e = tid; e < GEN_ROWS * GEN_COLS; e += GEN_THREADS) {
+    const int r = e / GEN_COLS, cc = e % GEN_COLS;
+    const int64_t m = m0 + r, nn = n0 + cc;
+    if (m >= M || nn >= N) continue;
+    const float inv = inv_s[r];
+    const float z1 = (red[0][0][r][cc] + red[0][1][r][cc] + red[0][2][r][cc] + red[0][3][r][cc]) * inv;
+    float y = z1;
+    if (GATED) {
+      const int b = GATED ? 1 : 0;
+      const float z3 = (red[b][0][r][cc] + red[b][1][r][cc] + red[b][2][r][cc] + red[b][3][r][cc]) * inv;
+      y = silu_gate(z1, z3);
+    }
+    store_f32(Y + m * N + nn, y);
+  }
+}
+
+}  // namespace rmm
+
+hipError_t rmm_launch_generic(const RmmArgs& a, bool bf16) {
+  using namespace rmm;
+  dim3 grid((unsigned)((a.N + GEN_COLS - 1) / GEN_COLS), (unsigned)((a.M + GEN_ROWS - 1) / GEN_ROWS));
+  dim3 block(GEN_THREADS);
+  if (bf16) {
+    auto X = (const bf16_t*)a.X, g = (const bf16_t*)a.g, W1 = (const bf16_t*)a.W1,
+         W3 = (const bf16_t*)a.W3;
+    auto Y = (bf16_t*)a.Y;
+    if (a.gated)
+      hipLaunchKernelGGL((generic_kernel<bf16_t, true>), grid, block, 0, a.stream, X, g, W1, W3,
+                         Y, a.eps, a.M, a.N, a.K);
+    else
+      hipLaunchKernelGGL((generic_kernel<bf16_t, false>), grid, block, 0, a.stream, X, g, W1,
+                         W3, Y, a.eps, a.M, a.N, a.K);
+  } else {
+    auto X = (const float*)a.X, g = (const float*)a.g, W1 = (const float*)a.W1,
+         W3 = (const float*)a.W3;
+    auto Y = (float*)a.Y;
+    if (a.gated)
+      hipLaunchKernelGGL((generic_kernel<float, true>), grid, block, 0, a.stream, X, g, W1, W3, Y,
+                         a.eps, a.M, a.N, a.K);
+    else
+      hipLaunchKernelGGL((generic_kernel<float, false>), grid, block, 0, a.stream, X, g, W1, W3,
+                         Y, a.eps, a.M, a.N, a.K);
+  }
+  return hipGetLastError();
+}

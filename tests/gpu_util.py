@@ -1,0 +1,79 @@
+"""Helpers for the GPU parity tests: moving seeded inputs to the device and
+comparing the HIP path with the oracle."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import synth
+import tensor_program_amd as tpa
+
+BF16_TOL = 1e-2   # |Y_gpu - Y_ref| <= tol * (|Y_ref| + 1), bf16 storage
+F32_TOL = 1e-5    # same form, fp32 storage
+
+
+def tol_for(dtype: str) -> float:
+    return BF16_TOL if dtype == "bf16" else F32_TOL
+
+
+def to_device(inp: "synth.Inputs", name: str, device="cuda"):
+    a = inp.device_array(name)
+    if inp.wl.dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device)
+
+
+def from_device(y: torch.Tensor) -> np.ndarray:
+    """Device output -> float64 numpy (exact widening)."""
+    return y.detach().float().cpu().numpy().astype(np.float64)
+
+
+def bits_of(y: torch.Tensor) -> np.ndarray:
+    """bf16 output -> uint16 bit patterns."""
+    return y.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def run_gpu(inp: "synth.Inputs", eps: float, variant="auto", splits=0, out=None, x=None):
+    dev = "cuda"
+    X = to_device(inp, "X", dev) if x is None else x
+    g = to_device(inp, "g", dev)
+    W1 = to_device(inp, "W1", dev)
+    if inp.wl.gated:
+        W3 = to_device(inp, "W3", dev)
+        y = tpa.rmsnorm_gated_mlp(X, g, W1, W3, eps, out=out, variant=variant, splits=splits)
+    else:
+        y = tpa.rmsnorm_matmul(X, g, W1, eps, out=out, variant=variant, splits=splits)
+    torch.cuda.synchronize()
+    return y
+
+
+def run_oracle(inp: "synth.Inputs", eps: float, rows=None, cols=None):
+    X = inp.X if rows is None else inp.X[rows]
+    W1 = inp.W1 if cols is None else inp.W1[:, cols]
+    e = oracle.eps_as_passed(eps)
+    if inp.wl.gated:
+        W3 = inp.W3 if cols is None else inp.W3[:, cols]
+        return oracle.rmsnorm_gated_mlp(X, inp.g, W1, W3, e)
+    return oracle.rmsnorm_matmul(X, inp.g, W1, e)
+
+
+def assert_within_tol(y_gpu: np.ndarray, y_ref: np.ndarray, tol: float, what: str = ""):
+    assert y_gpu.shape == y_ref.shape, (y_gpu.shape, y_ref.shape)
+    assert np.all(np.isfinite(y_gpu)), f"{what}: non-finite outputs"
+    err = np.abs(y_gpu - y_ref)
+    lim = tol * (np.abs(y_ref) + 1.0)
+    bad = err > lim
+    if bad.any():
+        i = np.unravel_index(np.argmax(err / lim), err.shape)
+        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outside tolerance; worst at {i}: "
+                             f"gpu {y_gpu[i]!r} ref {y_ref[i]!r} (err/lim {err[i] / lim[i]:.3g})")
+    return float((err / lim).max()) if err.size else 0.0
+
+
+def expected_exact(y_ref: np.ndarray, dtype: str) -> np.ndarray:
+    """For exact-arithmetic inputs the oracle's result is exact; the stored
+    output is its one rounding to the storage type (nearest even)."""
+    y32 = y_ref.astype(np.float32)
+    assert np.array_equal(y32.astype(np.float64), y_ref), "exact inputs gave an inexact oracle value"
+    return synth.to_bf16_bits(y32) if dtype == "bf16" else y32

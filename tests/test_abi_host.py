@@ -1,0 +1,137 @@
+"""The C ABI on the host: the library loads, exports every symbol the header
+declares, validates arguments in the documented order and plans variants --
+all without touching a GPU (every call here fails validation or is empty,
+so no HIP call is made)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import tensor_program_amd as tpa
+from tensor_program_amd import _binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rmm.h")
+
+OK, NULL, SHAPE, EPS, DTYPE, ALIAS, WORKSPACE, HIP, VARIANT = range(9)
+BF16, F32 = _binding.DTYPE_BF16, _binding.DTYPE_F32
+# Fake, distinct, 16-byte aligned device addresses: never dereferenced here.
+A = [(1 << 40) + i * (1 << 34) for i in range(8)]
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return tpa.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"defined"})
+
+
+def test_header_symbols_exported(lib):
+    names = declared_functions()
+    assert set(names) == set(_binding.SYMBOLS), names
+    out = subprocess.run(["nm", "-D", "--defined-only", _binding.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for n in names:
+        assert n in exported, n
+        getattr(lib, n)
+
+
+def test_abi_version(lib):
+    assert lib.rmm_abi_version() == 1
+
+
+def call(lib, X=A[0], g=A[1], W=A[2], Y=A[3], eps=1e-6, M=16, N=64, K=64, dtype=BF16,
+         variant=0, splits=0, ws=None, ws_bytes=0):
+    return lib.rmsnorm_matmul_ex(X, g, W, Y, eps, M, N, K, dtype, variant, splits, ws, ws_bytes,
+                                 None)
+
+
+def call_gated(lib, W3=A[4], **kw):
+    kw.setdefault("X", A[0])
+    return lib.rmsnorm_gated_mlp_ex(kw.get("X"), A[1], A[2], W3, A[3], kw.get("eps", 1e-6),
+                                    16, 64, 64, BF16, 0, 0, None, 0, None)
+
+
+def test_validation_order(lib):
+    assert call(lib, X=None) == NULL
+    assert call(lib, Y=None) == NULL
+    assert call_gated(lib, W3=None) == NULL
+    assert call(lib, X=None, K=0) == NULL           # NULL is checked first
+    assert call(lib, K=0) == SHAPE
+    assert call(lib, M=-1) == SHAPE
+    assert call(lib, N=-3) == SHAPE
+    assert call(lib, M=1 << 62, K=1 << 4) == SHAPE  # element count overflow
+    assert call(lib, K=0, eps=-1.0) == SHAPE        # shape before eps
+    assert call(lib, eps=-1e-6) == EPS
+    assert call(lib, eps=float("nan")) == EPS
+    assert call(lib, eps=float("inf")) == EPS
+    assert call(lib, eps=-1.0, dtype=7) == EPS      # eps before dtype
+    assert call(lib, dtype=7) == DTYPE
+    assert call(lib, Y=A[0] + 16) == ALIAS           # Y inside X
+    assert call(lib, Y=A[2] - 8) == ALIAS            # Y overlapping the start of W
+    assert call(lib, ws=A[3] + 64, ws_bytes=1 << 20) == ALIAS
+    assert call(lib, variant=9) == VARIANT
+    assert call(lib, variant=1, splits=2) == VARIANT  # splits only for decode
+    assert call(lib, variant=2, dtype=F32) == VARIANT  # decode is bf16 only
+    assert call(lib, variant=2, M=33) == VARIANT
+    assert call(lib, variant=2, N=60) == VARIANT      # N % 8 != 0
+    assert call(lib, variant=2, X=A[0] + 2) == VARIANT  # unaligned
+    assert call(lib, variant=2, splits=2) == VARIANT   # K=64: one 128-deep granule
+    assert call(lib, variant=2, K=4096, N=6144, splits=8) == WORKSPACE  # needs a workspace
+    need = lib.rmm_workspace_bytes_ex(BF16, 16, 6144, 4096, 0, 2, 8)
+    assert need > 0
+    assert call(lib, variant=2, K=4096, N=6144, splits=8, ws=A[6], ws_bytes=need - 1) == WORKSPACE
+
+
+def test_empty_shapes_are_noops(lib):
+    # M == 0 or N == 0: RMM_OK, nothing launched (NULL pointers allowed).
+    assert call(lib, X=None, g=None, W=None, Y=None, M=0) == OK
+    assert call(lib, X=None, g=None, W=None, Y=None, N=0) == OK
+
+
+def test_empty_shapes_plan_without_work(lib):
+    # Regression: sizing an empty call used to divide by the (zero) tile count.
+    for (M, N) in ((0, 6144), (16, 0), (0, 0)):
+        assert lib.rmm_workspace_bytes(BF16, M, N, 4096, 0) == 0
+        assert lib.rmm_workspace_bytes_ex(BF16, M, N, 4096, 1, 2, 0) == 0
+        assert tpa.plan(M, N, 4096)[0] == OK
+
+
+def test_status_strings(lib):
+    for s in range(9):
+        assert _binding.status_string(s).startswith("RMM_")
+    assert "unknown" in _binding.status_string(99)
+
+
+def test_variant_selection():
+    import torch
+    assert tpa.plan(16, 6144, 4096)[1:] == ("decode", 16)
+    assert tpa.plan(16, 6144, 4096, with_workspace=False)[1:] == ("decode", 1)
+    assert tpa.plan(64, 14336, 4096, gated=True)[1] == "generic"
+    assert tpa.plan(8, 1024, 1024, dtype=torch.float32)[1] == "generic"
+    assert tpa.plan(16, 6144, 4096, variant="decode", splits=3)[1:] == ("decode", 3)
+    # split counts that do not divide K evenly are rounded to 128-deep chunks
+    st, v, s = tpa.plan(17, 520, 1000, variant="decode", splits=4)
+    assert (st, v, s) == (0, "decode", 4)
+    st, v, s = tpa.plan(32, 1032, 1024, variant="decode", splits=5)
+    assert (st, v, s) == (0, "decode", 4)
+
+
+def test_workspace_sizes(lib):
+    assert lib.rmm_workspace_bytes(BF16, 16, 6144, 4096, 0) == \
+        lib.rmm_workspace_bytes_ex(BF16, 16, 6144, 4096, 0, 0, 0) > 0
+    assert lib.rmm_workspace_bytes_ex(BF16, 16, 6144, 4096, 0, 2, 1) == 0
+    assert lib.rmm_workspace_bytes(F32, 8, 1024, 1024, 0) == 0
+    assert lib.rmm_workspace_bytes(BF16, 16, 6144, 0, 0) == 0  # invalid -> 0
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(ImportError):
+        _binding.load_library(str(tmp_path / "missing.so"))

@@ -1,0 +1,206 @@
+"""Parity of the HIP path with the CPU oracle (needs an MI355X).
+
+* exact-arithmetic cases: inputs on which every product and partial sum is
+  exact in fp32 in any order, so the kernels must reproduce the oracle's
+  result bit for bit (after its one rounding to the storage type), for every
+  variant and forced split count -- the float analogue of the randomised
+  equivalence test of the Mirage paper review ("等价性验证");
+* the five workloads within tolerance, on all outputs where the oracle is
+  quick and on sampled rows/columns at the full sizes;
+* edge cases: empty, ragged, unaligned, zero rows, canaries around Y.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+import tensor_program_amd as tpa
+from tests.gpu_util import (assert_within_tol, bits_of, expected_exact, from_device, run_gpu,
+                            run_oracle, to_device, tol_for)
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+# ---------------------------------------------------------------- exact cases
+EXACT_CASES = [
+    # (M, K, N, dtype, variant, splits)
+    (1, 8, 8, "f32", "generic", 0),
+    (5, 40, 24, "f32", "generic", 0),
+    (33, 200, 136, "bf16", "generic", 0),
+    (8, 1024, 1024, "f32", "generic", 0),
+    (16, 4096, 6144, "bf16", "generic", 0),
+    (16, 4096, 6144, "bf16", "decode", 1),
+    (16, 4096, 6144, "bf16", "decode", 3),
+    (16, 4096, 6144, "bf16", "decode", 16),
+    (16, 4096, 6144, "bf16", "decode", 32),
+    (5, 136, 264, "bf16", "decode", 1),
+    (5, 136, 264, "bf16", "decode", 2),
+    (1, 8, 8, "bf16", "decode", 0),
+    (32, 1024, 1032, "bf16", "decode", 5),
+    (17, 1000, 520, "bf16", "decode", 4),
+]
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+@pytest.mark.parametrize("case", EXACT_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_exact_bitwise(case, seed, require_gpu):
+    M, K, N, dtype, variant, splits = case
+    _log(f"exact {case} seed {seed}")
+    inp = synth.make_exact_inputs(M, K, N, dtype, seed=seed, row_pow2=(seed == 1))
+    y = run_gpu(inp, 0.0, variant=variant, splits=splits)
+    want = expected_exact(run_oracle(inp, 0.0), dtype)
+    got = bits_of(y) if dtype == "bf16" else y.cpu().numpy()
+    mism = np.argwhere(got != want)
+    assert mism.size == 0, f"{len(mism)} mismatches, first at {tuple(mism[0])}"
+
+
+# ------------------------------------------------------------ the workloads
+def _check_workload(name, variant="auto", splits=0, rows=None, cols=None):
+    wl = synth.get_workload(name)
+    _log(f"workload {name} variant {variant} splits {splits}")
+    inp = synth.make_inputs(wl)
+    y = from_device(run_gpu(inp, wl.eps, variant=variant, splits=splits))
+    if rows is not None:
+        y = y[rows]
+    if cols is not None:
+        y = y[:, cols]
+    ref = run_oracle(inp, wl.eps, rows=rows, cols=cols)
+    worst = assert_within_tol(y, ref, tol_for(wl.dtype), f"{name}/{variant}")
+    _log(f"  worst err/tol {worst:.3f}")
+
+
+def test_f32_m8_k1024_n1024(require_gpu):
+    _check_workload("f32_m8_k1024_n1024")
+
+
+@pytest.mark.parametrize("variant,splits", [("auto", 0), ("generic", 0), ("decode", 1),
+                                            ("decode", 8)])
+def test_decode_m16_k4096_n6144(variant, splits, require_gpu):
+    _check_workload("decode_m16_k4096_n6144", variant, splits)
+
+
+def _sample_rows(wl, n_random=48):
+    rng = np.random.default_rng(7)
+    rows = set(rng.choice(wl.M, size=n_random, replace=False).tolist()) | {0, wl.M - 1}
+    scale = synth.row_scales(wl)
+    if scale is not None:
+        # every scaled-by-100 row, and the smallest and largest LogUniform scales
+        if wl.row_scale == "pick_x100":
+            rows |= set(np.nonzero(scale == 100.0)[0].tolist())
+        else:
+            order = np.argsort(scale)
+            rows |= set(order[:8].tolist()) | set(order[-8:].tolist())
+    return np.array(sorted(rows))
+
+
+def test_prefill_m4096_k4096_n4096_sampled(require_gpu):
+    wl = synth.get_workload("prefill_m4096_k4096_n4096")
+    _check_workload(wl.name, rows=_sample_rows(wl))
+
+
+def test_gated_m64_k4096_n14336_sampled_cols(require_gpu):
+    wl = synth.get_workload("gated_m64_k4096_n14336")
+    cols = np.sort(np.random.default_rng(8).choice(wl.N, size=1024, replace=False))
+    _check_workload(wl.name, cols=cols)
+
+
+def test_large_m8192_k8192_n28672_sampled(require_gpu):
+    wl = synth.get_workload("large_m8192_k8192_n28672")
+    _check_workload(wl.name, rows=_sample_rows(wl, n_random=24))
+
+
+# ----------------------------------------------------------------- gated small
+@pytest.mark.parametrize("variant,splits", [("generic", 0), ("decode", 1), ("decode", 3)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_gated_small(variant, splits, dtype, require_gpu):
+    if dtype == "f32" and variant == "decode":
+        pytest.skip("decode variant is bf16 only")
+    wl = synth.Workload("gated_small", dtype, 13, 520, 392, 1e-6, True, None)
+    _log(f"gated small {dtype} {variant} {splits}")
+    inp = synth.make_inputs(wl, seed=5)
+    y = from_device(run_gpu(inp, wl.eps, variant=variant, splits=splits))
+    assert_within_tol(y, run_oracle(inp, wl.eps), tol_for(dtype), "gated_small")
+
+
+# ------------------------------------------------------------------ edge cases
+def _tensors(M, K, N, dtype=torch.bfloat16, seed=0):
+    gen = torch.Generator().manual_seed(seed)
+    x = torch.randn(M, K, generator=gen).to(dtype).cuda()
+    g = (1 + 0.1 * torch.randn(K, generator=gen)).to(dtype).cuda()
+    w = (torch.randn(K, N, generator=gen) / K ** 0.5).to(dtype).cuda()
+    return x, g, w
+
+
+def test_empty_is_noop(require_gpu):
+    for (M, N) in ((0, 16), (4, 0)):
+        x, g, w = _tensors(max(M, 1), 16, max(N, 1))
+        x = x[:M].contiguous()
+        w = w[:, :N].contiguous()
+        y = tpa.rmsnorm_matmul(x, g, w, 1e-6)
+        torch.cuda.synchronize()
+        assert tuple(y.shape) == (M, N)
+
+
+def test_zero_row_gives_zero(require_gpu):
+    for variant in ("generic", "decode"):
+        x, g, w = _tensors(4, 256, 128)
+        x[2] = 0
+        y = tpa.rmsnorm_matmul(x, g, w, 1e-6, variant=variant)
+        torch.cuda.synchronize()
+        assert torch.all(y[2] == 0)
+        assert torch.all(torch.isfinite(y.float()))
+
+
+def test_canaries_around_output(require_gpu):
+    """Y is written in full and nothing outside it is touched."""
+    for variant, (M, K, N) in (("generic", (7, 72, 200)), ("decode", (7, 1024, 1032)),
+                               ("decode", (16, 4096, 6144))):
+        x, g, w = _tensors(M, K, N)
+        guard = 4096
+        buf = torch.full((guard + M * N + guard,), float("nan"), dtype=torch.bfloat16, device="cuda")
+        buf[:guard] = 7.0
+        buf[-guard:] = -7.0
+        y = buf[guard:guard + M * N].view(M, N)
+        tpa.rmsnorm_matmul(x, g, w, 1e-6, out=y, variant=variant)
+        torch.cuda.synchronize()
+        assert torch.all(torch.isfinite(y.float())), variant
+        assert torch.all(buf[:guard] == 7.0) and torch.all(buf[-guard:] == -7.0), variant
+
+
+def test_unaligned_pointers_take_generic_and_match(require_gpu):
+    M, K, N = 6, 256, 264
+    inp = synth.make_inputs(synth.Workload("unaligned", "bf16", M, K, N, 1e-6, False, None), seed=3)
+    X = to_device(inp, "X")
+    big = torch.empty(M * K + 1, dtype=torch.bfloat16, device="cuda")
+    xs = big[1:].view(M, K)  # 2-byte offset: not 16-byte aligned
+    xs.copy_(X)
+    y = from_device(run_gpu(inp, 1e-6, x=xs))
+    assert_within_tol(y, run_oracle(inp, 1e-6), 1e-2, "unaligned")
+
+
+def test_workspace_reuse_and_streams(require_gpu):
+    """Arrival counters reset themselves: repeated calls give identical bits,
+    also on a second stream with its own workspace."""
+    x, g, w = _tensors(16, 4096, 6144)
+    y0 = tpa.rmsnorm_matmul(x, g, w, 1e-6, variant="decode", splits=16)
+    ys = [tpa.rmsnorm_matmul(x, g, w, 1e-6, variant="decode", splits=16) for _ in range(5)]
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        ys.append(tpa.rmsnorm_matmul(x, g, w, 1e-6, variant="decode", splits=16))
+    torch.cuda.synchronize()
+    for y in ys:
+        assert torch.equal(y.view(torch.int16), y0.view(torch.int16))
+
+
+def test_errors_raise(require_gpu):
+    x, g, w = _tensors(4, 64, 32)
+    with pytest.raises(tpa.RmmError):
+        tpa.rmsnorm_matmul(x, g, w, -1.0)
+    with pytest.raises(tpa.RmmError):
+        tpa.rmsnorm_matmul(x, g, w, 1e-6, variant="decode", splits=99)
+    with pytest.raises(tpa.RmmError):  # output overlapping the input X
+        tpa.rmsnorm_matmul(x, g, w, 1e-6, out=x.view(-1)[:128].view(4, 32))

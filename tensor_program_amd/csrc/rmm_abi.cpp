@@ -27,10 +27,15 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
   return a0 < b0 + bn && b0 < a0 + an;
 }
 
-// Decode: few rows; the split count aims at ~3 workgroups per CU (256 CUs).
+// Decode: few rows.  The split count aims at ~1.5 workgroups per CU (256 CUs):
+// more splits add partial-sum traffic and lengthen the combine that the last
+// arriving workgroup of each tile does alone.
 constexpr int64_t kDecodeMaxM = 32;
 constexpr int64_t kDecodeMaxMGated = 16;
-constexpr int64_t kTargetWorkgroups = 768;
+constexpr int64_t kTargetWorkgroups = 384;
+#ifndef RMM_DECODE_NBW
+#define RMM_DECODE_NBW 1  // 32-deep k-blocks per wave per pipeline stage
+#endif
 
 int auto_decode_splits(int64_t N, int64_t K) {
   const int64_t tiles = (N + 127) / 128;
@@ -56,7 +61,9 @@ rmm_status plan_shape(int64_t M, int64_t N, int64_t K, rmm_dtype dtype, int gate
     return RMM_OK;
   }
   const bool fast_layout = dtype == RMM_DTYPE_BF16 && K % 8 == 0 && N % 8 == 0 && aligned;
-  const bool decode_ok = fast_layout && M <= (gated ? kDecodeMaxMGated : kDecodeMaxM);
+  // The decode variant addresses X and W with 32-bit buffer offsets.
+  const bool decode_ok = fast_layout && M <= (gated ? kDecodeMaxMGated : kDecodeMaxM) &&
+                         K * N * 2 <= (int64_t)INT32_MAX && M * K * 2 <= (int64_t)INT32_MAX;
   rmm_variant v = variant;
   if (v == RMM_VARIANT_AUTO) v = decode_ok ? RMM_VARIANT_DECODE : RMM_VARIANT_GENERIC;
   if (v == RMM_VARIANT_DECODE && !decode_ok) return RMM_ERR_VARIANT;
@@ -69,7 +76,8 @@ rmm_status plan_shape(int64_t M, int64_t N, int64_t K, rmm_dtype dtype, int gate
     if (s == 0) s = have_ws ? auto_decode_splits(N, K) : 1;
     if (s > (K + 127) / 128) return RMM_ERR_VARIANT;
     if (s > 1 && !have_ws) return RMM_ERR_WORKSPACE;  // a forced split count needs one
-    rmm_decode_plan(M, N, K, gated, s, 2, &out->dec);
+    rmm_decode_plan(M, N, K, gated, s, RMM_DECODE_NBW, &out->dec);
+    if (out->dec.ws_bytes > (size_t)INT32_MAX) return RMM_ERR_VARIANT;  // 32-bit offsets
     out->splits = out->dec.splits;
     out->ws_bytes = out->dec.ws_bytes;
   }

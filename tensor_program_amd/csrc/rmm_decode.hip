@@ -24,9 +24,14 @@
 //     the workgroup stores its fp32 partial to the workspace, and the last
 //     workgroup to arrive at a tile (arrival counter) adds the partials and
 //     runs the epilogue  Y = acc / RMS  (gated: silu(acc1/RMS) * acc3/RMS).
-//   * the block index is remapped so that all chunks of a tile run on the
-//     same XCD (workgroups are dispatched round-robin over the 8 XCDs), so
-//     the partials of a tile meet in one L2.
+//   * the partials cross XCDs (each XCD has its own L2), so they are written
+//     and read with device-scope coherent accesses, ordered by waiting for the
+//     stores' acknowledgements before the arrival count.  A device-wide fence
+//     per workgroup (an L2 write-back plus invalidate on gfx950) would also be
+//     correct but costs several microseconds per call at this size.
+//   * the block index is remapped so that all chunks of a tile are dispatched
+//     to the same XCD (workgroups go round-robin over the 8 XCDs); this only
+//     affects locality, never correctness.
 #include "rmm_device.h"
 
 namespace rmm {
@@ -37,7 +42,7 @@ constexpr int DEC_KWG = 128;   // k per workgroup step (4 waves x 32)
 
 template <int MB, int NW>
 struct DecodeSmem {
-  float red[4][NW * MB * 32][64];  // per-wave accumulators, [wave][element][lane]
+  alignas(16) float red[4][NW * MB * 32][64];  // per-wave accumulators, [wave][element][lane]
   float ss[4][MB * 16];
   float inv[MB * 16];
   int last;
@@ -56,6 +61,88 @@ __device__ __forceinline__ u32x4 column_of(const u32x4 (&rows)[8], int c) {
   return out;
 }
 
+// Registers of one pipeline stage: NBW k-blocks of W (and W3), X and g.
+template <int MB, int NBW, int NW>
+struct DecodeStage {
+  u32x4 w[NW][NBW][8];
+  u32x4 x[NBW][MB];
+  u32x4 g[NBW];
+};
+
+// Buffer resources (base, size) of the operands.  Loads go through them
+// with a 32-bit byte offset per lane; an offset past the end returns zeros
+// (hardware range check), which is how rows beyond K and M, and columns
+// beyond N, read as zero without a branch.
+struct DecodeSrc {
+  __amdgpu_buffer_rsrc_t w1, w3, x, g;
+};
+constexpr uint32_t kOutOfRange = 0x80000000u;  // > every buffer the variant accepts
+
+template <int MB, int NBW, int NW>
+__device__ __forceinline__ void decode_load(DecodeStage<MB, NBW, NW>& st, const DecodeSrc& src,
+                                            int M, int64_t N, int64_t K, int64_t k0,
+                                            int64_t k_hi, int64_t col, bool col_ok, int w, int q,
+                                            int p) {
+  const uint32_t row_bytes = (uint32_t)(N * 2);
+#pragma unroll
+  for (int i = 0; i < NBW; ++i) {
+    const int64_t krow = k0 + 32 * (w + 4 * i) + 8 * q;
+    const bool k_ok = krow < k_hi;  // K % 8 == 0: the 8 rows are all in or all out
+    const uint32_t wo = (k_ok && col_ok) ? (uint32_t)((krow * N + col) * 2) : kOutOfRange;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      st.w[0][i][j] = __builtin_amdgcn_raw_buffer_load_b128(src.w1, wo, j * row_bytes, 0);
+      if (NW == 2)
+        st.w[NW - 1][i][j] = __builtin_amdgcn_raw_buffer_load_b128(src.w3, wo, j * row_bytes, 0);
+    }
+    const uint32_t go = k_ok ? (uint32_t)(krow * 2) : kOutOfRange;
+    st.g[i] = __builtin_amdgcn_raw_buffer_load_b128(src.g, go, 0, 0);
+#pragma unroll
+    for (int b = 0; b < MB; ++b) {
+      const int row = 16 * b + p;
+      const uint32_t xo = (k_ok && row < M) ? (uint32_t)(((int64_t)row * K + krow) * 2) : kOutOfRange;
+      st.x[i][b] = __builtin_amdgcn_raw_buffer_load_b128(src.x, xo, 0, 0);
+    }
+  }
+}
+
+template <int MB, int NBW, int NW>
+__device__ __forceinline__ void decode_compute(const DecodeStage<MB, NBW, NW>& st,
+                                               floatx4 (&acc)[NW][MB][8], float (&ss)[MB]) {
+#pragma unroll
+  for (int i = 0; i < NBW; ++i) {
+    bf16x8 a[MB];
+#pragma unroll
+    for (int b = 0; b < MB; ++b) {
+      u32x4 av;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const float x0 = bf16_lo(st.x[i][b][d]), x1 = bf16_hi(st.x[i][b][d]);
+        const float g0 = bf16_lo(st.g[i][d]), g1 = bf16_hi(st.g[i][d]);
+        ss[b] += x0 * x0 + x1 * x1;
+        av[d] = pack_bf16x2(x0 * g0, x1 * g1);
+      }
+      a[b] = __builtin_bit_cast(bf16x8, av);
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+#pragma unroll
+      for (int wi = 0; wi < NW; ++wi) {
+        const bf16x8 bop = __builtin_bit_cast(bf16x8, column_of(st.w[wi][i], c));
+#pragma unroll
+        for (int b = 0; b < MB; ++b)
+          acc[wi][b][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[b], bop, acc[wi][b][c], 0, 0, 0);
+      }
+    }
+  }
+}
+
+// Workspace accesses of the split-K combine: 16-byte buffer loads/stores
+// with device (agent) scope coherence (the SC1 cache-policy bit), so the
+// partials written on one XCD are read correctly on any other without a
+// cache-wide write-back or invalidate.
+constexpr int kCoherentDevice = 16;  // SC1
+
 template <int MB, int NBW, bool GATED>
 __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ g, const bf16_t* __restrict__ W1,
@@ -64,6 +151,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(
     float* __restrict__ ssq_ws, float* __restrict__ part_ws) {
   constexpr int NW = GATED ? 2 : 1;
   constexpr int E = NW * MB * 32 * 64;  // accumulator floats per workgroup
+  constexpr int PER = E / DEC_THREADS;  // floats per thread in the combine (8 NW MB)
   __shared__ DecodeSmem<MB, NW> sm;
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, q = l >> 4, p = l & 15;
@@ -95,56 +183,25 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(
 #pragma unroll
   for (int b = 0; b < MB; ++b) ss[b] = 0.f;
 
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
-  for (int64_t k0 = k_lo; k0 < k_hi; k0 += (int64_t)DEC_KWG * NBW) {
-    u32x4 wv[NW][NBW][8];
-    u32x4 xv[NBW][MB];
-    u32x4 gv[NBW];
-    // Issue every load of this step before any arithmetic.
-#pragma unroll
-    for (int i = 0; i < NBW; ++i) {
-      const int64_t krow = k0 + 32 * (w + 4 * i) + 8 * q;
-      const bool k_ok = krow < k_hi;  // K % 8 == 0: the 8 rows are all in or all out
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int64_t off = (krow + j) * N + col;
-        wv[0][i][j] = (k_ok && col_ok) ? *(const u32x4*)(W1 + off) : zero4;
-        if (GATED) wv[NW - 1][i][j] = (k_ok && col_ok) ? *(const u32x4*)(W3 + off) : zero4;
-      }
-      gv[i] = k_ok ? *(const u32x4*)(g + krow) : zero4;
-#pragma unroll
-      for (int b = 0; b < MB; ++b) {
-        const int row = 16 * b + p;
-        xv[i][b] = (k_ok && row < M) ? *(const u32x4*)(X + (int64_t)row * K + krow) : zero4;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < NBW; ++i) {
-      bf16x8 a[MB];
-#pragma unroll
-      for (int b = 0; b < MB; ++b) {
-        u32x4 av;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const float x0 = bf16_lo(xv[i][b][d]), x1 = bf16_hi(xv[i][b][d]);
-          const float g0 = bf16_lo(gv[i][d]), g1 = bf16_hi(gv[i][d]);
-          ss[b] += x0 * x0 + x1 * x1;
-          av[d] = pack_bf16x2(x0 * g0, x1 * g1);
-        }
-        a[b] = __builtin_bit_cast(bf16x8, av);
-      }
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-#pragma unroll
-        for (int wi = 0; wi < NW; ++wi) {
-          const bf16x8 bop = __builtin_bit_cast(bf16x8, column_of(wv[wi][i], c));
-#pragma unroll
-          for (int b = 0; b < MB; ++b)
-            acc[wi][b][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[b], bop, acc[wi][b][c], 0, 0, 0);
-        }
-      }
-    }
+  // Two register stages: the loads of step s+1 are in flight while step s
+  // is multiplied.
+  const int64_t step = (int64_t)DEC_KWG * NBW;
+  const int nsteps = (int)((k_hi - k_lo + step - 1) / step);
+  DecodeSrc src;
+  src.w1 = __builtin_amdgcn_make_buffer_rsrc((void*)W1, 0, (int)(K * N * 2), 0x00020000);
+  src.w3 = __builtin_amdgcn_make_buffer_rsrc((void*)(GATED ? W3 : W1), 0, (int)(K * N * 2), 0x00020000);
+  src.x = __builtin_amdgcn_make_buffer_rsrc((void*)X, 0, (int)((int64_t)M * K * 2), 0x00020000);
+  src.g = __builtin_amdgcn_make_buffer_rsrc((void*)g, 0, (int)(K * 2), 0x00020000);
+  DecodeStage<MB, NBW, NW> sa, sb;
+  decode_load(sa, src, M, N, K, k_lo, k_hi, col, col_ok, w, q, p);
+  int s = 0;
+  for (; s + 2 <= nsteps; s += 2) {
+    decode_load(sb, src, M, N, K, k_lo + (s + 1) * step, k_hi, col, col_ok, w, q, p);
+    decode_compute(sa, acc, ss);
+    if (s + 2 < nsteps) decode_load(sa, src, M, N, K, k_lo + (s + 2) * step, k_hi, col, col_ok, w, q, p);
+    decode_compute(sb, acc, ss);
   }
+  if (s < nsteps) decode_compute(sa, acc, ss);
 
   // Row sums of squares: lanes p, p+16, p+32, p+48 hold the four k-groups.
 #pragma unroll
@@ -164,46 +221,75 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(
         for (int r = 0; r < 4; ++r) sm.red[w][(wi * MB + b) * 32 + c * 4 + r][l] = acc[wi][b][c][r];
   __syncthreads();
 
-  // Workgroup sum of the four waves; thread owns flat indices tid + 256 t.
-  float v[E / DEC_THREADS];
+  // Workgroup sum of the four waves; thread owns flat floats [PER*tid, PER*tid + PER).
   float* red0 = &sm.red[0][0][0];
+  floatx4 v[PER / 4];
 #pragma unroll
-  for (int t = 0; t < E / DEC_THREADS; ++t) {
-    const int f = tid + DEC_THREADS * t;
-    v[t] = (&sm.red[0][0][0])[f] + (&sm.red[1][0][0])[f] + (&sm.red[2][0][0])[f] +
-           (&sm.red[3][0][0])[f];
+  for (int t = 0; t < PER / 4; ++t) {
+    const int f = PER * tid + 4 * t;
+    v[t] = *(const floatx4*)(&sm.red[0][0][0] + f) + *(const floatx4*)(&sm.red[1][0][0] + f) +
+           *(const floatx4*)(&sm.red[2][0][0] + f) + *(const floatx4*)(&sm.red[3][0][0] + f);
   }
   float ssw = 0.f;
   if (tid < MB * 16) ssw = sm.ss[0][tid] + sm.ss[1][tid] + sm.ss[2][tid] + sm.ss[3][tid];
 
   if (S > 1) {
     const int64_t slot = (int64_t)split * tiles + tile;
-    float* part = part_ws + slot * E;
+    const int64_t nslots = (int64_t)S * tiles;
+    const __amdgpu_buffer_rsrc_t prs =
+        __builtin_amdgcn_make_buffer_rsrc(part_ws, 0, (int)(nslots * E * 4), 0x00020000);
+    // Partials go out with device-scope coherence; waiting for every store's
+    // acknowledgement before the arrival count makes them visible to
+    // whichever workgroup arrives last.
 #pragma unroll
-    for (int t = 0; t < E / DEC_THREADS; ++t) part[tid + DEC_THREADS * t] = v[t];
-    if (tid < MB * 16) ssq_ws[slot * (MB * 16) + tid] = ssw;
-    // Release the partial, count arrivals; the last arrival combines.
-    __threadfence();
+    for (int t = 0; t < PER / 4; ++t)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v[t]), prs,
+                                             (int)((slot * E + PER * tid + 4 * t) * 4), 0,
+                                             kCoherentDevice);
+    if (tid < MB * 16)
+      __hip_atomic_store(&ssq_ws[slot * (MB * 16) + tid], ssw, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (tid == 0) sm.last = (atomicAdd(&cnt[tile], 1u) == (unsigned)(S - 1));
+    if (tid == 0)
+      sm.last = (__hip_atomic_fetch_add(&cnt[tile], 1u, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(S - 1));
     __syncthreads();
     if (!sm.last) return;
-    __threadfence();
+    // Last arrival: add the S partials, four splits' loads in flight at a time.
 #pragma unroll
-    for (int t = 0; t < E / DEC_THREADS; ++t) v[t] = 0.f;
+    for (int t = 0; t < PER / 4; ++t) v[t] = floatx4{0.f, 0.f, 0.f, 0.f};
     ssw = 0.f;
-    for (int s = 0; s < S; ++s) {
-      const int64_t sl = (int64_t)s * tiles + tile;
-      const float* ps = part_ws + sl * E;
+    for (int s0 = 0; s0 < S; s0 += 4) {
+      u32x4 buf[4][PER / 4];
+      float sbuf[4];
 #pragma unroll
-      for (int t = 0; t < E / DEC_THREADS; ++t) v[t] += ps[tid + DEC_THREADS * t];
-      if (tid < MB * 16) ssw += ssq_ws[sl * (MB * 16) + tid];
+      for (int u = 0; u < 4; ++u) {
+        const int64_t sl = (int64_t)(s0 + u) * tiles + tile;
+        const bool ok = s0 + u < S;
+#pragma unroll
+        for (int t = 0; t < PER / 4; ++t)
+          buf[u][t] = ok ? __builtin_amdgcn_raw_buffer_load_b128(
+                               prs, (int)((sl * E + PER * tid + 4 * t) * 4), 0, kCoherentDevice)
+                         : u32x4{0u, 0u, 0u, 0u};
+        sbuf[u] = (ok && tid < MB * 16)
+                      ? __hip_atomic_load(&ssq_ws[sl * (MB * 16) + tid], __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT)
+                      : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+#pragma unroll
+        for (int t = 0; t < PER / 4; ++t) v[t] += __builtin_bit_cast(floatx4, buf[u][t]);
+        ssw += sbuf[u];
+      }
     }
-    if (tid == 0) cnt[tile] = 0u;  // leave the workspace zeroed for the next call
+    // Leave the workspace zeroed for the next call (all arrivals are in).
+    if (tid == 0) __hip_atomic_store(&cnt[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();  // everyone is done reading sm.red before it is overwritten
 #pragma unroll
-  for (int t = 0; t < E / DEC_THREADS; ++t) red0[tid + DEC_THREADS * t] = v[t];
+  for (int t = 0; t < PER / 4; ++t) *(floatx4*)(red0 + PER * tid + 4 * t) = v[t];
   if (tid < MB * 16) sm.inv[tid] = inv_rms(ssw, K, eps);
   __syncthreads();
 

@@ -112,7 +112,7 @@ def test_status_strings(lib):
 
 def test_variant_selection():
     import torch
-    assert tpa.plan(16, 6144, 4096)[1:] == ("decode", 16)
+    assert tpa.plan(16, 6144, 4096)[1:] == ("decode", 8)
     assert tpa.plan(16, 6144, 4096, with_workspace=False)[1:] == ("decode", 1)
     assert tpa.plan(64, 14336, 4096, gated=True)[1] == "generic"
     assert tpa.plan(8, 1024, 1024, dtype=torch.float32)[1] == "generic"

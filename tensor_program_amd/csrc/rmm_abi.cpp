@@ -17,6 +17,7 @@ struct Plan {
   int splits;
   size_t ws_bytes;
   DecodePlan dec;
+  PrefillPlan pre;
 };
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -64,10 +65,14 @@ rmm_status plan_shape(int64_t M, int64_t N, int64_t K, rmm_dtype dtype, int gate
   // The decode variant addresses X and W with 32-bit buffer offsets.
   const bool decode_ok = fast_layout && M <= (gated ? kDecodeMaxMGated : kDecodeMaxM) &&
                          K * N * 2 <= (int64_t)INT32_MAX && M * K * 2 <= (int64_t)INT32_MAX;
+  // The fast variants address X and W with 32-bit buffer offsets.
+  const bool prefill_ok = fast_layout && !gated && K * N * 2 <= (int64_t)INT32_MAX &&
+                          M * K * 2 <= (int64_t)INT32_MAX;
   rmm_variant v = variant;
-  if (v == RMM_VARIANT_AUTO) v = decode_ok ? RMM_VARIANT_DECODE : RMM_VARIANT_GENERIC;
+  if (v == RMM_VARIANT_AUTO)
+    v = decode_ok ? RMM_VARIANT_DECODE : (prefill_ok ? RMM_VARIANT_PREFILL : RMM_VARIANT_GENERIC);
   if (v == RMM_VARIANT_DECODE && !decode_ok) return RMM_ERR_VARIANT;
-  if (v == RMM_VARIANT_PREFILL) return RMM_ERR_VARIANT;  // not built yet
+  if (v == RMM_VARIANT_PREFILL && !prefill_ok) return RMM_ERR_VARIANT;
   out->variant = v;
   out->splits = 1;
   out->ws_bytes = 0;
@@ -80,6 +85,8 @@ rmm_status plan_shape(int64_t M, int64_t N, int64_t K, rmm_dtype dtype, int gate
     if (out->dec.ws_bytes > (size_t)INT32_MAX) return RMM_ERR_VARIANT;  // 32-bit offsets
     out->splits = out->dec.splits;
     out->ws_bytes = out->dec.ws_bytes;
+  } else if (v == RMM_VARIANT_PREFILL) {
+    rmm_prefill_plan(M, N, K, &out->pre);
   }
   return RMM_OK;
 }
@@ -136,6 +143,9 @@ rmm_status run(const void* X, const void* g, const void* W1, const void* W3, voi
       break;
     case RMM_VARIANT_DECODE:
       err = rmm_launch_decode(a, plan.dec, plan.dec.splits > 1 ? ws : nullptr);
+      break;
+    case RMM_VARIANT_PREFILL:
+      err = rmm_launch_prefill(a, plan.pre);
       break;
     default:
       return RMM_ERR_VARIANT;

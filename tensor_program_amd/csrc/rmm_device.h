@@ -75,3 +75,11 @@ struct DecodePlan {
 void rmm_decode_plan(int64_t M, int64_t N, int64_t K, int gated, int splits, int nbw,
                      DecodePlan* p);
 hipError_t rmm_launch_decode(const RmmArgs& a, const DecodePlan& p, void* ws);
+
+struct PrefillPlan {
+  int tiles_m, tiles_n;  // 256 x 256 output tiles
+  int group_m;           // tile-rows walked together (L2 reuse)
+  int xcd_remap;         // contiguous tile ranges per XCD
+};
+void rmm_prefill_plan(int64_t M, int64_t N, int64_t K, PrefillPlan* p);
+hipError_t rmm_launch_prefill(const RmmArgs& a, const PrefillPlan& p);

@@ -116,6 +116,12 @@ def test_variant_selection():
     assert tpa.plan(16, 6144, 4096, with_workspace=False)[1:] == ("decode", 1)
     assert tpa.plan(64, 14336, 4096, gated=True)[1] == "generic"
     assert tpa.plan(8, 1024, 1024, dtype=torch.float32)[1] == "generic"
+    assert tpa.plan(4096, 4096, 4096)[1:] == ("prefill", 1)
+    assert tpa.plan(8192, 28672, 8192)[1] == "prefill"
+    assert tpa.plan(33, 520, 1000)[1] == "prefill"
+    assert tpa.plan(4096, 4096, 4095)[1] == "generic"   # K % 8 != 0
+    assert tpa.plan(4096, 4096, 4096, variant="prefill", dtype=torch.float32)[0] == VARIANT
+    assert tpa.plan(128, 256, 64, gated=True, variant="prefill")[0] == VARIANT
     assert tpa.plan(16, 6144, 4096, variant="decode", splits=3)[1:] == ("decode", 3)
     # split counts that do not divide K evenly are rounded to 128-deep chunks
     st, v, s = tpa.plan(17, 520, 1000, variant="decode", splits=4)

@@ -5,7 +5,7 @@
 #include <stdint.h>
 #include <string.h>
 
-#include "../../include/rmm.h"
+#include "rmm.h"
 #include "rmm_device.h"
 
 namespace {

@@ -25,9 +25,13 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
   __bf16 b = (__bf16)f;
   return __builtin_bit_cast(bf16_t, b);
 }
-// Two fp32 -> packed bf16 pair (lo, hi), round to nearest even.
+// Two fp32 -> packed bf16 pair (lo, hi), round to nearest even (one
+// v_cvt_pk_bf16_f32).
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  const floatx2 f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
 
 // Load/store of one element of the storage type as fp32.

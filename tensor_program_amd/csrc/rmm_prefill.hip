@@ -4,114 +4,226 @@
 // pieces of the fused form (Mirage paper review, "核心公式": the abstract
 // expression E(O) = sum(k, div(mul(I1,I2), I3)) with the k-independent I3
 // taken outside the sum):
-//   * while a tile of X is staged into LDS it is multiplied by g in fp32 and
-//     rounded once to bf16 -- the A operand is (X g), so g never has to be
-//     applied to W;
-//   * the same registers give the row sums of squares of raw X, kept in fp32;
+//   * while a tile of X is staged into LDS it is multiplied by g and rounded
+//     once to bf16 -- the A operand is (X g), so g never touches W;
+//   * the same registers give the row sums of squares of raw X, in fp32;
 //   * after the k-loop the accumulators are scaled by 1/sqrt(ss/K + eps) and
 //     stored: the normalised X is never written anywhere.
 //
-// Tiling: workgroup tile 256 (M) x 256 (N) x 64 (K), 4 waves in a 2x2 grid,
-// each wave owning a 128x128 block = 4x4 v_mfma_f32_32x32x16_bf16 tiles
-// (256 fp32 accumulators per lane).  Two LDS stages of (A 32 KB + B 32 KB);
-// the global loads of step k+1 are issued before the MFMAs of step k.
+// Tiling: workgroup tile 256 (M) x 256 (N) x 64 (K), 8 waves in a 2x4 grid,
+// each wave owning a 128x64 block = 4x2 v_mfma_f32_32x32x16_bf16 tiles (128
+// fp32 accumulators per lane).  Two waves per SIMD let one wave's MFMAs run
+// while the other waits on LDS, memory or the barrier.
 //
-// W is K x N with n contiguous, but an MFMA operand wants 8 consecutive k per
-// lane.  Each thread loads an 8 (k) x 8 (n) block of W with eight 16-byte
-// loads (coalesced: 32 lanes cover a 512-byte row segment), transposes it in
-// registers and writes eight k-contiguous 16-byte chunks to LDS.
-//
-// LDS layout: both tiles are [256 rows][64 k] bf16 with 128-byte rows; the
-// 16-byte chunk kc of row r is stored at chunk kc ^ ((r ^ r>>3) & 7).  Eight
-// consecutive lanes then hit eight different 16-byte bank groups both when
-// MFMA fragments are read (consecutive rows, same chunk) and when staging
-// writes land (A: same row, consecutive chunks; B: rows 8 apart, same chunk).
+// Operand paths:
+//   * W (B operand) goes straight from memory into LDS (buffer loads with
+//     the LDS-direct bit), one k-step ahead, as the raw K x N block with n
+//     contiguous.  MFMA wants 8 consecutive k per lane; ds_read_b64_tr_b16
+//     (gfx950's transposing LDS read) delivers exactly that: each 16-lane
+//     group reads 4 rows x 16 columns and lane i receives column i.
+//   * X (A operand) is loaded into registers two k-steps ahead, scaled by g
+//     and written to LDS with 144-byte rows (128 + 16 padding), which makes
+//     both the staging writes and the fragment reads bank-conflict-free.
+// W tile layout: [64 k][256 n] bf16, 512-byte rows; 16-byte chunk c of row k
+// sits at chunk c ^ 2(k & 3), so the 4 rows x 32 bytes that one 16-lane group
+// reads land on 8 different bank groups.
 #include "rmm_device.h"
 
 namespace rmm {
 
-constexpr int PF_BM = 256, PF_BN = 256, PF_BK = 64, PF_THREADS = 256;
-constexpr int PF_TILE_BYTES = 256 * 128;  // one [256][64] bf16 tile
+constexpr int PF_BM = 256, PF_BN = 256, PF_BK = 64, PF_THREADS = 512;
+constexpr int PF_A_ROW = 144;                   // 64 bf16 + 16 bytes of padding
+constexpr int PF_A_BYTES = PF_BM * PF_A_ROW;    // one A stage
+constexpr int PF_B_BYTES = PF_BK * PF_BN * 2;   // one W stage, 32 KB
 constexpr uint32_t kPfOutOfRange = 0x80000000u;
 
-__device__ __forceinline__ int pf_lds_off(int r, int kc) {
-  return r * 128 + ((kc ^ ((r ^ (r >> 3)) & 7)) << 4);
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2, v); }
+
+// Byte offset of element n (a multiple of 4) of row k in a W stage.
+__device__ __forceinline__ int pf_b_off(int k, int n) {
+  return k * 512 + (((n >> 3) ^ (2 * (k & 3))) << 4) + ((n & 7) << 1);
 }
 
-// Column c (0..7) of an 8x8 bf16 block held as 8 rows of 4 dwords.
-__device__ __forceinline__ u32x4 pf_column(const u32x4 (&rows)[8], int c) {
-  u32x4 out;
-  const int e = c >> 1;
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const uint32_t lo = rows[2 * d][e], hi = rows[2 * d + 1][e];
-    out[d] = (c & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-  }
-  return out;
-}
-
-struct PfStage {
-  u32x4 a[8];  // X rows (t>>3) + 32 i, chunk t&7
-  u32x4 g;     // g for chunk t&7
-  u32x4 b[8];  // W rows 8 (t>>5) + j, columns 8 (t&31) .. +7
+// X of one k-step for this thread: rows (t>>3) + 64 i, chunk t&7, and g.
+struct PfA {
+  u32x4 a[4];
+  u32x4 g;
 };
 
-__device__ __forceinline__ void pf_load(PfStage& st, __amdgpu_buffer_rsrc_t xr,
-                                        __amdgpu_buffer_rsrc_t gr, __amdgpu_buffer_rsrc_t wr,
-                                        int64_t m0, int64_t n0, int64_t k0, int64_t M, int64_t N,
-                                        int64_t K, int tid) {
-  const int ca = tid & 7;
-  const int64_t ka = k0 + 8 * ca;
+__device__ __forceinline__ void pf_load_a(PfA& st, __amdgpu_buffer_rsrc_t xr,
+                                          __amdgpu_buffer_rsrc_t gr, int64_t m0, int64_t k0,
+                                          int64_t M, int64_t K, int tid) {
+  const int64_t ka = k0 + 8 * (tid & 7);
   const bool ka_ok = ka < K;  // K % 8 == 0: a chunk is all in or all out
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t m = m0 + (tid >> 3) + 32 * i;
+  for (int i = 0; i < 4; ++i) {
+    const int64_t m = m0 + (tid >> 3) + 64 * i;
     const uint32_t off = (ka_ok && m < M) ? (uint32_t)((m * K + ka) * 2) : kPfOutOfRange;
     st.a[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
   }
   st.g = __builtin_amdgcn_raw_buffer_load_b128(gr, ka_ok ? (uint32_t)(ka * 2) : kPfOutOfRange, 0, 0);
-  const int64_t kb = k0 + 8 * (tid >> 5);
-  const int64_t nb = n0 + 8 * (tid & 31);
-  const uint32_t row_bytes = (uint32_t)(N * 2);
-  const uint32_t wo = (kb < K && nb < N) ? (uint32_t)((kb * N + nb) * 2) : kPfOutOfRange;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) st.b[j] = __builtin_amdgcn_raw_buffer_load_b128(wr, wo, j * row_bytes, 0);
 }
 
-// Stage registers -> LDS (A: X*g rounded to bf16; B: transposed W), and the
-// row sums of squares of raw X.
-__device__ __forceinline__ void pf_store(const PfStage& st, char* a_lds, char* b_lds, float (&ss)[8],
-                                         int tid) {
-  const int ca = tid & 7;
-  float gf[8];
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource (stride 0, 32-bit data format) for [base, base+bytes).
+__device__ __forceinline__ i32x4 pf_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// One 16-byte-per-lane load straight into LDS: lane l's data lands at
+// lds_addr + 16 l.  Issued as inline asm so that the compiler does not
+// serialise it against the other loads in flight; the k-loop waits for it
+// explicitly (vmcnt) before the barrier that publishes the stage.
+__device__ __forceinline__ void pf_lds_load16(uint32_t lds_addr, uint32_t voff, i32x4 rsrc) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(rsrc)
+               : "memory");
+}
+
+// W block of step k0 into an LDS stage: wave w fills the four 1-KB blocks
+// 4w .. 4w+3 (two k-rows each); lane l of a block lands at byte 16 l of the
+// block, so it fetches the logical chunk the swizzle maps there.  The
+// resource starts at row k0, so rows past K fall outside it and read as
+// zeros; columns past N are given an out-of-range offset.
+struct PfDma {
+  uint32_t off[4];  // per-lane byte offsets from row k0 (step independent)
+};
+
+__device__ __forceinline__ void pf_dma_setup(PfDma& d, int64_t n0, int64_t N, int w, int l) {
 #pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    gf[2 * d] = bf16_lo(st.g[d]);
-    gf[2 * d + 1] = bf16_hi(st.g[d]);
+  for (int q = 0; q < 4; ++q) {
+    const int blk = 4 * w + q;
+    const int kl = 2 * blk + (l >> 5);
+    const int c = (l & 31) ^ (2 * (kl & 3));
+    const int64_t nn = n0 + 8 * c;
+    d.off[q] = nn < N ? (uint32_t)((kl * N + nn) * 2) : kPfOutOfRange;
   }
+}
+
+__device__ __forceinline__ void pf_dma_b(uint32_t b_lds, const PfDma& d, const bf16_t* W,
+                                         int64_t k0, int64_t N, int64_t K, int w) {
+  const int64_t rows = K - k0 > 0 ? K - k0 : 0;
+  const i32x4 rsrc = pf_rsrc(W + k0 * N, (uint32_t)(rows * N * 2));
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int q = 0; q < 4; ++q) pf_lds_load16(b_lds + (4 * w + q) * 1024, d.off[q], rsrc);
+}
+
+// Rows i0, i0+1 of a register stage -> A stage: X*g, each product formed
+// exactly in fp32 by a bf16 dot2 with the other lane of g zeroed, then
+// rounded once to bf16; the same dot2 unit accumulates the row sums of
+// squares of raw X.
+__device__ __forceinline__ void pf_store_a(const PfA& st, char* a_lds, float (&ss)[4], int tid,
+                                           int i0) {
+#pragma unroll
+  for (int i = i0; i < i0 + 2; ++i) {
     u32x4 v;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      const float x0 = bf16_lo(st.a[i][d]), x1 = bf16_hi(st.a[i][d]);
-      ss[i] += x0 * x0 + x1 * x1;
-      v[d] = pack_bf16x2(x0 * gf[2 * d], x1 * gf[2 * d + 1]);
+      const bf16x2 x = as_bf16x2(st.a[i][d]);
+      v[d] = pack_bf16x2(__builtin_amdgcn_fdot2_f32_bf16(x, as_bf16x2(st.g[d] & 0xffffu), 0.0f, false),
+                         __builtin_amdgcn_fdot2_f32_bf16(x, as_bf16x2(st.g[d] & 0xffff0000u), 0.0f, false));
+      ss[i] = __builtin_amdgcn_fdot2_f32_bf16(x, x, ss[i], false);
     }
-    *(u32x4*)(a_lds + pf_lds_off((tid >> 3) + 32 * i, ca)) = v;
+    *(u32x4*)(a_lds + ((tid >> 3) + 64 * i) * PF_A_ROW + 16 * (tid & 7)) = v;
   }
-  const int kc = tid >> 5, nc = 8 * (tid & 31);
+}
+
+// MFMA operand fragments of one 16-deep sub-step of the 128x64 wave tile.
+struct PfFrag {
+  bf16x8 a[4], b[2];
+};
+
+// a_base: this lane's A row (wm*128 + lane%32) and chunk (lane/32) in a stage;
+// b_off0/1: this lane's transpose-read addresses for B fragments j = 0, 1.
+__device__ __forceinline__ void pf_read_frags(PfFrag& f, const char* a_lds, const lds_char* b_lds,
+                                              int a_base, int b_off0, int b_off1, int s) {
 #pragma unroll
-  for (int c = 0; c < 8; ++c) *(u32x4*)(b_lds + pf_lds_off(nc + c, kc)) = pf_column(st.b, c);
+  for (int i = 0; i < 4; ++i)
+    f.a[i] = *(const bf16x8*)(a_lds + a_base + 32 * i * PF_A_ROW + 32 * s);
+  const int bo[2] = {b_off0, b_off1};
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const u32x2 lo = __builtin_bit_cast(
+        u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(b_lds + bo[j] + 16 * s * 512)));
+    const u32x2 hi = __builtin_bit_cast(
+        u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(b_lds + bo[j] + (16 * s + 4) * 512)));
+    const u32x4 v = {lo[0], lo[1], hi[0], hi[1]};
+    f.b[j] = __builtin_bit_cast(bf16x8, v);
+  }
+}
+
+__device__ __forceinline__ void pf_mfma(const PfFrag& f, floatx16 (&acc)[4][2]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+}
+
+// s_waitcnt with only the vector-memory counter limited (gfx9 encoding:
+// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14).
+#define PF_WAIT_VMCNT(n) \
+  __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
+
+// One k-step: multiply the stage (a_cur, b_cur) while X of the next step
+// (st) is scaled into a_nxt.  Fragments of sub-step s+1 are read while the
+// MFMAs of sub-step s run; the staging is fenced behind the first two
+// sub-steps.
+__device__ __forceinline__ void pf_step(const char* a_cur, const lds_char* b_cur, char* a_nxt,
+                                        const PfA& st, floatx16 (&acc)[4][2], float (&ss)[4],
+                                        int a_base, int b0, int b1, int tid) {
+  PfFrag fa, fb;
+  pf_read_frags(fa, a_cur, b_cur, a_base, b0, b1, 0);
+  pf_read_frags(fb, a_cur, b_cur, a_base, b0, b1, 1);
+  pf_mfma(fa, acc);
+  pf_read_frags(fa, a_cur, b_cur, a_base, b0, b1, 2);
+  pf_mfma(fb, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  pf_store_a(st, a_nxt, ss, tid, 0);
+  pf_read_frags(fb, a_cur, b_cur, a_base, b0, b1, 3);
+  pf_mfma(fa, acc);
+  pf_store_a(st, a_nxt, ss, tid, 2);
+  pf_mfma(fb, acc);
+}
+
+__device__ __forceinline__ void pf_step_last(const char* a_cur, const lds_char* b_cur,
+                                             floatx16 (&acc)[4][2], int a_base, int b0, int b1) {
+  PfFrag fa, fb;
+  pf_read_frags(fa, a_cur, b_cur, a_base, b0, b1, 0);
+  pf_read_frags(fb, a_cur, b_cur, a_base, b0, b1, 1);
+  pf_mfma(fa, acc);
+  pf_read_frags(fa, a_cur, b_cur, a_base, b0, b1, 2);
+  pf_mfma(fb, acc);
+  pf_read_frags(fb, a_cur, b_cur, a_base, b0, b1, 3);
+  pf_mfma(fa, acc);
+  pf_mfma(fb, acc);
 }
 
 template <bool GATED>
-__global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(
+__global__ __launch_bounds__(PF_THREADS, 2) void prefill_kernel(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ g, const bf16_t* __restrict__ W1,
     const bf16_t* __restrict__ W3, bf16_t* __restrict__ Y, float eps, int64_t M, int64_t N,
     int64_t K, int tiles_m, int tiles_n, int group_m, int xcd_remap) {
   static_assert(!GATED, "gated prefill tiles are not built");
-  __shared__ __attribute__((aligned(16))) char smem[2][2][PF_TILE_BYTES];  // [stage][A|B]
+  // Separate objects per stage, so the compiler can tell the W stage being
+  // filled by direct loads from the one being read.
+  __shared__ __attribute__((aligned(16))) char a_s0[PF_A_BYTES];
+  __shared__ __attribute__((aligned(16))) char a_s1[PF_A_BYTES];
+  __shared__ __attribute__((aligned(1024))) char b_s0[PF_B_BYTES];
+  __shared__ __attribute__((aligned(1024))) char b_s1[PF_B_BYTES];
   __shared__ float inv_s[PF_BM];
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
@@ -131,59 +243,80 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(
 
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc((void*)X, 0, (int)(M * K * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t gr = __builtin_amdgcn_make_buffer_rsrc((void*)g, 0, (int)(K * 2), 0x00020000);
-  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc((void*)W1, 0, (int)(K * N * 2), 0x00020000);
+  lds_char* b0s = (lds_char*)b_s0;
+  lds_char* b1s = (lds_char*)b_s1;
+  const uint32_t b0a = (uint32_t)(uintptr_t)b0s, b1a = (uint32_t)(uintptr_t)b1s;
+  PfDma dma;
+  pf_dma_setup(dma, n0, N, w, l);
 
-  floatx16 acc[4][4];
+  floatx16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-  float ss[8];
+  float ss[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) ss[i] = 0.f;
+  for (int i = 0; i < 4; ++i) ss[i] = 0.f;
 
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w >> 2, wn = w & 3;
+  const int a_base = (wm * 128 + (l & 31)) * PF_A_ROW + 16 * (l >> 5);
+  const int bG = l >> 4, bi = l & 15;
+  const int bk = 8 * (bG >> 1) + (bi >> 2);
+  const int bn = wn * 64 + 16 * (bG & 1) + 4 * (bi & 3);
+  const int bo0 = pf_b_off(bk, bn), bo1 = pf_b_off(bk, bn + 32);
   const int nk = (int)((K + PF_BK - 1) / PF_BK);
-  PfStage st;
-  pf_load(st, xr, gr, wr, m0, n0, 0, M, N, K, tid);
-  pf_store(st, smem[0][0], smem[0][1], ss, tid);
+
+  // Pipeline, with LDS stage kt&1 holding step kt at the top of iteration kt:
+  // W of step kt+1 streams into the other W stage, X of step kt+1 (in
+  // registers since the previous iteration) is scaled into the other A
+  // stage, X of step kt+2 is in flight, and step kt is multiplied.  Loads
+  // past the last step read zeros (buffer range check), so the loop body has
+  // no branches; it is unrolled by two so each register stage is static.
+  // The 5 X/g loads of a step are issued after its W transfers, so
+  // vmcnt <= 5 means those transfers have landed.
+  PfA sa, sb;
+  pf_dma_b(b0a, dma, W1, 0, N, K, w);
+  pf_load_a(sa, xr, gr, m0, 0, M, K, tid);
+  pf_load_a(sb, xr, gr, m0, PF_BK, M, K, tid);
+  pf_store_a(sa, a_s0, ss, tid, 0);
+  pf_store_a(sa, a_s0, ss, tid, 2);
+  PF_WAIT_VMCNT(0);
   __syncthreads();
 
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) pf_load(st, xr, gr, wr, m0, n0, (int64_t)(kt + 1) * PF_BK, M, N, K, tid);
-    const char* a_lds = smem[cur][0];
-    const char* b_lds = smem[cur][1];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int kc = 2 * s + (l >> 5);
-      bf16x8 af[4], bfr[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = *(const bf16x8*)(a_lds + pf_lds_off(wm * 128 + 32 * i + (l & 31), kc));
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bfr[j] = *(const bf16x8*)(b_lds + pf_lds_off(wn * 128 + 32 * j + (l & 31), kc));
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) pf_store(st, smem[cur ^ 1][0], smem[cur ^ 1][1], ss, tid);
+  int kt = 0;
+  for (; kt + 2 < nk; kt += 2) {
+    pf_dma_b(b1a, dma, W1, (int64_t)(kt + 1) * PF_BK, N, K, w);
+    pf_load_a(sa, xr, gr, m0, (int64_t)(kt + 2) * PF_BK, M, K, tid);
+    pf_step(a_s0, b0s, a_s1, sb, acc, ss, a_base, bo0, bo1, tid);
+    PF_WAIT_VMCNT(5);
+    __syncthreads();
+    pf_dma_b(b0a, dma, W1, (int64_t)(kt + 2) * PF_BK, N, K, w);
+    pf_load_a(sb, xr, gr, m0, (int64_t)(kt + 3) * PF_BK, M, K, tid);
+    pf_step(a_s1, b1s, a_s0, sa, acc, ss, a_base, bo0, bo1, tid);
+    PF_WAIT_VMCNT(5);
     __syncthreads();
   }
+  // Tail: stage 0 holds step kt; sb holds X of step kt+1 (if it exists).
+  if (kt + 1 < nk) {
+    pf_dma_b(b1a, dma, W1, (int64_t)(kt + 1) * PF_BK, N, K, w);
+    pf_step(a_s0, b0s, a_s1, sb, acc, ss, a_base, bo0, bo1, tid);
+    PF_WAIT_VMCNT(0);
+    __syncthreads();
+    pf_step_last(a_s1, b1s, acc, a_base, bo0, bo1);
+  } else {
+    pf_step_last(a_s0, b0s, acc, a_base, bo0, bo1);
+  }
 
-  // Row sums of squares: the 8 lanes tid&7 = 0..7 share rows (tid>>3) + 32 i.
+  // Row sums of squares: the 8 lanes tid&7 = 0..7 share rows (tid>>3) + 64 i.
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 4; ++i) {
     float v = ss[i];
     v += __shfl_xor(v, 1);
     v += __shfl_xor(v, 2);
     v += __shfl_xor(v, 4);
-    if ((tid & 7) == 0) inv_s[(tid >> 3) + 32 * i] = inv_rms(v, K, eps);
+    if ((tid & 7) == 0) inv_s[(tid >> 3) + 64 * i] = inv_rms(v, K, eps);
   }
   __syncthreads();
 
@@ -192,8 +325,8 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t n = n0 + wn * 128 + 32 * j + (l & 31);
+    for (int j = 0; j < 2; ++j) {
+      const int64_t n = n0 + wn * 64 + 32 * j + (l & 31);
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
 #pragma unroll

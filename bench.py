@@ -35,7 +35,7 @@ F32_VALU_PEAK_TFLOPS = 78.6    # fp32 FMA on the vector ALUs without packed math
 RIDGE = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
 ROTATE_BYTES = 1 << 30
 KERNEL_SOURCES = {"decode": "rmm_decode.hip", "generic": "rmm_generic.hip",
-                  "prefill": "rmm_prefill.hip"}
+                  "prefill": "rmm_prefill.hip", "stream": "rmm_stream.hip"}
 
 
 def log(msg):

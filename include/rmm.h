@@ -87,18 +87,23 @@ typedef enum {
 } rmm_status;
 
 /* Kernel variants.  AUTO picks by shape; the others force one (tests, bench).
+ * The fast variants need bf16, K % 8 == 0, N % 8 == 0, 16-byte aligned
+ * pointers, and X and each weight below 2 GiB.
  *   GENERIC : any shape, alignment and dtype; VALU fp32 products.
- *   DECODE  : bf16, M <= 64, K % 8 == 0, N % 8 == 0, 16-byte aligned
- *             pointers; streams W once with split-K across workgroups and
- *             bf16 matrix-core (MFMA) products.  Bandwidth-bound shapes.
- *   PREFILL : bf16, K % 8 == 0, N % 8 == 0, 16-byte aligned pointers;
- *             LDS-tiled MFMA GEMM with the row sum of squares fused into
- *             its k-loop.  Matrix-core-bound shapes.                        */
+ *   DECODE  : M <= 32 (gated: M <= 16); streams W once with split-K across
+ *             workgroups, bf16 matrix-core (MFMA) products, fp32 partials
+ *             combined by the last-arriving workgroup.  Bandwidth-bound.
+ *   PREFILL : not gated; LDS-tiled MFMA GEMM with the row sum of squares
+ *             fused into its k-loop.  Matrix-core-bound shapes.
+ *   STREAM  : M <= 64; each workgroup streams 64-column strips of W (W1 and
+ *             W3 when gated) over all of K through LDS, no split-K.
+ *             Bandwidth-bound shapes with enough columns.                  */
 typedef enum {
   RMM_VARIANT_AUTO = 0,
   RMM_VARIANT_GENERIC = 1,
   RMM_VARIANT_DECODE = 2,
-  RMM_VARIANT_PREFILL = 3
+  RMM_VARIANT_PREFILL = 3,
+  RMM_VARIANT_STREAM = 4
 } rmm_variant;
 
 /* Y = RMSNorm(X; g, eps) W  (see the header comment for the definition).

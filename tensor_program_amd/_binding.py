@@ -13,7 +13,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "librmm.so")
 
 DTYPE_F32, DTYPE_BF16 = 0, 1
-VARIANTS = {"auto": 0, "generic": 1, "decode": 2, "prefill": 3}
+VARIANTS = {"auto": 0, "generic": 1, "decode": 2, "prefill": 3, "stream": 4}
 VARIANT_NAMES = {v: k for k, v in VARIANTS.items()}
 STATUS_OK = 0
 

@@ -20,7 +20,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "librmm.so")
-SOURCES = ["rmm_abi.cpp", "rmm_generic.hip", "rmm_decode.hip", "rmm_prefill.hip"]
+SOURCES = ["rmm_abi.cpp", "rmm_generic.hip", "rmm_decode.hip", "rmm_prefill.hip",
+           "rmm_stream.hip"]
 ARCH = "gfx950"
 
 

@@ -34,6 +34,10 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
 constexpr int64_t kDecodeMaxM = 32;
 constexpr int64_t kDecodeMaxMGated = 16;
 constexpr int64_t kTargetWorkgroups = 384;
+// Stream: up to 64 rows; auto-selected for plain calls only when there are
+// enough 64-column strips to keep most CUs streaming.
+constexpr int64_t kStreamMaxM = 64;
+constexpr int64_t kStreamMinTiles = 192;
 #ifndef RMM_DECODE_NBW
 #define RMM_DECODE_NBW 1  // 32-deep k-blocks per wave per pipeline stage
 #endif
@@ -52,7 +56,7 @@ int auto_decode_splits(int64_t N, int64_t K) {
 // 16-byte aligned, `have_ws` whether a workspace was passed.
 rmm_status plan_shape(int64_t M, int64_t N, int64_t K, rmm_dtype dtype, int gated,
                       rmm_variant variant, int splits, bool aligned, bool have_ws, Plan* out) {
-  if (variant < RMM_VARIANT_AUTO || variant > RMM_VARIANT_PREFILL) return RMM_ERR_VARIANT;
+  if (variant < RMM_VARIANT_AUTO || variant > RMM_VARIANT_STREAM) return RMM_ERR_VARIANT;
   if (splits < 0) return RMM_ERR_VARIANT;
   if (splits != 0 && variant != RMM_VARIANT_DECODE) return RMM_ERR_VARIANT;
   if (M == 0 || N == 0) {  // nothing to compute, nothing launched
@@ -61,18 +65,26 @@ rmm_status plan_shape(int64_t M, int64_t N, int64_t K, rmm_dtype dtype, int gate
     out->ws_bytes = 0;
     return RMM_OK;
   }
-  const bool fast_layout = dtype == RMM_DTYPE_BF16 && K % 8 == 0 && N % 8 == 0 && aligned;
-  // The decode variant addresses X and W with 32-bit buffer offsets.
-  const bool decode_ok = fast_layout && M <= (gated ? kDecodeMaxMGated : kDecodeMaxM) &&
-                         K * N * 2 <= (int64_t)INT32_MAX && M * K * 2 <= (int64_t)INT32_MAX;
   // The fast variants address X and W with 32-bit buffer offsets.
-  const bool prefill_ok = fast_layout && !gated && K * N * 2 <= (int64_t)INT32_MAX &&
-                          M * K * 2 <= (int64_t)INT32_MAX;
+  const bool fast_layout = dtype == RMM_DTYPE_BF16 && K % 8 == 0 && N % 8 == 0 && aligned &&
+                           K * N * 2 <= (int64_t)INT32_MAX && M * K * 2 <= (int64_t)INT32_MAX;
+  const bool decode_ok = fast_layout && M <= (gated ? kDecodeMaxMGated : kDecodeMaxM);
+  const bool prefill_ok = fast_layout && !gated;
+  const bool stream_ok = fast_layout && M <= kStreamMaxM;
   rmm_variant v = variant;
-  if (v == RMM_VARIANT_AUTO)
-    v = decode_ok ? RMM_VARIANT_DECODE : (prefill_ok ? RMM_VARIANT_PREFILL : RMM_VARIANT_GENERIC);
+  if (v == RMM_VARIANT_AUTO) {
+    if (gated)
+      v = stream_ok ? RMM_VARIANT_STREAM : RMM_VARIANT_GENERIC;
+    else if (decode_ok)
+      v = RMM_VARIANT_DECODE;
+    else if (stream_ok && (N + 63) / 64 >= kStreamMinTiles)
+      v = RMM_VARIANT_STREAM;
+    else
+      v = prefill_ok ? RMM_VARIANT_PREFILL : RMM_VARIANT_GENERIC;
+  }
   if (v == RMM_VARIANT_DECODE && !decode_ok) return RMM_ERR_VARIANT;
   if (v == RMM_VARIANT_PREFILL && !prefill_ok) return RMM_ERR_VARIANT;
+  if (v == RMM_VARIANT_STREAM && !stream_ok) return RMM_ERR_VARIANT;
   out->variant = v;
   out->splits = 1;
   out->ws_bytes = 0;
@@ -146,6 +158,9 @@ rmm_status run(const void* X, const void* g, const void* W1, const void* W3, voi
       break;
     case RMM_VARIANT_PREFILL:
       err = rmm_launch_prefill(a, plan.pre);
+      break;
+    case RMM_VARIANT_STREAM:
+      err = rmm_launch_stream(a);
       break;
     default:
       return RMM_ERR_VARIANT;

@@ -87,3 +87,5 @@ struct PrefillPlan {
 };
 void rmm_prefill_plan(int64_t M, int64_t N, int64_t K, PrefillPlan* p);
 hipError_t rmm_launch_prefill(const RmmArgs& a, const PrefillPlan& p);
+
+hipError_t rmm_launch_stream(const RmmArgs& a);

@@ -78,6 +78,8 @@ def test_validation_order(lib):
     assert call(lib, Y=A[2] - 8) == ALIAS            # Y overlapping the start of W
     assert call(lib, ws=A[3] + 64, ws_bytes=1 << 20) == ALIAS
     assert call(lib, variant=9) == VARIANT
+    assert call(lib, variant=4, splits=2) == VARIANT  # splits only for decode
+    assert call(lib, variant=4, dtype=F32) == VARIANT  # stream is bf16 only
     assert call(lib, variant=1, splits=2) == VARIANT  # splits only for decode
     assert call(lib, variant=2, dtype=F32) == VARIANT  # decode is bf16 only
     assert call(lib, variant=2, M=33) == VARIANT
@@ -114,7 +116,12 @@ def test_variant_selection():
     import torch
     assert tpa.plan(16, 6144, 4096)[1:] == ("decode", 8)
     assert tpa.plan(16, 6144, 4096, with_workspace=False)[1:] == ("decode", 1)
-    assert tpa.plan(64, 14336, 4096, gated=True)[1] == "generic"
+    assert tpa.plan(64, 14336, 4096, gated=True)[1] == "stream"
+    assert tpa.plan(16, 14336, 4096, gated=True)[1] == "stream"
+    assert tpa.plan(65, 14336, 4096, gated=True)[1] == "generic"
+    assert tpa.plan(48, 14336, 4096)[1] == "stream"
+    assert tpa.plan(48, 2048, 4096)[1] == "prefill"   # too few 64-column strips
+    assert tpa.plan(65, 4096, 4096, variant="stream")[0] == VARIANT
     assert tpa.plan(8, 1024, 1024, dtype=torch.float32)[1] == "generic"
     assert tpa.plan(4096, 4096, 4096)[1:] == ("prefill", 1)
     assert tpa.plan(8192, 28672, 8192)[1] == "prefill"

@@ -49,6 +49,10 @@ EXACT_CASES = [
     (40, 4096, 2048, "bf16", "prefill", 0),
     (4096, 4096, 4096, "bf16", "prefill", 0),
     (1024, 8192, 28672, "bf16", "prefill", 0),
+    (64, 4096, 14336, "bf16", "stream", 0),
+    (33, 1000, 520, "bf16", "stream", 0),
+    (1, 8, 8, "bf16", "stream", 0),
+    (64, 136, 4104, "bf16", "stream", 0),
 ]
 
 EXACT_SAMPLE_ROWS = 48  # above ~1e10 multiply-adds the oracle checks sampled rows
@@ -118,10 +122,11 @@ def test_prefill_m4096_k4096_n4096_sampled(variant, require_gpu):
     _check_workload(wl.name, variant=variant, rows=_sample_rows(wl))
 
 
-def test_gated_m64_k4096_n14336_sampled_cols(require_gpu):
+@pytest.mark.parametrize("variant", ["auto", "stream", "generic"])
+def test_gated_m64_k4096_n14336_sampled_cols(variant, require_gpu):
     wl = synth.get_workload("gated_m64_k4096_n14336")
     cols = np.sort(np.random.default_rng(8).choice(wl.N, size=1024, replace=False))
-    _check_workload(wl.name, cols=cols)
+    _check_workload(wl.name, variant=variant, cols=cols)
 
 
 def test_large_m8192_k8192_n28672_sampled(require_gpu):
@@ -130,11 +135,12 @@ def test_large_m8192_k8192_n28672_sampled(require_gpu):
 
 
 # ----------------------------------------------------------------- gated small
-@pytest.mark.parametrize("variant,splits", [("generic", 0), ("decode", 1), ("decode", 3)])
+@pytest.mark.parametrize("variant,splits", [("generic", 0), ("decode", 1), ("decode", 3),
+                                            ("stream", 0)])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_gated_small(variant, splits, dtype, require_gpu):
-    if dtype == "f32" and variant == "decode":
-        pytest.skip("decode variant is bf16 only")
+    if dtype == "f32" and variant in ("decode", "stream"):
+        pytest.skip("decode and stream variants are bf16 only")
     wl = synth.Workload("gated_small", dtype, 13, 520, 392, 1e-6, True, None)
     _log(f"gated small {dtype} {variant} {splits}")
     inp = synth.make_inputs(wl, seed=5)
@@ -162,7 +168,7 @@ def test_empty_is_noop(require_gpu):
 
 
 def test_zero_row_gives_zero(require_gpu):
-    for variant in ("generic", "decode", "prefill"):
+    for variant in ("generic", "decode", "prefill", "stream"):
         x, g, w = _tensors(4, 256, 128)
         x[2] = 0
         y = tpa.rmsnorm_matmul(x, g, w, 1e-6, variant=variant)
@@ -175,7 +181,7 @@ def test_canaries_around_output(require_gpu):
     """Y is written in full and nothing outside it is touched."""
     for variant, (M, K, N) in (("generic", (7, 72, 200)), ("decode", (7, 1024, 1032)),
                                ("decode", (16, 4096, 6144)), ("prefill", (300, 200, 264)),
-                               ("prefill", (512, 256, 512))):
+                               ("prefill", (512, 256, 512)), ("stream", (40, 520, 328))):
         x, g, w = _tensors(M, K, N)
         guard = 4096
         buf = torch.full((guard + M * N + guard,), float("nan"), dtype=torch.bfloat16, device="cuda")
@@ -221,3 +227,13 @@ def test_errors_raise(require_gpu):
         tpa.rmsnorm_matmul(x, g, w, 1e-6, variant="decode", splits=99)
     with pytest.raises(tpa.RmmError):  # output overlapping the input X
         tpa.rmsnorm_matmul(x, g, w, 1e-6, out=x.view(-1)[:128].view(4, 32))
+
+
+@pytest.mark.parametrize("M", [1, 16, 40, 64])
+def test_gated_stream_shapes(M, require_gpu):
+    """Gated stream variant on ragged shapes, against the oracle."""
+    wl = synth.Workload("gated_stream", "bf16", M, 1032, 584, 1e-6, True, None)
+    _log(f"gated stream M={M}")
+    inp = synth.make_inputs(wl, seed=11)
+    y = from_device(run_gpu(inp, wl.eps, variant="stream"))
+    assert_within_tol(y, run_oracle(inp, wl.eps), 1e-2, "gated_stream")

@@ -7,7 +7,10 @@ of the whole hot path.  Inputs are seeded synthetic tensors already resident
 in HBM.  R input sets are rotated so that each timed pass touches >= 1 GiB,
 more than the 256 MB Infinity Cache, so W really streams from HBM.  The R
 calls are captured once in a HIP graph (no allocation or memset inside) and
-replayed; HIP events on the launch stream bracket the K timed steps.
+replayed; HIP events on the launch stream bracket the K timed steps.  Before
+the W warm-up steps, untimed calls run for --settle-ms of wall time: after an
+idle period the GPU takes some 10-20 ms under load to reach its steady clocks,
+and a short timed region would otherwise measure that ramp.
 
 Prints one JSON line.  `value` is the algorithmic HBM throughput (every input
 byte once + Y once, per second) for bandwidth-bound workloads, or TFLOP/s for
@@ -118,6 +121,8 @@ def main():
     ap.add_argument("--variant", default="auto")
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--no-graph", action="store_true", help="plain launches instead of a graph")
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="untimed calls for this long before the warm-up steps (clock ramp)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds for the oracle leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -125,8 +130,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: the fused RMSNorm+MatMul path has no "
-              "multi-GPU component in this build (--gpus must be 1).", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: the fused RMSNorm+MatMul path is measured "
+              "on one GPU's share (--gpus must be 1).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -219,6 +224,15 @@ def main():
 
     steps = max(R, (args.steps // R) * R)
     warm = max(R, (args.warmup // R) * R) if args.warmup > 0 else 0
+    settle_calls = 0
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < args.settle_ms:
+        run_steps(R)
+        settle_calls += R
+        if settle_calls % (16 * R) == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    log(f"clock settle: {settle_calls} untimed calls in {(time.perf_counter() - t0) * 1e3:.0f} ms")
     log(f"warmup {warm} steps")
     run_steps(warm)
     torch.cuda.synchronize()
@@ -263,7 +277,8 @@ def main():
         "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
         "config": {"workload": wl.name, "M": wl.M, "K": wl.K, "N": wl.N, "gated": wl.gated,
                    "eps": wl.eps, "variant": variant, "splits": splits,
-                   "rotating_input_sets": R, "hip_graph": graph is not None},
+                   "rotating_input_sets": R, "hip_graph": graph is not None,
+                   "clock_settle_calls": settle_calls},
         "tflops": tflops, "hbm_gbs_algorithmic": gbs,
         "roofline": roof, "cpu_baseline": cpu,
     }

@@ -28,27 +28,24 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
   return a0 < b0 + bn && b0 < a0 + an;
 }
 
-// Decode: few rows.  The split count aims at ~1.5 workgroups per CU (256 CUs):
-// more splits add partial-sum traffic and lengthen the combine that the last
-// arriving workgroup of each tile does alone.
+// Decode: few rows.  The split count is the largest power of two that keeps
+// the grid at one workgroup per CU (256 CUs): more splits add partial-sum
+// traffic and lengthen the combine that the last arriving workgroup of each
+// tile does alone, and measured fastest at this size.
 constexpr int64_t kDecodeMaxM = 32;
 constexpr int64_t kDecodeMaxMGated = 16;
-constexpr int64_t kTargetWorkgroups = 384;
+constexpr int64_t kTargetWorkgroups = 256;
 // Stream: up to 64 rows; auto-selected for plain calls only when there are
 // enough 64-column strips to keep most CUs streaming.
 constexpr int64_t kStreamMaxM = 64;
 constexpr int64_t kStreamMinTiles = 192;
-#ifndef RMM_DECODE_NBW
-#define RMM_DECODE_NBW 1  // 32-deep k-blocks per wave per pipeline stage
-#endif
 
 int auto_decode_splits(int64_t N, int64_t K) {
   const int64_t tiles = (N + 127) / 128;
   if (tiles < 1) return 1;
-  int64_t s = (kTargetWorkgroups + tiles / 2) / tiles;
   const int64_t kgran = (K + 127) / 128;
-  if (s < 1) s = 1;
-  if (s > kgran) s = kgran;
+  int64_t s = 1;
+  while (2 * s * tiles <= kTargetWorkgroups && 2 * s <= kgran) s *= 2;
   return (int)s;
 }
 
@@ -93,7 +90,7 @@ rmm_status plan_shape(int64_t M, int64_t N, int64_t K, rmm_dtype dtype, int gate
     if (s == 0) s = have_ws ? auto_decode_splits(N, K) : 1;
     if (s > (K + 127) / 128) return RMM_ERR_VARIANT;
     if (s > 1 && !have_ws) return RMM_ERR_WORKSPACE;  // a forced split count needs one
-    rmm_decode_plan(M, N, K, gated, s, RMM_DECODE_NBW, &out->dec);
+    rmm_decode_plan(M, N, K, gated, s, &out->dec);
     if (out->dec.ws_bytes > (size_t)INT32_MAX) return RMM_ERR_VARIANT;  // 32-bit offsets
     out->splits = out->dec.splits;
     out->ws_bytes = out->dec.ws_bytes;

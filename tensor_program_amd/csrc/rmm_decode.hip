@@ -10,25 +10,29 @@
 // of the Mirage paper review ("核心公式") with the k-independent divisor I3
 // moved outside the sum.
 //
-// Work decomposition (one workgroup = 4 waves of 64 lanes):
+// Work decomposition (one workgroup = WV waves of 64 lanes):
 //   * a workgroup owns a 128-column tile of Y and a chunk of K;
-//   * its 4 waves take interleaved 32-deep k-blocks of the chunk;
-//   * per k-block, lane (q = lane/16, p = lane%16) loads rows kb+8q .. kb+8q+7
-//     of W at columns 8p .. 8p+7 of the tile (eight 16-byte loads; each load
-//     instruction reads four 256-byte row segments), transposes the 8x8 block
-//     in registers, and feeds it as the B operand of eight
-//     v_mfma_f32_16x16x32_bf16 (one per column 8p+c).  The A operand is
-//     (X g) for rows 16*mb + p, k = kb+8q .. +7, formed in fp32 and rounded
-//     once to bf16; the same lanes accumulate X^2 in fp32 for the row RMS.
-//   * the 4 waves' accumulators are summed through LDS; with several K chunks
+//   * first it stages A = bf16(X g) for (a segment of) its chunk in LDS,
+//     laid out [k/8][row] in 16-byte units, and accumulates the row sums of
+//     squares while doing so; these loads are issued before any W load, so
+//     the W stream starts at once behind them;
+//   * the waves take interleaved 32-deep k-blocks; per k-block, lane
+//     (q = lane/16, p = lane%16) holds rows kb+8q .. kb+8q+7 of W at columns
+//     8p .. 8p+7 of the tile (eight 16-byte loads, each load instruction
+//     reading four 256-byte row segments), transposes the 8x8 block in
+//     registers with byte permutes, and feeds column c as the B operand of
+//     v_mfma_f32_16x16x32_bf16 number c; the A operand is one 16-byte LDS
+//     read.  W is double-buffered in registers: the loads of the next k-block
+//     are in flight while one is multiplied.  Loads past the chunk are issued
+//     anyway (their range check returns zeros without a memory access), so
+//     the compiler's wait counters track a fixed pattern;
+//   * the waves' accumulators are summed through LDS; with several K chunks
 //     the workgroup stores its fp32 partial to the workspace, and the last
 //     workgroup to arrive at a tile (arrival counter) adds the partials and
 //     runs the epilogue  Y = acc / RMS  (gated: silu(acc1/RMS) * acc3/RMS).
 //   * the partials cross XCDs (each XCD has its own L2), so they are written
 //     and read with device-scope coherent accesses, ordered by waiting for the
-//     stores' acknowledgements before the arrival count.  A device-wide fence
-//     per workgroup (an L2 write-back plus invalidate on gfx950) would also be
-//     correct but costs several microseconds per call at this size.
+//     stores' acknowledgements before the arrival count.
 //   * the block index is remapped so that all chunks of a tile are dispatched
 //     to the same XCD (workgroups go round-robin over the 8 XCDs); this only
 //     affects locality, never correctness.
@@ -36,123 +40,83 @@
 
 namespace rmm {
 
-constexpr int DEC_THREADS = 256;
-constexpr int DEC_COLS = 128;  // columns per workgroup tile
-constexpr int DEC_KWG = 128;   // k per workgroup step (4 waves x 32)
+constexpr int DEC_COLS = 128;             // columns per workgroup tile
+constexpr int DEC_STAGE_BYTES = 32768;    // LDS for the staged A operand
+constexpr uint32_t kOutOfRange = 0x80000000u;  // > every buffer the variant accepts
+// Workspace accesses of the split-K combine: device (agent) scope coherence
+// (the SC1 cache-policy bit), so partials written on one XCD are read
+// correctly on any other without a cache-wide write-back or invalidate.
+constexpr int kCoherentDevice = 16;
 
-template <int MB, int NW>
+template <int MB, int NW, int WV>
 struct DecodeSmem {
-  alignas(16) float red[4][NW * MB * 32][64];  // per-wave accumulators, [wave][element][lane]
-  float ss[4][MB * 16];
-  float inv[MB * 16];
+  floatx4 red[WV][NW * MB * 8][64];  // per-wave accumulators [wave][(wi,b,c)][lane]
+  u32x4 xg[DEC_STAGE_BYTES / (16 * 16 * MB)][16 * MB];  // A operand, [k/8][row]
+  float ssr[16 * MB];
+  float inv[16 * MB];
   int last;
 };
 
-// Column c (0..7) of an 8x8 bf16 block held as 8 rows of 4 dwords (row j,
-// dword e = columns 2e, 2e+1) -> 8 consecutive-k values of that column.
-__device__ __forceinline__ u32x4 column_of(const u32x4 (&rows)[8], int c) {
-  u32x4 out;
-  const int e = c >> 1;
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const uint32_t lo = rows[2 * d][e], hi = rows[2 * d + 1][e];
-    out[d] = (c & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-  }
-  return out;
-}
-
-// Registers of one pipeline stage: NBW k-blocks of W (and W3), X and g.
-template <int MB, int NBW, int NW>
-struct DecodeStage {
-  u32x4 w[NW][NBW][8];
-  u32x4 x[NBW][MB];
-  u32x4 g[NBW];
-};
-
-// Buffer resources (base, size) of the operands.  Loads go through them
-// with a 32-bit byte offset per lane; an offset past the end returns zeros
-// (hardware range check), which is how rows beyond K and M, and columns
-// beyond N, read as zero without a branch.
 struct DecodeSrc {
   __amdgpu_buffer_rsrc_t w1, w3, x, g;
 };
-constexpr uint32_t kOutOfRange = 0x80000000u;  // > every buffer the variant accepts
 
-template <int MB, int NBW, int NW>
-__device__ __forceinline__ void decode_load(DecodeStage<MB, NBW, NW>& st, const DecodeSrc& src,
-                                            int M, int64_t N, int64_t K, int64_t k0,
-                                            int64_t k_hi, int64_t col, bool col_ok, int w, int q,
-                                            int p) {
+// W rows krow .. krow+7 (krow = k0 + 32 w + 8 q) at columns col .. col+7 of
+// one or two weights.  An offset past the end returns zeros (range check).
+template <int NW>
+__device__ __forceinline__ void decode_load(u32x4 (&wv)[NW][8], const DecodeSrc& src, int64_t N,
+                                            int64_t krow, int64_t k_hi, int64_t col,
+                                            bool col_ok) {
   const uint32_t row_bytes = (uint32_t)(N * 2);
+  const uint32_t wo = (krow < k_hi && col_ok) ? (uint32_t)((krow * N + col) * 2) : kOutOfRange;
 #pragma unroll
-  for (int i = 0; i < NBW; ++i) {
-    const int64_t krow = k0 + 32 * (w + 4 * i) + 8 * q;
-    const bool k_ok = krow < k_hi;  // K % 8 == 0: the 8 rows are all in or all out
-    const uint32_t wo = (k_ok && col_ok) ? (uint32_t)((krow * N + col) * 2) : kOutOfRange;
+  for (int j = 0; j < 8; ++j) {
+    wv[0][j] = __builtin_amdgcn_raw_buffer_load_b128(src.w1, wo, j * row_bytes, 0);
+    if (NW == 2) wv[NW - 1][j] = __builtin_amdgcn_raw_buffer_load_b128(src.w3, wo, j * row_bytes, 0);
+  }
+}
+
+// Column c of the 8x8 block (row j, dword e = columns 2e, 2e+1) -> 8
+// consecutive-k values; one byte permute per output dword.
+template <int MB, int NW>
+__device__ __forceinline__ void decode_mma(const u32x4 (&wv)[NW][8], const u32x4 (&a)[MB],
+                                           floatx4 (&acc)[NW][MB][8]) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      st.w[0][i][j] = __builtin_amdgcn_raw_buffer_load_b128(src.w1, wo, j * row_bytes, 0);
-      if (NW == 2)
-        st.w[NW - 1][i][j] = __builtin_amdgcn_raw_buffer_load_b128(src.w3, wo, j * row_bytes, 0);
-    }
-    const uint32_t go = k_ok ? (uint32_t)(krow * 2) : kOutOfRange;
-    st.g[i] = __builtin_amdgcn_raw_buffer_load_b128(src.g, go, 0, 0);
+  for (int c = 0; c < 8; ++c) {
 #pragma unroll
-    for (int b = 0; b < MB; ++b) {
-      const int row = 16 * b + p;
-      const uint32_t xo = (k_ok && row < M) ? (uint32_t)(((int64_t)row * K + krow) * 2) : kOutOfRange;
-      st.x[i][b] = __builtin_amdgcn_raw_buffer_load_b128(src.x, xo, 0, 0);
+    for (int wi = 0; wi < NW; ++wi) {
+      u32x4 bop;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        bop[d] = __builtin_amdgcn_perm(wv[wi][2 * d + 1][c >> 1], wv[wi][2 * d][c >> 1],
+                                       (c & 1) ? 0x07060302u : 0x05040100u);
+#pragma unroll
+      for (int b = 0; b < MB; ++b)
+        acc[wi][b][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, a[b]), __builtin_bit_cast(bf16x8, bop), acc[wi][b][c], 0, 0,
+            0);
     }
   }
 }
 
-template <int MB, int NBW, int NW>
-__device__ __forceinline__ void decode_compute(const DecodeStage<MB, NBW, NW>& st,
-                                               floatx4 (&acc)[NW][MB][8], float (&ss)[MB]) {
-#pragma unroll
-  for (int i = 0; i < NBW; ++i) {
-    bf16x8 a[MB];
-#pragma unroll
-    for (int b = 0; b < MB; ++b) {
-      u32x4 av;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const float x0 = bf16_lo(st.x[i][b][d]), x1 = bf16_hi(st.x[i][b][d]);
-        const float g0 = bf16_lo(st.g[i][d]), g1 = bf16_hi(st.g[i][d]);
-        ss[b] += x0 * x0 + x1 * x1;
-        av[d] = pack_bf16x2(x0 * g0, x1 * g1);
-      }
-      a[b] = __builtin_bit_cast(bf16x8, av);
-    }
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-#pragma unroll
-      for (int wi = 0; wi < NW; ++wi) {
-        const bf16x8 bop = __builtin_bit_cast(bf16x8, column_of(st.w[wi][i], c));
-#pragma unroll
-        for (int b = 0; b < MB; ++b)
-          acc[wi][b][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[b], bop, acc[wi][b][c], 0, 0, 0);
-      }
-    }
-  }
-}
-
-// Workspace accesses of the split-K combine: 16-byte buffer loads/stores
-// with device (agent) scope coherence (the SC1 cache-policy bit), so the
-// partials written on one XCD are read correctly on any other without a
-// cache-wide write-back or invalidate.
-constexpr int kCoherentDevice = 16;  // SC1
-
-template <int MB, int NBW, bool GATED>
-__global__ __launch_bounds__(DEC_THREADS) void decode_kernel(
+template <int MB, bool GATED, int WV>
+__global__ __launch_bounds__(WV * 64) void decode_kernel(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ g, const bf16_t* __restrict__ W1,
     const bf16_t* __restrict__ W3, bf16_t* __restrict__ Y, float eps, int M, int64_t N,
     int64_t K, int64_t kchunk, int S, int tiles, int xcd_remap, unsigned* __restrict__ cnt,
     float* __restrict__ ssq_ws, float* __restrict__ part_ws) {
   constexpr int NW = GATED ? 2 : 1;
-  constexpr int E = NW * MB * 32 * 64;  // accumulator floats per workgroup
-  constexpr int PER = E / DEC_THREADS;  // floats per thread in the combine (8 NW MB)
-  __shared__ DecodeSmem<MB, NW> sm;
+  constexpr int NT = WV * 64;
+  constexpr int E4 = NW * MB * 8 * 64;  // floatx4 per partial
+  constexpr int PER4 = E4 / NT;         // floatx4 per thread in the combine
+  constexpr int ROWS = 16 * MB;
+  constexpr int SEG = DEC_STAGE_BYTES / (16 * ROWS) * 8;  // k rows staged at a time
+  constexpr int TPR = NT / ROWS;                          // staging threads per row
+  constexpr int NU = SEG / 8 / TPR;                       // 16-byte chunks per staging thread
+  constexpr int STEP = 32 * WV;                           // k rows per pipeline step
+  constexpr int SPS = SEG / STEP;                         // steps per staged segment
+  static_assert(SPS % 2 == 0 && NU >= 1, "segment must hold an even number of steps");
+  __shared__ DecodeSmem<MB, NW, WV> sm;
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, q = l >> 4, p = l & 15;
   int tile, split;
@@ -171,6 +135,52 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(
   const bool col_ok = col < N;
   const int64_t k_lo = (int64_t)split * kchunk;
   const int64_t k_hi = (k_lo + kchunk < K) ? (k_lo + kchunk) : K;
+  const int nsteps = (int)((k_hi - k_lo + STEP - 1) / STEP);
+
+  DecodeSrc src;
+  src.w1 = __builtin_amdgcn_make_buffer_rsrc((void*)W1, 0, (int)(K * N * 2), 0x00020000);
+  src.w3 = __builtin_amdgcn_make_buffer_rsrc((void*)(GATED ? W3 : W1), 0, (int)(K * N * 2), 0x00020000);
+  src.x = __builtin_amdgcn_make_buffer_rsrc((void*)X, 0, (int)((int64_t)M * K * 2), 0x00020000);
+  src.g = __builtin_amdgcn_make_buffer_rsrc((void*)g, 0, (int)(K * 2), 0x00020000);
+
+  // Staging: thread -> row srow, 16-byte k-chunks sj + TPR u of the segment.
+  const int srow = tid / TPR, sj = tid % TPR;
+  float ssl = 0.f;
+  auto stage_load = [&](int64_t seg_lo, u32x4 (&xs)[NU], u32x4 (&gs)[NU]) {
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int64_t k = seg_lo + 8 * (sj + TPR * u);
+      const bool ok = k < k_hi && k < seg_lo + SEG;
+      xs[u] = __builtin_amdgcn_raw_buffer_load_b128(
+          src.x, (ok && srow < M) ? (uint32_t)(((int64_t)srow * K + k) * 2) : kOutOfRange, 0, 0);
+      gs[u] = __builtin_amdgcn_raw_buffer_load_b128(src.g, ok ? (uint32_t)(k * 2) : kOutOfRange, 0, 0);
+    }
+  };
+  auto stage_form = [&](const u32x4 (&xs)[NU], const u32x4 (&gs)[NU]) {
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      u32x4 av;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const float x0 = bf16_lo(xs[u][d]), x1 = bf16_hi(xs[u][d]);
+        const float g0 = bf16_lo(gs[u][d]), g1 = bf16_hi(gs[u][d]);
+        ssl += x0 * x0 + x1 * x1;
+        av[d] = pack_bf16x2(x0 * g0, x1 * g1);
+      }
+      sm.xg[sj + TPR * u][srow] = av;
+    }
+  };
+
+  // Segment 0 staging loads, then both W stages, then the A operand.
+  u32x4 wa[NW][8], wb[NW][8];
+  {
+    u32x4 xs[NU], gs[NU];
+    stage_load(k_lo, xs, gs);
+    decode_load<NW>(wa, src, N, k_lo + 32 * w + 8 * q, k_hi, col, col_ok);
+    decode_load<NW>(wb, src, N, k_lo + STEP + 32 * w + 8 * q, k_hi, col, col_ok);
+    stage_form(xs, gs);
+  }
+  __syncthreads();
 
   floatx4 acc[NW][MB][8];
 #pragma unroll
@@ -179,75 +189,79 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(
     for (int b = 0; b < MB; ++b)
 #pragma unroll
       for (int c = 0; c < 8; ++c) acc[a][b][c] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float ss[MB];
-#pragma unroll
-  for (int b = 0; b < MB; ++b) ss[b] = 0.f;
 
-  // Two register stages: the loads of step s+1 are in flight while step s
-  // is multiplied.
-  const int64_t step = (int64_t)DEC_KWG * NBW;
-  const int nsteps = (int)((k_hi - k_lo + step - 1) / step);
-  DecodeSrc src;
-  src.w1 = __builtin_amdgcn_make_buffer_rsrc((void*)W1, 0, (int)(K * N * 2), 0x00020000);
-  src.w3 = __builtin_amdgcn_make_buffer_rsrc((void*)(GATED ? W3 : W1), 0, (int)(K * N * 2), 0x00020000);
-  src.x = __builtin_amdgcn_make_buffer_rsrc((void*)X, 0, (int)((int64_t)M * K * 2), 0x00020000);
-  src.g = __builtin_amdgcn_make_buffer_rsrc((void*)g, 0, (int)(K * 2), 0x00020000);
-  DecodeStage<MB, NBW, NW> sa, sb;
-  decode_load(sa, src, M, N, K, k_lo, k_hi, col, col_ok, w, q, p);
+  auto fetch_a = [&](int s, u32x4 (&a)[MB]) {
+    const int kc = ((s % SPS) * STEP + 32 * w + 8 * q) >> 3;
+#pragma unroll
+    for (int b = 0; b < MB; ++b) a[b] = sm.xg[kc][16 * b + p];
+  };
+  // A new segment: everyone is done with the old one, stage, publish.
+  auto restage = [&](int s) {
+    __syncthreads();
+    u32x4 xs[NU], gs[NU];
+    stage_load(k_lo + (int64_t)s * STEP, xs, gs);
+    stage_form(xs, gs);
+    __syncthreads();
+  };
   int s = 0;
   for (; s + 2 <= nsteps; s += 2) {
-    decode_load(sb, src, M, N, K, k_lo + (s + 1) * step, k_hi, col, col_ok, w, q, p);
-    decode_compute(sa, acc, ss);
-    if (s + 2 < nsteps) decode_load(sa, src, M, N, K, k_lo + (s + 2) * step, k_hi, col, col_ok, w, q, p);
-    decode_compute(sb, acc, ss);
+    if (s > 0 && s % SPS == 0) restage(s);
+    u32x4 a[MB];
+    fetch_a(s, a);
+    decode_mma<MB, NW>(wa, a, acc);
+    decode_load<NW>(wa, src, N, k_lo + (int64_t)(s + 2) * STEP + 32 * w + 8 * q, k_hi, col, col_ok);
+    fetch_a(s + 1, a);
+    decode_mma<MB, NW>(wb, a, acc);
+    decode_load<NW>(wb, src, N, k_lo + (int64_t)(s + 3) * STEP + 32 * w + 8 * q, k_hi, col, col_ok);
   }
-  if (s < nsteps) decode_compute(sa, acc, ss);
+  if (s < nsteps) {
+    if (s > 0 && s % SPS == 0) restage(s);
+    u32x4 a[MB];
+    fetch_a(s, a);
+    decode_mma<MB, NW>(wa, a, acc);
+  }
 
-  // Row sums of squares: lanes p, p+16, p+32, p+48 hold the four k-groups.
+  // Row sums of squares: the TPR staging threads of a row are adjacent lanes.
 #pragma unroll
-  for (int b = 0; b < MB; ++b) {
-    ss[b] += __shfl_xor(ss[b], 16);
-    ss[b] += __shfl_xor(ss[b], 32);
-    if (q == 0) sm.ss[w][16 * b + p] = ss[b];
-  }
-  // Per-wave accumulators to LDS: element e = (wi*MB + b)*32 + c*4 + r.
+  for (int o = 1; o < TPR; o <<= 1) ssl += __shfl_xor(ssl, o);
+  if (sj == 0) sm.ssr[srow] = ssl;
+  // Per-wave accumulators to LDS as floatx4: e = (wi*MB + b)*8 + c.
 #pragma unroll
   for (int wi = 0; wi < NW; ++wi)
 #pragma unroll
     for (int b = 0; b < MB; ++b)
 #pragma unroll
-      for (int c = 0; c < 8; ++c)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sm.red[w][(wi * MB + b) * 32 + c * 4 + r][l] = acc[wi][b][c][r];
+      for (int c = 0; c < 8; ++c) sm.red[w][(wi * MB + b) * 8 + c][l] = acc[wi][b][c];
   __syncthreads();
 
-  // Workgroup sum of the four waves; thread owns flat floats [PER*tid, PER*tid + PER).
-  float* red0 = &sm.red[0][0][0];
-  floatx4 v[PER / 4];
+  // Workgroup sum of the waves; thread owns floatx4 tid + NT u.
+  floatx4* red0 = &sm.red[0][0][0];
+  floatx4 v[PER4];
 #pragma unroll
-  for (int t = 0; t < PER / 4; ++t) {
-    const int f = PER * tid + 4 * t;
-    v[t] = *(const floatx4*)(&sm.red[0][0][0] + f) + *(const floatx4*)(&sm.red[1][0][0] + f) +
-           *(const floatx4*)(&sm.red[2][0][0] + f) + *(const floatx4*)(&sm.red[3][0][0] + f);
+  for (int u = 0; u < PER4; ++u) {
+    const int f = tid + NT * u;
+    floatx4 t4 = red0[f];
+#pragma unroll
+    for (int ww = 1; ww < WV; ++ww) t4 += red0[ww * E4 + f];
+    v[u] = t4;
   }
-  float ssw = 0.f;
-  if (tid < MB * 16) ssw = sm.ss[0][tid] + sm.ss[1][tid] + sm.ss[2][tid] + sm.ss[3][tid];
+  float ssw = tid < ROWS ? sm.ssr[tid] : 0.f;
 
   if (S > 1) {
     const int64_t slot = (int64_t)split * tiles + tile;
     const int64_t nslots = (int64_t)S * tiles;
     const __amdgpu_buffer_rsrc_t prs =
-        __builtin_amdgcn_make_buffer_rsrc(part_ws, 0, (int)(nslots * E * 4), 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc(part_ws, 0, (int)(nslots * E4 * 16), 0x00020000);
     // Partials go out with device-scope coherence; waiting for every store's
     // acknowledgement before the arrival count makes them visible to
     // whichever workgroup arrives last.
 #pragma unroll
-    for (int t = 0; t < PER / 4; ++t)
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v[t]), prs,
-                                             (int)((slot * E + PER * tid + 4 * t) * 4), 0,
+    for (int u = 0; u < PER4; ++u)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v[u]), prs,
+                                             (int)((slot * E4 + tid + NT * u) * 16), 0,
                                              kCoherentDevice);
-    if (tid < MB * 16)
-      __hip_atomic_store(&ssq_ws[slot * (MB * 16) + tid], ssw, __ATOMIC_RELAXED,
+    if (tid < ROWS)
+      __hip_atomic_store(&ssq_ws[slot * ROWS + tid], ssw, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -256,32 +270,32 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(
                                         __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(S - 1));
     __syncthreads();
     if (!sm.last) return;
-    // Last arrival: add the S partials, four splits' loads in flight at a time.
+    // Last arrival: add the S partials, up to 8 splits' loads in flight.
+    constexpr int RS = 8 / PER4 > 0 ? 8 / PER4 : 1;
 #pragma unroll
-    for (int t = 0; t < PER / 4; ++t) v[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < PER4; ++u) v[u] = floatx4{0.f, 0.f, 0.f, 0.f};
     ssw = 0.f;
-    for (int s0 = 0; s0 < S; s0 += 4) {
-      u32x4 buf[4][PER / 4];
-      float sbuf[4];
+    for (int s0 = 0; s0 < S; s0 += RS) {
+      u32x4 buf[RS][PER4];
+      float sb[RS];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int64_t sl = (int64_t)(s0 + u) * tiles + tile;
-        const bool ok = s0 + u < S;
+      for (int uu = 0; uu < RS; ++uu) {
+        const int64_t sl = (int64_t)(s0 + uu) * tiles + tile;
+        const bool ok = s0 + uu < S;
 #pragma unroll
-        for (int t = 0; t < PER / 4; ++t)
-          buf[u][t] = ok ? __builtin_amdgcn_raw_buffer_load_b128(
-                               prs, (int)((sl * E + PER * tid + 4 * t) * 4), 0, kCoherentDevice)
-                         : u32x4{0u, 0u, 0u, 0u};
-        sbuf[u] = (ok && tid < MB * 16)
-                      ? __hip_atomic_load(&ssq_ws[sl * (MB * 16) + tid], __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT)
-                      : 0.f;
+        for (int u = 0; u < PER4; ++u)
+          buf[uu][u] = ok ? __builtin_amdgcn_raw_buffer_load_b128(
+                                prs, (int)((sl * E4 + tid + NT * u) * 16), 0, kCoherentDevice)
+                          : u32x4{0u, 0u, 0u, 0u};
+        sb[uu] = (ok && tid < ROWS) ? __hip_atomic_load(&ssq_ws[sl * ROWS + tid], __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT)
+                                    : 0.f;
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int uu = 0; uu < RS; ++uu) {
 #pragma unroll
-        for (int t = 0; t < PER / 4; ++t) v[t] += __builtin_bit_cast(floatx4, buf[u][t]);
-        ssw += sbuf[u];
+        for (int u = 0; u < PER4; ++u) v[u] += __builtin_bit_cast(floatx4, buf[uu][u]);
+        ssw += sb[uu];
       }
     }
     // Leave the workspace zeroed for the next call (all arrivals are in).
@@ -289,14 +303,18 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(
   }
   __syncthreads();  // everyone is done reading sm.red before it is overwritten
 #pragma unroll
-  for (int t = 0; t < PER / 4; ++t) *(floatx4*)(red0 + PER * tid + 4 * t) = v[t];
-  if (tid < MB * 16) sm.inv[tid] = inv_rms(ssw, K, eps);
+  for (int u = 0; u < PER4; ++u) red0[tid + NT * u] = v[u];
+  if (tid < ROWS) sm.inv[tid] = inv_rms(ssw, K, eps);
   __syncthreads();
 
-  // Epilogue: group (b, r, lane) -> row 16b + 4(lane/16) + r, 8 columns.
+  // Epilogue: group (b, r, lane) -> row 16b + 4(lane/16) + r, 8 columns
+  // 8(lane%16) .. +7; element (wi, b, c, lane, r) is float
+  // (((wi*MB + b)*8 + c)*64 + lane)*4 + r of the summed block.
+  const float* redf = (const float*)red0;
 #pragma unroll
-  for (int t = 0; t < MB; ++t) {
-    const int grp = tid + DEC_THREADS * t;
+  for (int t = 0; t < (MB * 256 + NT - 1) / NT; ++t) {
+    const int grp = tid + NT * t;
+    if (grp >= MB * 256) break;
     const int ln = grp & 63, br = grp >> 6, b = br >> 2, r = br & 3;
     const int row = 16 * b + 4 * (ln >> 4) + r;
     const int64_t cc = (int64_t)tile * DEC_COLS + 8 * (ln & 15);
@@ -305,11 +323,11 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(
     u32x4 out;
 #pragma unroll
     for (int c = 0; c < 8; c += 2) {
-      float y0 = red0[((0 * MB + b) * 32 + c * 4 + r) * 64 + ln] * inv;
-      float y1 = red0[((0 * MB + b) * 32 + (c + 1) * 4 + r) * 64 + ln] * inv;
+      float y0 = redf[(((0 * MB + b) * 8 + c) * 64 + ln) * 4 + r] * inv;
+      float y1 = redf[(((0 * MB + b) * 8 + c + 1) * 64 + ln) * 4 + r] * inv;
       if (GATED) {
-        const float z0 = red0[((1 * MB + b) * 32 + c * 4 + r) * 64 + ln] * inv;
-        const float z1 = red0[((1 * MB + b) * 32 + (c + 1) * 4 + r) * 64 + ln] * inv;
+        const float z0 = redf[(((1 * MB + b) * 8 + c) * 64 + ln) * 4 + r] * inv;
+        const float z1 = redf[(((1 * MB + b) * 8 + c + 1) * 64 + ln) * 4 + r] * inv;
         y0 = silu_gate(y0, z0);
         y1 = silu_gate(y1, z1);
       }
@@ -323,28 +341,29 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-void rmm_decode_plan(int64_t M, int64_t N, int64_t K, int gated, int splits, int nbw,
-                     DecodePlan* p) {
+// Chunks are whole 128-deep granules; eight waves (256-deep steps) when the
+// grid has at most one workgroup per CU and the per-wave accumulators fit.
+void rmm_decode_plan(int64_t M, int64_t N, int64_t K, int gated, int splits, DecodePlan* p) {
   using namespace rmm;
   p->mb = (int)((M + 15) / 16);
-  p->nbw = nbw;
   p->tiles = (N + DEC_COLS - 1) / DEC_COLS;
-  const int64_t kgran = (K + DEC_KWG - 1) / DEC_KWG;  // 128-deep granules
+  const int64_t kgran = (K + 127) / 128;
   int64_t s = splits;
   if (s < 1) s = 1;
   if (s > kgran) s = kgran;
   const int64_t gran_per = (kgran + s - 1) / s;
-  p->kchunk = gran_per * DEC_KWG;
+  p->kchunk = gran_per * 128;
   p->splits = (int)((K + p->kchunk - 1) / p->kchunk);
   const int nw = gated ? 2 : 1;
-  const size_t E = (size_t)nw * p->mb * 32 * 64;
+  p->wv = (nw * p->mb == 1 && p->tiles * p->splits <= 256) ? 8 : 4;
+  const size_t E = (size_t)nw * p->mb * 32 * 64;  // floats per partial
   p->ws_cnt_off = 0;
   p->ws_ssq_off = align256(sizeof(unsigned) * (size_t)p->tiles);
   p->ws_part_off = p->ws_ssq_off + align256(sizeof(float) * (size_t)p->splits * p->tiles * p->mb * 16);
   p->ws_bytes = p->splits > 1 ? p->ws_part_off + align256(sizeof(float) * (size_t)p->splits * p->tiles * E) : 0;
 }
 
-template <int MB, int NBW, bool GATED>
+template <int MB, bool GATED, int WV>
 static void launch_decode_t(const RmmArgs& a, const DecodePlan& p, void* ws) {
   using namespace rmm;
   const int xcd_remap = (p.tiles % 8) == 0;
@@ -353,7 +372,7 @@ static void launch_decode_t(const RmmArgs& a, const DecodePlan& p, void* ws) {
   float* ssq = ws ? (float*)(base + p.ws_ssq_off) : nullptr;
   float* part = ws ? (float*)(base + p.ws_part_off) : nullptr;
   const unsigned grid = (unsigned)(p.tiles * p.splits);
-  hipLaunchKernelGGL((decode_kernel<MB, NBW, GATED>), dim3(grid), dim3(DEC_THREADS), 0, a.stream,
+  hipLaunchKernelGGL((decode_kernel<MB, GATED, WV>), dim3(grid), dim3(WV * 64), 0, a.stream,
                      (const bf16_t*)a.X, (const bf16_t*)a.g, (const bf16_t*)a.W1,
                      (const bf16_t*)a.W3, (bf16_t*)a.Y, a.eps, (int)a.M, a.N, a.K, p.kchunk,
                      p.splits, (int)p.tiles, xcd_remap, cnt, ssq, part);
@@ -361,18 +380,10 @@ static void launch_decode_t(const RmmArgs& a, const DecodePlan& p, void* ws) {
 
 hipError_t rmm_launch_decode(const RmmArgs& a, const DecodePlan& p, void* ws) {
   const bool gd = a.gated != 0;
-  if (p.nbw == 2) {
-    if (!gd && p.mb == 1) launch_decode_t<1, 2, false>(a, p, ws);
-    else if (!gd && p.mb == 2) launch_decode_t<2, 2, false>(a, p, ws);
-    else if (gd && p.mb == 1) launch_decode_t<1, 2, true>(a, p, ws);
-    else return hipErrorInvalidValue;
-  } else if (p.nbw == 1) {
-    if (!gd && p.mb == 1) launch_decode_t<1, 1, false>(a, p, ws);
-    else if (!gd && p.mb == 2) launch_decode_t<2, 1, false>(a, p, ws);
-    else if (gd && p.mb == 1) launch_decode_t<1, 1, true>(a, p, ws);
-    else return hipErrorInvalidValue;
-  } else {
-    return hipErrorInvalidValue;
-  }
+  if (!gd && p.mb == 1 && p.wv == 8) launch_decode_t<1, false, 8>(a, p, ws);
+  else if (!gd && p.mb == 1 && p.wv == 4) launch_decode_t<1, false, 4>(a, p, ws);
+  else if (!gd && p.mb == 2 && p.wv == 4) launch_decode_t<2, false, 4>(a, p, ws);
+  else if (gd && p.mb == 1 && p.wv == 4) launch_decode_t<1, true, 4>(a, p, ws);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -69,15 +69,14 @@ struct RmmArgs {
 hipError_t rmm_launch_generic(const RmmArgs& a, bool bf16);
 
 struct DecodePlan {
-  int mb;          // 16-row blocks (1..4)
-  int nbw;         // 32-deep k-blocks per wave per step
+  int mb;          // 16-row blocks (1..2)
+  int wv;          // waves per workgroup (4 or 8); a step covers 32 wv rows of K
   int splits;      // K chunks combined across workgroups
   int64_t kchunk;  // K per chunk (multiple of 128)
   int64_t tiles;   // 128-column tiles
   size_t ws_cnt_off, ws_ssq_off, ws_part_off, ws_bytes;
 };
-void rmm_decode_plan(int64_t M, int64_t N, int64_t K, int gated, int splits, int nbw,
-                     DecodePlan* p);
+void rmm_decode_plan(int64_t M, int64_t N, int64_t K, int gated, int splits, DecodePlan* p);
 hipError_t rmm_launch_decode(const RmmArgs& a, const DecodePlan& p, void* ws);
 
 struct PrefillPlan {

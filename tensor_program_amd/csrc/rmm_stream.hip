@@ -13,20 +13,22 @@
 // memory into an LDS ring (buffer loads with the LDS-direct bit) several
 // k-steps ahead -- the W strips, the X rows and the g slice of a step.
 // Vector-memory loads complete in issue order, so keeping every load in this
-// one stream lets each iteration wait only for its own (oldest) step.
+// one stream lets each iteration wait only for the steps it needs.
 //   * W slot layout [64 k][64 n] bf16, 128-byte rows, 16-byte chunk c of row
 //     k at chunk c ^ 2(k & 3): the transposing LDS reads are conflict-free.
 //   * X slot layout [64 rows][64 k] bf16, 128-byte rows, chunk c of row r at
-//     chunk c ^ (r & 7): the fragment reads (8 consecutive rows) are
-//     conflict-free.
-//   * each wave multiplies one 32x32 output tile per weight (gated) or one
-//     k-half of a tile (plain) with v_mfma_f32_32x32x16_bf16.  The A operand
-//     is formed from the X fragment as X*g in fp32 (bf16 dot2 with one lane
-//     of g zeroed) rounded once to bf16; the same registers give sum_k X^2.
-//     B fragments come from ds_read_b64_tr_b16 (gfx950's transposing LDS
-//     read): lane i of each 16-lane group receives 4 consecutive k of
-//     column i.
-//   * epilogue through LDS: Y = acc / RMS, gated Y = silu(acc1/RMS) * acc3/RMS.
+//     chunk c ^ (r & 7): row-wise and fragment reads are conflict-free.
+//   * one step ahead of its use, the workgroup turns the X slot into the
+//     matrix operand in place: each thread takes 8 consecutive k of one row,
+//     forms X*g in fp32 (bf16 dot2 with one lane of g zeroed: an exact
+//     product) rounded once to bf16, and adds X^2 to its row's sum of squares.
+//   * each wave multiplies a 64-row x 32-column block of one weight over a
+//     k-half (gated) or a k-quarter (plain) of every step with
+//     v_mfma_f32_32x32x16_bf16; B fragments come from ds_read_b64_tr_b16
+//     (gfx950's transposing LDS read): lane i of each 16-lane group receives
+//     4 consecutive k of column i.  Each W element is read from LDS once.
+//   * epilogue through LDS: the partial k-sums are added, Y = acc / RMS,
+//     gated Y = silu(acc1/RMS) * acc3/RMS.
 #include "rmm_device.h"
 
 namespace rmm {
@@ -43,8 +45,9 @@ constexpr uint32_t kStOutOfRange = 0x80000000u;
 // Ring depth per weight count: enough bytes in flight per CU, within 160 KB.
 template <int NW>
 struct StCfg {
-  static constexpr int RING = NW == 2 ? 5 : 6;
-  static constexpr int AHEAD = RING - 2;  // steps in flight ahead of the one multiplied
+  static constexpr int RING = NW == 2 ? 6 : 8;
+  static constexpr int AHEAD = RING - 2;  // steps issued ahead of the one multiplied
+  static constexpr int SUBS = NW == 2 ? 2 : 1;  // 16-deep sub-steps per wave per step
 };
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -84,16 +87,22 @@ struct StSmem {
   char w[StCfg<NW>::RING][NW][ST_W_BYTES];
   char x[StCfg<NW>::RING][ST_X_BYTES];
   char g[StCfg<NW>::RING][ST_G_BYTES];
-  float ss[2][ST_BM];
+  float ss[ST_BM];
   float inv[ST_BM];
 };
+// The epilogue reuses the W and X rings (contiguous) for 4 fp32 partial
+// blocks of 64 x 64.
+constexpr int ST_RED_BYTES = 4 * ST_BM * ST_BN * 4;
+static_assert(sizeof(StSmem<1>::w) + sizeof(StSmem<1>::x) >= ST_RED_BYTES, "ring too small");
+static_assert(sizeof(StSmem<2>::w) + sizeof(StSmem<2>::x) >= ST_RED_BYTES, "ring too small");
+static_assert(sizeof(StSmem<2>) <= 160 * 1024 && sizeof(StSmem<1>) <= 160 * 1024, "LDS");
 
 template <int NW>
 __global__ __launch_bounds__(ST_THREADS, 1) void stream_kernel(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ g, const bf16_t* __restrict__ W1,
     const bf16_t* __restrict__ W3, bf16_t* __restrict__ Y, float eps, int M, int64_t N,
     int64_t K) {
-  constexpr int RING = StCfg<NW>::RING, AHEAD = StCfg<NW>::AHEAD;
+  constexpr int RING = StCfg<NW>::RING, AHEAD = StCfg<NW>::AHEAD, SUBS = StCfg<NW>::SUBS;
   __shared__ __attribute__((aligned(1024))) StSmem<NW> sm;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int64_t n0 = (int64_t)blockIdx.x * ST_BN;
@@ -135,84 +144,106 @@ __global__ __launch_bounds__(ST_THREADS, 1) void stream_kernel(
     if (l < 8) st_lds_load16(lds_g + (uint32_t)(slot * ST_G_BYTES), (uint32_t)(16 * l), gs);
   };
 
-  // Wave roles.  Gated: wave w -> weight w>>2, row block (w>>1)&1, column
-  // block w&1.  Plain: wave w -> k-half w>>2 of the same 32x32 blocks.
-  const int wsel = NW == 2 ? (w >> 2) : 0;
-  const int set = w >> 2;  // accumulator set in the epilogue (weight or k-half)
-  const int rb = (w >> 1) & 1, cb = w & 1;
-  const bool owns_ss = cb == 0 && (NW == 1 || wsel == 0);
-  const int a_row = rb * 32 + (l & 31);
+  // Operand forming: thread -> row tid/8, logical k-chunk tid%8 of a step.
+  // The X slot is overwritten in place with bf16(X * g); the row's sum of
+  // squares accumulates in the thread (its row never changes).
+  const int f_row = tid >> 3, f_c = tid & 7;
+  const int f_off = f_row * 128 + ((f_c ^ (f_row & 7)) << 4);
+  float ss = 0.f;
+  auto form = [&](int step) {
+    const int slot = step % RING;
+    char* xp = &sm.x[slot][f_off];
+    const u32x4 xv = *(const u32x4*)xp;
+    const u32x4 gv = *(const u32x4*)&sm.g[slot][w * 128 + 16 * f_c];
+    u32x4 av;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const bf16x2 x = st_bf16x2(xv[d]);
+      av[d] = pack_bf16x2(__builtin_amdgcn_fdot2_f32_bf16(x, st_bf16x2(gv[d] & 0xffffu), 0.0f, false),
+                          __builtin_amdgcn_fdot2_f32_bf16(x, st_bf16x2(gv[d] & 0xffff0000u), 0.0f, false));
+      ss = __builtin_amdgcn_fdot2_f32_bf16(x, x, ss, false);
+    }
+    *(u32x4*)xp = av;
+  };
+
+  // Wave roles: partial set w>>1 (gated: weight set>>1, k-half set&1;
+  // plain: k-quarter set), column block w&1, both 32-row blocks.
+  const int set = w >> 1, cb = w & 1;
+  const int wsel = NW == 2 ? (set >> 1) : 0;
+  const int s_first = NW == 2 ? 2 * (set & 1) : set;
+  const int a_lo = l & 31;  // fragment row within a 32-row block
   const int bG = l >> 4, bi = l & 15;
   const int b_k = 8 * (bG >> 1) + (bi >> 2), b_n = cb * 32 + 16 * (bG & 1) + 4 * (bi & 3);
   const int b_off = b_k * 128 + (((b_n >> 3) ^ (2 * (b_k & 3))) << 4) + ((b_n & 7) << 1);
-  floatx16 acc;
+  floatx16 acc[2];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
-  float ss = 0.f;
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[rb][e] = 0.f;
 
-  auto mfma_step = [&](int step) {
-    const int slot = step % RING;
+  // Steps 0 .. AHEAD-1 in flight, step 0 formed, before the loop.
+  // Iteration kt issues step kt+AHEAD into the slot last read in iteration
+  // kt-2 (the barrier of iteration kt-1 orders that), waits until only the
+  // AHEAD-1 newest steps may be outstanding (step kt+1 has landed for this
+  // wave); after the barrier (every wave's part of step kt+1 has landed and
+  // iteration kt-1 is finished everywhere) it reads the operands of step kt
+  // (formed in iteration kt-1), forms step kt+1 and multiplies step kt.
+  // Steps past the last one read zeros (range checks).
+  for (int st = 0; st < AHEAD; ++st) issue_step(st);
+  ST_WAIT_VMCNT((AHEAD - 1) * (NW + 2));
+  __syncthreads();
+  form(0);
+  for (int kt = 0; kt < nk; ++kt) {
+    issue_step(kt + AHEAD);
+    ST_WAIT_VMCNT((AHEAD - 1) * (NW + 2));
+    __syncthreads();
+    const int slot = kt % RING;
     const char* x_lds = &sm.x[slot][0];
-    const char* g_lds = &sm.g[slot][w * 128];
     const lds_char* b_lds = (const lds_char*)&sm.w[slot][wsel][0];
+    u32x4 av[SUBS][2], bv[SUBS];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      if (NW == 1 && (s >> 1) != set) continue;
+    for (int i = 0; i < SUBS; ++i) {
+      const int s = s_first + i;
       const int kc = 2 * s + (l >> 5);
-      const u32x4 xv = *(const u32x4*)(x_lds + a_row * 128 + ((kc ^ (a_row & 7)) << 4));
-      const u32x4 gv = *(const u32x4*)(g_lds + 16 * kc);
-      u32x4 av;
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const bf16x2 x = st_bf16x2(xv[d]);
-        av[d] = pack_bf16x2(__builtin_amdgcn_fdot2_f32_bf16(x, st_bf16x2(gv[d] & 0xffffu), 0.0f, false),
-                            __builtin_amdgcn_fdot2_f32_bf16(x, st_bf16x2(gv[d] & 0xffff0000u), 0.0f, false));
-        if (owns_ss) ss = __builtin_amdgcn_fdot2_f32_bf16(x, x, ss, false);
-      }
+      for (int rb = 0; rb < 2; ++rb)
+        av[i][rb] = *(const u32x4*)(x_lds + (rb * 32 + a_lo) * 128 + ((kc ^ (a_lo & 7)) << 4));
       const u32x2 lo = __builtin_bit_cast(
           u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(b_lds + b_off + 16 * s * 128)));
       const u32x2 hi = __builtin_bit_cast(
           u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(b_lds + b_off + (16 * s + 4) * 128)));
-      const u32x4 bv = {lo[0], lo[1], hi[0], hi[1]};
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
-                                                    __builtin_bit_cast(bf16x8, bv), acc, 0, 0, 0);
+      bv[i] = u32x4{lo[0], lo[1], hi[0], hi[1]};
     }
-  };
-
-  // Steps 0 .. AHEAD-1 in flight before the loop.  Iteration kt issues step
-  // kt+AHEAD into the slot last read in iteration kt-2 (the barrier of
-  // iteration kt-1 orders that), waits until only the AHEAD newer steps'
-  // transfers may be outstanding (step kt has landed for this wave), and
-  // after the barrier (every wave's part of step kt has landed) multiplies
-  // step kt.  Steps past the last one read zeros (range checks).
-  for (int st = 0; st < AHEAD; ++st) issue_step(st);
-  for (int kt = 0; kt < nk; ++kt) {
-    issue_step(kt + AHEAD);
-    ST_WAIT_VMCNT(AHEAD * (NW + 2));
-    __syncthreads();
-    mfma_step(kt);
+    if (kt + 1 < nk) form(kt + 1);
+#pragma unroll
+    for (int i = 0; i < SUBS; ++i)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+        acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[i][rb]),
+                                                          __builtin_bit_cast(bf16x8, bv[i]),
+                                                          acc[rb], 0, 0, 0);
   }
   ST_WAIT_VMCNT(0);
 
-  // Row sums of squares: owners hold row (l&31) over k-half (l>>5) of their
-  // sub-steps; plain layouts split k between two wave groups.
-  ss += __shfl_xor(ss, 32);
+  // Row sums of squares: the 8 threads of a row hold disjoint k-chunks.
+  ss += __shfl_xor(ss, 1);
+  ss += __shfl_xor(ss, 2);
+  ss += __shfl_xor(ss, 4);
+  if (f_c == 0) sm.ss[f_row] = ss;
   __syncthreads();  // every wave is done with the rings before they are reused
-  if (NW == 2 && tid < ST_BM) sm.ss[1][tid] = 0.f;
-  if (owns_ss && l < 32) sm.ss[NW == 2 ? 0 : set][a_row] = ss;
-  // Accumulators to LDS as [set][row][col] fp32, reusing the W ring.
-  // 32x32 layout: lane l holds column l%32 and, for register 4 jj + r, row
-  // 8 jj + 4 (l/32) + r.
+  // Partial blocks to LDS as [set][row][col] fp32.  32x32 layout: lane l
+  // holds column l%32 and, for register 4 jj + r, row 8 jj + 4 (l/32) + r.
   float* red = (float*)&sm.w[0][0][0];
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj)
+  for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = rb * 32 + 8 * jj + 4 * (l >> 5) + r, col = cb * 32 + (l & 31);
-      red[(set * ST_BM + row) * ST_BN + col] = acc[4 * jj + r];
-    }
-  __syncthreads();
-  if (tid < ST_BM) sm.inv[tid] = inv_rms(sm.ss[0][tid] + sm.ss[1][tid], K, eps);
+    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = rb * 32 + 8 * jj + 4 * (l >> 5) + r, col = cb * 32 + (l & 31);
+        red[(set * ST_BM + row) * ST_BN + col] = acc[rb][4 * jj + r];
+      }
+  if (tid < ST_BM) sm.inv[tid] = inv_rms(sm.ss[tid], K, eps);
   __syncthreads();
 
   // Epilogue: thread -> row tid>>3, columns 8 (tid&7) .. +7.
@@ -220,20 +251,29 @@ __global__ __launch_bounds__(ST_THREADS, 1) void stream_kernel(
   const int64_t n = n0 + oc;
   if (orow < M && n < N) {
     const float inv = sm.inv[orow];
+    float p[4][8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const floatx4* src = (const floatx4*)(red + (q * ST_BM + orow) * ST_BN + oc);
+      const floatx4 u = src[0], v = src[1];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        p[q][e] = u[e];
+        p[q][4 + e] = v[e];
+      }
+    }
     u32x4 out;
 #pragma unroll
     for (int c = 0; c < 8; c += 2) {
-      const float* r0 = red + (0 * ST_BM + orow) * ST_BN + oc + c;
-      const float* r1 = red + (1 * ST_BM + orow) * ST_BN + oc + c;
-      float y0, y1;
-      if (NW == 2) {
-        y0 = silu_gate(r0[0] * inv, r1[0] * inv);
-        y1 = silu_gate(r0[1] * inv, r1[1] * inv);
-      } else {
-        y0 = (r0[0] + r1[0]) * inv;
-        y1 = (r0[1] + r1[1]) * inv;
+      float y[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        if (NW == 2)
+          y[e] = silu_gate((p[0][c + e] + p[1][c + e]) * inv, (p[2][c + e] + p[3][c + e]) * inv);
+        else
+          y[e] = ((p[0][c + e] + p[1][c + e]) + (p[2][c + e] + p[3][c + e])) * inv;
       }
-      out[c >> 1] = pack_bf16x2(y0, y1);
+      out[c >> 1] = pack_bf16x2(y[0], y[1]);
     }
     *(u32x4*)(Y + (int64_t)orow * N + n) = out;
   }

@@ -114,7 +114,9 @@ def test_status_strings(lib):
 
 def test_variant_selection():
     import torch
-    assert tpa.plan(16, 6144, 4096)[1:] == ("decode", 8)
+    assert tpa.plan(16, 6144, 4096)[1:] == ("decode", 4)   # 48 tiles x 4 = 192 workgroups
+    assert tpa.plan(16, 1024, 4096)[1:] == ("decode", 32)  # 8 tiles: 32 granules of 128
+    assert tpa.plan(16, 32768, 4096)[1:] == ("decode", 1)  # 256 tiles already fill the CUs
     assert tpa.plan(16, 6144, 4096, with_workspace=False)[1:] == ("decode", 1)
     assert tpa.plan(64, 14336, 4096, gated=True)[1] == "stream"
     assert tpa.plan(16, 14336, 4096, gated=True)[1] == "stream"

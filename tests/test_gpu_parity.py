@@ -42,6 +42,8 @@ EXACT_CASES = [
     (1, 8, 8, "bf16", "decode", 0),
     (32, 1024, 1032, "bf16", "decode", 5),
     (17, 1000, 520, "bf16", "decode", 4),
+    (32, 4096, 1032, "bf16", "decode", 1),   # A operand re-staged in 8 segments
+    (16, 8192, 264, "bf16", "decode", 2),    # 8 waves, 4 segments per split
     (256, 64, 256, "bf16", "prefill", 0),
     (300, 200, 264, "bf16", "prefill", 0),
     (513, 1032, 520, "bf16", "prefill", 0),

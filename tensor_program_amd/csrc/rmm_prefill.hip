@@ -49,26 +49,6 @@ __device__ __forceinline__ int pf_b_off(int k, int n) {
   return k * 512 + (((n >> 3) ^ (2 * (k & 3))) << 4) + ((n & 7) << 1);
 }
 
-// X of one k-step for this thread: rows (t>>3) + 64 i, chunk t&7, and g.
-struct PfA {
-  u32x4 a[4];
-  u32x4 g;
-};
-
-__device__ __forceinline__ void pf_load_a(PfA& st, __amdgpu_buffer_rsrc_t xr,
-                                          __amdgpu_buffer_rsrc_t gr, int64_t m0, int64_t k0,
-                                          int64_t M, int64_t K, int tid) {
-  const int64_t ka = k0 + 8 * (tid & 7);
-  const bool ka_ok = ka < K;  // K % 8 == 0: a chunk is all in or all out
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t m = m0 + (tid >> 3) + 64 * i;
-    const uint32_t off = (ka_ok && m < M) ? (uint32_t)((m * K + ka) * 2) : kPfOutOfRange;
-    st.a[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
-  }
-  st.g = __builtin_amdgcn_raw_buffer_load_b128(gr, ka_ok ? (uint32_t)(ka * 2) : kPfOutOfRange, 0, 0);
-}
-
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // Raw buffer resource (stride 0, 32-bit data format) for [base, base+bytes).
@@ -80,6 +60,44 @@ __device__ __forceinline__ i32x4 pf_rsrc(const void* base, uint32_t bytes) {
   r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
   r[3] = 0x00020000;
   return r;
+}
+
+// X of one k-step for this thread: rows (t>>3) + 64 i, chunk t&7, and g.
+struct PfA {
+  u32x4 a[4];
+  u32x4 g;
+};
+
+// 16 bytes per lane into registers.  Issued as inline asm, like the W
+// transfers, so that the compiler does not place its own (too strict) wait
+// for these registers: pf_wait_a below waits for exactly the loads that
+// must have landed and is the only producer the compiler sees for them.
+__device__ __forceinline__ u32x4 pf_load16(uint32_t voff, i32x4 rsrc) {
+  u32x4 v;
+  asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(v) : "v"(voff), "s"(rsrc));
+  return v;
+}
+
+__device__ __forceinline__ void pf_load_a(PfA& st, i32x4 xr, i32x4 gr, int64_t m0, int64_t k0,
+                                          int64_t M, int64_t K, int tid) {
+  const int64_t ka = k0 + 8 * (tid & 7);
+  const bool ka_ok = ka < K;  // K % 8 == 0: a chunk is all in or all out
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t m = m0 + (tid >> 3) + 64 * i;
+    const uint32_t off = (ka_ok && m < M) ? (uint32_t)((m * K + ka) * 2) : kPfOutOfRange;
+    st.a[i] = pf_load16(off, xr);
+  }
+  st.g = pf_load16(ka_ok ? (uint32_t)(ka * 2) : kPfOutOfRange, gr);
+}
+
+// Wait until at most N vector-memory loads are outstanding; the registers
+// of st are in/out operands, so no use of them moves above the wait.
+template <int N>
+__device__ __forceinline__ void pf_wait_a(PfA& st) {
+  asm volatile("s_waitcnt vmcnt(%5)"
+               : "+v"(st.a[0]), "+v"(st.a[1]), "+v"(st.a[2]), "+v"(st.a[3]), "+v"(st.g)
+               : "n"(N));
 }
 
 // One 16-byte-per-lane load straight into LDS: lane l's data lands at
@@ -182,8 +200,9 @@ __device__ __forceinline__ void pf_mfma(const PfFrag& f, floatx16 (&acc)[4][2]) 
 // (st) is scaled into a_nxt.  Fragments of sub-step s+1 are read while the
 // MFMAs of sub-step s run; the staging is fenced behind the first two
 // sub-steps.
+template <int VM>
 __device__ __forceinline__ void pf_step(const char* a_cur, const lds_char* b_cur, char* a_nxt,
-                                        const PfA& st, floatx16 (&acc)[4][2], float (&ss)[4],
+                                        PfA& st, floatx16 (&acc)[4][2], float (&ss)[4],
                                         int a_base, int b0, int b1, int tid) {
   PfFrag fa, fb;
   pf_read_frags(fa, a_cur, b_cur, a_base, b0, b1, 0);
@@ -192,23 +211,11 @@ __device__ __forceinline__ void pf_step(const char* a_cur, const lds_char* b_cur
   pf_read_frags(fa, a_cur, b_cur, a_base, b0, b1, 2);
   pf_mfma(fb, acc);
   __builtin_amdgcn_sched_barrier(0);
+  pf_wait_a<VM>(st);
   pf_store_a(st, a_nxt, ss, tid, 0);
   pf_read_frags(fb, a_cur, b_cur, a_base, b0, b1, 3);
   pf_mfma(fa, acc);
   pf_store_a(st, a_nxt, ss, tid, 2);
-  pf_mfma(fb, acc);
-}
-
-__device__ __forceinline__ void pf_step_last(const char* a_cur, const lds_char* b_cur,
-                                             floatx16 (&acc)[4][2], int a_base, int b0, int b1) {
-  PfFrag fa, fb;
-  pf_read_frags(fa, a_cur, b_cur, a_base, b0, b1, 0);
-  pf_read_frags(fb, a_cur, b_cur, a_base, b0, b1, 1);
-  pf_mfma(fa, acc);
-  pf_read_frags(fa, a_cur, b_cur, a_base, b0, b1, 2);
-  pf_mfma(fb, acc);
-  pf_read_frags(fb, a_cur, b_cur, a_base, b0, b1, 3);
-  pf_mfma(fa, acc);
   pf_mfma(fb, acc);
 }
 
@@ -241,8 +248,8 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_kernel(
   const int tn = (t % group) / gm;
   const int64_t m0 = (int64_t)tm * PF_BM, n0 = (int64_t)tn * PF_BN;
 
-  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc((void*)X, 0, (int)(M * K * 2), 0x00020000);
-  const __amdgpu_buffer_rsrc_t gr = __builtin_amdgcn_make_buffer_rsrc((void*)g, 0, (int)(K * 2), 0x00020000);
+  const i32x4 xr = pf_rsrc(X, (uint32_t)(M * K * 2));
+  const i32x4 gr = pf_rsrc(g, (uint32_t)(K * 2));
   lds_char* b0s = (lds_char*)b_s0;
   lds_char* b1s = (lds_char*)b_s1;
   const uint32_t b0a = (uint32_t)(uintptr_t)b0s, b1a = (uint32_t)(uintptr_t)b1s;
@@ -275,39 +282,36 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_kernel(
   // past the last step read zeros (buffer range check), so the loop body has
   // no branches; it is unrolled by two so each register stage is static.
   // The 5 X/g loads of a step are issued after its W transfers, so
-  // vmcnt <= 5 means those transfers have landed.
+  // vmcnt <= 5 means those transfers have landed; before X of the next step
+  // is scaled, vmcnt <= 9 (this iteration's 4 W and 5 X/g loads may still
+  // be in flight) means it has.  Both waits are explicit: the compiler sees
+  // none of these loads.
   PfA sa, sb;
   pf_dma_b(b0a, dma, W1, 0, N, K, w);
   pf_load_a(sa, xr, gr, m0, 0, M, K, tid);
   pf_load_a(sb, xr, gr, m0, PF_BK, M, K, tid);
+  pf_wait_a<5>(sa);
   pf_store_a(sa, a_s0, ss, tid, 0);
   pf_store_a(sa, a_s0, ss, tid, 2);
   PF_WAIT_VMCNT(0);
   __syncthreads();
 
-  int kt = 0;
-  for (; kt + 2 < nk; kt += 2) {
+  // Whole pairs of steps: with an odd step count the last one multiplies
+  // zeros (every operand past K reads as zero), which leaves the sums as
+  // they are and keeps the accumulators in one place.
+  for (int kt = 0; kt < nk; kt += 2) {
     pf_dma_b(b1a, dma, W1, (int64_t)(kt + 1) * PF_BK, N, K, w);
     pf_load_a(sa, xr, gr, m0, (int64_t)(kt + 2) * PF_BK, M, K, tid);
-    pf_step(a_s0, b0s, a_s1, sb, acc, ss, a_base, bo0, bo1, tid);
+    pf_step<9>(a_s0, b0s, a_s1, sb, acc, ss, a_base, bo0, bo1, tid);
     PF_WAIT_VMCNT(5);
     __syncthreads();
     pf_dma_b(b0a, dma, W1, (int64_t)(kt + 2) * PF_BK, N, K, w);
     pf_load_a(sb, xr, gr, m0, (int64_t)(kt + 3) * PF_BK, M, K, tid);
-    pf_step(a_s1, b1s, a_s0, sa, acc, ss, a_base, bo0, bo1, tid);
+    pf_step<9>(a_s1, b1s, a_s0, sa, acc, ss, a_base, bo0, bo1, tid);
     PF_WAIT_VMCNT(5);
     __syncthreads();
   }
-  // Tail: stage 0 holds step kt; sb holds X of step kt+1 (if it exists).
-  if (kt + 1 < nk) {
-    pf_dma_b(b1a, dma, W1, (int64_t)(kt + 1) * PF_BK, N, K, w);
-    pf_step(a_s0, b0s, a_s1, sb, acc, ss, a_base, bo0, bo1, tid);
-    PF_WAIT_VMCNT(0);
-    __syncthreads();
-    pf_step_last(a_s1, b1s, acc, a_base, bo0, bo1);
-  } else {
-    pf_step_last(a_s0, b0s, acc, a_base, bo0, bo1);
-  }
+  PF_WAIT_VMCNT(0);
 
   // Row sums of squares: the 8 lanes tid&7 = 0..7 share rows (tid>>3) + 64 i.
 #pragma unroll

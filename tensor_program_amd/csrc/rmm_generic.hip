@@ -32,15 +32,18 @@ __global__ __launch_bounds__(GEN_THREADS) void generic_kernel(
   const int64_t n0 = (int64_t)blockIdx.x * GEN_COLS;
   const int64_t m0 = (int64_t)blockIdx.y * GEN_ROWS;
 
-  // Row sums of squares of raw X (32 threads per row).
+  // Row sums of squares of raw X (32 threads per row, 8 loads in flight).
   {
     const int r = tid / 32, j = tid % 32;
     float ss = 0.0f;
     if (m0 + r < M) {
       const T* xr = X + (m0 + r) * K;
-      for (int64_t k = j; k < K; k += 32) {
-        float x = load_f32(xr + k);
-        ss += x * x;
+      for (int64_t k = j; k < K; k += 256) {
+        float x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = (k + 32 * u < K) ? load_f32(xr + k + 32 * u) : 0.0f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) ss += x[u] * x[u];
       }
     }
     ss_s[r][j] = ss;
@@ -59,6 +62,21 @@ __global__ __launch_bounds__(GEN_THREADS) void generic_kernel(
 #pragma unroll
   for (int i = 0; i < GEN_ROWS; ++i) acc1[i] = acc3[i] = 0.0f;
 
+  // W of a chunk: thread (c, s) loads k = s, s+4, ..., s+60 of column c,
+  // all at once; the next chunk's loads are in flight while this one is
+  // multiplied.
+  constexpr int NU = GEN_KC / 4;
+  auto load_w = [&](int64_t k0, float (&w1)[NU], float (&w3)[NU]) {
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int64_t k = k0 + s + 4 * u;
+      const bool ok = col_ok && k < K;
+      w1[u] = ok ? load_f32(W1 + k * N + n) : 0.0f;
+      w3[u] = (GATED && ok) ? load_f32(W3 + k * N + n) : 0.0f;
+    }
+  };
+  float w1c[NU], w3c[NU];
+  load_w(0, w1c, w3c);
   for (int64_t k0 = 0; k0 < K; k0 += GEN_KC) {
     __syncthreads();
     // Stage X*g for the chunk (fp32, no rounding).
@@ -68,18 +86,20 @@ __global__ __launch_bounds__(GEN_THREADS) void generic_kernel(
       a_s[r][kk] = (m < M && k < K) ? load_f32(X + m * K + k) * load_f32(g + k) : 0.0f;
     }
     __syncthreads();
-    if (col_ok) {
-      const int64_t kend = (K - k0 < GEN_KC) ? (K - k0) : GEN_KC;
-      for (int kk = s; kk < kend; kk += 4) {
-        const float w1 = load_f32(W1 + (k0 + kk) * N + n);
-        float w3 = 0.0f;
-        if (GATED) w3 = load_f32(W3 + (k0 + kk) * N + n);
+    float w1n[NU], w3n[NU];
+    load_w(k0 + GEN_KC, w1n, w3n);
 #pragma unroll
-        for (int i = 0; i < GEN_ROWS; ++i) {
-          acc1[i] += a_s[i][kk] * w1;
-          if (GATED) acc3[i] += a_s[i][kk] * w3;
-        }
+    for (int u = 0; u < NU; ++u) {
+#pragma unroll
+      for (int i = 0; i < GEN_ROWS; ++i) {
+        acc1[i] += a_s[i][s + 4 * u] * w1c[u];
+        if (GATED) acc3[i] += a_s[i][s + 4 * u] * w3c[u];
       }
+    }
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      w1c[u] = w1n[u];
+      w3c[u] = w3n[u];
     }
   }
 

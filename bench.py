@@ -125,6 +125,8 @@ def main():
                     help="untimed calls for this long before the warm-up steps (clock ramp)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds for the oracle leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-unfused", action="store_true",
+                    help="skip timing the unfused two-kernel program beside the fused call")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -196,31 +198,47 @@ def main():
             tpa.rmsnorm_matmul(s["X"], s["g"], s["W1"], wl.eps, out=s["Y"],
                                variant=args.variant, splits=args.splits, workspace=ws)
 
-    with torch.cuda.stream(stream):
-        for s in sets:  # eager warm-up of every set (also loads the code objects)
-            call(s)
-    torch.cuda.synchronize()
-
-    graph = None
-    if not args.no_graph:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=stream):
-            for s in sets:
-                call(s)
-        torch.cuda.synchronize()
-
-    def run_steps(n):
-        """n steps = n calls, rotating through the sets."""
+    def make_runner(fn, use_graph):
+        """Returns run(n): n calls of fn(i) rotating over the R sets, replayed
+        from a HIP graph of R calls when use_graph."""
         with torch.cuda.stream(stream):
-            if graph is not None:
-                reps = n // R
-                for _ in range(reps):
-                    graph.replay()
-                for i in range(n - reps * R):
-                    call(sets[i])
-            else:
-                for i in range(n):
-                    call(sets[i % R])
+            for i in range(R):  # eager warm-up of every set (also loads the code objects)
+                fn(i)
+        torch.cuda.synchronize()
+        g = None
+        if use_graph:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(R):
+                    fn(i)
+            torch.cuda.synchronize()
+
+        def run(n):
+            with torch.cuda.stream(stream):
+                if g is not None:
+                    reps = n // R
+                    for _ in range(reps):
+                        g.replay()
+                    for i in range(n - reps * R):
+                        fn(i)
+                else:
+                    for i in range(n):
+                        fn(i % R)
+        return run
+
+    def time_steps(run, n):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            start.record(stream)
+        run(n)
+        with torch.cuda.stream(stream):
+            end.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end)
+
+    run_steps = make_runner(lambda i: call(sets[i]), not args.no_graph)
+    graph = None if args.no_graph else True
 
     steps = max(R, (args.steps // R) * R)
     warm = max(R, (args.warmup // R) * R) if args.warmup > 0 else 0
@@ -237,17 +255,48 @@ def main():
     run_steps(warm)
     torch.cuda.synchronize()
     log(f"timing {steps} steps")
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    with torch.cuda.stream(stream):
-        start.record(stream)
-    run_steps(steps)
-    with torch.cuda.stream(stream):
-        end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end)
+    ms = time_steps(run_steps, steps)
     per_launch_s = ms / 1e3 / steps
     log(f"{ms:.3f} ms for {steps} steps: {per_launch_s * 1e6:.2f} us/step")
+
+    # The unfused program the fused kernel replaces (the comparison of the
+    # worked example): an RMSNorm kernel writes the normalised X, then a
+    # product reads it back -- our plain-product kernels, and the vendor GEMM.
+    unfused = None
+    if not args.no_unfused:
+        xn = [torch.empty_like(s["X"]) for s in sets]
+
+        def unfused_ours(i):
+            s = sets[i]
+            tpa.rmsnorm(s["X"], s["g"], wl.eps, out=xn[i])
+            if wl.gated:
+                tpa.gated_matmul(xn[i], s["W1"], s["W3"], out=s["Y"], workspace=ws)
+            else:
+                tpa.matmul(xn[i], s["W1"], out=s["Y"], workspace=ws)
+
+        def unfused_vendor(i):
+            s = sets[i]
+            tpa.rmsnorm(s["X"], s["g"], wl.eps, out=xn[i])
+            if wl.gated:
+                torch.mul(torch.nn.functional.silu(torch.matmul(xn[i], s["W1"])),
+                          torch.matmul(xn[i], s["W3"]), out=s["Y"])
+            else:
+                torch.matmul(xn[i], s["W1"], out=s["Y"])
+
+        run_u = make_runner(unfused_ours, not args.no_graph)
+        run_u(warm)
+        ms_u = time_steps(run_u, steps)
+        run_v = make_runner(unfused_vendor, False)  # library GEMMs stay out of graphs
+        run_v(warm)
+        ms_v = time_steps(run_v, steps)
+        unfused = {
+            "ms_per_step": ms_u / steps, "fused_speedup": ms_u / ms,
+            "vendor_gemm_ms_per_step": ms_v / steps, "fused_speedup_vs_vendor_gemm": ms_v / ms,
+            "normalised_x_bytes": 2 * wl.M * wl.K * wl.elem_bytes,
+            "note": "rmm_rmsnorm writes X*g/RMS to memory, then rmm_matmul (this library's "
+                    "kernels) or torch.matmul (hipBLASLt) reads it back"}
+        log(f"unfused: {ms_u / steps * 1e3:.2f} us/step (ours), {ms_v / steps * 1e3:.2f} us/step "
+            f"(vendor GEMM); fused {ms / steps * 1e3:.2f}")
 
     gbs = per_set / per_launch_s / 1e9
     tflops = wl.flops() / per_launch_s / 1e12
@@ -280,7 +329,7 @@ def main():
                    "rotating_input_sets": R, "hip_graph": graph is not None,
                    "clock_settle_calls": settle_calls},
         "tflops": tflops, "hbm_gbs_algorithmic": gbs,
-        "roofline": roof, "cpu_baseline": cpu,
+        "roofline": roof, "cpu_baseline": cpu, "unfused_baseline": unfused,
     }
     print(json.dumps(line), flush=True)
 

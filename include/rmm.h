@@ -132,6 +132,32 @@ rmm_status rmsnorm_gated_mlp_ex(const void* X, const void* g, const void* W1, co
                                 rmm_dtype dtype, rmm_variant variant, int splits, void* ws,
                                 size_t ws_bytes, hipStream_t stream);
 
+/* The unfused program, for comparison.  The page that introduces the worked
+ * example ("核心概念 / μGraph示例") contrasts the fused kernel with what
+ * existing systems run: an RMSNorm kernel that writes the normalised
+ * activations to device memory, then a MatMul kernel that reads them back.
+ * These three calls are that program, built from the same kernels:
+ *
+ *   rmm_rmsnorm:      Xn = RMSNorm(X; g, eps), M x K, same dtype as X (bf16:
+ *                     X*g*(1/RMS) formed in fp32, rounded once to nearest even).
+ *   rmm_matmul:       Y = X W (no gain, no 1/RMS scale); the variants, split
+ *                     counts and workspace rules of rmsnorm_matmul apply.
+ *   rmm_gated_matmul: Y = silu(X W1) * (X W3).
+ *
+ * rmm_rmsnorm followed by rmm_matmul computes the same Y as rmsnorm_matmul up to
+ * the extra rounding of Xn.  Validation order and error codes are those of
+ * the fused calls (rmm_rmsnorm: RMM_ERR_NULL, RMM_ERR_SHAPE for M < 0 or
+ * K <= 0, RMM_ERR_EPS, RMM_ERR_DTYPE, RMM_ERR_ALIAS when Xn overlaps X or
+ * g; any alignment and K are accepted).  Xn may not be X: the kernel reads
+ * each row twice. */
+rmm_status rmm_rmsnorm(const void* X, const void* g, void* Xn, float eps, int64_t M, int64_t K,
+                       rmm_dtype dtype, hipStream_t stream);
+rmm_status rmm_matmul(const void* X, const void* W, void* Y, int64_t M, int64_t N, int64_t K,
+                      rmm_dtype dtype, void* ws, size_t ws_bytes, hipStream_t stream);
+rmm_status rmm_gated_matmul(const void* X, const void* W1, const void* W3, void* Y, int64_t M,
+                            int64_t N, int64_t K, rmm_dtype dtype, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
+
 /* Workspace bytes the call with these arguments would use (0 if none).  The
  * plain entry points use variant = AUTO, splits = 0.  Returns 0 for
  * arguments that would fail validation. */

@@ -40,6 +40,12 @@ def load(path: str = _LIB):
     lib.rmm_oracle_rmsnorm_matmul_f64.restype = ctypes.c_int
     lib.rmm_oracle_rmsnorm_gated_mlp_f64.argtypes = [vp, vp, vp, vp, dbl, i64, i64, i64, vp]
     lib.rmm_oracle_rmsnorm_gated_mlp_f64.restype = ctypes.c_int
+    lib.rmm_oracle_rmsnorm_f64.argtypes = [vp, vp, dbl, i64, i64, vp]
+    lib.rmm_oracle_rmsnorm_f64.restype = ctypes.c_int
+    lib.rmm_oracle_matmul_f64.argtypes = [vp, vp, i64, i64, i64, vp]
+    lib.rmm_oracle_matmul_f64.restype = ctypes.c_int
+    lib.rmm_oracle_gated_matmul_f64.argtypes = [vp, vp, vp, i64, i64, i64, vp]
+    lib.rmm_oracle_gated_matmul_f64.restype = ctypes.c_int
     return lib
 
 
@@ -84,6 +90,48 @@ def rmsnorm_gated_mlp(X, g, W1, W3, eps, lib=None) -> np.ndarray:
     Y = np.empty((M, N), np.float64)
     rc = lib.rmm_oracle_rmsnorm_gated_mlp_f64(_p(X), _p(g), _p(W1), _p(W3), float(eps), M, N,
                                               K, _p(Y))
+    if rc != 0:
+        raise ValueError(f"oracle error {rc}")
+    return Y
+
+
+def rmsnorm(X, g, eps, lib=None) -> np.ndarray:
+    """The normalised, gained rows (X / r) * g in fp64 -- the tensor the fused
+    kernels never write, produced by the first kernel of the unfused program."""
+    lib = lib or _default()
+    X, g = _d(X), _d(g)
+    M, K = X.shape
+    assert g.shape == (K,)
+    out = np.empty((M, K), np.float64)
+    rc = lib.rmm_oracle_rmsnorm_f64(_p(X), _p(g), float(eps), M, K, _p(out))
+    if rc != 0:
+        raise ValueError(f"oracle error {rc}")
+    return out
+
+
+def matmul(A, B, lib=None) -> np.ndarray:
+    """Y = A @ B in fp64, the oracle's own i-k-j loops."""
+    lib = lib or _default()
+    A, B = _d(A), _d(B)
+    M, K = A.shape
+    K2, N = B.shape
+    assert K2 == K
+    Y = np.empty((M, N), np.float64)
+    rc = lib.rmm_oracle_matmul_f64(_p(A), _p(B), M, N, K, _p(Y))
+    if rc != 0:
+        raise ValueError(f"oracle error {rc}")
+    return Y
+
+
+def gated_matmul(A, W1, W3, lib=None) -> np.ndarray:
+    """Y = silu(A @ W1) * (A @ W3) in fp64."""
+    lib = lib or _default()
+    A, W1, W3 = _d(A), _d(W1), _d(W3)
+    M, K = A.shape
+    K2, N = W1.shape
+    assert K2 == K and W3.shape == W1.shape
+    Y = np.empty((M, N), np.float64)
+    rc = lib.rmm_oracle_gated_matmul_f64(_p(A), _p(W1), _p(W3), M, N, K, _p(Y))
     if rc != 0:
         raise ValueError(f"oracle error {rc}")
     return Y

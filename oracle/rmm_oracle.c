@@ -28,6 +28,11 @@
  * the page does not define it, the reading is SwiGLU):
  *   Z1 = Nrm * W1,  Z3 = Nrm * W3,  Y = Z1 / (1 + exp(-Z1)) * Z3.
  *
+ * The steps are also exported one by one (rmm_oracle_rmsnorm_f64: steps 1-2,
+ * rmm_oracle_matmul_f64: step 3, rmm_oracle_gated_matmul_f64: the two
+ * products and the gate), because the unfused program is itself measured:
+ * it is the comparison point of the same section.
+ *
  * Build: gcc -O2 -fopenmp -ffp-contract=off (no fast-math).  OpenMP splits
  * rows across threads only for timing; each output element is computed by
  * one thread in the same order as the serial program.
@@ -92,31 +97,64 @@ int rmm_oracle_rmsnorm_matmul_f64(const double* X, const double* g, const double
   return 0;
 }
 
-int rmm_oracle_rmsnorm_gated_mlp_f64(const double* X, const double* g, const double* W1,
-                                     const double* W3, double eps, int64_t M, int64_t N,
-                                     int64_t K, double* Y) {
-  if (M < 0 || N < 0 || K <= 0) return 1;
-  size_t mn = (size_t)(M * N > 0 ? M * N : 1);
-  double* r = (double*)malloc(sizeof(double) * (size_t)(M > 0 ? M : 1));
-  double* Nrm = (double*)malloc(sizeof(double) * (size_t)(M > 0 ? M * K : 1));
-  double* Z3 = (double*)malloc(sizeof(double) * mn);
-  if (!r || !Nrm || !Z3) {
-    free(r);
-    free(Nrm);
-    free(Z3);
-    return 2;
-  }
-  row_rms(X, M, K, eps, r);
-  normalise(X, g, r, M, K, Nrm);
-  matmul(Nrm, W1, M, N, K, Y); /* Y holds Z1 until the gate below */
-  matmul(Nrm, W3, M, N, K, Z3);
+/* Gated products on activations A: Y = silu(A W1) * (A W3). */
+static int gated_products(const double* A, const double* W1, const double* W3, int64_t M,
+                          int64_t N, int64_t K, double* Y) {
+  double* Z3 = (double*)malloc(sizeof(double) * (size_t)(M * N > 0 ? M * N : 1));
+  if (!Z3) return 2;
+  matmul(A, W1, M, N, K, Y); /* Y holds Z1 until the gate below */
+  matmul(A, W3, M, N, K, Z3);
 #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < M * N; ++i) {
     const double z1 = Y[i];
     Y[i] = z1 / (1.0 + exp(-z1)) * Z3[i];
   }
-  free(r);
-  free(Nrm);
   free(Z3);
   return 0;
+}
+
+int rmm_oracle_rmsnorm_gated_mlp_f64(const double* X, const double* g, const double* W1,
+                                     const double* W3, double eps, int64_t M, int64_t N,
+                                     int64_t K, double* Y) {
+  if (M < 0 || N < 0 || K <= 0) return 1;
+  double* r = (double*)malloc(sizeof(double) * (size_t)(M > 0 ? M : 1));
+  double* Nrm = (double*)malloc(sizeof(double) * (size_t)(M > 0 ? M * K : 1));
+  if (!r || !Nrm) {
+    free(r);
+    free(Nrm);
+    return 2;
+  }
+  row_rms(X, M, K, eps, r);
+  normalise(X, g, r, M, K, Nrm);
+  const int rc = gated_products(Nrm, W1, W3, M, N, K, Y);
+  free(r);
+  free(Nrm);
+  return rc;
+}
+
+/* Steps 1-2 alone: the normalised, gained rows, M x K. */
+int rmm_oracle_rmsnorm_f64(const double* X, const double* g, double eps, int64_t M, int64_t K,
+                           double* Nrm) {
+  if (M < 0 || K <= 0) return 1;
+  double* r = (double*)malloc(sizeof(double) * (size_t)(M > 0 ? M : 1));
+  if (!r) return 2;
+  row_rms(X, M, K, eps, r);
+  normalise(X, g, r, M, K, Nrm);
+  free(r);
+  return 0;
+}
+
+/* Step 3 alone: Y = A * B. */
+int rmm_oracle_matmul_f64(const double* A, const double* B, int64_t M, int64_t N, int64_t K,
+                          double* Y) {
+  if (M < 0 || N < 0 || K <= 0) return 1;
+  matmul(A, B, M, N, K, Y);
+  return 0;
+}
+
+/* Gated products on given activations: Y = silu(A W1) * (A W3). */
+int rmm_oracle_gated_matmul_f64(const double* A, const double* W1, const double* W3, int64_t M,
+                                int64_t N, int64_t K, double* Y) {
+  if (M < 0 || N < 0 || K <= 0) return 1;
+  return gated_products(A, W1, W3, M, N, K, Y);
 }

@@ -4,6 +4,11 @@
     y = tpa.rmsnorm_matmul(x, g, w, eps)             # Y = RMSNorm(x; g, eps) @ w
     y = tpa.rmsnorm_gated_mlp(x, g, w1, w3, eps)     # silu(norm(x) @ w1) * (norm(x) @ w3)
 
+    # the unfused two-kernel program the fused calls replace (for comparison)
+    xn = tpa.rmsnorm(x, g, eps)                       # normalised x, written to memory
+    y = tpa.matmul(xn, w)                             # plain product
+    y = tpa.gated_matmul(xn, w1, w3)                  # silu(xn @ w1) * (xn @ w3)
+
 x: [M, K], g: [K], w/w1/w3: [K, N], all contiguous, on one GPU, all float32 or
 all bfloat16.  The work is enqueued on torch's current stream; this module
 only marshals arguments (see include/rmm.h for the contract).
@@ -15,7 +20,8 @@ import torch
 from . import _binding
 from ._binding import RmmError, load_library  # noqa: F401
 
-__all__ = ["rmsnorm_matmul", "rmsnorm_gated_mlp", "RmmError", "load_library", "Workspace"]
+__all__ = ["rmsnorm_matmul", "rmsnorm_gated_mlp", "rmsnorm", "matmul", "gated_matmul",
+           "RmmError", "load_library", "Workspace"]
 
 _DTYPES = {torch.float32: _binding.DTYPE_F32, torch.bfloat16: _binding.DTYPE_BF16}
 
@@ -112,6 +118,67 @@ def rmsnorm_gated_mlp(x, g, w1, w3, eps: float, out=None, variant: str = "auto",
                       splits: int = 0, workspace: Workspace | None = None):
     """Y = silu(RMSNorm(x) @ w1) * (RMSNorm(x) @ w3), fused."""
     return _call(x, g, w1, w3, eps, out, variant, splits, workspace)
+
+
+def rmsnorm(x, g, eps: float, out=None):
+    """Xn = RMSNorm(x; g, eps), written to memory (first kernel of the unfused program)."""
+    _check_operands([x, g], ["x", "g"])
+    if x.dim() != 2 or g.dim() != 1 or g.shape[0] != x.shape[1]:
+        raise ValueError("expected x: [M, K], g: [K]")
+    M, K = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    else:
+        _check_operands([x, out], ["x", "out"])
+        if tuple(out.shape) != (M, K):
+            raise ValueError(f"out has shape {tuple(out.shape)}, expected {(M, K)}")
+    stream = torch.cuda.current_stream(x.device).cuda_stream
+    _binding.check(load_library().rmm_rmsnorm(x.data_ptr(), g.data_ptr(), out.data_ptr(),
+                                              float(eps), M, K, _DTYPES[x.dtype], stream))
+    return out
+
+
+def _plain(x, w1, w3, out, workspace):
+    gated = w3 is not None
+    tensors = [x, w1] + ([w3] if gated else [])
+    _check_operands(tensors, ["x", "w1", "w3"] if gated else ["x", "w"])
+    if x.dim() != 2 or w1.dim() != 2 or w1.shape[0] != x.shape[1] or \
+            (gated and tuple(w3.shape) != tuple(w1.shape)):
+        raise ValueError("expected x: [M, K], w: [K, N]")
+    M, K = x.shape
+    N = w1.shape[1]
+    if out is None:
+        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    else:
+        _check_operands([x, out], ["x", "out"])
+        if tuple(out.shape) != (M, N):
+            raise ValueError(f"out has shape {tuple(out.shape)}, expected {(M, N)}")
+    lib = load_library()
+    dtype = _DTYPES[x.dtype]
+    stream = torch.cuda.current_stream(x.device).cuda_stream
+    need = _binding.workspace_bytes(dtype, M, N, K, gated)
+    if workspace is None and need > 0:
+        workspace = _workspace_for(x.device, stream, need)
+    ws_ptr = workspace.ptr if workspace is not None else None
+    ws_bytes = workspace.nbytes if workspace is not None else 0
+    if gated:
+        st = lib.rmm_gated_matmul(x.data_ptr(), w1.data_ptr(), w3.data_ptr(), out.data_ptr(), M, N,
+                                  K, dtype, ws_ptr, ws_bytes, stream)
+    else:
+        st = lib.rmm_matmul(x.data_ptr(), w1.data_ptr(), out.data_ptr(), M, N, K, dtype, ws_ptr,
+                            ws_bytes, stream)
+    _binding.check(st)
+    return out
+
+
+def matmul(x, w, out=None, workspace: Workspace | None = None):
+    """Y = x @ w with the same kernels, no norm (second kernel of the unfused program)."""
+    return _plain(x, w, None, out, workspace)
+
+
+def gated_matmul(x, w1, w3, out=None, workspace: Workspace | None = None):
+    """Y = silu(x @ w1) * (x @ w3) with the same kernels, no norm."""
+    return _plain(x, w1, w3, out, workspace)
 
 
 def plan(M, N, K, dtype=torch.bfloat16, gated=False, variant="auto", splits=0,

@@ -19,8 +19,9 @@ STATUS_OK = 0
 
 # Exported symbols of include/rmm.h.
 SYMBOLS = ("rmsnorm_matmul", "rmsnorm_gated_mlp", "rmsnorm_matmul_ex", "rmsnorm_gated_mlp_ex",
-           "rmm_workspace_bytes", "rmm_workspace_bytes_ex", "rmm_plan", "rmm_status_string",
-           "rmm_last_hip_error", "rmm_abi_version")
+           "rmm_rmsnorm", "rmm_matmul", "rmm_gated_matmul", "rmm_workspace_bytes",
+           "rmm_workspace_bytes_ex", "rmm_plan", "rmm_status_string", "rmm_last_hip_error",
+           "rmm_abi_version")
 
 _lib = None
 
@@ -48,7 +49,11 @@ def load_library(path: str = LIB_PATH):
                                       vp]
     lib.rmsnorm_gated_mlp_ex.argtypes = [vp, vp, vp, vp, vp, f32, i64, i64, i64, i32, i32, i32,
                                          vp, sz, vp]
-    for f in ("rmsnorm_matmul", "rmsnorm_gated_mlp", "rmsnorm_matmul_ex", "rmsnorm_gated_mlp_ex"):
+    lib.rmm_rmsnorm.argtypes = [vp, vp, vp, f32, i64, i64, i32, vp]
+    lib.rmm_matmul.argtypes = [vp, vp, vp, i64, i64, i64, i32, vp, sz, vp]
+    lib.rmm_gated_matmul.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, vp, sz, vp]
+    for f in ("rmsnorm_matmul", "rmsnorm_gated_mlp", "rmsnorm_matmul_ex", "rmsnorm_gated_mlp_ex",
+              "rmm_rmsnorm", "rmm_matmul", "rmm_gated_matmul"):
         getattr(lib, f).restype = i32
     lib.rmm_workspace_bytes.argtypes = [i32, i64, i64, i64, i32]
     lib.rmm_workspace_bytes.restype = sz

@@ -138,13 +138,13 @@ rmm_status plan_call(const void* X, const void* g, const void* W1, const void* W
 
 rmm_status run(const void* X, const void* g, const void* W1, const void* W3, void* Y, float eps,
                int64_t M, int64_t N, int64_t K, rmm_dtype dtype, int gated, rmm_variant variant,
-               int splits, void* ws, size_t ws_bytes, hipStream_t stream) {
+               int splits, void* ws, size_t ws_bytes, hipStream_t stream, int norm = 1) {
   Plan plan;
   rmm_status st =
       plan_call(X, g, W1, W3, Y, eps, M, N, K, dtype, gated, variant, splits, ws, ws_bytes, &plan);
   if (st != RMM_OK) return st;
   if (M == 0 || N == 0) return RMM_OK;
-  RmmArgs a{X, g, W1, gated ? W3 : nullptr, Y, eps, M, N, K, gated, stream};
+  RmmArgs a{X, g, W1, gated ? W3 : nullptr, Y, eps, M, N, K, gated, norm, stream};
   hipError_t err = hipSuccess;
   switch (plan.variant) {
     case RMM_VARIANT_GENERIC:
@@ -198,6 +198,41 @@ rmm_status rmsnorm_gated_mlp_ex(const void* X, const void* g, const void* W1, co
                                 rmm_dtype dtype, rmm_variant variant, int splits, void* ws,
                                 size_t ws_bytes, hipStream_t stream) {
   return run(X, g, W1, W3, Y, eps, M, N, K, dtype, 1, variant, splits, ws, ws_bytes, stream);
+}
+
+rmm_status rmm_matmul(const void* X, const void* W, void* Y, int64_t M, int64_t N, int64_t K,
+                      rmm_dtype dtype, void* ws, size_t ws_bytes, hipStream_t stream) {
+  // The kernels take the gain from X's buffer and ignore it (norm = 0).
+  return run(X, X, W, nullptr, Y, 0.0f, M, N, K, dtype, 0, RMM_VARIANT_AUTO, 0, ws, ws_bytes,
+             stream, 0);
+}
+
+rmm_status rmm_gated_matmul(const void* X, const void* W1, const void* W3, void* Y, int64_t M,
+                            int64_t N, int64_t K, rmm_dtype dtype, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+  return run(X, X, W1, W3, Y, 0.0f, M, N, K, dtype, 1, RMM_VARIANT_AUTO, 0, ws, ws_bytes, stream,
+             0);
+}
+
+rmm_status rmm_rmsnorm(const void* X, const void* g, void* Xn, float eps, int64_t M, int64_t K,
+                       rmm_dtype dtype, hipStream_t stream) {
+  if (M != 0 && (!X || !g || !Xn)) return RMM_ERR_NULL;
+  int64_t mk, tmp;
+  if (M < 0 || K <= 0 || __builtin_mul_overflow(M, K, &mk) ||
+      __builtin_mul_overflow(mk, (int64_t)4, &tmp))
+    return RMM_ERR_SHAPE;
+  if (!isfinite(eps) || eps < 0.0f) return RMM_ERR_EPS;
+  if (dtype != RMM_DTYPE_F32 && dtype != RMM_DTYPE_BF16) return RMM_ERR_DTYPE;
+  if (M == 0) return RMM_OK;
+  const size_t es = dtype == RMM_DTYPE_F32 ? 4 : 2;
+  if (overlaps(Xn, (size_t)mk * es, X, (size_t)mk * es) || overlaps(Xn, (size_t)mk * es, g, (size_t)K * es))
+    return RMM_ERR_ALIAS;
+  const hipError_t err = rmm_launch_rmsnorm(X, g, Xn, eps, M, K, dtype == RMM_DTYPE_BF16, stream);
+  if (err != hipSuccess) {
+    g_last_hip_error = (int)err;
+    return RMM_ERR_HIP;
+  }
+  return RMM_OK;
 }
 
 size_t rmm_workspace_bytes_ex(rmm_dtype dtype, int64_t M, int64_t N, int64_t K, int gated,

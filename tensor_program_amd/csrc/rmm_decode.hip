@@ -104,7 +104,7 @@ __global__ __launch_bounds__(WV * 64) void decode_kernel(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ g, const bf16_t* __restrict__ W1,
     const bf16_t* __restrict__ W3, bf16_t* __restrict__ Y, float eps, int M, int64_t N,
     int64_t K, int64_t kchunk, int S, int tiles, int xcd_remap, unsigned* __restrict__ cnt,
-    float* __restrict__ ssq_ws, float* __restrict__ part_ws) {
+    float* __restrict__ ssq_ws, float* __restrict__ part_ws, int norm) {
   constexpr int NW = GATED ? 2 : 1;
   constexpr int NT = WV * 64;
   constexpr int E4 = NW * MB * 8 * 64;  // floatx4 per partial
@@ -163,7 +163,8 @@ __global__ __launch_bounds__(WV * 64) void decode_kernel(
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         const float x0 = bf16_lo(xs[u][d]), x1 = bf16_hi(xs[u][d]);
-        const float g0 = bf16_lo(gs[u][d]), g1 = bf16_hi(gs[u][d]);
+        const uint32_t gd = norm ? gs[u][d] : kBf16OnePair;
+        const float g0 = bf16_lo(gd), g1 = bf16_hi(gd);
         ssl += x0 * x0 + x1 * x1;
         av[d] = pack_bf16x2(x0 * g0, x1 * g1);
       }
@@ -304,7 +305,7 @@ __global__ __launch_bounds__(WV * 64) void decode_kernel(
   __syncthreads();  // everyone is done reading sm.red before it is overwritten
 #pragma unroll
   for (int u = 0; u < PER4; ++u) red0[tid + NT * u] = v[u];
-  if (tid < ROWS) sm.inv[tid] = inv_rms(ssw, K, eps);
+  if (tid < ROWS) sm.inv[tid] = norm ? inv_rms(ssw, K, eps) : 1.0f;
   __syncthreads();
 
   // Epilogue: group (b, r, lane) -> row 16b + 4(lane/16) + r, 8 columns
@@ -375,7 +376,7 @@ static void launch_decode_t(const RmmArgs& a, const DecodePlan& p, void* ws) {
   hipLaunchKernelGGL((decode_kernel<MB, GATED, WV>), dim3(grid), dim3(WV * 64), 0, a.stream,
                      (const bf16_t*)a.X, (const bf16_t*)a.g, (const bf16_t*)a.W1,
                      (const bf16_t*)a.W3, (bf16_t*)a.Y, a.eps, (int)a.M, a.N, a.K, p.kchunk,
-                     p.splits, (int)p.tiles, xcd_remap, cnt, ssq, part);
+                     p.splits, (int)p.tiles, xcd_remap, cnt, ssq, part, a.norm);
 }
 
 hipError_t rmm_launch_decode(const RmmArgs& a, const DecodePlan& p, void* ws) {

@@ -15,6 +15,9 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// bf16 pair (1.0, 1.0): the gain when the call is a plain product.
+constexpr uint32_t kBf16OnePair = 0x3f803f80u;
+
 // bf16 bits -> fp32 (exact).
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -63,6 +66,7 @@ struct RmmArgs {
   float eps;
   int64_t M, N, K;
   int gated;
+  int norm;  // 1: fused RMSNorm (gain g, 1/RMS scale); 0: plain product (g = 1, no scale)
   hipStream_t stream;
 };
 
@@ -88,3 +92,7 @@ void rmm_prefill_plan(int64_t M, int64_t N, int64_t K, PrefillPlan* p);
 hipError_t rmm_launch_prefill(const RmmArgs& a, const PrefillPlan& p);
 
 hipError_t rmm_launch_stream(const RmmArgs& a);
+
+// Unfused baseline, first kernel: Xn = bf16/f32(X * g / RMS) written out.
+hipError_t rmm_launch_rmsnorm(const void* X, const void* g, void* Xn, float eps, int64_t M,
+                              int64_t K, bool bf16, hipStream_t stream);

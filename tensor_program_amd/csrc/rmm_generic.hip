@@ -22,7 +22,8 @@ constexpr int GEN_THREADS = 256;
 template <typename T, bool GATED>
 __global__ __launch_bounds__(GEN_THREADS) void generic_kernel(
     const T* __restrict__ X, const T* __restrict__ g, const T* __restrict__ W1,
-    const T* __restrict__ W3, T* __restrict__ Y, float eps, int64_t M, int64_t N, int64_t K) {
+    const T* __restrict__ W3, T* __restrict__ Y, float eps, int64_t M, int64_t N, int64_t K,
+    int norm) {
   __shared__ float a_s[GEN_ROWS][GEN_KC];
   __shared__ float red[GATED ? 2 : 1][4][GEN_ROWS][GEN_COLS];
   __shared__ float ss_s[GEN_ROWS][32];
@@ -52,7 +53,7 @@ __global__ __launch_bounds__(GEN_THREADS) void generic_kernel(
   if (tid < GEN_ROWS) {
     float ss = 0.0f;
     for (int j = 0; j < 32; ++j) ss += ss_s[tid][j];
-    inv_s[tid] = inv_rms(ss, K, eps);
+    inv_s[tid] = norm ? inv_rms(ss, K, eps) : 1.0f;
   }
 
   const int c = tid % GEN_COLS, s = tid / GEN_COLS;
@@ -83,7 +84,7 @@ __global__ __launch_bounds__(GEN_THREADS) void generic_kernel(
     for (int e = tid; e < GEN_ROWS * GEN_KC; e += GEN_THREADS) {
       const int r = e / GEN_KC, kk = e % GEN_KC;
       const int64_t m = m0 + r, k = k0 + kk;
-      a_s[r][kk] = (m < M && k < K) ? load_f32(X + m * K + k) * load_f32(g + k) : 0.0f;
+      a_s[r][kk] = (m < M && k < K) ? load_f32(X + m * K + k) * (norm ? load_f32(g + k) : 1.0f) : 0.0f;
     }
     __syncthreads();
     float w1n[NU], w3n[NU];
@@ -138,20 +139,20 @@ hipError_t rmm_launch_generic(const RmmArgs& a, bool bf16) {
     auto Y = (bf16_t*)a.Y;
     if (a.gated)
       hipLaunchKernelGGL((generic_kernel<bf16_t, true>), grid, block, 0, a.stream, X, g, W1, W3,
-                         Y, a.eps, a.M, a.N, a.K);
+                         Y, a.eps, a.M, a.N, a.K, a.norm);
     else
       hipLaunchKernelGGL((generic_kernel<bf16_t, false>), grid, block, 0, a.stream, X, g, W1,
-                         W3, Y, a.eps, a.M, a.N, a.K);
+                         W3, Y, a.eps, a.M, a.N, a.K, a.norm);
   } else {
     auto X = (const float*)a.X, g = (const float*)a.g, W1 = (const float*)a.W1,
          W3 = (const float*)a.W3;
     auto Y = (float*)a.Y;
     if (a.gated)
       hipLaunchKernelGGL((generic_kernel<float, true>), grid, block, 0, a.stream, X, g, W1, W3, Y,
-                         a.eps, a.M, a.N, a.K);
+                         a.eps, a.M, a.N, a.K, a.norm);
     else
       hipLaunchKernelGGL((generic_kernel<float, false>), grid, block, 0, a.stream, X, g, W1, W3,
-                         Y, a.eps, a.M, a.N, a.K);
+                         Y, a.eps, a.M, a.N, a.K, a.norm);
   }
   return hipGetLastError();
 }

@@ -144,15 +144,16 @@ __device__ __forceinline__ void pf_dma_b(uint32_t b_lds, const PfDma& d, const b
 // rounded once to bf16; the same dot2 unit accumulates the row sums of
 // squares of raw X.
 __device__ __forceinline__ void pf_store_a(const PfA& st, char* a_lds, float (&ss)[4], int tid,
-                                           int i0) {
+                                           int i0, int norm) {
 #pragma unroll
   for (int i = i0; i < i0 + 2; ++i) {
     u32x4 v;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
       const bf16x2 x = as_bf16x2(st.a[i][d]);
-      v[d] = pack_bf16x2(__builtin_amdgcn_fdot2_f32_bf16(x, as_bf16x2(st.g[d] & 0xffffu), 0.0f, false),
-                         __builtin_amdgcn_fdot2_f32_bf16(x, as_bf16x2(st.g[d] & 0xffff0000u), 0.0f, false));
+      const uint32_t gd = norm ? st.g[d] : kBf16OnePair;
+      v[d] = pack_bf16x2(__builtin_amdgcn_fdot2_f32_bf16(x, as_bf16x2(gd & 0xffffu), 0.0f, false),
+                         __builtin_amdgcn_fdot2_f32_bf16(x, as_bf16x2(gd & 0xffff0000u), 0.0f, false));
       ss[i] = __builtin_amdgcn_fdot2_f32_bf16(x, x, ss[i], false);
     }
     *(u32x4*)(a_lds + ((tid >> 3) + 64 * i) * PF_A_ROW + 16 * (tid & 7)) = v;
@@ -203,7 +204,7 @@ __device__ __forceinline__ void pf_mfma(const PfFrag& f, floatx16 (&acc)[4][2]) 
 template <int VM>
 __device__ __forceinline__ void pf_step(const char* a_cur, const lds_char* b_cur, char* a_nxt,
                                         PfA& st, floatx16 (&acc)[4][2], float (&ss)[4],
-                                        int a_base, int b0, int b1, int tid) {
+                                        int a_base, int b0, int b1, int tid, int norm) {
   PfFrag fa, fb;
   pf_read_frags(fa, a_cur, b_cur, a_base, b0, b1, 0);
   pf_read_frags(fb, a_cur, b_cur, a_base, b0, b1, 1);
@@ -212,10 +213,10 @@ __device__ __forceinline__ void pf_step(const char* a_cur, const lds_char* b_cur
   pf_mfma(fb, acc);
   __builtin_amdgcn_sched_barrier(0);
   pf_wait_a<VM>(st);
-  pf_store_a(st, a_nxt, ss, tid, 0);
+  pf_store_a(st, a_nxt, ss, tid, 0, norm);
   pf_read_frags(fb, a_cur, b_cur, a_base, b0, b1, 3);
   pf_mfma(fa, acc);
-  pf_store_a(st, a_nxt, ss, tid, 2);
+  pf_store_a(st, a_nxt, ss, tid, 2, norm);
   pf_mfma(fb, acc);
 }
 
@@ -223,7 +224,7 @@ template <bool GATED>
 __global__ __launch_bounds__(PF_THREADS, 2) void prefill_kernel(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ g, const bf16_t* __restrict__ W1,
     const bf16_t* __restrict__ W3, bf16_t* __restrict__ Y, float eps, int64_t M, int64_t N,
-    int64_t K, int tiles_m, int tiles_n, int group_m, int xcd_remap) {
+    int64_t K, int tiles_m, int tiles_n, int group_m, int xcd_remap, int norm) {
   static_assert(!GATED, "gated prefill tiles are not built");
   // Separate objects per stage, so the compiler can tell the W stage being
   // filled by direct loads from the one being read.
@@ -291,8 +292,8 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_kernel(
   pf_load_a(sa, xr, gr, m0, 0, M, K, tid);
   pf_load_a(sb, xr, gr, m0, PF_BK, M, K, tid);
   pf_wait_a<5>(sa);
-  pf_store_a(sa, a_s0, ss, tid, 0);
-  pf_store_a(sa, a_s0, ss, tid, 2);
+  pf_store_a(sa, a_s0, ss, tid, 0, norm);
+  pf_store_a(sa, a_s0, ss, tid, 2, norm);
   PF_WAIT_VMCNT(0);
   __syncthreads();
 
@@ -302,12 +303,12 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_kernel(
   for (int kt = 0; kt < nk; kt += 2) {
     pf_dma_b(b1a, dma, W1, (int64_t)(kt + 1) * PF_BK, N, K, w);
     pf_load_a(sa, xr, gr, m0, (int64_t)(kt + 2) * PF_BK, M, K, tid);
-    pf_step<9>(a_s0, b0s, a_s1, sb, acc, ss, a_base, bo0, bo1, tid);
+    pf_step<9>(a_s0, b0s, a_s1, sb, acc, ss, a_base, bo0, bo1, tid, norm);
     PF_WAIT_VMCNT(5);
     __syncthreads();
     pf_dma_b(b0a, dma, W1, (int64_t)(kt + 2) * PF_BK, N, K, w);
     pf_load_a(sb, xr, gr, m0, (int64_t)(kt + 3) * PF_BK, M, K, tid);
-    pf_step<9>(a_s1, b1s, a_s0, sa, acc, ss, a_base, bo0, bo1, tid);
+    pf_step<9>(a_s1, b1s, a_s0, sa, acc, ss, a_base, bo0, bo1, tid, norm);
     PF_WAIT_VMCNT(5);
     __syncthreads();
   }
@@ -320,7 +321,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_kernel(
     v += __shfl_xor(v, 1);
     v += __shfl_xor(v, 2);
     v += __shfl_xor(v, 4);
-    if ((tid & 7) == 0) inv_s[(tid >> 3) + 64 * i] = inv_rms(v, K, eps);
+    if ((tid & 7) == 0) inv_s[(tid >> 3) + 64 * i] = norm ? inv_rms(v, K, eps) : 1.0f;
   }
   __syncthreads();
 
@@ -361,6 +362,6 @@ hipError_t rmm_launch_prefill(const RmmArgs& a, const PrefillPlan& p) {
   hipLaunchKernelGGL((prefill_kernel<false>), dim3(grid), dim3(PF_THREADS), 0, a.stream,
                      (const bf16_t*)a.X, (const bf16_t*)a.g, (const bf16_t*)a.W1,
                      (const bf16_t*)a.W3, (bf16_t*)a.Y, a.eps, a.M, a.N, a.K, p.tiles_m,
-                     p.tiles_n, p.group_m, p.xcd_remap);
+                     p.tiles_n, p.group_m, p.xcd_remap, a.norm);
   return hipGetLastError();
 }

@@ -101,7 +101,7 @@ template <int NW>
 __global__ __launch_bounds__(ST_THREADS, 1) void stream_kernel(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ g, const bf16_t* __restrict__ W1,
     const bf16_t* __restrict__ W3, bf16_t* __restrict__ Y, float eps, int M, int64_t N,
-    int64_t K) {
+    int64_t K, int norm) {
   constexpr int RING = StCfg<NW>::RING, AHEAD = StCfg<NW>::AHEAD, SUBS = StCfg<NW>::SUBS;
   __shared__ __attribute__((aligned(1024))) StSmem<NW> sm;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
@@ -154,7 +154,8 @@ __global__ __launch_bounds__(ST_THREADS, 1) void stream_kernel(
     const int slot = step % RING;
     char* xp = &sm.x[slot][f_off];
     const u32x4 xv = *(const u32x4*)xp;
-    const u32x4 gv = *(const u32x4*)&sm.g[slot][w * 128 + 16 * f_c];
+    const u32x4 gl = *(const u32x4*)&sm.g[slot][w * 128 + 16 * f_c];
+    const u32x4 gv = norm ? gl : u32x4{kBf16OnePair, kBf16OnePair, kBf16OnePair, kBf16OnePair};
     u32x4 av;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
@@ -243,7 +244,7 @@ __global__ __launch_bounds__(ST_THREADS, 1) void stream_kernel(
         const int row = rb * 32 + 8 * jj + 4 * (l >> 5) + r, col = cb * 32 + (l & 31);
         red[(set * ST_BM + row) * ST_BN + col] = acc[rb][4 * jj + r];
       }
-  if (tid < ST_BM) sm.inv[tid] = inv_rms(sm.ss[tid], K, eps);
+  if (tid < ST_BM) sm.inv[tid] = norm ? inv_rms(sm.ss[tid], K, eps) : 1.0f;
   __syncthreads();
 
   // Epilogue: thread -> row tid>>3, columns 8 (tid&7) .. +7.
@@ -287,10 +288,10 @@ hipError_t rmm_launch_stream(const RmmArgs& a) {
   if (a.gated)
     hipLaunchKernelGGL((stream_kernel<2>), dim3(grid), dim3(ST_THREADS), 0, a.stream,
                        (const bf16_t*)a.X, (const bf16_t*)a.g, (const bf16_t*)a.W1,
-                       (const bf16_t*)a.W3, (bf16_t*)a.Y, a.eps, (int)a.M, a.N, a.K);
+                       (const bf16_t*)a.W3, (bf16_t*)a.Y, a.eps, (int)a.M, a.N, a.K, a.norm);
   else
     hipLaunchKernelGGL((stream_kernel<1>), dim3(grid), dim3(ST_THREADS), 0, a.stream,
                        (const bf16_t*)a.X, (const bf16_t*)a.g, (const bf16_t*)a.W1,
-                       (const bf16_t*)a.W3, (bf16_t*)a.Y, a.eps, (int)a.M, a.N, a.K);
+                       (const bf16_t*)a.W3, (bf16_t*)a.Y, a.eps, (int)a.M, a.N, a.K, a.norm);
   return hipGetLastError();
 }

@@ -225,6 +225,59 @@ def pin_gated_closed_forms(lib):
     _close(y, z / (1.0 + np.exp(-z)) * nrm0, rtol=1e-12)
 
 
+def _brute_rows(X, g, eps):
+    """Exact rationals for the mean square, 50-digit sqrt: (X / r) * g."""
+    getcontext().prec = 50
+    out = []
+    for row in X:
+        S = sum(Fraction(v) ** 2 for v in row) / len(row) + Fraction(eps)
+        rms = Decimal(S.numerator).sqrt() / Decimal(S.denominator).sqrt()
+        out.append([float(Decimal(Fraction(v).numerator) / Decimal(Fraction(v).denominator) / rms
+                          * Decimal(Fraction(gk).numerator) / Decimal(Fraction(gk).denominator))
+                    for v, gk in zip(row, g)])
+    return np.array(out)
+
+
+def pin_unfused_steps(lib):
+    # The unfused program's pieces on their own.  Worked example: X = [3, 4],
+    # eps = 12.5 -> RMS 5, normalised [0.6, 0.8], gained by g = [1, 2].
+    _close(oracle.rmsnorm(np.array([[3.0, 4.0]]), np.array([1.0, 2.0]), 12.5, lib=lib),
+           [[0.6, 1.6]])
+    # Hand product with k-indexed rows of B: [[0,1,2],[3,4,5]] @ [[0..3],[4..7],[8..11]].
+    A = np.arange(6.0).reshape(2, 3)
+    B = np.arange(12.0).reshape(3, 4)
+    _close(oracle.matmul(A, B, lib=lib), [[20, 23, 26, 29], [56, 68, 80, 92]])
+    # Brute force: exact rationals for the rows and for integer products.
+    rng = np.random.default_rng(21)
+    for _ in range(8):
+        M, K, N = (int(v) for v in rng.integers(1, 6, size=3))
+        X = rng.normal(size=(M, K))
+        X[:, 0] += 0.5
+        g = rng.normal(1.0, 0.3, size=K)
+        eps = float(rng.choice([0.0, 1e-6, 0.5]))
+        _close(oracle.rmsnorm(X, g, eps, lib=lib), _brute_rows(X.tolist(), g.tolist(), eps),
+               rtol=1e-14, atol=1e-15)
+        Ai = rng.integers(-9, 10, size=(M, K))
+        Bi = rng.integers(-9, 10, size=(K, N))
+        want = [[sum(int(Ai[m, k]) * int(Bi[k, n]) for k in range(K)) for n in range(N)]
+                for m in range(M)]
+        assert np.array_equal(oracle.matmul(Ai, Bi, lib=lib), np.array(want, np.float64))
+    # Gate closed forms on given activations A = [1, 1]: z1 = column sums.
+    ln3 = math.log(3.0)
+    W1 = np.array([[ln3 / 2, 0.0, -ln3 / 2], [ln3 / 2, 0.0, -ln3 / 2]])
+    W3 = np.array([[1.0, 2.5, 0.5], [1.0, 2.5, 0.5]])
+    _close(oracle.gated_matmul(np.ones((1, 2)), W1, W3, lib=lib),
+           [[0.75 * ln3 * 2.0, 0.0, -0.25 * ln3 * 1.0]])
+    # The pieces compose to the fused definition exactly (same operations).
+    X = rng.normal(size=(4, 6))
+    g = rng.normal(1.0, 0.2, size=6)
+    W = rng.normal(size=(6, 5))
+    W3r = rng.normal(size=(6, 5))
+    n = oracle.rmsnorm(X, g, 1e-3, lib=lib)
+    assert np.array_equal(oracle.matmul(n, W, lib=lib), _mm(lib, X, g, W, 1e-3))
+    assert np.array_equal(oracle.gated_matmul(n, W, W3r, lib=lib), _gated(lib, X, g, W, W3r, 1e-3))
+
+
 ALL_PINS = [pin_worked_example, pin_library_matmul, pin_identity_weight, pin_constant_row,
             pin_scale_law, pin_gain_fold, pin_structure, pin_zero_row, pin_brute_force,
-            pin_gated_closed_forms]
+            pin_gated_closed_forms, pin_unfused_steps]

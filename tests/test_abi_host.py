@@ -92,6 +92,36 @@ def test_validation_order(lib):
     assert call(lib, variant=2, K=4096, N=6144, splits=8, ws=A[6], ws_bytes=need - 1) == WORKSPACE
 
 
+def test_unfused_entry_points_validate(lib):
+    # rmm_rmsnorm: NULL, SHAPE, EPS, DTYPE, ALIAS, in that order.
+    def norm(X=A[0], g=A[1], Xn=A[3], eps=1e-6, M=16, K=64, dtype=BF16):
+        return lib.rmm_rmsnorm(X, g, Xn, eps, M, K, dtype, None)
+    assert norm(X=None) == NULL
+    assert norm(Xn=None, K=0) == NULL
+    assert norm(K=0) == SHAPE
+    assert norm(M=-1) == SHAPE
+    assert norm(M=1 << 62, K=1 << 4) == SHAPE
+    assert norm(K=0, eps=-1.0) == SHAPE
+    assert norm(eps=-1.0) == EPS
+    assert norm(eps=float("nan"), dtype=7) == EPS
+    assert norm(dtype=7) == DTYPE
+    assert norm(Xn=A[0]) == ALIAS                     # in place is not allowed
+    assert norm(Xn=A[1] - 8) == ALIAS                 # overlapping g
+    assert norm(X=None, g=None, Xn=None, M=0) == OK   # empty: nothing launched
+    # rmm_matmul / rmm_gated_matmul: the fused calls' rules, no eps.
+    def mm(X=A[0], W=A[2], Y=A[3], M=16, N=64, K=64, dtype=BF16, ws=None, ws_bytes=0):
+        return lib.rmm_matmul(X, W, Y, M, N, K, dtype, ws, ws_bytes, None)
+    assert mm(X=None) == NULL
+    assert mm(W=None) == NULL
+    assert mm(K=0) == SHAPE
+    assert mm(dtype=7) == DTYPE
+    assert mm(Y=A[0] + 16) == ALIAS
+    assert mm(Y=A[2] + 32) == ALIAS
+    assert mm(X=None, W=None, Y=None, N=0) == OK
+    assert lib.rmm_gated_matmul(A[0], A[2], None, A[3], 16, 64, 64, BF16, None, 0, None) == NULL
+    assert lib.rmm_gated_matmul(A[0], A[2], A[4], A[4] + 8, 16, 64, 64, BF16, None, 0, None) == ALIAS
+
+
 def test_empty_shapes_are_noops(lib):
     # M == 0 or N == 0: RMM_OK, nothing launched (NULL pointers allowed).
     assert call(lib, X=None, g=None, W=None, Y=None, M=0) == OK

@@ -26,7 +26,7 @@ MUTANTS = {
     "gate_sign": ("z1 / (1.0 + exp(-z1)) * Z3[i]", "z1 / (1.0 + exp(z1)) * Z3[i]"),
     "gate_swapped": ("z1 / (1.0 + exp(-z1)) * Z3[i]", "Z3[i] / (1.0 + exp(-Z3[i])) * z1"),
     "gate_no_silu": ("z1 / (1.0 + exp(-z1)) * Z3[i]", "z1 * Z3[i]"),
-    "gate_both_w1": ("matmul(Nrm, W3, M, N, K, Z3);", "matmul(Nrm, W1, M, N, K, Z3);"),
+    "gate_both_w1": ("matmul(A, W3, M, N, K, Z3);", "matmul(A, W1, M, N, K, Z3);"),
 }
 
 

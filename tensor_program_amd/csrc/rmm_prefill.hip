@@ -78,6 +78,7 @@ __device__ __forceinline__ u32x4 pf_load16(uint32_t voff, i32x4 rsrc) {
   return v;
 }
 
+template <bool GL>
 __device__ __forceinline__ void pf_load_a(PfA& st, i32x4 xr, i32x4 gr, int64_t m0, int64_t k0,
                                           int64_t M, int64_t K, int tid) {
   const int64_t ka = k0 + 8 * (tid & 7);
@@ -88,7 +89,10 @@ __device__ __forceinline__ void pf_load_a(PfA& st, i32x4 xr, i32x4 gr, int64_t m
     const uint32_t off = (ka_ok && m < M) ? (uint32_t)((m * K + ka) * 2) : kPfOutOfRange;
     st.a[i] = pf_load16(off, xr);
   }
-  st.g = pf_load16(ka_ok ? (uint32_t)(ka * 2) : kPfOutOfRange, gr);
+  // With the gain held in LDS (GL) it is not loaded per step: every wave of
+  // every workgroup reading the same 128 bytes of g at the same k-step
+  // queues those requests on one L2 channel.
+  if (!GL) st.g = pf_load16(ka_ok ? (uint32_t)(ka * 2) : kPfOutOfRange, gr);
 }
 
 // Wait until at most N vector-memory loads are outstanding; the registers
@@ -143,15 +147,17 @@ __device__ __forceinline__ void pf_dma_b(uint32_t b_lds, const PfDma& d, const b
 // exactly in fp32 by a bf16 dot2 with the other lane of g zeroed, then
 // rounded once to bf16; the same dot2 unit accumulates the row sums of
 // squares of raw X.
+template <bool GL>
 __device__ __forceinline__ void pf_store_a(const PfA& st, char* a_lds, float (&ss)[4], int tid,
-                                           int i0, int norm) {
+                                           int i0, int norm, const char* g_lds, int64_t k0) {
+  const u32x4 gsrc = GL ? *(const u32x4*)(g_lds + 2 * (k0 + 8 * (tid & 7))) : st.g;
 #pragma unroll
   for (int i = i0; i < i0 + 2; ++i) {
     u32x4 v;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
       const bf16x2 x = as_bf16x2(st.a[i][d]);
-      const uint32_t gd = norm ? st.g[d] : kBf16OnePair;
+      const uint32_t gd = norm ? gsrc[d] : kBf16OnePair;
       v[d] = pack_bf16x2(__builtin_amdgcn_fdot2_f32_bf16(x, as_bf16x2(gd & 0xffffu), 0.0f, false),
                          __builtin_amdgcn_fdot2_f32_bf16(x, as_bf16x2(gd & 0xffff0000u), 0.0f, false));
       ss[i] = __builtin_amdgcn_fdot2_f32_bf16(x, x, ss[i], false);
@@ -201,10 +207,11 @@ __device__ __forceinline__ void pf_mfma(const PfFrag& f, floatx16 (&acc)[4][2]) 
 // (st) is scaled into a_nxt.  Fragments of sub-step s+1 are read while the
 // MFMAs of sub-step s run; the staging is fenced behind the first two
 // sub-steps.
-template <int VM>
+template <int VM, bool GL>
 __device__ __forceinline__ void pf_step(const char* a_cur, const lds_char* b_cur, char* a_nxt,
                                         PfA& st, floatx16 (&acc)[4][2], float (&ss)[4],
-                                        int a_base, int b0, int b1, int tid, int norm) {
+                                        int a_base, int b0, int b1, int tid, int norm,
+                                        const char* g_lds, int64_t k_nxt) {
   PfFrag fa, fb;
   pf_read_frags(fa, a_cur, b_cur, a_base, b0, b1, 0);
   pf_read_frags(fb, a_cur, b_cur, a_base, b0, b1, 1);
@@ -213,19 +220,27 @@ __device__ __forceinline__ void pf_step(const char* a_cur, const lds_char* b_cur
   pf_mfma(fb, acc);
   __builtin_amdgcn_sched_barrier(0);
   pf_wait_a<VM>(st);
-  pf_store_a(st, a_nxt, ss, tid, 0, norm);
+  pf_store_a<GL>(st, a_nxt, ss, tid, 0, norm, g_lds, k_nxt);
   pf_read_frags(fb, a_cur, b_cur, a_base, b0, b1, 3);
   pf_mfma(fa, acc);
-  pf_store_a(st, a_nxt, ss, tid, 2, norm);
+  pf_store_a<GL>(st, a_nxt, ss, tid, 2, norm, g_lds, k_nxt);
   pf_mfma(fb, acc);
 }
 
-template <bool GATED>
+// Largest K whose gain vector is held in LDS for the whole call (20 KB, the
+// room left beside the A and W stages); the k-steps past K (up to one more
+// step) read zeros from the padding.
+constexpr int PF_G_LDS_MAX = 10240;
+
+template <bool GATED, bool GL>
 __global__ __launch_bounds__(PF_THREADS, 2) void prefill_kernel(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ g, const bf16_t* __restrict__ W1,
     const bf16_t* __restrict__ W3, bf16_t* __restrict__ Y, float eps, int64_t M, int64_t N,
     int64_t K, int tiles_m, int tiles_n, int group_m, int xcd_remap, int norm) {
   static_assert(!GATED, "gated prefill tiles are not built");
+  // Loads per thread per k-step outside the W transfers: 4 rows of X, and
+  // the gain unless it sits in LDS.
+  constexpr int XL = GL ? 4 : 5;
   // Separate objects per stage, so the compiler can tell the W stage being
   // filled by direct loads from the one being read.
   __shared__ __attribute__((aligned(16))) char a_s0[PF_A_BYTES];
@@ -233,6 +248,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_kernel(
   __shared__ __attribute__((aligned(1024))) char b_s0[PF_B_BYTES];
   __shared__ __attribute__((aligned(1024))) char b_s1[PF_B_BYTES];
   __shared__ float inv_s[PF_BM];
+  __shared__ __attribute__((aligned(16))) char g_s[GL ? 2 * (PF_G_LDS_MAX + 2 * PF_BK) : 16];
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   // Tile order: with xcd_remap, XCD x (workgroups bid % 8 == x) takes a
@@ -282,18 +298,24 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_kernel(
   // stage, X of step kt+2 is in flight, and step kt is multiplied.  Loads
   // past the last step read zeros (buffer range check), so the loop body has
   // no branches; it is unrolled by two so each register stage is static.
-  // The 5 X/g loads of a step are issued after its W transfers, so
-  // vmcnt <= 5 means those transfers have landed; before X of the next step
-  // is scaled, vmcnt <= 9 (this iteration's 4 W and 5 X/g loads may still
-  // be in flight) means it has.  Both waits are explicit: the compiler sees
-  // none of these loads.
+  // The XL X (and g) loads of a step are issued after its W transfers, so
+  // vmcnt <= XL means those transfers have landed; before X of the next step
+  // is scaled, vmcnt <= XL + 4 (this iteration's 4 W and XL X loads may
+  // still be in flight) means it has.  Both waits are explicit: the compiler
+  // sees none of these loads.
+  if (GL) {  // the whole gain vector, zero past K
+    for (int c = tid; c < (PF_G_LDS_MAX + 2 * PF_BK) / 8; c += PF_THREADS)
+      *(u32x4*)(g_s + 16 * c) = 8 * c < K ? *(const u32x4*)(g + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+    __syncthreads();
+  }
+
   PfA sa, sb;
   pf_dma_b(b0a, dma, W1, 0, N, K, w);
-  pf_load_a(sa, xr, gr, m0, 0, M, K, tid);
-  pf_load_a(sb, xr, gr, m0, PF_BK, M, K, tid);
-  pf_wait_a<5>(sa);
-  pf_store_a(sa, a_s0, ss, tid, 0, norm);
-  pf_store_a(sa, a_s0, ss, tid, 2, norm);
+  pf_load_a<GL>(sa, xr, gr, m0, 0, M, K, tid);
+  pf_load_a<GL>(sb, xr, gr, m0, PF_BK, M, K, tid);
+  pf_wait_a<XL>(sa);
+  pf_store_a<GL>(sa, a_s0, ss, tid, 0, norm, g_s, 0);
+  pf_store_a<GL>(sa, a_s0, ss, tid, 2, norm, g_s, 0);
   PF_WAIT_VMCNT(0);
   __syncthreads();
 
@@ -302,14 +324,16 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_kernel(
   // they are and keeps the accumulators in one place.
   for (int kt = 0; kt < nk; kt += 2) {
     pf_dma_b(b1a, dma, W1, (int64_t)(kt + 1) * PF_BK, N, K, w);
-    pf_load_a(sa, xr, gr, m0, (int64_t)(kt + 2) * PF_BK, M, K, tid);
-    pf_step<9>(a_s0, b0s, a_s1, sb, acc, ss, a_base, bo0, bo1, tid, norm);
-    PF_WAIT_VMCNT(5);
+    pf_load_a<GL>(sa, xr, gr, m0, (int64_t)(kt + 2) * PF_BK, M, K, tid);
+    pf_step<XL + 4, GL>(a_s0, b0s, a_s1, sb, acc, ss, a_base, bo0, bo1, tid, norm, g_s,
+                        (int64_t)(kt + 1) * PF_BK);
+    PF_WAIT_VMCNT(XL);
     __syncthreads();
     pf_dma_b(b0a, dma, W1, (int64_t)(kt + 2) * PF_BK, N, K, w);
-    pf_load_a(sb, xr, gr, m0, (int64_t)(kt + 3) * PF_BK, M, K, tid);
-    pf_step<9>(a_s1, b1s, a_s0, sa, acc, ss, a_base, bo0, bo1, tid, norm);
-    PF_WAIT_VMCNT(5);
+    pf_load_a<GL>(sb, xr, gr, m0, (int64_t)(kt + 3) * PF_BK, M, K, tid);
+    pf_step<XL + 4, GL>(a_s1, b1s, a_s0, sa, acc, ss, a_base, bo0, bo1, tid, norm, g_s,
+                        (int64_t)(kt + 2) * PF_BK);
+    PF_WAIT_VMCNT(XL);
     __syncthreads();
   }
   PF_WAIT_VMCNT(0);
@@ -359,9 +383,15 @@ hipError_t rmm_launch_prefill(const RmmArgs& a, const PrefillPlan& p) {
   using namespace rmm;
   if (a.gated) return hipErrorInvalidValue;
   const unsigned grid = (unsigned)((int64_t)p.tiles_m * p.tiles_n);
-  hipLaunchKernelGGL((prefill_kernel<false>), dim3(grid), dim3(PF_THREADS), 0, a.stream,
-                     (const bf16_t*)a.X, (const bf16_t*)a.g, (const bf16_t*)a.W1,
-                     (const bf16_t*)a.W3, (bf16_t*)a.Y, a.eps, a.M, a.N, a.K, p.tiles_m,
-                     p.tiles_n, p.group_m, p.xcd_remap, a.norm);
+  if (a.K <= PF_G_LDS_MAX)
+    hipLaunchKernelGGL((prefill_kernel<false, true>), dim3(grid), dim3(PF_THREADS), 0, a.stream,
+                       (const bf16_t*)a.X, (const bf16_t*)a.g, (const bf16_t*)a.W1,
+                       (const bf16_t*)a.W3, (bf16_t*)a.Y, a.eps, a.M, a.N, a.K, p.tiles_m,
+                       p.tiles_n, p.group_m, p.xcd_remap, a.norm);
+  else
+    hipLaunchKernelGGL((prefill_kernel<false, false>), dim3(grid), dim3(PF_THREADS), 0, a.stream,
+                       (const bf16_t*)a.X, (const bf16_t*)a.g, (const bf16_t*)a.W1,
+                       (const bf16_t*)a.W3, (bf16_t*)a.Y, a.eps, a.M, a.N, a.K, p.tiles_m,
+                       p.tiles_n, p.group_m, p.xcd_remap, a.norm);
   return hipGetLastError();
 }

@@ -46,6 +46,10 @@ def load(path: str = _LIB):
     lib.rmm_oracle_matmul_f64.restype = ctypes.c_int
     lib.rmm_oracle_gated_matmul_f64.argtypes = [vp, vp, vp, i64, i64, i64, vp]
     lib.rmm_oracle_gated_matmul_f64.restype = ctypes.c_int
+    lib.rmm_oracle_rmsnorm_lora_f64.argtypes = [vp, vp, vp, vp, vp, dbl, i64, i64, i64, i64, vp]
+    lib.rmm_oracle_rmsnorm_lora_f64.restype = ctypes.c_int
+    lib.rmm_oracle_lora_matmul_f64.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, vp]
+    lib.rmm_oracle_lora_matmul_f64.restype = ctypes.c_int
     return lib
 
 
@@ -132,6 +136,38 @@ def gated_matmul(A, W1, W3, lib=None) -> np.ndarray:
     assert K2 == K and W3.shape == W1.shape
     Y = np.empty((M, N), np.float64)
     rc = lib.rmm_oracle_gated_matmul_f64(_p(A), _p(W1), _p(W3), M, N, K, _p(Y))
+    if rc != 0:
+        raise ValueError(f"oracle error {rc}")
+    return Y
+
+
+def rmsnorm_lora(X, g, W, A, B, eps, lib=None) -> np.ndarray:
+    """Y = Nrm @ W + (Nrm @ A.T) @ B in fp64, Nrm = RMSNorm(X; g, eps).
+    X: [M,K], g: [K], W: [K,N], A: [R,K] (down-projection rows), B: [R,N]."""
+    lib = lib or _default()
+    X, g, W, A, B = _d(X), _d(g), _d(W), _d(A), _d(B)
+    M, K = X.shape
+    K2, N = W.shape
+    R = A.shape[0]
+    assert K2 == K and g.shape == (K,) and A.shape == (R, K) and B.shape == (R, N)
+    Y = np.empty((M, N), np.float64)
+    rc = lib.rmm_oracle_rmsnorm_lora_f64(_p(X), _p(g), _p(W), _p(A), _p(B), float(eps), M, N, K,
+                                         R, _p(Y))
+    if rc != 0:
+        raise ValueError(f"oracle error {rc}")
+    return Y
+
+
+def lora_matmul(X, W, A, B, lib=None) -> np.ndarray:
+    """Y = X @ W + (X @ A.T) @ B in fp64 (the adapter without the norm)."""
+    lib = lib or _default()
+    X, W, A, B = _d(X), _d(W), _d(A), _d(B)
+    M, K = X.shape
+    K2, N = W.shape
+    R = A.shape[0]
+    assert K2 == K and A.shape == (R, K) and B.shape == (R, N)
+    Y = np.empty((M, N), np.float64)
+    rc = lib.rmm_oracle_lora_matmul_f64(_p(X), _p(W), _p(A), _p(B), M, N, K, R, _p(Y))
     if rc != 0:
         raise ValueError(f"oracle error {rc}")
     return Y

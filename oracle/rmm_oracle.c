@@ -28,6 +28,14 @@
  * the page does not define it, the reading is SwiGLU):
  *   Z1 = Nrm * W1,  Z3 = Nrm * W3,  Y = Z1 / (1 + exp(-Z1)) * Z3.
  *
+ * LoRA (paper review, section "五、实验结果", the LoRA row; the page names the
+ * benchmark only, the reading is the usual low-rank adapter): the frozen
+ * product plus a rank-R update applied as two thin products,
+ *   T = Act * A^T   (A: R x K, row r is the r-th down-projection vector),
+ *   Y = Act * W + T * B   (B: R x N),
+ * with Act = Nrm (rmm_oracle_rmsnorm_lora_f64) or X itself
+ * (rmm_oracle_lora_matmul_f64, the adapter alone).
+ *
  * The steps are also exported one by one (rmm_oracle_rmsnorm_f64: steps 1-2,
  * rmm_oracle_matmul_f64: step 3, rmm_oracle_gated_matmul_f64: the two
  * products and the gate), because the unfused program is itself measured:
@@ -157,4 +165,54 @@ int rmm_oracle_gated_matmul_f64(const double* A, const double* W1, const double*
                                 int64_t N, int64_t K, double* Y) {
   if (M < 0 || N < 0 || K <= 0) return 1;
   return gated_products(A, W1, W3, M, N, K, Y);
+}
+
+/* LoRA on activations Act: Y = Act W + (Act A^T) B.  A: R x K, B: R x N. */
+static int lora_products(const double* Act, const double* W, const double* A, const double* B,
+                         int64_t M, int64_t N, int64_t K, int64_t R, double* Y) {
+  double* T = (double*)malloc(sizeof(double) * (size_t)(M * R > 0 ? M * R : 1));
+  if (!T) return 2;
+  matmul(Act, W, M, N, K, Y);
+#pragma omp parallel for schedule(static)
+  for (int64_t m = 0; m < M; ++m) {
+    for (int64_t r = 0; r < R; ++r) {
+      double t = 0.0;
+      for (int64_t k = 0; k < K; ++k) t += Act[m * K + k] * A[r * K + k];
+      T[m * R + r] = t;
+    }
+    for (int64_t r = 0; r < R; ++r) {
+      const double t = T[m * R + r];
+      for (int64_t n = 0; n < N; ++n) Y[m * N + n] += t * B[r * N + n];
+    }
+  }
+  free(T);
+  return 0;
+}
+
+/* Y = Nrm W + (Nrm A^T) B with Nrm the normalised, gained rows. */
+int rmm_oracle_rmsnorm_lora_f64(const double* X, const double* g, const double* W,
+                                const double* A, const double* B, double eps, int64_t M,
+                                int64_t N, int64_t K, int64_t R, double* Y) {
+  if (M < 0 || N < 0 || K <= 0 || R <= 0) return 1;
+  double* r = (double*)malloc(sizeof(double) * (size_t)(M > 0 ? M : 1));
+  double* Nrm = (double*)malloc(sizeof(double) * (size_t)(M > 0 ? M * K : 1));
+  if (!r || !Nrm) {
+    free(r);
+    free(Nrm);
+    return 2;
+  }
+  row_rms(X, M, K, eps, r);
+  normalise(X, g, r, M, K, Nrm);
+  const int rc = lora_products(Nrm, W, A, B, M, N, K, R, Y);
+  free(r);
+  free(Nrm);
+  return rc;
+}
+
+/* The adapter on raw activations: Y = X W + (X A^T) B. */
+int rmm_oracle_lora_matmul_f64(const double* X, const double* W, const double* A,
+                               const double* B, int64_t M, int64_t N, int64_t K, int64_t R,
+                               double* Y) {
+  if (M < 0 || N < 0 || K <= 0 || R <= 0) return 1;
+  return lora_products(X, W, A, B, M, N, K, R, Y);
 }

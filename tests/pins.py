@@ -12,7 +12,9 @@ every expected value below is a closed form or a property of the definition):
   * the normalised rows' mean square, S / (S + eps), when W = I;
   * invariants: scale law, gain folding, linearity, permutations;
   * exact rational / 50-digit brute force on tiny shapes;
-  * the gate's closed forms at z = +-ln 3 (sigmoid = 3/4 and 1/4 exactly).
+  * the gate's closed forms at z = +-ln 3 (sigmoid = 3/4 and 1/4 exactly);
+  * LoRA: a hand-worked 1x2 example, B = 0, and the merged-weight identity
+    Act W + (Act A^T) B = Act (W + A^T B) on exactly representable inputs.
 """
 from __future__ import annotations
 
@@ -278,6 +280,52 @@ def pin_unfused_steps(lib):
     assert np.array_equal(oracle.gated_matmul(n, W, W3r, lib=lib), _gated(lib, X, g, W, W3r, 1e-3))
 
 
+def pin_lora(lib):
+    # Hand-worked: X = [3, 4], g = [1, 2], eps = 12.5 -> Nrm = [0.6, 1.6];
+    # W = [[1, 0], [1, 2]] -> Nrm W = [2.2, 3.2].  Rank 1: A = [1, -1] gives
+    # T = -1, B = [2, -1] adds [-2, 1].  Rank 2 adds A row [0, 1] (T = 1.6)
+    # with B row [1, 1]: T B = [-2 + 1.6, 1 + 1.6].
+    X, g = np.array([[3.0, 4.0]]), np.array([1.0, 2.0])
+    W = np.array([[1.0, 0.0], [1.0, 2.0]])
+    A, B = np.array([[1.0, -1.0], [0.0, 1.0]]), np.array([[2.0, -1.0], [1.0, 1.0]])
+    _close(oracle.rmsnorm_lora(X, g, W, A[:1], B[:1], 12.5, lib=lib), [[0.2, 4.2]])
+    _close(oracle.rmsnorm_lora(X, g, W, A, B, 12.5, lib=lib), [[1.8, 5.8]])
+    # Without the norm, by hand: X W = [7, 8], X A^T = [-1, 4], T B = [-2 + 4, 1 + 4].
+    _close(oracle.lora_matmul(X, W, A, B, lib=lib), [[9.0, 13.0]])
+    rng = np.random.default_rng(33)
+    for (M, K, N, R) in ((3, 8, 5, 2), (4, 6, 7, 6), (2, 5, 3, 9), (1, 1, 1, 1)):
+        # B = 0: the plain fused product, bit for bit.
+        Xf = rng.normal(size=(M, K))
+        gf = rng.normal(1.0, 0.2, size=K)
+        Wf = rng.normal(size=(K, N))
+        Af = rng.normal(size=(R, K))
+        assert np.array_equal(oracle.rmsnorm_lora(Xf, gf, Wf, Af, np.zeros((R, N)), 1e-3, lib=lib),
+                              _mm(lib, Xf, gf, Wf, 1e-3))
+        # Merged weights on exact inputs: rows of +-2^j (RMS 2^j with eps = 0),
+        # small-integer g, W, A, B; every value is a short dyadic rational, so
+        # both sides are exact and must agree bit for bit.  R = K (case 2)
+        # tells A from A^T.
+        Xi = rng.choice([-1.0, 1.0], size=(M, K)) * np.exp2(rng.integers(-3, 4, size=(M, 1)))
+        gi = rng.integers(1, 4, size=K).astype(np.float64)
+        Wi = rng.integers(-3, 4, size=(K, N)).astype(np.float64)
+        Ai = rng.integers(-3, 4, size=(R, K)).astype(np.float64)
+        Bi = rng.integers(-3, 4, size=(R, N)).astype(np.float64)
+        merged = Wi + Ai.T @ Bi
+        assert np.array_equal(oracle.rmsnorm_lora(Xi, gi, Wi, Ai, Bi, 0.0, lib=lib),
+                              _mm(lib, Xi, gi, merged, 0.0))
+        assert np.array_equal(oracle.lora_matmul(Xi, Wi, Ai, Bi, lib=lib), Xi @ merged)
+        # Brute force: 50-digit rows, then exact-rational sums of the two terms.
+        eps = 0.25
+        nrm = _brute_rows(Xf.tolist(), gf.tolist(), eps)
+        Bf = rng.normal(size=(R, N))
+        T = [[sum(Fraction(nrm[m, k]) * Fraction(Af[r, k]) for k in range(K)) for r in range(R)]
+             for m in range(M)]
+        want = [[float(sum(Fraction(nrm[m, k]) * Fraction(Wf[k, n]) for k in range(K))
+                       + sum(T[m][r] * Fraction(Bf[r, n]) for r in range(R)))
+                 for n in range(N)] for m in range(M)]
+        _close(oracle.rmsnorm_lora(Xf, gf, Wf, Af, Bf, eps, lib=lib), want, rtol=1e-12, atol=1e-12)
+
+
 ALL_PINS = [pin_worked_example, pin_library_matmul, pin_identity_weight, pin_constant_row,
             pin_scale_law, pin_gain_fold, pin_structure, pin_zero_row, pin_brute_force,
-            pin_gated_closed_forms, pin_unfused_steps]
+            pin_gated_closed_forms, pin_unfused_steps, pin_lora]

@@ -27,6 +27,16 @@ MUTANTS = {
     "gate_swapped": ("z1 / (1.0 + exp(-z1)) * Z3[i]", "Z3[i] / (1.0 + exp(-Z3[i])) * z1"),
     "gate_no_silu": ("z1 / (1.0 + exp(-z1)) * Z3[i]", "z1 * Z3[i]"),
     "gate_both_w1": ("matmul(A, W3, M, N, K, Z3);", "matmul(A, W1, M, N, K, Z3);"),
+    "lora_a_transposed": ("t += Act[m * K + k] * A[r * K + k];",
+                          "t += Act[m * K + k] * A[(k * R + r) % (R * K)];"),
+    "lora_term_dropped": ("Y[m * N + n] += t * B[r * N + n];", "Y[m * N + n] += 0.0 * B[r * N + n];"),
+    "lora_term_sign": ("Y[m * N + n] += t * B[r * N + n];", "Y[m * N + n] -= t * B[r * N + n];"),
+    "lora_b_row_wrong": ("Y[m * N + n] += t * B[r * N + n];",
+                         "Y[m * N + n] += t * B[((r + 1) % R) * N + n];"),
+    "lora_raw_x": ("lora_products(Nrm, W, A, B, M, N, K, R, Y);",
+                   "lora_products(X, W, A, B, M, N, K, R, Y);"),
+    "lora_last_rank_skipped": ("for (int64_t r = 0; r < R; ++r) {\n      double t = 0.0;",
+                               "for (int64_t r = 0; r < R - 1; ++r) {\n      double t = 0.0;"),
 }
 
 

@@ -83,6 +83,8 @@ def cpu_baseline(wl, inp, budget_s: float):
         t0 = time.perf_counter()
         if wl.gated:
             oracle.rmsnorm_gated_mlp(Xs, inp.g, inp.W1, inp.W3, eps)
+        elif wl.lora:
+            oracle.rmsnorm_lora(Xs, inp.g, inp.W1, inp.LA, inp.LB, eps)
         else:
             oracle.rmsnorm_matmul(Xs, inp.g, inp.W1, eps)
         return time.perf_counter() - t0
@@ -168,7 +170,8 @@ def main():
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
 
-    base = {n: dev_tensor(n) for n in (["X", "g", "W1"] + (["W3"] if wl.gated else []))}
+    base = {n: dev_tensor(n) for n in (["X", "g", "W1"] + (["W3"] if wl.gated else [])
+                                         + (["LA", "LB"] if wl.lora else []))}
     per_set = wl.algo_bytes()
     free = torch.cuda.mem_get_info(dev)[0]
     R = max(1, math.ceil(ROTATE_BYTES / per_set))
@@ -178,15 +181,24 @@ def main():
         s = {n: (t if r == 0 else t.clone()) for n, t in base.items()}
         s["Y"] = torch.empty((wl.M, wl.N), dtype=s["X"].dtype, device=dev)
         sets.append(s)
-    st, variant, splits = tpa.plan(wl.M, wl.N, wl.K, dtype=sets[0]["X"].dtype, gated=wl.gated,
-                                   variant=args.variant, splits=args.splits)
+    if wl.lora:
+        st, variant, splits = tpa.plan_lora(wl.M, wl.N, wl.K, wl.lora, dtype=sets[0]["X"].dtype,
+                                            variant=args.variant, splits=args.splits)
+    else:
+        st, variant, splits = tpa.plan(wl.M, wl.N, wl.K, dtype=sets[0]["X"].dtype,
+                                       gated=wl.gated, variant=args.variant, splits=args.splits)
     if st != 0:
         raise SystemExit(f"plan failed with status {st}")
     log(f"variant {variant}, splits {splits}, {R} rotating input sets "
         f"({R * per_set / 2**20:.0f} MiB)")
     stream = torch.cuda.Stream(dev)
-    nbytes = tpa._binding.workspace_bytes(tpa._DTYPES[sets[0]["X"].dtype], wl.M, wl.N, wl.K,
-                                          wl.gated, args.variant, args.splits)
+    dcode = tpa._DTYPES[sets[0]["X"].dtype]
+    if wl.lora:
+        nbytes = tpa._binding.lora_workspace_bytes(dcode, wl.M, wl.N, wl.K, wl.lora, args.variant,
+                                                   args.splits)
+    else:
+        nbytes = tpa._binding.workspace_bytes(dcode, wl.M, wl.N, wl.K, wl.gated, args.variant,
+                                              args.splits)
     ws = tpa.Workspace(nbytes, dev) if nbytes > 0 else None
     torch.cuda.synchronize()
 
@@ -194,6 +206,9 @@ def main():
         if wl.gated:
             tpa.rmsnorm_gated_mlp(s["X"], s["g"], s["W1"], s["W3"], wl.eps, out=s["Y"],
                                   variant=args.variant, splits=args.splits, workspace=ws)
+        elif wl.lora:
+            tpa.rmsnorm_lora(s["X"], s["g"], s["W1"], s["LA"], s["LB"], wl.eps, out=s["Y"],
+                             variant=args.variant, splits=args.splits, workspace=ws)
         else:
             tpa.rmsnorm_matmul(s["X"], s["g"], s["W1"], wl.eps, out=s["Y"],
                                variant=args.variant, splits=args.splits, workspace=ws)
@@ -265,12 +280,16 @@ def main():
     unfused = None
     if not args.no_unfused:
         xn = [torch.empty_like(s["X"]) for s in sets]
+        # the vendor leg multiplies by A^T as a K x R matrix (made once, untimed)
+        at = [s["LA"].t().contiguous() for s in sets] if wl.lora else None
 
         def unfused_ours(i):
             s = sets[i]
             tpa.rmsnorm(s["X"], s["g"], wl.eps, out=xn[i])
             if wl.gated:
                 tpa.gated_matmul(xn[i], s["W1"], s["W3"], out=s["Y"], workspace=ws)
+            elif wl.lora:
+                tpa.lora_matmul(xn[i], s["W1"], s["LA"], s["LB"], out=s["Y"], workspace=ws)
             else:
                 tpa.matmul(xn[i], s["W1"], out=s["Y"], workspace=ws)
 
@@ -280,6 +299,9 @@ def main():
             if wl.gated:
                 torch.mul(torch.nn.functional.silu(torch.matmul(xn[i], s["W1"])),
                           torch.matmul(xn[i], s["W3"]), out=s["Y"])
+            elif wl.lora:
+                torch.addmm(torch.matmul(xn[i], s["W1"]), torch.matmul(xn[i], at[i]), s["LB"],
+                            out=s["Y"])
             else:
                 torch.matmul(xn[i], s["W1"], out=s["Y"])
 
@@ -294,7 +316,8 @@ def main():
             "vendor_gemm_ms_per_step": ms_v / steps, "fused_speedup_vs_vendor_gemm": ms_v / ms,
             "normalised_x_bytes": 2 * wl.M * wl.K * wl.elem_bytes,
             "note": "rmm_rmsnorm writes X*g/RMS to memory, then rmm_matmul (this library's "
-                    "kernels) or torch.matmul (hipBLASLt) reads it back"}
+                    "kernels; rmm_lora_matmul with the adapter) or torch.matmul (hipBLASLt; "
+                    "with the adapter, three products) reads it back"}
         log(f"unfused: {ms_u / steps * 1e3:.2f} us/step (ours), {ms_v / steps * 1e3:.2f} us/step "
             f"(vendor GEMM); fused {ms / steps * 1e3:.2f}")
 
@@ -325,6 +348,7 @@ def main():
         "warmup": warm, "ms_per_step": ms / steps, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
         "config": {"workload": wl.name, "M": wl.M, "K": wl.K, "N": wl.N, "gated": wl.gated,
+                   "lora_rank": wl.lora,
                    "eps": wl.eps, "variant": variant, "splits": splits,
                    "rotating_input_sets": R, "hip_graph": graph is not None,
                    "clock_settle_calls": settle_calls},

@@ -38,16 +38,18 @@
  * Workspace.  The decode (split-K) variant combines partial k-sums across
  * workgroups through a caller-owned workspace.  `ws` may be NULL: the library
  * then picks a variant that needs none (correct, slower).  A non-NULL `ws` must
- * be zero-filled before its first use; the kernels leave it zeroed again
- * (their arrival counters reset themselves), so it can be reused by later
- * calls on the same stream without clearing.  One workspace must not be used
+ * be zero-filled before its first use; the kernels reset its arrival counters
+ * to zero (the partial-sum slots keep the last call's values, which every
+ * call overwrites before reading), so it can be reused by later calls on the
+ * same stream without clearing.  One workspace must not be used
  * by two calls that may run at the same time.  ws_bytes below
  * rmm_workspace_bytes*() returns RMM_ERR_WORKSPACE.
  *
  * Errors.  Validation happens on the host before any HIP call, in this order:
  *   RMM_ERR_NULL      a NULL data pointer (when M*N > 0)
  *   RMM_ERR_SHAPE     M < 0, N < 0, K <= 0 (the mean over an empty row is
- *                     undefined), or an element count that overflows int64
+ *                     undefined), an adapter rank outside 1..64, or an
+ *                     element count that overflows int64
  *   RMM_ERR_EPS       eps negative or not finite (eps = 0 is allowed)
  *   RMM_ERR_DTYPE     unknown dtype
  *   RMM_ERR_ALIAS     Y's byte range overlaps an input or the workspace
@@ -158,6 +160,42 @@ rmm_status rmm_gated_matmul(const void* X, const void* W1, const void* W3, void*
                             int64_t N, int64_t K, rmm_dtype dtype, void* ws, size_t ws_bytes,
                             hipStream_t stream);
 
+/* Low-rank adapter (LoRA), the LoRA row of the same page's benchmark table
+ * ("五、实验结果"; the page names the benchmark only, the reading is the usual
+ * adapter): the frozen product plus a rank-R update applied as two thin
+ * products,
+ *
+ *   rmsnorm_lora:    Y = Nrm W + (Nrm A^T) B,   Nrm = RMSNorm(X; g, eps)
+ *   rmm_lora_matmul: Y = X W + (X A^T) B        (no gain, no 1/RMS scale)
+ *
+ * Layouts: A is R x K row-major (row r is the r-th down-projection vector,
+ * A[r*K + k]; the layout of a torch Linear(K, R) weight), B is R x N
+ * row-major (B[r*N + n]); both in the call's dtype, 1 <= R <= 64
+ * (RMM_LORA_MAX_RANK, else RMM_ERR_SHAPE).  The down-projection T = Act A^T
+ * is summed in fp32 from the same operand the weight product uses (bf16:
+ * X*g rounded once), kept in fp32 (never rounded to the storage type), and
+ * T B is added to the k-sum before the 1/RMS scale, so one rounding produces
+ * Y.  Not combined with the gate.  Variants: DECODE (bf16, M <= 32, R <= 32;
+ * the down-projection partials travel with the split-K partials) and
+ * GENERIC (everything else); forcing PREFILL or STREAM returns
+ * RMM_ERR_VARIANT.  NULL checks cover A and B; Y must not overlap them.
+ * Workspace rules are those of rmsnorm_matmul, sized by
+ * rmm_lora_workspace_bytes (variant = RMM_VARIANT_AUTO, splits = 0 for the
+ * plain entry points). */
+#define RMM_LORA_MAX_RANK 64
+rmm_status rmsnorm_lora(const void* X, const void* g, const void* W, const void* A, const void* B,
+                        void* Y, float eps, int64_t M, int64_t N, int64_t K, int64_t R,
+                        rmm_dtype dtype, void* ws, size_t ws_bytes, hipStream_t stream);
+rmm_status rmsnorm_lora_ex(const void* X, const void* g, const void* W, const void* A,
+                           const void* B, void* Y, float eps, int64_t M, int64_t N, int64_t K,
+                           int64_t R, rmm_dtype dtype, rmm_variant variant, int splits, void* ws,
+                           size_t ws_bytes, hipStream_t stream);
+rmm_status rmm_lora_matmul(const void* X, const void* W, const void* A, const void* B, void* Y,
+                           int64_t M, int64_t N, int64_t K, int64_t R, rmm_dtype dtype, void* ws,
+                           size_t ws_bytes, hipStream_t stream);
+size_t rmm_lora_workspace_bytes(rmm_dtype dtype, int64_t M, int64_t N, int64_t K, int64_t R,
+                                rmm_variant variant, int splits);
+
 /* Workspace bytes the call with these arguments would use (0 if none).  The
  * plain entry points use variant = AUTO, splits = 0.  Returns 0 for
  * arguments that would fail validation. */
@@ -173,6 +211,13 @@ rmm_status rmm_plan(const void* X, const void* g, const void* W1, const void* W3
                     float eps, int64_t M, int64_t N, int64_t K, rmm_dtype dtype, int gated,
                     rmm_variant variant, int splits, const void* ws, size_t ws_bytes,
                     rmm_variant* variant_out, int* splits_out);
+
+/* rmm_plan for the adapter entry points (A, B, R as in rmsnorm_lora). */
+rmm_status rmm_plan_lora(const void* X, const void* g, const void* W, const void* A,
+                         const void* B, const void* Y, float eps, int64_t M, int64_t N, int64_t K,
+                         int64_t R, rmm_dtype dtype, rmm_variant variant, int splits,
+                         const void* ws, size_t ws_bytes, rmm_variant* variant_out,
+                         int* splits_out);
 
 const char* rmm_status_string(rmm_status s);
 int rmm_last_hip_error(void);

@@ -22,6 +22,7 @@ _lib = None
 # Tensor streams of the generator.
 STREAM_X, STREAM_G, STREAM_W1, STREAM_W3, STREAM_ROWSCALE, STREAM_ROWPICK = 1, 2, 3, 4, 5, 6
 STREAM_EXACT = 7
+STREAM_LA, STREAM_LB = 20, 21  # adapter down- and up-projection (clear of the exact streams)
 
 
 def build(force: bool = False) -> str:
@@ -136,11 +137,12 @@ class Inputs:
     bf16 workloads, i.e. exactly what is handed to the library.
     """
 
-    def __init__(self, wl, X, g, W1, W3, rows):
+    def __init__(self, wl, X, g, W1, W3, rows, LA=None, LB=None):
         self.wl, self.rows = wl, rows
         self.bits = {}
+        self.LA, self.LB = LA, LB  # adapter: [R, K] and [R, N], or None
         if wl.dtype == "bf16":
-            for name, a in (("X", X), ("g", g), ("W1", W1), ("W3", W3)):
+            for name, a in (("X", X), ("g", g), ("W1", W1), ("W3", W3), ("LA", LA), ("LB", LB)):
                 if a is not None:
                     b = to_bf16_bits(a)
                     self.bits[name] = b
@@ -166,24 +168,28 @@ def make_inputs(wl: "Workload", seed: int = 0, rows=None, weights: bool = True) 
         X = normals(seed, STREAM_X, len(rows), K,
                     row_scale=None if scale is None else scale[rows], row_idx=rows)
     g = normals(seed, STREAM_G, 1, K, mul=0.1, add=1.0).reshape(K)
-    W1 = W3 = None
+    W1 = W3 = LA = LB = None
     if weights:
         W1 = normals(seed, STREAM_W1, K, N, mul=1.0 / np.sqrt(K))
         if wl.gated:
             W3 = normals(seed, STREAM_W3, K, N, mul=1.0 / np.sqrt(K))
-    return Inputs(wl, X, g, W1, W3, rows)
+        if wl.lora:
+            LA = normals(seed, STREAM_LA, wl.lora, K, mul=1.0 / np.sqrt(K))
+            LB = normals(seed, STREAM_LB, wl.lora, N, mul=1.0 / np.sqrt(wl.lora))
+    return Inputs(wl, X, g, W1, W3, rows, LA, LB)
 
 
 def make_exact_inputs(M: int, K: int, N: int, dtype: str, seed: int = 0, gated: bool = False,
-                      density: float = 0.25, row_pow2: bool = False) -> Inputs:
+                      density: float = 0.25, row_pow2: bool = False, lora: int = 0) -> Inputs:
     """Inputs on which fp32 accumulation (and bf16 storage of X*g) is exact.
 
     X in {+-1} (optionally each row times 2^j, j in [-6, 6]), g in {1, 2},
-    W in {-2..2} with the given density; used with eps = 0, so the row RMS is
-    1 (or 2^j) exactly and every product and partial sum is a small integer
-    times a power of two, whatever the order of summation.
+    W (and the adapter's A and B) in {-2..2} with the given density; used with
+    eps = 0, so the row RMS is 1 (or 2^j) exactly and every product and
+    partial sum is a small integer times a power of two, whatever the order of
+    summation (below 2^24 for K up to 2^12 and ranks up to 64).
     """
-    wl = Workload("exact", dtype, M, K, N, 0.0, gated, None)
+    wl = Workload("exact", dtype, M, K, N, 0.0, gated, None, lora)
     X = exact_values(seed, STREAM_EXACT, (M, K), 0)
     if row_pow2:
         j = (hashes(seed, STREAM_EXACT + 4, 0, M, 0) % np.uint64(13)).astype(np.int64) - 6
@@ -191,4 +197,6 @@ def make_exact_inputs(M: int, K: int, N: int, dtype: str, seed: int = 0, gated: 
     g = exact_values(seed, STREAM_EXACT + 1, (K,), 1)
     W1 = exact_values(seed, STREAM_EXACT + 2, (K, N), 2, density)
     W3 = exact_values(seed, STREAM_EXACT + 3, (K, N), 2, density) if gated else None
-    return Inputs(wl, X, g, W1, W3, None)
+    LA = exact_values(seed, STREAM_EXACT + 5, (lora, K), 2, density) if lora else None
+    LB = exact_values(seed, STREAM_EXACT + 6, (lora, N), 2, density) if lora else None
+    return Inputs(wl, X, g, W1, W3, None, LA, LB)

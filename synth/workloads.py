@@ -1,7 +1,9 @@
-"""The five synthetic workloads of the fused RMSNorm+MatMul path.
+"""The synthetic workloads of the fused RMSNorm+MatMul path.
 
 Shapes and value distributions (all seed 0, one generator stream per tensor):
-  X ~ N(0,1) (optionally row-scaled), g ~ 1 + 0.1 N(0,1), W ~ N(0, 1/K).
+  X ~ N(0,1) (optionally row-scaled), g ~ 1 + 0.1 N(0,1), W ~ N(0, 1/K);
+  with a low-rank adapter of rank R: A ~ N(0, 1/K) (R x K), B ~ N(0, 1/R)
+  (R x N), so the adapter term has the size of the frozen product.
 The pages give no shapes; these stand in for their (unnamed) benchmarks.
 """
 from __future__ import annotations
@@ -19,6 +21,7 @@ class Workload:
     eps: float
     gated: bool
     row_scale: str | None   # None, "pick_x100" (1% of rows x100) or "loguniform"
+    lora: int = 0           # adapter rank R (0: none)
 
     @property
     def n_weights(self) -> int:
@@ -29,13 +32,14 @@ class Workload:
         return 4 if self.dtype == "f32" else 2
 
     def flops(self) -> int:
-        """Algorithmic flops: 2*M*N*K per contraction."""
-        return 2 * self.M * self.N * self.K * self.n_weights
+        """Algorithmic flops: 2*M*N*K per contraction (the adapter: 2*M*R*(K + N))."""
+        return 2 * self.M * self.N * self.K * self.n_weights + 2 * self.M * self.lora * (
+            self.K + self.N)
 
     def algo_bytes(self) -> int:
         """Algorithmic HBM bytes: every input once and Y once."""
         return (self.M * self.K + self.K + self.n_weights * self.K * self.N
-                + self.M * self.N) * self.elem_bytes
+                + self.lora * (self.K + self.N) + self.M * self.N) * self.elem_bytes
 
 
 WORKLOADS = {
@@ -47,6 +51,8 @@ WORKLOADS = {
         Workload("gated_m64_k4096_n14336", "bf16", 64, 4096, 14336, 1e-6, True, None),
         Workload("large_m8192_k8192_n28672", "bf16", 8192, 8192, 28672, 1e-5, False,
                  "loguniform"),
+        # the adapter on the decode shape, so its cost over the plain call shows
+        Workload("lora_m16_k4096_n6144_r16", "bf16", 16, 4096, 6144, 1e-6, False, None, 16),
     )
 }
 

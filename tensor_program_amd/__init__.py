@@ -9,6 +9,10 @@
     y = tpa.matmul(xn, w)                             # plain product
     y = tpa.gated_matmul(xn, w1, w3)                  # silu(xn @ w1) * (xn @ w3)
 
+    # low-rank adapter (a: [R, K] down-projection rows, b: [R, N])
+    y = tpa.rmsnorm_lora(x, g, w, a, b, eps)          # norm(x) @ w + (norm(x) @ a.T) @ b
+    y = tpa.lora_matmul(x, w, a, b)                   # x @ w + (x @ a.T) @ b
+
 x: [M, K], g: [K], w/w1/w3: [K, N], all contiguous, on one GPU, all float32 or
 all bfloat16.  The work is enqueued on torch's current stream; this module
 only marshals arguments (see include/rmm.h for the contract).
@@ -21,7 +25,7 @@ from . import _binding
 from ._binding import RmmError, load_library  # noqa: F401
 
 __all__ = ["rmsnorm_matmul", "rmsnorm_gated_mlp", "rmsnorm", "matmul", "gated_matmul",
-           "RmmError", "load_library", "Workspace"]
+           "rmsnorm_lora", "lora_matmul", "RmmError", "load_library", "Workspace"]
 
 _DTYPES = {torch.float32: _binding.DTYPE_F32, torch.bfloat16: _binding.DTYPE_BF16}
 
@@ -29,7 +33,8 @@ _DTYPES = {torch.float32: _binding.DTYPE_F32, torch.bfloat16: _binding.DTYPE_BF1
 class Workspace:
     """A zero-filled device workspace for the split-K variant.
 
-    The kernels leave it zeroed after every call, so one workspace serves any
+    The kernels reset its arrival counters after every call (the partial-sum
+    slots are overwritten before they are read), so one workspace serves any
     number of calls on one stream.  Calls that may overlap (different streams)
     need different workspaces.
     """
@@ -179,6 +184,68 @@ def matmul(x, w, out=None, workspace: Workspace | None = None):
 def gated_matmul(x, w1, w3, out=None, workspace: Workspace | None = None):
     """Y = silu(x @ w1) * (x @ w3) with the same kernels, no norm."""
     return _plain(x, w1, w3, out, workspace)
+
+
+def _lora(x, g, w, a, b, eps, out, variant, splits, workspace, norm):
+    tensors = [x, w, a, b] + ([g] if norm else [])
+    _check_operands(tensors, ["x", "w", "a", "b", "g"][:len(tensors)])
+    if x.dim() != 2 or w.dim() != 2 or a.dim() != 2 or b.dim() != 2 or (norm and g.dim() != 1):
+        raise ValueError("expected x: [M, K], g: [K], w: [K, N], a: [R, K], b: [R, N]")
+    M, K = x.shape
+    N = w.shape[1]
+    R = a.shape[0]
+    if w.shape[0] != K or tuple(a.shape) != (R, K) or tuple(b.shape) != (R, N) or \
+            (norm and g.shape[0] != K):
+        raise ValueError(f"shape mismatch: x {tuple(x.shape)}, w {tuple(w.shape)}, "
+                         f"a {tuple(a.shape)}, b {tuple(b.shape)}")
+    if out is None:
+        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    else:
+        _check_operands([x, out], ["x", "out"])
+        if tuple(out.shape) != (M, N):
+            raise ValueError(f"out has shape {tuple(out.shape)}, expected {(M, N)}")
+    lib = load_library()
+    dtype = _DTYPES[x.dtype]
+    stream = torch.cuda.current_stream(x.device).cuda_stream
+    need = _binding.lora_workspace_bytes(dtype, M, N, K, R, variant, splits)
+    if workspace is None and need > 0:
+        workspace = _workspace_for(x.device, stream, need)
+    ws_ptr = workspace.ptr if workspace is not None else None
+    ws_bytes = workspace.nbytes if workspace is not None else 0
+    if norm:
+        st = lib.rmsnorm_lora_ex(x.data_ptr(), g.data_ptr(), w.data_ptr(), a.data_ptr(),
+                                 b.data_ptr(), out.data_ptr(), float(eps), M, N, K, R, dtype,
+                                 _binding.VARIANTS[variant], splits, ws_ptr, ws_bytes, stream)
+    else:
+        if variant != "auto" or splits != 0:
+            raise ValueError("lora_matmul takes no variant or split count")
+        st = lib.rmm_lora_matmul(x.data_ptr(), w.data_ptr(), a.data_ptr(), b.data_ptr(),
+                                 out.data_ptr(), M, N, K, R, dtype, ws_ptr, ws_bytes, stream)
+    _binding.check(st)
+    return out
+
+
+def rmsnorm_lora(x, g, w, a, b, eps: float, out=None, variant: str = "auto", splits: int = 0,
+                 workspace: Workspace | None = None):
+    """Y = norm(x) @ w + (norm(x) @ a.T) @ b, fused; a: [R, K], b: [R, N], 1 <= R <= 64."""
+    return _lora(x, g, w, a, b, eps, out, variant, splits, workspace, True)
+
+
+def lora_matmul(x, w, a, b, out=None, workspace: Workspace | None = None):
+    """Y = x @ w + (x @ a.T) @ b with the same kernels, no norm."""
+    return _lora(x, None, w, a, b, 0.0, out, "auto", 0, workspace, False)
+
+
+def plan_lora(M, N, K, R, dtype=torch.bfloat16, variant="auto", splits=0, with_workspace=True):
+    """Which variant and split count an adapter call of this shape would run (host only)."""
+    base = 1 << 40
+    span = 1 << 36
+    ptrs = [base + i * span for i in range(7)]
+    d = _DTYPES[dtype]
+    ws = ptrs[6] if with_workspace else None
+    nb = _binding.lora_workspace_bytes(d, M, N, K, R, variant, splits) if with_workspace else 0
+    return _binding.plan_lora(ptrs[0], ptrs[1], ptrs[2], ptrs[3], ptrs[4], ptrs[5], 1e-6, M, N, K,
+                              R, d, variant, splits, ws, nb)
 
 
 def plan(M, N, K, dtype=torch.bfloat16, gated=False, variant="auto", splits=0,

@@ -21,7 +21,9 @@ STATUS_OK = 0
 SYMBOLS = ("rmsnorm_matmul", "rmsnorm_gated_mlp", "rmsnorm_matmul_ex", "rmsnorm_gated_mlp_ex",
            "rmm_rmsnorm", "rmm_matmul", "rmm_gated_matmul", "rmm_workspace_bytes",
            "rmm_workspace_bytes_ex", "rmm_plan", "rmm_status_string", "rmm_last_hip_error",
-           "rmm_abi_version")
+           "rmm_abi_version", "rmsnorm_lora", "rmsnorm_lora_ex", "rmm_lora_matmul",
+           "rmm_lora_workspace_bytes", "rmm_plan_lora")
+LORA_MAX_RANK = 64
 
 _lib = None
 
@@ -52,9 +54,19 @@ def load_library(path: str = LIB_PATH):
     lib.rmm_rmsnorm.argtypes = [vp, vp, vp, f32, i64, i64, i32, vp]
     lib.rmm_matmul.argtypes = [vp, vp, vp, i64, i64, i64, i32, vp, sz, vp]
     lib.rmm_gated_matmul.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, vp, sz, vp]
+    lib.rmsnorm_lora.argtypes = [vp, vp, vp, vp, vp, vp, f32, i64, i64, i64, i64, i32, vp, sz, vp]
+    lib.rmsnorm_lora_ex.argtypes = [vp, vp, vp, vp, vp, vp, f32, i64, i64, i64, i64, i32, i32,
+                                    i32, vp, sz, vp]
+    lib.rmm_lora_matmul.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp, sz, vp]
     for f in ("rmsnorm_matmul", "rmsnorm_gated_mlp", "rmsnorm_matmul_ex", "rmsnorm_gated_mlp_ex",
-              "rmm_rmsnorm", "rmm_matmul", "rmm_gated_matmul"):
+              "rmm_rmsnorm", "rmm_matmul", "rmm_gated_matmul", "rmsnorm_lora", "rmsnorm_lora_ex",
+              "rmm_lora_matmul"):
         getattr(lib, f).restype = i32
+    lib.rmm_lora_workspace_bytes.argtypes = [i32, i64, i64, i64, i64, i32, i32]
+    lib.rmm_lora_workspace_bytes.restype = sz
+    lib.rmm_plan_lora.argtypes = [vp, vp, vp, vp, vp, vp, f32, i64, i64, i64, i64, i32, i32, i32,
+                                  vp, sz, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.rmm_plan_lora.restype = i32
     lib.rmm_workspace_bytes.argtypes = [i32, i64, i64, i64, i32]
     lib.rmm_workspace_bytes.restype = sz
     lib.rmm_workspace_bytes_ex.argtypes = [i32, i64, i64, i64, i32, i32, i32]
@@ -99,4 +111,20 @@ def plan(X, g, W1, W3, Y, eps, M, N, K, dtype, gated, variant="auto", splits=0, 
     st = load_library().rmm_plan(X, g, W1, W3, Y, eps, M, N, K, dtype, int(gated),
                                  VARIANTS[variant], splits, ws, ws_bytes, ctypes.byref(v),
                                  ctypes.byref(s))
+    return st, VARIANT_NAMES.get(v.value), s.value
+
+
+def lora_workspace_bytes(dtype: int, M: int, N: int, K: int, R: int, variant: str = "auto",
+                         splits: int = 0) -> int:
+    return int(load_library().rmm_lora_workspace_bytes(dtype, M, N, K, R, VARIANTS[variant],
+                                                       splits))
+
+
+def plan_lora(X, g, W, A, B, Y, eps, M, N, K, R, dtype, variant="auto", splits=0, ws=None,
+              ws_bytes=0):
+    """Host-only planning through rmm_plan_lora: (status, variant name, splits)."""
+    v = ctypes.c_int(-1)
+    s = ctypes.c_int(-1)
+    st = load_library().rmm_plan_lora(X, g, W, A, B, Y, eps, M, N, K, R, dtype, VARIANTS[variant],
+                                      splits, ws, ws_bytes, ctypes.byref(v), ctypes.byref(s))
     return st, VARIANT_NAMES.get(v.value), s.value

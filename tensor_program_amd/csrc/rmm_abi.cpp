@@ -39,6 +39,9 @@ constexpr int64_t kTargetWorkgroups = 256;
 // enough 64-column strips to keep most CUs streaming.
 constexpr int64_t kStreamMaxM = 64;
 constexpr int64_t kStreamMinTiles = 192;
+// Low-rank adapter: ranks 1..RMM_LORA_MAX_RANK; the decode kernel carries up
+// to two 16-wide rank blocks, every other shape runs the generic kernel.
+constexpr int64_t kLoraDecodeMaxRank = 32;
 
 int auto_decode_splits(int64_t N, int64_t K) {
   const int64_t tiles = (N + 127) / 128;
@@ -52,7 +55,8 @@ int auto_decode_splits(int64_t N, int64_t K) {
 // Shape/variant part of the plan; `aligned` says whether every pointer is
 // 16-byte aligned, `have_ws` whether a workspace was passed.
 rmm_status plan_shape(int64_t M, int64_t N, int64_t K, rmm_dtype dtype, int gated,
-                      rmm_variant variant, int splits, bool aligned, bool have_ws, Plan* out) {
+                      rmm_variant variant, int splits, bool aligned, bool have_ws, Plan* out,
+                      int64_t R = 0) {
   if (variant < RMM_VARIANT_AUTO || variant > RMM_VARIANT_STREAM) return RMM_ERR_VARIANT;
   if (splits < 0) return RMM_ERR_VARIANT;
   if (splits != 0 && variant != RMM_VARIANT_DECODE) return RMM_ERR_VARIANT;
@@ -65,12 +69,17 @@ rmm_status plan_shape(int64_t M, int64_t N, int64_t K, rmm_dtype dtype, int gate
   // The fast variants address X and W with 32-bit buffer offsets.
   const bool fast_layout = dtype == RMM_DTYPE_BF16 && K % 8 == 0 && N % 8 == 0 && aligned &&
                            K * N * 2 <= (int64_t)INT32_MAX && M * K * 2 <= (int64_t)INT32_MAX;
-  const bool decode_ok = fast_layout && M <= (gated ? kDecodeMaxMGated : kDecodeMaxM);
-  const bool prefill_ok = fast_layout && !gated;
-  const bool stream_ok = fast_layout && M <= kStreamMaxM;
+  // With the adapter: 32-bit offsets into A as well (rank rows up to 32).
+  const bool lora_ok = R == 0 || (R <= kLoraDecodeMaxRank && kLoraDecodeMaxRank * K * 2 <= (int64_t)INT32_MAX &&
+                                  R * N * 2 <= (int64_t)INT32_MAX);
+  const bool decode_ok = fast_layout && lora_ok && M <= (gated ? kDecodeMaxMGated : kDecodeMaxM);
+  const bool prefill_ok = fast_layout && !gated && R == 0;
+  const bool stream_ok = fast_layout && M <= kStreamMaxM && R == 0;
   rmm_variant v = variant;
   if (v == RMM_VARIANT_AUTO) {
-    if (gated)
+    if (R > 0)
+      v = decode_ok ? RMM_VARIANT_DECODE : RMM_VARIANT_GENERIC;
+    else if (gated)
       v = stream_ok ? RMM_VARIANT_STREAM : RMM_VARIANT_GENERIC;
     else if (decode_ok)
       v = RMM_VARIANT_DECODE;
@@ -90,7 +99,7 @@ rmm_status plan_shape(int64_t M, int64_t N, int64_t K, rmm_dtype dtype, int gate
     if (s == 0) s = have_ws ? auto_decode_splits(N, K) : 1;
     if (s > (K + 127) / 128) return RMM_ERR_VARIANT;
     if (s > 1 && !have_ws) return RMM_ERR_WORKSPACE;  // a forced split count needs one
-    rmm_decode_plan(M, N, K, gated, s, &out->dec);
+    rmm_decode_plan(M, N, K, gated, s, R, &out->dec);
     if (out->dec.ws_bytes > (size_t)INT32_MAX) return RMM_ERR_VARIANT;  // 32-bit offsets
     out->splits = out->dec.splits;
     out->ws_bytes = out->dec.ws_bytes;
@@ -100,19 +109,25 @@ rmm_status plan_shape(int64_t M, int64_t N, int64_t K, rmm_dtype dtype, int gate
   return RMM_OK;
 }
 
+// R < 0: no adapter; R >= 0: the adapter entry points (R must be 1..max).
 rmm_status plan_call(const void* X, const void* g, const void* W1, const void* W3, const void* Y,
                      float eps, int64_t M, int64_t N, int64_t K, rmm_dtype dtype, int gated,
-                     rmm_variant variant, int splits, const void* ws, size_t ws_bytes, Plan* out) {
+                     rmm_variant variant, int splits, const void* ws, size_t ws_bytes, Plan* out,
+                     const void* LA = nullptr, const void* LB = nullptr, int64_t R = -1) {
+  const bool lora = R >= 0;
   // 1. pointers
   const bool empty = (M == 0 || N == 0);
-  if (!empty && (!X || !g || !W1 || !Y || (gated && !W3))) return RMM_ERR_NULL;
+  if (!empty && (!X || !g || !W1 || !Y || (gated && !W3) || (lora && (!LA || !LB))))
+    return RMM_ERR_NULL;
   // 2. shape
   if (M < 0 || N < 0 || K <= 0) return RMM_ERR_SHAPE;
+  if (lora && (R < 1 || R > RMM_LORA_MAX_RANK)) return RMM_ERR_SHAPE;
   int64_t mk, kn, mn, tmp;
   if (__builtin_mul_overflow(M, K, &mk) || __builtin_mul_overflow(K, N, &kn) ||
       __builtin_mul_overflow(M, N, &mn) || __builtin_mul_overflow(mk, (int64_t)4, &tmp) ||
       __builtin_mul_overflow(kn, (int64_t)4, &tmp) || __builtin_mul_overflow(mn, (int64_t)4, &tmp))
     return RMM_ERR_SHAPE;
+  const int64_t rank = lora ? R : 0;  // R * K and R * N fit: R <= 64 and K * 4, N * 4 fit
   // 3. eps
   if (!isfinite(eps) || eps < 0.0f) return RMM_ERR_EPS;
   // 4. dtype
@@ -123,13 +138,17 @@ rmm_status plan_call(const void* X, const void* g, const void* W1, const void* W
     const size_t yb = (size_t)mn * es;
     if (overlaps(Y, yb, X, (size_t)mk * es) || overlaps(Y, yb, g, (size_t)K * es) ||
         overlaps(Y, yb, W1, (size_t)kn * es) || (gated && overlaps(Y, yb, W3, (size_t)kn * es)) ||
-        overlaps(Y, yb, ws, ws ? ws_bytes : 0))
+        overlaps(Y, yb, ws, ws ? ws_bytes : 0) ||
+        (lora && (overlaps(Y, yb, LA, (size_t)(rank * K) * es) ||
+                  overlaps(Y, yb, LB, (size_t)(rank * N) * es))))
       return RMM_ERR_ALIAS;
   }
   // 6. variant (and the split count it would use)
   const bool aligned = empty || (aligned16(X) && aligned16(g) && aligned16(W1) &&
-                                 (!gated || aligned16(W3)) && aligned16(Y));
-  rmm_status st = plan_shape(M, N, K, dtype, gated, variant, splits, aligned, ws != nullptr, out);
+                                 (!gated || aligned16(W3)) && aligned16(Y) &&
+                                 (!lora || (aligned16(LA) && aligned16(LB))));
+  rmm_status st =
+      plan_shape(M, N, K, dtype, gated, variant, splits, aligned, ws != nullptr, out, rank);
   if (st != RMM_OK) return st;
   // 7. workspace
   if (ws && ws_bytes < out->ws_bytes) return RMM_ERR_WORKSPACE;
@@ -138,13 +157,19 @@ rmm_status plan_call(const void* X, const void* g, const void* W1, const void* W
 
 rmm_status run(const void* X, const void* g, const void* W1, const void* W3, void* Y, float eps,
                int64_t M, int64_t N, int64_t K, rmm_dtype dtype, int gated, rmm_variant variant,
-               int splits, void* ws, size_t ws_bytes, hipStream_t stream, int norm = 1) {
+               int splits, void* ws, size_t ws_bytes, hipStream_t stream, int norm = 1,
+               const void* LA = nullptr, const void* LB = nullptr, int64_t R = -1) {
   Plan plan;
-  rmm_status st =
-      plan_call(X, g, W1, W3, Y, eps, M, N, K, dtype, gated, variant, splits, ws, ws_bytes, &plan);
+  rmm_status st = plan_call(X, g, W1, W3, Y, eps, M, N, K, dtype, gated, variant, splits, ws,
+                            ws_bytes, &plan, LA, LB, R);
   if (st != RMM_OK) return st;
   if (M == 0 || N == 0) return RMM_OK;
   RmmArgs a{X, g, W1, gated ? W3 : nullptr, Y, eps, M, N, K, gated, norm, stream};
+  if (R > 0) {
+    a.LA = LA;
+    a.LB = LB;
+    a.R = R;
+  }
   hipError_t err = hipSuccess;
   switch (plan.variant) {
     case RMM_VARIANT_GENERIC:
@@ -168,6 +193,11 @@ rmm_status run(const void* X, const void* g, const void* W1, const void* W3, voi
   }
   return RMM_OK;
 }
+
+// The adapter entry points pass their rank through this: internally R < 0
+// means "no adapter", so a negative rank from a caller becomes 0, which
+// fails the rank check like any other rank outside 1..64.
+int64_t lora_rank_arg(int64_t R) { return R < 0 ? 0 : R; }
 
 }  // namespace
 
@@ -214,6 +244,28 @@ rmm_status rmm_gated_matmul(const void* X, const void* W1, const void* W3, void*
              0);
 }
 
+rmm_status rmsnorm_lora(const void* X, const void* g, const void* W, const void* A, const void* B,
+                        void* Y, float eps, int64_t M, int64_t N, int64_t K, int64_t R,
+                        rmm_dtype dtype, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return run(X, g, W, nullptr, Y, eps, M, N, K, dtype, 0, RMM_VARIANT_AUTO, 0, ws, ws_bytes,
+             stream, 1, A, B, lora_rank_arg(R));
+}
+
+rmm_status rmsnorm_lora_ex(const void* X, const void* g, const void* W, const void* A,
+                           const void* B, void* Y, float eps, int64_t M, int64_t N, int64_t K,
+                           int64_t R, rmm_dtype dtype, rmm_variant variant, int splits, void* ws,
+                           size_t ws_bytes, hipStream_t stream) {
+  return run(X, g, W, nullptr, Y, eps, M, N, K, dtype, 0, variant, splits, ws, ws_bytes, stream, 1,
+             A, B, lora_rank_arg(R));
+}
+
+rmm_status rmm_lora_matmul(const void* X, const void* W, const void* A, const void* B, void* Y,
+                           int64_t M, int64_t N, int64_t K, int64_t R, rmm_dtype dtype, void* ws,
+                           size_t ws_bytes, hipStream_t stream) {
+  return run(X, X, W, nullptr, Y, 0.0f, M, N, K, dtype, 0, RMM_VARIANT_AUTO, 0, ws, ws_bytes,
+             stream, 0, A, B, lora_rank_arg(R));
+}
+
 rmm_status rmm_rmsnorm(const void* X, const void* g, void* Xn, float eps, int64_t M, int64_t K,
                        rmm_dtype dtype, hipStream_t stream) {
   if (M != 0 && (!X || !g || !Xn)) return RMM_ERR_NULL;
@@ -250,6 +302,15 @@ size_t rmm_workspace_bytes(rmm_dtype dtype, int64_t M, int64_t N, int64_t K, int
   return rmm_workspace_bytes_ex(dtype, M, N, K, gated, RMM_VARIANT_AUTO, 0);
 }
 
+size_t rmm_lora_workspace_bytes(rmm_dtype dtype, int64_t M, int64_t N, int64_t K, int64_t R,
+                                rmm_variant variant, int splits) {
+  if (M < 0 || N < 0 || K <= 0 || R < 1 || R > RMM_LORA_MAX_RANK) return 0;
+  if (dtype != RMM_DTYPE_F32 && dtype != RMM_DTYPE_BF16) return 0;
+  Plan plan;
+  if (plan_shape(M, N, K, dtype, 0, variant, splits, true, true, &plan, R) != RMM_OK) return 0;
+  return plan.ws_bytes;
+}
+
 rmm_status rmm_plan(const void* X, const void* g, const void* W1, const void* W3, const void* Y,
                     float eps, int64_t M, int64_t N, int64_t K, rmm_dtype dtype, int gated,
                     rmm_variant variant, int splits, const void* ws, size_t ws_bytes,
@@ -264,11 +325,26 @@ rmm_status rmm_plan(const void* X, const void* g, const void* W1, const void* W3
   return st;
 }
 
+rmm_status rmm_plan_lora(const void* X, const void* g, const void* W, const void* A,
+                         const void* B, const void* Y, float eps, int64_t M, int64_t N, int64_t K,
+                         int64_t R, rmm_dtype dtype, rmm_variant variant, int splits,
+                         const void* ws, size_t ws_bytes, rmm_variant* variant_out,
+                         int* splits_out) {
+  Plan plan;
+  rmm_status st = plan_call(X, g, W, nullptr, Y, eps, M, N, K, dtype, 0, variant, splits, ws,
+                            ws_bytes, &plan, A, B, lora_rank_arg(R));
+  if (st == RMM_OK) {
+    if (variant_out) *variant_out = plan.variant;
+    if (splits_out) *splits_out = plan.splits;
+  }
+  return st;
+}
+
 const char* rmm_status_string(rmm_status s) {
   switch (s) {
     case RMM_OK: return "RMM_OK";
     case RMM_ERR_NULL: return "RMM_ERR_NULL: a required pointer is NULL";
-    case RMM_ERR_SHAPE: return "RMM_ERR_SHAPE: M < 0, N < 0, K <= 0 or size overflow";
+    case RMM_ERR_SHAPE: return "RMM_ERR_SHAPE: M < 0, N < 0, K <= 0, rank outside 1..64 or size overflow";
     case RMM_ERR_EPS: return "RMM_ERR_EPS: eps must be finite and >= 0";
     case RMM_ERR_DTYPE: return "RMM_ERR_DTYPE: unknown dtype";
     case RMM_ERR_ALIAS: return "RMM_ERR_ALIAS: Y overlaps an input or the workspace";

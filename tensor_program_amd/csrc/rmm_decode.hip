@@ -48,9 +48,11 @@ constexpr uint32_t kOutOfRange = 0x80000000u;  // > every buffer the variant acc
 // correctly on any other without a cache-wide write-back or invalidate.
 constexpr int kCoherentDevice = 16;
 
-template <int MB, int NW, int WV>
+template <int MB, int NW, int WV, int LR>
 struct DecodeSmem {
-  floatx4 red[WV][NW * MB * 8][64];  // per-wave accumulators [wave][(wi,b,c)][lane]
+  // per-wave accumulators [wave][slot][lane]: slots (wi,b,c) of the weight
+  // products, then (b,lb) of the adapter's down-projection
+  floatx4 red[WV][NW * MB * 8 + MB * LR][64];
   u32x4 xg[DEC_STAGE_BYTES / (16 * 16 * MB)][16 * MB];  // A operand, [k/8][row]
   float ssr[16 * MB];
   float inv[16 * MB];
@@ -99,16 +101,20 @@ __device__ __forceinline__ void decode_mma(const u32x4 (&wv)[NW][8], const u32x4
   }
 }
 
-template <int MB, bool GATED, int WV>
+template <int MB, bool GATED, int WV, int LR>
 __global__ __launch_bounds__(WV * 64) void decode_kernel(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ g, const bf16_t* __restrict__ W1,
     const bf16_t* __restrict__ W3, bf16_t* __restrict__ Y, float eps, int M, int64_t N,
     int64_t K, int64_t kchunk, int S, int tiles, int xcd_remap, unsigned* __restrict__ cnt,
-    float* __restrict__ ssq_ws, float* __restrict__ part_ws, int norm) {
+    float* __restrict__ ssq_ws, float* __restrict__ part_ws, int norm,
+    const bf16_t* __restrict__ LA, const bf16_t* __restrict__ LB, int R) {
   constexpr int NW = GATED ? 2 : 1;
+  static_assert(!(GATED && LR), "the adapter is not combined with the gate");
   constexpr int NT = WV * 64;
-  constexpr int E4 = NW * MB * 8 * 64;  // floatx4 per partial
-  constexpr int PER4 = E4 / NT;         // floatx4 per thread in the combine
+  constexpr int EW = NW * MB * 8;                 // weight-product slots
+  constexpr int E4 = (EW + MB * LR) * 64;         // floatx4 per partial
+  constexpr int PER4 = (E4 + NT - 1) / NT;        // floatx4 per thread in the combine
+  constexpr bool E4_FULL = E4 % NT == 0;          // every thread owns PER4 of them
   constexpr int ROWS = 16 * MB;
   constexpr int SEG = DEC_STAGE_BYTES / (16 * ROWS) * 8;  // k rows staged at a time
   constexpr int TPR = NT / ROWS;                          // staging threads per row
@@ -116,7 +122,7 @@ __global__ __launch_bounds__(WV * 64) void decode_kernel(
   constexpr int STEP = 32 * WV;                           // k rows per pipeline step
   constexpr int SPS = SEG / STEP;                         // steps per staged segment
   static_assert(SPS % 2 == 0 && NU >= 1, "segment must hold an even number of steps");
-  __shared__ DecodeSmem<MB, NW, WV> sm;
+  __shared__ DecodeSmem<MB, NW, WV, LR> sm;
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, q = l >> 4, p = l & 15;
   int tile, split;
@@ -142,6 +148,17 @@ __global__ __launch_bounds__(WV * 64) void decode_kernel(
   src.w3 = __builtin_amdgcn_make_buffer_rsrc((void*)(GATED ? W3 : W1), 0, (int)(K * N * 2), 0x00020000);
   src.x = __builtin_amdgcn_make_buffer_rsrc((void*)X, 0, (int)((int64_t)M * K * 2), 0x00020000);
   src.g = __builtin_amdgcn_make_buffer_rsrc((void*)g, 0, (int)(K * 2), 0x00020000);
+  // Adapter: lane (q, p) of block lb reads A[16 lb + p][krow .. krow+7], the
+  // B fragment of one v_mfma_f32_16x16x32_bf16 as stored; rows past R fall
+  // outside the buffer and read zeros.
+  const __amdgpu_buffer_rsrc_t lar =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(LR ? LA : W1), 0, LR ? (int)(R * K * 2) : 0, 0x00020000);
+  auto lora_load = [&](u32x4 (&lv)[LR > 0 ? LR : 1], int64_t krow) {
+#pragma unroll
+    for (int lb = 0; lb < LR; ++lb)
+      lv[lb] = __builtin_amdgcn_raw_buffer_load_b128(
+          lar, krow < k_hi ? (uint32_t)(((int64_t)(16 * lb + p) * K + krow) * 2) : kOutOfRange, 0, 0);
+  };
 
   // Staging: thread -> row srow, 16-byte k-chunks sj + TPR u of the segment.
   const int srow = tid / TPR, sj = tid % TPR;
@@ -174,11 +191,14 @@ __global__ __launch_bounds__(WV * 64) void decode_kernel(
 
   // Segment 0 staging loads, then both W stages, then the A operand.
   u32x4 wa[NW][8], wb[NW][8];
+  u32x4 la[LR > 0 ? LR : 1], lb[LR > 0 ? LR : 1];
   {
     u32x4 xs[NU], gs[NU];
     stage_load(k_lo, xs, gs);
     decode_load<NW>(wa, src, N, k_lo + 32 * w + 8 * q, k_hi, col, col_ok);
+    lora_load(la, k_lo + 32 * w + 8 * q);
     decode_load<NW>(wb, src, N, k_lo + STEP + 32 * w + 8 * q, k_hi, col, col_ok);
+    lora_load(lb, k_lo + STEP + 32 * w + 8 * q);
     stage_form(xs, gs);
   }
   __syncthreads();
@@ -190,6 +210,21 @@ __global__ __launch_bounds__(WV * 64) void decode_kernel(
     for (int b = 0; b < MB; ++b)
 #pragma unroll
       for (int c = 0; c < 8; ++c) acc[a][b][c] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // Adapter down-projection T = (X g) A^T: lane element (row 16b + 4q + r,
+  // rank 16 lb + p) of block (b, lb).
+  floatx4 lacc[MB][LR > 0 ? LR : 1];
+#pragma unroll
+  for (int b = 0; b < MB; ++b)
+#pragma unroll
+    for (int i = 0; i < LR; ++i) lacc[b][i] = floatx4{0.f, 0.f, 0.f, 0.f};
+  auto lora_mma = [&](const u32x4 (&lv)[LR > 0 ? LR : 1], const u32x4 (&a)[MB]) {
+#pragma unroll
+    for (int b = 0; b < MB; ++b)
+#pragma unroll
+      for (int i = 0; i < LR; ++i)
+        lacc[b][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, a[b]), __builtin_bit_cast(bf16x8, lv[i]), lacc[b][i], 0, 0, 0);
+  };
 
   auto fetch_a = [&](int s, u32x4 (&a)[MB]) {
     const int kc = ((s % SPS) * STEP + 32 * w + 8 * q) >> 3;
@@ -210,16 +245,21 @@ __global__ __launch_bounds__(WV * 64) void decode_kernel(
     u32x4 a[MB];
     fetch_a(s, a);
     decode_mma<MB, NW>(wa, a, acc);
+    lora_mma(la, a);
     decode_load<NW>(wa, src, N, k_lo + (int64_t)(s + 2) * STEP + 32 * w + 8 * q, k_hi, col, col_ok);
+    lora_load(la, k_lo + (int64_t)(s + 2) * STEP + 32 * w + 8 * q);
     fetch_a(s + 1, a);
     decode_mma<MB, NW>(wb, a, acc);
+    lora_mma(lb, a);
     decode_load<NW>(wb, src, N, k_lo + (int64_t)(s + 3) * STEP + 32 * w + 8 * q, k_hi, col, col_ok);
+    lora_load(lb, k_lo + (int64_t)(s + 3) * STEP + 32 * w + 8 * q);
   }
   if (s < nsteps) {
     if (s > 0 && s % SPS == 0) restage(s);
     u32x4 a[MB];
     fetch_a(s, a);
     decode_mma<MB, NW>(wa, a, acc);
+    lora_mma(la, a);
   }
 
   // Row sums of squares: the TPR staging threads of a row are adjacent lanes.
@@ -233,20 +273,43 @@ __global__ __launch_bounds__(WV * 64) void decode_kernel(
     for (int b = 0; b < MB; ++b)
 #pragma unroll
       for (int c = 0; c < 8; ++c) sm.red[w][(wi * MB + b) * 8 + c][l] = acc[wi][b][c];
+#pragma unroll
+  for (int b = 0; b < MB; ++b)
+#pragma unroll
+    for (int i = 0; i < LR; ++i) sm.red[w][EW + b * LR + i][l] = lacc[b][i];
   __syncthreads();
 
-  // Workgroup sum of the waves; thread owns floatx4 tid + NT u.
+  // Workgroup sum of the waves; thread owns floatx4 tid + NT u (E4 is a
+  // multiple of 64, so the bound is uniform per wave).
   floatx4* red0 = &sm.red[0][0][0];
   floatx4 v[PER4];
 #pragma unroll
   for (int u = 0; u < PER4; ++u) {
     const int f = tid + NT * u;
-    floatx4 t4 = red0[f];
+    floatx4 t4 = floatx4{0.f, 0.f, 0.f, 0.f};
+    if (E4_FULL || f < E4) {
+      t4 = red0[f];
 #pragma unroll
-    for (int ww = 1; ww < WV; ++ww) t4 += red0[ww * E4 + f];
+      for (int ww = 1; ww < WV; ++ww) t4 += red0[ww * E4 + f];
+    }
     v[u] = t4;
   }
   float ssw = tid < ROWS ? sm.ssr[tid] : 0.f;
+
+  // Epilogue thread layout (see below): this thread's 8 columns; with the
+  // adapter it needs B[r][cc .. cc+7] for every rank r, loaded next to the
+  // partials so the latencies overlap.
+  const int64_t ecc = (int64_t)tile * DEC_COLS + 8 * (l & 15);
+  u32x4 bq[LR > 0 ? 16 * LR : 1];
+  auto lora_b_load = [&]() {
+    if (LR == 0) return;
+    const __amdgpu_buffer_rsrc_t lbr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)LB, 0, (int)(R * N * 2), 0x00020000);
+#pragma unroll
+    for (int r = 0; r < 16 * LR; ++r)
+      bq[r] = __builtin_amdgcn_raw_buffer_load_b128(
+          lbr, (r < R && ecc < N) ? (uint32_t)(((int64_t)r * N + ecc) * 2) : kOutOfRange, 0, 0);
+  };
 
   if (S > 1) {
     const int64_t slot = (int64_t)split * tiles + tile;
@@ -258,9 +321,10 @@ __global__ __launch_bounds__(WV * 64) void decode_kernel(
     // whichever workgroup arrives last.
 #pragma unroll
     for (int u = 0; u < PER4; ++u)
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v[u]), prs,
-                                             (int)((slot * E4 + tid + NT * u) * 16), 0,
-                                             kCoherentDevice);
+      if (E4_FULL || tid + NT * u < E4)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v[u]), prs,
+                                               (int)((slot * E4 + tid + NT * u) * 16), 0,
+                                               kCoherentDevice);
     if (tid < ROWS)
       __hip_atomic_store(&ssq_ws[slot * ROWS + tid], ssw, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
@@ -273,6 +337,7 @@ __global__ __launch_bounds__(WV * 64) void decode_kernel(
     if (!sm.last) return;
     // Last arrival: add the S partials, up to 8 splits' loads in flight.
     constexpr int RS = 8 / PER4 > 0 ? 8 / PER4 : 1;
+    lora_b_load();
 #pragma unroll
     for (int u = 0; u < PER4; ++u) v[u] = floatx4{0.f, 0.f, 0.f, 0.f};
     ssw = 0.f;
@@ -285,7 +350,7 @@ __global__ __launch_bounds__(WV * 64) void decode_kernel(
         const bool ok = s0 + uu < S;
 #pragma unroll
         for (int u = 0; u < PER4; ++u)
-          buf[uu][u] = ok ? __builtin_amdgcn_raw_buffer_load_b128(
+          buf[uu][u] = (ok && (E4_FULL || tid + NT * u < E4)) ? __builtin_amdgcn_raw_buffer_load_b128(
                                 prs, (int)((sl * E4 + tid + NT * u) * 16), 0, kCoherentDevice)
                           : u32x4{0u, 0u, 0u, 0u};
         sb[uu] = (ok && tid < ROWS) ? __hip_atomic_load(&ssq_ws[sl * ROWS + tid], __ATOMIC_RELAXED,
@@ -299,12 +364,16 @@ __global__ __launch_bounds__(WV * 64) void decode_kernel(
         ssw += sb[uu];
       }
     }
-    // Leave the workspace zeroed for the next call (all arrivals are in).
+    // Reset the tile's arrival counter for the next call (all arrivals are
+    // in); the partial slots are overwritten by the next call before use.
     if (tid == 0) __hip_atomic_store(&cnt[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    lora_b_load();
   }
   __syncthreads();  // everyone is done reading sm.red before it is overwritten
 #pragma unroll
-  for (int u = 0; u < PER4; ++u) red0[tid + NT * u] = v[u];
+  for (int u = 0; u < PER4; ++u)
+    if (E4_FULL || tid + NT * u < E4) red0[tid + NT * u] = v[u];
   if (tid < ROWS) sm.inv[tid] = norm ? inv_rms(ssw, K, eps) : 1.0f;
   __syncthreads();
 
@@ -321,11 +390,29 @@ __global__ __launch_bounds__(WV * 64) void decode_kernel(
     const int64_t cc = (int64_t)tile * DEC_COLS + 8 * (ln & 15);
     if (row >= M || cc >= N) continue;
     const float inv = sm.inv[row];
+    // Adapter: y += sum_r T[row][r] B[r][cc + c], T from slot (b, r / 16),
+    // lane 16 (ln / 16) + r % 16, component r of the summed block.
+    float ya[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int rr = 0; rr < 16 * LR; ++rr) {
+      const float t = redf[((EW + b * LR + rr / 16) * 64 + 16 * (ln >> 4) + rr % 16) * 4 + r];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        ya[2 * d] += t * bf16_lo(bq[rr][d]);
+        ya[2 * d + 1] += t * bf16_hi(bq[rr][d]);
+      }
+    }
     u32x4 out;
 #pragma unroll
     for (int c = 0; c < 8; c += 2) {
-      float y0 = redf[(((0 * MB + b) * 8 + c) * 64 + ln) * 4 + r] * inv;
-      float y1 = redf[(((0 * MB + b) * 8 + c + 1) * 64 + ln) * 4 + r] * inv;
+      float y0 = redf[(((0 * MB + b) * 8 + c) * 64 + ln) * 4 + r];
+      float y1 = redf[(((0 * MB + b) * 8 + c + 1) * 64 + ln) * 4 + r];
+      if (LR > 0) {
+        y0 += ya[c];
+        y1 += ya[c + 1];
+      }
+      y0 *= inv;
+      y1 *= inv;
       if (GATED) {
         const float z0 = redf[(((1 * MB + b) * 8 + c) * 64 + ln) * 4 + r] * inv;
         const float z1 = redf[(((1 * MB + b) * 8 + c + 1) * 64 + ln) * 4 + r] * inv;
@@ -344,9 +431,11 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Chunks are whole 128-deep granules; eight waves (256-deep steps) when the
 // grid has at most one workgroup per CU and the per-wave accumulators fit.
-void rmm_decode_plan(int64_t M, int64_t N, int64_t K, int gated, int splits, DecodePlan* p) {
+void rmm_decode_plan(int64_t M, int64_t N, int64_t K, int gated, int splits, int64_t lora_rank,
+                     DecodePlan* p) {
   using namespace rmm;
   p->mb = (int)((M + 15) / 16);
+  p->lr = (int)((lora_rank + 15) / 16);
   p->tiles = (N + DEC_COLS - 1) / DEC_COLS;
   const int64_t kgran = (K + 127) / 128;
   int64_t s = splits;
@@ -357,14 +446,14 @@ void rmm_decode_plan(int64_t M, int64_t N, int64_t K, int gated, int splits, Dec
   p->splits = (int)((K + p->kchunk - 1) / p->kchunk);
   const int nw = gated ? 2 : 1;
   p->wv = (nw * p->mb == 1 && p->tiles * p->splits <= 256) ? 8 : 4;
-  const size_t E = (size_t)nw * p->mb * 32 * 64;  // floats per partial
+  const size_t E = ((size_t)nw * p->mb * 8 + (size_t)p->mb * p->lr) * 64 * 4;  // floats per partial
   p->ws_cnt_off = 0;
   p->ws_ssq_off = align256(sizeof(unsigned) * (size_t)p->tiles);
   p->ws_part_off = p->ws_ssq_off + align256(sizeof(float) * (size_t)p->splits * p->tiles * p->mb * 16);
   p->ws_bytes = p->splits > 1 ? p->ws_part_off + align256(sizeof(float) * (size_t)p->splits * p->tiles * E) : 0;
 }
 
-template <int MB, bool GATED, int WV>
+template <int MB, bool GATED, int WV, int LR>
 static void launch_decode_t(const RmmArgs& a, const DecodePlan& p, void* ws) {
   using namespace rmm;
   const int xcd_remap = (p.tiles % 8) == 0;
@@ -373,18 +462,27 @@ static void launch_decode_t(const RmmArgs& a, const DecodePlan& p, void* ws) {
   float* ssq = ws ? (float*)(base + p.ws_ssq_off) : nullptr;
   float* part = ws ? (float*)(base + p.ws_part_off) : nullptr;
   const unsigned grid = (unsigned)(p.tiles * p.splits);
-  hipLaunchKernelGGL((decode_kernel<MB, GATED, WV>), dim3(grid), dim3(WV * 64), 0, a.stream,
+  hipLaunchKernelGGL((decode_kernel<MB, GATED, WV, LR>), dim3(grid), dim3(WV * 64), 0, a.stream,
                      (const bf16_t*)a.X, (const bf16_t*)a.g, (const bf16_t*)a.W1,
                      (const bf16_t*)a.W3, (bf16_t*)a.Y, a.eps, (int)a.M, a.N, a.K, p.kchunk,
-                     p.splits, (int)p.tiles, xcd_remap, cnt, ssq, part, a.norm);
+                     p.splits, (int)p.tiles, xcd_remap, cnt, ssq, part, a.norm,
+                     (const bf16_t*)a.LA, (const bf16_t*)a.LB, (int)a.R);
 }
 
 hipError_t rmm_launch_decode(const RmmArgs& a, const DecodePlan& p, void* ws) {
   const bool gd = a.gated != 0;
-  if (!gd && p.mb == 1 && p.wv == 8) launch_decode_t<1, false, 8>(a, p, ws);
-  else if (!gd && p.mb == 1 && p.wv == 4) launch_decode_t<1, false, 4>(a, p, ws);
-  else if (!gd && p.mb == 2 && p.wv == 4) launch_decode_t<2, false, 4>(a, p, ws);
-  else if (gd && p.mb == 1 && p.wv == 4) launch_decode_t<1, true, 4>(a, p, ws);
+  const int lr = a.R > 0 ? p.lr : 0;
+  if (lr != p.lr) return hipErrorInvalidValue;
+  if (!gd && lr == 0 && p.mb == 1 && p.wv == 8) launch_decode_t<1, false, 8, 0>(a, p, ws);
+  else if (!gd && lr == 0 && p.mb == 1 && p.wv == 4) launch_decode_t<1, false, 4, 0>(a, p, ws);
+  else if (!gd && lr == 0 && p.mb == 2 && p.wv == 4) launch_decode_t<2, false, 4, 0>(a, p, ws);
+  else if (gd && lr == 0 && p.mb == 1 && p.wv == 4) launch_decode_t<1, true, 4, 0>(a, p, ws);
+  else if (!gd && lr == 1 && p.mb == 1 && p.wv == 8) launch_decode_t<1, false, 8, 1>(a, p, ws);
+  else if (!gd && lr == 1 && p.mb == 1 && p.wv == 4) launch_decode_t<1, false, 4, 1>(a, p, ws);
+  else if (!gd && lr == 1 && p.mb == 2 && p.wv == 4) launch_decode_t<2, false, 4, 1>(a, p, ws);
+  else if (!gd && lr == 2 && p.mb == 1 && p.wv == 8) launch_decode_t<1, false, 8, 2>(a, p, ws);
+  else if (!gd && lr == 2 && p.mb == 1 && p.wv == 4) launch_decode_t<1, false, 4, 2>(a, p, ws);
+  else if (!gd && lr == 2 && p.mb == 2 && p.wv == 4) launch_decode_t<2, false, 4, 2>(a, p, ws);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

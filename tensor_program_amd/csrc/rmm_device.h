@@ -68,6 +68,11 @@ struct RmmArgs {
   int gated;
   int norm;  // 1: fused RMSNorm (gain g, 1/RMS scale); 0: plain product (g = 1, no scale)
   hipStream_t stream;
+  // Low-rank adapter (R = 0: none): Y += (Act A^T) B before the 1/RMS scale,
+  // A: R x K (row r = down-projection vector r), B: R x N.  Not with gated.
+  const void* LA = nullptr;
+  const void* LB = nullptr;
+  int64_t R = 0;
 };
 
 hipError_t rmm_launch_generic(const RmmArgs& a, bool bf16);
@@ -78,9 +83,11 @@ struct DecodePlan {
   int splits;      // K chunks combined across workgroups
   int64_t kchunk;  // K per chunk (multiple of 128)
   int64_t tiles;   // 128-column tiles
+  int lr;          // 16-wide blocks of the adapter rank (0: no adapter)
   size_t ws_cnt_off, ws_ssq_off, ws_part_off, ws_bytes;
 };
-void rmm_decode_plan(int64_t M, int64_t N, int64_t K, int gated, int splits, DecodePlan* p);
+void rmm_decode_plan(int64_t M, int64_t N, int64_t K, int gated, int splits, int64_t lora_rank,
+                     DecodePlan* p);
 hipError_t rmm_launch_decode(const RmmArgs& a, const DecodePlan& p, void* ws);
 
 struct PrefillPlan {

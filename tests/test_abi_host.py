@@ -122,6 +122,67 @@ def test_unfused_entry_points_validate(lib):
     assert lib.rmm_gated_matmul(A[0], A[2], A[4], A[4] + 8, 16, 64, 64, BF16, None, 0, None) == ALIAS
 
 
+def test_lora_entry_points_validate(lib):
+    # rmsnorm_lora: NULL (A, B too), SHAPE (rank 1..64), EPS, DTYPE, ALIAS
+    # (Y against A and B as well), VARIANT, WORKSPACE, in that order.
+    def lo(X=A[0], g=A[1], W=A[2], LA=A[5], LB=A[6], Y=A[3], eps=1e-6, M=16, N=64, K=64, R=16,
+           dtype=BF16, variant=0, splits=0, ws=None, ws_bytes=0):
+        return lib.rmsnorm_lora_ex(X, g, W, LA, LB, Y, eps, M, N, K, R, dtype, variant, splits,
+                                   ws, ws_bytes, None)
+    assert lo(LA=None) == NULL
+    assert lo(LB=None, R=0) == NULL
+    assert lo(R=0) == SHAPE
+    assert lo(R=65) == SHAPE
+    assert lo(R=-1, eps=-1.0) == SHAPE
+    assert lo(eps=float("inf"), R=0) == SHAPE
+    assert lo(eps=-1.0, dtype=7) == EPS
+    assert lo(dtype=7, Y=A[5]) == DTYPE
+    assert lo(Y=A[5] + 16) == ALIAS                 # Y overlapping A
+    assert lo(Y=A[6] - 64) == ALIAS                 # Y overlapping B
+    assert lo(variant=3) == VARIANT                 # no adapter prefill tile
+    assert lo(variant=4) == VARIANT
+    assert lo(M=33, variant=2) == VARIANT           # decode: M <= 32
+    assert lo(R=33, variant=2) == VARIANT           # decode: R <= 32
+    assert lo(K=256, variant=2, splits=2) == WORKSPACE  # forced split count, no workspace
+    assert lo(X=None, g=None, W=None, LA=None, LB=None, Y=None, M=0) == OK
+    # rmm_lora_matmul: the same rules without eps and gain.
+    assert lib.rmm_lora_matmul(A[0], A[2], None, A[6], A[3], 16, 64, 64, 16, BF16, None, 0,
+                               None) == NULL
+    assert lib.rmm_lora_matmul(A[0], A[2], A[5], A[6], A[3], 16, 64, 64, 0, BF16, None, 0,
+                               None) == SHAPE
+    assert lib.rmm_lora_matmul(A[0], A[2], A[5], A[6], A[6], 16, 64, 64, 16, BF16, None, 0,
+                               None) == ALIAS
+
+
+def test_lora_plans():
+    import torch
+    assert tpa.plan_lora(16, 6144, 4096, 16)[1:] == ("decode", 4)
+    assert tpa.plan_lora(16, 6144, 4096, 32)[1:] == ("decode", 4)
+    assert tpa.plan_lora(16, 6144, 4096, 1)[1] == "decode"
+    assert tpa.plan_lora(32, 6144, 4096, 16)[1] == "decode"
+    assert tpa.plan_lora(16, 6144, 4096, 33)[1] == "generic"
+    assert tpa.plan_lora(16, 6144, 4096, 64)[1] == "generic"
+    assert tpa.plan_lora(33, 6144, 4096, 16)[1] == "generic"
+    assert tpa.plan_lora(4096, 4096, 4096, 16)[1] == "generic"
+    assert tpa.plan_lora(8, 1024, 1024, 16, dtype=torch.float32)[1] == "generic"
+    assert tpa.plan_lora(16, 6144, 4096, 16, with_workspace=False)[1:] == ("decode", 1)
+    assert tpa.plan_lora(16, 6144, 4096, 16, variant="decode", splits=3)[1:] == ("decode", 3)
+    assert tpa.plan_lora(16, 6144, 4096, 16, variant="prefill")[0] == VARIANT
+    assert tpa.plan_lora(16, 6144, 4096, 65)[0] == SHAPE
+
+
+def test_lora_workspace_sizes(lib):
+    plain = lib.rmm_workspace_bytes(BF16, 16, 6144, 4096, 0)
+    lora16 = lib.rmm_lora_workspace_bytes(BF16, 16, 6144, 4096, 16, 0, 0)
+    lora32 = lib.rmm_lora_workspace_bytes(BF16, 16, 6144, 4096, 32, 0, 0)
+    assert plain < lora16 < lora32   # the down-projection partials ride along
+    # 4 splits x 48 tiles x (8 + 1) blocks of 16 x 16 fp32 beyond the plain partials' 8
+    assert lora16 - plain == 4 * 48 * 1 * 256 * 4
+    assert lib.rmm_lora_workspace_bytes(BF16, 16, 6144, 4096, 48, 0, 0) == 0  # generic: none
+    assert lib.rmm_lora_workspace_bytes(BF16, 16, 6144, 4096, 0, 0, 0) == 0   # invalid rank
+    assert lib.rmm_lora_workspace_bytes(BF16, 16, 6144, 4096, 16, 2, 1) == 0
+
+
 def test_empty_shapes_are_noops(lib):
     # M == 0 or N == 0: RMM_OK, nothing launched (NULL pointers allowed).
     assert call(lib, X=None, g=None, W=None, Y=None, M=0) == OK

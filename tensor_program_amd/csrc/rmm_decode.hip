@@ -54,6 +54,7 @@ struct DecodeSmem {
   // products, then (b,lb) of the adapter's down-projection
   floatx4 red[WV][NW * MB * 8 + MB * LR][64];
   u32x4 xg[DEC_STAGE_BYTES / (16 * 16 * MB)][16 * MB];  // A operand, [k/8][row]
+  u32x4 lb[LR > 0 ? 16 * LR : 1][16];  // adapter: the tile's B rows, [rank][8-column chunk]
   float ssr[16 * MB];
   float inv[16 * MB];
   int last;
@@ -189,9 +190,14 @@ __global__ __launch_bounds__(WV * 64) void decode_kernel(
     }
   };
 
-  // Segment 0 staging loads, then both W stages, then the A operand.
+  // Segment 0 staging loads, then both W stages (with the adapter: then this
+  // tile's rows of B, which only the workgroup combining the tile uses but
+  // which would otherwise be fetched on its critical path; they are parked in
+  // LDS after the k-loop), then the A operand.
   u32x4 wa[NW][8], wb[NW][8];
   u32x4 la[LR > 0 ? LR : 1], lb[LR > 0 ? LR : 1];
+  constexpr int BCH = LR > 0 ? (256 * LR + NT - 1) / NT : 1;  // B chunks per thread
+  u32x4 bv[BCH];
   {
     u32x4 xs[NU], gs[NU];
     stage_load(k_lo, xs, gs);
@@ -199,6 +205,18 @@ __global__ __launch_bounds__(WV * 64) void decode_kernel(
     lora_load(la, k_lo + 32 * w + 8 * q);
     decode_load<NW>(wb, src, N, k_lo + STEP + 32 * w + 8 * q, k_hi, col, col_ok);
     lora_load(lb, k_lo + STEP + 32 * w + 8 * q);
+    if (LR > 0) {
+      const __amdgpu_buffer_rsrc_t lbr =
+          __builtin_amdgcn_make_buffer_rsrc((void*)LB, 0, (int)(R * N * 2), 0x00020000);
+#pragma unroll
+      for (int i = 0; i < BCH; ++i) {
+        const int e = tid + NT * i, r = e >> 4;
+        const int64_t bc = (int64_t)tile * DEC_COLS + 8 * (e & 15);
+        bv[i] = __builtin_amdgcn_raw_buffer_load_b128(
+            lbr, (r < R && e < 256 * LR && bc < N) ? (uint32_t)(((int64_t)r * N + bc) * 2) : kOutOfRange,
+            0, 0);
+      }
+    }
     stage_form(xs, gs);
   }
   __syncthreads();
@@ -262,6 +280,13 @@ __global__ __launch_bounds__(WV * 64) void decode_kernel(
     lora_mma(la, a);
   }
 
+  if (LR > 0) {
+#pragma unroll
+    for (int i = 0; i < BCH; ++i) {
+      const int e = tid + NT * i;
+      if ((256 * LR) % NT == 0 || e < 256 * LR) sm.lb[e >> 4][e & 15] = bv[i];
+    }
+  }
   // Row sums of squares: the TPR staging threads of a row are adjacent lanes.
 #pragma unroll
   for (int o = 1; o < TPR; o <<= 1) ssl += __shfl_xor(ssl, o);
@@ -296,20 +321,6 @@ __global__ __launch_bounds__(WV * 64) void decode_kernel(
   }
   float ssw = tid < ROWS ? sm.ssr[tid] : 0.f;
 
-  // Epilogue thread layout (see below): this thread's 8 columns; with the
-  // adapter it needs B[r][cc .. cc+7] for every rank r, loaded next to the
-  // partials so the latencies overlap.
-  const int64_t ecc = (int64_t)tile * DEC_COLS + 8 * (l & 15);
-  u32x4 bq[LR > 0 ? 16 * LR : 1];
-  auto lora_b_load = [&]() {
-    if (LR == 0) return;
-    const __amdgpu_buffer_rsrc_t lbr =
-        __builtin_amdgcn_make_buffer_rsrc((void*)LB, 0, (int)(R * N * 2), 0x00020000);
-#pragma unroll
-    for (int r = 0; r < 16 * LR; ++r)
-      bq[r] = __builtin_amdgcn_raw_buffer_load_b128(
-          lbr, (r < R && ecc < N) ? (uint32_t)(((int64_t)r * N + ecc) * 2) : kOutOfRange, 0, 0);
-  };
 
   if (S > 1) {
     const int64_t slot = (int64_t)split * tiles + tile;
@@ -337,7 +348,6 @@ __global__ __launch_bounds__(WV * 64) void decode_kernel(
     if (!sm.last) return;
     // Last arrival: add the S partials, up to 8 splits' loads in flight.
     constexpr int RS = 8 / PER4 > 0 ? 8 / PER4 : 1;
-    lora_b_load();
 #pragma unroll
     for (int u = 0; u < PER4; ++u) v[u] = floatx4{0.f, 0.f, 0.f, 0.f};
     ssw = 0.f;
@@ -367,8 +377,6 @@ __global__ __launch_bounds__(WV * 64) void decode_kernel(
     // Reset the tile's arrival counter for the next call (all arrivals are
     // in); the partial slots are overwritten by the next call before use.
     if (tid == 0) __hip_atomic_store(&cnt[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  } else {
-    lora_b_load();
   }
   __syncthreads();  // everyone is done reading sm.red before it is overwritten
 #pragma unroll
@@ -396,10 +404,11 @@ __global__ __launch_bounds__(WV * 64) void decode_kernel(
 #pragma unroll
     for (int rr = 0; rr < 16 * LR; ++rr) {
       const float t = redf[((EW + b * LR + rr / 16) * 64 + 16 * (ln >> 4) + rr % 16) * 4 + r];
+      const u32x4 bq = sm.lb[rr][ln & 15];
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        ya[2 * d] += t * bf16_lo(bq[rr][d]);
-        ya[2 * d + 1] += t * bf16_hi(bq[rr][d]);
+        ya[2 * d] += t * bf16_lo(bq[d]);
+        ya[2 * d + 1] += t * bf16_hi(bq[d]);
       }
     }
     u32x4 out;

@@ -50,6 +50,8 @@ def load(path: str = _LIB):
     lib.rmm_oracle_rmsnorm_lora_f64.restype = ctypes.c_int
     lib.rmm_oracle_lora_matmul_f64.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, vp]
     lib.rmm_oracle_lora_matmul_f64.restype = ctypes.c_int
+    lib.rmm_oracle_qknorm_attention_f64.argtypes = [vp, vp, vp, vp, vp, dbl, i64, i64, i64, vp]
+    lib.rmm_oracle_qknorm_attention_f64.restype = ctypes.c_int
     return lib
 
 
@@ -171,6 +173,23 @@ def lora_matmul(X, W, A, B, lib=None) -> np.ndarray:
     if rc != 0:
         raise ValueError(f"oracle error {rc}")
     return Y
+
+
+def qknorm_attention(Q, K, V, gq, gk, eps, lib=None) -> np.ndarray:
+    """o = softmax(norm(q) . norm(K)^T / sqrt(D)) V per batch-head, in fp64.
+    Q: [BH, D], K and V: [BH, S, D], gq and gk: [D] -> O: [BH, D]."""
+    lib = lib or _default()
+    Q, K, V, gq, gk = _d(Q), _d(K), _d(V), _d(gq), _d(gk)
+    BH, D = Q.shape
+    S = K.shape[1]
+    assert K.shape == (BH, S, D) and V.shape == (BH, S, D) and gq.shape == (D,) and \
+        gk.shape == (D,)
+    O = np.empty((BH, D), np.float64)
+    rc = lib.rmm_oracle_qknorm_attention_f64(_p(Q), _p(K), _p(V), _p(gq), _p(gk), float(eps), BH,
+                                             S, D, _p(O))
+    if rc != 0:
+        raise ValueError(f"oracle error {rc}")
+    return O
 
 
 def eps_as_passed(eps: float) -> float:

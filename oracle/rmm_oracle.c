@@ -36,6 +36,15 @@
  * with Act = Nrm (rmm_oracle_rmsnorm_lora_f64) or X itself
  * (rmm_oracle_lora_matmul_f64, the adapter alone).
  *
+ * QKNorm + attention (paper review, section "五、实验结果", the QKNorm + Attention
+ * row; the page names the benchmark only).  Reading: RMSNorm over the head
+ * dimension D with per-dimension gains, applied to the query and to every
+ * key, then scaled dot-product attention over the cached keys (one query per
+ * batch-head, no mask):
+ *   qn = q / rms(q) * gq,   kn_s = k_s / rms(k_s) * gk,
+ *   p_s = softmax_s(qn . kn_s / sqrt(D)),   o = sum_s p_s v_s.
+ * (rmm_oracle_qknorm_attention_f64; the normalised vectors are materialised.)
+ *
  * The steps are also exported one by one (rmm_oracle_rmsnorm_f64: steps 1-2,
  * rmm_oracle_matmul_f64: step 3, rmm_oracle_gated_matmul_f64: the two
  * products and the gate), because the unfused program is itself measured:
@@ -215,4 +224,57 @@ int rmm_oracle_lora_matmul_f64(const double* X, const double* W, const double* A
                                double* Y) {
   if (M < 0 || N < 0 || K <= 0 || R <= 0) return 1;
   return lora_products(X, W, A, B, M, N, K, R, Y);
+}
+
+/* QKNorm + attention for one query per batch-head.  Q: BH x D, K and V:
+ * BH x S x D (row s of head h at (h*S + s)*D), O: BH x D. */
+int rmm_oracle_qknorm_attention_f64(const double* Q, const double* K, const double* V,
+                                    const double* gq, const double* gk, double eps, int64_t BH,
+                                    int64_t S, int64_t D, double* O) {
+  if (BH < 0 || S <= 0 || D <= 0) return 1;
+  int rc = 0;
+#pragma omp parallel for schedule(static)
+  for (int64_t h = 0; h < BH; ++h) {
+    double* qn = (double*)malloc(sizeof(double) * (size_t)D);
+    double* kn = (double*)malloc(sizeof(double) * (size_t)D);
+    double* sc = (double*)malloc(sizeof(double) * (size_t)S);
+    if (!qn || !kn || !sc) {
+      free(qn);
+      free(kn);
+      free(sc);
+#pragma omp atomic write
+      rc = 2;
+      continue;
+    }
+    double rq;
+    row_rms(Q + h * D, 1, D, eps, &rq);
+    normalise(Q + h * D, gq, &rq, 1, D, qn);
+    for (int64_t s = 0; s < S; ++s) {
+      const double* k = K + (h * S + s) * D;
+      double rk;
+      row_rms(k, 1, D, eps, &rk);
+      normalise(k, gk, &rk, 1, D, kn);
+      double dot = 0.0;
+      for (int64_t d = 0; d < D; ++d) dot += qn[d] * kn[d];
+      sc[s] = dot / sqrt((double)D);
+    }
+    double mx = sc[0];
+    for (int64_t s = 1; s < S; ++s) mx = sc[s] > mx ? sc[s] : mx;
+    double den = 0.0;
+    for (int64_t s = 0; s < S; ++s) {
+      sc[s] = exp(sc[s] - mx);
+      den += sc[s];
+    }
+    double* o = O + h * D;
+    for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
+    for (int64_t s = 0; s < S; ++s) {
+      const double p = sc[s] / den;
+      const double* v = V + (h * S + s) * D;
+      for (int64_t d = 0; d < D; ++d) o[d] += p * v[d];
+    }
+    free(qn);
+    free(kn);
+    free(sc);
+  }
+  return rc;
 }

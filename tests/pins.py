@@ -14,7 +14,11 @@ every expected value below is a closed form or a property of the definition):
   * exact rational / 50-digit brute force on tiny shapes;
   * the gate's closed forms at z = +-ln 3 (sigmoid = 3/4 and 1/4 exactly);
   * LoRA: a hand-worked 1x2 example, B = 0, and the merged-weight identity
-    Act W + (Act A^T) B = Act (W + A^T B) on exactly representable inputs.
+    Act W + (Act A^T) B = Act (W + A^T B) on exactly representable inputs;
+  * QKNorm + attention: a two-key closed form (scores sqrt 2 and 0), one key,
+    identical keys, invariance to each key's scale (the norm removes it),
+    only g_q * g_k mattering, key permutations, one-hot limits and overflow
+    of large scores, 50-digit brute force.
 """
 from __future__ import annotations
 
@@ -326,6 +330,78 @@ def pin_lora(lib):
         _close(oracle.rmsnorm_lora(Xf, gf, Wf, Af, Bf, eps, lib=lib), want, rtol=1e-12, atol=1e-12)
 
 
+def _attn(lib, Q, K, V, gq, gk, eps):
+    return oracle.qknorm_attention(Q, K, V, gq, gk, eps, lib=lib)
+
+
+def _brute_attention(Q, K, V, gq, gk, eps):
+    getcontext().prec = 50
+    D = lambda x: Decimal(Fraction(float(x)).numerator) / Decimal(Fraction(float(x)).denominator)
+    out = []
+    for h in range(Q.shape[0]):
+        def norm(x, g):
+            S = sum(D(v) ** 2 for v in x) / len(x) + D(eps)
+            r = S.sqrt()
+            return [D(v) / r * D(gg) for v, gg in zip(x, g)]
+        qn = norm(Q[h], gq)
+        sc = []
+        for s in range(K.shape[1]):
+            kn = norm(K[h, s], gk)
+            sc.append(sum(a * b for a, b in zip(qn, kn)) / Decimal(K.shape[2]).sqrt())
+        mx = max(sc)
+        e = [(x - mx).exp() for x in sc]
+        den = sum(e)
+        out.append([float(sum(e[s] / den * D(V[h, s, d]) for s in range(K.shape[1])))
+                    for d in range(K.shape[2])])
+    return np.array(out)
+
+
+def pin_qknorm_attention(lib):
+    # Two keys, D = 2: q = [1, 0], k0 = [1, 0], k1 = [0, 1], unit gains, eps = 0:
+    # normalised q = k0 = [sqrt 2, 0], k1 = [0, sqrt 2]; scores 2 / sqrt 2 and 0.
+    Q = np.array([[1.0, 0.0]])
+    K = np.array([[[1.0, 0.0], [0.0, 1.0]]])
+    V = np.array([[[1.0, 2.0], [3.0, 5.0]]])
+    one = np.ones(2)
+    p0 = math.exp(math.sqrt(2.0)) / (math.exp(math.sqrt(2.0)) + 1.0)
+    _close(_attn(lib, Q, K, V, one, one, 0.0), [[p0 * 1 + (1 - p0) * 3, p0 * 2 + (1 - p0) * 5]])
+    rng = np.random.default_rng(41)
+    for (BH, S, D) in ((3, 5, 8), (2, 1, 4), (4, 7, 16)):
+        Q = rng.normal(size=(BH, D))
+        K = rng.normal(size=(BH, S, D))
+        V = rng.normal(size=(BH, S, D))
+        gq = rng.normal(1.0, 0.3, size=D)
+        gk = rng.normal(1.0, 0.3, size=D)
+        ref = _attn(lib, Q, K, V, gq, gk, 0.0)
+        # one key: the weight is exactly 1
+        assert np.array_equal(_attn(lib, Q, K[:, :1], V[:, :1], gq, gk, 1e-3), V[:, 0])
+        # identical keys: uniform weights, the mean of the values
+        Ks = np.repeat(K[:, :1], S, axis=1)
+        _close(_attn(lib, Q, Ks, V, gq, gk, 1e-3), V.mean(axis=1))
+        # each key's scale (powers of two: exact) is removed by its norm (eps = 0)
+        scale = np.exp2(rng.integers(-4, 5, size=(BH, S, 1)))
+        assert np.array_equal(_attn(lib, Q, K * scale, V, gq, gk, 0.0), ref)
+        # only the product of the gains enters the score
+        _close(_attn(lib, Q, K, V, gq * gk, np.ones(D), 0.0), ref, rtol=1e-12, atol=1e-13)
+        # keys (with their values) in another order
+        perm = rng.permutation(S)
+        _close(_attn(lib, Q, K[:, perm], V[:, perm], gq, gk, 0.0), ref, rtol=1e-12, atol=1e-13)
+        # brute force at 50 digits
+        eps = 0.125
+        _close(_attn(lib, Q, K, V, gq, gk, eps), _brute_attention(Q, K, V, gq, gk, eps),
+               rtol=1e-12, atol=1e-13)
+    # One-hot limit and overflow: with gains of 40 the aligned key's score is
+    # 1600 sqrt(D) above the others'; the result is that key's value, and the
+    # maximum is subtracted before exp (exp(1600 sqrt 8) would overflow).
+    D, S = 8, 6
+    Q = rng.normal(size=(1, D))
+    K = rng.normal(size=(1, S, D))
+    K[0, 3] = Q[0] * 0.5
+    V = rng.normal(size=(1, S, D))
+    g = np.full(D, 40.0)
+    _close(_attn(lib, Q, K, V, g, g, 0.0), V[:, 3], rtol=1e-12, atol=1e-12)
+
+
 ALL_PINS = [pin_worked_example, pin_library_matmul, pin_identity_weight, pin_constant_row,
             pin_scale_law, pin_gain_fold, pin_structure, pin_zero_row, pin_brute_force,
-            pin_gated_closed_forms, pin_unfused_steps, pin_lora]
+            pin_gated_closed_forms, pin_unfused_steps, pin_lora, pin_qknorm_attention]

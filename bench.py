@@ -38,7 +38,8 @@ F32_VALU_PEAK_TFLOPS = 78.6    # fp32 FMA on the vector ALUs without packed math
 RIDGE = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
 ROTATE_BYTES = 1 << 30
 KERNEL_SOURCES = {"decode": "rmm_decode.hip", "generic": "rmm_generic.hip",
-                  "prefill": "rmm_prefill.hip", "stream": "rmm_stream.hip"}
+                  "prefill": "rmm_prefill.hip", "stream": "rmm_stream.hip",
+                  "attention": "rmm_attn.hip"}
 
 
 def log(msg):
@@ -67,6 +68,11 @@ def stored_traffic(workload: str, variant: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def synth_attn_type():
+    import synth
+    return synth.AttnWorkload
+
+
 def cpu_baseline(wl, inp, budget_s: float):
     """The oracle, as it stands, on the host cores: whole workload if it fits
     the time budget, else a leading block of rows (rows are independent)."""
@@ -75,13 +81,18 @@ def cpu_baseline(wl, inp, budget_s: float):
 
     eps = oracle.eps_as_passed(wl.eps)
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    attn = isinstance(wl, synth_attn_type())
+    total = wl.BH if attn else wl.M  # independent rows (batch-heads for attention)
     # Probe on a small block of rows, then size the sample to the budget.
-    rows = min(wl.M, max(1, threads))
-    X = inp.X[:rows]
+    rows = min(total, max(1, threads))
+    X = inp.Q[:rows] if attn else inp.X[:rows]
 
     def once(Xs):
         t0 = time.perf_counter()
-        if wl.gated:
+        if attn:
+            n = Xs.shape[0]
+            oracle.qknorm_attention(Xs, inp.K[:n], inp.V[:n], inp.gq, inp.gk, eps)
+        elif wl.gated:
             oracle.rmsnorm_gated_mlp(Xs, inp.g, inp.W1, inp.W3, eps)
         elif wl.lora:
             oracle.rmsnorm_lora(Xs, inp.g, inp.W1, inp.LA, inp.LB, eps)
@@ -89,20 +100,23 @@ def cpu_baseline(wl, inp, budget_s: float):
             oracle.rmsnorm_matmul(Xs, inp.g, inp.W1, eps)
         return time.perf_counter() - t0
 
+    full = inp.Q if attn else inp.X
+    unit_name = "batch-heads" if attn else "rows"
     t_probe = once(X)
     per_row = t_probe / rows
     rows_budget = int(budget_s / max(per_row, 1e-9))
-    if rows_budget >= wl.M:
-        reps = max(1, int(budget_s / max(per_row * wl.M, 1e-9)))
+    if rows_budget >= total:
+        reps = max(1, int(budget_s / max(per_row * total, 1e-9)))
         reps = min(reps, 50)
-        t = sum(once(inp.X) for _ in range(reps)) / reps
-        sample = f"full workload ({wl.M} rows), mean of {reps} runs"
+        t = sum(once(full) for _ in range(reps)) / reps
+        sample = f"full workload ({total} {unit_name}), mean of {reps} runs"
         frac = 1.0
     else:
         rows = max(rows, (rows_budget // threads) * threads)
-        t = once(inp.X[:rows])
-        frac = rows / wl.M
-        sample = f"first {rows} of {wl.M} rows (rows are independent); time scaled x{wl.M / rows:.1f}"
+        t = once(full[:rows])
+        frac = rows / total
+        sample = (f"first {rows} of {total} {unit_name} (they are independent); time scaled "
+                  f"x{total / rows:.1f}")
     t_full = t / frac
     bound = "hbm" if wl.flops() / wl.algo_bytes() < RIDGE else "mfma"
     if bound == "hbm":
@@ -159,10 +173,11 @@ def main():
         print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 10}))
         return
     wl = synth.get_workload(args.workload)
+    attn = isinstance(wl, synth.AttnWorkload)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     log(f"workload {wl.name}: generating inputs")
-    inp = synth.make_inputs(wl)
+    inp = synth.make_attention_inputs(wl.BH, wl.S, wl.D) if attn else synth.make_inputs(wl)
 
     def dev_tensor(name):
         a = inp.device_array(name)
@@ -170,8 +185,11 @@ def main():
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
 
-    base = {n: dev_tensor(n) for n in (["X", "g", "W1"] + (["W3"] if wl.gated else [])
-                                         + (["LA", "LB"] if wl.lora else []))}
+    if attn:
+        names = ["Q", "K", "V", "gq", "gk"]
+    else:
+        names = (["X", "g", "W1"] + (["W3"] if wl.gated else []) + (["LA", "LB"] if wl.lora else []))
+    base = {n: dev_tensor(n) for n in names}
     per_set = wl.algo_bytes()
     free = torch.cuda.mem_get_info(dev)[0]
     R = max(1, math.ceil(ROTATE_BYTES / per_set))
@@ -179,21 +197,27 @@ def main():
     sets = []
     for r in range(R):
         s = {n: (t if r == 0 else t.clone()) for n, t in base.items()}
-        s["Y"] = torch.empty((wl.M, wl.N), dtype=s["X"].dtype, device=dev)
+        s["Y"] = torch.empty((wl.BH, wl.D) if attn else (wl.M, wl.N), dtype=torch.bfloat16
+                             if wl.dtype == "bf16" else torch.float32, device=dev)
         sets.append(s)
-    if wl.lora:
-        st, variant, splits = tpa.plan_lora(wl.M, wl.N, wl.K, wl.lora, dtype=sets[0]["X"].dtype,
+    if attn:
+        st, splits, _ = tpa.plan_attention(wl.BH, wl.S, wl.D, splits=args.splits)
+        variant = "attention"
+    elif wl.lora:
+        st, variant, splits = tpa.plan_lora(wl.M, wl.N, wl.K, wl.lora, dtype=sets[0]["Y"].dtype,
                                             variant=args.variant, splits=args.splits)
     else:
-        st, variant, splits = tpa.plan(wl.M, wl.N, wl.K, dtype=sets[0]["X"].dtype,
+        st, variant, splits = tpa.plan(wl.M, wl.N, wl.K, dtype=sets[0]["Y"].dtype,
                                        gated=wl.gated, variant=args.variant, splits=args.splits)
     if st != 0:
         raise SystemExit(f"plan failed with status {st}")
     log(f"variant {variant}, splits {splits}, {R} rotating input sets "
         f"({R * per_set / 2**20:.0f} MiB)")
     stream = torch.cuda.Stream(dev)
-    dcode = tpa._DTYPES[sets[0]["X"].dtype]
-    if wl.lora:
+    dcode = tpa._DTYPES[sets[0]["Y"].dtype]
+    if attn:
+        nbytes = tpa._binding.attention_workspace_bytes(dcode, wl.BH, wl.S, wl.D, args.splits)
+    elif wl.lora:
         nbytes = tpa._binding.lora_workspace_bytes(dcode, wl.M, wl.N, wl.K, wl.lora, args.variant,
                                                    args.splits)
     else:
@@ -203,7 +227,10 @@ def main():
     torch.cuda.synchronize()
 
     def call(s):
-        if wl.gated:
+        if attn:
+            tpa.qknorm_attention(s["Q"], s["K"], s["V"], s["gq"], s["gk"], wl.eps, out=s["Y"],
+                                 splits=args.splits, workspace=ws)
+        elif wl.gated:
             tpa.rmsnorm_gated_mlp(s["X"], s["g"], s["W1"], s["W3"], wl.eps, out=s["Y"],
                                   variant=args.variant, splits=args.splits, workspace=ws)
         elif wl.lora:
@@ -278,7 +305,7 @@ def main():
     # worked example): an RMSNorm kernel writes the normalised X, then a
     # product reads it back -- our plain-product kernels, and the vendor GEMM.
     unfused = None
-    if not args.no_unfused:
+    if not args.no_unfused and not attn:
         xn = [torch.empty_like(s["X"]) for s in sets]
         # the vendor leg multiplies by A^T as a K x R matrix (made once, untimed)
         at = [s["LA"].t().contiguous() for s in sets] if wl.lora else None
@@ -334,7 +361,7 @@ def main():
         roof = {"bound": "mfma" if wl.dtype == "bf16" else "alu", "achieved": tflops,
                 "peak": peak, "unit": "TFLOP/s", "frac": tflops / peak}
     roof["traffic"] = stored_traffic(wl.name, variant)
-    roof["kernel"] = f"{variant}_kernel"
+    roof["kernel"] = "qknorm_attention_kernel" if attn else f"{variant}_kernel"
     roof["algorithmic_bytes_per_launch"] = per_set
     roof["algorithmic_flops_per_launch"] = wl.flops()
 
@@ -347,8 +374,9 @@ def main():
         "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": steps,
         "warmup": warm, "ms_per_step": ms / steps, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
-        "config": {"workload": wl.name, "M": wl.M, "K": wl.K, "N": wl.N, "gated": wl.gated,
-                   "lora_rank": wl.lora,
+        "config": ({"workload": wl.name, "BH": wl.BH, "S": wl.S, "D": wl.D} if attn else
+                   {"workload": wl.name, "M": wl.M, "K": wl.K, "N": wl.N, "gated": wl.gated,
+                    "lora_rank": wl.lora}) | {
                    "eps": wl.eps, "variant": variant, "splits": splits,
                    "rotating_input_sets": R, "hip_graph": graph is not None,
                    "clock_settle_calls": settle_calls},

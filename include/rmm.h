@@ -38,10 +38,14 @@
  * Workspace.  The decode (split-K) variant combines partial k-sums across
  * workgroups through a caller-owned workspace.  `ws` may be NULL: the library
  * then picks a variant that needs none (correct, slower).  A non-NULL `ws` must
- * be zero-filled before its first use; the kernels reset its arrival counters
- * to zero (the partial-sum slots keep the last call's values, which every
- * call overwrites before reading), so it can be reused by later calls on the
- * same stream without clearing.  One workspace must not be used
+ * be zero-filled before its first use.  A call resets its arrival counters to
+ * zero but leaves its partial sums in the rest of the workspace (every call
+ * overwrites its slots before reading them), so the workspace can be reused
+ * without clearing by later calls with the same layout -- the same entry
+ * point, shape, dtype, variant and split count -- on the same stream.  A call
+ * with another layout may keep its counters where the earlier call left
+ * partial sums: zero-fill the workspace again first, or give each layout its
+ * own.  One workspace must not be used
  * by two calls that may run at the same time.  ws_bytes below
  * rmm_workspace_bytes*() returns RMM_ERR_WORKSPACE.
  *
@@ -195,6 +199,43 @@ rmm_status rmm_lora_matmul(const void* X, const void* W, const void* A, const vo
                            size_t ws_bytes, hipStream_t stream);
 size_t rmm_lora_workspace_bytes(rmm_dtype dtype, int64_t M, int64_t N, int64_t K, int64_t R,
                                 rmm_variant variant, int splits);
+
+/* QKNorm + attention, one query per batch-head (the QKNorm + Attention row of
+ * the same page's benchmark table, "五、实验结果"; the page names the fusion
+ * only, the reading is RMSNorm over the head dimension applied to the query
+ * and to every cached key, then scaled dot-product attention, no mask):
+ *
+ *   qn = q / rms(q) * gq,  kn_s = k_s / rms(k_s) * gk,  rms(x) = sqrt(mean_d x^2 + eps)
+ *   O  = sum_s softmax_s(qn . kn_s / sqrt(D)) v_s
+ *
+ * Layouts (row-major, packed, bf16 only): Q: BH x D (BH = batch x heads),
+ * K and V: BH x S x D (key s of head h at (h*S + s)*D), gq, gk: D, O: BH x D.
+ * The normalised keys are never formed: one pass over each key row
+ * accumulates (q*gq*gk) . k_s and sum_d k_sd^2 in fp32, and the key's 1/RMS
+ * scales the finished dot product; softmax in fp32 with a running maximum;
+ * O rounded once to bf16.  D must be 64 or 128 and S >= 1 (RMM_ERR_SHAPE),
+ * dtype RMM_DTYPE_BF16 (RMM_ERR_DTYPE), every pointer 16-byte aligned and
+ * S*D*2 < 2^31 (RMM_ERR_VARIANT).  The keys of one batch-head are split
+ * into chunks combined by the last workgroup to arrive (log-sum-exp merge of
+ * (o, max, sum) partials); that needs a workspace (rules as above, sized by
+ * rmm_attention_workspace_bytes); without one each batch-head runs in a
+ * single workgroup.  splits (qknorm_attention_ex): chunks per batch-head,
+ * 0 = chosen by the library, 1..S forced.  BH == 0 is a no-op. */
+rmm_status qknorm_attention(const void* Q, const void* K, const void* V, const void* gq,
+                            const void* gk, void* O, float eps, int64_t BH, int64_t S, int64_t D,
+                            rmm_dtype dtype, void* ws, size_t ws_bytes, hipStream_t stream);
+rmm_status qknorm_attention_ex(const void* Q, const void* K, const void* V, const void* gq,
+                               const void* gk, void* O, float eps, int64_t BH, int64_t S,
+                               int64_t D, rmm_dtype dtype, int splits, void* ws, size_t ws_bytes,
+                               hipStream_t stream);
+size_t rmm_attention_workspace_bytes(rmm_dtype dtype, int64_t BH, int64_t S, int64_t D,
+                                     int splits);
+/* Host-only: validates like qknorm_attention_ex and reports the chunk count
+ * and keys per chunk that would run (either output may be NULL). */
+rmm_status rmm_plan_attention(const void* Q, const void* K, const void* V, const void* gq,
+                              const void* gk, const void* O, float eps, int64_t BH, int64_t S,
+                              int64_t D, rmm_dtype dtype, int splits, const void* ws,
+                              size_t ws_bytes, int* chunks_out, int64_t* keys_per_chunk_out);
 
 /* Workspace bytes the call with these arguments would use (0 if none).  The
  * plain entry points use variant = AUTO, splits = 0.  Returns 0 for

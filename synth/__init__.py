@@ -12,7 +12,7 @@ import subprocess
 
 import numpy as np
 
-from .workloads import WORKLOADS, Workload, get_workload  # noqa: F401
+from .workloads import ATTN_WORKLOADS, WORKLOADS, AttnWorkload, Workload, get_workload  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "synth.c")
@@ -23,6 +23,7 @@ _lib = None
 STREAM_X, STREAM_G, STREAM_W1, STREAM_W3, STREAM_ROWSCALE, STREAM_ROWPICK = 1, 2, 3, 4, 5, 6
 STREAM_EXACT = 7
 STREAM_LA, STREAM_LB = 20, 21  # adapter down- and up-projection (clear of the exact streams)
+STREAM_Q, STREAM_K, STREAM_V, STREAM_GQ, STREAM_GK, STREAM_PICK = 22, 23, 24, 25, 26, 27
 
 
 def build(force: bool = False) -> str:
@@ -200,3 +201,42 @@ def make_exact_inputs(M: int, K: int, N: int, dtype: str, seed: int = 0, gated: 
     LA = exact_values(seed, STREAM_EXACT + 5, (lora, K), 2, density) if lora else None
     LB = exact_values(seed, STREAM_EXACT + 6, (lora, N), 2, density) if lora else None
     return Inputs(wl, X, g, W1, W3, None, LA, LB)
+
+
+class AttnInputs:
+    """Stored values (float32, bf16-exact) and bf16 bit patterns of one
+    attention call: Q [BH, D], K and V [BH, S, D], gq and gk [D]."""
+
+    def __init__(self, Q, K, V, gq, gk):
+        self.bits = {}
+        for name, a in (("Q", Q), ("K", K), ("V", V), ("gq", gq), ("gk", gk)):
+            b = to_bf16_bits(a)
+            self.bits[name] = b
+            setattr(self, name, bf16_bits_to_f32(b))
+
+    def device_array(self, name):
+        return self.bits[name]
+
+
+def make_attention_inputs(BH: int, S: int, D: int, seed: int = 0) -> AttnInputs:
+    Q = normals(seed, STREAM_Q, BH, D)
+    K = normals(seed, STREAM_K, BH * S, D).reshape(BH, S, D)
+    V = normals(seed, STREAM_V, BH * S, D).reshape(BH, S, D)
+    gq = normals(seed, STREAM_GQ, 1, D, mul=0.1, add=1.0).reshape(D)
+    gk = normals(seed, STREAM_GK, 1, D, mul=0.1, add=1.0).reshape(D)
+    return AttnInputs(Q, K, V, gq, gk)
+
+
+def make_attention_onehot(BH: int, S: int, D: int, seed: int = 0):
+    """Inputs whose softmax is exactly one-hot in fp32: gains of 40 and, per
+    batch-head, one key equal to q / 2 (exact in bf16), picked by the hash;
+    that key's score exceeds every other by thousands, so its weight is 1
+    and the others' are 0, and the output is that key's value row.
+    Returns (inputs, picked key index per batch-head)."""
+    inp = make_attention_inputs(BH, S, D, seed)
+    pick = (hashes(seed, STREAM_PICK, 0, BH, 0) % np.uint64(S)).astype(np.int64)
+    Q = inp.Q.copy()
+    K = inp.K.copy()
+    K[np.arange(BH), pick] = 0.5 * Q
+    g = np.full(D, 40.0, np.float32)
+    return AttnInputs(Q, K, inp.V, g, g), pick

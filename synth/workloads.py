@@ -59,5 +59,37 @@ WORKLOADS = {
 ORDER = list(WORKLOADS)
 
 
-def get_workload(name: str) -> Workload:
-    return WORKLOADS[name]
+@dataclass(frozen=True)
+class AttnWorkload:
+    """QKNorm + attention, one query per batch-head: Q [BH, D], K and V
+    [BH, S, D], gains [D], all bf16.  Q, K, V ~ N(0,1); gains ~ 1 + 0.1 N(0,1)."""
+    name: str
+    BH: int
+    S: int
+    D: int
+    eps: float
+    dtype: str = "bf16"
+
+    @property
+    def elem_bytes(self) -> int:
+        return 2
+
+    def flops(self) -> int:
+        """Algorithmic flops: q.k and p.v, 2 * D each per key."""
+        return 4 * self.BH * self.S * self.D
+
+    def algo_bytes(self) -> int:
+        """Every input once and O once."""
+        return (2 * self.BH * self.S * self.D + 2 * self.BH * self.D + 2 * self.D) * 2
+
+
+ATTN_WORKLOADS = {
+    w.name: w for w in (
+        # 8 sequences x 32 heads attending over a 2048-token cache, head dim 128
+        AttnWorkload("attn_bh256_s2048_d128", 256, 2048, 128, 1e-6),
+    )
+}
+
+
+def get_workload(name: str):
+    return WORKLOADS[name] if name in WORKLOADS else ATTN_WORKLOADS[name]

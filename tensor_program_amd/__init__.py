@@ -13,6 +13,9 @@
     y = tpa.rmsnorm_lora(x, g, w, a, b, eps)          # norm(x) @ w + (norm(x) @ a.T) @ b
     y = tpa.lora_matmul(x, w, a, b)                   # x @ w + (x @ a.T) @ b
 
+    # QKNorm + attention, one query per batch-head (q: [BH, D], k, v: [BH, S, D])
+    o = tpa.qknorm_attention(q, k, v, gq, gk, eps)
+
 x: [M, K], g: [K], w/w1/w3: [K, N], all contiguous, on one GPU, all float32 or
 all bfloat16.  The work is enqueued on torch's current stream; this module
 only marshals arguments (see include/rmm.h for the contract).
@@ -25,18 +28,22 @@ from . import _binding
 from ._binding import RmmError, load_library  # noqa: F401
 
 __all__ = ["rmsnorm_matmul", "rmsnorm_gated_mlp", "rmsnorm", "matmul", "gated_matmul",
-           "rmsnorm_lora", "lora_matmul", "RmmError", "load_library", "Workspace"]
+           "rmsnorm_lora", "lora_matmul", "qknorm_attention", "RmmError", "load_library",
+           "Workspace"]
 
 _DTYPES = {torch.float32: _binding.DTYPE_F32, torch.bfloat16: _binding.DTYPE_BF16}
 
 
 class Workspace:
-    """A zero-filled device workspace for the split-K variant.
+    """A zero-filled device workspace for the split-K and split-key combines.
 
-    The kernels reset its arrival counters after every call (the partial-sum
-    slots are overwritten before they are read), so one workspace serves any
-    number of calls on one stream.  Calls that may overlap (different streams)
-    need different workspaces.
+    A call resets its arrival counters but leaves its partial sums behind, so
+    a workspace serves any number of calls with the same layout (shape, dtype,
+    variant, split count) on one stream without clearing; a call with another
+    layout could find those partials where it keeps its counters, so it needs
+    a zero-filled workspace of its own (the functions below keep one per
+    layout).  Calls that may overlap (different streams) need different
+    workspaces.
     """
 
     def __init__(self, nbytes: int, device):
@@ -51,8 +58,8 @@ class Workspace:
 _workspaces: dict = {}
 
 
-def _workspace_for(device, stream_handle: int, nbytes: int) -> Workspace:
-    key = (str(device), stream_handle)
+def _workspace_for(device, stream_handle: int, nbytes: int, layout: tuple) -> Workspace:
+    key = (str(device), stream_handle, layout)
     ws = _workspaces.get(key)
     if ws is None or ws.nbytes < nbytes:
         ws = Workspace(nbytes, device)
@@ -98,7 +105,8 @@ def _call(x, g, w1, w3, eps, out, variant, splits, workspace):
     stream = torch.cuda.current_stream(x.device).cuda_stream
     need = _binding.workspace_bytes(dtype, M, N, K, gated, variant, splits)
     if workspace is None and need > 0:
-        workspace = _workspace_for(x.device, stream, need)
+        workspace = _workspace_for(x.device, stream, need,
+                                   ("fused", dtype, M, N, K, gated, variant, splits))
     ws_ptr = workspace.ptr if workspace is not None else None
     ws_bytes = workspace.nbytes if workspace is not None else 0
     v = _binding.VARIANTS[variant]
@@ -163,7 +171,7 @@ def _plain(x, w1, w3, out, workspace):
     stream = torch.cuda.current_stream(x.device).cuda_stream
     need = _binding.workspace_bytes(dtype, M, N, K, gated)
     if workspace is None and need > 0:
-        workspace = _workspace_for(x.device, stream, need)
+        workspace = _workspace_for(x.device, stream, need, ("plain", dtype, M, N, K, gated))
     ws_ptr = workspace.ptr if workspace is not None else None
     ws_bytes = workspace.nbytes if workspace is not None else 0
     if gated:
@@ -209,7 +217,8 @@ def _lora(x, g, w, a, b, eps, out, variant, splits, workspace, norm):
     stream = torch.cuda.current_stream(x.device).cuda_stream
     need = _binding.lora_workspace_bytes(dtype, M, N, K, R, variant, splits)
     if workspace is None and need > 0:
-        workspace = _workspace_for(x.device, stream, need)
+        workspace = _workspace_for(x.device, stream, need,
+                                   ("lora", dtype, M, N, K, R, variant, splits, norm))
     ws_ptr = workspace.ptr if workspace is not None else None
     ws_bytes = workspace.nbytes if workspace is not None else 0
     if norm:
@@ -246,6 +255,50 @@ def plan_lora(M, N, K, R, dtype=torch.bfloat16, variant="auto", splits=0, with_w
     nb = _binding.lora_workspace_bytes(d, M, N, K, R, variant, splits) if with_workspace else 0
     return _binding.plan_lora(ptrs[0], ptrs[1], ptrs[2], ptrs[3], ptrs[4], ptrs[5], 1e-6, M, N, K,
                               R, d, variant, splits, ws, nb)
+
+
+def qknorm_attention(q, k, v, gq, gk, eps: float, out=None, splits: int = 0,
+                     workspace: Workspace | None = None):
+    """o = softmax(norm(q) . norm(k)^T / sqrt(D)) v per batch-head, fused (bf16;
+    q: [BH, D], k, v: [BH, S, D], gq, gk: [D], D = 64 or 128)."""
+    _check_operands([q, k, v, gq, gk], ["q", "k", "v", "gq", "gk"])
+    if q.dim() != 2 or k.dim() != 3 or gq.dim() != 1 or gk.dim() != 1:
+        raise ValueError("expected q: [BH, D], k, v: [BH, S, D], gq, gk: [D]")
+    BH, D = q.shape
+    S = k.shape[1]
+    if tuple(k.shape) != (BH, S, D) or tuple(v.shape) != (BH, S, D) or gq.shape[0] != D or \
+            gk.shape[0] != D:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, "
+                         f"v {tuple(v.shape)}")
+    if out is None:
+        out = torch.empty((BH, D), dtype=q.dtype, device=q.device)
+    else:
+        _check_operands([q, out], ["q", "out"])
+        if tuple(out.shape) != (BH, D):
+            raise ValueError(f"out has shape {tuple(out.shape)}, expected {(BH, D)}")
+    dtype = _DTYPES[q.dtype]
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    need = _binding.attention_workspace_bytes(dtype, BH, S, D, splits)
+    if workspace is None and need > 0:
+        workspace = _workspace_for(q.device, stream, need, ("attention", BH, S, D, splits))
+    ws_ptr = workspace.ptr if workspace is not None else None
+    ws_bytes = workspace.nbytes if workspace is not None else 0
+    _binding.check(load_library().qknorm_attention_ex(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), gq.data_ptr(), gk.data_ptr(), out.data_ptr(),
+        float(eps), BH, S, D, dtype, splits, ws_ptr, ws_bytes, stream))
+    return out
+
+
+def plan_attention(BH, S, D, splits=0, with_workspace=True):
+    """Chunks per batch-head and keys per chunk an attention call would run (host only)."""
+    base = 1 << 40
+    span = 1 << 36
+    ptrs = [base + i * span for i in range(7)]
+    d = _binding.DTYPE_BF16
+    ws = ptrs[6] if with_workspace else None
+    nb = _binding.attention_workspace_bytes(d, BH, S, D, splits) if with_workspace else 0
+    return _binding.plan_attention(ptrs[0], ptrs[1], ptrs[2], ptrs[3], ptrs[4], ptrs[5], 1e-6, BH,
+                                   S, D, d, splits, ws, nb)
 
 
 def plan(M, N, K, dtype=torch.bfloat16, gated=False, variant="auto", splits=0,

@@ -22,7 +22,8 @@ SYMBOLS = ("rmsnorm_matmul", "rmsnorm_gated_mlp", "rmsnorm_matmul_ex", "rmsnorm_
            "rmm_rmsnorm", "rmm_matmul", "rmm_gated_matmul", "rmm_workspace_bytes",
            "rmm_workspace_bytes_ex", "rmm_plan", "rmm_status_string", "rmm_last_hip_error",
            "rmm_abi_version", "rmsnorm_lora", "rmsnorm_lora_ex", "rmm_lora_matmul",
-           "rmm_lora_workspace_bytes", "rmm_plan_lora")
+           "rmm_lora_workspace_bytes", "rmm_plan_lora", "qknorm_attention",
+           "qknorm_attention_ex", "rmm_attention_workspace_bytes", "rmm_plan_attention")
 LORA_MAX_RANK = 64
 
 _lib = None
@@ -67,6 +68,16 @@ def load_library(path: str = LIB_PATH):
     lib.rmm_plan_lora.argtypes = [vp, vp, vp, vp, vp, vp, f32, i64, i64, i64, i64, i32, i32, i32,
                                   vp, sz, ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.rmm_plan_lora.restype = i32
+    lib.qknorm_attention.argtypes = [vp, vp, vp, vp, vp, vp, f32, i64, i64, i64, i32, vp, sz, vp]
+    lib.qknorm_attention.restype = i32
+    lib.qknorm_attention_ex.argtypes = [vp, vp, vp, vp, vp, vp, f32, i64, i64, i64, i32, i32, vp,
+                                        sz, vp]
+    lib.qknorm_attention_ex.restype = i32
+    lib.rmm_attention_workspace_bytes.argtypes = [i32, i64, i64, i64, i32]
+    lib.rmm_attention_workspace_bytes.restype = sz
+    lib.rmm_plan_attention.argtypes = [vp, vp, vp, vp, vp, vp, f32, i64, i64, i64, i32, i32, vp, sz,
+                                       ctypes.POINTER(i32), ctypes.POINTER(i64)]
+    lib.rmm_plan_attention.restype = i32
     lib.rmm_workspace_bytes.argtypes = [i32, i64, i64, i64, i32]
     lib.rmm_workspace_bytes.restype = sz
     lib.rmm_workspace_bytes_ex.argtypes = [i32, i64, i64, i64, i32, i32, i32]
@@ -128,3 +139,16 @@ def plan_lora(X, g, W, A, B, Y, eps, M, N, K, R, dtype, variant="auto", splits=0
     st = load_library().rmm_plan_lora(X, g, W, A, B, Y, eps, M, N, K, R, dtype, VARIANTS[variant],
                                       splits, ws, ws_bytes, ctypes.byref(v), ctypes.byref(s))
     return st, VARIANT_NAMES.get(v.value), s.value
+
+
+def attention_workspace_bytes(dtype: int, BH: int, S: int, D: int, splits: int = 0) -> int:
+    return int(load_library().rmm_attention_workspace_bytes(dtype, BH, S, D, splits))
+
+
+def plan_attention(Q, K, V, gq, gk, O, eps, BH, S, D, dtype, splits=0, ws=None, ws_bytes=0):
+    """Host-only planning through rmm_plan_attention: (status, chunks, keys per chunk)."""
+    c = ctypes.c_int(-1)
+    kc = ctypes.c_int64(-1)
+    st = load_library().rmm_plan_attention(Q, K, V, gq, gk, O, eps, BH, S, D, dtype, splits, ws,
+                                           ws_bytes, ctypes.byref(c), ctypes.byref(kc))
+    return st, c.value, kc.value

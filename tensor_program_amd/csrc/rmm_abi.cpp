@@ -194,6 +194,51 @@ rmm_status run(const void* X, const void* g, const void* W1, const void* W3, voi
   return RMM_OK;
 }
 
+// QKNorm + attention: validation in the documented order, then the plan.
+rmm_status attn_plan_call(const void* Q, const void* K, const void* V, const void* gq,
+                          const void* gk, const void* O, float eps, int64_t BH, int64_t S,
+                          int64_t D, rmm_dtype dtype, int splits, const void* ws, size_t ws_bytes,
+                          AttnPlan* plan) {
+  // 1. pointers
+  if (BH > 0 && (!Q || !K || !V || !gq || !gk || !O)) return RMM_ERR_NULL;
+  // 2. shape: head dimension 64 or 128, at least one key
+  if (BH < 0 || S < 1 || (D != 64 && D != 128)) return RMM_ERR_SHAPE;
+  int64_t sd, bhsd, tmp;
+  if (__builtin_mul_overflow(S, D, &sd) || __builtin_mul_overflow(BH, sd, &bhsd) ||
+      __builtin_mul_overflow(bhsd, (int64_t)2, &tmp))
+    return RMM_ERR_SHAPE;
+  // 3. eps
+  if (!isfinite(eps) || eps < 0.0f) return RMM_ERR_EPS;
+  // 4. dtype: this path stores bf16 only
+  if (dtype != RMM_DTYPE_BF16) return RMM_ERR_DTYPE;
+  if (BH == 0) {
+    plan->chunks = 1;
+    plan->kchunk = S;
+    plan->ws_bytes = 0;
+    return RMM_OK;
+  }
+  // 5. aliasing of the output
+  const size_t ob = (size_t)(BH * D) * 2;
+  if (overlaps(O, ob, Q, ob) || overlaps(O, ob, K, (size_t)bhsd * 2) ||
+      overlaps(O, ob, V, (size_t)bhsd * 2) || overlaps(O, ob, gq, (size_t)D * 2) ||
+      overlaps(O, ob, gk, (size_t)D * 2) || overlaps(O, ob, ws, ws ? ws_bytes : 0))
+    return RMM_ERR_ALIAS;
+  // 6. what the kernel can run: 16-byte aligned operands, 32-bit offsets
+  // within one batch-head's keys, a split count between 1 and S
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(gq) || !aligned16(gk) ||
+      !aligned16(O))
+    return RMM_ERR_VARIANT;
+  if (sd * 2 > (int64_t)INT32_MAX || splits < 0 || splits > S) return RMM_ERR_VARIANT;
+  const int s = splits == 0 ? (ws ? 0 : 1) : splits;
+  if (s > 1 && !ws) return RMM_ERR_WORKSPACE;
+  rmm_attention_plan(BH, S, D, s, plan);
+  if ((int64_t)plan->chunks * BH > (int64_t)INT32_MAX || plan->ws_bytes > (size_t)INT32_MAX)
+    return RMM_ERR_VARIANT;
+  // 7. workspace
+  if (ws && ws_bytes < plan->ws_bytes) return RMM_ERR_WORKSPACE;
+  return RMM_OK;
+}
+
 // The adapter entry points pass their rank through this: internally R < 0
 // means "no adapter", so a negative rank from a caller becomes 0, which
 // fails the rank check like any other rank outside 1..64.
@@ -264,6 +309,53 @@ rmm_status rmm_lora_matmul(const void* X, const void* W, const void* A, const vo
                            size_t ws_bytes, hipStream_t stream) {
   return run(X, X, W, nullptr, Y, 0.0f, M, N, K, dtype, 0, RMM_VARIANT_AUTO, 0, ws, ws_bytes,
              stream, 0, A, B, lora_rank_arg(R));
+}
+
+rmm_status qknorm_attention_ex(const void* Q, const void* K, const void* V, const void* gq,
+                               const void* gk, void* O, float eps, int64_t BH, int64_t S,
+                               int64_t D, rmm_dtype dtype, int splits, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
+  AttnPlan plan;
+  const rmm_status st =
+      attn_plan_call(Q, K, V, gq, gk, O, eps, BH, S, D, dtype, splits, ws, ws_bytes, &plan);
+  if (st != RMM_OK || BH == 0) return st;
+  const AttnArgs a{Q, K, V, gq, gk, O, eps, BH, S, D, stream};
+  const hipError_t err = rmm_launch_attention(a, plan, plan.chunks > 1 ? ws : nullptr);
+  if (err != hipSuccess) {
+    g_last_hip_error = (int)err;
+    return RMM_ERR_HIP;
+  }
+  return RMM_OK;
+}
+
+rmm_status qknorm_attention(const void* Q, const void* K, const void* V, const void* gq,
+                            const void* gk, void* O, float eps, int64_t BH, int64_t S, int64_t D,
+                            rmm_dtype dtype, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return qknorm_attention_ex(Q, K, V, gq, gk, O, eps, BH, S, D, dtype, 0, ws, ws_bytes, stream);
+}
+
+size_t rmm_attention_workspace_bytes(rmm_dtype dtype, int64_t BH, int64_t S, int64_t D,
+                                     int splits) {
+  if (dtype != RMM_DTYPE_BF16 || BH <= 0 || S < 1 || (D != 64 && D != 128) || splits < 0 ||
+      splits > S)
+    return 0;
+  AttnPlan plan;
+  rmm_attention_plan(BH, S, D, splits, &plan);
+  return plan.ws_bytes;
+}
+
+rmm_status rmm_plan_attention(const void* Q, const void* K, const void* V, const void* gq,
+                              const void* gk, const void* O, float eps, int64_t BH, int64_t S,
+                              int64_t D, rmm_dtype dtype, int splits, const void* ws,
+                              size_t ws_bytes, int* chunks_out, int64_t* keys_per_chunk_out) {
+  AttnPlan plan;
+  const rmm_status st =
+      attn_plan_call(Q, K, V, gq, gk, O, eps, BH, S, D, dtype, splits, ws, ws_bytes, &plan);
+  if (st == RMM_OK) {
+    if (chunks_out) *chunks_out = plan.chunks;
+    if (keys_per_chunk_out) *keys_per_chunk_out = plan.kchunk;
+  }
+  return st;
 }
 
 rmm_status rmm_rmsnorm(const void* X, const void* g, void* Xn, float eps, int64_t M, int64_t K,

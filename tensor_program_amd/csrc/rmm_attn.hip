@@ -1,0 +1,286 @@
+// QKNorm + attention for one query per batch-head (decode), bandwidth-bound.
+//
+// The QKNorm + Attention row of the Mirage paper review's benchmark table
+// ("五、实验结果") names the fusion only; the reading is RMSNorm over the head
+// dimension D (gains gq, gk) applied to the query and to every cached key,
+// then scaled dot-product attention over the keys:
+//
+//   score_s = (q/rms(q)*gq) . (k_s/rms(k_s)*gk) / sqrt(D)
+//           = (sum_d u_d k_sd) / (rms(q) rms(k_s) sqrt(D)),   u = q * gq * gk
+//   o = sum_s softmax(score)_s v_s
+//
+// As in the fused RMSNorm+MatMul ("核心公式": the k-independent divisor moves
+// out of the sum), the normalised keys are never formed: each key row is read
+// once, and the same pass accumulates u . k_s and sum_d k_sd^2; the division
+// by the key's RMS is applied to the finished dot product.  u is exact in fp32
+// (a product of three bf16 values has at most 24 significant bits).
+//
+// Work decomposition: a workgroup (4 waves) owns one batch-head and a chunk of
+// its keys.  D/8 lanes cover one key row (16 bytes each); a wave loads 64/(D/8)
+// keys per instruction and U instructions per block, K and V double-buffered
+// in registers.  Every lane group keeps its own running (max, sum, o) and
+// rescales once per block (online softmax); groups merge by shuffles, waves
+// through LDS.  With several chunks the workgroup stores (o, max, sum) with
+// device-scope coherence and the last one to arrive merges them (log-sum-exp)
+// and writes o / sum.  Keys past S or past the chunk are range-checked loads
+// that read zeros and get weight 0.
+#include "rmm_device.h"
+
+namespace rmm {
+
+constexpr int AT_THREADS = 256;
+constexpr int AT_U = 4;                          // key loads per block and lane
+constexpr uint32_t kAtOutOfRange = 0x80000000u;  // past every buffer this path accepts
+constexpr int kAtCoherentDevice = 16;            // SC1: device-scope coherence
+constexpr float kAtNone = -1.0e30f;              // running max before any valid key
+
+template <int D>
+__global__ __launch_bounds__(AT_THREADS) void qknorm_attention_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc,
+    const bf16_t* __restrict__ gq, const bf16_t* __restrict__ gk, bf16_t* __restrict__ O,
+    float eps, int64_t S, int64_t kchunk, int C, unsigned* __restrict__ cnt,
+    float* __restrict__ part) {
+  constexpr int LPK = D / 8;          // lanes per key row
+  constexpr int KPI = 64 / LPK;       // keys per load instruction (per wave)
+  constexpr int BLK = AT_U * KPI;     // keys per wave block
+  constexpr int NWV = AT_THREADS / 64;
+  __shared__ float sm_o[NWV][D];
+  __shared__ float sm_m[NWV], sm_l[NWV];
+  __shared__ int last;
+
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int j = l / LPK, c = l % LPK;  // key slot in an instruction, 8-dim chunk
+  const int64_t bh = blockIdx.x / C;
+  const int chunk = (int)(blockIdx.x % C);
+  const int64_t s_lo = (int64_t)chunk * kchunk;
+  const int64_t s_hi = (s_lo + kchunk < S) ? (s_lo + kchunk) : S;
+
+  // u = q * gq * gk for this lane's 8 dims; sum of q^2 over D (per wave).
+  float u[8];
+  float qss = 0.f;
+  {
+    const u32x4 qv = *(const u32x4*)(Q + bh * D + 8 * c);
+    const u32x4 a = *(const u32x4*)(gq + 8 * c);
+    const u32x4 b = *(const u32x4*)(gk + 8 * c);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const float q0 = bf16_lo(qv[d]), q1 = bf16_hi(qv[d]);
+      u[2 * d] = q0 * bf16_lo(a[d]) * bf16_lo(b[d]);
+      u[2 * d + 1] = q1 * bf16_hi(a[d]) * bf16_hi(b[d]);
+      qss += q0 * q0 + q1 * q1;
+    }
+#pragma unroll
+    for (int o = 1; o < LPK; o <<= 1) qss += __shfl_xor(qss, o);
+  }
+  // 1 / (rms(q) sqrt(D)), IEEE divide and square root.
+  const float cq = 1.0f / (__fsqrt_rn(__fdiv_rn(qss, (float)D) + eps) * __fsqrt_rn((float)D));
+
+  // Buffer resources over this batch-head's S x D rows (the plan keeps
+  // S * D * 2 below 2^31), so offsets are 32-bit and past-the-end reads zero.
+  const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(Kc + bh * S * D), 0, (int)(S * D * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(Vc + bh * S * D), 0, (int)(S * D * 2), 0x00020000);
+  auto key_of = [&](int64_t blk, int uu) { return s_lo + blk * BLK + uu * KPI + j; };
+  auto load = [&](int64_t blk, u32x4 (&kk)[AT_U], u32x4 (&vv)[AT_U]) {
+#pragma unroll
+    for (int uu = 0; uu < AT_U; ++uu) {
+      const int64_t s = key_of(blk, uu);
+      const uint32_t off = s < s_hi ? (uint32_t)((s * D + 8 * c) * 2) : kAtOutOfRange;
+      kk[uu] = __builtin_amdgcn_raw_buffer_load_b128(kr, off, 0, 0);
+      vv[uu] = __builtin_amdgcn_raw_buffer_load_b128(vr, off, 0, 0);
+    }
+  };
+
+  float m = kAtNone, lsum = 0.f, o[8];
+#pragma unroll
+  for (int d = 0; d < 8; ++d) o[d] = 0.f;
+
+  auto consume = [&](int64_t blk, const u32x4 (&kk)[AT_U], const u32x4 (&vv)[AT_U]) {
+    float sc[AT_U];
+    bool ok[AT_U];
+    float mb = kAtNone;
+#pragma unroll
+    for (int uu = 0; uu < AT_U; ++uu) {
+      float dot = 0.f, ss = 0.f;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const float k0 = bf16_lo(kk[uu][d]), k1 = bf16_hi(kk[uu][d]);
+        dot += u[2 * d] * k0 + u[2 * d + 1] * k1;
+        ss += k0 * k0 + k1 * k1;
+      }
+#pragma unroll
+      for (int x = 1; x < LPK; x <<= 1) {
+        dot += __shfl_xor(dot, x);
+        ss += __shfl_xor(ss, x);
+      }
+      ok[uu] = key_of(blk, uu) < s_hi;
+      sc[uu] = dot * cq / __fsqrt_rn(__fdiv_rn(ss, (float)D) + eps);
+      if (ok[uu]) mb = fmaxf(mb, sc[uu]);
+    }
+    const float mn = fmaxf(m, mb);
+    const float alpha = __expf(m - mn);
+    lsum *= alpha;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) o[d] *= alpha;
+#pragma unroll
+    for (int uu = 0; uu < AT_U; ++uu) {
+      const float p = ok[uu] ? __expf(sc[uu] - mn) : 0.f;
+      lsum += p;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        o[2 * d] += p * bf16_lo(vv[uu][d]);
+        o[2 * d + 1] += p * bf16_hi(vv[uu][d]);
+      }
+    }
+    m = mn;
+  };
+
+  // Blocks w, w + NWV, ... of the chunk; two register stages.
+  const int64_t nblk = (s_hi - s_lo + BLK - 1) / BLK;
+  u32x4 ka[AT_U], va[AT_U], kb[AT_U], vb[AT_U];
+  load(w, ka, va);
+  load(w + NWV, kb, vb);
+  int64_t blk = w;
+  for (; blk + NWV < nblk; blk += 2 * NWV) {
+    consume(blk, ka, va);
+    load(blk + 2 * NWV, ka, va);
+    consume(blk + NWV, kb, vb);
+    load(blk + 3 * NWV, kb, vb);
+  }
+  if (blk < nblk) consume(blk, ka, va);
+
+  // Merge the lane groups of a wave (same dims, different keys).
+#pragma unroll
+  for (int x = LPK; x < 64; x <<= 1) {
+    const float mo = __shfl_xor(m, x), lo = __shfl_xor(lsum, x);
+    const float mn = fmaxf(m, mo);
+    const float a = __expf(m - mn), b = __expf(mo - mn);
+    lsum = lsum * a + lo * b;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) o[d] = o[d] * a + __shfl_xor(o[d], x) * b;
+    m = mn;
+  }
+  if (l < LPK) {
+#pragma unroll
+    for (int d = 0; d < 8; ++d) sm_o[w][8 * c + d] = o[d];
+    if (l == 0) {
+      sm_m[w] = m;
+      sm_l[w] = lsum;
+    }
+  }
+  __syncthreads();
+
+  // Thread d < D merges the waves for dim d.
+  float od = 0.f, ld = 0.f, md = kAtNone;
+  if (tid < D) {
+#pragma unroll
+    for (int ww = 0; ww < NWV; ++ww) md = fmaxf(md, sm_m[ww]);
+#pragma unroll
+    for (int ww = 0; ww < NWV; ++ww) {
+      const float a = __expf(sm_m[ww] - md);
+      od += sm_o[ww][tid] * a;
+      ld += sm_l[ww] * a;
+    }
+  }
+  if (C > 1) {
+    // Partial (o[D], max, sum) of this chunk; device-scope stores acknowledged
+    // before the arrival count, as in the split-K combine of the decode path.
+    const int64_t slot = bh * C + chunk;
+    // The plan keeps the whole partial area below 2^31 bytes.
+    const __amdgpu_buffer_rsrc_t pr =
+        __builtin_amdgcn_make_buffer_rsrc(part, 0, 0x7fffffff, 0x00020000);
+    if (tid < D)
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(od), pr,
+                                            (int)((slot * (D + 2) + tid) * 4), 0,
+                                            kAtCoherentDevice);
+    if (tid == 0) {
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(md), pr,
+                                            (int)((slot * (D + 2) + D) * 4), 0, kAtCoherentDevice);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ld), pr,
+                                            (int)((slot * (D + 2) + D + 1) * 4), 0,
+                                            kAtCoherentDevice);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0)
+      last = (__hip_atomic_fetch_add(&cnt[bh], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+              (unsigned)(C - 1));
+    __syncthreads();
+    if (!last) return;
+    if (tid < D) {
+      md = kAtNone;
+      for (int cc = 0; cc < C; ++cc) {
+        const float mc = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            pr, (int)(((bh * C + cc) * (D + 2) + D) * 4), 0, kAtCoherentDevice));
+        md = fmaxf(md, mc);
+      }
+      od = 0.f;
+      ld = 0.f;
+      for (int cc = 0; cc < C; ++cc) {
+        const int64_t base = (bh * C + cc) * (D + 2);
+        const float oc = __uint_as_float(
+            __builtin_amdgcn_raw_buffer_load_b32(pr, (int)((base + tid) * 4), 0, kAtCoherentDevice));
+        const float mc = __uint_as_float(
+            __builtin_amdgcn_raw_buffer_load_b32(pr, (int)((base + D) * 4), 0, kAtCoherentDevice));
+        const float lc = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            pr, (int)((base + D + 1) * 4), 0, kAtCoherentDevice));
+        const float a = __expf(mc - md);
+        od += oc * a;
+        ld += lc * a;
+      }
+    }
+    // All arrivals are in: reset the counter for the next call.
+    if (tid == 0) __hip_atomic_store(&cnt[bh], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (tid < D) O[bh * D + tid] = f32_to_bf16(__fdiv_rn(od, ld));
+}
+
+}  // namespace rmm
+
+static size_t at_align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Chunks: enough workgroups for ~4 per CU, at least 256 keys per chunk, a
+// whole number of 64-key rounds of the workgroup per chunk.
+void rmm_attention_plan(int64_t BH, int64_t S, int64_t D, int splits, AttnPlan* p) {
+  using namespace rmm;
+  const int64_t round = (int64_t)(AT_THREADS / 64) * AT_U * (64 / (D / 8));  // keys per WG round
+  int64_t C = splits;
+  if (C <= 0) {
+    const int64_t want = BH > 0 ? (1024 + BH - 1) / BH : 1;
+    const int64_t most = (S + 255) / 256;
+    C = want < most ? want : most;
+  }
+  if (C < 1) C = 1;
+  if (C > S) C = S;
+  int64_t kc = (S + C - 1) / C;
+  kc = (kc + round - 1) / round * round;
+  p->kchunk = kc;
+  p->chunks = (int)((S + kc - 1) / kc);
+  p->ws_cnt_off = 0;
+  p->ws_part_off = at_align256(sizeof(unsigned) * (size_t)BH);
+  p->ws_bytes = p->chunks > 1
+                    ? p->ws_part_off + at_align256(sizeof(float) * (size_t)BH * p->chunks * (D + 2))
+                    : 0;
+}
+
+hipError_t rmm_launch_attention(const AttnArgs& a, const AttnPlan& p, void* ws) {
+  using namespace rmm;
+  char* base = (char*)ws;
+  unsigned* cnt = (ws && p.chunks > 1) ? (unsigned*)(base + p.ws_cnt_off) : nullptr;
+  float* part = (ws && p.chunks > 1) ? (float*)(base + p.ws_part_off) : nullptr;
+  const dim3 grid((unsigned)(a.BH * p.chunks)), block(AT_THREADS);
+  if (a.D == 128)
+    hipLaunchKernelGGL((qknorm_attention_kernel<128>), grid, block, 0, a.stream,
+                       (const bf16_t*)a.Q, (const bf16_t*)a.K, (const bf16_t*)a.V,
+                       (const bf16_t*)a.gq, (const bf16_t*)a.gk, (bf16_t*)a.O, a.eps, a.S,
+                       p.kchunk, p.chunks, cnt, part);
+  else if (a.D == 64)
+    hipLaunchKernelGGL((qknorm_attention_kernel<64>), grid, block, 0, a.stream,
+                       (const bf16_t*)a.Q, (const bf16_t*)a.K, (const bf16_t*)a.V,
+                       (const bf16_t*)a.gq, (const bf16_t*)a.gk, (bf16_t*)a.O, a.eps, a.S,
+                       p.kchunk, p.chunks, cnt, part);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}

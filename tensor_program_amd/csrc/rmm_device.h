@@ -100,6 +100,26 @@ hipError_t rmm_launch_prefill(const RmmArgs& a, const PrefillPlan& p);
 
 hipError_t rmm_launch_stream(const RmmArgs& a);
 
+// QKNorm + attention, one query per batch-head (bf16, D = 64 or 128).
+struct AttnArgs {
+  const void* Q;   // BH x D
+  const void* K;   // BH x S x D
+  const void* V;   // BH x S x D
+  const void* gq;  // D
+  const void* gk;  // D
+  void* O;         // BH x D
+  float eps;
+  int64_t BH, S, D;
+  hipStream_t stream;
+};
+struct AttnPlan {
+  int64_t kchunk;  // keys per workgroup (a multiple of the workgroup's 64- or 128-key round)
+  int chunks;      // key chunks per batch-head, merged by the last arriving workgroup
+  size_t ws_cnt_off, ws_part_off, ws_bytes;
+};
+void rmm_attention_plan(int64_t BH, int64_t S, int64_t D, int splits, AttnPlan* p);
+hipError_t rmm_launch_attention(const AttnArgs& a, const AttnPlan& p, void* ws);
+
 // Unfused baseline, first kernel: Xn = bf16/f32(X * g / RMS) written out.
 hipError_t rmm_launch_rmsnorm(const void* X, const void* g, void* Xn, float eps, int64_t M,
                               int64_t K, bool bf16, hipStream_t stream);

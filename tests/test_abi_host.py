@@ -183,6 +183,45 @@ def test_lora_workspace_sizes(lib):
     assert lib.rmm_lora_workspace_bytes(BF16, 16, 6144, 4096, 16, 2, 1) == 0
 
 
+def test_attention_entry_points_validate(lib):
+    # qknorm_attention_ex: NULL, SHAPE, EPS, DTYPE, ALIAS, VARIANT, WORKSPACE.
+    def at(Q=A[0], K=A[1], V=A[2], gq=A[3], gk=A[4], O=A[5], eps=1e-6, BH=16, S=512, D=128,
+           dtype=BF16, splits=0, ws=None, ws_bytes=0):
+        return lib.qknorm_attention_ex(Q, K, V, gq, gk, O, eps, BH, S, D, dtype, splits, ws,
+                                       ws_bytes, None)
+    assert at(V=None) == NULL
+    assert at(gk=None, D=96) == NULL
+    assert at(D=96) == SHAPE
+    assert at(S=0) == SHAPE
+    assert at(BH=-1) == SHAPE
+    assert at(BH=1 << 40, S=1 << 20) == SHAPE          # element count overflows
+    assert at(eps=float("nan")) == EPS
+    assert at(eps=-1.0, dtype=F32) == EPS
+    assert at(dtype=F32) == DTYPE                        # bf16 only
+    assert at(O=A[1] + 256) == ALIAS                     # O inside K
+    assert at(O=A[3] - 16) == ALIAS                      # O overlapping gq
+    assert at(O=A[0] + 2) == ALIAS
+    assert at(Q=A[0] + 8) == VARIANT                     # not 16-byte aligned
+    assert at(S=1 << 23) == VARIANT                      # one head's keys need 32-bit offsets
+    assert at(splits=513) == VARIANT                     # more chunks than keys
+    assert at(splits=2) == WORKSPACE                     # forced chunks without a workspace
+    assert at(splits=2, ws=A[6], ws_bytes=16) == WORKSPACE
+    assert at(Q=None, K=None, V=None, gq=None, gk=None, O=None, BH=0) == OK
+
+
+def test_attention_plans(lib):
+    assert tpa.plan_attention(256, 2048, 128) == (0, 4, 512)    # 1024 workgroups
+    assert tpa.plan_attention(256, 2048, 128, with_workspace=False) == (0, 1, 2048)
+    assert tpa.plan_attention(16, 4096, 128, splits=3) == (0, 3, 1408)
+    assert tpa.plan_attention(4, 5, 64) == (0, 1, 128)          # chunks are whole 128-key rounds
+    assert tpa.plan_attention(1, 1, 128) == (0, 1, 64)
+    assert tpa.plan_attention(1, 100000, 64)[1] > 1
+    nb = lib.rmm_attention_workspace_bytes(BF16, 256, 2048, 128, 0)
+    assert nb == 256 * 4 + 256 * 4 * 130 * 4                  # counters, then (o, max, sum)
+    assert lib.rmm_attention_workspace_bytes(BF16, 256, 2048, 128, 1) == 0
+    assert lib.rmm_attention_workspace_bytes(F32, 256, 2048, 128, 0) == 0
+
+
 def test_empty_shapes_are_noops(lib):
     # M == 0 or N == 0: RMM_OK, nothing launched (NULL pointers allowed).
     assert call(lib, X=None, g=None, W=None, Y=None, M=0) == OK

@@ -1,0 +1,134 @@
+"""Parity of QKNorm + attention with the CPU oracle (needs an MI355X).
+
+o = softmax(norm(q) . norm(K)^T / sqrt(D)) V per batch-head (the QKNorm +
+Attention row of the Mirage paper review's benchmark table, "五、实验结果").
+
+* one-hot inputs (gains of 40, one key equal to q / 2): the softmax is
+  exactly one-hot in fp32, so the output must be that key's value row bit for
+  bit -- every key index, chunk boundary and merge is checked exactly, over
+  head dims, key counts around the kernel's 64/128-key rounds and forced
+  chunk counts;
+* random inputs within tolerance, on all outputs for small shapes and on
+  sampled batch-heads of the benchmark workload;
+* canaries around O, repeat determinism, the workspace counters reset.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import tensor_program_amd as tpa
+from tests.gpu_util import BF16_TOL
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _dev(inp, name):
+    return torch.from_numpy(np.ascontiguousarray(inp.device_array(name)).view(np.int16)).to(
+        "cuda").view(torch.bfloat16)
+
+
+def _run(inp, eps, splits=0, out=None, workspace=None):
+    o = tpa.qknorm_attention(_dev(inp, "Q"), _dev(inp, "K"), _dev(inp, "V"), _dev(inp, "gq"),
+                             _dev(inp, "gk"), eps, out=out, splits=splits, workspace=workspace)
+    torch.cuda.synchronize()
+    return o
+
+
+def _bits(t):
+    return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+ONEHOT = [
+    # (BH, S, D, splits)
+    (8, 1, 128, 0), (8, 1, 64, 0),
+    (5, 63, 128, 0), (5, 64, 128, 0), (5, 65, 128, 0),
+    (3, 127, 64, 0), (3, 128, 64, 0), (3, 129, 64, 0),
+    (16, 1000, 128, 1), (16, 1000, 128, 2), (16, 1000, 128, 3), (16, 1000, 128, 0),
+    (7, 4096, 64, 5), (7, 4096, 64, 0),
+    (4, 333, 128, 333),                     # one key per chunk
+    (256, 2048, 128, 0),                    # the benchmark shape
+]
+
+
+@pytest.mark.parametrize("case", ONEHOT, ids=lambda c: "x".join(map(str, c)))
+def test_attention_onehot_bitwise(case, require_gpu):
+    BH, S, D, splits = case
+    _log(f"attention one-hot {case}")
+    inp, pick = synth.make_attention_onehot(BH, S, D, seed=BH + S)
+    o = _run(inp, 0.0, splits=splits)
+    want = synth.to_bf16_bits(inp.V[np.arange(BH), pick])
+    got = _bits(o)
+    mism = np.argwhere(got != want)
+    assert mism.size == 0, f"{len(mism)} mismatches, first at {tuple(mism[0])}"
+
+
+def _check(o, ref, what):
+    y = o.float().cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(y)), f"{what}: non-finite outputs"
+    err = np.abs(y - ref)
+    lim = BF16_TOL * (np.abs(ref) + 1.0)
+    worst = float((err / lim).max())
+    _log(f"  worst err/tol {worst:.3f}")
+    assert worst <= 1.0, f"{what}: {(err > lim).sum()} outside tolerance, worst {worst:.3g}"
+
+
+@pytest.mark.parametrize("case", [(16, 1, 128, 0), (16, 100, 64, 0), (16, 1000, 128, 0),
+                                  (16, 1000, 128, 7), (8, 4096, 128, 0), (8, 4096, 64, 2)],
+                         ids=lambda c: "x".join(map(str, c)))
+@pytest.mark.parametrize("eps", [1e-6, 0.5])
+def test_attention_random(case, eps, require_gpu):
+    BH, S, D, splits = case
+    _log(f"attention random {case} eps {eps}")
+    inp = synth.make_attention_inputs(BH, S, D, seed=S)
+    o = _run(inp, eps, splits=splits)
+    ref = oracle.qknorm_attention(inp.Q, inp.K, inp.V, inp.gq, inp.gk, oracle.eps_as_passed(eps))
+    _check(o, ref, f"random {case}")
+
+
+def test_attention_workload_sampled(require_gpu):
+    wl = synth.get_workload("attn_bh256_s2048_d128")
+    inp = synth.make_attention_inputs(wl.BH, wl.S, wl.D)
+    o = _run(inp, wl.eps)
+    heads = np.unique(np.concatenate([[0, wl.BH - 1],
+                                      np.random.default_rng(3).choice(wl.BH, 30, replace=False)]))
+    ref = oracle.qknorm_attention(inp.Q[heads], inp.K[heads], inp.V[heads], inp.gq, inp.gk,
+                                  oracle.eps_as_passed(wl.eps))
+    _check(o[torch.from_numpy(heads).cuda()], ref, "workload")
+
+
+def test_attention_canaries_repeat_and_counters(require_gpu):
+    BH, S, D = 9, 777, 128
+    inp, pick = synth.make_attention_onehot(BH, S, D, seed=4)
+    big = torch.full((BH * D + 256,), 3.0, dtype=torch.bfloat16, device="cuda")
+    out = big[128:128 + BH * D].view(BH, D)
+    ws = tpa.Workspace(tpa._binding.attention_workspace_bytes(tpa._binding.DTYPE_BF16, BH, S, D,
+                                                              4), "cuda")
+    _run(inp, 0.0, splits=4, out=out, workspace=ws)
+    first = _bits(out).copy()
+    _run(inp, 0.0, splits=4, out=out, workspace=ws)
+    assert np.array_equal(_bits(out), first)
+    assert np.array_equal(first, synth.to_bf16_bits(inp.V[np.arange(BH), pick]))
+    guard = torch.cat([big[:128], big[128 + BH * D:]]).float()
+    assert torch.all(guard == 3.0)
+    assert torch.count_nonzero(ws.tensor[:4 * BH]) == 0  # arrival counters reset
+
+
+def test_binding_workspace_per_layout(require_gpu):
+    # Regression: with one cached workspace per stream, a call with few
+    # batch-heads left partial sums at byte 256 onward, which a later call
+    # with 256 batch-heads read as arrival counters.  Same sequence, checked.
+    small = synth.make_attention_inputs(8, 4096, 128, seed=11)
+    _run(small, 1e-6)
+    wl = synth.get_workload("attn_bh256_s2048_d128")
+    inp = synth.make_attention_inputs(wl.BH, wl.S, wl.D, seed=12)
+    o = _run(inp, wl.eps)
+    heads = np.array([0, 63, 64, 200, 255])
+    ref = oracle.qknorm_attention(inp.Q[heads], inp.K[heads], inp.V[heads], inp.gq, inp.gk,
+                                  oracle.eps_as_passed(wl.eps))
+    _check(o[torch.from_numpy(heads).cuda()], ref, "after a smaller call")

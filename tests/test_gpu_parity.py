@@ -239,3 +239,18 @@ def test_gated_stream_shapes(M, require_gpu):
     inp = synth.make_inputs(wl, seed=11)
     y = from_device(run_gpu(inp, wl.eps, variant="stream"))
     assert_within_tol(y, run_oracle(inp, wl.eps), 1e-2, "gated_stream")
+
+
+def test_binding_workspace_per_layout_decode(require_gpu):
+    # Regression: a decode call with 8 column tiles leaves its row-sum
+    # partials at byte 256 onward of the cached workspace; a later call with
+    # 72 tiles keeps its arrival counters in bytes 0..287, so it needs a
+    # workspace of its own layout.  The sequence, then exact parity.
+    first = synth.make_exact_inputs(16, 4096, 1024, "bf16", seed=2)
+    run_gpu(first, 0.0, variant="decode", splits=4)
+    inp = synth.make_exact_inputs(16, 1024, 9216, "bf16", seed=3)
+    assert tpa.plan(16, 9216, 1024, variant="decode", splits=2)[1:] == ("decode", 2)
+    y = run_gpu(inp, 0.0, variant="decode", splits=2)
+    want = expected_exact(run_oracle(inp, 0.0), "bf16")
+    mism = np.argwhere(bits_of(y) != want)
+    assert mism.size == 0, f"{len(mism)} mismatches, first at {tuple(mism[0])}"

@@ -11,9 +11,9 @@
 //
 // As in the fused RMSNorm+MatMul ("核心公式": the k-independent divisor moves
 // out of the sum), the normalised keys are never formed: each key row is read
-// once, and the same pass accumulates u . k_s and sum_d k_sd^2; the division
-// by the key's RMS is applied to the finished dot product.  u is exact in fp32
-// (a product of three bf16 values has at most 24 significant bits).
+// once, and the same pass accumulates u . k_s and sum_d k_sd^2; the key's
+// 1/RMS scales the finished dot product.  u is exact in fp32 (a product of
+// three bf16 values has at most 24 significant bits).
 //
 // Work decomposition: a workgroup (4 waves) owns one batch-head and a chunk of
 // its keys.  D/8 lanes cover one key row (16 bytes each); a wave loads 64/(D/8)
@@ -33,6 +33,20 @@ constexpr int AT_U = 4;                          // key loads per block and lane
 constexpr uint32_t kAtOutOfRange = 0x80000000u;  // past every buffer this path accepts
 constexpr int kAtCoherentDevice = 16;            // SC1: device-scope coherence
 constexpr float kAtNone = -1.0e30f;              // running max before any valid key
+
+// Sum over aligned groups of LPK (8 or 16) lanes with DPP moves: swaps
+// within quads, then the mirrored half-row and row.  Every lane of a group
+// ends with the same bits (each step adds two operands in either order),
+// which the softmax relies on: all lanes of a key see one score.
+template <int LPK>
+__device__ __forceinline__ float group_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));  // xor 1
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));  // xor 2
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true));  // half mirror
+  if (LPK == 16)
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, true));  // mirror
+  return v;
+}
 
 template <int D>
 __global__ __launch_bounds__(AT_THREADS) void qknorm_attention_kernel(
@@ -109,13 +123,11 @@ __global__ __launch_bounds__(AT_THREADS) void qknorm_attention_kernel(
         dot += u[2 * d] * k0 + u[2 * d + 1] * k1;
         ss += k0 * k0 + k1 * k1;
       }
-#pragma unroll
-      for (int x = 1; x < LPK; x <<= 1) {
-        dot += __shfl_xor(dot, x);
-        ss += __shfl_xor(ss, x);
-      }
+      dot = group_sum<LPK>(dot);
+      ss = group_sum<LPK>(ss);
       ok[uu] = key_of(blk, uu) < s_hi;
-      sc[uu] = dot * cq / __fsqrt_rn(__fdiv_rn(ss, (float)D) + eps);
+      // 1/D is a power of two (exact); v_rsq_f32 for the key's 1/RMS.
+      sc[uu] = dot * cq * __builtin_amdgcn_rsqf(ss * (1.0f / D) + eps);
       if (ok[uu]) mb = fmaxf(mb, sc[uu]);
     }
     const float mn = fmaxf(m, mb);
@@ -240,14 +252,15 @@ __global__ __launch_bounds__(AT_THREADS) void qknorm_attention_kernel(
 
 static size_t at_align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Chunks: enough workgroups for ~4 per CU, at least 256 keys per chunk, a
-// whole number of 64-key rounds of the workgroup per chunk.
+// Chunks: about one workgroup per CU (256; measured fastest: with more,
+// the combine costs more than the extra loads in flight buy), at least 256
+// keys per chunk, a whole number of the workgroup's 64- or 128-key rounds.
 void rmm_attention_plan(int64_t BH, int64_t S, int64_t D, int splits, AttnPlan* p) {
   using namespace rmm;
   const int64_t round = (int64_t)(AT_THREADS / 64) * AT_U * (64 / (D / 8));  // keys per WG round
   int64_t C = splits;
   if (C <= 0) {
-    const int64_t want = BH > 0 ? (1024 + BH - 1) / BH : 1;
+    const int64_t want = BH > 0 ? (256 + BH - 1) / BH : 1;
     const int64_t most = (S + 255) / 256;
     C = want < most ? want : most;
   }

@@ -210,13 +210,15 @@ def test_attention_entry_points_validate(lib):
 
 
 def test_attention_plans(lib):
-    assert tpa.plan_attention(256, 2048, 128) == (0, 4, 512)    # 1024 workgroups
+    assert tpa.plan_attention(256, 2048, 128) == (0, 1, 2048)   # one workgroup per CU
     assert tpa.plan_attention(256, 2048, 128, with_workspace=False) == (0, 1, 2048)
+    assert tpa.plan_attention(16, 4096, 128) == (0, 16, 256)    # 256 workgroups
     assert tpa.plan_attention(16, 4096, 128, splits=3) == (0, 3, 1408)
     assert tpa.plan_attention(4, 5, 64) == (0, 1, 128)          # chunks are whole 128-key rounds
     assert tpa.plan_attention(1, 1, 128) == (0, 1, 64)
     assert tpa.plan_attention(1, 100000, 64)[1] > 1
-    nb = lib.rmm_attention_workspace_bytes(BF16, 256, 2048, 128, 0)
+    assert lib.rmm_attention_workspace_bytes(BF16, 256, 2048, 128, 0) == 0
+    nb = lib.rmm_attention_workspace_bytes(BF16, 256, 2048, 128, 4)
     assert nb == 256 * 4 + 256 * 4 * 130 * 4                  # counters, then (o, max, sum)
     assert lib.rmm_attention_workspace_bytes(BF16, 256, 2048, 128, 1) == 0
     assert lib.rmm_attention_workspace_bytes(F32, 256, 2048, 128, 0) == 0

@@ -121,13 +121,13 @@ def test_attention_canaries_repeat_and_counters(require_gpu):
 
 def test_binding_workspace_per_layout(require_gpu):
     # Regression: with one cached workspace per stream, a call with few
-    # batch-heads left partial sums at byte 256 onward, which a later call
-    # with 256 batch-heads read as arrival counters.  Same sequence, checked.
+    # batch-heads (16 key chunks each) left partial sums at byte 256 onward,
+    # which a later call with 256 batch-heads read as arrival counters.
     small = synth.make_attention_inputs(8, 4096, 128, seed=11)
     _run(small, 1e-6)
     wl = synth.get_workload("attn_bh256_s2048_d128")
     inp = synth.make_attention_inputs(wl.BH, wl.S, wl.D, seed=12)
-    o = _run(inp, wl.eps)
+    o = _run(inp, wl.eps, splits=4)  # 4 chunks: 256 arrival counters in bytes 0..1023
     heads = np.array([0, 63, 64, 200, 255])
     ref = oracle.qknorm_attention(inp.Q[heads], inp.K[heads], inp.V[heads], inp.gq, inp.gk,
                                   oracle.eps_as_passed(wl.eps))

@@ -97,11 +97,17 @@ __device__ __forceinline__ void pf_load_a(PfA& st, i32x4 xr, i32x4 gr, int64_t m
 
 // Wait until at most N vector-memory loads are outstanding; the registers
 // of st are in/out operands, so no use of them moves above the wait.
-template <int N>
+// With the gain in LDS (GL) its register is not loaded and not tied here.
+template <int N, bool GL>
 __device__ __forceinline__ void pf_wait_a(PfA& st) {
-  asm volatile("s_waitcnt vmcnt(%5)"
-               : "+v"(st.a[0]), "+v"(st.a[1]), "+v"(st.a[2]), "+v"(st.a[3]), "+v"(st.g)
-               : "n"(N));
+  if (GL)
+    asm volatile("s_waitcnt vmcnt(%4)"
+                 : "+v"(st.a[0]), "+v"(st.a[1]), "+v"(st.a[2]), "+v"(st.a[3])
+                 : "n"(N));
+  else
+    asm volatile("s_waitcnt vmcnt(%5)"
+                 : "+v"(st.a[0]), "+v"(st.a[1]), "+v"(st.a[2]), "+v"(st.a[3]), "+v"(st.g)
+                 : "n"(N));
 }
 
 // One 16-byte-per-lane load straight into LDS: lane l's data lands at
@@ -204,22 +210,25 @@ __device__ __forceinline__ void pf_mfma(const PfFrag& f, floatx16 (&acc)[4][2]) 
   __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
 
 // One k-step: multiply the stage (a_cur, b_cur) while X of the next step
-// (st) is scaled into a_nxt.  Fragments of sub-step s+1 are read while the
-// MFMAs of sub-step s run; the staging is fenced behind the first two
-// sub-steps.
-template <int VM, bool GL>
+// (st) is scaled into a_nxt.  The fragment reads of the first two sub-steps
+// go out before `issue` (the W transfer and the X loads of later steps), so
+// the first MFMAs do not wait behind the address work of those loads.
+// Fragments of sub-step s+1 are read while the MFMAs of sub-step s run; the
+// staging is fenced behind the first two sub-steps.
+template <int VM, bool GL, typename Issue>
 __device__ __forceinline__ void pf_step(const char* a_cur, const lds_char* b_cur, char* a_nxt,
                                         PfA& st, floatx16 (&acc)[4][2], float (&ss)[4],
                                         int a_base, int b0, int b1, int tid, int norm,
-                                        const char* g_lds, int64_t k_nxt) {
+                                        const char* g_lds, int64_t k_nxt, Issue issue) {
   PfFrag fa, fb;
   pf_read_frags(fa, a_cur, b_cur, a_base, b0, b1, 0);
   pf_read_frags(fb, a_cur, b_cur, a_base, b0, b1, 1);
+  issue();
   pf_mfma(fa, acc);
   pf_read_frags(fa, a_cur, b_cur, a_base, b0, b1, 2);
   pf_mfma(fb, acc);
   __builtin_amdgcn_sched_barrier(0);
-  pf_wait_a<VM>(st);
+  pf_wait_a<VM, GL>(st);
   pf_store_a<GL>(st, a_nxt, ss, tid, 0, norm, g_lds, k_nxt);
   pf_read_frags(fb, a_cur, b_cur, a_base, b0, b1, 3);
   pf_mfma(fa, acc);
@@ -313,7 +322,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_kernel(
   pf_dma_b(b0a, dma, W1, 0, N, K, w);
   pf_load_a<GL>(sa, xr, gr, m0, 0, M, K, tid);
   pf_load_a<GL>(sb, xr, gr, m0, PF_BK, M, K, tid);
-  pf_wait_a<XL>(sa);
+  pf_wait_a<XL, GL>(sa);
   pf_store_a<GL>(sa, a_s0, ss, tid, 0, norm, g_s, 0);
   pf_store_a<GL>(sa, a_s0, ss, tid, 2, norm, g_s, 0);
   PF_WAIT_VMCNT(0);
@@ -323,16 +332,18 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_kernel(
   // zeros (every operand past K reads as zero), which leaves the sums as
   // they are and keeps the accumulators in one place.
   for (int kt = 0; kt < nk; kt += 2) {
-    pf_dma_b(b1a, dma, W1, (int64_t)(kt + 1) * PF_BK, N, K, w);
-    pf_load_a<GL>(sa, xr, gr, m0, (int64_t)(kt + 2) * PF_BK, M, K, tid);
     pf_step<XL + 4, GL>(a_s0, b0s, a_s1, sb, acc, ss, a_base, bo0, bo1, tid, norm, g_s,
-                        (int64_t)(kt + 1) * PF_BK);
+                        (int64_t)(kt + 1) * PF_BK, [&] {
+                          pf_dma_b(b1a, dma, W1, (int64_t)(kt + 1) * PF_BK, N, K, w);
+                          pf_load_a<GL>(sa, xr, gr, m0, (int64_t)(kt + 2) * PF_BK, M, K, tid);
+                        });
     PF_WAIT_VMCNT(XL);
     __syncthreads();
-    pf_dma_b(b0a, dma, W1, (int64_t)(kt + 2) * PF_BK, N, K, w);
-    pf_load_a<GL>(sb, xr, gr, m0, (int64_t)(kt + 3) * PF_BK, M, K, tid);
     pf_step<XL + 4, GL>(a_s1, b1s, a_s0, sa, acc, ss, a_base, bo0, bo1, tid, norm, g_s,
-                        (int64_t)(kt + 2) * PF_BK);
+                        (int64_t)(kt + 2) * PF_BK, [&] {
+                          pf_dma_b(b0a, dma, W1, (int64_t)(kt + 2) * PF_BK, N, K, w);
+                          pf_load_a<GL>(sb, xr, gr, m0, (int64_t)(kt + 3) * PF_BK, M, K, tid);
+                        });
     PF_WAIT_VMCNT(XL);
     __syncthreads();
   }

@@ -37,7 +37,8 @@ BF16_PEAK_TFLOPS = 2516.6      # dense bf16 MFMA, 256 CU x 4096 flop/clk x 2.4 G
 F32_VALU_PEAK_TFLOPS = 78.6    # fp32 FMA on the vector ALUs without packed math
 RIDGE = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
 ROTATE_BYTES = 1 << 30
-KERNEL_SOURCES = {"decode": "rmm_decode.hip", "generic": "rmm_generic.hip",
+KERNEL_SOURCES = {"decode": "rmm_decode.hip", "decode32": "rmm_decode32.hip",
+                  "generic": "rmm_generic.hip",
                   "prefill": "rmm_prefill.hip", "stream": "rmm_stream.hip",
                   "attention": "rmm_attn.hip"}
 
@@ -360,8 +361,10 @@ def main():
         value, unit = tflops, "TFLOP/s"
         roof = {"bound": "mfma" if wl.dtype == "bf16" else "alu", "achieved": tflops,
                 "peak": peak, "unit": "TFLOP/s", "frac": tflops / peak}
-    roof["traffic"] = stored_traffic(wl.name, variant)
-    roof["kernel"] = "qknorm_attention_kernel" if attn else f"{variant}_kernel"
+    # the fp32 decode variant is its own kernel (rmm_decode32.hip)
+    kvar = "decode32" if (variant == "decode" and wl.dtype == "f32") else variant
+    roof["traffic"] = stored_traffic(wl.name, kvar)
+    roof["kernel"] = "qknorm_attention_kernel" if attn else f"{kvar}_kernel"
     roof["algorithmic_bytes_per_launch"] = per_set
     roof["algorithmic_flops_per_launch"] = wl.flops()
 

@@ -94,11 +94,14 @@ typedef enum {
 
 /* Kernel variants.  AUTO picks by shape; the others force one (tests, bench).
  * The fast variants need bf16, K % 8 == 0, N % 8 == 0, 16-byte aligned
- * pointers, and X and each weight below 2 GiB.
+ * pointers, and X and each weight below 2 GiB (except fp32 DECODE, below).
  *   GENERIC : any shape, alignment and dtype; VALU fp32 products.
- *   DECODE  : M <= 32 (gated: M <= 16); streams W once with split-K across
- *             workgroups, bf16 matrix-core (MFMA) products, fp32 partials
- *             combined by the last-arriving workgroup.  Bandwidth-bound.
+ *   DECODE  : bf16: M <= 32 (gated: M <= 16); streams W once with split-K
+ *             across workgroups, bf16 matrix-core (MFMA) products, fp32
+ *             partials combined by the last-arriving workgroup.
+ *             fp32: M <= 16, not gated, no adapter, 16-byte aligned
+ *             pointers; the same split-K scheme with fp32 fused
+ *             multiply-adds (no bf16 rounding).  Bandwidth-bound.
  *   PREFILL : not gated; LDS-tiled MFMA GEMM with the row sum of squares
  *             fused into its k-loop.  Matrix-core-bound shapes.
  *   STREAM  : M <= 64; each workgroup streams 64-column strips of W (W1 and

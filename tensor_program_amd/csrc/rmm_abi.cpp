@@ -17,6 +17,7 @@ struct Plan {
   int splits;
   size_t ws_bytes;
   DecodePlan dec;
+  Decode32Plan d32;
   PrefillPlan pre;
 };
 
@@ -34,6 +35,7 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
 // tile does alone, and measured fastest at this size.
 constexpr int64_t kDecodeMaxM = 32;
 constexpr int64_t kDecodeMaxMGated = 16;
+constexpr int64_t kDecodeMaxMF32 = 16;  // fp32 decode: plain calls only
 constexpr int64_t kTargetWorkgroups = 256;
 // Stream: up to 64 rows; auto-selected for plain calls only when there are
 // enough 64-column strips to keep most CUs streaming.
@@ -42,6 +44,16 @@ constexpr int64_t kStreamMinTiles = 192;
 // Low-rank adapter: ranks 1..RMM_LORA_MAX_RANK; the decode kernel carries up
 // to two 16-wide rank blocks, every other shape runs the generic kernel.
 constexpr int64_t kLoraDecodeMaxRank = 32;
+
+// fp32 decode: about one workgroup per CU over 32-column tiles, each K range
+// at least 64 rows.
+int auto_decode32_splits(int64_t N, int64_t K) {
+  const int64_t tiles = (N + 31) / 32;
+  int64_t s = kTargetWorkgroups / (tiles > 0 ? tiles : 1);
+  const int64_t smax = (K + 63) / 64;
+  if (s > smax) s = smax;
+  return (int)(s < 1 ? 1 : s);
+}
 
 int auto_decode_splits(int64_t N, int64_t K) {
   const int64_t tiles = (N + 127) / 128;
@@ -72,7 +84,10 @@ rmm_status plan_shape(int64_t M, int64_t N, int64_t K, rmm_dtype dtype, int gate
   // With the adapter: 32-bit offsets into A as well (rank rows up to 32).
   const bool lora_ok = R == 0 || (R <= kLoraDecodeMaxRank && kLoraDecodeMaxRank * K * 2 <= (int64_t)INT32_MAX &&
                                   R * N * 2 <= (int64_t)INT32_MAX);
-  const bool decode_ok = fast_layout && lora_ok && M <= (gated ? kDecodeMaxMGated : kDecodeMaxM);
+  const bool f32 = dtype == RMM_DTYPE_F32;
+  const bool decode32_ok = f32 && aligned && !gated && R == 0 && M <= kDecodeMaxMF32;
+  const bool decode_ok = (fast_layout && lora_ok && M <= (gated ? kDecodeMaxMGated : kDecodeMaxM)) ||
+                         decode32_ok;
   const bool prefill_ok = fast_layout && !gated && R == 0;
   const bool stream_ok = fast_layout && M <= kStreamMaxM && R == 0;
   rmm_variant v = variant;
@@ -94,7 +109,16 @@ rmm_status plan_shape(int64_t M, int64_t N, int64_t K, rmm_dtype dtype, int gate
   out->variant = v;
   out->splits = 1;
   out->ws_bytes = 0;
-  if (v == RMM_VARIANT_DECODE) {
+  if (v == RMM_VARIANT_DECODE && f32) {
+    int s = splits;
+    if (s == 0) s = have_ws ? auto_decode32_splits(N, K) : 1;
+    if (s > (K + 63) / 64 && s > 1) return RMM_ERR_VARIANT;
+    if (s > 1 && !have_ws) return RMM_ERR_WORKSPACE;  // a forced split count needs one
+    rmm_decode32_plan(M, N, K, s, &out->d32);
+    if (out->d32.ws_bytes > (size_t)INT32_MAX) return RMM_ERR_VARIANT;  // 32-bit offsets
+    out->splits = out->d32.splits;
+    out->ws_bytes = out->d32.ws_bytes;
+  } else if (v == RMM_VARIANT_DECODE) {
     int s = splits;
     if (s == 0) s = have_ws ? auto_decode_splits(N, K) : 1;
     if (s > (K + 127) / 128) return RMM_ERR_VARIANT;
@@ -176,7 +200,10 @@ rmm_status run(const void* X, const void* g, const void* W1, const void* W3, voi
       err = rmm_launch_generic(a, dtype == RMM_DTYPE_BF16);
       break;
     case RMM_VARIANT_DECODE:
-      err = rmm_launch_decode(a, plan.dec, plan.dec.splits > 1 ? ws : nullptr);
+      if (dtype == RMM_DTYPE_F32)
+        err = rmm_launch_decode32(a, plan.d32, plan.d32.splits > 1 ? ws : nullptr);
+      else
+        err = rmm_launch_decode(a, plan.dec, plan.dec.splits > 1 ? ws : nullptr);
       break;
     case RMM_VARIANT_PREFILL:
       err = rmm_launch_prefill(a, plan.pre);

@@ -81,7 +81,8 @@ def test_validation_order(lib):
     assert call(lib, variant=4, splits=2) == VARIANT  # splits only for decode
     assert call(lib, variant=4, dtype=F32) == VARIANT  # stream is bf16 only
     assert call(lib, variant=1, splits=2) == VARIANT  # splits only for decode
-    assert call(lib, variant=2, dtype=F32) == VARIANT  # decode is bf16 only
+    assert call(lib, variant=2, dtype=F32, M=17) == VARIANT  # fp32 decode: M <= 16
+    assert call(lib, variant=2, dtype=F32, X=A[0] + 4) == VARIANT  # fp32 decode: aligned
     assert call(lib, variant=2, M=33) == VARIANT
     assert call(lib, variant=2, N=60) == VARIANT      # N % 8 != 0
     assert call(lib, variant=2, X=A[0] + 2) == VARIANT  # unaligned
@@ -256,7 +257,13 @@ def test_variant_selection():
     assert tpa.plan(48, 14336, 4096)[1] == "stream"
     assert tpa.plan(48, 2048, 4096)[1] == "prefill"   # too few 64-column strips
     assert tpa.plan(65, 4096, 4096, variant="stream")[0] == VARIANT
-    assert tpa.plan(8, 1024, 1024, dtype=torch.float32)[1] == "generic"
+    f32 = torch.float32
+    assert tpa.plan(8, 1024, 1024, dtype=f32)[1:] == ("decode", 8)   # 32 tiles x 8 = 256
+    assert tpa.plan(8, 1024, 1024, dtype=f32, with_workspace=False)[1:] == ("decode", 1)
+    assert tpa.plan(16, 64, 100, dtype=f32)[1:] == ("decode", 2)     # K ranges of >= 64 rows
+    assert tpa.plan(17, 1024, 1024, dtype=f32)[1] == "generic"
+    assert tpa.plan(8, 1024, 1024, dtype=f32, gated=True)[1] == "generic"
+    assert tpa.plan(8, 1024, 1024, dtype=f32, variant="decode", splits=5)[1:] == ("decode", 4)
     assert tpa.plan(4096, 4096, 4096)[1:] == ("prefill", 1)
     assert tpa.plan(8192, 28672, 8192)[1] == "prefill"
     assert tpa.plan(33, 520, 1000)[1] == "prefill"
@@ -275,7 +282,10 @@ def test_workspace_sizes(lib):
     assert lib.rmm_workspace_bytes(BF16, 16, 6144, 4096, 0) == \
         lib.rmm_workspace_bytes_ex(BF16, 16, 6144, 4096, 0, 0, 0) > 0
     assert lib.rmm_workspace_bytes_ex(BF16, 16, 6144, 4096, 0, 2, 1) == 0
-    assert lib.rmm_workspace_bytes(F32, 8, 1024, 1024, 0) == 0
+    # fp32 decode at 8 x 1024 x 1024: 32 tiles x 8 splits; counters (one 256-byte
+    # region), 8-row sums of squares, 8 x 32 fp32 partials per tile and split
+    assert lib.rmm_workspace_bytes(F32, 8, 1024, 1024, 0) == 256 + 8 * 32 * 8 * 4 + 8 * 32 * 8 * 32 * 4
+    assert lib.rmm_workspace_bytes(F32, 8, 1024, 1024, 1) == 0   # gated fp32: generic kernel
     assert lib.rmm_workspace_bytes(BF16, 16, 6144, 0, 0) == 0  # invalid -> 0
 
 

@@ -32,6 +32,13 @@ EXACT_CASES = [
     (5, 40, 24, "f32", "generic", 0),
     (33, 200, 136, "bf16", "generic", 0),
     (8, 1024, 1024, "f32", "generic", 0),
+    (8, 1024, 1024, "f32", "decode", 0),     # 32 tiles x 8 K ranges, split-K combine
+    (8, 1024, 1024, "f32", "decode", 1),     # one range: 4 chunks of 256 in one workgroup
+    (1, 8, 8, "f32", "decode", 0),
+    (5, 40, 24, "f32", "decode", 0),
+    (16, 1000, 520, "f32", "decode", 3),     # ragged K ranges, N % 32 != 0
+    (13, 4096, 136, "f32", "decode", 0),     # 32 ranges of 128
+    (11, 1000, 72, "f32", "decode", 1),      # multi-chunk loop with a partial last chunk
     (16, 4096, 6144, "bf16", "generic", 0),
     (16, 4096, 6144, "bf16", "decode", 1),
     (16, 4096, 6144, "bf16", "decode", 3),
@@ -94,8 +101,10 @@ def _check_workload(name, variant="auto", splits=0, rows=None, cols=None):
     _log(f"  worst err/tol {worst:.3f}")
 
 
-def test_f32_m8_k1024_n1024(require_gpu):
-    _check_workload("f32_m8_k1024_n1024")
+@pytest.mark.parametrize("variant,splits", [("auto", 0), ("generic", 0), ("decode", 1),
+                                            ("decode", 16)])
+def test_f32_m8_k1024_n1024(variant, splits, require_gpu):
+    _check_workload("f32_m8_k1024_n1024", variant, splits)
 
 
 @pytest.mark.parametrize("variant,splits", [("auto", 0), ("generic", 0), ("decode", 1),
@@ -142,7 +151,7 @@ def test_large_m8192_k8192_n28672_sampled(require_gpu):
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_gated_small(variant, splits, dtype, require_gpu):
     if dtype == "f32" and variant in ("decode", "stream"):
-        pytest.skip("decode and stream variants are bf16 only")
+        pytest.skip("the gated product in fp32 runs the generic kernel only")
     wl = synth.Workload("gated_small", dtype, 13, 520, 392, 1e-6, True, None)
     _log(f"gated small {dtype} {variant} {splits}")
     inp = synth.make_inputs(wl, seed=5)

@@ -66,7 +66,8 @@ PLAIN_CASES = [
     (16, 4096, 6144, "bf16", "decode"),
     (64, 4096, 14336, "bf16", "stream"),
     (512, 1024, 1024, "bf16", "prefill"),
-    (8, 1024, 1024, "f32", "generic"),
+    (8, 1024, 1024, "f32", "decode"),
+    (24, 1024, 1024, "f32", "generic"),
     (7, 100, 36, "bf16", "generic"),
 ]
 

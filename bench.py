@@ -37,10 +37,11 @@ BF16_PEAK_TFLOPS = 2516.6      # dense bf16 MFMA, 256 CU x 4096 flop/clk x 2.4 G
 F32_VALU_PEAK_TFLOPS = 78.6    # fp32 FMA on the vector ALUs without packed math
 RIDGE = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
 ROTATE_BYTES = 1 << 30
-KERNEL_SOURCES = {"decode": "rmm_decode.hip", "decode32": "rmm_decode32.hip",
-                  "generic": "rmm_generic.hip",
-                  "prefill": "rmm_prefill.hip", "stream": "rmm_stream.hip",
-                  "attention": "rmm_attn.hip"}
+# files each kernel is built from (their bytes, in order, make the source hash)
+KERNEL_SOURCES = {"decode": ("rmm_decode.hip", "rmm_decode_core.h"),
+                  "decode32": ("rmm_decode32.hip",), "generic": ("rmm_generic.hip",),
+                  "prefill": ("rmm_prefill.hip",), "stream": ("rmm_stream.hip",),
+                  "attention": ("rmm_attn.hip",), "chain": ("rmm_chain.hip", "rmm_decode_core.h")}
 
 
 def log(msg):
@@ -48,11 +49,17 @@ def log(msg):
 
 
 def source_hash(variant: str) -> str | None:
-    path = os.path.join(ROOT, "tensor_program_amd", "csrc", KERNEL_SOURCES.get(variant, ""))
-    if not os.path.isfile(path):
+    files = KERNEL_SOURCES.get(variant)
+    if not files:
         return None
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in files:
+        path = os.path.join(ROOT, "tensor_program_amd", "csrc", f)
+        if not os.path.isfile(path):
+            return None
+        with open(path, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def stored_traffic(workload: str, variant: str):
@@ -129,6 +136,111 @@ def cpu_baseline(wl, inp, budget_s: float):
             "seconds_full_workload": t_full}
 
 
+def bench_chain(args, name):
+    """The persistent layer chain (rmsnorm_matmul_chain) on `chain_l{L}_m{M}_k{K}`:
+    one call runs L layers x_{l+1} = RMSNorm(x_l; g_l) W_l with K x K weights.
+    Timed beside the same L layers as separate calls of the single-layer
+    kernel (decode variant), both as HIP-graph replays over rotating input
+    sets; `value` is the chain's algorithmic GB/s (every weight, gain and
+    activation byte once per layer)."""
+    import re
+    import numpy as np
+    import torch
+
+    import oracle
+    import synth
+    import tensor_program_amd as tpa
+
+    m = re.fullmatch(r"chain_l(\d+)_m(\d+)_k(\d+)", name)
+    if not m:
+        raise SystemExit(f"unknown workload {name}")
+    L, M, K = (int(v) for v in m.groups())
+    eps = 1e-6
+    dev = torch.device("cuda", 0)
+    log(f"workload {name}: generating inputs")
+    layers = [synth.make_inputs(synth.Workload(f"chain_{l}", "bf16", M, K, K, eps, False, None),
+                                seed=l) for l in range(L)]
+
+    def d(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    x0 = d(layers[0].bits["X"])
+    G = d(np.stack([lay.bits["g"] for lay in layers]))
+    W = d(np.stack([lay.bits["W1"] for lay in layers]))
+    per_set = L * (K * K + K + 2 * M * K) * 2
+    R = max(1, math.ceil(ROTATE_BYTES / (L * K * K * 2)))
+    sets = [(x0, G, W if r == 0 else W.clone(), torch.empty((L, M, K), dtype=torch.bfloat16,
+                                                            device=dev)) for r in range(R)]
+    stream = torch.cuda.Stream(dev)
+    results = {}
+    for mode in ("chain", "separate"):
+        def call(st):
+            x, g, w, xs = st
+            if mode == "chain":
+                tpa.rmsnorm_matmul_chain(x, g, w, eps, out=xs)
+            else:
+                prev = x
+                for layer in range(L):
+                    tpa.rmsnorm_matmul(prev, g[layer], w[layer], eps, out=xs[layer], variant="decode")
+                    prev = xs[layer]
+        with torch.cuda.stream(stream):
+            for st in sets:
+                call(st)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=stream):
+                for st in sets:
+                    call(st)
+            torch.cuda.synchronize()
+            t0 = time.time()
+            while time.time() - t0 < args.settle_ms / 1e3:
+                graph.replay()
+            reps_w = max(1, args.warmup // R)
+            for _ in range(reps_w):
+                graph.replay()
+            reps = max(1, args.steps // R)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            stream.synchronize()
+            e0.record(stream)
+            for _ in range(reps):
+                graph.replay()
+            e1.record(stream)
+            e1.synchronize()
+        results[mode] = (e0.elapsed_time(e1) / (reps * R), reps * R, reps_w * R)
+        log(f"{mode}: {results[mode][0] * 1e3:.1f} us per call ({results[mode][0] * 1e3 / L:.2f} "
+            f"us per layer)")
+    ms, steps, warm = results["chain"]
+    gbs = per_set / (ms * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        t0 = time.time()
+        x = layers[0].X
+        ref_layers = 0
+        for layer in range(L):
+            x = oracle.rmsnorm_matmul(x, layers[layer].g, layers[layer].W1, oracle.eps_as_passed(eps))
+            ref_layers += 1
+            if time.time() - t0 > args.cpu_budget:
+                break
+        sec = (time.time() - t0) / ref_layers
+        cpu = {"value": (per_set / L) / sec / 1e9, "unit": "GB/s", "cores": os.cpu_count(),
+               "kind": "oracle", "sample": f"{ref_layers} of {L} layers (fp64, unfused), "
+                                           f"{sec * 1e3:.1f} ms per layer"}
+    out = {"metric": METRIC, "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": steps,
+           "warmup": warm, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": name, "layers": L, "M": M, "K": K, "N": K, "eps": eps,
+                      "rotating_input_sets": R, "hip_graph": True},
+           "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "chain_kernel",
+                        "algorithmic_bytes_per_launch": per_set},
+           "cpu_baseline": cpu,
+           "separate_calls": {"ms_per_step": results["separate"][0],
+                              "chain_speedup": results["separate"][0] / ms,
+                              "note": "the same layers as L graph-captured single-layer calls"}}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -173,6 +285,8 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 10}))
         return
+    if args.workload.startswith("chain_"):
+        return bench_chain(args, args.workload)
     wl = synth.get_workload(args.workload)
     attn = isinstance(wl, synth.AttnWorkload)
     dev = torch.device("cuda", 0)

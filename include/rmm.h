@@ -240,6 +240,40 @@ rmm_status rmm_plan_attention(const void* Q, const void* K, const void* V, const
                               int64_t D, rmm_dtype dtype, int splits, const void* ws,
                               size_t ws_bytes, int* chunks_out, int64_t* keys_per_chunk_out);
 
+/* A chain of L fused layers in one persistent launch (the multi-layer
+ * decode that the Mirage pages' persistent-kernel runtime, "Mirage
+ * Persistent Kernel" on the first page, runs as one kernel):
+ *   X_{l+1} = RMSNorm(X_l; g_l, eps) W_l,   l = 0 .. L-1,
+ * each layer computed as rmsnorm_matmul computes it, the output of one
+ * layer (rounded to bf16) being the input of the next.
+ *   X0 : M x K          (layer-0 input)
+ *   G  : L x K          (g_l = row l)
+ *   W  : L x K x K      (W_l = W + l*K*K, K x K row-major: W_l[k*K + n])
+ *   Xs : L x M x K      (output: Xs + l*M*K = X_{l+1}; every layer is kept)
+ * bf16 only (else RMM_ERR_DTYPE); M <= 16, K a multiple of 128 small enough
+ * that the decode tiling of a layer fits one resident workgroup per CU
+ * (K <= 4096 on MI355X), 16-byte aligned pointers (else RMM_ERR_VARIANT).
+ * One workgroup per CU at most (RMM_ERR_HIP with hipErrorInvalidConfiguration
+ * if the device has fewer CUs than the tiling needs); every workgroup stays
+ * resident and waits on a device-side counter for the previous layer; the
+ * first W loads of a layer are issued before that wait.  The call assumes no
+ * other kernel holds CUs while it runs: a wait that gives up (bounded poll)
+ * sets the flag word below and the results are then wrong.  A workspace is
+ * required (RMM_ERR_WORKSPACE
+ * if NULL or shorter than rmm_chain_workspace_bytes); zero-fill it before
+ * first use; the kernel leaves its counters zeroed.  The 32-bit word at byte
+ * offset ws + rmm_chain_flag_offset(M, K, L) becomes nonzero if a layer
+ * wait ever gave up (a grid that was not resident); it is never cleared by
+ * the library.  Xs must not overlap X0, G, W or the workspace.  M == 0 is a
+ * no-op. */
+rmm_status rmsnorm_matmul_chain(const void* X0, const void* G, const void* W, void* Xs, float eps,
+                                int64_t M, int64_t K, int64_t L, rmm_dtype dtype, void* ws,
+                                size_t ws_bytes, hipStream_t stream);
+/* Workspace bytes of the chain call (0 for arguments it rejects). */
+size_t rmm_chain_workspace_bytes(int64_t M, int64_t K, int64_t L);
+/* Byte offset of the flag word in the chain workspace (0 for rejected arguments). */
+size_t rmm_chain_flag_offset(int64_t M, int64_t K, int64_t L);
+
 /* Workspace bytes the call with these arguments would use (0 if none).  The
  * plain entry points use variant = AUTO, splits = 0.  Returns 0 for
  * arguments that would fail validation. */

@@ -28,8 +28,8 @@ from . import _binding
 from ._binding import RmmError, load_library  # noqa: F401
 
 __all__ = ["rmsnorm_matmul", "rmsnorm_gated_mlp", "rmsnorm", "matmul", "gated_matmul",
-           "rmsnorm_lora", "lora_matmul", "qknorm_attention", "RmmError", "load_library",
-           "Workspace"]
+           "rmsnorm_lora", "lora_matmul", "qknorm_attention", "rmsnorm_matmul_chain", "RmmError",
+           "load_library", "Workspace"]
 
 _DTYPES = {torch.float32: _binding.DTYPE_F32, torch.bfloat16: _binding.DTYPE_BF16}
 
@@ -287,6 +287,42 @@ def qknorm_attention(q, k, v, gq, gk, eps: float, out=None, splits: int = 0,
         q.data_ptr(), k.data_ptr(), v.data_ptr(), gq.data_ptr(), gk.data_ptr(), out.data_ptr(),
         float(eps), BH, S, D, dtype, splits, ws_ptr, ws_bytes, stream))
     return out
+
+
+def rmsnorm_matmul_chain(x0, g, w, eps: float, out=None, workspace: Workspace | None = None):
+    """L fused layers in one persistent launch, x_{l+1} = RMSNorm(x_l; g[l], eps) @ w[l]
+    (bf16; x0: [M, K], g: [L, K], w: [L, K, K], M <= 16).  Returns every layer's
+    output, [L, M, K] (out[l] = x_{l+1})."""
+    _check_operands([x0, g, w], ["x0", "g", "w"])
+    if x0.dim() != 2 or g.dim() != 2 or w.dim() != 3:
+        raise ValueError("expected x0: [M, K], g: [L, K], w: [L, K, K]")
+    M, K = x0.shape
+    L = g.shape[0]
+    if tuple(g.shape) != (L, K) or tuple(w.shape) != (L, K, K):
+        raise ValueError(f"shape mismatch: x0 {tuple(x0.shape)}, g {tuple(g.shape)}, "
+                         f"w {tuple(w.shape)}")
+    if out is None:
+        out = torch.empty((L, M, K), dtype=x0.dtype, device=x0.device)
+    else:
+        _check_operands([x0, out], ["x0", "out"])
+        if tuple(out.shape) != (L, M, K):
+            raise ValueError(f"out has shape {tuple(out.shape)}, expected {(L, M, K)}")
+    stream = torch.cuda.current_stream(x0.device).cuda_stream
+    need = _binding.chain_workspace_bytes(M, K, L)
+    if workspace is None and need > 0:
+        workspace = _workspace_for(x0.device, stream, need, ("chain", M, K, L))
+    ws_ptr = workspace.ptr if workspace is not None else None
+    ws_bytes = workspace.nbytes if workspace is not None else 0
+    _binding.check(load_library().rmsnorm_matmul_chain(
+        x0.data_ptr(), g.data_ptr(), w.data_ptr(), out.data_ptr(), float(eps), M, K, L,
+        _DTYPES[x0.dtype], ws_ptr, ws_bytes, stream))
+    return out
+
+
+def chain_wait_flag(workspace: Workspace, M: int, K: int, L: int) -> int:
+    """The chain workspace's flag word (nonzero if a layer wait ever gave up)."""
+    off = _binding.chain_flag_offset(M, K, L)
+    return int(workspace.tensor[off:off + 4].view(torch.int32).item())
 
 
 def plan_attention(BH, S, D, splits=0, with_workspace=True):

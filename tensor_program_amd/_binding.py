@@ -23,7 +23,8 @@ SYMBOLS = ("rmsnorm_matmul", "rmsnorm_gated_mlp", "rmsnorm_matmul_ex", "rmsnorm_
            "rmm_workspace_bytes_ex", "rmm_plan", "rmm_status_string", "rmm_last_hip_error",
            "rmm_abi_version", "rmsnorm_lora", "rmsnorm_lora_ex", "rmm_lora_matmul",
            "rmm_lora_workspace_bytes", "rmm_plan_lora", "qknorm_attention",
-           "qknorm_attention_ex", "rmm_attention_workspace_bytes", "rmm_plan_attention")
+           "qknorm_attention_ex", "rmm_attention_workspace_bytes", "rmm_plan_attention",
+           "rmsnorm_matmul_chain", "rmm_chain_workspace_bytes", "rmm_chain_flag_offset")
 LORA_MAX_RANK = 64
 
 _lib = None
@@ -78,6 +79,12 @@ def load_library(path: str = LIB_PATH):
     lib.rmm_plan_attention.argtypes = [vp, vp, vp, vp, vp, vp, f32, i64, i64, i64, i32, i32, vp, sz,
                                        ctypes.POINTER(i32), ctypes.POINTER(i64)]
     lib.rmm_plan_attention.restype = i32
+    lib.rmsnorm_matmul_chain.argtypes = [vp, vp, vp, vp, f32, i64, i64, i64, i32, vp, sz, vp]
+    lib.rmsnorm_matmul_chain.restype = i32
+    lib.rmm_chain_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.rmm_chain_workspace_bytes.restype = sz
+    lib.rmm_chain_flag_offset.argtypes = [i64, i64, i64]
+    lib.rmm_chain_flag_offset.restype = sz
     lib.rmm_workspace_bytes.argtypes = [i32, i64, i64, i64, i32]
     lib.rmm_workspace_bytes.restype = sz
     lib.rmm_workspace_bytes_ex.argtypes = [i32, i64, i64, i64, i32, i32, i32]
@@ -139,6 +146,14 @@ def plan_lora(X, g, W, A, B, Y, eps, M, N, K, R, dtype, variant="auto", splits=0
     st = load_library().rmm_plan_lora(X, g, W, A, B, Y, eps, M, N, K, R, dtype, VARIANTS[variant],
                                       splits, ws, ws_bytes, ctypes.byref(v), ctypes.byref(s))
     return st, VARIANT_NAMES.get(v.value), s.value
+
+
+def chain_workspace_bytes(M: int, K: int, L: int) -> int:
+    return int(load_library().rmm_chain_workspace_bytes(M, K, L))
+
+
+def chain_flag_offset(M: int, K: int, L: int) -> int:
+    return int(load_library().rmm_chain_flag_offset(M, K, L))
 
 
 def attention_workspace_bytes(dtype: int, BH: int, S: int, D: int, splits: int = 0) -> int:

@@ -271,6 +271,33 @@ rmm_status attn_plan_call(const void* Q, const void* K, const void* V, const voi
 // fails the rank check like any other rank outside 1..64.
 int64_t lora_rank_arg(int64_t R) { return R < 0 ? 0 : R; }
 
+// Chain validation: NULL, shape, eps, dtype, alias, tiling, workspace.
+rmm_status chain_plan_call(const void* X0, const void* G, const void* W, const void* Xs, float eps,
+                           int64_t M, int64_t K, int64_t L, rmm_dtype dtype, const void* ws,
+                           size_t ws_bytes, ChainPlan* plan) {
+  if (M != 0 && (!X0 || !G || !W || !Xs)) return RMM_ERR_NULL;
+  if (M < 0 || K <= 0 || L < 1) return RMM_ERR_SHAPE;
+  int64_t mk, kk, lkk, lmk, lk, tmp;
+  if (__builtin_mul_overflow(M, K, &mk) || __builtin_mul_overflow(K, K, &kk) ||
+      __builtin_mul_overflow(L, kk, &lkk) || __builtin_mul_overflow(L, mk, &lmk) ||
+      __builtin_mul_overflow(L, K, &lk) || __builtin_mul_overflow(lkk, (int64_t)2, &tmp) ||
+      __builtin_mul_overflow(lmk, (int64_t)2, &tmp))
+    return RMM_ERR_SHAPE;
+  if (!isfinite(eps) || eps < 0.0f) return RMM_ERR_EPS;
+  if (dtype != RMM_DTYPE_BF16) return RMM_ERR_DTYPE;
+  if (M == 0) return RMM_OK;
+  const size_t xsb = (size_t)lmk * 2;
+  if (overlaps(Xs, xsb, X0, (size_t)mk * 2) || overlaps(Xs, xsb, G, (size_t)lk * 2) ||
+      overlaps(Xs, xsb, W, (size_t)lkk * 2) || overlaps(Xs, xsb, ws, ws ? ws_bytes : 0))
+    return RMM_ERR_ALIAS;
+  if (M > 16 || K % 128 != 0 || kk * 2 > (int64_t)INT32_MAX ||
+      !(aligned16(X0) && aligned16(G) && aligned16(W) && aligned16(Xs)))
+    return RMM_ERR_VARIANT;
+  if (rmm_chain_plan(M, K, L, plan) != 0) return RMM_ERR_VARIANT;  // not one workgroup per CU
+  if (!ws || ws_bytes < plan->ws_bytes) return RMM_ERR_WORKSPACE;
+  return RMM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -477,5 +504,33 @@ const char* rmm_status_string(rmm_status s) {
 int rmm_last_hip_error(void) { return g_last_hip_error; }
 
 int rmm_abi_version(void) { return RMM_ABI_VERSION; }
+
+rmm_status rmsnorm_matmul_chain(const void* X0, const void* G, const void* W, void* Xs, float eps,
+                                int64_t M, int64_t K, int64_t L, rmm_dtype dtype, void* ws,
+                                size_t ws_bytes, hipStream_t stream) {
+  ChainPlan plan;
+  const rmm_status st = chain_plan_call(X0, G, W, Xs, eps, M, K, L, dtype, ws, ws_bytes, &plan);
+  if (st != RMM_OK || M == 0) return st;
+  const hipError_t err = rmm_launch_chain(X0, G, W, Xs, eps, M, K, L, plan, ws, stream);
+  if (err != hipSuccess) {
+    g_last_hip_error = (int)err;
+    return RMM_ERR_HIP;
+  }
+  return RMM_OK;
+}
+
+size_t rmm_chain_workspace_bytes(int64_t M, int64_t K, int64_t L) {
+  if (M < 1 || M > 16 || K <= 0 || K % 128 != 0 || L < 1 || K * K * 2 > (int64_t)INT32_MAX) return 0;
+  ChainPlan plan;
+  if (rmm_chain_plan(M, K, L, &plan) != 0) return 0;
+  return plan.ws_bytes;
+}
+
+size_t rmm_chain_flag_offset(int64_t M, int64_t K, int64_t L) {
+  if (rmm_chain_workspace_bytes(M, K, L) == 0) return 0;
+  ChainPlan plan;
+  rmm_chain_plan(M, K, L, &plan);
+  return plan.ws_done_off + sizeof(unsigned);
+}
 
 }  // extern "C"

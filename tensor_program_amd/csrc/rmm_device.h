@@ -103,6 +103,19 @@ struct Decode32Plan {
 void rmm_decode32_plan(int64_t M, int64_t N, int64_t K, int splits, Decode32Plan* p);
 hipError_t rmm_launch_decode32(const RmmArgs& a, const Decode32Plan& p, void* ws);
 
+// Layer chain (persistent decode over L square layers): the decode tiling
+// with every workgroup resident (tiles * splits <= 256).
+struct ChainPlan {
+  int64_t tiles;   // 128-column tiles (N = K)
+  int splits;      // K chunks per tile
+  int64_t kchunk;  // rows per chunk (<= 1024, whole 128-row granules)
+  size_t ws_cnt_off, ws_done_off, ws_ssq_off, ws_part_off, ws_bytes;
+};
+int rmm_chain_plan(int64_t M, int64_t K, int64_t L, ChainPlan* p);  // 0, or -1 if not co-resident
+hipError_t rmm_launch_chain(const void* X0, const void* G, const void* W, void* Xs, float eps,
+                            int64_t M, int64_t K, int64_t L, const ChainPlan& p, void* ws,
+                            hipStream_t stream);
+
 struct PrefillPlan {
   int tiles_m, tiles_n;  // 256 x 256 output tiles
   int group_m;           // tile-rows walked together (L2 reuse)

@@ -289,6 +289,35 @@ def test_workspace_sizes(lib):
     assert lib.rmm_workspace_bytes(BF16, 16, 6144, 0, 0) == 0  # invalid -> 0
 
 
+def test_chain_validation_and_workspace(lib):
+    def chain(X0=A[0], G=A[1], W=A[2], Xs=A[3], eps=1e-6, M=16, K=1024, L=4, dtype=BF16,
+              ws=A[6], ws_bytes=1 << 30):
+        return lib.rmsnorm_matmul_chain(X0, G, W, Xs, eps, M, K, L, dtype, ws, ws_bytes, None)
+    assert chain(X0=None) == NULL
+    assert chain(Xs=None, K=0) == NULL            # NULL before shape
+    assert chain(K=0) == SHAPE
+    assert chain(L=0) == SHAPE
+    assert chain(M=-1) == SHAPE
+    assert chain(K=1 << 40, L=1 << 30) == SHAPE   # element count overflow
+    assert chain(eps=-1.0) == EPS
+    assert chain(dtype=F32) == DTYPE              # bf16 only
+    assert chain(Xs=A[0] + 64) == ALIAS           # output inside X0
+    assert chain(Xs=A[6] - 64) == ALIAS           # output overlapping the workspace
+    assert chain(M=17) == VARIANT
+    assert chain(K=1000) == VARIANT               # K % 128 != 0
+    assert chain(K=8192) == VARIANT               # 64 tiles x 4 chunks: not one workgroup per CU
+    assert chain(X0=A[0] + 2) == VARIANT          # unaligned
+    assert chain(ws=None) == WORKSPACE
+    need = lib.rmm_chain_workspace_bytes(16, 1024, 4)
+    assert need > 0 and chain(ws_bytes=need - 1) == WORKSPACE
+    assert chain(M=0, ws=None) == OK              # nothing to do, nothing launched
+    # 8 tiles x 8 chunks of 128: counters, done + flag words, 16-row sums, 8 x 64 floatx4 partials
+    assert need == 256 + 256 + 8 * 8 * 16 * 4 + 8 * 8 * 8 * 64 * 16
+    assert lib.rmm_chain_flag_offset(16, 1024, 4) == 256 + 4
+    assert lib.rmm_chain_workspace_bytes(16, 8192, 4) == 0
+    assert lib.rmm_chain_workspace_bytes(17, 1024, 4) == 0
+
+
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(ImportError):
         _binding.load_library(str(tmp_path / "missing.so"))

@@ -1,0 +1,90 @@
+"""Seeded random-shape sweep of every variant against the CPU oracle (needs
+an MI355X).
+
+For each drawn shape (ragged M, K and N, including K and N that are not
+multiples of 8, both storage types, plain and gated) every variant the
+planner accepts for that shape is run -- the automatic choice and each forced
+one -- and compared with the oracle within the storage type's tolerance.
+Forced variants a shape cannot take must be refused with RMM_ERR_VARIANT.
+
+Gated outputs: y = silu(z1) z3 multiplies two products that each carry the
+one bf16 rounding of X g; where a large gate meets a small linear term, that
+product can leave the elementwise bound 1e-2 (|y| + 1) although each product
+is within it (seen at 17 x 480 x 928, where the GPU value equals an exact
+emulation of the rounding bit for bit).  An element then passes if it is
+within the bound that the per-product tolerance 1e-2 (|z| + 1) gives after
+propagation through the gate, plus the bf16 rounding of y.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+import tensor_program_amd as tpa
+import oracle
+from tests.gpu_util import assert_within_tol, from_device, run_gpu, run_oracle, tol_for
+
+pytestmark = pytest.mark.gpu
+
+VARIANTS = ("auto", "generic", "decode", "prefill", "stream")
+
+
+def _gated_bound(inp, eps, tol):
+    """Per-element bound for silu(z1) z3 from the per-product bound
+    tol (|z| + 1), first and second order, plus the bf16 rounding of y."""
+    xn = oracle.rmsnorm(inp.X, inp.g, oracle.eps_as_passed(eps))
+    z1, z3 = oracle.matmul(xn, inp.W1), oracle.matmul(xn, inp.W3)
+    sig = 1.0 / (1.0 + np.exp(-z1))
+    silu, dsilu = z1 * sig, sig * (1.0 + z1 * (1.0 - sig))
+    t1, t3 = tol * (np.abs(z1) + 1.0), tol * (np.abs(z3) + 1.0)
+    y = silu * z3
+    return np.abs(dsilu * z3) * t1 + np.abs(silu) * t3 + t1 * t3 + 2.0 ** -8 * np.abs(y)
+
+
+def _check(y, ref, inp, eps, dtype, what):
+    tol = tol_for(dtype)
+    if not inp.wl.gated:
+        assert_within_tol(y, ref, tol, what)
+        return
+    assert np.all(np.isfinite(y)), f"{what}: non-finite outputs"
+    err = np.abs(y - ref)
+    lim = np.maximum(tol * (np.abs(ref) + 1.0), _gated_bound(inp, eps, tol))
+    bad = err > lim
+    assert not bad.any(), f"{what}: {bad.sum()} outside the propagated bound, worst {(err / lim).max():.3g}"
+
+
+def _shapes(seed, n):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        M = int(rng.choice([1, 2, 5, 8, 13, 16, 17, 31, 32, 40, 64, 65, 130, 257, 300]))
+        K = int(rng.integers(1, 160)) * 8 + int(rng.choice([0, 0, 0, 4]))
+        N = int(rng.integers(1, 120)) * 8 + int(rng.choice([0, 0, 0, 2]))
+        dtype = str(rng.choice(["bf16", "bf16", "f32"]))
+        gated = bool(rng.random() < 0.3)
+        out.append((M, K, N, dtype, gated))
+    return out
+
+
+CASES = _shapes(20260, 24) + _shapes(777, 16)
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "x".join(map(str, c)))
+def test_sweep(case, require_gpu):
+    M, K, N, dtype, gated = case
+    print(f"sweep {case}", flush=True)
+    wl = synth.Workload("sweep", dtype, M, K, N, 1e-6, gated, None)
+    inp = synth.make_inputs(wl, seed=M * 7 + K)
+    ref = run_oracle(inp, wl.eps)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    ran = 0
+    for variant in VARIANTS:
+        st = tpa.plan(M, N, K, dtype=tdt, gated=gated, variant=variant)[0]
+        if st != 0:
+            with pytest.raises(tpa.RmmError):
+                run_gpu(inp, wl.eps, variant=variant)
+            continue
+        y = from_device(run_gpu(inp, wl.eps, variant=variant))
+        _check(y, ref, inp, wl.eps, dtype, f"{case}/{variant}")
+        ran += 1
+    assert ran >= 2  # the automatic choice and the generic kernel at least

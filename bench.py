@@ -223,7 +223,8 @@ def bench_chain(args, name):
             if time.time() - t0 > args.cpu_budget:
                 break
         sec = (time.time() - t0) / ref_layers
-        cpu = {"value": (per_set / L) / sec / 1e9, "unit": "GB/s", "cores": os.cpu_count(),
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        cpu = {"value": (per_set / L) / sec / 1e9, "unit": "GB/s", "cores": min(threads, M),
                "kind": "oracle", "sample": f"{ref_layers} of {L} layers (fp64, unfused), "
                                            f"{sec * 1e3:.1f} ms per layer"}
     out = {"metric": METRIC, "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": steps,

@@ -17,7 +17,9 @@
 //   * W slot layout [64 k][64 n] bf16, 128-byte rows, 16-byte chunk c of row
 //     k at chunk c ^ 2(k & 3): the transposing LDS reads are conflict-free.
 //   * X slot layout [64 rows][64 k] bf16, 128-byte rows, chunk c of row r at
-//     chunk c ^ (r & 7): row-wise and fragment reads are conflict-free.
+//     chunk c ^ ((r >> 1) & 7): the 16 rows one quarter-wave reads in a
+//     fragment load fall on 16 distinct 16-byte bank groups (a plain
+//     c ^ (r & 7) puts rows r and r + 8 on the same banks).
 //   * one step ahead of its use, the workgroup turns the X slot into the
 //     matrix operand in place: each thread takes 8 consecutive k of one row,
 //     forms X*g in fp32 (bf16 dot2 with one lane of g zeroed: an exact
@@ -57,6 +59,10 @@ typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 __device__ __forceinline__ bf16x2 st_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2, v); }
+
+// X slot swizzle: physical 16-byte chunk of logical chunk c in row r is
+// c ^ st_xswz(r).  Rows 32 apart share it (fragment row blocks).
+__device__ __forceinline__ int st_xswz(int r) { return (r >> 1) & 7; }
 
 // Raw buffer resource (stride 0, 32-bit data format) for [base, base+bytes).
 __device__ __forceinline__ i32x4 st_rsrc(const void* base, uint32_t bytes) {
@@ -118,9 +124,9 @@ __global__ __launch_bounds__(ST_THREADS, 1) void stream_kernel(
     w_off = nn < N ? (uint32_t)((kl * N + nn) * 2) : kStOutOfRange;
   }
   // X: wave w fills rows 8w .. 8w+7; lane l -> row 8w + l/8, chunk
-  // (l&7) ^ (row & 7); the k-range check happens per step.
+  // (l&7) ^ st_xswz(row); the k-range check happens per step.
   const int x_row = 8 * w + (l >> 3);
-  const int x_kc = (l & 7) ^ (x_row & 7);
+  const int x_kc = (l & 7) ^ st_xswz(x_row);
   const uint32_t x_off = x_row < M ? (uint32_t)(((int64_t)x_row * K + 8 * x_kc) * 2) : kStOutOfRange;
   const uint32_t lds_w = (uint32_t)(uintptr_t)(lds_char*)&sm.w[0][0][0] + w * 1024;
   const uint32_t lds_x = (uint32_t)(uintptr_t)(lds_char*)&sm.x[0][0] + w * 1024;
@@ -148,7 +154,7 @@ __global__ __launch_bounds__(ST_THREADS, 1) void stream_kernel(
   // The X slot is overwritten in place with bf16(X * g); the row's sum of
   // squares accumulates in the thread (its row never changes).
   const int f_row = tid >> 3, f_c = tid & 7;
-  const int f_off = f_row * 128 + ((f_c ^ (f_row & 7)) << 4);
+  const int f_off = f_row * 128 + ((f_c ^ st_xswz(f_row)) << 4);
   float ss = 0.f;
   auto form = [&](int step) {
     const int slot = step % RING;
@@ -208,7 +214,7 @@ __global__ __launch_bounds__(ST_THREADS, 1) void stream_kernel(
       const int kc = 2 * s + (l >> 5);
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
-        av[i][rb] = *(const u32x4*)(x_lds + (rb * 32 + a_lo) * 128 + ((kc ^ (a_lo & 7)) << 4));
+        av[i][rb] = *(const u32x4*)(x_lds + (rb * 32 + a_lo) * 128 + ((kc ^ st_xswz(a_lo)) << 4));
       const u32x2 lo = __builtin_bit_cast(
           u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(b_lds + b_off + 16 * s * 128)));
       const u32x2 hi = __builtin_bit_cast(

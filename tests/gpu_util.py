@@ -71,6 +71,33 @@ def assert_within_tol(y_gpu: np.ndarray, y_ref: np.ndarray, tol: float, what: st
     return float((err / lim).max()) if err.size else 0.0
 
 
+def gated_bound(inp: "synth.Inputs", eps: float, tol: float) -> np.ndarray:
+    """Per-element bound for y = silu(z1) z3 from the per-product bound
+    tol (|z| + 1) on z1 and z3, first and second order, plus the bf16 rounding
+    of y.  The gate multiplies the two products' errors by the other factor,
+    so an element of y can be off by more than tol (|y| + 1) while both
+    products are within their bound."""
+    xn = oracle.rmsnorm(inp.X, inp.g, oracle.eps_as_passed(eps))
+    z1, z3 = oracle.matmul(xn, inp.W1), oracle.matmul(xn, inp.W3)
+    sig = 1.0 / (1.0 + np.exp(-z1))
+    silu, dsilu = z1 * sig, sig * (1.0 + z1 * (1.0 - sig))
+    t1, t3 = tol * (np.abs(z1) + 1.0), tol * (np.abs(z3) + 1.0)
+    y = silu * z3
+    return np.abs(dsilu * z3) * t1 + np.abs(silu) * t3 + t1 * t3 + 2.0 ** -8 * np.abs(y)
+
+
+def assert_gated_within_bound(y_gpu: np.ndarray, y_ref: np.ndarray, inp: "synth.Inputs",
+                              eps: float, tol: float, what: str = ""):
+    """Gated outputs: within tol (|y| + 1) or within gated_bound."""
+    assert y_gpu.shape == y_ref.shape, (y_gpu.shape, y_ref.shape)
+    assert np.all(np.isfinite(y_gpu)), f"{what}: non-finite outputs"
+    err = np.abs(y_gpu - y_ref)
+    lim = np.maximum(tol * (np.abs(y_ref) + 1.0), gated_bound(inp, eps, tol))
+    bad = err > lim
+    assert not bad.any(), (f"{what}: {bad.sum()} outside the propagated bound, "
+                           f"worst {(err / lim).max():.3g}")
+
+
 def expected_exact(y_ref: np.ndarray, dtype: str) -> np.ndarray:
     """For exact-arithmetic inputs the oracle's result is exact; the stored
     output is its one rounding to the storage type (nearest even)."""

@@ -15,8 +15,8 @@ import torch
 
 import synth
 import tensor_program_amd as tpa
-from tests.gpu_util import (assert_within_tol, bits_of, expected_exact, from_device, run_gpu,
-                            run_oracle, to_device, tol_for)
+from tests.gpu_util import (assert_gated_within_bound, assert_within_tol, bits_of, expected_exact,
+                            from_device, run_gpu, run_oracle, to_device, tol_for)
 
 pytestmark = pytest.mark.gpu
 
@@ -62,6 +62,13 @@ EXACT_CASES = [
     (33, 1000, 520, "bf16", "stream", 0),
     (1, 8, 8, "bf16", "stream", 0),
     (64, 136, 4104, "bf16", "stream", 0),
+    # stream at wide N: 256 strips (one per CU), 257 (a second round with an
+    # 8-column last strip), 219 and 96 strips with 48- and 56-column last
+    # strips
+    (16, 136, 16384, "bf16", "stream", 0),
+    (8, 200, 16392, "bf16", "stream", 0),
+    (20, 264, 14000, "bf16", "stream", 0),
+    (16, 520, 6136, "bf16", "stream", 0),
 ]
 
 EXACT_SAMPLE_ROWS = 48  # above ~1e10 multiply-adds the oracle checks sampled rows
@@ -248,6 +255,20 @@ def test_gated_stream_shapes(M, require_gpu):
     inp = synth.make_inputs(wl, seed=11)
     y = from_device(run_gpu(inp, wl.eps, variant="stream"))
     assert_within_tol(y, run_oracle(inp, wl.eps), 1e-2, "gated_stream")
+
+
+@pytest.mark.parametrize("M,K,N", [(64, 264, 16392), (48, 264, 14336), (64, 136, 6136)])
+def test_gated_stream_wide(M, K, N, require_gpu):
+    """Gated stream variant at wide N (257 strips with an 8-column last one,
+    224 strips, 96 strips with a 56-column last one), against the oracle.
+    Over a million outputs
+    at a short K, a few meet a large gate with a small linear term: they are
+    held to the bound the per-product tolerance gives through the gate."""
+    wl = synth.Workload("gated_stream", "bf16", M, K, N, 1e-6, True, None)
+    _log(f"gated stream wide M={M} K={K} N={N}")
+    inp = synth.make_inputs(wl, seed=12)
+    y = from_device(run_gpu(inp, wl.eps, variant="stream"))
+    assert_gated_within_bound(y, run_oracle(inp, wl.eps), inp, wl.eps, 1e-2, "gated_stream_wide")
 
 
 def test_binding_workspace_per_layout_decode(require_gpu):

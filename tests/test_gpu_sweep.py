@@ -21,24 +21,12 @@ import torch
 
 import synth
 import tensor_program_amd as tpa
-import oracle
-from tests.gpu_util import assert_within_tol, from_device, run_gpu, run_oracle, tol_for
+from tests.gpu_util import (assert_gated_within_bound, assert_within_tol, from_device, run_gpu,
+                            run_oracle, tol_for)
 
 pytestmark = pytest.mark.gpu
 
 VARIANTS = ("auto", "generic", "decode", "prefill", "stream")
-
-
-def _gated_bound(inp, eps, tol):
-    """Per-element bound for silu(z1) z3 from the per-product bound
-    tol (|z| + 1), first and second order, plus the bf16 rounding of y."""
-    xn = oracle.rmsnorm(inp.X, inp.g, oracle.eps_as_passed(eps))
-    z1, z3 = oracle.matmul(xn, inp.W1), oracle.matmul(xn, inp.W3)
-    sig = 1.0 / (1.0 + np.exp(-z1))
-    silu, dsilu = z1 * sig, sig * (1.0 + z1 * (1.0 - sig))
-    t1, t3 = tol * (np.abs(z1) + 1.0), tol * (np.abs(z3) + 1.0)
-    y = silu * z3
-    return np.abs(dsilu * z3) * t1 + np.abs(silu) * t3 + t1 * t3 + 2.0 ** -8 * np.abs(y)
 
 
 def _check(y, ref, inp, eps, dtype, what):
@@ -46,11 +34,7 @@ def _check(y, ref, inp, eps, dtype, what):
     if not inp.wl.gated:
         assert_within_tol(y, ref, tol, what)
         return
-    assert np.all(np.isfinite(y)), f"{what}: non-finite outputs"
-    err = np.abs(y - ref)
-    lim = np.maximum(tol * (np.abs(ref) + 1.0), _gated_bound(inp, eps, tol))
-    bad = err > lim
-    assert not bad.any(), f"{what}: {bad.sum()} outside the propagated bound, worst {(err / lim).max():.3g}"
+    assert_gated_within_bound(y, ref, inp, eps, tol, what)
 
 
 def _shapes(seed, n):

@@ -222,11 +222,12 @@ __global__ __launch_bounds__(CH_NT) void chain_kernel(
         if (tid == 0) __hip_atomic_store(&cnt[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
-    if (layer + 1 < L) {
+    auto prefetch_next = [&] {
       const DecodeSrc nsrc = sources(layer + 1);
       decode_load<1>(wa, nsrc, N, k_lo + 32 * w + 8 * q, k_hi, col, col_ok);
       decode_load<1>(wb, nsrc, N, k_lo + STEP + 32 * w + 8 * q, k_hi, col, col_ok);
-    }
+    };
+    if (layer + 1 < L && !last) prefetch_next();
     if (last) {
       __syncthreads();  // every thread is done reading sm.red
       red0[tid] = v;
@@ -251,9 +252,17 @@ __global__ __launch_bounds__(CH_NT) void chain_kernel(
           __builtin_amdgcn_raw_buffer_store_b128(out, yrs, (int)((row * K + cc) * 2), 0, kCoherentDevice);
         }
       }
-      // The tile is visible device-wide before it is counted as done.
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+      // The tile is visible device-wide before it is counted as done.  The
+      // next layer's first W loads go out behind the tile's stores; vector
+      // memory operations complete in issue order, so waiting until only
+      // those 16 loads may be outstanding waits for the stores alone.
+      if (layer + 1 < L) {
+        prefetch_next();
+        __builtin_amdgcn_s_waitcnt(0x0 | (7 << 4) | (15 << 8) | (1 << 14));  // vmcnt(16)
+      } else {
+        __builtin_amdgcn_s_waitcnt(0);
+      }
+      __builtin_amdgcn_s_barrier();
       if (tid == 0) {
         const unsigned prev =
             __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

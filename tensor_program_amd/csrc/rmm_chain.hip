@@ -7,9 +7,11 @@
 // kernel: instead of one launch per layer, every workgroup stays resident
 // and moves from layer to layer, waiting on a device-side counter for the
 // layer before to finish.  The weights do not depend on the activations, so
-// each workgroup issues the first W loads of its next layer before it waits;
-// the W stream of layer l+1 overlaps the tail (split-K combine, epilogue) of
-// layer l that a chain of separate launches would expose.
+// each workgroup issues half of its next layer's W loads before it waits
+// (the other half behind that layer's X loads, once the wait is over): the
+// W stream of layer l+1 overlaps the tail (split-K combine, epilogue) of
+// layer l that a chain of separate launches would expose, without flooding
+// the memory system while that latency-bound combine runs.
 //
 // Per layer the work is the decode kernel's: a workgroup (8 waves) owns a
 // 128-column tile and a K chunk of at most 1024 rows (one staged segment),
@@ -93,10 +95,13 @@ __global__ __launch_bounds__(CH_NT) void chain_kernel(
     src.g = __builtin_amdgcn_make_buffer_rsrc((void*)(G + (int64_t)layer * K), 0, (int)(K * 2), 0x00020000);
     return src;
   };
-  // The first two W stages of a layer do not depend on its input: every
-  // workgroup issues them as soon as its part of the layer before is counted
-  // (before any combine work it then does, and before it waits), so the
-  // workgroups that combine tiles do not start the next layer behind.
+  // The W stages of a layer do not depend on its input.  Every workgroup
+  // issues the first one as soon as its part of the layer before is counted
+  // (a combining workgroup: right behind its tile stores), and the second
+  // after the wait, behind the layer's X loads.  Issuing both before the
+  // wait was slower (8 layers of 4096 x 4096: 110.1 vs 103.1 us): 33 MB of
+  // W requests in flight queue the latency-bound combine, count and reload
+  // of x behind them.
   u32x4 wa[1][8], wb[1][8];
   {
     const DecodeSrc src0 = sources(0);
@@ -137,6 +142,7 @@ __global__ __launch_bounds__(CH_NT) void chain_kernel(
             kCoherentDevice);
         gs[u] = __builtin_amdgcn_raw_buffer_load_b128(src.g, ok ? (uint32_t)(k * 2) : kOutOfRange, 0, 0);
       }
+      if (layer > 0) decode_load<1>(wb, src, N, k_lo + STEP + 32 * w + 8 * q, k_hi, col, col_ok);
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
         u32x4 av;
@@ -225,7 +231,6 @@ __global__ __launch_bounds__(CH_NT) void chain_kernel(
     auto prefetch_next = [&] {
       const DecodeSrc nsrc = sources(layer + 1);
       decode_load<1>(wa, nsrc, N, k_lo + 32 * w + 8 * q, k_hi, col, col_ok);
-      decode_load<1>(wb, nsrc, N, k_lo + STEP + 32 * w + 8 * q, k_hi, col, col_ok);
     };
     if (layer + 1 < L && !last) prefetch_next();
     if (last) {
@@ -255,10 +260,10 @@ __global__ __launch_bounds__(CH_NT) void chain_kernel(
       // The tile is visible device-wide before it is counted as done.  The
       // next layer's first W loads go out behind the tile's stores; vector
       // memory operations complete in issue order, so waiting until only
-      // those 16 loads may be outstanding waits for the stores alone.
+      // those 8 loads may be outstanding waits for the stores alone.
       if (layer + 1 < L) {
         prefetch_next();
-        __builtin_amdgcn_s_waitcnt(0x0 | (7 << 4) | (15 << 8) | (1 << 14));  // vmcnt(16)
+        __builtin_amdgcn_s_waitcnt(0x8 | (7 << 4) | (15 << 8));  // vmcnt(8)
       } else {
         __builtin_amdgcn_s_waitcnt(0);
       }

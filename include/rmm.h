@@ -255,8 +255,9 @@ rmm_status rmm_plan_attention(const void* Q, const void* K, const void* V, const
  * (K <= 4096 on MI355X), 16-byte aligned pointers (else RMM_ERR_VARIANT).
  * One workgroup per CU at most (RMM_ERR_HIP with hipErrorInvalidConfiguration
  * if the device has fewer CUs than the tiling needs); every workgroup stays
- * resident and waits on a device-side counter for the previous layer; the
- * first W loads of a layer are issued before that wait.  The call assumes no
+ * resident and, before a layer, waits on device-side per-tile counters for
+ * the tiles of the previous layer's output that its K chunk reads; half of
+ * a layer's W loads are issued before that wait.  The call assumes no
  * other kernel holds CUs while it runs: a wait that gives up (bounded poll)
  * sets the flag word below and the results are then wrong.  A workspace is
  * required (RMM_ERR_WORKSPACE

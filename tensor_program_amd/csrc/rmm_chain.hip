@@ -22,7 +22,9 @@
 // E(O) = sum(k, div(mul(I1,I2), I3)) of the paper review's "核心公式", with
 // the k-independent divisor moved outside the sum).  That workgroup writes
 // the tile of X_{l+1} with device-coherent stores and then counts the tile
-// as done; a layer is finished when tiles * (l+1) tiles are done.
+// as done (a per-tile count of finished layers).  A workgroup starts layer
+// l+1 once the tiles of X_{l+1} its K chunk reads (kchunk / 128 of them)
+// have finished layer l: it never waits on tiles it does not read.
 //
 // The grid has at most one workgroup per CU (the launcher checks the
 // device's CU count) and each workgroup needs a whole CU's LDS share, so on
@@ -49,6 +51,7 @@ struct ChainSmem {
   float ssr[16];
   float inv[16];
   int last;
+  int reset;
 };
 
 __global__ __launch_bounds__(CH_NT) void chain_kernel(
@@ -59,6 +62,10 @@ __global__ __launch_bounds__(CH_NT) void chain_kernel(
   constexpr int ROWS = 16, STEP = 32 * CH_WV, TPR = CH_NT / ROWS, NU = CH_SEG / 8 / TPR;
   __shared__ ChainSmem sm;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, q = l >> 4, p = l & 15;
+  // Per-tile counts of finished layers follow the call-wide count and the
+  // flag word.
+  unsigned* done_t = done + 2;
+  if (tid == 0) sm.reset = 0;
   int tile, split;
   {
     const int bid = blockIdx.x;
@@ -114,10 +121,14 @@ __global__ __launch_bounds__(CH_NT) void chain_kernel(
     const DecodeSrc src = sources(layer);
 
     if (layer > 0) {
-      if (tid == 0) {
-        const unsigned target = (unsigned)tiles * (unsigned)layer;
+      // Thread j polls the count of tile j0 + j of X_l (columns k_lo ..
+      // k_hi of the layer before's output).
+      const int j0 = (int)(k_lo / DEC_COLS), nj = (int)((k_hi - k_lo + DEC_COLS - 1) / DEC_COLS);
+      if (tid < nj) {
         for (int it = 0;; ++it) {
-          if (__hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) break;
+          if (__hip_atomic_load(&done_t[j0 + tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >=
+              (unsigned)layer)
+            break;
           if (it >= kChainSpinMax) {
             __hip_atomic_store(flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             break;
@@ -269,15 +280,32 @@ __global__ __launch_bounds__(CH_NT) void chain_kernel(
       }
       __builtin_amdgcn_s_barrier();
       if (tid == 0) {
+        __hip_atomic_fetch_add(&done_t[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const unsigned prev =
             __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        // Every tile of the last layer done: no workgroup waits any more, so
-        // the counter can be cleared for the next call.
-        if (prev + 1 == (unsigned)tiles * (unsigned)L)
-          __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // Every tile of every layer counted: every workgroup has passed its
+        // last wait, so this workgroup clears the counts for the next call.
+        if (prev + 1 == (unsigned)tiles * (unsigned)L) sm.reset = 1;
       }
     }
     __syncthreads();  // LDS is reused by the next layer
+  }
+  if (sm.reset) {
+    // A tile count may still be on its way (it is a separate atomic from the
+    // call-wide one): wait until it reads L before clearing it.
+    for (int j = tid; j < tiles; j += CH_NT) {
+      for (int it = 0;; ++it) {
+        if (__hip_atomic_load(&done_t[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= (unsigned)L)
+          break;
+        if (it >= kChainSpinMax) {
+          __hip_atomic_store(flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      __hip_atomic_store(&done_t[j], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (tid == 0) __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -303,6 +331,9 @@ int rmm_chain_plan(int64_t M, int64_t K, int64_t L, ChainPlan* p) {
   p->ws_ssq_off = p->ws_done_off + 256;
   p->ws_part_off = p->ws_ssq_off + chain_align256(sizeof(float) * (size_t)p->splits * p->tiles * 16);
   p->ws_bytes = p->ws_part_off + chain_align256((size_t)p->splits * p->tiles * 8 * 64 * 16);
+  // The 256-byte counter block holds the call-wide count, the flag and one
+  // count per tile.
+  if (4 * (2 + p->tiles) > 256) return -1;
   return p->tiles * p->splits <= 256 ? 0 : -1;
 }
 

@@ -316,6 +316,12 @@ def test_chain_validation_and_workspace(lib):
     assert lib.rmm_chain_flag_offset(16, 1024, 4) == 256 + 4
     assert lib.rmm_chain_workspace_bytes(16, 8192, 4) == 0
     assert lib.rmm_chain_workspace_bytes(17, 1024, 4) == 0
+    # The largest accepted tiling, K = 4480: 35 tiles x 7 chunks of 640.  The
+    # 256-byte counter block (call-wide count, flag, one count per tile) holds
+    # 2 + 35 words.
+    need = lib.rmm_chain_workspace_bytes(16, 4480, 2)
+    assert need == 256 + 256 + 15872 + 7 * 35 * 8 * 64 * 16  # row sums: 15,680 bytes, 256-aligned
+    assert lib.rmm_chain_workspace_bytes(16, 4608, 2) == 0  # 36 tiles need 8 chunks: 288 workgroups
 
 
 def test_binding_fails_loudly_without_library(tmp_path):

@@ -40,8 +40,15 @@ def _as64(t):
     return t.float().cpu().numpy().astype(np.float64)
 
 
-@pytest.mark.parametrize("M,K,L", [(16, 4096, 4), (5, 1024, 3), (1, 128, 2), (16, 1024, 1)])
-def test_chain_layers(M, K, L, require_gpu):
+# (M, K, L, split count of the single-layer reference call: 0 = the
+# automatic one, which equals the chain's at these shapes).  K = 4480 is the
+# largest tiling the chain accepts: 35 tiles x 7 chunks of 640 rows (five
+# tiles of the layer before per chunk, an odd number of 256-row steps), where
+# the automatic decode split count (4) differs from the chain's, so the
+# reference call is given 7.
+@pytest.mark.parametrize("M,K,L,splits", [(16, 4096, 4, 0), (5, 1024, 3, 0), (1, 128, 2, 0),
+                                          (16, 1024, 1, 0), (16, 4480, 3, 7)])
+def test_chain_layers(M, K, L, splits, require_gpu):
     _log(f"chain M={M} K={K} L={L}")
     x0, G, W, layers = _chain_inputs(M, K, L)
     ws = tpa.Workspace(tpa._binding.chain_workspace_bytes(M, K, L), "cuda")
@@ -50,7 +57,7 @@ def test_chain_layers(M, K, L, require_gpu):
     assert tpa.chain_wait_flag(ws, M, K, L) == 0
     prev = x0
     for layer in range(L):
-        want = tpa.rmsnorm_matmul(prev, G[layer], W[layer], 1e-6, variant="decode")
+        want = tpa.rmsnorm_matmul(prev, G[layer], W[layer], 1e-6, variant="decode", splits=splits)
         torch.cuda.synchronize()
         got = xs[layer]
         diff = (got.view(torch.int16) != want.view(torch.int16)).sum().item()

@@ -41,7 +41,7 @@ constexpr int ST_BM = 64;                        // rows (M <= 64)
 constexpr int ST_BK = 64;                        // k per step
 constexpr int ST_W_BYTES = ST_BK * ST_BN * 2;    // 8 KB per weight per slot
 constexpr int ST_X_BYTES = ST_BM * ST_BK * 2;    // 8 KB per slot
-constexpr int ST_G_BYTES = 8 * 128;              // one 128-byte copy of g per wave
+constexpr int ST_G_BYTES = 128;                  // the g slice of a step
 constexpr uint32_t kStOutOfRange = 0x80000000u;
 
 // Ring depth per weight count: enough bytes in flight per CU, within 160 KB.
@@ -130,11 +130,13 @@ __global__ __launch_bounds__(ST_THREADS, 1) void stream_kernel(
   const uint32_t x_off = x_row < M ? (uint32_t)(((int64_t)x_row * K + 8 * x_kc) * 2) : kStOutOfRange;
   const uint32_t lds_w = (uint32_t)(uintptr_t)(lds_char*)&sm.w[0][0][0] + w * 1024;
   const uint32_t lds_x = (uint32_t)(uintptr_t)(lds_char*)&sm.x[0][0] + w * 1024;
-  const uint32_t lds_g = (uint32_t)(uintptr_t)(lds_char*)&sm.g[0][0] + w * 128;
+  const uint32_t lds_g = (uint32_t)(uintptr_t)(lds_char*)&sm.g[0][0];
   const bf16_t* Wp[2] = {W1, NW == 2 ? W3 : W1};
 
-  // Issue every transfer of one step: NW W blocks, one X block, one g slice
-  // (lanes 0..7 only) -- NW + 2 vector-memory instructions per wave.
+  // Issue every transfer of one step: NW W blocks, one X block and, from
+  // lanes 0..7 of wave 0 only, the step's g slice (every wave reads it after
+  // the barrier) -- NW + 1 vector-memory instructions per wave, NW + 2 for
+  // wave 0.
   auto issue_step = [&](int step) {
     const int64_t k0 = (int64_t)step * ST_BK;
     const int64_t rows = K - k0 > 0 ? K - k0 : 0;
@@ -147,7 +149,7 @@ __global__ __launch_bounds__(ST_THREADS, 1) void stream_kernel(
     const i32x4 xs = st_rsrc(X + k0, (uint32_t)(((int64_t)M * K - (k0 < (int64_t)M * K ? k0 : 0)) * 2));
     st_lds_load16(lds_x + (uint32_t)(slot * ST_X_BYTES), k0 + 8 * x_kc < K ? x_off : kStOutOfRange, xs);
     const i32x4 gs = st_rsrc(g + k0, (uint32_t)(rows * 2));
-    if (l < 8) st_lds_load16(lds_g + (uint32_t)(slot * ST_G_BYTES), (uint32_t)(16 * l), gs);
+    if (w == 0 && l < 8) st_lds_load16(lds_g + (uint32_t)(slot * ST_G_BYTES), (uint32_t)(16 * l), gs);
   };
 
   // Operand forming: thread -> row tid/8, logical k-chunk tid%8 of a step.
@@ -160,7 +162,7 @@ __global__ __launch_bounds__(ST_THREADS, 1) void stream_kernel(
     const int slot = step % RING;
     char* xp = &sm.x[slot][f_off];
     const u32x4 xv = *(const u32x4*)xp;
-    const u32x4 gl = *(const u32x4*)&sm.g[slot][w * 128 + 16 * f_c];
+    const u32x4 gl = *(const u32x4*)&sm.g[slot][16 * f_c];
     const u32x4 gv = norm ? gl : u32x4{kBf16OnePair, kBf16OnePair, kBf16OnePair, kBf16OnePair};
     u32x4 av;
 #pragma unroll
@@ -196,13 +198,20 @@ __global__ __launch_bounds__(ST_THREADS, 1) void stream_kernel(
   // iteration kt-1 is finished everywhere) it reads the operands of step kt
   // (formed in iteration kt-1), forms step kt+1 and multiplies step kt.
   // Steps past the last one read zeros (range checks).
+  // Wait until this wave's part of the step AHEAD-1 issues back has landed.
+  auto wait_landed = [&] {
+    if (w == 0)
+      ST_WAIT_VMCNT((AHEAD - 1) * (NW + 2));
+    else
+      ST_WAIT_VMCNT((AHEAD - 1) * (NW + 1));
+  };
   for (int st = 0; st < AHEAD; ++st) issue_step(st);
-  ST_WAIT_VMCNT((AHEAD - 1) * (NW + 2));
+  wait_landed();
   __syncthreads();
   form(0);
   for (int kt = 0; kt < nk; ++kt) {
     issue_step(kt + AHEAD);
-    ST_WAIT_VMCNT((AHEAD - 1) * (NW + 2));
+    wait_landed();
     __syncthreads();
     const int slot = kt % RING;
     const char* x_lds = &sm.x[slot][0];

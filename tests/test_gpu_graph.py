@@ -1,4 +1,4 @@
-"""HIP-graph replay of the split-K calls (needs an MI355X).
+"""HIP-graph replay of every kernel variant (needs an MI355X).
 
 The benchmark replays captured calls; the split-K combines rely on arrival
 counters that each call resets itself (no memset is captured).  Each graph
@@ -83,3 +83,39 @@ def test_graph_lora_and_attention(require_gpu):
     call = lambda out: tpa.qknorm_attention(dv["Q"], dv["K"], dv["V"], dv["gq"], dv["gk"], 1e-6,
                                             out=out, splits=5, workspace=aws)
     _replays(lambda: call(o), o, lambda: call(None))
+
+
+def test_graph_stream_prefill_and_chain(require_gpu):
+    """The other variants under replay: the gated stream kernel, the prefill
+    tile, and the persistent layer chain (its layer counters are cleared by
+    the kernel itself, so a replay must find them as an eager call does)."""
+    wl = synth.Workload("graph_gated", "bf16", 64, 1024, 2048, 1e-6, True, None)
+    inp = synth.make_inputs(wl, seed=21)
+    x, g = to_device(inp, "X"), to_device(inp, "g")
+    w1, w3 = to_device(inp, "W1"), to_device(inp, "W3")
+    out = torch.empty((wl.M, wl.N), dtype=torch.bfloat16, device="cuda")
+    _replays(lambda: tpa.rmsnorm_gated_mlp(x, g, w1, w3, wl.eps, out=out, variant="stream"), out,
+             lambda: tpa.rmsnorm_gated_mlp(x, g, w1, w3, wl.eps, variant="stream"))
+
+    wl = synth.Workload("graph_prefill", "bf16", 520, 512, 1032, 1e-6, False, None)
+    inp = synth.make_inputs(wl, seed=22)
+    x, g, w = to_device(inp, "X"), to_device(inp, "g"), to_device(inp, "W1")
+    out = torch.empty((wl.M, wl.N), dtype=torch.bfloat16, device="cuda")
+    _replays(lambda: tpa.rmsnorm_matmul(x, g, w, wl.eps, out=out, variant="prefill"), out,
+             lambda: tpa.rmsnorm_matmul(x, g, w, wl.eps, variant="prefill"))
+
+    M, K, L = 16, 1024, 3
+    layers = [synth.make_inputs(synth.Workload(f"graph_chain_{l}", "bf16", M, K, K, 1e-6, False,
+                                               None), seed=30 + l) for l in range(L)]
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+    x0 = dev(layers[0].bits["X"])
+    G = dev(np.stack([lay.bits["g"] for lay in layers]))
+    W = dev(np.stack([lay.bits["W1"] for lay in layers]))
+    xs = torch.empty((L, M, K), dtype=torch.bfloat16, device="cuda")
+    ws = tpa.Workspace(tpa._binding.chain_workspace_bytes(M, K, L), "cuda")
+    _replays(lambda: tpa.rmsnorm_matmul_chain(x0, G, W, 1e-6, out=xs, workspace=ws), xs,
+             lambda: tpa.rmsnorm_matmul_chain(x0, G, W, 1e-6, workspace=ws))
+    assert tpa.chain_wait_flag(ws, M, K, L) == 0

@@ -19,6 +19,7 @@ struct Plan {
   DecodePlan dec;
   Decode32Plan d32;
   PrefillPlan pre;
+  StreamPlan st;
 };
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -129,6 +130,10 @@ rmm_status plan_shape(int64_t M, int64_t N, int64_t K, rmm_dtype dtype, int gate
     out->ws_bytes = out->dec.ws_bytes;
   } else if (v == RMM_VARIANT_PREFILL) {
     rmm_prefill_plan(M, N, K, &out->pre);
+  } else if (v == RMM_VARIANT_STREAM) {
+    rmm_stream_plan(N, K, gated, (int)kTargetWorkgroups, have_ws, &out->st);
+    if (out->st.ws_bytes > (size_t)INT32_MAX) return RMM_ERR_VARIANT;  // 32-bit offsets
+    out->ws_bytes = out->st.split ? out->st.ws_bytes : 0;
   }
   return RMM_OK;
 }
@@ -209,7 +214,7 @@ rmm_status run(const void* X, const void* g, const void* W1, const void* W3, voi
       err = rmm_launch_prefill(a, plan.pre);
       break;
     case RMM_VARIANT_STREAM:
-      err = rmm_launch_stream(a);
+      err = rmm_launch_stream(a, plan.st, plan.st.split ? ws : nullptr);
       break;
     default:
       return RMM_ERR_VARIANT;

@@ -124,7 +124,18 @@ struct PrefillPlan {
 void rmm_prefill_plan(int64_t M, int64_t N, int64_t K, PrefillPlan* p);
 hipError_t rmm_launch_prefill(const RmmArgs& a, const PrefillPlan& p);
 
-hipError_t rmm_launch_stream(const RmmArgs& a);
+// Stream variant: one workgroup per 64-column strip, or (split form, with a
+// workspace, when there are fewer strips than workgroups wanted) `grid`
+// workgroups each taking an equal share of the strips' k-steps, partial
+// sums combined in the workspace.
+struct StreamPlan {
+  int split;   // 1: split form
+  int strips;  // 64-column strips
+  int grid;    // workgroups launched
+  size_t ws_cnt_off, ws_part_off, ws_ssq_off, ws_bytes;
+};
+void rmm_stream_plan(int64_t N, int64_t K, int gated, int target, bool have_ws, StreamPlan* p);
+hipError_t rmm_launch_stream(const RmmArgs& a, const StreamPlan& p, void* ws);
 
 // QKNorm + attention, one query per batch-head (bf16, D = 64 or 128).
 struct AttnArgs {

@@ -327,3 +327,22 @@ def test_chain_validation_and_workspace(lib):
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(ImportError):
         _binding.load_library(str(tmp_path / "missing.so"))
+
+
+def test_stream_split_workspace(lib):
+    """The stream variant's split form: with at most 128 64-column strips
+    (half the 256 workgroups) it needs a workspace (strip counters, then 2
+    segments x 256 workgroups of fp32 sums per weight, then their row sums
+    of squares); with more strips it needs none."""
+    STREAM = 4
+    # gated 64 x 4096 x 8192: 128 strips, two weights
+    assert lib.rmm_workspace_bytes(BF16, 64, 8192, 4096, 1) == \
+        512 + 2 * 256 * 2 * 64 * 64 * 4 + 2 * 256 * 64 * 4
+    # plain, forced stream, 96 strips: one weight
+    assert lib.rmm_workspace_bytes_ex(BF16, 16, 6144, 4096, 0, STREAM, 0) == \
+        512 + 2 * 256 * 64 * 64 * 4 + 2 * 256 * 64 * 4
+    assert lib.rmm_workspace_bytes(BF16, 64, 8200, 4096, 1) == 0       # 129 strips
+    assert lib.rmm_workspace_bytes(BF16, 64, 14336, 4096, 1) == 0      # 224 strips
+    # the split form is planned only with a workspace; without one the call is valid
+    assert tpa.plan(64, 8192, 4096, gated=True)[:2] == (0, "stream")
+    assert tpa.plan(64, 8192, 4096, gated=True, with_workspace=False)[:2] == (0, "stream")

@@ -92,7 +92,9 @@ typedef enum {
   RMM_ERR_VARIANT = 8
 } rmm_status;
 
-/* Kernel variants.  AUTO picks by shape; the others force one (tests, bench).
+/* Kernel variants.  AUTO picks by shape (gated M <= 16 takes DECODE only
+ * when a workspace is passed, STREAM otherwise); the others force one
+ * (tests, bench).
  * The fast variants need bf16, K % 8 == 0, N % 8 == 0, 16-byte aligned
  * pointers, and X and each weight below 2 GiB (except fp32 DECODE, below).
  *   GENERIC : any shape, alignment and dtype; VALU fp32 products.
@@ -105,8 +107,10 @@ typedef enum {
  *   PREFILL : not gated; LDS-tiled MFMA GEMM with the row sum of squares
  *             fused into its k-loop.  Matrix-core-bound shapes.
  *   STREAM  : M <= 64; each workgroup streams 64-column strips of W (W1 and
- *             W3 when gated) over all of K through LDS, no split-K.
- *             Bandwidth-bound shapes with enough columns.                  */
+ *             W3 when gated) over all of K through LDS.  With a workspace
+ *             and at most 128 strips, the split form: every workgroup takes
+ *             an equal share of the strips' k-steps, partial sums combined
+ *             in the workspace.  Bandwidth-bound shapes.                  */
 typedef enum {
   RMM_VARIANT_AUTO = 0,
   RMM_VARIANT_GENERIC = 1,

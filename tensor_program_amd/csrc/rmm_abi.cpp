@@ -95,8 +95,9 @@ rmm_status plan_shape(int64_t M, int64_t N, int64_t K, rmm_dtype dtype, int gate
   if (v == RMM_VARIANT_AUTO) {
     if (R > 0)
       v = decode_ok ? RMM_VARIANT_DECODE : RMM_VARIANT_GENERIC;
-    else if (gated)
-      v = stream_ok ? RMM_VARIANT_STREAM : RMM_VARIANT_GENERIC;
+    else if (gated)  // decode (split-K over every CU) only with a workspace for its partials
+      v = (decode_ok && have_ws) ? RMM_VARIANT_DECODE
+                                 : (stream_ok ? RMM_VARIANT_STREAM : RMM_VARIANT_GENERIC);
     else if (decode_ok)
       v = RMM_VARIANT_DECODE;
     else if (stream_ok && (N + 63) / 64 >= kStreamMinTiles)

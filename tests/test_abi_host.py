@@ -252,7 +252,10 @@ def test_variant_selection():
     assert tpa.plan(16, 32768, 4096)[1:] == ("decode", 1)  # 256 tiles already fill the CUs
     assert tpa.plan(16, 6144, 4096, with_workspace=False)[1:] == ("decode", 1)
     assert tpa.plan(64, 14336, 4096, gated=True)[1] == "stream"
-    assert tpa.plan(16, 14336, 4096, gated=True)[1] == "stream"
+    # gated, M <= 16: decode with a workspace (16 x 4096 x 14336: 45.9 vs 47.3 us), else stream
+    assert tpa.plan(16, 14336, 4096, gated=True)[1] == "decode"
+    assert tpa.plan(16, 14336, 4096, gated=True, with_workspace=False)[1] == "stream"
+    assert tpa.plan(17, 14336, 4096, gated=True)[1] == "stream"
     assert tpa.plan(65, 14336, 4096, gated=True)[1] == "generic"
     assert tpa.plan(48, 14336, 4096)[1] == "stream"
     assert tpa.plan(48, 2048, 4096)[1] == "prefill"   # too few 64-column strips

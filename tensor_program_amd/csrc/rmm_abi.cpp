@@ -41,7 +41,6 @@ constexpr int64_t kTargetWorkgroups = 256;
 // Stream: up to 64 rows; auto-selected for plain calls only when there are
 // enough 64-column strips to keep most CUs streaming.
 constexpr int64_t kStreamMaxM = 64;
-constexpr int64_t kStreamMinTiles = 192;
 // Low-rank adapter: ranks 1..RMM_LORA_MAX_RANK; the decode kernel carries up
 // to two 16-wide rank blocks, every other shape runs the generic kernel.
 constexpr int64_t kLoraDecodeMaxRank = 32;
@@ -100,7 +99,7 @@ rmm_status plan_shape(int64_t M, int64_t N, int64_t K, rmm_dtype dtype, int gate
                                  : (stream_ok ? RMM_VARIANT_STREAM : RMM_VARIANT_GENERIC);
     else if (decode_ok)
       v = RMM_VARIANT_DECODE;
-    else if (stream_ok && (N + 63) / 64 >= kStreamMinTiles)
+    else if (stream_ok)  // M <= 64: far faster than one row of 256 x 256 prefill tiles
       v = RMM_VARIANT_STREAM;
     else
       v = prefill_ok ? RMM_VARIANT_PREFILL : RMM_VARIANT_GENERIC;

@@ -106,8 +106,9 @@ typedef enum {
  *             multiply-adds (no bf16 rounding).  Bandwidth-bound.
  *   PREFILL : not gated; LDS-tiled MFMA GEMM with the row sum of squares
  *             fused into its k-loop.  Matrix-core-bound shapes.
- *   STREAM  : M <= 64; each workgroup streams 64-column strips of W (W1 and
- *             W3 when gated) over all of K through LDS.  With a workspace
+ *   STREAM  : M <= 128 (above 64 rows: one launch per 64-row block); each
+ *             workgroup streams 64-column strips of W (W1 and W3 when
+ *             gated) over all of K through LDS.  With a workspace
  *             and at most 128 strips, the split form: every workgroup takes
  *             an equal share of the strips' k-steps, partial sums combined
  *             in the workspace.  Bandwidth-bound shapes.                  */

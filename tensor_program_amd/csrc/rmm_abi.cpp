@@ -40,7 +40,11 @@ constexpr int64_t kDecodeMaxMF32 = 16;  // fp32 decode: plain calls only
 constexpr int64_t kTargetWorkgroups = 256;
 // Stream: up to 64 rows; auto-selected for plain calls only when there are
 // enough 64-column strips to keep most CUs streaming.
-constexpr int64_t kStreamMaxM = 64;
+// The stream kernel computes 64 rows; up to 128 rows run as two launches
+// (one per 64-row block, each reading W again), which still beats one row
+// of 256 x 256 prefill tiles there.
+constexpr int64_t kStreamRows = 64;
+constexpr int64_t kStreamMaxM = 128;
 // Low-rank adapter: ranks 1..RMM_LORA_MAX_RANK; the decode kernel carries up
 // to two 16-wide rank blocks, every other shape runs the generic kernel.
 constexpr int64_t kLoraDecodeMaxRank = 32;
@@ -214,7 +218,15 @@ rmm_status run(const void* X, const void* g, const void* W1, const void* W3, voi
       err = rmm_launch_prefill(a, plan.pre);
       break;
     case RMM_VARIANT_STREAM:
-      err = rmm_launch_stream(a, plan.st, plan.st.split ? ws : nullptr);
+      // Row blocks of 64, in order on the stream (the split form's workspace
+      // is left ready for the next launch by the one before).
+      for (int64_t r0 = 0; r0 < a.M && err == hipSuccess; r0 += kStreamRows) {
+        RmmArgs b = a;
+        b.X = (const char*)a.X + r0 * a.K * 2;
+        b.Y = (char*)a.Y + r0 * a.N * 2;
+        b.M = a.M - r0 < kStreamRows ? a.M - r0 : kStreamRows;
+        err = rmm_launch_stream(b, plan.st, plan.st.split ? ws : nullptr);
+      }
       break;
     default:
       return RMM_ERR_VARIANT;

@@ -69,6 +69,9 @@ EXACT_CASES = [
     (8, 200, 16392, "bf16", "stream", 0),
     (20, 264, 14000, "bf16", "stream", 0),
     (16, 520, 6136, "bf16", "stream", 0),
+    # two 64-row launches: a full and a ragged second block, split and unsplit
+    (100, 264, 1032, "bf16", "stream", 0),
+    (128, 136, 16392, "bf16", "stream", 0),
 ]
 
 EXACT_SAMPLE_ROWS = 48  # above ~1e10 multiply-adds the oracle checks sampled rows
@@ -247,7 +250,7 @@ def test_errors_raise(require_gpu):
         tpa.rmsnorm_matmul(x, g, w, 1e-6, out=x.view(-1)[:128].view(4, 32))
 
 
-@pytest.mark.parametrize("M", [1, 16, 40, 64])
+@pytest.mark.parametrize("M", [1, 16, 40, 64, 65, 128])
 def test_gated_stream_shapes(M, require_gpu):
     """Gated stream variant on ragged shapes, against the oracle."""
     wl = synth.Workload("gated_stream", "bf16", M, 1032, 584, 1e-6, True, None)

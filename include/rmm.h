@@ -101,8 +101,8 @@ typedef enum {
  *   DECODE  : bf16: M <= 32 (gated: M <= 16); streams W once with split-K
  *             across workgroups, bf16 matrix-core (MFMA) products, fp32
  *             partials combined by the last-arriving workgroup.
- *             fp32: M <= 16, not gated, no adapter, 16-byte aligned
- *             pointers; the same split-K scheme with fp32 fused
+ *             fp32: M <= 32 (16 rows per launch), not gated, no adapter,
+ *             16-byte aligned pointers; the same split-K scheme with fp32 fused
  *             multiply-adds (no bf16 rounding).  Bandwidth-bound.
  *   PREFILL : not gated; LDS-tiled MFMA GEMM with the row sum of squares
  *             fused into its k-loop.  Matrix-core-bound shapes.

@@ -81,7 +81,7 @@ def test_validation_order(lib):
     assert call(lib, variant=4, splits=2) == VARIANT  # splits only for decode
     assert call(lib, variant=4, dtype=F32) == VARIANT  # stream is bf16 only
     assert call(lib, variant=1, splits=2) == VARIANT  # splits only for decode
-    assert call(lib, variant=2, dtype=F32, M=17) == VARIANT  # fp32 decode: M <= 16
+    assert call(lib, variant=2, dtype=F32, M=33) == VARIANT  # fp32 decode: M <= 32
     assert call(lib, variant=2, dtype=F32, X=A[0] + 4) == VARIANT  # fp32 decode: aligned
     assert call(lib, variant=2, M=33) == VARIANT
     assert call(lib, variant=2, N=60) == VARIANT      # N % 8 != 0
@@ -267,7 +267,8 @@ def test_variant_selection():
     assert tpa.plan(8, 1024, 1024, dtype=f32)[1:] == ("decode", 8)   # 32 tiles x 8 = 256
     assert tpa.plan(8, 1024, 1024, dtype=f32, with_workspace=False)[1:] == ("decode", 1)
     assert tpa.plan(16, 64, 100, dtype=f32)[1:] == ("decode", 2)     # K ranges of >= 64 rows
-    assert tpa.plan(17, 1024, 1024, dtype=f32)[1] == "generic"
+    assert tpa.plan(32, 1024, 1024, dtype=f32)[1] == "decode"    # two 16-row launches
+    assert tpa.plan(33, 1024, 1024, dtype=f32)[1] == "generic"
     assert tpa.plan(8, 1024, 1024, dtype=f32, gated=True)[1] == "generic"
     assert tpa.plan(8, 1024, 1024, dtype=f32, variant="decode", splits=5)[1:] == ("decode", 4)
     assert tpa.plan(4096, 4096, 4096)[1:] == ("prefill", 1)

@@ -39,6 +39,8 @@ EXACT_CASES = [
     (16, 1000, 520, "f32", "decode", 3),     # ragged K ranges, N % 32 != 0
     (13, 4096, 136, "f32", "decode", 0),     # 32 ranges of 128
     (11, 1000, 72, "f32", "decode", 1),      # multi-chunk loop with a partial last chunk
+    (32, 1024, 1024, "f32", "decode", 0),    # two 16-row launches
+    (21, 520, 136, "f32", "decode", 3),      # a ragged second block
     (16, 4096, 6144, "bf16", "generic", 0),
     (16, 4096, 6144, "bf16", "decode", 1),
     (16, 4096, 6144, "bf16", "decode", 3),

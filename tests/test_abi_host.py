@@ -262,7 +262,8 @@ def test_variant_selection():
     # M <= 64 takes the stream kernel at any width (48 x 4096 x 4096: 21 us
     # against 107 us for the prefill tiles)
     assert tpa.plan(48, 2048, 4096)[1] == "stream"
-    assert tpa.plan(129, 4096, 4096, variant="stream")[0] == VARIANT
+    assert tpa.plan(129, 4104, 4096, variant="stream")[0] == VARIANT
+    assert tpa.plan(257, 4096, 4096, variant="stream")[0] == VARIANT
     f32 = torch.float32
     assert tpa.plan(8, 1024, 1024, dtype=f32)[1:] == ("decode", 8)   # 32 tiles x 8 = 256
     assert tpa.plan(8, 1024, 1024, dtype=f32, with_workspace=False)[1:] == ("decode", 1)
@@ -275,7 +276,9 @@ def test_variant_selection():
     assert tpa.plan(8192, 28672, 8192)[1] == "prefill"
     assert tpa.plan(33, 520, 1000)[1] == "stream"
     assert tpa.plan(65, 520, 1000)[1] == "stream"    # two 64-row launches
-    assert tpa.plan(129, 520, 1000)[1] == "prefill"
+    assert tpa.plan(129, 520, 1000)[1] == "stream"    # N <= 4096: up to 256 rows
+    assert tpa.plan(257, 520, 1000)[1] == "prefill"
+    assert tpa.plan(129, 4104, 1000)[1] == "prefill"
     assert tpa.plan(4096, 4096, 4095)[1] == "generic"   # K % 8 != 0
     assert tpa.plan(4096, 4096, 4096, variant="prefill", dtype=torch.float32)[0] == VARIANT
     assert tpa.plan(128, 256, 64, gated=True, variant="prefill")[0] == VARIANT

@@ -106,8 +106,8 @@ typedef enum {
  *             multiply-adds (no bf16 rounding).  Bandwidth-bound.
  *   PREFILL : not gated; LDS-tiled MFMA GEMM with the row sum of squares
  *             fused into its k-loop.  Matrix-core-bound shapes.
- *   STREAM  : M <= 128, or M <= 256 with N <= 4096 (above 64 rows: one
- *             launch per 64-row block); each
+ *   STREAM  : gated: any M; plain: M <= 128, or M <= 256 with N <= 4096
+ *             (above 64 rows: one launch per 64-row block); each
  *             workgroup streams 64-column strips of W (W1 and W3 when
  *             gated) over all of K through LDS.  With a workspace
  *             and at most 128 strips, the split form: every workgroup takes

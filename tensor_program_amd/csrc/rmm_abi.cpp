@@ -98,7 +98,10 @@ rmm_status plan_shape(int64_t M, int64_t N, int64_t K, rmm_dtype dtype, int gate
   const bool decode_ok = (fast_layout && lora_ok && M <= (gated ? kDecodeMaxMGated : kDecodeMaxM)) ||
                          decode32_ok;
   const bool prefill_ok = fast_layout && !gated && R == 0;
-  const bool stream_ok = fast_layout && R == 0 && (M <= kStreamMaxM || (M <= 256 && N <= 4096));
+  // Gated calls have no prefill tile: any M runs as 64-row stream launches
+  // (far faster than the generic kernel's vector products).
+  const bool stream_ok =
+      fast_layout && R == 0 && (gated || M <= kStreamMaxM || (M <= 256 && N <= 4096));
   rmm_variant v = variant;
   if (v == RMM_VARIANT_AUTO) {
     if (R > 0)

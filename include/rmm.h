@@ -98,7 +98,8 @@ typedef enum {
  * The fast variants need bf16, K % 8 == 0, N % 8 == 0, 16-byte aligned
  * pointers, and X and each weight below 2 GiB (except fp32 DECODE, below).
  *   GENERIC : any shape, alignment and dtype; VALU fp32 products.
- *   DECODE  : bf16: M <= 32 (gated: M <= 16); streams W once with split-K
+ *   DECODE  : bf16: M <= 32 (gated: M <= 16; with the adapter M <= 128 as
+ *             one launch per 32-row block); streams W once with split-K
  *             across workgroups, bf16 matrix-core (MFMA) products, fp32
  *             partials combined by the last-arriving workgroup.
  *             fp32: M <= 32 (16 rows per launch), not gated, no adapter,

@@ -35,6 +35,9 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
 // traffic and lengthen the combine that the last arriving workgroup of each
 // tile does alone, and measured fastest at this size.
 constexpr int64_t kDecodeMaxM = 32;
+// With the adapter (no other fast kernel takes it) up to 128 rows run as
+// one decode launch per 32-row block.
+constexpr int64_t kDecodeMaxMLora = 128;
 constexpr int64_t kDecodeMaxMGated = 16;
 // fp32 decode: plain calls only; 16 rows per launch, up to 32 rows as two
 // launches (32 x 1024 x 1024: ~23 us against 40 us for the generic kernel;
@@ -95,7 +98,8 @@ rmm_status plan_shape(int64_t M, int64_t N, int64_t K, rmm_dtype dtype, int gate
                                   R * N * 2 <= (int64_t)INT32_MAX);
   const bool f32 = dtype == RMM_DTYPE_F32;
   const bool decode32_ok = f32 && aligned && !gated && R == 0 && M <= kDecodeMaxMF32;
-  const bool decode_ok = (fast_layout && lora_ok && M <= (gated ? kDecodeMaxMGated : kDecodeMaxM)) ||
+  const bool decode_ok = (fast_layout && lora_ok &&
+                          M <= (gated ? kDecodeMaxMGated : (R > 0 ? kDecodeMaxMLora : kDecodeMaxM))) ||
                          decode32_ok;
   const bool prefill_ok = fast_layout && !gated && R == 0;
   // Gated calls have no prefill tile: any M runs as 64-row stream launches
@@ -137,7 +141,7 @@ rmm_status plan_shape(int64_t M, int64_t N, int64_t K, rmm_dtype dtype, int gate
     if (s == 0) s = have_ws ? auto_decode_splits(N, K) : 1;
     if (s > (K + 127) / 128) return RMM_ERR_VARIANT;
     if (s > 1 && !have_ws) return RMM_ERR_WORKSPACE;  // a forced split count needs one
-    rmm_decode_plan(M, N, K, gated, s, R, &out->dec);
+    rmm_decode_plan(M < kDecodeMaxM ? M : kDecodeMaxM, N, K, gated, s, R, &out->dec);
     if (out->dec.ws_bytes > (size_t)INT32_MAX) return RMM_ERR_VARIANT;  // 32-bit offsets
     out->splits = out->dec.splits;
     out->ws_bytes = out->dec.ws_bytes;
@@ -229,7 +233,15 @@ rmm_status run(const void* X, const void* g, const void* W1, const void* W3, voi
           err = rmm_launch_decode32(b, plan.d32, plan.d32.splits > 1 ? ws : nullptr);
         }
       else
-        err = rmm_launch_decode(a, plan.dec, plan.dec.splits > 1 ? ws : nullptr);
+        // Row blocks of 32 (only calls with the adapter have more rows), in
+        // order on the stream (each leaves the split counters cleared).
+        for (int64_t r0 = 0; r0 < a.M && err == hipSuccess; r0 += kDecodeMaxM) {
+          RmmArgs b = a;
+          b.X = (const char*)a.X + r0 * a.K * 2;
+          b.Y = (char*)a.Y + r0 * a.N * 2;
+          b.M = a.M - r0 < kDecodeMaxM ? a.M - r0 : kDecodeMaxM;
+          err = rmm_launch_decode(b, plan.dec, plan.dec.splits > 1 ? ws : nullptr);
+        }
       break;
     case RMM_VARIANT_PREFILL:
       err = rmm_launch_prefill(a, plan.pre);

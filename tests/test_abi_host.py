@@ -142,7 +142,7 @@ def test_lora_entry_points_validate(lib):
     assert lo(Y=A[6] - 64) == ALIAS                 # Y overlapping B
     assert lo(variant=3) == VARIANT                 # no adapter prefill tile
     assert lo(variant=4) == VARIANT
-    assert lo(M=33, variant=2) == VARIANT           # decode: M <= 32
+    assert lo(M=129, variant=2) == VARIANT          # decode with the adapter: M <= 128 (32-row launches)
     assert lo(R=33, variant=2) == VARIANT           # decode: R <= 32
     assert lo(K=256, variant=2, splits=2) == WORKSPACE  # forced split count, no workspace
     assert lo(X=None, g=None, W=None, LA=None, LB=None, Y=None, M=0) == OK
@@ -163,7 +163,9 @@ def test_lora_plans():
     assert tpa.plan_lora(32, 6144, 4096, 16)[1] == "decode"
     assert tpa.plan_lora(16, 6144, 4096, 33)[1] == "generic"
     assert tpa.plan_lora(16, 6144, 4096, 64)[1] == "generic"
-    assert tpa.plan_lora(33, 6144, 4096, 16)[1] == "generic"
+    assert tpa.plan_lora(33, 6144, 4096, 16)[1] == "decode"    # 32-row launches
+    assert tpa.plan_lora(128, 6144, 4096, 16)[1] == "decode"
+    assert tpa.plan_lora(129, 6144, 4096, 16)[1] == "generic"
     assert tpa.plan_lora(4096, 4096, 4096, 16)[1] == "generic"
     assert tpa.plan_lora(8, 1024, 1024, 16, dtype=torch.float32)[1] == "generic"
     assert tpa.plan_lora(16, 6144, 4096, 16, with_workspace=False)[1:] == ("decode", 1)

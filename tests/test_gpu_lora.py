@@ -6,7 +6,8 @@ rmsnorm_lora computes Nrm W + (Nrm A^T) B and lora_matmul X W + (X A^T) B
 * exact-arithmetic cases, bit for bit after the one rounding of Y: the
   decode kernel at every split count (the down-projection partials ride the
   split-K combine), ranks below, at and between its 16-wide blocks, ragged
-  N and K, both row blocks; the generic kernel for larger ranks and fp32;
+  N and K, both 16-row blocks, and several 32-row launches (M up to 128);
+  the generic kernel for larger ranks, more rows and fp32;
 * the adapter workload within tolerance, and B = 0 against the plain fused
   call on the same kernels.
 """
@@ -52,7 +53,9 @@ LORA_EXACT = [
     (33, 200, 136, 48, "bf16", "generic", 0),
     (8, 1024, 1024, 16, "f32", "generic", 0),
     (5, 40, 24, 3, "f32", "generic", 0),
-    (64, 1024, 2048, 16, "bf16", "auto", 0),    # M > 32: the generic kernel
+    (64, 1024, 2048, 16, "bf16", "auto", 0),    # M > 32: two 32-row decode launches
+    (100, 520, 1032, 16, "bf16", "decode", 3),  # four launches, ragged last block
+    (129, 200, 136, 8, "bf16", "generic", 0),   # above 128 rows: the generic kernel
 ]
 
 

@@ -31,7 +31,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "fused RMSNorm+MatMul TFLOP/s and HBM GB/s (% of MI355X roofline)"
-DEFAULT_WORKLOAD = "decode_m16_k4096_n6144"
+# the largest single-GPU workload (the headline line)
+DEFAULT_WORKLOAD = "large_m8192_k8192_n28672"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2516.6      # dense bf16 MFMA, 256 CU x 4096 flop/clk x 2.4 GHz
 F32_VALU_PEAK_TFLOPS = 78.6    # fp32 FMA on the vector ALUs without packed math
@@ -74,6 +75,60 @@ def stored_traffic(workload: str, variant: str):
     if not rec or rec.get("kernel_source_sha256_16") != source_hash(variant):
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def host_cpu() -> dict:
+    """The host's CPU model and logical CPU count (the oracle's machine)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "logical_cpus": os.cpu_count()}
+
+
+def measure_peaks(stream, dev):
+    """Achievable ceilings of this part, from the library's own probes
+    (rmm_probe_hbm_read over a 2 GiB buffer, far past the 256 MB last-level
+    cache; rmm_probe_mfma_bf16, a dense v_mfma_f32_32x32x16_bf16 loop),
+    timed with HIP events on the launch stream."""
+    import ctypes
+    import torch
+    import tensor_program_amd as tpa
+
+    lib = tpa.load_library()
+    nbytes = 2 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    h = ctypes.c_void_p(stream.cuda_stream)
+    iters = 20000
+    out = {}
+    with torch.cuda.stream(stream):
+        for name, launch, work in (
+                ("hbm_read_gbs", lambda: lib.rmm_probe_hbm_read(buf.data_ptr(), nbytes,
+                                                               sink.data_ptr(), h), nbytes / 1e9),
+                ("mfma_bf16_tflops", lambda: lib.rmm_probe_mfma_bf16(iters, sink.data_ptr(), h),
+                 lib.rmm_probe_mfma_flops(iters) / 1e12)):
+            for _ in range(5):
+                tpa._binding.check(launch())
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            n = 20
+            e0.record(stream)
+            for _ in range(n):
+                launch()
+            e1.record(stream)
+            e1.synchronize()
+            out[name] = work / (e0.elapsed_time(e1) / 1e3 / n)
+    del buf
+    torch.cuda.empty_cache()
+    out["probes"] = ("rmm_probe_hbm_read (2 GiB linear read, 16-byte loads) and "
+                     "rmm_probe_mfma_bf16 (4 chains of v_mfma_f32_32x32x16_bf16 per wave, 2 waves "
+                     "per SIMD), 20 launches each after 5 untimed")
+    return out
 
 
 def synth_attn_type():
@@ -123,8 +178,8 @@ def cpu_baseline(wl, inp, budget_s: float):
         rows = max(rows, (rows_budget // threads) * threads)
         t = once(full[:rows])
         frac = rows / total
-        sample = (f"first {rows} of {total} {unit_name} (they are independent); time scaled "
-                  f"x{total / rows:.1f}")
+        sample = (f"first {rows} of {total} {unit_name} (they are independent), fp64 unfused; "
+                  f"time extrapolated x{total / rows:.1f} to the whole workload")
     t_full = t / frac
     bound = "hbm" if wl.flops() / wl.algo_bytes() < RIDGE else "mfma"
     if bound == "hbm":
@@ -133,7 +188,7 @@ def cpu_baseline(wl, inp, budget_s: float):
         value, unit = wl.flops() / t_full / 1e12, "TFLOP/s"
     used = min(threads, rows)
     return {"value": value, "unit": unit, "cores": used, "kind": "oracle", "sample": sample,
-            "seconds_full_workload": t_full}
+            "seconds_full_workload": t_full, "omp_threads": threads} | host_cpu()
 
 
 def bench_chain(args, name):
@@ -195,19 +250,21 @@ def bench_chain(args, name):
             t0 = time.time()
             while time.time() - t0 < args.settle_ms / 1e3:
                 graph.replay()
-            reps_w = max(1, args.warmup // R)
-            for _ in range(reps_w):
-                graph.replay()
-            reps = max(1, args.steps // R)
+            def run(n):  # exactly n calls: whole rotations from the graph, the rest eager
+                for _ in range(n // R):
+                    graph.replay()
+                for i in range(n % R):
+                    call(sets[i])
+            n_warm, n_steps = max(0, args.warmup), max(1, args.steps)
+            run(n_warm)
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             stream.synchronize()
             e0.record(stream)
-            for _ in range(reps):
-                graph.replay()
+            run(n_steps)
             e1.record(stream)
             e1.synchronize()
-        results[mode] = (e0.elapsed_time(e1) / (reps * R), reps * R, reps_w * R)
+        results[mode] = (e0.elapsed_time(e1) / n_steps, n_steps, n_warm)
         log(f"{mode}: {results[mode][0] * 1e3:.1f} us per call ({results[mode][0] * 1e3 / L:.2f} "
             f"us per layer)")
     ms, steps, warm = results["chain"]
@@ -245,8 +302,8 @@ def bench_chain(args, name):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--variant", default="auto")
     ap.add_argument("--splits", type=int, default=0)
@@ -257,6 +314,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unfused", action="store_true",
                     help="skip timing the unfused two-kernel program beside the fused call")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the achievable-peak probes (HBM read, MFMA loop)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -398,8 +457,10 @@ def main():
     run_steps = make_runner(lambda i: call(sets[i]), not args.no_graph)
     graph = None if args.no_graph else True
 
-    steps = max(R, (args.steps // R) * R)
-    warm = max(R, (args.warmup // R) * R) if args.warmup > 0 else 0
+    # exactly the requested counts (run() replays whole rotations from the
+    # graph and launches any remainder eagerly)
+    steps = max(1, args.steps)
+    warm = max(0, args.warmup)
     settle_calls = 0
     t0 = time.perf_counter()
     while (time.perf_counter() - t0) * 1e3 < args.settle_ms:
@@ -479,6 +540,15 @@ def main():
     # the fp32 decode variant is its own kernel (rmm_decode32.hip)
     kvar = "decode32" if (variant == "decode" and wl.dtype == "f32") else variant
     roof["traffic"] = stored_traffic(wl.name, kvar)
+    peaks = None
+    if not args.no_peaks:
+        log("achievable-peak probes")
+        peaks = measure_peaks(stream, dev)
+        ach = peaks["hbm_read_gbs"] if roof["bound"] == "hbm" else (
+            peaks["mfma_bf16_tflops"] if roof["bound"] == "mfma" else None)
+        if ach:
+            roof["achievable_peak"] = ach
+            roof["frac_of_achievable"] = roof["achieved"] / ach
     roof["kernel"] = "qknorm_attention_kernel" if attn else f"{kvar}_kernel"
     roof["algorithmic_bytes_per_launch"] = per_set
     roof["algorithmic_flops_per_launch"] = wl.flops()
@@ -500,6 +570,7 @@ def main():
                    "clock_settle_calls": settle_calls},
         "tflops": tflops, "hbm_gbs_algorithmic": gbs,
         "roofline": roof, "cpu_baseline": cpu, "unfused_baseline": unfused,
+        "achievable_peaks": peaks,
     }
     print(json.dumps(line), flush=True)
 

@@ -26,8 +26,12 @@
  *   Y  : M x N   (Y[m*N + n])
  * dtype selects the storage type of X, g, W*, Y together; products are summed
  * in fp32 whatever the dtype.  With RMM_DTYPE_BF16 the operand X[m,k]*g[k] is
- * formed in fp32 and rounded once (round to nearest even) to bf16 before the
- * matrix-core product; Y is rounded once from fp32 to bf16 (nearest even).
+ * formed exactly in fp32 (a product of two bf16 values); the plain product
+ * rounds it once (round to nearest even) to bf16 before the matrix-core
+ * product, while the gated product and the low-rank adapter carry it exactly
+ * as two bf16 parts hi + lo (two matrix-core products), because the gate
+ * multiplies one product's error by the other and the adapter's two terms can
+ * cancel.  Y is rounded once from fp32 to bf16 (nearest even).
  *
  * Ownership and ordering.  Every data pointer is a DEVICE pointer owned by the
  * caller; the library keeps none after it returns, allocates nothing and
@@ -304,6 +308,24 @@ rmm_status rmm_plan_lora(const void* X, const void* g, const void* W, const void
                          int64_t R, rmm_dtype dtype, rmm_variant variant, int splits,
                          const void* ws, size_t ws_bytes, rmm_variant* variant_out,
                          int* splits_out);
+
+/* Measurement probes (not part of the operation): the two ceilings this
+ * part sustains, against which the kernels' roofline fractions are also
+ * stated besides the published peaks.
+ *   rmm_probe_hbm_read: reads `bytes` (a multiple of 16, > 0) from the device
+ *     buffer `src` (16-byte aligned) once, linearly, with 16-byte loads; the
+ *     4-byte device word `sink` is written only if the folded data hits one
+ *     fixed pattern (in practice never).  Time it to get the achievable read
+ *     bandwidth; pass a buffer far larger than the 256 MB last-level cache.
+ *   rmm_probe_mfma_bf16: a dense loop of iters x 4 dependent-chain
+ *     v_mfma_f32_32x32x16_bf16 per wave over two waves per SIMD of 256 CUs;
+ *     rmm_probe_mfma_flops(iters) is the flop count of one launch (0 for
+ *     iters outside 1..2^40).  `sink` as above (a 4-byte device word).
+ * Errors: RMM_ERR_NULL, RMM_ERR_SHAPE (bytes or iters), RMM_ERR_VARIANT
+ * (unaligned src), RMM_ERR_HIP.  Stream ordered, like every call here. */
+rmm_status rmm_probe_hbm_read(const void* src, size_t bytes, void* sink, hipStream_t stream);
+rmm_status rmm_probe_mfma_bf16(int64_t iters, void* sink, hipStream_t stream);
+int64_t rmm_probe_mfma_flops(int64_t iters);
 
 const char* rmm_status_string(rmm_status s);
 int rmm_last_hip_error(void);

@@ -24,7 +24,8 @@ SYMBOLS = ("rmsnorm_matmul", "rmsnorm_gated_mlp", "rmsnorm_matmul_ex", "rmsnorm_
            "rmm_abi_version", "rmsnorm_lora", "rmsnorm_lora_ex", "rmm_lora_matmul",
            "rmm_lora_workspace_bytes", "rmm_plan_lora", "qknorm_attention",
            "qknorm_attention_ex", "rmm_attention_workspace_bytes", "rmm_plan_attention",
-           "rmsnorm_matmul_chain", "rmm_chain_workspace_bytes", "rmm_chain_flag_offset")
+           "rmsnorm_matmul_chain", "rmm_chain_workspace_bytes", "rmm_chain_flag_offset",
+           "rmm_probe_hbm_read", "rmm_probe_mfma_bf16", "rmm_probe_mfma_flops")
 LORA_MAX_RANK = 64
 
 _lib = None
@@ -85,6 +86,12 @@ def load_library(path: str = LIB_PATH):
     lib.rmm_chain_workspace_bytes.restype = sz
     lib.rmm_chain_flag_offset.argtypes = [i64, i64, i64]
     lib.rmm_chain_flag_offset.restype = sz
+    lib.rmm_probe_hbm_read.argtypes = [vp, sz, vp, vp]
+    lib.rmm_probe_hbm_read.restype = i32
+    lib.rmm_probe_mfma_bf16.argtypes = [i64, vp, vp]
+    lib.rmm_probe_mfma_bf16.restype = i32
+    lib.rmm_probe_mfma_flops.argtypes = [i64]
+    lib.rmm_probe_mfma_flops.restype = i64
     lib.rmm_workspace_bytes.argtypes = [i32, i64, i64, i64, i32]
     lib.rmm_workspace_bytes.restype = sz
     lib.rmm_workspace_bytes_ex.argtypes = [i32, i64, i64, i64, i32, i32, i32]

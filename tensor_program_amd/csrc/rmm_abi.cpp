@@ -572,6 +572,33 @@ size_t rmm_chain_workspace_bytes(int64_t M, int64_t K, int64_t L) {
   return plan.ws_bytes;
 }
 
+rmm_status rmm_probe_hbm_read(const void* src, size_t bytes, void* sink, hipStream_t stream) {
+  if (!src || !sink) return RMM_ERR_NULL;
+  if (bytes == 0 || bytes % 16 != 0) return RMM_ERR_SHAPE;
+  if (!aligned16(src)) return RMM_ERR_VARIANT;
+  const hipError_t err = rmm_launch_probe_read(src, bytes, sink, stream);
+  if (err != hipSuccess) {
+    g_last_hip_error = (int)err;
+    return RMM_ERR_HIP;
+  }
+  return RMM_OK;
+}
+
+rmm_status rmm_probe_mfma_bf16(int64_t iters, void* sink, hipStream_t stream) {
+  if (!sink) return RMM_ERR_NULL;
+  if (iters < 1 || iters > ((int64_t)1 << 40)) return RMM_ERR_SHAPE;
+  const hipError_t err = rmm_launch_probe_mfma(iters, sink, stream);
+  if (err != hipSuccess) {
+    g_last_hip_error = (int)err;
+    return RMM_ERR_HIP;
+  }
+  return RMM_OK;
+}
+
+int64_t rmm_probe_mfma_flops(int64_t iters) {
+  return iters < 1 || iters > ((int64_t)1 << 40) ? 0 : rmm_probe_mfma_flops_per_launch(iters);
+}
+
 size_t rmm_chain_flag_offset(int64_t M, int64_t K, int64_t L) {
   if (rmm_chain_workspace_bytes(M, K, L) == 0) return 0;
   ChainPlan plan;

@@ -42,12 +42,25 @@ namespace rmm {
 
 constexpr int DEC_STAGE_BYTES = 32768;    // LDS for the staged A operand
 
+// The gated and adapter calls carry the operand X*g exactly as two bf16
+// parts (split_bf16x2): the gate multiplies one product's error by the other
+// product, and the adapter's two terms can cancel, so a single rounding of
+// X*g would not keep those outputs within the elementwise bound the plain
+// product meets.  The extra matrix-core work is free here (bandwidth-bound).
+template <int NW, int LR>
+struct DecSplit {
+  static constexpr bool value = NW == 2 || LR > 0;
+};
+
 template <int MB, int NW, int WV, int LR>
 struct DecodeSmem {
+  static constexpr bool SPLIT = DecSplit<NW, LR>::value;
   // per-wave accumulators [wave][slot][lane]: slots (wi,b,c) of the weight
   // products, then (b,lb) of the adapter's down-projection
   floatx4 red[WV][NW * MB * 8 + MB * LR][64];
   u32x4 xg[DEC_STAGE_BYTES / (16 * 16 * MB)][16 * MB];  // A operand, [k/8][row]
+  // low part of the split operand, same layout
+  u32x4 xl[SPLIT ? DEC_STAGE_BYTES / (16 * 16 * MB) : 1][16 * MB];
   u32x4 lb[LR > 0 ? 16 * LR : 1][16];  // adapter: the tile's B rows, [rank][8-column chunk]
   float ssr[16 * MB];
   float inv[16 * MB];
@@ -62,7 +75,9 @@ __global__ __launch_bounds__(WV * 64) void decode_kernel(
     float* __restrict__ ssq_ws, float* __restrict__ part_ws, int norm,
     const bf16_t* __restrict__ LA, const bf16_t* __restrict__ LB, int R) {
   constexpr int NW = GATED ? 2 : 1;
+  constexpr bool SPLIT = DecSplit<NW, LR>::value;
   static_assert(!(GATED && LR), "the adapter is not combined with the gate");
+  static_assert(sizeof(DecodeSmem<MB, NW, WV, LR>) <= 160 * 1024, "LDS");
   constexpr int NT = WV * 64;
   constexpr int EW = NW * MB * 8;                 // weight-product slots
   constexpr int E4 = (EW + MB * LR) * 64;         // floatx4 per partial
@@ -129,16 +144,22 @@ __global__ __launch_bounds__(WV * 64) void decode_kernel(
   auto stage_form = [&](const u32x4 (&xs)[NU], const u32x4 (&gs)[NU]) {
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
-      u32x4 av;
+      u32x4 av, al;
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         const float x0 = bf16_lo(xs[u][d]), x1 = bf16_hi(xs[u][d]);
         const uint32_t gd = norm ? gs[u][d] : kBf16OnePair;
         const float g0 = bf16_lo(gd), g1 = bf16_hi(gd);
         ssl += x0 * x0 + x1 * x1;
-        av[d] = pack_bf16x2(x0 * g0, x1 * g1);
+        if (SPLIT) {
+          const u32x2 hl = split_bf16x2(x0 * g0, x1 * g1);
+          av[d] = hl[0];
+          al[d] = hl[1];
+        } else
+          av[d] = pack_bf16x2(x0 * g0, x1 * g1);
       }
       sm.xg[sj + TPR * u][srow] = av;
+      if (SPLIT) sm.xl[sj + TPR * u][srow] = al;
     }
   };
 
@@ -187,19 +208,32 @@ __global__ __launch_bounds__(WV * 64) void decode_kernel(
   for (int b = 0; b < MB; ++b)
 #pragma unroll
     for (int i = 0; i < LR; ++i) lacc[b][i] = floatx4{0.f, 0.f, 0.f, 0.f};
-  auto lora_mma = [&](const u32x4 (&lv)[LR > 0 ? LR : 1], const u32x4 (&a)[MB]) {
+  auto lora_mma = [&](const u32x4 (&lv)[LR > 0 ? LR : 1], const u32x4 (&a)[MB],
+                      const u32x4 (&al)[MB]) {
 #pragma unroll
     for (int b = 0; b < MB; ++b)
 #pragma unroll
-      for (int i = 0; i < LR; ++i)
+      for (int i = 0; i < LR; ++i) {
         lacc[b][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             __builtin_bit_cast(bf16x8, a[b]), __builtin_bit_cast(bf16x8, lv[i]), lacc[b][i], 0, 0, 0);
+        lacc[b][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, al[b]), __builtin_bit_cast(bf16x8, lv[i]), lacc[b][i], 0, 0, 0);
+      }
+  };
+  auto mma = [&](const u32x4 (&wv)[NW][8], const u32x4 (&a)[MB], const u32x4 (&al)[MB]) {
+    if (SPLIT)
+      decode_mma2<MB, NW>(wv, a, al, acc);
+    else
+      decode_mma<MB, NW>(wv, a, acc);
   };
 
-  auto fetch_a = [&](int s, u32x4 (&a)[MB]) {
+  auto fetch_a = [&](int s, u32x4 (&a)[MB], u32x4 (&al)[MB]) {
     const int kc = ((s % SPS) * STEP + 32 * w + 8 * q) >> 3;
 #pragma unroll
-    for (int b = 0; b < MB; ++b) a[b] = sm.xg[kc][16 * b + p];
+    for (int b = 0; b < MB; ++b) {
+      a[b] = sm.xg[kc][16 * b + p];
+      if (SPLIT) al[b] = sm.xl[kc][16 * b + p];
+    }
   };
   // A new segment: everyone is done with the old one, stage, publish.
   auto restage = [&](int s) {
@@ -212,24 +246,24 @@ __global__ __launch_bounds__(WV * 64) void decode_kernel(
   int s = 0;
   for (; s + 2 <= nsteps; s += 2) {
     if (s > 0 && s % SPS == 0) restage(s);
-    u32x4 a[MB];
-    fetch_a(s, a);
-    decode_mma<MB, NW>(wa, a, acc);
-    lora_mma(la, a);
+    u32x4 a[MB], al[MB];
+    fetch_a(s, a, al);
+    mma(wa, a, al);
+    lora_mma(la, a, al);
     decode_load<NW>(wa, src, N, k_lo + (int64_t)(s + 2) * STEP + 32 * w + 8 * q, k_hi, col, col_ok);
     lora_load(la, k_lo + (int64_t)(s + 2) * STEP + 32 * w + 8 * q);
-    fetch_a(s + 1, a);
-    decode_mma<MB, NW>(wb, a, acc);
-    lora_mma(lb, a);
+    fetch_a(s + 1, a, al);
+    mma(wb, a, al);
+    lora_mma(lb, a, al);
     decode_load<NW>(wb, src, N, k_lo + (int64_t)(s + 3) * STEP + 32 * w + 8 * q, k_hi, col, col_ok);
     lora_load(lb, k_lo + (int64_t)(s + 3) * STEP + 32 * w + 8 * q);
   }
   if (s < nsteps) {
     if (s > 0 && s % SPS == 0) restage(s);
-    u32x4 a[MB];
-    fetch_a(s, a);
-    decode_mma<MB, NW>(wa, a, acc);
-    lora_mma(la, a);
+    u32x4 a[MB], al[MB];
+    fetch_a(s, a, al);
+    mma(wa, a, al);
+    lora_mma(la, a, al);
   }
 
   if (LR > 0) {

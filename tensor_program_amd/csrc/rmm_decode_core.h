@@ -56,4 +56,31 @@ __device__ __forceinline__ void decode_mma(const u32x4 (&wv)[NW][8], const u32x4
   }
 }
 
+// As decode_mma, for an operand carried exactly as two bf16 parts: the
+// k-sum takes a_hi + a_lo against each transposed W column.
+template <int MB, int NW>
+__device__ __forceinline__ void decode_mma2(const u32x4 (&wv)[NW][8], const u32x4 (&a)[MB],
+                                            const u32x4 (&al)[MB], floatx4 (&acc)[NW][MB][8]) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+#pragma unroll
+    for (int wi = 0; wi < NW; ++wi) {
+      u32x4 bop;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        bop[d] = __builtin_amdgcn_perm(wv[wi][2 * d + 1][c >> 1], wv[wi][2 * d][c >> 1],
+                                       (c & 1) ? 0x07060302u : 0x05040100u);
+#pragma unroll
+      for (int b = 0; b < MB; ++b) {
+        acc[wi][b][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, a[b]), __builtin_bit_cast(bf16x8, bop), acc[wi][b][c], 0, 0,
+            0);
+        acc[wi][b][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, al[b]), __builtin_bit_cast(bf16x8, bop), acc[wi][b][c], 0, 0,
+            0);
+      }
+    }
+  }
+}
+
 }  // namespace rmm

@@ -37,15 +37,31 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
 
+// Two fp32 values that are each the exact product of two bf16 values (at
+// most 16 significant bits) -> packed bf16 pairs hi and lo with
+// hi + lo == the products exactly: hi is the nearest-even rounding, and the
+// remainder (computed exactly in fp32) has at most 8 significant bits, so
+// its own rounding to bf16 is exact.  The gated and adapter paths feed both
+// parts to the matrix cores, so their k-sums see X*g without rounding.
+// Returns {hi, lo}.
+__device__ __forceinline__ u32x2 split_bf16x2(float p0, float p1) {
+  const uint32_t hi = pack_bf16x2(p0, p1);
+  return u32x2{hi, pack_bf16x2(p0 - __uint_as_float(hi << 16), p1 - __uint_as_float(hi & 0xffff0000u))};
+}
+
 // Load/store of one element of the storage type as fp32.
 __device__ __forceinline__ float load_f32(const float* p) { return *p; }
 __device__ __forceinline__ float load_f32(const bf16_t* p) { return bf16_to_f32(*p); }
 __device__ __forceinline__ void store_f32(float* p, float v) { *p = v; }
 __device__ __forceinline__ void store_f32(bf16_t* p, float v) { *p = f32_to_bf16(v); }
 
-// silu(z) * z3 for the gated epilogue.
+// silu(z1) * z3 for the gated epilogue, silu(z) = z / (1 + e^-z), with the
+// logistic factor taken as 1 / (1 + e^-|z|) for z >= 0 and e^-|z| / (1 + e^-|z|)
+// for z < 0: e^-|z| never overflows, so below z = -88.7 (where e^-z is past
+// the fp32 range) the result stays the small number it is instead of 0.
 __device__ __forceinline__ float silu_gate(float z1, float z3) {
-  return z1 / (1.0f + expf(-z1)) * z3;
+  const float e = expf(-fabsf(z1));
+  return z1 * ((z1 >= 0.0f ? 1.0f : e) / (1.0f + e)) * z3;
 }
 
 // 1 / sqrt(ss / K + eps) with IEEE division and square root, so that
@@ -160,3 +176,8 @@ hipError_t rmm_launch_attention(const AttnArgs& a, const AttnPlan& p, void* ws);
 // Unfused baseline, first kernel: Xn = bf16/f32(X * g / RMS) written out.
 hipError_t rmm_launch_rmsnorm(const void* X, const void* g, void* Xn, float eps, int64_t M,
                               int64_t K, bool bf16, hipStream_t stream);
+
+// Achievable-peak probes (rmm_probe.hip).
+hipError_t rmm_launch_probe_read(const void* src, size_t bytes, void* sink, hipStream_t stream);
+hipError_t rmm_launch_probe_mfma(int64_t iters, void* sink, hipStream_t stream);
+int64_t rmm_probe_mfma_flops_per_launch(int64_t iters);

@@ -93,10 +93,22 @@ __device__ __forceinline__ void st_lds_load16(uint32_t lds_addr, uint32_t voff, 
 #define ST_WAIT_VMCNT(n) \
   __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
 
+// The gated form carries the operand X*g exactly as two bf16 parts
+// (split_bf16x2): the gate multiplies one product's error by the other
+// product, so a single rounding of X*g would not keep every output within
+// the elementwise bound the plain product meets.  The high part replaces X
+// in its ring slot; the low part goes to a two-slot ring of its own (the
+// step being multiplied and the step being formed).
+template <int NW>
+struct StSplitOp {
+  static constexpr bool value = NW == 2;
+};
+
 template <int NW>
 struct StSmem {
   char w[StCfg<NW>::RING][NW][ST_W_BYTES];
   char x[StCfg<NW>::RING][ST_X_BYTES];
+  char xl[StSplitOp<NW>::value ? 2 : 1][StSplitOp<NW>::value ? ST_X_BYTES : 16];
   char g[StCfg<NW>::RING][ST_G_BYTES];
   float ss[ST_BM];
   float inv[ST_BM];
@@ -132,6 +144,7 @@ __global__ __launch_bounds__(ST_THREADS, 1) void stream_kernel(
     const bf16_t* __restrict__ W3, bf16_t* __restrict__ Y, float eps, int M, int64_t N,
     int64_t K, int norm, StSplit sp) {
   constexpr int RING = StCfg<NW>::RING, AHEAD = StCfg<NW>::AHEAD, SUBS = StCfg<NW>::SUBS;
+  constexpr bool SPLIT = StSplitOp<NW>::value;
   __shared__ __attribute__((aligned(1024))) StSmem<NW> sm;
   __shared__ int last2[2];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
@@ -208,15 +221,22 @@ __global__ __launch_bounds__(ST_THREADS, 1) void stream_kernel(
     const u32x4 xv = *(const u32x4*)xp;
     const u32x4 gl = *(const u32x4*)&sm.g[slot][16 * f_c];
     const u32x4 gv = norm ? gl : u32x4{kBf16OnePair, kBf16OnePair, kBf16OnePair, kBf16OnePair};
-    u32x4 av;
+    u32x4 av, al;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
       const bf16x2 x = st_bf16x2(xv[d]);
-      av[d] = pack_bf16x2(__builtin_amdgcn_fdot2_f32_bf16(x, st_bf16x2(gv[d] & 0xffffu), 0.0f, false),
-                          __builtin_amdgcn_fdot2_f32_bf16(x, st_bf16x2(gv[d] & 0xffff0000u), 0.0f, false));
+      const float p0 = __builtin_amdgcn_fdot2_f32_bf16(x, st_bf16x2(gv[d] & 0xffffu), 0.0f, false);
+      const float p1 = __builtin_amdgcn_fdot2_f32_bf16(x, st_bf16x2(gv[d] & 0xffff0000u), 0.0f, false);
+      if (SPLIT) {
+        const u32x2 hl = split_bf16x2(p0, p1);
+        av[d] = hl[0];
+        al[d] = hl[1];
+      } else
+        av[d] = pack_bf16x2(p0, p1);
       ss = __builtin_amdgcn_fdot2_f32_bf16(x, x, ss, false);
     }
     *(u32x4*)xp = av;
+    if (SPLIT) *(u32x4*)&sm.xl[step & 1][f_off] = al;
   };
 
   // Wave roles: partial set w>>1 (gated: weight set>>1, k-half set&1;
@@ -262,15 +282,19 @@ __global__ __launch_bounds__(ST_THREADS, 1) void stream_kernel(
     // Split form: local step kt+1 starts the range's second strip.
     const bool seg_end = SK && kt + 1 == nb;
     const char* x_lds = &sm.x[slot][0];
+    const char* xl_lds = &sm.xl[SPLIT ? (kt & 1) : 0][0];
     const lds_char* b_lds = (const lds_char*)&sm.w[slot][wsel][0];
-    u32x4 av[SUBS][2], bv[SUBS];
+    u32x4 av[SUBS][2], avl[SUBS][2], bv[SUBS];
 #pragma unroll
     for (int i = 0; i < SUBS; ++i) {
       const int s = s_first + i;
       const int kc = 2 * s + (l >> 5);
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-        av[i][rb] = *(const u32x4*)(x_lds + (rb * 32 + a_lo) * 128 + ((kc ^ st_xswz(a_lo)) << 4));
+      for (int rb = 0; rb < 2; ++rb) {
+        const int ao = (rb * 32 + a_lo) * 128 + ((kc ^ st_xswz(a_lo)) << 4);
+        av[i][rb] = *(const u32x4*)(x_lds + ao);
+        if (SPLIT) avl[i][rb] = *(const u32x4*)(xl_lds + ao);
+      }
       const u32x2 lo = __builtin_bit_cast(
           u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(b_lds + b_off + 16 * s * 128)));
       const u32x2 hi = __builtin_bit_cast(
@@ -289,6 +313,15 @@ __global__ __launch_bounds__(ST_THREADS, 1) void stream_kernel(
         acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[i][rb]),
                                                           __builtin_bit_cast(bf16x8, bv[i]),
                                                           acc[rb], 0, 0, 0);
+    if (SPLIT) {
+#pragma unroll
+      for (int i = 0; i < SUBS; ++i)
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+          acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, avl[i][rb]),
+                                                            __builtin_bit_cast(bf16x8, bv[i]),
+                                                            acc[rb], 0, 0, 0);
+    }
     if (seg_end) {
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {

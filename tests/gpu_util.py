@@ -71,31 +71,23 @@ def assert_within_tol(y_gpu: np.ndarray, y_ref: np.ndarray, tol: float, what: st
     return float((err / lim).max()) if err.size else 0.0
 
 
-def gated_bound(inp: "synth.Inputs", eps: float, tol: float) -> np.ndarray:
-    """Per-element bound for y = silu(z1) z3 from the per-product bound
-    tol (|z| + 1) on z1 and z3, first and second order, plus the bf16 rounding
-    of y.  The gate multiplies the two products' errors by the other factor,
-    so an element of y can be off by more than tol (|y| + 1) while both
-    products are within their bound."""
-    xn = oracle.rmsnorm(inp.X, inp.g, oracle.eps_as_passed(eps))
-    z1, z3 = oracle.matmul(xn, inp.W1), oracle.matmul(xn, inp.W3)
-    sig = 1.0 / (1.0 + np.exp(-z1))
-    silu, dsilu = z1 * sig, sig * (1.0 + z1 * (1.0 - sig))
-    t1, t3 = tol * (np.abs(z1) + 1.0), tol * (np.abs(z3) + 1.0)
-    y = silu * z3
-    return np.abs(dsilu * z3) * t1 + np.abs(silu) * t3 + t1 * t3 + 2.0 ** -8 * np.abs(y)
+# Where z1 < -87.3 the gate's factor e^-|z1| is below the normal fp32 range
+# (gradual underflow: fewer significant bits than bf16); every output there
+# is below 2^-100 (|z1 z3| < 1e6 on these inputs), so outputs whose exact
+# value is below 2^-100 are only required to be that small.
+GATE_TINY = 2.0 ** -100
 
 
-def assert_gated_within_bound(y_gpu: np.ndarray, y_ref: np.ndarray, inp: "synth.Inputs",
-                              eps: float, tol: float, what: str = ""):
-    """Gated outputs: within tol (|y| + 1) or within gated_bound."""
-    assert y_gpu.shape == y_ref.shape, (y_gpu.shape, y_ref.shape)
-    assert np.all(np.isfinite(y_gpu)), f"{what}: non-finite outputs"
-    err = np.abs(y_gpu - y_ref)
-    lim = np.maximum(tol * (np.abs(y_ref) + 1.0), gated_bound(inp, eps, tol))
-    bad = err > lim
-    assert not bad.any(), (f"{what}: {bad.sum()} outside the propagated bound, "
-                           f"worst {(err / lim).max():.3g}")
+def expected_gated_exact(y_ref: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """For exact-arithmetic inputs both products z1, z3 are exact, so the only
+    inexact steps of the gated output are the gate (exp, in fp32 on the GPU)
+    and the one rounding to bf16.  Returns the bf16 bit patterns of the
+    nearest-even rounding of y_ref (1 -+ 1e-6): where the two agree the
+    kernel must give exactly those bits; where y_ref lies within fp32 noise
+    of a rounding boundary either neighbour is correct."""
+    lo = synth.to_bf16_bits((y_ref * (1 - 1e-6)).astype(np.float32))
+    hi = synth.to_bf16_bits((y_ref * (1 + 1e-6)).astype(np.float32))
+    return lo, hi
 
 
 def expected_exact(y_ref: np.ndarray, dtype: str) -> np.ndarray:

@@ -361,3 +361,45 @@ def test_stream_split_workspace(lib):
     # the split form is planned only with a workspace; without one the call is valid
     assert tpa.plan(64, 8192, 4096, gated=True)[:2] == (0, "stream")
     assert tpa.plan(64, 8192, 4096, gated=True, with_workspace=False)[:2] == (0, "stream")
+
+
+def test_plain_entry_points_validate(lib):
+    """rmsnorm_matmul and rmsnorm_gated_mlp themselves (not the _ex forms):
+    every error in the documented order, and the empty no-op, with no HIP call."""
+    def mm(X=A[0], g=A[1], W=A[2], Y=A[3], eps=1e-6, M=16, N=64, K=64, dtype=BF16, ws=None,
+           ws_bytes=0):
+        return lib.rmsnorm_matmul(X, g, W, Y, eps, M, N, K, dtype, ws, ws_bytes, None)
+
+    def gm(X=A[0], g=A[1], W1=A[2], W3=A[4], Y=A[3], eps=1e-6, M=16, N=64, K=64, dtype=BF16,
+           ws=None, ws_bytes=0):
+        return lib.rmsnorm_gated_mlp(X, g, W1, W3, Y, eps, M, N, K, dtype, ws, ws_bytes, None)
+
+    for f in (mm, gm):
+        assert f(X=None) == NULL
+        assert f(g=None) == NULL
+        assert f(Y=None) == NULL
+        assert f(X=None, K=0) == NULL          # NULL is checked before the shape
+        assert f(K=0) == SHAPE
+        assert f(M=-1) == SHAPE
+        assert f(N=-1) == SHAPE
+        assert f(M=1 << 62, K=1 << 10) == SHAPE
+        assert f(K=0, eps=-1.0) == SHAPE        # shape before eps
+        assert f(eps=-1e-6) == EPS
+        assert f(eps=float("nan")) == EPS
+        assert f(eps=float("inf")) == EPS
+        assert f(eps=-1.0, dtype=7) == EPS     # eps before dtype
+        assert f(dtype=7) == DTYPE
+        assert f(Y=A[0]) == ALIAS              # Y on top of X
+        assert f(Y=A[0], dtype=7) == DTYPE     # dtype before alias
+        assert f(M=0) == OK and f(N=0) == OK   # empty: nothing launched
+        assert f(M=0, X=None, Y=None) == OK
+    assert gm(W3=None) == NULL
+    assert gm(Y=A[4]) == ALIAS                 # Y on top of W3
+    assert mm(W=None) == NULL
+    # the documented workspace sizes are what the plain calls accept
+    need = lib.rmm_workspace_bytes(BF16, 16, 6144, 4096, 0)
+    assert need > 0
+    assert mm(M=16, N=6144, K=4096, ws=A[5], ws_bytes=need - 1) == WORKSPACE
+    needg = lib.rmm_workspace_bytes(BF16, 16, 6144, 4096, 1)
+    assert needg > 0
+    assert gm(M=16, N=6144, K=4096, ws=A[5], ws_bytes=needg - 1) == WORKSPACE

@@ -15,8 +15,9 @@ import torch
 
 import synth
 import tensor_program_amd as tpa
-from tests.gpu_util import (assert_gated_within_bound, assert_within_tol, bits_of, expected_exact,
-                            from_device, run_gpu, run_oracle, to_device, tol_for)
+from tests.gpu_util import (GATE_TINY, assert_within_tol, bits_of, expected_exact,
+                            expected_gated_exact, from_device, run_gpu, run_oracle, to_device,
+                            tol_for)
 
 pytestmark = pytest.mark.gpu
 
@@ -146,11 +147,28 @@ def test_prefill_m4096_k4096_n4096_sampled(variant, require_gpu):
     _check_workload(wl.name, variant=variant, rows=_sample_rows(wl))
 
 
-@pytest.mark.parametrize("variant", ["auto", "stream", "generic"])
-def test_gated_m64_k4096_n14336_sampled_cols(variant, require_gpu):
+_GATED_REF = {}
+
+
+@pytest.mark.parametrize("variant", ["auto", "stream", "decode", "generic"])
+def test_gated_m64_k4096_n14336_full(variant, require_gpu):
+    """The gated workload on every one of its 64 x 14336 outputs, at the
+    elementwise bound (decode: 16-row launches are refused above 16 rows, so
+    it runs on the first 16 rows)."""
     wl = synth.get_workload("gated_m64_k4096_n14336")
-    cols = np.sort(np.random.default_rng(8).choice(wl.N, size=1024, replace=False))
-    _check_workload(wl.name, variant=variant, cols=cols)
+    inp = synth.make_inputs(wl)
+    if "ref" not in _GATED_REF:
+        _GATED_REF["ref"] = run_oracle(inp, wl.eps)
+    ref = _GATED_REF["ref"]
+    _log(f"workload {wl.name} variant {variant} (all outputs)")
+    if variant == "decode":
+        x16 = to_device(inp, "X")[:16].contiguous()
+        y = from_device(run_gpu(inp, wl.eps, variant=variant, x=x16))
+        ref = ref[:16]
+    else:
+        y = from_device(run_gpu(inp, wl.eps, variant=variant))
+    worst = assert_within_tol(y, ref, tol_for(wl.dtype), f"{wl.name}/{variant}")
+    _log(f"  worst err/tol {worst:.3f}")
 
 
 def test_large_m8192_k8192_n28672_sampled(require_gpu):
@@ -256,27 +274,26 @@ def test_errors_raise(require_gpu):
 @pytest.mark.parametrize("M", [1, 16, 40, 64, 65, 128, 256, 300])
 def test_gated_stream_shapes(M, require_gpu):
     """Gated stream variant on ragged shapes (above 64 rows: several 64-row
-    launches), against the oracle, held to the bound the per-product
-    tolerance gives through the gate."""
+    launches), against the oracle at the elementwise bound."""
     wl = synth.Workload("gated_stream", "bf16", M, 1032, 584, 1e-6, True, None)
     _log(f"gated stream M={M}")
     inp = synth.make_inputs(wl, seed=11)
     y = from_device(run_gpu(inp, wl.eps, variant="stream"))
-    assert_gated_within_bound(y, run_oracle(inp, wl.eps), inp, wl.eps, 1e-2, "gated_stream")
+    worst = assert_within_tol(y, run_oracle(inp, wl.eps), 1e-2, "gated_stream")
+    _log(f"  worst err/tol {worst:.3f}")
 
 
 @pytest.mark.parametrize("M,K,N", [(64, 264, 16392), (48, 264, 14336), (64, 136, 6136)])
 def test_gated_stream_wide(M, K, N, require_gpu):
     """Gated stream variant at wide N (257 strips with an 8-column last one,
-    224 strips, 96 strips with a 56-column last one), against the oracle.
-    Over a million outputs
-    at a short K, a few meet a large gate with a small linear term: they are
-    held to the bound the per-product tolerance gives through the gate."""
+    224 strips, 96 strips with a 56-column last one), against the oracle at
+    the elementwise bound."""
     wl = synth.Workload("gated_stream", "bf16", M, K, N, 1e-6, True, None)
     _log(f"gated stream wide M={M} K={K} N={N}")
     inp = synth.make_inputs(wl, seed=12)
     y = from_device(run_gpu(inp, wl.eps, variant="stream"))
-    assert_gated_within_bound(y, run_oracle(inp, wl.eps), inp, wl.eps, 1e-2, "gated_stream_wide")
+    worst = assert_within_tol(y, run_oracle(inp, wl.eps), 1e-2, "gated_stream_wide")
+    _log(f"  worst err/tol {worst:.3f}")
 
 
 def test_binding_workspace_per_layout_decode(require_gpu):
@@ -292,3 +309,37 @@ def test_binding_workspace_per_layout_decode(require_gpu):
     want = expected_exact(run_oracle(inp, 0.0), "bf16")
     mism = np.argwhere(bits_of(y) != want)
     assert mism.size == 0, f"{len(mism)} mismatches, first at {tuple(mism[0])}"
+
+
+# Gated exact-arithmetic cases: both products are exact, so every output must
+# be the one bf16 rounding of silu(z1) z3 (up to fp32 noise in the gate).
+GATED_EXACT = [
+    (16, 4096, 6144, "decode", 4),
+    (13, 1000, 520, "decode", 3),
+    (5, 136, 264, "decode", 1),
+    (64, 4096, 14336, "stream", 0),
+    (33, 1000, 520, "stream", 0),     # split form (9 strips)
+    (100, 264, 1032, "stream", 0),    # two 64-row launches
+    (64, 264, 16392, "stream", 0),    # 257 strips
+    (300, 200, 264, "stream", 0),
+    (13, 1000, 520, "generic", 0),
+]
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+@pytest.mark.parametrize("case", GATED_EXACT, ids=lambda c: "x".join(map(str, c)))
+def test_gated_exact(case, seed, require_gpu):
+    M, K, N, variant, splits = case
+    _log(f"gated exact {case} seed {seed}")
+    inp = synth.make_exact_inputs(M, K, N, "bf16", seed=seed, gated=True, row_pow2=(seed == 1))
+    yt = run_gpu(inp, 0.0, variant=variant, splits=splits)
+    y = bits_of(yt)
+    ref = run_oracle(inp, 0.0)
+    lo, hi = expected_gated_exact(ref)
+    for a in (y, lo, hi):  # the sign of a zero output is not compared
+        a[a == 0x8000] = 0
+    tiny = np.abs(ref) < GATE_TINY
+    assert np.all(np.abs(from_device(yt)[tiny]) < 2 * GATE_TINY)
+    bad = np.argwhere((y != lo) & (y != hi) & ~tiny)
+    assert bad.size == 0, f"{len(bad)} mismatches, first at {tuple(bad[0])}"
+    _log(f"  {int(tiny.sum())} outputs below 2^-100 of {tiny.size}")

@@ -42,16 +42,15 @@
  * Workspace.  The decode (split-K) variant combines partial k-sums across
  * workgroups through a caller-owned workspace.  `ws` may be NULL: the library
  * then picks a variant that needs none (correct, slower).  A non-NULL `ws` must
- * be zero-filled before its first use.  A call resets its arrival counters to
- * zero but leaves its partial sums in the rest of the workspace (every call
- * overwrites its slots before reading them), so the workspace can be reused
- * without clearing by later calls with the same layout -- the same entry
- * point, shape, dtype, variant and split count -- on the same stream.  A call
- * with another layout may keep its counters where the earlier call left
- * partial sums: zero-fill the workspace again first, or give each layout its
- * own.  One workspace must not be used
- * by two calls that may run at the same time.  ws_bytes below
- * rmm_workspace_bytes*() returns RMM_ERR_WORKSPACE.
+ * be zero-filled before its first use.  Every layout keeps its arrival
+ * counters in the workspace's first 64 KiB and its partial sums after that;
+ * a call resets its counters to zero and overwrites its partial-sum slots
+ * before reading them, so one workspace serves any sequence of calls -- any
+ * entry point, shape, dtype, variant or split count -- without clearing, as
+ * long as each call runs to completion (a call forced to a split count
+ * needing more than 16320 counters returns RMM_ERR_VARIANT).  One workspace
+ * must not be used by two calls that may run at the same time.  ws_bytes
+ * below rmm_workspace_bytes*() returns RMM_ERR_WORKSPACE.
  *
  * Errors.  Validation happens on the host before any HIP call, in this order:
  *   RMM_ERR_NULL      a NULL data pointer (when M*N > 0)

@@ -37,12 +37,11 @@ _DTYPES = {torch.float32: _binding.DTYPE_F32, torch.bfloat16: _binding.DTYPE_BF1
 class Workspace:
     """A zero-filled device workspace for the split-K and split-key combines.
 
-    A call resets its arrival counters but leaves its partial sums behind, so
-    a workspace serves any number of calls with the same layout (shape, dtype,
-    variant, split count) on one stream without clearing; a call with another
-    layout could find those partials where it keeps its counters, so it needs
-    a zero-filled workspace of its own (the functions below keep one per
-    layout).  Calls that may overlap (different streams) need different
+    Every call keeps its arrival counters in the first 64 KiB, resets them,
+    and overwrites its partial sums before reading them, so one workspace
+    serves any sequence of calls on one stream without clearing (the
+    functions below keep one per device and stream, grown when a call needs
+    more).  Calls that may overlap (different streams) need different
     workspaces.
     """
 
@@ -58,8 +57,10 @@ class Workspace:
 _workspaces: dict = {}
 
 
-def _workspace_for(device, stream_handle: int, nbytes: int, layout: tuple) -> Workspace:
-    key = (str(device), stream_handle, layout)
+def _workspace_for(device, stream_handle: int, nbytes: int) -> Workspace:
+    """The binding's workspace for one device and stream, grown (a new
+    zero-filled buffer) when a call needs more than it holds."""
+    key = (str(device), stream_handle)
     ws = _workspaces.get(key)
     if ws is None or ws.nbytes < nbytes:
         ws = Workspace(nbytes, device)
@@ -105,8 +106,7 @@ def _call(x, g, w1, w3, eps, out, variant, splits, workspace):
     stream = torch.cuda.current_stream(x.device).cuda_stream
     need = _binding.workspace_bytes(dtype, M, N, K, gated, variant, splits)
     if workspace is None and need > 0:
-        workspace = _workspace_for(x.device, stream, need,
-                                   ("fused", dtype, M, N, K, gated, variant, splits))
+        workspace = _workspace_for(x.device, stream, need)
     ws_ptr = workspace.ptr if workspace is not None else None
     ws_bytes = workspace.nbytes if workspace is not None else 0
     v = _binding.VARIANTS[variant]
@@ -171,7 +171,7 @@ def _plain(x, w1, w3, out, workspace):
     stream = torch.cuda.current_stream(x.device).cuda_stream
     need = _binding.workspace_bytes(dtype, M, N, K, gated)
     if workspace is None and need > 0:
-        workspace = _workspace_for(x.device, stream, need, ("plain", dtype, M, N, K, gated))
+        workspace = _workspace_for(x.device, stream, need)
     ws_ptr = workspace.ptr if workspace is not None else None
     ws_bytes = workspace.nbytes if workspace is not None else 0
     if gated:
@@ -217,8 +217,7 @@ def _lora(x, g, w, a, b, eps, out, variant, splits, workspace, norm):
     stream = torch.cuda.current_stream(x.device).cuda_stream
     need = _binding.lora_workspace_bytes(dtype, M, N, K, R, variant, splits)
     if workspace is None and need > 0:
-        workspace = _workspace_for(x.device, stream, need,
-                                   ("lora", dtype, M, N, K, R, variant, splits, norm))
+        workspace = _workspace_for(x.device, stream, need)
     ws_ptr = workspace.ptr if workspace is not None else None
     ws_bytes = workspace.nbytes if workspace is not None else 0
     if norm:
@@ -280,7 +279,7 @@ def qknorm_attention(q, k, v, gq, gk, eps: float, out=None, splits: int = 0,
     stream = torch.cuda.current_stream(q.device).cuda_stream
     need = _binding.attention_workspace_bytes(dtype, BH, S, D, splits)
     if workspace is None and need > 0:
-        workspace = _workspace_for(q.device, stream, need, ("attention", BH, S, D, splits))
+        workspace = _workspace_for(q.device, stream, need)
     ws_ptr = workspace.ptr if workspace is not None else None
     ws_bytes = workspace.nbytes if workspace is not None else 0
     _binding.check(load_library().qknorm_attention_ex(
@@ -289,10 +288,17 @@ def qknorm_attention(q, k, v, gq, gk, eps: float, out=None, splits: int = 0,
     return out
 
 
-def rmsnorm_matmul_chain(x0, g, w, eps: float, out=None, workspace: Workspace | None = None):
+def rmsnorm_matmul_chain(x0, g, w, eps: float, out=None, workspace: Workspace | None = None,
+                         check_wait: bool = True):
     """L fused layers in one persistent launch, x_{l+1} = RMSNorm(x_l; g[l], eps) @ w[l]
     (bf16; x0: [M, K], g: [L, K], w: [L, K, K], M <= 16).  Returns every layer's
-    output, [L, M, K] (out[l] = x_{l+1})."""
+    output, [L, M, K] (out[l] = x_{l+1}).
+
+    With check_wait (the default) the call synchronises the stream and reads
+    the workspace's flag word: if a layer wait gave up (a workgroup of the
+    grid was not resident, so the outputs are wrong) it clears the flag and
+    raises RmmError.  Pass check_wait=False inside HIP graph capture or to
+    keep the call asynchronous, and read chain_wait_flag() yourself."""
     _check_operands([x0, g, w], ["x0", "g", "w"])
     if x0.dim() != 2 or g.dim() != 2 or w.dim() != 3:
         raise ValueError("expected x0: [M, K], g: [L, K], w: [L, K, K]")
@@ -310,12 +316,20 @@ def rmsnorm_matmul_chain(x0, g, w, eps: float, out=None, workspace: Workspace | 
     stream = torch.cuda.current_stream(x0.device).cuda_stream
     need = _binding.chain_workspace_bytes(M, K, L)
     if workspace is None and need > 0:
-        workspace = _workspace_for(x0.device, stream, need, ("chain", M, K, L))
+        workspace = _workspace_for(x0.device, stream, need)
     ws_ptr = workspace.ptr if workspace is not None else None
     ws_bytes = workspace.nbytes if workspace is not None else 0
     _binding.check(load_library().rmsnorm_matmul_chain(
         x0.data_ptr(), g.data_ptr(), w.data_ptr(), out.data_ptr(), float(eps), M, K, L,
         _DTYPES[x0.dtype], ws_ptr, ws_bytes, stream))
+    if check_wait and workspace is not None:
+        torch.cuda.current_stream(x0.device).synchronize()
+        if chain_wait_flag(workspace, M, K, L):
+            off = _binding.chain_flag_offset(M, K, L)
+            workspace.tensor[off:off + 4].zero_()
+            raise RmmError(_binding.STATUS_CHAIN_WAIT,
+                           "rmsnorm_matmul_chain: a layer wait gave up (the grid was not "
+                           "resident on the GPU); the outputs of this call are wrong")
     return out
 
 

@@ -16,6 +16,9 @@ DTYPE_F32, DTYPE_BF16 = 0, 1
 VARIANTS = {"auto": 0, "generic": 1, "decode": 2, "prefill": 3, "stream": 4}
 VARIANT_NAMES = {v: k for k, v in VARIANTS.items()}
 STATUS_OK = 0
+# Not a status of the C ABI: raised by the Python front end when the layer
+# chain's flag word reports a wait that gave up.
+STATUS_CHAIN_WAIT = 100
 
 # Exported symbols of include/rmm.h.
 SYMBOLS = ("rmsnorm_matmul", "rmsnorm_gated_mlp", "rmsnorm_matmul_ex", "rmsnorm_gated_mlp_ex",

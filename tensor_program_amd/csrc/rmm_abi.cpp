@@ -134,6 +134,7 @@ rmm_status plan_shape(int64_t M, int64_t N, int64_t K, rmm_dtype dtype, int gate
     if (s > 1 && !have_ws) return RMM_ERR_WORKSPACE;  // a forced split count needs one
     rmm_decode32_plan(M, N, K, s, &out->d32);
     if (out->d32.ws_bytes > (size_t)INT32_MAX) return RMM_ERR_VARIANT;  // 32-bit offsets
+    if (out->d32.splits > 1 && out->d32.tiles > kWsMaxCounters) return RMM_ERR_VARIANT;
     out->splits = out->d32.splits;
     out->ws_bytes = out->d32.ws_bytes;
   } else if (v == RMM_VARIANT_DECODE) {
@@ -143,6 +144,8 @@ rmm_status plan_shape(int64_t M, int64_t N, int64_t K, rmm_dtype dtype, int gate
     if (s > 1 && !have_ws) return RMM_ERR_WORKSPACE;  // a forced split count needs one
     rmm_decode_plan(M < kDecodeMaxM ? M : kDecodeMaxM, N, K, gated, s, R, &out->dec);
     if (out->dec.ws_bytes > (size_t)INT32_MAX) return RMM_ERR_VARIANT;  // 32-bit offsets
+    // one arrival counter per tile, all in the workspace's counter region
+    if (out->dec.splits > 1 && out->dec.tiles > kWsMaxCounters) return RMM_ERR_VARIANT;
     out->splits = out->dec.splits;
     out->ws_bytes = out->dec.ws_bytes;
   } else if (v == RMM_VARIANT_PREFILL) {
@@ -307,6 +310,8 @@ rmm_status attn_plan_call(const void* Q, const void* K, const void* V, const voi
   rmm_attention_plan(BH, S, D, s, plan);
   if ((int64_t)plan->chunks * BH > (int64_t)INT32_MAX || plan->ws_bytes > (size_t)INT32_MAX)
     return RMM_ERR_VARIANT;
+  // one arrival counter per batch-head, all in the workspace's counter region
+  if (plan->chunks > 1 && BH > kWsMaxCounters) return RMM_ERR_VARIANT;
   // 7. workspace
   if (ws && ws_bytes < plan->ws_bytes) return RMM_ERR_WORKSPACE;
   return RMM_OK;

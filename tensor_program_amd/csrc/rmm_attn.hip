@@ -271,7 +271,7 @@ void rmm_attention_plan(int64_t BH, int64_t S, int64_t D, int splits, AttnPlan* 
   p->kchunk = kc;
   p->chunks = (int)((S + kc - 1) / kc);
   p->ws_cnt_off = 0;
-  p->ws_part_off = at_align256(sizeof(unsigned) * (size_t)BH);
+  p->ws_part_off = kWsCounterBytes;
   p->ws_bytes = p->chunks > 1
                     ? p->ws_part_off + at_align256(sizeof(float) * (size_t)BH * p->chunks * (D + 2))
                     : 0;

@@ -327,8 +327,8 @@ int rmm_chain_plan(int64_t M, int64_t K, int64_t L, ChainPlan* p) {
   p->kchunk = (kgran + s - 1) / s * 128;
   p->splits = (int)((K + p->kchunk - 1) / p->kchunk);
   p->ws_cnt_off = 0;
-  p->ws_done_off = chain_align256(sizeof(unsigned) * (size_t)p->tiles);
-  p->ws_ssq_off = p->ws_done_off + 256;
+  p->ws_done_off = kWsChainBlockOff;
+  p->ws_ssq_off = kWsCounterBytes;
   p->ws_part_off = p->ws_ssq_off + chain_align256(sizeof(float) * (size_t)p->splits * p->tiles * 16);
   p->ws_bytes = p->ws_part_off + chain_align256((size_t)p->splits * p->tiles * 8 * 64 * 16);
   // The 256-byte counter block holds the call-wide count, the flag and one

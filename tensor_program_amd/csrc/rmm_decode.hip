@@ -443,7 +443,7 @@ void rmm_decode_plan(int64_t M, int64_t N, int64_t K, int gated, int splits, int
   p->wv = (nw * p->mb == 1 && p->tiles * p->splits <= 256) ? 8 : 4;
   const size_t E = ((size_t)nw * p->mb * 8 + (size_t)p->mb * p->lr) * 64 * 4;  // floats per partial
   p->ws_cnt_off = 0;
-  p->ws_ssq_off = align256(sizeof(unsigned) * (size_t)p->tiles);
+  p->ws_ssq_off = kWsCounterBytes;
   p->ws_part_off = p->ws_ssq_off + align256(sizeof(float) * (size_t)p->splits * p->tiles * p->mb * 16);
   p->ws_bytes = p->splits > 1 ? p->ws_part_off + align256(sizeof(float) * (size_t)p->splits * p->tiles * E) : 0;
 }

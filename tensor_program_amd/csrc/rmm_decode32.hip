@@ -190,7 +190,7 @@ void rmm_decode32_plan(int64_t M, int64_t N, int64_t K, int splits, Decode32Plan
   p->krange = ((per + p->kc - 1) / p->kc) * p->kc;
   p->splits = (int)((K + p->krange - 1) / p->krange);
   p->ws_cnt_off = 0;
-  p->ws_ssq_off = align256_32(sizeof(unsigned) * (size_t)p->tiles);
+  p->ws_ssq_off = kWsCounterBytes;
   p->ws_part_off = p->ws_ssq_off + align256_32(sizeof(float) * (size_t)p->splits * p->tiles * p->mr);
   p->ws_bytes = p->splits > 1
                     ? p->ws_part_off + align256_32(sizeof(float) * (size_t)p->splits * p->tiles * p->mr * 32)

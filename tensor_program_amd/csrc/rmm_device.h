@@ -93,6 +93,18 @@ struct RmmArgs {
 
 hipError_t rmm_launch_generic(const RmmArgs& a, bool bf16);
 
+// Every workspace layout starts with the same 64 KiB counter region: the
+// arrival counters of any call are its first words (at most
+// kWsMaxCounters of them; a call that would need more runs without a
+// cross-workgroup combine or is refused), the layer chain keeps its
+// call-wide counts and flag word in the region's last 256 bytes, and the
+// partial sums of every layout start after the region.  Each call leaves
+// its counters at zero, so one zero-filled workspace serves any sequence of
+// calls, whatever their shapes and variants.
+constexpr size_t kWsCounterBytes = 64 * 1024;
+constexpr int64_t kWsMaxCounters = (int64_t)((kWsCounterBytes - 256) / 4);
+constexpr size_t kWsChainBlockOff = kWsCounterBytes - 256;
+
 struct DecodePlan {
   int mb;          // 16-row blocks (1..2)
   int wv;          // waves per workgroup (4 or 8); a step covers 32 wv rows of K

@@ -533,7 +533,7 @@ void rmm_stream_plan(int64_t N, int64_t K, int gated, int target, bool have_ws, 
   p->split = have_ws && 2 * strips <= target;
   p->grid = p->split ? (int)(T < target ? T : target) : (int)strips;
   p->ws_cnt_off = 0;
-  p->ws_part_off = st_align256(sizeof(unsigned) * (size_t)strips);
+  p->ws_part_off = kWsCounterBytes;
   p->ws_ssq_off = p->ws_part_off + (size_t)2 * target * nw * ST_BM * ST_BN * sizeof(float);
   // Sized for `target` workgroups whatever the grid, so the size depends on
   // the shape and the weight count only.

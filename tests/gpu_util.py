@@ -34,16 +34,19 @@ def bits_of(y: torch.Tensor) -> np.ndarray:
     return y.detach().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def run_gpu(inp: "synth.Inputs", eps: float, variant="auto", splits=0, out=None, x=None):
+def run_gpu(inp: "synth.Inputs", eps: float, variant="auto", splits=0, out=None, x=None,
+            workspace=None):
     dev = "cuda"
     X = to_device(inp, "X", dev) if x is None else x
     g = to_device(inp, "g", dev)
     W1 = to_device(inp, "W1", dev)
     if inp.wl.gated:
         W3 = to_device(inp, "W3", dev)
-        y = tpa.rmsnorm_gated_mlp(X, g, W1, W3, eps, out=out, variant=variant, splits=splits)
+        y = tpa.rmsnorm_gated_mlp(X, g, W1, W3, eps, out=out, variant=variant, splits=splits,
+                                  workspace=workspace)
     else:
-        y = tpa.rmsnorm_matmul(X, g, W1, eps, out=out, variant=variant, splits=splits)
+        y = tpa.rmsnorm_matmul(X, g, W1, eps, out=out, variant=variant, splits=splits,
+                               workspace=workspace)
     torch.cuda.synchronize()
     return y
 

@@ -17,6 +17,8 @@ HEADER = os.path.join(ROOT, "include", "rmm.h")
 
 OK, NULL, SHAPE, EPS, DTYPE, ALIAS, WORKSPACE, HIP, VARIANT = range(9)
 BF16, F32 = _binding.DTYPE_BF16, _binding.DTYPE_F32
+# Every workspace starts with a 64 KiB region holding the arrival counters.
+CNT = 64 * 1024
 # Fake, distinct, 16-byte aligned device addresses: never dereferenced here.
 A = [(1 << 40) + i * (1 << 34) for i in range(8)]
 
@@ -222,7 +224,7 @@ def test_attention_plans(lib):
     assert tpa.plan_attention(1, 100000, 64)[1] > 1
     assert lib.rmm_attention_workspace_bytes(BF16, 256, 2048, 128, 0) == 0
     nb = lib.rmm_attention_workspace_bytes(BF16, 256, 2048, 128, 4)
-    assert nb == 256 * 4 + 256 * 4 * 130 * 4                  # counters, then (o, max, sum)
+    assert nb == CNT + 256 * 4 * 130 * 4                  # counters, then (o, max, sum)
     assert lib.rmm_attention_workspace_bytes(BF16, 256, 2048, 128, 1) == 0
     assert lib.rmm_attention_workspace_bytes(F32, 256, 2048, 128, 0) == 0
 
@@ -297,9 +299,9 @@ def test_workspace_sizes(lib):
     assert lib.rmm_workspace_bytes(BF16, 16, 6144, 4096, 0) == \
         lib.rmm_workspace_bytes_ex(BF16, 16, 6144, 4096, 0, 0, 0) > 0
     assert lib.rmm_workspace_bytes_ex(BF16, 16, 6144, 4096, 0, 2, 1) == 0
-    # fp32 decode at 8 x 1024 x 1024: 32 tiles x 8 splits; counters (one 256-byte
-    # region), 8-row sums of squares, 8 x 32 fp32 partials per tile and split
-    assert lib.rmm_workspace_bytes(F32, 8, 1024, 1024, 0) == 256 + 8 * 32 * 8 * 4 + 8 * 32 * 8 * 32 * 4
+    # fp32 decode at 8 x 1024 x 1024: 32 tiles x 8 splits; the counter region,
+    # 8-row sums of squares, 8 x 32 fp32 partials per tile and split
+    assert lib.rmm_workspace_bytes(F32, 8, 1024, 1024, 0) == CNT + 8 * 32 * 8 * 4 + 8 * 32 * 8 * 32 * 4
     assert lib.rmm_workspace_bytes(F32, 8, 1024, 1024, 1) == 0   # gated fp32: generic kernel
     assert lib.rmm_workspace_bytes(BF16, 16, 6144, 0, 0) == 0  # invalid -> 0
 
@@ -326,16 +328,17 @@ def test_chain_validation_and_workspace(lib):
     need = lib.rmm_chain_workspace_bytes(16, 1024, 4)
     assert need > 0 and chain(ws_bytes=need - 1) == WORKSPACE
     assert chain(M=0, ws=None) == OK              # nothing to do, nothing launched
-    # 8 tiles x 8 chunks of 128: counters, done + flag words, 16-row sums, 8 x 64 floatx4 partials
-    assert need == 256 + 256 + 8 * 8 * 16 * 4 + 8 * 8 * 8 * 64 * 16
-    assert lib.rmm_chain_flag_offset(16, 1024, 4) == 256 + 4
+    # 8 tiles x 8 chunks of 128: the counter region (tile counters first, the
+    # done + flag words in its last 256 bytes), 16-row sums, 8 x 64 floatx4 partials
+    assert need == CNT + 8 * 8 * 16 * 4 + 8 * 8 * 8 * 64 * 16
+    assert lib.rmm_chain_flag_offset(16, 1024, 4) == CNT - 256 + 4
     assert lib.rmm_chain_workspace_bytes(16, 8192, 4) == 0
     assert lib.rmm_chain_workspace_bytes(17, 1024, 4) == 0
     # The largest accepted tiling, K = 4480: 35 tiles x 7 chunks of 640.  The
-    # 256-byte counter block (call-wide count, flag, one count per tile) holds
+    # 256-byte chain block (call-wide count, flag, one count per tile) holds
     # 2 + 35 words.
     need = lib.rmm_chain_workspace_bytes(16, 4480, 2)
-    assert need == 256 + 256 + 15872 + 7 * 35 * 8 * 64 * 16  # row sums: 15,680 bytes, 256-aligned
+    assert need == CNT + 15872 + 7 * 35 * 8 * 64 * 16  # row sums: 15,680 bytes, 256-aligned
     assert lib.rmm_chain_workspace_bytes(16, 4608, 2) == 0  # 36 tiles need 8 chunks: 288 workgroups
 
 
@@ -352,10 +355,10 @@ def test_stream_split_workspace(lib):
     STREAM = 4
     # gated 64 x 4096 x 8192: 128 strips, two weights
     assert lib.rmm_workspace_bytes(BF16, 64, 8192, 4096, 1) == \
-        512 + 2 * 256 * 2 * 64 * 64 * 4 + 2 * 256 * 64 * 4
+        CNT + 2 * 256 * 2 * 64 * 64 * 4 + 2 * 256 * 64 * 4
     # plain, forced stream, 96 strips: one weight
     assert lib.rmm_workspace_bytes_ex(BF16, 16, 6144, 4096, 0, STREAM, 0) == \
-        512 + 2 * 256 * 64 * 64 * 4 + 2 * 256 * 64 * 4
+        CNT + 2 * 256 * 64 * 64 * 4 + 2 * 256 * 64 * 4
     assert lib.rmm_workspace_bytes(BF16, 64, 8200, 4096, 1) == 0       # 129 strips
     assert lib.rmm_workspace_bytes(BF16, 64, 14336, 4096, 1) == 0      # 224 strips
     # the split form is planned only with a workspace; without one the call is valid
@@ -403,3 +406,16 @@ def test_plain_entry_points_validate(lib):
     needg = lib.rmm_workspace_bytes(BF16, 16, 6144, 4096, 1)
     assert needg > 0
     assert gm(M=16, N=6144, K=4096, ws=A[5], ws_bytes=needg - 1) == WORKSPACE
+
+
+def test_forced_splits_beyond_the_counter_region(lib):
+    """A split form needs one arrival counter per tile in the workspace's
+    64 KiB counter region (16320 of them): forcing splits on more tiles is
+    refused, the automatic choice runs without a combine there."""
+    DECODE = 2
+    N = 16321 * 128
+    assert lib.rmm_workspace_bytes_ex(BF16, 16, N, 256, 0, DECODE, 2) == 0
+    assert call(lib, M=16, N=N, K=256, variant=DECODE, splits=2, ws=A[5], ws_bytes=1 << 40) == VARIANT
+    assert tpa.plan(16, N, 256, variant="decode")[1:] == ("decode", 1)
+    N = 16320 * 128
+    assert lib.rmm_workspace_bytes_ex(BF16, 16, N, 256, 0, DECODE, 2) > 0

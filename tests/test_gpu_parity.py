@@ -296,19 +296,35 @@ def test_gated_stream_wide(M, K, N, require_gpu):
     _log(f"  worst err/tol {worst:.3f}")
 
 
-def test_binding_workspace_per_layout_decode(require_gpu):
-    # Regression: a decode call with 8 column tiles leaves its row-sum
-    # partials at byte 256 onward of the cached workspace; a later call with
-    # 72 tiles keeps its arrival counters in bytes 0..287, so it needs a
-    # workspace of its own layout.  The sequence, then exact parity.
-    first = synth.make_exact_inputs(16, 4096, 1024, "bf16", seed=2)
-    run_gpu(first, 0.0, variant="decode", splits=4)
-    inp = synth.make_exact_inputs(16, 1024, 9216, "bf16", seed=3)
-    assert tpa.plan(16, 9216, 1024, variant="decode", splits=2)[1:] == ("decode", 2)
-    y = run_gpu(inp, 0.0, variant="decode", splits=2)
-    want = expected_exact(run_oracle(inp, 0.0), "bf16")
-    mism = np.argwhere(bits_of(y) != want)
-    assert mism.size == 0, f"{len(mism)} mismatches, first at {tuple(mism[0])}"
+def test_one_workspace_for_every_layout(require_gpu):
+    """One zero-filled workspace passed to a sequence of calls with different
+    layouts (tile counts, variants, split counts, weight counts, dtypes):
+    every call's exact result is right, so no call reads what another left
+    in the workspace as its arrival counters.  (The second call has 72
+    column tiles: in a layout whose counters were not in a fixed region, its
+    counters would sit where the first call left its row-sum partials.)"""
+    ws = tpa.Workspace(64 << 20, "cuda")
+    seq = [(16, 4096, 1024, "bf16", False, "decode", 4), (16, 1024, 9216, "bf16", False, "decode", 2),
+           (33, 1000, 520, "bf16", False, "stream", 0), (8, 1024, 1024, "f32", False, "decode", 0),
+           (16, 4096, 6144, "bf16", False, "decode", 8), (13, 1000, 520, "bf16", True, "decode", 3),
+           (16, 4096, 1024, "bf16", False, "decode", 4)]
+    for i, (M, K, N, dtype, gated, variant, splits) in enumerate(seq):
+        _log(f"shared workspace call {i}: {M}x{K}x{N} {dtype} gated={gated} {variant} {splits}")
+        inp = synth.make_exact_inputs(M, K, N, dtype, seed=40 + i, gated=gated)
+        y = run_gpu(inp, 0.0, variant=variant, splits=splits, workspace=ws)
+        ref = run_oracle(inp, 0.0)
+        if gated:
+            lo, hi = expected_gated_exact(ref)
+            got = bits_of(y)
+            for a in (got, lo, hi):
+                a[a == 0x8000] = 0
+            tiny = np.abs(ref) < GATE_TINY
+            assert not np.any((got != lo) & (got != hi) & ~tiny), f"call {i}"
+        else:
+            got = bits_of(y) if dtype == "bf16" else y.cpu().numpy()
+            assert np.array_equal(got, expected_exact(ref, dtype)), f"call {i}"
+    # every call left the counters at zero
+    assert torch.count_nonzero(ws.tensor[:64 * 1024]) == 0
 
 
 # Gated exact-arithmetic cases: both products are exact, so every output must

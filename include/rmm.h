@@ -92,7 +92,8 @@ typedef enum {
   RMM_ERR_ALIAS = 5,
   RMM_ERR_WORKSPACE = 6,
   RMM_ERR_HIP = 7,
-  RMM_ERR_VARIANT = 8
+  RMM_ERR_VARIANT = 8,
+  RMM_ERR_SCRATCH = 9
 } rmm_status;
 
 /* Kernel variants.  AUTO picks by shape (gated M <= 16 takes DECODE only
@@ -131,6 +132,22 @@ typedef enum {
 rmm_status rmsnorm_matmul(const void* X, const void* g, const void* W, void* Y, float eps,
                           int64_t M, int64_t N, int64_t K, rmm_dtype dtype, void* ws,
                           size_t ws_bytes, hipStream_t stream);
+
+/* rmsnorm_matmul for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments and result as rmsnorm_matmul without the workspace: the split-K
+ * partial sums go to a fixed 16 MiB device array inside the library (one per
+ * GPU, held until the process ends; its device address is looked up once per
+ * device on the first call there).  Validation and errors as rmsnorm_matmul,
+ * plus RMM_ERR_SCRATCH when the call would need more than 16 MiB of scratch
+ * (never for M <= 32, nor for the stream variant's split form); nothing is
+ * allocated or freed.  Every call on one GPU shares that array: calls that
+ * may overlap on one GPU (different streams or threads) race and must be
+ * serialised by the caller.  A call leaves the array's counters zeroed for
+ * the next, whatever its shape. */
+rmm_status rmsnorm_matmul_noalloc(const void* X, const void* g, const void* W, void* Y, float eps,
+                                  int64_t M, int64_t N, int64_t K, rmm_dtype dtype,
+                                  hipStream_t stream);
 
 /* Y = silu(RMSNorm(X) W1) * (RMSNorm(X) W3); W1 and W3 are both K x N and the
  * 1/RMS scale is applied to both products before the SiLU. */

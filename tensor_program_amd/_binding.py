@@ -28,7 +28,8 @@ SYMBOLS = ("rmsnorm_matmul", "rmsnorm_gated_mlp", "rmsnorm_matmul_ex", "rmsnorm_
            "rmm_lora_workspace_bytes", "rmm_plan_lora", "qknorm_attention",
            "qknorm_attention_ex", "rmm_attention_workspace_bytes", "rmm_plan_attention",
            "rmsnorm_matmul_chain", "rmm_chain_workspace_bytes", "rmm_chain_flag_offset",
-           "rmm_probe_hbm_read", "rmm_probe_mfma_bf16", "rmm_probe_mfma_flops")
+           "rmm_probe_hbm_read", "rmm_probe_mfma_bf16", "rmm_probe_mfma_flops",
+           "rmsnorm_matmul_noalloc")
 LORA_MAX_RANK = 64
 
 _lib = None
@@ -53,6 +54,7 @@ def load_library(path: str = LIB_PATH):
                              ctypes.c_size_t)
     lib.rmsnorm_matmul.argtypes = [vp, vp, vp, vp, f32, i64, i64, i64, i32, vp, sz, vp]
     lib.rmsnorm_gated_mlp.argtypes = [vp, vp, vp, vp, vp, f32, i64, i64, i64, i32, vp, sz, vp]
+    lib.rmsnorm_matmul_noalloc.argtypes = [vp, vp, vp, vp, f32, i64, i64, i64, i32, vp]
     lib.rmsnorm_matmul_ex.argtypes = [vp, vp, vp, vp, f32, i64, i64, i64, i32, i32, i32, vp, sz,
                                       vp]
     lib.rmsnorm_gated_mlp_ex.argtypes = [vp, vp, vp, vp, vp, f32, i64, i64, i64, i32, i32, i32,
@@ -65,6 +67,7 @@ def load_library(path: str = LIB_PATH):
                                     i32, vp, sz, vp]
     lib.rmm_lora_matmul.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp, sz, vp]
     for f in ("rmsnorm_matmul", "rmsnorm_gated_mlp", "rmsnorm_matmul_ex", "rmsnorm_gated_mlp_ex",
+              "rmsnorm_matmul_noalloc",
               "rmm_rmsnorm", "rmm_matmul", "rmm_gated_matmul", "rmsnorm_lora", "rmsnorm_lora_ex",
               "rmm_lora_matmul"):
         getattr(lib, f).restype = i32

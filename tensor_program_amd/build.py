@@ -22,7 +22,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "librmm.so")
 SOURCES = ["rmm_abi.cpp", "rmm_generic.hip", "rmm_decode.hip", "rmm_decode32.hip", "rmm_prefill.hip",
            "rmm_stream.hip", "rmm_norm.hip", "rmm_attn.hip",
-           "rmm_chain.hip", "rmm_probe.hip"]
+           "rmm_chain.hip", "rmm_probe.hip", "rmm_noalloc.hip"]
 ARCH = "gfx950"
 
 

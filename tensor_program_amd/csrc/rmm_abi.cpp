@@ -12,6 +12,12 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 
+}  // namespace
+
+void rmm_set_last_hip_error(int err) { g_last_hip_error = err; }
+
+namespace {
+
 struct Plan {
   rmm_variant variant;
   int splits;
@@ -548,6 +554,9 @@ const char* rmm_status_string(rmm_status s) {
     case RMM_ERR_WORKSPACE: return "RMM_ERR_WORKSPACE: workspace too small";
     case RMM_ERR_HIP: return "RMM_ERR_HIP: kernel launch failed";
     case RMM_ERR_VARIANT: return "RMM_ERR_VARIANT: variant/splits cannot run this call";
+    case RMM_ERR_SCRATCH:
+      return "RMM_ERR_SCRATCH: the call needs more than the 16 MiB device scratch array of "
+             "rmsnorm_matmul_noalloc (use rmsnorm_matmul with a workspace)";
   }
   return "unknown rmm_status";
 }

@@ -93,6 +93,9 @@ struct RmmArgs {
 
 hipError_t rmm_launch_generic(const RmmArgs& a, bool bf16);
 
+// Records the hipError_t behind an RMM_ERR_HIP (rmm_last_hip_error).
+void rmm_set_last_hip_error(int err);
+
 // Every workspace layout starts with the same 64 KiB counter region: the
 // arrival counters of any call are its first words (at most
 // kWsMaxCounters of them; a call that would need more runs without a

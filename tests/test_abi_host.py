@@ -419,3 +419,23 @@ def test_forced_splits_beyond_the_counter_region(lib):
     assert tpa.plan(16, N, 256, variant="decode")[1:] == ("decode", 1)
     N = 16320 * 128
     assert lib.rmm_workspace_bytes_ex(BF16, 16, N, 256, 0, DECODE, 2) > 0
+
+
+def test_noalloc_validates_and_fits_its_scratch(lib):
+    """rmsnorm_matmul_noalloc validates like rmsnorm_matmul (no HIP call on
+    these failures), and every plain call's workspace fits its 16 MiB array."""
+    def na(X=A[0], g=A[1], W=A[2], Y=A[3], eps=1e-6, M=16, N=64, K=64, dtype=BF16):
+        return lib.rmsnorm_matmul_noalloc(X, g, W, Y, eps, M, N, K, dtype, None)
+    assert na(X=None) == NULL
+    assert na(K=0) == SHAPE
+    assert na(eps=-1.0) == EPS
+    assert na(dtype=7) == DTYPE
+    assert na(Y=A[0]) == ALIAS
+    assert na(M=0) == OK and na(N=0, W=None) == OK and na(N=0) == OK  # empty: NULL allowed
+    worst = 0
+    for dtype in (BF16, F32):
+        for M in (1, 8, 16, 17, 32, 33, 64, 100, 128, 200, 256):
+            for K in (64, 1024, 4096, 8192):
+                for N in (8, 128, 1024, 4096, 6144, 8192, 16384, 28672):
+                    worst = max(worst, lib.rmm_workspace_bytes(dtype, M, N, K, 0))
+    assert 0 < worst <= 16 << 20, worst

@@ -347,6 +347,12 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_kernel(
     PF_WAIT_VMCNT(XL);
     __syncthreads();
   }
+  // The last iteration's X loads (past K: zeros) are still in flight and
+  // their registers are dead to the compiler; the tied waits keep those
+  // registers reserved until the loads have landed, so nothing after the
+  // loop can be placed in them and then overwritten.
+  pf_wait_a<0, GL>(sa);
+  pf_wait_a<0, GL>(sb);
   PF_WAIT_VMCNT(0);
 
   // Row sums of squares: the 8 lanes tid&7 = 0..7 share rows (tid>>3) + 64 i.

@@ -248,12 +248,12 @@ __global__ __launch_bounds__(ST_THREADS, 1) void stream_kernel(
   const int bG = l >> 4, bi = l & 15;
   const int b_k = 8 * (bG >> 1) + (bi >> 2), b_n = cb * 32 + 16 * (bG & 1) + 4 * (bi & 3);
   const int b_off = b_k * 128 + (((b_n >> 3) ^ (2 * (b_k & 3))) << 4) + ((b_n & 7) << 1);
-  floatx16 acc[2], acc0[2];
+  floatx16 acc[2], acc0[2], accl[2];
   float ss0 = 0.f;
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[rb][e] = acc0[rb][e] = 0.f;
+    for (int e = 0; e < 16; ++e) acc[rb][e] = acc0[rb][e] = accl[rb][e] = 0.f;
 
   // Steps 0 .. AHEAD-1 in flight, step 0 formed, before the loop.
   // Iteration kt issues step kt+AHEAD into the slot last read in iteration
@@ -301,11 +301,9 @@ __global__ __launch_bounds__(ST_THREADS, 1) void stream_kernel(
           u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(b_lds + b_off + (16 * s + 4) * 128)));
       bv[i] = u32x4{lo[0], lo[1], hi[0], hi[1]};
     }
-    if (seg_end) {
-      ss0 = ss;
-      ss = 0.f;
-    }
-    if (kt + 1 < n) form(kt + 1);
+    // The MFMAs go out first, the forming of the next step (VALU and LDS)
+    // runs in their shadow.  The low parts accumulate separately (two more
+    // independent accumulator chains per wave).
 #pragma unroll
     for (int i = 0; i < SUBS; ++i)
 #pragma unroll
@@ -318,18 +316,27 @@ __global__ __launch_bounds__(ST_THREADS, 1) void stream_kernel(
       for (int i = 0; i < SUBS; ++i)
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
-          acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, avl[i][rb]),
-                                                            __builtin_bit_cast(bf16x8, bv[i]),
-                                                            acc[rb], 0, 0, 0);
+          accl[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, avl[i][rb]),
+                                                             __builtin_bit_cast(bf16x8, bv[i]),
+                                                             accl[rb], 0, 0, 0);
     }
+    if (seg_end) {
+      ss0 = ss;
+      ss = 0.f;
+    }
+    if (kt + 1 < n) form(kt + 1);
     if (seg_end) {
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
-        acc0[rb] = acc[rb];
+        acc0[rb] = SPLIT ? acc[rb] + accl[rb] : acc[rb];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[rb][e] = 0.f;
+        for (int e = 0; e < 16; ++e) acc[rb][e] = accl[rb][e] = 0.f;
       }
     }
+  }
+  if (SPLIT) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) acc[rb] += accl[rb];
   }
   ST_WAIT_VMCNT(0);
 

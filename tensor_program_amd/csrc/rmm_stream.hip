@@ -20,17 +20,18 @@
 //     chunk c ^ ((r >> 1) & 7): the 16 rows one quarter-wave reads in a
 //     fragment load fall on 16 distinct 16-byte bank groups (a plain
 //     c ^ (r & 7) puts rows r and r + 8 on the same banks).
-//   * one step ahead of its use, the workgroup turns the X slot into the
-//     matrix operand in place: each thread takes 8 consecutive k of one row,
-//     forms X*g in fp32 (bf16 dot2 with one lane of g zeroed: an exact
-//     product) rounded once to bf16, and adds X^2 to its row's sum of squares.
-//   * each wave multiplies a 64-row x 32-column block of one weight over a
-//     k-half (gated) or a k-quarter (plain) of every step with
-//     v_mfma_f32_32x32x16_bf16; B fragments come from ds_read_b64_tr_b16
-//     (gfx950's transposing LDS read): lane i of each 16-lane group receives
-//     4 consecutive k of column i.  Each W element is read from LDS once.
-//   * epilogue through LDS: the partial k-sums are added, Y = acc / RMS,
-//     gated Y = silu(acc1/RMS) * acc3/RMS.
+//   * wave w takes row block w & 1 (32 rows) over k-quarter w >> 1 of every
+//     step, for every 32-column block of the strip (2 per weight), with
+//     v_mfma_f32_32x32x16_bf16.  Each X element of a step is read by one
+//     lane, which forms the matrix operand in registers: X*g in fp32 (bf16
+//     dot2 with one lane of g zeroed: an exact product) rounded once to bf16
+//     -- for two weights split into two exact bf16 parts, both multiplied --
+//     and X^2 added to its row's partial sum of squares.  B fragments come
+//     from ds_read_b64_tr_b16 (gfx950's transposing LDS read): lane i of each
+//     16-lane group receives 4 consecutive k of column i.  Each W element is
+//     read from LDS by the two row-block waves of its k-quarter.
+//   * epilogue through LDS: the k-quarters' partial sums are added, Y =
+//     acc / RMS, gated Y = silu(acc1/RMS) * acc3/RMS.
 #include "rmm_device.h"
 
 namespace rmm {
@@ -47,14 +48,11 @@ constexpr uint32_t kStOutOfRange = 0x80000000u;
 // workgroups sharing a strip run on different XCDs (no shared L2).
 constexpr int kStCoherent = 16;
 
-// Ring depth per weight count.  The load latency is covered with 2 steps
-// ahead already (what bounds the kernel is the bytes each CU takes in); with
-// two weights 3 steps ahead (5 slots) measured ~1% faster than 4 or 2.
+// Ring depth per weight count: RING - 1 steps are in flight while one is
+// multiplied.
 template <int NW>
 struct StCfg {
-  static constexpr int RING = NW == 2 ? 5 : 8;
-  static constexpr int AHEAD = RING - 2;  // steps issued ahead of the one multiplied
-  static constexpr int SUBS = NW == 2 ? 2 : 1;  // 16-deep sub-steps per wave per step
+  static constexpr int RING = NW == 2 ? 6 : 8;
 };
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -64,6 +62,13 @@ typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 __device__ __forceinline__ bf16x2 st_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2, v); }
+
+// a.lo * b.lo + a.hi * b.hi in fp32.  Written with the builtin, not inline
+// asm: the compiler tracks the hazard of a VALU write to a register an
+// in-flight MFMA still reads only for the instructions it emits itself.
+__device__ __forceinline__ float st_dot2_bf16(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_fdot2_f32_bf16(st_bf16x2(a), st_bf16x2(b), 0.0f, false);
+}
 
 // X slot swizzle: physical 16-byte chunk of logical chunk c in row r is
 // c ^ st_xswz(r).  Rows 32 apart share it (fragment row blocks).
@@ -96,9 +101,8 @@ __device__ __forceinline__ void st_lds_load16(uint32_t lds_addr, uint32_t voff, 
 // The gated form carries the operand X*g exactly as two bf16 parts
 // (split_bf16x2): the gate multiplies one product's error by the other
 // product, so a single rounding of X*g would not keep every output within
-// the elementwise bound the plain product meets.  The high part replaces X
-// in its ring slot; the low part goes to a two-slot ring of its own (the
-// step being multiplied and the step being formed).
+// the elementwise bound the plain product meets.  Both parts multiply the
+// same W fragment into the same accumulator.
 template <int NW>
 struct StSplitOp {
   static constexpr bool value = NW == 2;
@@ -108,16 +112,16 @@ template <int NW>
 struct StSmem {
   char w[StCfg<NW>::RING][NW][ST_W_BYTES];
   char x[StCfg<NW>::RING][ST_X_BYTES];
-  char xl[StSplitOp<NW>::value ? 2 : 1][StSplitOp<NW>::value ? ST_X_BYTES : 16];
   char g[StCfg<NW>::RING][ST_G_BYTES];
+  float ssp[4][ST_BM];  // row sums of squares per k-quarter
   float ss[ST_BM];
-  float inv[ST_BM];
 };
-// The epilogue reuses the W and X rings (contiguous) for 4 fp32 partial
-// blocks of 64 x 64.
-constexpr int ST_RED_BYTES = 4 * ST_BM * ST_BN * 4;
-static_assert(sizeof(StSmem<1>::w) + sizeof(StSmem<1>::x) >= ST_RED_BYTES, "ring too small");
-static_assert(sizeof(StSmem<2>::w) + sizeof(StSmem<2>::x) >= ST_RED_BYTES, "ring too small");
+// The epilogue reuses the W and X rings (contiguous) for 2 fp32 partial
+// sets of NW blocks of 64 x 64.
+template <int NW>
+constexpr int st_red_bytes() { return 2 * NW * ST_BM * ST_BN * 4; }
+static_assert(sizeof(StSmem<1>::w) + sizeof(StSmem<1>::x) >= st_red_bytes<1>(), "ring too small");
+static_assert(sizeof(StSmem<2>::w) + sizeof(StSmem<2>::x) >= st_red_bytes<2>(), "ring too small");
 static_assert(sizeof(StSmem<2>) <= 160 * 1024 && sizeof(StSmem<1>) <= 160 * 1024, "LDS");
 
 // Workspace of the split (stream-K) form: which global steps a workgroup
@@ -138,16 +142,18 @@ __device__ __forceinline__ int st_owner(int64_t s, int64_t T, int64_t P) {
   return (int)(((s + 1) * P - 1) / T);
 }
 
-template <int NW, bool SK>
+template <int NW, bool SK, bool NORM>
 __global__ __launch_bounds__(ST_THREADS, 1) void stream_kernel(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ g, const bf16_t* __restrict__ W1,
     const bf16_t* __restrict__ W3, bf16_t* __restrict__ Y, float eps, int M, int64_t N,
-    int64_t K, int norm, StSplit sp) {
-  constexpr int RING = StCfg<NW>::RING, AHEAD = StCfg<NW>::AHEAD, SUBS = StCfg<NW>::SUBS;
-  constexpr bool SPLIT = StSplitOp<NW>::value;
+    int64_t K, StSplit sp) {
+  constexpr int RING = StCfg<NW>::RING;
+  // Without the gain the operand is X itself: one exact part.
+  constexpr bool SPLIT = StSplitOp<NW>::value && NORM;
   __shared__ __attribute__((aligned(1024))) StSmem<NW> sm;
   __shared__ int last2[2];
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int tid = threadIdx.x, l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int nk = (int)((K + ST_BK - 1) / ST_BK);
   // Local steps 0 .. n-1 of this workgroup: strip strip0 from k-step kt0
   // on, continuing into strip strip0 + 1 past its last k-step.
@@ -164,227 +170,253 @@ __global__ __launch_bounds__(ST_THREADS, 1) void stream_kernel(
   // a batched combine).
   const int nb = kt0 + n > nk ? kt0 + n - nk : 0;
 
-  // Per-lane source offsets of one step (relative to the step's resource).
-  // W: wave w fills rows 8w .. 8w+7 of a slot; lane l lands at byte 16 l;
-  // the strip's column offset is added per step.
-  uint32_t w_lane;
-  int w_col;
+  // Per-lane source offsets of one step (relative to the step's resource,
+  // which starts at the step's first row and the strip's first column).
+  // W: wave w fills rows 8w .. 8w+7 of a slot; lane l lands at byte 16 l.
+  // Columns past N read zeros; the check depends on the strip only, so it
+  // is made once for each of the (at most two) strips of the range.
+  uint32_t w_off0, w_off1;
   {
     const int kl = 8 * w + (l >> 3);
     const int c = (l & 7) ^ (2 * (kl & 3));
-    w_col = 8 * c;
-    w_lane = (uint32_t)((kl * N + w_col) * 2);
+    const uint32_t lane = (uint32_t)((kl * N + 8 * c) * 2);
+    w_off0 = (int64_t)strip0 * ST_BN + 8 * c < N ? lane : kStOutOfRange;
+    w_off1 = (int64_t)(strip0 + 1) * ST_BN + 8 * c < N ? lane : kStOutOfRange;
   }
   // X: wave w fills rows 8w .. 8w+7; lane l -> row 8w + l/8, chunk
-  // (l&7) ^ st_xswz(row); the k-range check happens per step.
+  // (l&7) ^ st_xswz(row); the k-range check only matters on a last,
+  // partial k-step.
   const int x_row = 8 * w + (l >> 3);
-  const int x_kc = (l & 7) ^ st_xswz(x_row);
-  const uint32_t x_off = x_row < M ? (uint32_t)(((int64_t)x_row * K + 8 * x_kc) * 2) : kStOutOfRange;
+  const int x_k = 8 * ((l & 7) ^ st_xswz(x_row));
+  const uint32_t x_off = x_row < M ? (uint32_t)(((int64_t)x_row * K + x_k) * 2) : kStOutOfRange;
   const uint32_t lds_w = (uint32_t)(uintptr_t)(lds_char*)&sm.w[0][0][0] + w * 1024;
   const uint32_t lds_x = (uint32_t)(uintptr_t)(lds_char*)&sm.x[0][0] + w * 1024;
   const uint32_t lds_g = (uint32_t)(uintptr_t)(lds_char*)&sm.g[0][0];
   const bf16_t* Wp[2] = {W1, NW == 2 ? W3 : W1};
 
-  // Issue every transfer of one step: NW W blocks, one X block and, from
-  // lanes 0..7 of wave 0 only, the step's g slice (every wave reads it after
-  // the barrier) -- NW + 1 vector-memory instructions per wave, NW + 2 for
-  // wave 0.
-  auto issue_step = [&](int step) {
+  // Issue every transfer of one step into ring slot `slot`: NW W blocks,
+  // one X block and, from lanes 0..7 of wave 0 only, the step's g slice
+  // (every wave reads it after the barrier) -- NW + 1 vector-memory
+  // instructions per wave, NW + 2 for wave 0.  Everything but the per-lane
+  // offsets is wave-uniform (scalar registers).
+  auto issue_step = [&](int step, int slot) {
     // Local step -> (strip, k-step); past the range: k-step nk (zeros).
-    const int strip = step < nb ? strip0 + 1 : strip0;
-    const int kt = step < nb ? step : (step < n ? kt0 + step - nb : nk);
+    const bool second = step < nb;
+    const int strip = second ? strip0 + 1 : strip0;
+    const int kt = second ? step : (step < n ? kt0 + step - nb : nk);
     const int64_t k0 = (int64_t)kt * ST_BK;
     const int64_t rows = K - k0 > 0 ? K - k0 : 0;
-    const int slot = step % RING;
     const int64_t ns = (int64_t)strip * ST_BN;
-    const uint32_t w_off = ns + w_col < N ? w_lane + (uint32_t)(ns * 2) : kStOutOfRange;
+    const uint32_t w_off = second ? w_off1 : w_off0;
 #pragma unroll
     for (int v = 0; v < NW; ++v) {
-      const i32x4 rs = st_rsrc(Wp[v] + k0 * N, (uint32_t)(rows * N * 2));
+      const i32x4 rs = st_rsrc(Wp[v] + k0 * N + ns, rows > 0 ? (uint32_t)((rows * N - ns) * 2) : 0u);
       st_lds_load16(lds_w + (uint32_t)((slot * NW + v) * ST_W_BYTES), w_off, rs);
     }
     const i32x4 xs = st_rsrc(X + k0, (uint32_t)(((int64_t)M * K - (k0 < (int64_t)M * K ? k0 : 0)) * 2));
-    st_lds_load16(lds_x + (uint32_t)(slot * ST_X_BYTES), k0 + 8 * x_kc < K ? x_off : kStOutOfRange, xs);
-    const i32x4 gs = st_rsrc(g + k0, (uint32_t)(rows * 2));
-    if (w == 0 && l < 8) st_lds_load16(lds_g + (uint32_t)(slot * ST_G_BYTES), (uint32_t)(16 * l), gs);
+    st_lds_load16(lds_x + (uint32_t)(slot * ST_X_BYTES), k0 + ST_BK <= K || k0 + x_k < K ? x_off : kStOutOfRange,
+                  xs);
+    if (NORM) {
+      const i32x4 gs = st_rsrc(g + k0, (uint32_t)(rows * 2));
+      if (w == 0 && l < 8) st_lds_load16(lds_g + (uint32_t)(slot * ST_G_BYTES), (uint32_t)(16 * l), gs);
+    }
   };
 
-  // Operand forming: thread -> row tid/8, logical k-chunk tid%8 of a step.
-  // The X slot is overwritten in place with bf16(X * g); the row's sum of
-  // squares accumulates in the thread (its row never changes).
-  const int f_row = tid >> 3, f_c = tid & 7;
-  const int f_off = f_row * 128 + ((f_c ^ st_xswz(f_row)) << 4);
-  float ss = 0.f;
-  auto form = [&](int step) {
-    const int slot = step % RING;
-    char* xp = &sm.x[slot][f_off];
-    const u32x4 xv = *(const u32x4*)xp;
-    const u32x4 gl = *(const u32x4*)&sm.g[slot][16 * f_c];
-    const u32x4 gv = norm ? gl : u32x4{kBf16OnePair, kBf16OnePair, kBf16OnePair, kBf16OnePair};
-    u32x4 av, al;
+  // Wave roles: wave w multiplies row block rb = w & 1 (32 rows) over
+  // k-quarter kq = w >> 1 of every step (16 k), for all 64 columns of each
+  // weight (2 NW column blocks of 32).  Every X element of a step is thus
+  // read by exactly one lane, which forms its operand in registers: lane l
+  // holds row 32 rb + l % 32, k 16 kq + 8 (l / 32) .. +7 of the step, the
+  // A-fragment layout of v_mfma_f32_32x32x16_bf16; it multiplies by g in
+  // fp32 (bf16 dot2 with one lane of g zeroed: an exact product), rounds once
+  // to bf16 (gated: splits into two exact parts) and adds X^2 to its row's
+  // partial sum of squares.
+  const int rb = w & 1, kq = w >> 1;
+  const int a_row = rb * 32 + (l & 31);
+  const int a_kc = 2 * kq + (l >> 5);
+  const int a_off = a_row * 128 + ((a_kc ^ st_xswz(a_row)) << 4);
+  const int g_off = 16 * a_kc;
+  // B fragments: lane i of each 16-lane group receives 4 consecutive k of
+  // one column (ds_read_b64_tr_b16); column half h of a weight's 64.
+  const int bG = l >> 4, bi = l & 15;
+  const int b_k = 8 * (bG >> 1) + (bi >> 2) + 16 * kq;
+  int b_off[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int b_n = h * 32 + 16 * (bG & 1) + 4 * (bi & 3);
+    b_off[h] = b_k * 128 + (((b_n >> 3) ^ (2 * (b_k & 3))) << 4) + ((b_n & 7) << 1);
+  }
+  constexpr int NB = 2 * NW;  // column blocks per wave
+  floatx16 acc[NB], acc0[NB];
+  float ss = 0.f, ss0 = 0.f;
+#pragma unroll
+  for (int c = 0; c < NB; ++c)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[c][e] = acc0[c][e] = 0.f;
+
+  // The operands of one step in registers: the W fragments of every column
+  // block, and X*g formed from the raw X chunk and g slice.  Slot offsets
+  // are compile-time constants in the unrolled loop below (immediate LDS
+  // offsets), so reading a step costs no address arithmetic.
+  auto read_b = [&](int slot, u32x4 (&bv)[NB]) {
+#pragma unroll
+    for (int c = 0; c < NB; ++c) {
+      const lds_char* bp = (const lds_char*)&sm.w[slot][c >> 1][b_off[c & 1]];
+      const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)bp));
+      const u32x2 hi =
+          __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(bp + 4 * 128)));
+      bv[c] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    }
+  };
+  auto read_xg = [&](int slot, u32x4& xv, u32x4& gl) {
+    xv = *(const u32x4*)&sm.x[slot][a_off];
+    if (NORM) gl = *(const u32x4*)&sm.g[slot][g_off];
+  };
+  auto form_regs = [&](const u32x4& xv, const u32x4& gl, u32x4& ah, u32x4& al) {
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
       const bf16x2 x = st_bf16x2(xv[d]);
-      const float p0 = __builtin_amdgcn_fdot2_f32_bf16(x, st_bf16x2(gv[d] & 0xffffu), 0.0f, false);
-      const float p1 = __builtin_amdgcn_fdot2_f32_bf16(x, st_bf16x2(gv[d] & 0xffff0000u), 0.0f, false);
-      if (SPLIT) {
-        const u32x2 hl = split_bf16x2(p0, p1);
-        av[d] = hl[0];
-        al[d] = hl[1];
-      } else
-        av[d] = pack_bf16x2(p0, p1);
+      if (NORM) {
+        const float p0 = st_dot2_bf16(xv[d], gl[d] & 0xffffu);
+        const float p1 = st_dot2_bf16(xv[d], gl[d] & 0xffff0000u);
+        if (SPLIT) {
+          const u32x2 hl = split_bf16x2(p0, p1);
+          ah[d] = hl[0];
+          al[d] = hl[1];
+        } else {
+          ah[d] = pack_bf16x2(p0, p1);
+        }
+      } else {
+        ah[d] = xv[d];
+      }
       ss = __builtin_amdgcn_fdot2_f32_bf16(x, x, ss, false);
     }
-    *(u32x4*)xp = av;
-    if (SPLIT) *(u32x4*)&sm.xl[step & 1][f_off] = al;
   };
 
-  // Wave roles: partial set w>>1 (gated: weight set>>1, k-half set&1;
-  // plain: k-quarter set), column block w&1, both 32-row blocks.
-  const int set = w >> 1, cb = w & 1;
-  const int wsel = NW == 2 ? (set >> 1) : 0;
-  const int s_first = NW == 2 ? 2 * (set & 1) : set;
-  const int a_lo = l & 31;  // fragment row within a 32-row block
-  const int bG = l >> 4, bi = l & 15;
-  const int b_k = 8 * (bG >> 1) + (bi >> 2), b_n = cb * 32 + 16 * (bG & 1) + 4 * (bi & 3);
-  const int b_off = b_k * 128 + (((b_n >> 3) ^ (2 * (b_k & 3))) << 4) + ((b_n & 7) << 1);
-  floatx16 acc[2], acc0[2], accl[2];
-  float ss0 = 0.f;
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc[rb][e] = acc0[rb][e] = accl[rb][e] = 0.f;
-
-  // Steps 0 .. AHEAD-1 in flight, step 0 formed, before the loop.
-  // Iteration kt issues step kt+AHEAD into the slot last read in iteration
-  // kt-2 (the barrier of iteration kt-1 orders that), waits until only the
-  // AHEAD-1 newest steps may be outstanding (step kt+1 has landed for this
-  // wave); after the barrier (every wave's part of step kt+1 has landed and
-  // iteration kt-1 is finished everywhere) it reads the operands of step kt
-  // (formed in iteration kt-1), forms step kt+1 and multiplies step kt.
-  // Steps past the last one read zeros (range checks).
-  // Wait until this wave's part of the step AHEAD-1 issues back has landed.
-  auto wait_landed = [&] {
-    if (w == 0)
-      ST_WAIT_VMCNT((AHEAD - 1) * (NW + 2));
-    else
-      ST_WAIT_VMCNT((AHEAD - 1) * (NW + 1));
-  };
-  for (int st = 0; st < AHEAD; ++st) issue_step(st);
-  wait_landed();
+  // Software pipeline over a ring of RING slots, all of them filled before
+  // the loop.  Iteration kt holds step kt's operands in registers; it waits
+  // until only the RING-2 newest steps may be outstanding (step kt+1 has
+  // landed for this wave); after the barrier every wave's part of step kt+1
+  // has landed and iteration kt-1 -- which read step kt into registers --
+  // is finished everywhere, so step kt's slot is free.  The wave then reads
+  // step kt+1's W fragments and raw X chunk and g slice, issues step
+  // kt+RING into step kt's slot, and multiplies step kt while it forms step
+  // kt+1: the MFMAs need nothing the new reads bring, and the forming
+  // arithmetic is placed between them (a wave issues in order).  Steps past
+  // the last one read zeros (range checks).
+  for (int st = 0; st < RING; ++st) issue_step(st, st);
+  if (w == 0)
+    ST_WAIT_VMCNT((RING - 1) * (NW + (NORM ? 2 : 1)));
+  else
+    ST_WAIT_VMCNT((RING - 1) * (NW + 1));
   __syncthreads();
-  form(0);
-  for (int kt = 0; kt < n; ++kt) {
-    issue_step(kt + AHEAD);
-    wait_landed();
-    __syncthreads();
-    const int slot = kt % RING;
-    // Split form: local step kt+1 starts the range's second strip.
-    const bool seg_end = SK && kt + 1 == nb;
-    const char* x_lds = &sm.x[slot][0];
-    const char* xl_lds = &sm.xl[SPLIT ? (kt & 1) : 0][0];
-    const lds_char* b_lds = (const lds_char*)&sm.w[slot][wsel][0];
-    u32x4 av[SUBS][2], avl[SUBS][2], bv[SUBS];
-#pragma unroll
-    for (int i = 0; i < SUBS; ++i) {
-      const int s = s_first + i;
-      const int kc = 2 * s + (l >> 5);
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const int ao = (rb * 32 + a_lo) * 128 + ((kc ^ st_xswz(a_lo)) << 4);
-        av[i][rb] = *(const u32x4*)(x_lds + ao);
-        if (SPLIT) avl[i][rb] = *(const u32x4*)(xl_lds + ao);
-      }
-      const u32x2 lo = __builtin_bit_cast(
-          u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(b_lds + b_off + 16 * s * 128)));
-      const u32x2 hi = __builtin_bit_cast(
-          u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(b_lds + b_off + (16 * s + 4) * 128)));
-      bv[i] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-    }
-    // The MFMAs go out first, the forming of the next step (VALU and LDS)
-    // runs in their shadow.  The low parts accumulate separately (two more
-    // independent accumulator chains per wave).
-#pragma unroll
-    for (int i = 0; i < SUBS; ++i)
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-        acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[i][rb]),
-                                                          __builtin_bit_cast(bf16x8, bv[i]),
-                                                          acc[rb], 0, 0, 0);
-    if (SPLIT) {
-#pragma unroll
-      for (int i = 0; i < SUBS; ++i)
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-          accl[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, avl[i][rb]),
-                                                             __builtin_bit_cast(bf16x8, bv[i]),
-                                                             accl[rb], 0, 0, 0);
-    }
-    if (seg_end) {
-      ss0 = ss;
-      ss = 0.f;
-    }
-    if (kt + 1 < n) form(kt + 1);
-    if (seg_end) {
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        acc0[rb] = SPLIT ? acc[rb] + accl[rb] : acc[rb];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[rb][e] = accl[rb][e] = 0.f;
-      }
-    }
+  u32x4 ah, al, bv[NB];
+  {
+    u32x4 xv, gl;
+    read_xg(0, xv, gl);
+    read_b(0, bv);
+    form_regs(xv, gl, ah, al);
   }
-  if (SPLIT) {
+  constexpr int NMFMA = NB * (SPLIT ? 2 : 1);
+  for (int kb = 0; kb < n; kb += RING) {
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) acc[rb] += accl[rb];
+    for (int u = 0; u < RING; ++u) {
+      const int kt = kb + u;
+      if (kt >= n) break;
+      if (w == 0)
+        ST_WAIT_VMCNT((RING - 2) * (NW + (NORM ? 2 : 1)));
+      else
+        ST_WAIT_VMCNT((RING - 2) * (NW + 1));
+      __syncthreads();
+      const int s1 = u + 1 < RING ? u + 1 : 0;
+      u32x4 xv, gl, bn[NB];
+      read_xg(s1, xv, gl);
+      read_b(s1, bn);
+      issue_step(kt + RING, u);
+      // Split form: local step kt+1 starts the range's second strip.
+      const bool seg_end = SK && kt + 1 == nb;
+      if (SK) {
+        ss0 = seg_end ? ss : ss0;
+        ss = seg_end ? 0.f : ss;
+      }
+#pragma unroll
+      for (int c = 0; c < NB; ++c)
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ah),
+                                                         __builtin_bit_cast(bf16x8, bv[c]), acc[c], 0, 0, 0);
+      if (SPLIT) {
+#pragma unroll
+        for (int c = 0; c < NB; ++c)
+          acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, al),
+                                                           __builtin_bit_cast(bf16x8, bv[c]), acc[c], 0, 0, 0);
+      }
+      form_regs(xv, gl, ah, al);
+#pragma unroll
+      for (int c = 0; c < NB; ++c) bv[c] = bn[c];
+      // Each MFMA followed by a share of the forming arithmetic.
+#pragma unroll
+      for (int q = 0; q < NMFMA; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, (48 + NMFMA - 1) / NMFMA, 0);
+      }
+      if (seg_end) {
+#pragma unroll
+        for (int c = 0; c < NB; ++c) {
+          acc0[c] = acc[c];
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[c][e] = 0.f;
+        }
+      }
+    }
   }
   ST_WAIT_VMCNT(0);
 
-  // Tail, per segment (one, or two in the split form): the waves' partial
-  // sets to LDS as [set][row][col] fp32 (the rings are free now), then for
-  // thread -> row tid>>3, columns 8 (tid&7) .. +7 the sums of the sets: the
-  // two k-halves of each weight (gated) or the four k-quarters (plain).
+  // Tail, per segment (one, or two in the split form): the row sums of
+  // squares and the waves' partial sums to LDS (the rings are free now),
+  // k-quarters 0 and 1 as two sets [set][weight][row][col] fp32, then
+  // k-quarters 2 and 3 added into them; thread -> row tid>>3, columns
+  // 8 (tid&7) .. +7 then adds the two sets.
   float* red = (float*)&sm.w[0][0][0];
   const int orow = tid >> 3, oc = 8 * (tid & 7);
-  auto stage_sets = [&](const floatx16 (&a)[2], float ssv) {
-    // Row sums of squares: the 8 threads of a row hold disjoint k-chunks.
-    ssv += __shfl_xor(ssv, 1);
-    ssv += __shfl_xor(ssv, 2);
-    ssv += __shfl_xor(ssv, 4);
+  auto stage_sets = [&](const floatx16 (&a)[NB], float ssv) {
+    ssv += __shfl_xor(ssv, 32);  // the two k-chunks of the row in this wave
     __syncthreads();  // the rings (or the previous segment's sets) are no longer read
-    if (f_c == 0) sm.ss[f_row] = ssv;
+    if (l < 32) sm.ssp[kq][a_row] = ssv;
     // 32x32 layout: lane l holds column l%32 and, for register 4 jj + r,
-    // row 8 jj + 4 (l/32) + r.
+    // row 8 jj + 4 (l/32) + r of the block.
+    auto red_at = [&](int c, int jj, int r) -> float& {
+      const int row = rb * 32 + 8 * jj + 4 * (l >> 5) + r, col = (c & 1) * 32 + (l & 31);
+      return red[(((kq & 1) * NW + (c >> 1)) * ST_BM + row) * ST_BN + col];
+    };
+    if (kq < 2) {
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+      for (int c = 0; c < NB; ++c)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
+        for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = rb * 32 + 8 * jj + 4 * (l >> 5) + r, col = cb * 32 + (l & 31);
-          red[(set * ST_BM + row) * ST_BN + col] = a[rb][4 * jj + r];
-        }
+          for (int r = 0; r < 4; ++r) red_at(c, jj, r) = a[c][4 * jj + r];
+    }
+    __syncthreads();
+    if (kq >= 2) {
+#pragma unroll
+      for (int c = 0; c < NB; ++c)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) red_at(c, jj, r) += a[c][4 * jj + r];
+    }
+    if (tid < ST_BM) sm.ss[tid] = (sm.ssp[0][tid] + sm.ssp[1][tid]) + (sm.ssp[2][tid] + sm.ssp[3][tid]);
     __syncthreads();
   };
   auto sum_sets = [&](float (&z)[NW][8]) {
-    float p[4][8];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const floatx4* src = (const floatx4*)(red + (q * ST_BM + orow) * ST_BN + oc);
-      const floatx4 u = src[0], v = src[1];
+    for (int v = 0; v < NW; ++v) {
+      const floatx4* s0 = (const floatx4*)(red + ((0 * NW + v) * ST_BM + orow) * ST_BN + oc);
+      const floatx4* s1 = (const floatx4*)(red + ((1 * NW + v) * ST_BM + orow) * ST_BN + oc);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        p[q][e] = u[e];
-        p[q][4 + e] = v[e];
-      }
-    }
+      for (int h = 0; h < 2; ++h) {
+        const floatx4 u = s0[h], q = s1[h];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      if (NW == 2) {
-        z[0][c] = p[0][c] + p[1][c];
-        z[NW - 1][c] = p[2][c] + p[3][c];
-      } else {
-        z[0][c] = (p[0][c] + p[1][c]) + (p[2][c] + p[3][c]);
+        for (int e = 0; e < 4; ++e) z[v][4 * h + e] = u[e] + q[e];
       }
     }
   };
@@ -392,7 +424,7 @@ __global__ __launch_bounds__(ST_THREADS, 1) void stream_kernel(
   auto store_y = [&](const float (&z)[NW][8], float ssr, int strip) {
     const int64_t n = (int64_t)strip * ST_BN + oc;
     if (orow < M && n < N) {
-      const float inv = norm ? inv_rms(ssr, K, eps) : 1.0f;
+      const float inv = NORM ? inv_rms(ssr, K, eps) : 1.0f;
       u32x4 out;
 #pragma unroll
       for (int c = 0; c < 8; c += 2) {
@@ -562,17 +594,19 @@ hipError_t rmm_launch_stream(const RmmArgs& a, const StreamPlan& p, void* ws) {
                *w3 = (const bf16_t*)a.W3;
   bf16_t* y = (bf16_t*)a.Y;
   const int m = (int)a.M;
-  if (a.gated && p.split)
-    hipLaunchKernelGGL((stream_kernel<2, true>), grid, block, 0, a.stream, x, g, w1, w3, y, a.eps, m, a.N,
-                       a.K, a.norm, sp);
-  else if (a.gated)
-    hipLaunchKernelGGL((stream_kernel<2, false>), grid, block, 0, a.stream, x, g, w1, w3, y, a.eps, m,
-                       a.N, a.K, a.norm, sp);
-  else if (p.split)
-    hipLaunchKernelGGL((stream_kernel<1, true>), grid, block, 0, a.stream, x, g, w1, w3, y, a.eps, m, a.N,
-                       a.K, a.norm, sp);
-  else
-    hipLaunchKernelGGL((stream_kernel<1, false>), grid, block, 0, a.stream, x, g, w1, w3, y, a.eps, m,
-                       a.N, a.K, a.norm, sp);
+  auto launch = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, block, 0, a.stream, x, g, w1, w3, y, a.eps, m, a.N, a.K, sp);
+  };
+  if (a.norm) {
+    if (a.gated)
+      p.split ? launch(stream_kernel<2, true, true>) : launch(stream_kernel<2, false, true>);
+    else
+      p.split ? launch(stream_kernel<1, true, true>) : launch(stream_kernel<1, false, true>);
+  } else {
+    if (a.gated)
+      p.split ? launch(stream_kernel<2, true, false>) : launch(stream_kernel<2, false, false>);
+    else
+      p.split ? launch(stream_kernel<1, true, false>) : launch(stream_kernel<1, false, false>);
+  }
   return hipGetLastError();
 }

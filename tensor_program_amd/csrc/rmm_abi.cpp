@@ -111,8 +111,9 @@ rmm_status plan_shape(int64_t M, int64_t N, int64_t K, rmm_dtype dtype, int gate
   // Gated calls have no prefill tile: any M runs as 64-row stream launches
   // (K = 4096, N = 14336, M = 256: 191 us against 3860 us for the generic
   // kernel's vector products).
-  const bool stream_ok =
-      fast_layout && R == 0 && (gated || M <= kStreamMaxM || (M <= 256 && N <= 4096));
+  const bool stream_ok = fast_layout && R == 0 &&
+                         (gated || M <= kStreamMaxM || (M <= 256 && N <= 4096)) &&
+                         rmm_stream_fits(M < kStreamRows ? M : kStreamRows, N, K);
   rmm_variant v = variant;
   if (v == RMM_VARIANT_AUTO) {
     if (R > 0)

@@ -167,6 +167,9 @@ struct StreamPlan {
 };
 void rmm_stream_plan(int64_t N, int64_t K, int gated, int target, bool have_ws, StreamPlan* p);
 hipError_t rmm_launch_stream(const RmmArgs& a, const StreamPlan& p, void* ws);
+// Whether a 64-row chunk of an M x K by K x N product fits the stream kernel's
+// 32-bit buffer offsets.
+bool rmm_stream_fits(int64_t M, int64_t N, int64_t K);
 
 // QKNorm + attention, one query per batch-head (bf16, D = 64 or 128).
 struct AttnArgs {

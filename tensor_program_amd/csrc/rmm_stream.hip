@@ -43,7 +43,12 @@ constexpr int ST_BK = 64;                        // k per step
 constexpr int ST_W_BYTES = ST_BK * ST_BN * 2;    // 8 KB per weight per slot
 constexpr int ST_X_BYTES = ST_BM * ST_BK * 2;    // 8 KB per slot
 constexpr int ST_G_BYTES = 128;                  // the g slice of a step
-constexpr uint32_t kStOutOfRange = 0x80000000u;
+// Out-of-range lane offset and the scalar offset of the steps past a range.
+// Every buffer is at most 2^30 bytes and a W step at most 2^25 bytes
+// (checked by the launcher), so a lane offset plus a scalar offset never
+// wraps 32 bits, and either constant in the sum puts it past the buffer.
+constexpr uint32_t kStOutOfRange = 0x40000000u;
+constexpr uint32_t kStPastRange = 0x40000000u;
 // Split-form partial sums: device-scope coherent (SC1) accesses, since the
 // workgroups sharing a strip run on different XCDs (no shared L2).
 constexpr int kStCoherent = 16;
@@ -86,13 +91,26 @@ __device__ __forceinline__ i32x4 st_rsrc(const void* base, uint32_t bytes) {
 }
 
 // 16 bytes per active lane from memory straight into LDS (lane l at
-// lds_addr + 16 l).  Inline asm keeps the compiler from serialising it
-// against the other loads in flight; the k-loop waits with explicit vmcnt.
-__device__ __forceinline__ void st_lds_load16(uint32_t lds_addr, uint32_t voff, i32x4 rsrc) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+// lds_addr + 16 l), from byte voff + soff of the buffer; the range check
+// covers voff + soff, so an offset at or past the buffer's size reads
+// zeros.  Inline asm keeps the compiler from serialising it against the
+// other loads in flight; the k-loop waits with explicit vmcnt.
+__device__ __forceinline__ void st_lds_load16(uint32_t lds_addr, uint32_t voff, i32x4 rsrc, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
-               : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(rsrc)
-               : "memory");
+               : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory", "m0");
+}
+// The same from lanes 0..7 only (128 bytes): the exec mask is narrowed and
+// restored inside the statement.
+__device__ __forceinline__ void st_lds_load16_x8(uint32_t lds_addr, uint32_t voff, i32x4 rsrc, uint32_t soff) {
+  uint64_t saved;
+  asm volatile(
+      "s_mov_b64 %0, exec\n\ts_mov_b64 exec, 0xff\n\ts_mov_b32 m0, %1\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\ts_mov_b64 exec, %0"
+      : "=&s"(saved)
+      : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(rsrc), "s"(soff)
+      : "memory", "m0");
 }
 
 #define ST_WAIT_VMCNT(n) \
@@ -112,7 +130,7 @@ template <int NW>
 struct StSmem {
   char w[StCfg<NW>::RING][NW][ST_W_BYTES];
   char x[StCfg<NW>::RING][ST_X_BYTES];
-  char g[StCfg<NW>::RING][ST_G_BYTES];
+  char g[StCfg<NW>::RING][8][ST_G_BYTES];  // one copy of the g slice per wave
   float ssp[4][ST_BM];  // row sums of squares per k-quarter
   float ss[ST_BM];
 };
@@ -170,11 +188,18 @@ __global__ __launch_bounds__(ST_THREADS, 1) void stream_kernel(
   // a batched combine).
   const int nb = kt0 + n > nk ? kt0 + n - nk : 0;
 
-  // Per-lane source offsets of one step (relative to the step's resource,
-  // which starts at the step's first row and the strip's first column).
-  // W: wave w fills rows 8w .. 8w+7 of a slot; lane l lands at byte 16 l.
-  // Columns past N read zeros; the check depends on the strip only, so it
-  // is made once for each of the (at most two) strips of the range.
+  // Buffer resources (fixed) and per-lane offsets; the step's position is a
+  // scalar byte offset (soffset) added to every lane's.
+  //   W (K x N): soffset (k0 N + n0) 2 for the step's first row and the
+  //   strip's first column n0; wave w fills rows 8w .. 8w+7 of a slot, lane
+  //   l lands at byte 16 l.  Rows past K fall past the buffer (zeros);
+  //   columns past N get an out-of-range lane offset, checked once for each
+  //   of the (at most two) strips of the range.
+  //   X (M x K) and g (K): soffset 2 k0.  Lanes whose k is past K, or whose
+  //   row is past M, get an out-of-range lane offset (a row's k past K
+  //   would otherwise read the next row).
+  // Past the last step of the range the offsets are moved out of range, so
+  // the steps issued there read zeros.
   uint32_t w_off0, w_off1;
   {
     const int kl = 8 * w + (l >> 3);
@@ -183,43 +208,46 @@ __global__ __launch_bounds__(ST_THREADS, 1) void stream_kernel(
     w_off0 = (int64_t)strip0 * ST_BN + 8 * c < N ? lane : kStOutOfRange;
     w_off1 = (int64_t)(strip0 + 1) * ST_BN + 8 * c < N ? lane : kStOutOfRange;
   }
-  // X: wave w fills rows 8w .. 8w+7; lane l -> row 8w + l/8, chunk
-  // (l&7) ^ st_xswz(row); the k-range check only matters on a last,
-  // partial k-step.
   const int x_row = 8 * w + (l >> 3);
   const int x_k = 8 * ((l & 7) ^ st_xswz(x_row));
-  const uint32_t x_off = x_row < M ? (uint32_t)(((int64_t)x_row * K + x_k) * 2) : kStOutOfRange;
+  const uint32_t x_off = x_row < M ? (uint32_t)((x_row * K + x_k) * 2) : kStOutOfRange;
   const uint32_t lds_w = (uint32_t)(uintptr_t)(lds_char*)&sm.w[0][0][0] + w * 1024;
   const uint32_t lds_x = (uint32_t)(uintptr_t)(lds_char*)&sm.x[0][0] + w * 1024;
-  const uint32_t lds_g = (uint32_t)(uintptr_t)(lds_char*)&sm.g[0][0];
-  const bf16_t* Wp[2] = {W1, NW == 2 ? W3 : W1};
+  const uint32_t lds_g = (uint32_t)(uintptr_t)(lds_char*)&sm.g[0][w][0];
+  const i32x4 rs_w[2] = {st_rsrc(W1, (uint32_t)(K * N * 2)), st_rsrc(NW == 2 ? W3 : W1, (uint32_t)(K * N * 2))};
+  const i32x4 rs_x = st_rsrc(X, (uint32_t)(M * K * 2));
+  const i32x4 rs_g = st_rsrc(g, (uint32_t)(K * 2));
+  const uint32_t w_step = (uint32_t)(ST_BK * N * 2);
+  // Issue state of the next step: W and X/g scalar offsets, K - k0.
+  uint32_t so_w, so_x;
+  int krem;
+  auto seg_start = [&](int strip, int kt) {
+    so_w = (uint32_t)(((int64_t)kt * ST_BK * N + (int64_t)strip * ST_BN) * 2);
+    so_x = (uint32_t)(kt * ST_BK * 2);
+    krem = (int)(K - (int64_t)kt * ST_BK);
+  };
+  seg_start(nb > 0 ? strip0 + 1 : strip0, nb > 0 ? 0 : kt0);
 
   // Issue every transfer of one step into ring slot `slot`: NW W blocks,
-  // one X block and, from lanes 0..7 of wave 0 only, the step's g slice
-  // (every wave reads it after the barrier) -- NW + 1 vector-memory
-  // instructions per wave, NW + 2 for wave 0.  Everything but the per-lane
-  // offsets is wave-uniform (scalar registers).
+  // one X block and the step's g slice (lanes 0..7, one copy per wave) --
+  // NW + 2 vector-memory instructions per wave (NW + 1 without the gain).
+  // The steps are issued in order; the split form's range moves to strip0
+  // at local step nb.
   auto issue_step = [&](int step, int slot) {
-    // Local step -> (strip, k-step); past the range: k-step nk (zeros).
-    const bool second = step < nb;
-    const int strip = second ? strip0 + 1 : strip0;
-    const int kt = second ? step : (step < n ? kt0 + step - nb : nk);
-    const int64_t k0 = (int64_t)kt * ST_BK;
-    const int64_t rows = K - k0 > 0 ? K - k0 : 0;
-    const int64_t ns = (int64_t)strip * ST_BN;
-    const uint32_t w_off = second ? w_off1 : w_off0;
+    if (SK && step == nb && nb > 0) seg_start(strip0, kt0);
+    if (step == n) {
+      so_w = so_x = kStPastRange;
+      krem = 0;
+    }
+    const uint32_t w_off = SK && step < nb ? w_off1 : w_off0;
 #pragma unroll
-    for (int v = 0; v < NW; ++v) {
-      const i32x4 rs = st_rsrc(Wp[v] + k0 * N + ns, rows > 0 ? (uint32_t)((rows * N - ns) * 2) : 0u);
-      st_lds_load16(lds_w + (uint32_t)((slot * NW + v) * ST_W_BYTES), w_off, rs);
-    }
-    const i32x4 xs = st_rsrc(X + k0, (uint32_t)(((int64_t)M * K - (k0 < (int64_t)M * K ? k0 : 0)) * 2));
-    st_lds_load16(lds_x + (uint32_t)(slot * ST_X_BYTES), k0 + ST_BK <= K || k0 + x_k < K ? x_off : kStOutOfRange,
-                  xs);
-    if (NORM) {
-      const i32x4 gs = st_rsrc(g + k0, (uint32_t)(rows * 2));
-      if (w == 0 && l < 8) st_lds_load16(lds_g + (uint32_t)(slot * ST_G_BYTES), (uint32_t)(16 * l), gs);
-    }
+    for (int v = 0; v < NW; ++v)
+      st_lds_load16(lds_w + (uint32_t)((slot * NW + v) * ST_W_BYTES), w_off, rs_w[v], so_w);
+    st_lds_load16(lds_x + (uint32_t)(slot * ST_X_BYTES), x_k < krem ? x_off : kStOutOfRange, rs_x, so_x);
+    if (NORM) st_lds_load16_x8(lds_g + (uint32_t)(slot * 8 * ST_G_BYTES), (uint32_t)(16 * l), rs_g, so_x);
+    so_w += w_step;
+    so_x += ST_BK * 2;
+    krem -= ST_BK;
   };
 
   // Wave roles: wave w multiplies row block rb = w & 1 (32 rows) over
@@ -270,7 +298,7 @@ __global__ __launch_bounds__(ST_THREADS, 1) void stream_kernel(
   };
   auto read_xg = [&](int slot, u32x4& xv, u32x4& gl) {
     xv = *(const u32x4*)&sm.x[slot][a_off];
-    if (NORM) gl = *(const u32x4*)&sm.g[slot][g_off];
+    if (NORM) gl = *(const u32x4*)&sm.g[slot][w][g_off];
   };
   auto form_regs = [&](const u32x4& xv, const u32x4& gl, u32x4& ah, u32x4& al) {
 #pragma unroll
@@ -304,11 +332,9 @@ __global__ __launch_bounds__(ST_THREADS, 1) void stream_kernel(
   // kt+1: the MFMAs need nothing the new reads bring, and the forming
   // arithmetic is placed between them (a wave issues in order).  Steps past
   // the last one read zeros (range checks).
+  constexpr int PER_STEP = NW + (NORM ? 2 : 1);  // loads per wave and step
   for (int st = 0; st < RING; ++st) issue_step(st, st);
-  if (w == 0)
-    ST_WAIT_VMCNT((RING - 1) * (NW + (NORM ? 2 : 1)));
-  else
-    ST_WAIT_VMCNT((RING - 1) * (NW + 1));
+  ST_WAIT_VMCNT((RING - 1) * PER_STEP);
   __syncthreads();
   u32x4 ah, al, bv[NB];
   {
@@ -323,10 +349,7 @@ __global__ __launch_bounds__(ST_THREADS, 1) void stream_kernel(
     for (int u = 0; u < RING; ++u) {
       const int kt = kb + u;
       if (kt >= n) break;
-      if (w == 0)
-        ST_WAIT_VMCNT((RING - 2) * (NW + (NORM ? 2 : 1)));
-      else
-        ST_WAIT_VMCNT((RING - 2) * (NW + 1));
+      ST_WAIT_VMCNT((RING - 2) * PER_STEP);
       __syncthreads();
       const int s1 = u + 1 < RING ? u + 1 : 0;
       u32x4 xv, gl, bn[NB];
@@ -555,6 +578,13 @@ __global__ __launch_bounds__(ST_THREADS, 1) void stream_kernel(
 
 static size_t st_align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// The stream kernel's buffer offsets are 32-bit: each operand at most 2^30
+// bytes, one W step (64 rows) at most 2^25 bytes.
+bool rmm_stream_fits(int64_t M, int64_t N, int64_t K) {
+  const int64_t lim = (int64_t)1 << 30;
+  return M >= 0 && M <= 64 && K * N * 2 <= lim && M * K * 2 <= lim && 64 * N * 2 <= ((int64_t)1 << 25);
+}
+
 // Split form when there are at most half as many 64-column strips as
 // `target` workgroups (one per CU): every CU then takes an equal share of
 // all the k-steps.  With more strips the unsplit form is faster: at 224
@@ -582,6 +612,7 @@ void rmm_stream_plan(int64_t N, int64_t K, int gated, int target, bool have_ws, 
 hipError_t rmm_launch_stream(const RmmArgs& a, const StreamPlan& p, void* ws) {
   using namespace rmm;
   if (p.split && !ws) return hipErrorInvalidValue;
+  if (!rmm_stream_fits(a.M, a.N, a.K)) return hipErrorInvalidValue;
   StSplit sp{p.strips, nullptr, nullptr, nullptr};
   if (p.split) {
     char* base = (char*)ws;

@@ -3,8 +3,12 @@
     python -m tensor_program_amd.build
 
 Every source is compiled with hipcc for gfx950 only.  Packed fp32 VALU
-instructions are switched off in device code (-packed-fp32-ops); hipcc's host
-pass warns that it does not know that feature, which is harmless.
+instructions are switched off in device code (-packed-fp32-ops).  The
+accumulating VOP2 form of the bf16 dot product is switched off too
+(-dot13-insts): with it the compiler turns every zero-accumulator dot product
+into a register clear plus the accumulating form, two instructions where the
+VOP3P form takes the zero as a constant.  hipcc's host pass warns that it does
+not know these features, which is harmless.
 """
 from __future__ import annotations
 
@@ -37,6 +41,7 @@ def hipcc() -> str:
 def cflags():
     return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE,
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-Xclang", "-target-feature", "-Xclang", "-dot13-insts",
             "-Wall", "-Wno-unused-command-line-argument"]
 
 

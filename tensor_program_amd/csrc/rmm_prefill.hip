@@ -149,10 +149,11 @@ __device__ __forceinline__ void pf_dma_b(uint32_t b_lds, const PfDma& d, const b
   for (int q = 0; q < 4; ++q) pf_lds_load16(b_lds + (4 * w + q) * 1024, d.off[q], rsrc);
 }
 
-// Rows i0, i0+1 of a register stage -> A stage: X*g, each product formed
-// exactly in fp32 by a bf16 dot2 with the other lane of g zeroed, then
-// rounded once to bf16; the same dot2 unit accumulates the row sums of
-// squares of raw X.
+// Rows i0, i0+1 of a register stage -> A stage (the first step; the k-loop
+// interleaves the same arithmetic with its MFMAs): X*g, each product formed
+// exactly in fp32 (bf16 -> fp32 is a shift, and a product of two bf16 is
+// exact in fp32), then rounded once to bf16; fp32 FMAs accumulate the row
+// sums of squares of raw X.
 template <bool GL>
 __device__ __forceinline__ void pf_store_a(const PfA& st, char* a_lds, float (&ss)[4], int tid,
                                            int i0, int norm, const char* g_lds, int64_t k0) {
@@ -162,11 +163,10 @@ __device__ __forceinline__ void pf_store_a(const PfA& st, char* a_lds, float (&s
     u32x4 v;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      const bf16x2 x = as_bf16x2(st.a[i][d]);
       const uint32_t gd = norm ? gsrc[d] : kBf16OnePair;
-      v[d] = pack_bf16x2(__builtin_amdgcn_fdot2_f32_bf16(x, as_bf16x2(gd & 0xffffu), 0.0f, false),
-                         __builtin_amdgcn_fdot2_f32_bf16(x, as_bf16x2(gd & 0xffff0000u), 0.0f, false));
-      ss[i] = __builtin_amdgcn_fdot2_f32_bf16(x, x, ss[i], false);
+      const float x0 = __uint_as_float(st.a[i][d] << 16), x1 = __uint_as_float(st.a[i][d] & 0xffff0000u);
+      v[d] = pack_bf16x2(x0 * __uint_as_float(gd << 16), x1 * __uint_as_float(gd & 0xffff0000u));
+      ss[i] = __builtin_fmaf(x1, x1, __builtin_fmaf(x0, x0, ss[i]));
     }
     *(u32x4*)(a_lds + ((tid >> 3) + 64 * i) * PF_A_ROW + 16 * (tid & 7)) = v;
   }
@@ -209,31 +209,109 @@ __device__ __forceinline__ void pf_mfma(const PfFrag& f, floatx16 (&acc)[4][2]) 
 #define PF_WAIT_VMCNT(n) \
   __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
 
-// One k-step: multiply the stage (a_cur, b_cur) while X of the next step
-// (st) is scaled into a_nxt.  The fragment reads of the first two sub-steps
-// go out before `issue` (the W transfer and the X loads of later steps), so
-// the first MFMAs do not wait behind the address work of those loads.
-// Fragments of sub-step s+1 are read while the MFMAs of sub-step s run; the
-// staging is fenced behind the first two sub-steps.
+// One k-step as 32 issue slots, one per MFMA: the wave issues in order, so
+// every MFMA is followed by a small share of the step's other work, which
+// then issues while the matrix pipe works (both waves of a SIMD reach the
+// step together after the barrier, so batching the other work would leave
+// the pipe idle).  Sub-step s (16 k) is 8 MFMAs over the 128 x 64 wave
+// tile, operands from fragment set s & 1:
+//   s = 0: + the fragment reads of sub-step 1, and `issue` (the W transfer
+//          and the X loads of later steps);
+//   s = 1, 2: + the fragment reads of sub-step s + 1, and the scaling of X
+//          of the next step into a_nxt (16 units of one 16-byte chunk each,
+//          a row written once its 4 chunks are formed);
+//   s = 3: + the last scaling units.
+// sched_barrier(0) between slots keeps this order.
 template <int VM, bool GL, typename Issue>
 __device__ __forceinline__ void pf_step(const char* a_cur, const lds_char* b_cur, char* a_nxt,
                                         PfA& st, floatx16 (&acc)[4][2], float (&ss)[4],
                                         int a_base, int b0, int b1, int tid, int norm,
                                         const char* g_lds, int64_t k_nxt, Issue issue) {
-  PfFrag fa, fb;
-  pf_read_frags(fa, a_cur, b_cur, a_base, b0, b1, 0);
-  pf_read_frags(fb, a_cur, b_cur, a_base, b0, b1, 1);
+  // Fragment sets, B fragments as the two halves of the transposing reads.
+  bf16x8 fa[2][4];
+  u32x2 fb[2][2][2];
+  const int bo[2] = {b0, b1};
+  // Read q (0..7) of sub-step s into set s & 1, in the order the MFMAs use them.
+  auto read_q = [&](int s, int q) {
+    const int f = s & 1;
+    // a0, b0lo, b0hi, a1, b1lo, b1hi, a2, a3
+    if (q == 0 || q == 3 || q >= 6) {
+      const int i = q == 0 ? 0 : (q == 3 ? 1 : q - 4);
+      fa[f][i] = *(const bf16x8*)(a_cur + a_base + 32 * i * PF_A_ROW + 32 * s);
+    } else {
+      const int j = q < 3 ? 0 : 1, h = (q == 2 || q == 5);
+      fb[f][j][h] = __builtin_bit_cast(
+          u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                     (lds_i16x4*)(b_cur + bo[j] + (16 * s + 4 * h) * 512)));
+    }
+  };
+  auto mfma_q = [&](int s, int q) {
+    const int f = s & 1, i = q >> 1, j = q & 1;
+    const u32x4 bv = {fb[f][j][0][0], fb[f][j][0][1], fb[f][j][1][0], fb[f][j][1][1]};
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[f][i], __builtin_bit_cast(bf16x8, bv),
+                                                        acc[i][j], 0, 0, 0);
+  };
+  // Scaling: the gain of this thread's k-chunk as fp32 (bf16 -> fp32 is a
+  // shift), once per step; unit u = 4 i + d forms chunk d of row i with
+  // plain fp32 multiplies (a product of two bf16 is exact in fp32) and adds
+  // the squares of X to the row's sum with fp32 FMAs.  No dot-product
+  // instructions here: on gfx950 they occupy the matrix pipe and would not
+  // overlap with the MFMAs.
+  float g_f[8];
+  u32x4 row_v, gsrc;
+  auto gain = [&] {
+    if (!GL) gsrc = st.g;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t gd = norm ? gsrc[d] : kBf16OnePair;
+      g_f[2 * d] = __uint_as_float(gd << 16);
+      g_f[2 * d + 1] = __uint_as_float(gd & 0xffff0000u);
+    }
+  };
+  auto unit = [&](int u) {
+    const int i = u >> 2, d = u & 3;
+    const float x0 = __uint_as_float(st.a[i][d] << 16), x1 = __uint_as_float(st.a[i][d] & 0xffff0000u);
+    row_v[d] = pack_bf16x2(x0 * g_f[2 * d], x1 * g_f[2 * d + 1]);
+    ss[i] = __builtin_fmaf(x1, x1, __builtin_fmaf(x0, x0, ss[i]));
+    if (d == 3) *(u32x4*)(a_nxt + ((tid >> 3) + 64 * i) * PF_A_ROW + 16 * (tid & 7)) = row_v;
+  };
+#define PF_SLOT_END __builtin_amdgcn_sched_barrier(0)
+  // Sub-step 0's fragments, then the transfers of later steps.
+#pragma unroll
+  for (int q = 0; q < 8; ++q) read_q(0, q);
+  if (GL) gsrc = *(const u32x4*)(g_lds + 2 * (k_nxt + 8 * (tid & 7)));
   issue();
-  pf_mfma(fa, acc);
-  pf_read_frags(fa, a_cur, b_cur, a_base, b0, b1, 2);
-  pf_mfma(fb, acc);
-  __builtin_amdgcn_sched_barrier(0);
+  PF_SLOT_END;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    mfma_q(0, q);
+    read_q(1, q);
+    PF_SLOT_END;
+  }
   pf_wait_a<VM, GL>(st);
-  pf_store_a<GL>(st, a_nxt, ss, tid, 0, norm, g_lds, k_nxt);
-  pf_read_frags(fb, a_cur, b_cur, a_base, b0, b1, 3);
-  pf_mfma(fa, acc);
-  pf_store_a<GL>(st, a_nxt, ss, tid, 2, norm, g_lds, k_nxt);
-  pf_mfma(fb, acc);
+  gain();
+  PF_SLOT_END;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    mfma_q(1, q);
+    read_q(2, q);
+    if (q < 6) unit(q);
+    PF_SLOT_END;
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    mfma_q(2, q);
+    read_q(3, q);
+    if (q < 6) unit(6 + q);
+    PF_SLOT_END;
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    mfma_q(3, q);
+    if (q < 4) unit(12 + q);
+    PF_SLOT_END;
+  }
+#undef PF_SLOT_END
 }
 
 // Largest K whose gain vector is held in LDS for the whole call (20 KB, the

@@ -68,12 +68,6 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 __device__ __forceinline__ bf16x2 st_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2, v); }
 
-// a.lo * b.lo + a.hi * b.hi in fp32.  Written with the builtin, not inline
-// asm: the compiler tracks the hazard of a VALU write to a register an
-// in-flight MFMA still reads only for the instructions it emits itself.
-__device__ __forceinline__ float st_dot2_bf16(uint32_t a, uint32_t b) {
-  return __builtin_amdgcn_fdot2_f32_bf16(st_bf16x2(a), st_bf16x2(b), 0.0f, false);
-}
 
 // X slot swizzle: physical 16-byte chunk of logical chunk c in row r is
 // c ^ st_xswz(r).  Rows 32 apart share it (fragment row blocks).
@@ -300,13 +294,16 @@ __global__ __launch_bounds__(ST_THREADS, 1) void stream_kernel(
     xv = *(const u32x4*)&sm.x[slot][a_off];
     if (NORM) gl = *(const u32x4*)&sm.g[slot][w][g_off];
   };
+  // Forming works on fp32 values (bf16 -> fp32 is a shift; a product of two
+  // bf16 is exact in fp32) with plain multiplies and FMAs: on gfx950 the
+  // bf16 dot-product instructions occupy the matrix pipe and would not
+  // overlap with the MFMAs they are interleaved with.
   auto form_regs = [&](const u32x4& xv, const u32x4& gl, u32x4& ah, u32x4& al) {
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      const bf16x2 x = st_bf16x2(xv[d]);
       if (NORM) {
-        const float p0 = st_dot2_bf16(xv[d], gl[d] & 0xffffu);
-        const float p1 = st_dot2_bf16(xv[d], gl[d] & 0xffff0000u);
+        const float x0 = __uint_as_float(xv[d] << 16), x1 = __uint_as_float(xv[d] & 0xffff0000u);
+        const float p0 = x0 * __uint_as_float(gl[d] << 16), p1 = x1 * __uint_as_float(gl[d] & 0xffff0000u);
         if (SPLIT) {
           const u32x2 hl = split_bf16x2(p0, p1);
           ah[d] = hl[0];
@@ -314,10 +311,10 @@ __global__ __launch_bounds__(ST_THREADS, 1) void stream_kernel(
         } else {
           ah[d] = pack_bf16x2(p0, p1);
         }
+        ss = __builtin_fmaf(x1, x1, __builtin_fmaf(x0, x0, ss));
       } else {
-        ah[d] = xv[d];
+        ah[d] = xv[d];  // without the gain no sums of squares are needed
       }
-      ss = __builtin_amdgcn_fdot2_f32_bf16(x, x, ss, false);
     }
   };
 

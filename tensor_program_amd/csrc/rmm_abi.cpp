@@ -59,6 +59,9 @@ constexpr int64_t kTargetWorkgroups = 256;
 // N = 2048 69.6 us, N = 4096 85.0 us, against 111-112 us).
 constexpr int64_t kStreamRows = 64;
 constexpr int64_t kStreamMaxM = 128;
+// Gated calls: 64-row stream launches up to this many rows, the gated
+// prefill tile above.
+constexpr int64_t kGatedStreamMaxM = 128;
 // Low-rank adapter: ranks 1..RMM_LORA_MAX_RANK; the decode kernel carries up
 // to two 16-wide rank blocks, every other shape runs the generic kernel.
 constexpr int64_t kLoraDecodeMaxRank = 32;
@@ -107,10 +110,7 @@ rmm_status plan_shape(int64_t M, int64_t N, int64_t K, rmm_dtype dtype, int gate
   const bool decode_ok = (fast_layout && lora_ok &&
                           M <= (gated ? kDecodeMaxMGated : (R > 0 ? kDecodeMaxMLora : kDecodeMaxM))) ||
                          decode32_ok;
-  const bool prefill_ok = fast_layout && !gated && R == 0;
-  // Gated calls have no prefill tile: any M runs as 64-row stream launches
-  // (K = 4096, N = 14336, M = 256: 191 us against 3860 us for the generic
-  // kernel's vector products).
+  const bool prefill_ok = fast_layout && R == 0;
   const bool stream_ok = fast_layout && R == 0 &&
                          (gated || M <= kStreamMaxM || (M <= 256 && N <= 4096)) &&
                          rmm_stream_fits(M < kStreamRows ? M : kStreamRows, N, K);
@@ -119,8 +119,11 @@ rmm_status plan_shape(int64_t M, int64_t N, int64_t K, rmm_dtype dtype, int gate
     if (R > 0)
       v = decode_ok ? RMM_VARIANT_DECODE : RMM_VARIANT_GENERIC;
     else if (gated)  // decode (split-K over every CU) only with a workspace for its partials
-      v = (decode_ok && have_ws) ? RMM_VARIANT_DECODE
-                                 : (stream_ok ? RMM_VARIANT_STREAM : RMM_VARIANT_GENERIC);
+      v = (decode_ok && have_ws)                 ? RMM_VARIANT_DECODE
+          : (stream_ok && M <= kGatedStreamMaxM) ? RMM_VARIANT_STREAM
+          : prefill_ok                           ? RMM_VARIANT_PREFILL
+          : stream_ok                            ? RMM_VARIANT_STREAM
+                                                 : RMM_VARIANT_GENERIC;
     else if (decode_ok)
       v = RMM_VARIANT_DECODE;
     else if (stream_ok)  // M <= 64: far faster than one row of 256 x 256 prefill tiles
@@ -156,7 +159,7 @@ rmm_status plan_shape(int64_t M, int64_t N, int64_t K, rmm_dtype dtype, int gate
     out->splits = out->dec.splits;
     out->ws_bytes = out->dec.ws_bytes;
   } else if (v == RMM_VARIANT_PREFILL) {
-    rmm_prefill_plan(M, N, K, &out->pre);
+    rmm_prefill_plan(M, N, K, gated, &out->pre);
   } else if (v == RMM_VARIANT_STREAM) {
     rmm_stream_plan(N, K, gated, (int)kTargetWorkgroups, have_ws, &out->st);
     if (out->st.ws_bytes > (size_t)INT32_MAX) return RMM_ERR_VARIANT;  // 32-bit offsets

@@ -148,11 +148,11 @@ hipError_t rmm_launch_chain(const void* X0, const void* G, const void* W, void* 
                             hipStream_t stream);
 
 struct PrefillPlan {
-  int tiles_m, tiles_n;  // 256 x 256 output tiles
+  int tiles_m, tiles_n;  // output tiles: 256 x 256, gated 128 x 128 (of each weight)
   int group_m;           // tile-rows walked together (L2 reuse)
   int xcd_remap;         // contiguous tile ranges per XCD
 };
-void rmm_prefill_plan(int64_t M, int64_t N, int64_t K, PrefillPlan* p);
+void rmm_prefill_plan(int64_t M, int64_t N, int64_t K, int gated, PrefillPlan* p);
 hipError_t rmm_launch_prefill(const RmmArgs& a, const PrefillPlan& p);
 
 // Stream variant: one workgroup per 64-column strip, or (split form, with a

@@ -324,7 +324,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_kernel(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ g, const bf16_t* __restrict__ W1,
     const bf16_t* __restrict__ W3, bf16_t* __restrict__ Y, float eps, int64_t M, int64_t N,
     int64_t K, int tiles_m, int tiles_n, int group_m, int xcd_remap, int norm) {
-  static_assert(!GATED, "gated prefill tiles are not built");
+  static_assert(!GATED, "the gated tile is prefill_gated_kernel");
   // Loads per thread per k-step outside the W transfers: 4 rows of X, and
   // the gain unless it sits in LDS.
   constexpr int XL = GL ? 4 : 5;
@@ -464,29 +464,373 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Gated tile: Y = silu(norm(X) W1) * (norm(X) W3) for many rows (the gated
+// MLP row of the Mirage paper review's benchmark table, "五、实验结果").
+//
+// The gate multiplies one product's error by the other product, so, as in
+// the decode and stream kernels, the operand X*g is carried exactly as two
+// bf16 parts (hi = bf16(X g), lo = bf16(X g - hi)), both multiplied into the
+// same accumulator.  Tile 128 rows x 128 columns of each weight x 64 k:
+//   * A: two stages (hi, lo), double-buffered, 144-byte rows as above;
+//   * W: one stage holds the 64 x 128 blocks of W1 and W3 ([weight][k][n],
+//     256-byte rows, chunk c of row k at c ^ 2(k & 3)); each 1 KB
+//     LDS-direct transfer reads 4 rows of one weight;
+//   * wave w: rows 64 (w >> 2) .. +63, weight (w >> 1) & 1, columns
+//     64 (w & 1) .. +63 of that weight: 2 x 2 v_mfma_f32_32x32x16_bf16
+//     tiles, hi and lo MFMAs per sub-step (32 per k-step, as in the plain
+//     tile);
+//   * epilogue: the W3 waves hand their sums to the W1 waves through LDS,
+//     which apply 1/RMS and the gate and store Y.
+constexpr int PG_BM = 128, PG_BNW = 128;              // rows, columns per weight
+constexpr int PG_A_BYTES = PG_BM * PF_A_ROW;          // one A stage (hi or lo)
+constexpr int PG_B_BYTES = 2 * PF_BK * PG_BNW * 2;    // one W stage, 32 KB
+constexpr int PG_W_BYTES = PF_BK * PG_BNW * 2;        // one weight's block, 16 KB
+
+// Byte offset of element n (a multiple of 4) of row k in one weight's block.
+__device__ __forceinline__ int pg_b_off(int k, int n) {
+  return k * 256 + (((n >> 3) ^ (2 * (k & 3))) << 4) + ((n & 7) << 1);
+}
+
+// X of one k-step for this thread: rows (t>>3) and (t>>3) + 64, chunk t&7.
+struct PgA {
+  u32x4 a[2];
+  u32x4 g;
+};
+
+template <bool GL>
+__device__ __forceinline__ void pg_load_a(PgA& st, i32x4 xr, i32x4 gr, int64_t m0, int64_t k0,
+                                          int64_t M, int64_t K, int tid) {
+  const int64_t ka = k0 + 8 * (tid & 7);
+  const bool ka_ok = ka < K;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int64_t m = m0 + (tid >> 3) + 64 * i;
+    st.a[i] = pf_load16((ka_ok && m < M) ? (uint32_t)((m * K + ka) * 2) : kPfOutOfRange, xr);
+  }
+  if (!GL) st.g = pf_load16(ka_ok ? (uint32_t)(ka * 2) : kPfOutOfRange, gr);
+}
+
+template <int N, bool GL>
+__device__ __forceinline__ void pg_wait_a(PgA& st) {
+  if (GL)
+    asm volatile("s_waitcnt vmcnt(%2)" : "+v"(st.a[0]), "+v"(st.a[1]) : "n"(N));
+  else
+    asm volatile("s_waitcnt vmcnt(%3)" : "+v"(st.a[0]), "+v"(st.a[1]), "+v"(st.g) : "n"(N));
+}
+
+// W of step k0 into a stage: wave w fills the 1-KB blocks 4w .. 4w+3 of
+// weight w >> 2 (4 rows each); lane l lands at byte 16 l of its block.
+struct PgDma {
+  uint32_t off[4];
+};
+
+__device__ __forceinline__ void pg_dma_setup(PgDma& d, int64_t n0, int64_t N, int w, int l) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int blk = (4 * w + q) & 15;
+    const int kl = 4 * blk + (l >> 4);
+    const int c = (l & 15) ^ (2 * (kl & 3));
+    const int64_t nn = n0 + 8 * c;
+    d.off[q] = nn < N ? (uint32_t)((kl * N + nn) * 2) : kPfOutOfRange;
+  }
+}
+
+__device__ __forceinline__ void pg_dma_b(uint32_t b_lds, const PgDma& d, const bf16_t* W1,
+                                         const bf16_t* W3, int64_t k0, int64_t N, int64_t K, int w) {
+  const int64_t rows = K - k0 > 0 ? K - k0 : 0;
+  const bf16_t* Wv = (w >> 2) ? W3 : W1;
+  const i32x4 rsrc = pf_rsrc(Wv + k0 * N, (uint32_t)(rows * N * 2));
+#pragma unroll
+  for (int q = 0; q < 4; ++q) pf_lds_load16(b_lds + (4 * w + q) * 1024, d.off[q], rsrc);
+}
+
+// Rows of a register stage -> A stages (hi, lo): X*g formed exactly in fp32,
+// split into two bf16 parts; fp32 FMAs accumulate the row sums of squares.
+template <bool GL>
+__device__ __forceinline__ void pg_form_unit(const PgA& st, const float (&g_f)[8], u32x4& hv, u32x4& lv,
+                                             float (&ss)[2], int i, int d) {
+  const float x0 = __uint_as_float(st.a[i][d] << 16), x1 = __uint_as_float(st.a[i][d] & 0xffff0000u);
+  const u32x2 hl = split_bf16x2(x0 * g_f[2 * d], x1 * g_f[2 * d + 1]);
+  hv[d] = hl[0];
+  lv[d] = hl[1];
+  ss[i] = __builtin_fmaf(x1, x1, __builtin_fmaf(x0, x0, ss[i]));
+}
+
+template <bool GL>
+__device__ __forceinline__ void pg_gain(float (&g_f)[8], const u32x4& gsrc, int norm) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t gd = norm ? gsrc[d] : kBf16OnePair;
+    g_f[2 * d] = __uint_as_float(gd << 16);
+    g_f[2 * d + 1] = __uint_as_float(gd & 0xffff0000u);
+  }
+}
+
+// One k-step in 32 issue slots (as pf_step): sub-step s is 4 hi then 4 lo
+// MFMAs over the 64 x 64 wave tile, fragments from set s & 1, each followed
+// by a fragment read of sub-step s + 1 and, in sub-steps 1 and 2, a share
+// of the forming of the next step's A stages.
+template <int VM, bool GL, typename Issue>
+__device__ __forceinline__ void pg_step(const char* ah_cur, const char* al_cur, const lds_char* b_cur,
+                                        char* ah_nxt, char* al_nxt, PgA& st, floatx16 (&acc)[2][2],
+                                        float (&ss)[2], int a_base, int b0, int b1, int tid, int norm,
+                                        const char* g_lds, int64_t k_nxt, Issue issue) {
+  bf16x8 fh[2][2], fl[2][2];
+  u32x2 fb[2][2][2];
+  const int bo[2] = {b0, b1};
+  // q: 0 hi0, 1 b0lo, 2 b0hi, 3 hi1, 4 b1lo, 5 b1hi, 6 lo0, 7 lo1
+  auto read_q = [&](int s, int q) {
+    const int f = s & 1;
+    if (q == 0 || q == 3) {
+      const int i = q == 0 ? 0 : 1;
+      fh[f][i] = *(const bf16x8*)(ah_cur + a_base + 32 * i * PF_A_ROW + 32 * s);
+    } else if (q >= 6) {
+      const int i = q - 6;
+      fl[f][i] = *(const bf16x8*)(al_cur + a_base + 32 * i * PF_A_ROW + 32 * s);
+    } else {
+      const int j = q < 3 ? 0 : 1, h = (q == 2 || q == 5);
+      fb[f][j][h] = __builtin_bit_cast(
+          u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(b_cur + bo[j] + (16 * s + 4 * h) * 256)));
+    }
+  };
+  auto mfma_q = [&](int s, int q) {
+    const int f = s & 1, i = (q & 3) >> 1, j = q & 1;
+    const u32x4 bv = {fb[f][j][0][0], fb[f][j][0][1], fb[f][j][1][0], fb[f][j][1][1]};
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q < 4 ? fh[f][i] : fl[f][i],
+                                                        __builtin_bit_cast(bf16x8, bv), acc[i][j], 0, 0, 0);
+  };
+  float g_f[8];
+  u32x4 hv, lv, gsrc;
+  auto unit = [&](int u) {
+    const int i = u >> 2, d = u & 3;
+    pg_form_unit<GL>(st, g_f, hv, lv, ss, i, d);
+    if (d == 3) {
+      const int off = ((tid >> 3) + 64 * i) * PF_A_ROW + 16 * (tid & 7);
+      *(u32x4*)(ah_nxt + off) = hv;
+      *(u32x4*)(al_nxt + off) = lv;
+    }
+  };
+#define PG_SLOT_END __builtin_amdgcn_sched_barrier(0)
+#pragma unroll
+  for (int q = 0; q < 8; ++q) read_q(0, q);
+  if (GL) gsrc = *(const u32x4*)(g_lds + 2 * (k_nxt + 8 * (tid & 7)));
+  issue();
+  PG_SLOT_END;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    mfma_q(0, q);
+    read_q(1, q);
+    PG_SLOT_END;
+  }
+  pg_wait_a<VM, GL>(st);
+  if (!GL) gsrc = st.g;
+  pg_gain<GL>(g_f, gsrc, norm);
+  PG_SLOT_END;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    mfma_q(1, q);
+    read_q(2, q);
+    if (q < 4) unit(q);
+    PG_SLOT_END;
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    mfma_q(2, q);
+    read_q(3, q);
+    if (q < 4) unit(4 + q);
+    PG_SLOT_END;
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    mfma_q(3, q);
+    PG_SLOT_END;
+  }
+#undef PG_SLOT_END
+}
+
+template <bool GL>
+__global__ __launch_bounds__(PF_THREADS, 1) void prefill_gated_kernel(
+    const bf16_t* __restrict__ X, const bf16_t* __restrict__ g, const bf16_t* __restrict__ W1,
+    const bf16_t* __restrict__ W3, bf16_t* __restrict__ Y, float eps, int64_t M, int64_t N,
+    int64_t K, int tiles_m, int tiles_n, int group_m, int xcd_remap, int norm) {
+  constexpr int XL = GL ? 2 : 3;  // X (and g) loads per thread per k-step
+  __shared__ __attribute__((aligned(16))) char ah_s0[PG_A_BYTES];
+  __shared__ __attribute__((aligned(16))) char ah_s1[PG_A_BYTES];
+  __shared__ __attribute__((aligned(16))) char al_s0[PG_A_BYTES];
+  __shared__ __attribute__((aligned(16))) char al_s1[PG_A_BYTES];
+  __shared__ __attribute__((aligned(1024))) char b_s0[PG_B_BYTES];
+  __shared__ __attribute__((aligned(1024))) char b_s1[PG_B_BYTES];
+  __shared__ float inv_s[PG_BM];
+  __shared__ __attribute__((aligned(16))) char g_s[GL ? 2 * (PF_G_LDS_MAX + 2 * PF_BK) : 16];
+
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int ntiles = tiles_m * tiles_n;
+  int t = blockIdx.x;
+  if (xcd_remap) t = (t & 7) * (ntiles >> 3) + (t >> 3);
+  const int group = group_m * tiles_n;
+  const int gid = t / group, first_m = gid * group_m;
+  const int gm = (tiles_m - first_m < group_m) ? (tiles_m - first_m) : group_m;
+  const int tm = first_m + (t % group) % gm;
+  const int tn = (t % group) / gm;
+  const int64_t m0 = (int64_t)tm * PG_BM, n0 = (int64_t)tn * PG_BNW;
+
+  const i32x4 xr = pf_rsrc(X, (uint32_t)(M * K * 2));
+  const i32x4 gr = pf_rsrc(g, (uint32_t)(K * 2));
+  lds_char* b0s = (lds_char*)b_s0;
+  lds_char* b1s = (lds_char*)b_s1;
+  const uint32_t b0a = (uint32_t)(uintptr_t)b0s, b1a = (uint32_t)(uintptr_t)b1s;
+  PgDma dma;
+  pg_dma_setup(dma, n0, N, w, l);
+
+  floatx16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  float ss[2] = {0.f, 0.f};
+
+  const int wm = w >> 2, wv = (w >> 1) & 1, wh = w & 1;
+  const int a_base = (wm * 64 + (l & 31)) * PF_A_ROW + 16 * (l >> 5);
+  const int bG = l >> 4, bi = l & 15;
+  const int bk = 8 * (bG >> 1) + (bi >> 2);
+  const int bn = wh * 64 + 16 * (bG & 1) + 4 * (bi & 3);
+  const int bo0 = wv * PG_W_BYTES + pg_b_off(bk, bn), bo1 = wv * PG_W_BYTES + pg_b_off(bk, bn + 32);
+  const int nk = (int)((K + PF_BK - 1) / PF_BK);
+
+  if (GL) {
+    for (int c = tid; c < (PF_G_LDS_MAX + 2 * PF_BK) / 8; c += PF_THREADS)
+      *(u32x4*)(g_s + 16 * c) = 8 * c < K ? *(const u32x4*)(g + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+    __syncthreads();
+  }
+
+  // Pipeline as in prefill_kernel: stage kt&1 holds step kt at the top of
+  // iteration kt, W of step kt+1 streams into the other stage, X of step
+  // kt+1 is formed into the other A stages, X of step kt+2 is in flight.
+  PgA sa, sb;
+  pg_dma_b(b0a, dma, W1, W3, 0, N, K, w);
+  pg_load_a<GL>(sa, xr, gr, m0, 0, M, K, tid);
+  pg_load_a<GL>(sb, xr, gr, m0, PF_BK, M, K, tid);
+  pg_wait_a<XL, GL>(sa);
+  {
+    float g_f[8];
+    const u32x4 gsrc = GL ? *(const u32x4*)(g_s + 16 * (tid & 7)) : sa.g;
+    pg_gain<GL>(g_f, gsrc, norm);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      u32x4 hv, lv;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) pg_form_unit<GL>(sa, g_f, hv, lv, ss, i, d);
+      const int off = ((tid >> 3) + 64 * i) * PF_A_ROW + 16 * (tid & 7);
+      *(u32x4*)(ah_s0 + off) = hv;
+      *(u32x4*)(al_s0 + off) = lv;
+    }
+  }
+  PF_WAIT_VMCNT(0);
+  __syncthreads();
+
+  for (int kt = 0; kt < nk; kt += 2) {
+    pg_step<XL + 4, GL>(ah_s0, al_s0, b0s, ah_s1, al_s1, sb, acc, ss, a_base, bo0, bo1, tid, norm, g_s,
+                        (int64_t)(kt + 1) * PF_BK, [&] {
+                          pg_dma_b(b1a, dma, W1, W3, (int64_t)(kt + 1) * PF_BK, N, K, w);
+                          pg_load_a<GL>(sa, xr, gr, m0, (int64_t)(kt + 2) * PF_BK, M, K, tid);
+                        });
+    PF_WAIT_VMCNT(XL);
+    __syncthreads();
+    pg_step<XL + 4, GL>(ah_s1, al_s1, b1s, ah_s0, al_s0, sa, acc, ss, a_base, bo0, bo1, tid, norm, g_s,
+                        (int64_t)(kt + 2) * PF_BK, [&] {
+                          pg_dma_b(b0a, dma, W1, W3, (int64_t)(kt + 2) * PF_BK, N, K, w);
+                          pg_load_a<GL>(sb, xr, gr, m0, (int64_t)(kt + 3) * PF_BK, M, K, tid);
+                        });
+    PF_WAIT_VMCNT(XL);
+    __syncthreads();
+  }
+  // The last X loads (past K: zeros) keep their registers reserved until
+  // they have landed.
+  pg_wait_a<0, GL>(sa);
+  pg_wait_a<0, GL>(sb);
+  PF_WAIT_VMCNT(0);
+
+  // Row sums of squares: the 8 lanes tid&7 share rows (tid>>3) and +64.
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    float v = ss[i];
+    v += __shfl_xor(v, 1);
+    v += __shfl_xor(v, 2);
+    v += __shfl_xor(v, 4);
+    if ((tid & 7) == 0) inv_s[(tid >> 3) + 64 * i] = norm ? inv_rms(v, K, eps) : 1.0f;
+  }
+  __syncthreads();
+
+  // Epilogue, one 64-row half at a time: the W3 waves of rows 64 r .. +63
+  // put their sums in a W stage as [column half][row][col] fp32, the W1
+  // waves of those rows read them back at the positions of their own sums.
+  // 32x32 accumulator layout: lane l holds column l%32 and, for register
+  // 4 jj + rr, row 8 jj + 4 (l/32) + rr.
+  float* ex = (float*)b_s0;
+  auto ex_at = [&](int i, int j, int jj, int rr) -> float& {
+    const int row = 32 * i + 8 * jj + 4 * (l >> 5) + rr, col = 32 * j + (l & 31);
+    return ex[(wh * 64 + row) * 64 + col];
+  };
+  for (int r = 0; r < 2; ++r) {
+    if (wm == r && wv == 1) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) ex_at(i, j, jj, rr) = acc[i][j][4 * jj + rr];
+    }
+    __syncthreads();
+    if (wm == r && wv == 0) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int64_t n = n0 + wh * 64 + 32 * j + (l & 31);
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+              const int lr = wm * 64 + 32 * i + 8 * jj + 4 * (l >> 5) + rr;
+              const int64_t m = m0 + lr;
+              const float inv = inv_s[lr];
+              const float y = silu_gate(acc[i][j][4 * jj + rr] * inv, ex_at(i, j, jj, rr) * inv);
+              if (m < M && n < N) Y[m * N + n] = f32_to_bf16(y);
+            }
+        }
+    }
+    __syncthreads();
+  }
+}
+
 }  // namespace rmm
 
-void rmm_prefill_plan(int64_t M, int64_t N, int64_t K, PrefillPlan* p) {
+void rmm_prefill_plan(int64_t M, int64_t N, int64_t K, int gated, PrefillPlan* p) {
   using namespace rmm;
-  p->tiles_m = (int)((M + PF_BM - 1) / PF_BM);
-  p->tiles_n = (int)((N + PF_BN - 1) / PF_BN);
+  const int bm = gated ? PG_BM : PF_BM, bn = gated ? PG_BNW : PF_BN;
+  p->tiles_m = (int)((M + bm - 1) / bm);
+  p->tiles_n = (int)((N + bn - 1) / bn);
   p->group_m = 4;
   p->xcd_remap = ((int64_t)p->tiles_m * p->tiles_n) % 8 == 0;
 }
 
 hipError_t rmm_launch_prefill(const RmmArgs& a, const PrefillPlan& p) {
   using namespace rmm;
-  if (a.gated) return hipErrorInvalidValue;
   const unsigned grid = (unsigned)((int64_t)p.tiles_m * p.tiles_n);
-  if (a.K <= PF_G_LDS_MAX)
-    hipLaunchKernelGGL((prefill_kernel<false, true>), dim3(grid), dim3(PF_THREADS), 0, a.stream,
-                       (const bf16_t*)a.X, (const bf16_t*)a.g, (const bf16_t*)a.W1,
-                       (const bf16_t*)a.W3, (bf16_t*)a.Y, a.eps, a.M, a.N, a.K, p.tiles_m,
-                       p.tiles_n, p.group_m, p.xcd_remap, a.norm);
+  auto launch = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(PF_THREADS), 0, a.stream, (const bf16_t*)a.X,
+                       (const bf16_t*)a.g, (const bf16_t*)a.W1, (const bf16_t*)a.W3, (bf16_t*)a.Y, a.eps,
+                       a.M, a.N, a.K, p.tiles_m, p.tiles_n, p.group_m, p.xcd_remap, a.norm);
+  };
+  const bool gl = a.K <= PF_G_LDS_MAX;
+  if (a.gated)
+    gl ? launch(prefill_gated_kernel<true>) : launch(prefill_gated_kernel<false>);
   else
-    hipLaunchKernelGGL((prefill_kernel<false, false>), dim3(grid), dim3(PF_THREADS), 0, a.stream,
-                       (const bf16_t*)a.X, (const bf16_t*)a.g, (const bf16_t*)a.W1,
-                       (const bf16_t*)a.W3, (bf16_t*)a.Y, a.eps, a.M, a.N, a.K, p.tiles_m,
-                       p.tiles_n, p.group_m, p.xcd_remap, a.norm);
+    gl ? launch(prefill_kernel<false, true>) : launch(prefill_kernel<false, false>);
   return hipGetLastError();
 }

@@ -261,7 +261,7 @@ def test_variant_selection():
     assert tpa.plan(16, 14336, 4096, gated=True, with_workspace=False)[1] == "stream"
     assert tpa.plan(17, 14336, 4096, gated=True)[1] == "stream"
     assert tpa.plan(128, 14336, 4096, gated=True)[1] == "stream"
-    assert tpa.plan(1024, 14336, 4096, gated=True)[1] == "stream"   # gated: any M, 64-row launches
+    assert tpa.plan(1024, 14336, 4096, gated=True)[1] == "prefill"  # gated: the 128-row tile above 128 rows
     assert tpa.plan(129, 14336, 4100, gated=True)[1] == "generic"   # K % 8 != 0
     assert tpa.plan(48, 14336, 4096)[1] == "stream"
     # M <= 64 takes the stream kernel at any width (48 x 4096 x 4096: 21 us
@@ -286,7 +286,9 @@ def test_variant_selection():
     assert tpa.plan(129, 4104, 1000)[1] == "prefill"
     assert tpa.plan(4096, 4096, 4095)[1] == "generic"   # K % 8 != 0
     assert tpa.plan(4096, 4096, 4096, variant="prefill", dtype=torch.float32)[0] == VARIANT
-    assert tpa.plan(128, 256, 64, gated=True, variant="prefill")[0] == VARIANT
+    assert tpa.plan(128, 256, 64, gated=True, variant="prefill")[1] == "prefill"
+    assert tpa.plan(4096, 14336, 4096, gated=True)[1] == "prefill"
+    assert tpa.plan(128, 14336, 4096, gated=True)[1] == "stream"
     assert tpa.plan(16, 6144, 4096, variant="decode", splits=3)[1:] == ("decode", 3)
     # split counts that do not divide K evenly are rounded to 128-deep chunks
     st, v, s = tpa.plan(17, 520, 1000, variant="decode", splits=4)

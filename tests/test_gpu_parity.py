@@ -171,6 +171,36 @@ def test_gated_m64_k4096_n14336_full(variant, require_gpu):
     _log(f"  worst err/tol {worst:.3f}")
 
 
+def test_gated_m4096_k4096_n14336_sampled(require_gpu):
+    """The gated product at prefill size (the 128-row gated tile, auto-selected
+    above 128 rows): the gated workload's shape and value recipe with 4096
+    rows, checked on sampled rows at the elementwise bound."""
+    base = synth.get_workload("gated_m64_k4096_n14336")
+    wl = synth.Workload("gated_m4096_k4096_n14336", base.dtype, 4096, base.K, base.N, base.eps,
+                        True, None)
+    assert tpa.plan(wl.M, wl.N, wl.K, gated=True)[1] == "prefill"
+    rows = _sample_rows(wl, n_random=24)
+    _log(f"gated prefill 4096 x 4096 x 14336, {len(rows)} sampled rows")
+    inp = synth.make_inputs(wl)
+    y = from_device(run_gpu(inp, wl.eps))[rows]
+    worst = assert_within_tol(y, run_oracle(inp, wl.eps, rows=rows), tol_for(wl.dtype), wl.name)
+    _log(f"  worst err/tol {worst:.3f}")
+
+
+@pytest.mark.parametrize("M,K,N", [(129, 1000, 520), (200, 264, 1032), (300, 136, 264),
+                                   (256, 4096, 384), (136, 10248, 136)])
+def test_gated_prefill_shapes(M, K, N, require_gpu):
+    """The gated prefill tile on ragged shapes: partial row and column tiles,
+    a partial last k-step, and K past the in-LDS gain (10248), against the
+    oracle at the elementwise bound."""
+    wl = synth.Workload("gated_prefill", "bf16", M, K, N, 1e-6, True, None)
+    _log(f"gated prefill M={M} K={K} N={N}")
+    inp = synth.make_inputs(wl, seed=13)
+    y = from_device(run_gpu(inp, wl.eps, variant="prefill"))
+    worst = assert_within_tol(y, run_oracle(inp, wl.eps), 1e-2, "gated_prefill")
+    _log(f"  worst err/tol {worst:.3f}")
+
+
 def test_large_m8192_k8192_n28672_sampled(require_gpu):
     wl = synth.get_workload("large_m8192_k8192_n28672")
     _check_workload(wl.name, rows=_sample_rows(wl, n_random=24))
@@ -339,6 +369,8 @@ GATED_EXACT = [
     (64, 264, 16392, "stream", 0),    # 257 strips
     (300, 200, 264, "stream", 0),
     (13, 1000, 520, "generic", 0),
+    (200, 264, 1032, "prefill", 0),   # gated tile: 2 x 9 tiles, ragged
+    (256, 4096, 512, "prefill", 0),
 ]
 
 

@@ -52,6 +52,8 @@ def load(path: str = _LIB):
     lib.rmm_oracle_lora_matmul_f64.restype = ctypes.c_int
     lib.rmm_oracle_qknorm_attention_f64.argtypes = [vp, vp, vp, vp, vp, dbl, i64, i64, i64, vp]
     lib.rmm_oracle_qknorm_attention_f64.restype = ctypes.c_int
+    lib.rmm_oracle_attention_f64.argtypes = [vp, vp, vp, i64, i64, i64, vp]
+    lib.rmm_oracle_attention_f64.restype = ctypes.c_int
     return lib
 
 
@@ -187,6 +189,21 @@ def qknorm_attention(Q, K, V, gq, gk, eps, lib=None) -> np.ndarray:
     O = np.empty((BH, D), np.float64)
     rc = lib.rmm_oracle_qknorm_attention_f64(_p(Q), _p(K), _p(V), _p(gq), _p(gk), float(eps), BH,
                                              S, D, _p(O))
+    if rc != 0:
+        raise ValueError(f"oracle error {rc}")
+    return O
+
+
+def attention(Q, K, V, lib=None) -> np.ndarray:
+    """o = softmax(q . K^T / sqrt(D)) V per batch-head, in fp64, on the vectors as
+    given (the unfused program's second kernel).  Q: [BH, D], K and V: [BH, S, D]."""
+    lib = lib or _default()
+    Q, K, V = _d(Q), _d(K), _d(V)
+    BH, D = Q.shape
+    S = K.shape[1]
+    assert K.shape == (BH, S, D) and V.shape == (BH, S, D)
+    O = np.empty((BH, D), np.float64)
+    rc = lib.rmm_oracle_attention_f64(_p(Q), _p(K), _p(V), BH, S, D, _p(O))
     if rc != 0:
         raise ValueError(f"oracle error {rc}")
     return O

@@ -44,6 +44,8 @@
  *   qn = q / rms(q) * gq,   kn_s = k_s / rms(k_s) * gk,
  *   p_s = softmax_s(qn . kn_s / sqrt(D)),   o = sum_s p_s v_s.
  * (rmm_oracle_qknorm_attention_f64; the normalised vectors are materialised.)
+ * The attention step alone, on given (already normalised) vectors, is
+ * rmm_oracle_attention_f64: the second kernel of the unfused program.
  *
  * The steps are also exported one by one (rmm_oracle_rmsnorm_f64: steps 1-2,
  * rmm_oracle_matmul_f64: step 3, rmm_oracle_gated_matmul_f64: the two
@@ -228,6 +230,54 @@ int rmm_oracle_lora_matmul_f64(const double* X, const double* W, const double* A
 
 /* QKNorm + attention for one query per batch-head.  Q: BH x D, K and V:
  * BH x S x D (row s of head h at (h*S + s)*D), O: BH x D. */
+/* The attention step for one batch-head: p_s = softmax_s(q . k_s / sqrt(D))
+ * (the largest score subtracted before exp), o = sum_s p_s v_s.  sc: S
+ * doubles of scratch. */
+static void attend(const double* q, const double* Kh, const double* Vh, int64_t S, int64_t D,
+                   double* sc, double* o) {
+  for (int64_t s = 0; s < S; ++s) {
+    const double* k = Kh + s * D;
+    double dot = 0.0;
+    for (int64_t d = 0; d < D; ++d) dot += q[d] * k[d];
+    sc[s] = dot / sqrt((double)D);
+  }
+  double mx = sc[0];
+  for (int64_t s = 1; s < S; ++s) mx = sc[s] > mx ? sc[s] : mx;
+  double den = 0.0;
+  for (int64_t s = 0; s < S; ++s) {
+    sc[s] = exp(sc[s] - mx);
+    den += sc[s];
+  }
+  for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
+  for (int64_t s = 0; s < S; ++s) {
+    const double p = sc[s] / den;
+    const double* v = Vh + s * D;
+    for (int64_t d = 0; d < D; ++d) o[d] += p * v[d];
+  }
+}
+
+/* Scaled dot-product attention on the given vectors (no normalisation):
+ * Q [BH, D], K and V [BH, S, D] -> O [BH, D]. */
+int rmm_oracle_attention_f64(const double* Q, const double* K, const double* V, int64_t BH,
+                             int64_t S, int64_t D, double* O) {
+  if (BH < 0 || S <= 0 || D <= 0) return 1;
+  int rc = 0;
+#pragma omp parallel for schedule(static)
+  for (int64_t h = 0; h < BH; ++h) {
+    double* sc = (double*)malloc(sizeof(double) * (size_t)S);
+    if (!sc) {
+#pragma omp atomic write
+      rc = 2;
+      continue;
+    }
+    attend(Q + h * D, K + h * S * D, V + h * S * D, S, D, sc, O + h * D);
+    free(sc);
+  }
+  return rc;
+}
+
+/* QKNorm + attention: the query and every key normalised (steps 1-2 on rows
+ * of length D), then the attention step. */
 int rmm_oracle_qknorm_attention_f64(const double* Q, const double* K, const double* V,
                                     const double* gq, const double* gk, double eps, int64_t BH,
                                     int64_t S, int64_t D, double* O) {
@@ -236,7 +286,7 @@ int rmm_oracle_qknorm_attention_f64(const double* Q, const double* K, const doub
 #pragma omp parallel for schedule(static)
   for (int64_t h = 0; h < BH; ++h) {
     double* qn = (double*)malloc(sizeof(double) * (size_t)D);
-    double* kn = (double*)malloc(sizeof(double) * (size_t)D);
+    double* kn = (double*)malloc(sizeof(double) * (size_t)(S * D));
     double* sc = (double*)malloc(sizeof(double) * (size_t)S);
     if (!qn || !kn || !sc) {
       free(qn);
@@ -253,25 +303,9 @@ int rmm_oracle_qknorm_attention_f64(const double* Q, const double* K, const doub
       const double* k = K + (h * S + s) * D;
       double rk;
       row_rms(k, 1, D, eps, &rk);
-      normalise(k, gk, &rk, 1, D, kn);
-      double dot = 0.0;
-      for (int64_t d = 0; d < D; ++d) dot += qn[d] * kn[d];
-      sc[s] = dot / sqrt((double)D);
+      normalise(k, gk, &rk, 1, D, kn + s * D);
     }
-    double mx = sc[0];
-    for (int64_t s = 1; s < S; ++s) mx = sc[s] > mx ? sc[s] : mx;
-    double den = 0.0;
-    for (int64_t s = 0; s < S; ++s) {
-      sc[s] = exp(sc[s] - mx);
-      den += sc[s];
-    }
-    double* o = O + h * D;
-    for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
-    for (int64_t s = 0; s < S; ++s) {
-      const double p = sc[s] / den;
-      const double* v = V + (h * S + s) * D;
-      for (int64_t d = 0; d < D; ++d) o[d] += p * v[d];
-    }
+    attend(qn, kn, V + h * S * D, S, D, sc, O + h * D);
     free(qn);
     free(kn);
     free(sc);

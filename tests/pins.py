@@ -402,6 +402,61 @@ def pin_qknorm_attention(lib):
     _close(_attn(lib, Q, K, V, g, g, 0.0), V[:, 3], rtol=1e-12, atol=1e-12)
 
 
+def _brute_plain_attention(Q, K, V):
+    getcontext().prec = 50
+    D = lambda x: Decimal(Fraction(float(x)).numerator) / Decimal(Fraction(float(x)).denominator)
+    out = []
+    for h in range(Q.shape[0]):
+        sc = [sum(D(a) * D(b) for a, b in zip(Q[h], K[h, s])) / Decimal(K.shape[2]).sqrt()
+              for s in range(K.shape[1])]
+        mx = max(sc)
+        e = [(x - mx).exp() for x in sc]
+        den = sum(e)
+        out.append([float(sum(e[s] / den * D(V[h, s, d]) for s in range(K.shape[1])))
+                    for d in range(K.shape[2])])
+    return np.array(out)
+
+
+def pin_attention(lib):
+    """The attention step alone (the unfused program's second kernel)."""
+    # Two keys, D = 2, no normalisation: q = [1, 0], k0 = [1, 0], k1 = [0, 1]:
+    # scores 1 / sqrt 2 and 0.
+    Q = np.array([[1.0, 0.0]])
+    K = np.array([[[1.0, 0.0], [0.0, 1.0]]])
+    V = np.array([[[1.0, 2.0], [3.0, 5.0]]])
+    e = math.exp(1.0 / math.sqrt(2.0))
+    p0 = e / (e + 1.0)
+    _close(oracle.attention(Q, K, V, lib=lib), [[p0 * 1 + (1 - p0) * 3, p0 * 2 + (1 - p0) * 5]])
+    rng = np.random.default_rng(43)
+    for (BH, S, D) in ((3, 5, 8), (2, 1, 4), (4, 7, 16)):
+        Q = rng.normal(size=(BH, D))
+        K = rng.normal(size=(BH, S, D))
+        V = rng.normal(size=(BH, S, D))
+        ref = oracle.attention(Q, K, V, lib=lib)
+        # one key: the weight is exactly 1
+        assert np.array_equal(oracle.attention(Q, K[:, :1], V[:, :1], lib=lib), V[:, 0])
+        # identical keys: the mean of the values
+        _close(oracle.attention(Q, np.repeat(K[:, :1], S, axis=1), V, lib=lib), V.mean(axis=1))
+        # a power-of-two scale may sit on the query or on the keys (exact)
+        _close(oracle.attention(4.0 * Q, K, V, lib=lib), oracle.attention(Q, 4.0 * K, V, lib=lib),
+               rtol=0, atol=0)
+        # keys (with their values) in another order
+        perm = rng.permutation(S)
+        _close(oracle.attention(Q, K[:, perm], V[:, perm], lib=lib), ref, rtol=1e-12, atol=1e-13)
+        # brute force at 50 digits
+        _close(ref, _brute_plain_attention(Q, K, V), rtol=1e-12, atol=1e-13)
+        # the fused definition is the unfused program: both vectors normalised as
+        # rows by the RMSNorm step, then this step -- the same operations
+        gq = rng.normal(1.0, 0.3, size=D)
+        gk = rng.normal(1.0, 0.3, size=D)
+        eps = 0.125
+        qn = oracle.rmsnorm(Q, gq, eps, lib=lib)
+        kn = oracle.rmsnorm(K.reshape(BH * S, D), gk, eps, lib=lib).reshape(BH, S, D)
+        assert np.array_equal(oracle.attention(qn, kn, V, lib=lib),
+                              oracle.qknorm_attention(Q, K, V, gq, gk, eps, lib=lib))
+
+
 ALL_PINS = [pin_worked_example, pin_library_matmul, pin_identity_weight, pin_constant_row,
             pin_scale_law, pin_gain_fold, pin_structure, pin_zero_row, pin_brute_force,
-            pin_gated_closed_forms, pin_unfused_steps, pin_lora, pin_qknorm_attention]
+            pin_gated_closed_forms, pin_unfused_steps, pin_lora, pin_qknorm_attention,
+            pin_attention]

@@ -39,11 +39,11 @@ MUTANTS = {
     "attn_scale_by_d": ("sc[s] = dot / sqrt((double)D);", "sc[s] = dot / (double)D;"),
     "attn_gk_on_query": ("normalise(Q + h * D, gq, &rq, 1, D, qn);",
                          "normalise(Q + h * D, gk, &rq, 1, D, qn);"),
-    "attn_key_rms_of_query": ("normalise(k, gk, &rk, 1, D, kn);",
-                              "normalise(k, gk, &rq, 1, D, kn);"),
+    "attn_key_rms_of_query": ("normalise(k, gk, &rk, 1, D, kn + s * D);",
+                              "normalise(k, gk, &rq, 1, D, kn + s * D);"),
     "attn_no_max_shift": ("sc[s] = exp(sc[s] - mx);", "sc[s] = exp(sc[s]);"),
-    "attn_values_reversed": ("const double* v = V + (h * S + s) * D;",
-                             "const double* v = V + (h * S + (S - 1 - s)) * D;"),
+    "attn_values_reversed": ("const double* v = Vh + s * D;",
+                             "const double* v = Vh + (S - 1 - s) * D;"),
     "attn_unnormalised_weights": ("const double p = sc[s] / den;", "const double p = sc[s];"),
     "lora_last_rank_skipped": ("for (int64_t r = 0; r < R; ++r) {\n      double t = 0.0;",
                                "for (int64_t r = 0; r < R - 1; ++r) {\n      double t = 0.0;"),

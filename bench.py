@@ -527,6 +527,30 @@ def main():
                     "with the adapter, three products) reads it back"}
         log(f"unfused: {ms_u / steps * 1e3:.2f} us/step (ours), {ms_v / steps * 1e3:.2f} us/step "
             f"(vendor GEMM); fused {ms / steps * 1e3:.2f}")
+    elif not args.no_unfused:
+        # QKNorm: RMSNorm of q and of every cached key written to memory, then
+        # the attention step alone on the normalised copies.
+        qn = [torch.empty_like(s["Q"]) for s in sets]
+        kn = [torch.empty_like(s["K"]) for s in sets]
+        na = tpa._binding.attention_workspace_bytes(dcode, wl.BH, wl.S, wl.D, 0)
+        wsa = tpa.Workspace(na, dev) if na > 0 else None
+
+        def unfused_attn(i):
+            s = sets[i]
+            tpa.rmsnorm(s["Q"], s["gq"], wl.eps, out=qn[i])
+            tpa.rmsnorm(s["K"].view(wl.BH * wl.S, wl.D), s["gk"], wl.eps,
+                        out=kn[i].view(wl.BH * wl.S, wl.D))
+            tpa.attention(qn[i], kn[i], s["V"], out=s["Y"], workspace=wsa)
+
+        run_u = make_runner(unfused_attn, not args.no_graph)
+        run_u(warm)
+        ms_u = time_steps(run_u, steps)
+        unfused = {
+            "ms_per_step": ms_u / steps, "fused_speedup": ms_u / ms,
+            "normalised_k_bytes": 2 * wl.BH * wl.S * wl.D * 2,
+            "note": "rmm_rmsnorm writes q*gq/RMS and every k*gk/RMS to memory, then "
+                    "rmm_attention reads the normalised keys back"}
+        log(f"unfused: {ms_u / steps * 1e3:.2f} us/step; fused {ms / steps * 1e3:.2f}")
 
     gbs = per_set / per_launch_s / 1e9
     tflops = wl.flops() / per_launch_s / 1e12

@@ -267,6 +267,19 @@ rmm_status rmm_plan_attention(const void* Q, const void* K, const void* V, const
                               int64_t D, rmm_dtype dtype, int splits, const void* ws,
                               size_t ws_bytes, int* chunks_out, int64_t* keys_per_chunk_out);
 
+/* The attention step alone (the second kernel of the unfused QKNorm +
+ * Attention program the same page's benchmark table compares against,
+ * "五、实验结果"): Q and K arrive already normalised (rmsnorm over rows of
+ * length D, one call for Q, one for K viewed as BH*S rows), and
+ *
+ *   O = sum_s softmax_s(q . k_s / sqrt(D)) v_s
+ *
+ * Layouts, dtype, alignment, size limits, workspace and error rules are
+ * those of qknorm_attention (the chunk count is chosen by the library). */
+rmm_status rmm_attention(const void* Q, const void* K, const void* V, void* O, int64_t BH,
+                         int64_t S, int64_t D, rmm_dtype dtype, void* ws, size_t ws_bytes,
+                         hipStream_t stream);
+
 /* A chain of L fused layers in one persistent launch (the multi-layer
  * decode that the Mirage pages' persistent-kernel runtime, "Mirage
  * Persistent Kernel" on the first page, runs as one kernel):

@@ -28,8 +28,8 @@ from . import _binding
 from ._binding import RmmError, load_library  # noqa: F401
 
 __all__ = ["rmsnorm_matmul", "rmsnorm_gated_mlp", "rmsnorm", "matmul", "gated_matmul",
-           "rmsnorm_lora", "lora_matmul", "qknorm_attention", "rmsnorm_matmul_chain", "RmmError",
-           "load_library", "Workspace"]
+           "rmsnorm_lora", "lora_matmul", "qknorm_attention", "attention", "rmsnorm_matmul_chain",
+           "RmmError", "load_library", "Workspace"]
 
 _DTYPES = {torch.float32: _binding.DTYPE_F32, torch.bfloat16: _binding.DTYPE_BF16}
 
@@ -285,6 +285,36 @@ def qknorm_attention(q, k, v, gq, gk, eps: float, out=None, splits: int = 0,
     _binding.check(load_library().qknorm_attention_ex(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), gq.data_ptr(), gk.data_ptr(), out.data_ptr(),
         float(eps), BH, S, D, dtype, splits, ws_ptr, ws_bytes, stream))
+    return out
+
+
+def attention(q, k, v, out=None, workspace: Workspace | None = None):
+    """o = softmax(q . k^T / sqrt(D)) v per batch-head, the attention step alone
+    (q and k already normalised; bf16; q: [BH, D], k, v: [BH, S, D], D = 64 or 128)."""
+    _check_operands([q, k, v], ["q", "k", "v"])
+    if q.dim() != 2 or k.dim() != 3:
+        raise ValueError("expected q: [BH, D], k, v: [BH, S, D]")
+    BH, D = q.shape
+    S = k.shape[1]
+    if tuple(k.shape) != (BH, S, D) or tuple(v.shape) != (BH, S, D):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, "
+                         f"v {tuple(v.shape)}")
+    if out is None:
+        out = torch.empty((BH, D), dtype=q.dtype, device=q.device)
+    else:
+        _check_operands([q, out], ["q", "out"])
+        if tuple(out.shape) != (BH, D):
+            raise ValueError(f"out has shape {tuple(out.shape)}, expected {(BH, D)}")
+    dtype = _DTYPES[q.dtype]
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    need = _binding.attention_workspace_bytes(dtype, BH, S, D, 0)
+    if workspace is None and need > 0:
+        workspace = _workspace_for(q.device, stream, need)
+    ws_ptr = workspace.ptr if workspace is not None else None
+    ws_bytes = workspace.nbytes if workspace is not None else 0
+    _binding.check(load_library().rmm_attention(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), BH, S, D, dtype, ws_ptr,
+        ws_bytes, stream))
     return out
 
 

@@ -434,7 +434,7 @@ rmm_status qknorm_attention_ex(const void* Q, const void* K, const void* V, cons
   const rmm_status st =
       attn_plan_call(Q, K, V, gq, gk, O, eps, BH, S, D, dtype, splits, ws, ws_bytes, &plan);
   if (st != RMM_OK || BH == 0) return st;
-  const AttnArgs a{Q, K, V, gq, gk, O, eps, BH, S, D, stream};
+  const AttnArgs a{Q, K, V, gq, gk, O, eps, BH, S, D, stream, 1};
   const hipError_t err = rmm_launch_attention(a, plan, plan.chunks > 1 ? ws : nullptr);
   if (err != hipSuccess) {
     g_last_hip_error = (int)err;
@@ -447,6 +447,24 @@ rmm_status qknorm_attention(const void* Q, const void* K, const void* V, const v
                             const void* gk, void* O, float eps, int64_t BH, int64_t S, int64_t D,
                             rmm_dtype dtype, void* ws, size_t ws_bytes, hipStream_t stream) {
   return qknorm_attention_ex(Q, K, V, gq, gk, O, eps, BH, S, D, dtype, 0, ws, ws_bytes, stream);
+}
+
+rmm_status rmm_attention(const void* Q, const void* K, const void* V, void* O, int64_t BH,
+                         int64_t S, int64_t D, rmm_dtype dtype, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
+  // Validated as the fused call with Q standing in for both gains (the
+  // kernel does not read them) and eps = 0.
+  AttnPlan plan;
+  const rmm_status st =
+      attn_plan_call(Q, K, V, Q, Q, O, 0.0f, BH, S, D, dtype, 0, ws, ws_bytes, &plan);
+  if (st != RMM_OK || BH == 0) return st;
+  const AttnArgs a{Q, K, V, Q, Q, O, 0.0f, BH, S, D, stream, 0};
+  const hipError_t err = rmm_launch_attention(a, plan, plan.chunks > 1 ? ws : nullptr);
+  if (err != hipSuccess) {
+    g_last_hip_error = (int)err;
+    return RMM_ERR_HIP;
+  }
+  return RMM_OK;
 }
 
 size_t rmm_attention_workspace_bytes(rmm_dtype dtype, int64_t BH, int64_t S, int64_t D,

@@ -48,7 +48,9 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
-template <int D>
+// NORM = false: plain scaled dot-product attention on q and k as given (the
+// second kernel of the unfused program; the gains are not read).
+template <int D, bool NORM>
 __global__ __launch_bounds__(AT_THREADS) void qknorm_attention_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc,
     const bf16_t* __restrict__ gq, const bf16_t* __restrict__ gk, bf16_t* __restrict__ O,
@@ -74,8 +76,9 @@ __global__ __launch_bounds__(AT_THREADS) void qknorm_attention_kernel(
   float qss = 0.f;
   {
     const u32x4 qv = *(const u32x4*)(Q + bh * D + 8 * c);
-    const u32x4 a = *(const u32x4*)(gq + 8 * c);
-    const u32x4 b = *(const u32x4*)(gk + 8 * c);
+    constexpr u32x4 ones{kBf16OnePair, kBf16OnePair, kBf16OnePair, kBf16OnePair};
+    const u32x4 a = NORM ? *(const u32x4*)(gq + 8 * c) : ones;
+    const u32x4 b = NORM ? *(const u32x4*)(gk + 8 * c) : ones;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
       const float q0 = bf16_lo(qv[d]), q1 = bf16_hi(qv[d]);
@@ -86,8 +89,10 @@ __global__ __launch_bounds__(AT_THREADS) void qknorm_attention_kernel(
 #pragma unroll
     for (int o = 1; o < LPK; o <<= 1) qss += __shfl_xor(qss, o);
   }
-  // 1 / (rms(q) sqrt(D)), IEEE divide and square root.
-  const float cq = 1.0f / (__fsqrt_rn(__fdiv_rn(qss, (float)D) + eps) * __fsqrt_rn((float)D));
+  // 1 / (rms(q) sqrt(D)), IEEE divide and square root (plain: 1 / sqrt(D)).
+  const float cq = NORM
+      ? 1.0f / (__fsqrt_rn(__fdiv_rn(qss, (float)D) + eps) * __fsqrt_rn((float)D))
+      : 1.0f / __fsqrt_rn((float)D);
 
   // Buffer resources over this batch-head's S x D rows (the plan keeps
   // S * D * 2 below 2^31), so offsets are 32-bit and past-the-end reads zero.
@@ -121,13 +126,13 @@ __global__ __launch_bounds__(AT_THREADS) void qknorm_attention_kernel(
       for (int d = 0; d < 4; ++d) {
         const float k0 = bf16_lo(kk[uu][d]), k1 = bf16_hi(kk[uu][d]);
         dot += u[2 * d] * k0 + u[2 * d + 1] * k1;
-        ss += k0 * k0 + k1 * k1;
+        if (NORM) ss += k0 * k0 + k1 * k1;
       }
       dot = group_sum<LPK>(dot);
-      ss = group_sum<LPK>(ss);
+      if (NORM) ss = group_sum<LPK>(ss);
       ok[uu] = key_of(blk, uu) < s_hi;
       // 1/D is a power of two (exact); v_rsq_f32 for the key's 1/RMS.
-      sc[uu] = dot * cq * __builtin_amdgcn_rsqf(ss * (1.0f / D) + eps);
+      sc[uu] = NORM ? dot * cq * __builtin_amdgcn_rsqf(ss * (1.0f / D) + eps) : dot * cq;
       if (ok[uu]) mb = fmaxf(mb, sc[uu]);
     }
     const float mn = fmaxf(m, mb);
@@ -283,16 +288,17 @@ hipError_t rmm_launch_attention(const AttnArgs& a, const AttnPlan& p, void* ws) 
   unsigned* cnt = (ws && p.chunks > 1) ? (unsigned*)(base + p.ws_cnt_off) : nullptr;
   float* part = (ws && p.chunks > 1) ? (float*)(base + p.ws_part_off) : nullptr;
   const dim3 grid((unsigned)(a.BH * p.chunks)), block(AT_THREADS);
+  auto launch = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, block, 0, a.stream, (const bf16_t*)a.Q, (const bf16_t*)a.K,
+                       (const bf16_t*)a.V, (const bf16_t*)a.gq, (const bf16_t*)a.gk, (bf16_t*)a.O,
+                       a.eps, a.S, p.kchunk, p.chunks, cnt, part);
+  };
   if (a.D == 128)
-    hipLaunchKernelGGL((qknorm_attention_kernel<128>), grid, block, 0, a.stream,
-                       (const bf16_t*)a.Q, (const bf16_t*)a.K, (const bf16_t*)a.V,
-                       (const bf16_t*)a.gq, (const bf16_t*)a.gk, (bf16_t*)a.O, a.eps, a.S,
-                       p.kchunk, p.chunks, cnt, part);
+    a.norm ? launch(qknorm_attention_kernel<128, true>)
+           : launch(qknorm_attention_kernel<128, false>);
   else if (a.D == 64)
-    hipLaunchKernelGGL((qknorm_attention_kernel<64>), grid, block, 0, a.stream,
-                       (const bf16_t*)a.Q, (const bf16_t*)a.K, (const bf16_t*)a.V,
-                       (const bf16_t*)a.gq, (const bf16_t*)a.gk, (bf16_t*)a.O, a.eps, a.S,
-                       p.kchunk, p.chunks, cnt, part);
+    a.norm ? launch(qknorm_attention_kernel<64, true>)
+           : launch(qknorm_attention_kernel<64, false>);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -182,6 +182,7 @@ struct AttnArgs {
   float eps;
   int64_t BH, S, D;
   hipStream_t stream;
+  int norm;  // 1: QKNorm + attention; 0: attention on q and k as given (gains unused)
 };
 struct AttnPlan {
   int64_t kchunk;  // keys per workgroup (a multiple of the workgroup's 64- or 128-key round)

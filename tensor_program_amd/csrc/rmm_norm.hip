@@ -10,7 +10,8 @@
 // the workgroup, then the row is scaled and stored (bf16: the fp32 value
 // X*g*(1/RMS) rounded once to nearest even).  Rows of bf16 with K % 8 == 0
 // and 16-byte-aligned pointers move 16 bytes per lane; anything else goes
-// element by element.
+// element by element.  Short aligned bf16 rows (K = 64 .. 512, at most 2^24
+// rows) take a group of lanes per row instead, many rows per workgroup.
 #include "rmm_device.h"
 
 namespace rmm {
@@ -75,6 +76,38 @@ __global__ __launch_bounds__(NORM_THREADS) void rmsnorm_kernel(const T* __restri
   }
 }
 
+// Short bf16 rows (K = 8 LPR, LPR a power of two up to 64; 16-byte aligned):
+// a group of LPR lanes per row, NORM_THREADS / LPR rows per workgroup, the
+// sum of squares reduced within the group by lane shuffles.  Same arithmetic
+// as rmsnorm_kernel.  (The unfused QKNorm program normalises every cached
+// key, rows of 64 or 128.)
+template <int LPR>
+__global__ __launch_bounds__(NORM_THREADS) void rmsnorm_rows_kernel(const bf16_t* __restrict__ X,
+                                                                    const bf16_t* __restrict__ g,
+                                                                    bf16_t* __restrict__ Xn,
+                                                                    float eps, int64_t M) {
+  constexpr int K = 8 * LPR, RPB = NORM_THREADS / LPR;
+  const int tid = threadIdx.x, c = tid % LPR;
+  const int64_t m = (int64_t)blockIdx.x * RPB + tid / LPR;
+  const bool ok = m < M;  // the whole group agrees
+  const u32x4 v = ok ? *(const u32x4*)(X + m * K + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+  float ss = 0.f;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const float a = bf16_lo(v[d]), b = bf16_hi(v[d]);
+    ss += a * a + b * b;
+  }
+#pragma unroll
+  for (int o = 1; o < LPR; o <<= 1) ss += __shfl_xor(ss, o);
+  const float inv = inv_rms(ss, K, eps);
+  const u32x4 gv = *(const u32x4*)(g + 8 * c);
+  u32x4 o;
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+    o[d] = pack_bf16x2(bf16_lo(v[d]) * bf16_lo(gv[d]) * inv, bf16_hi(v[d]) * bf16_hi(gv[d]) * inv);
+  if (ok) *(u32x4*)(Xn + m * K + 8 * c) = o;
+}
+
 }  // namespace rmm
 
 hipError_t rmm_launch_rmsnorm(const void* X, const void* g, void* Xn, float eps, int64_t M,
@@ -83,7 +116,17 @@ hipError_t rmm_launch_rmsnorm(const void* X, const void* g, void* Xn, float eps,
   const dim3 grid((unsigned)(M < (1 << 20) ? M : (1 << 20))), block(NORM_THREADS);
   if (bf16) {
     const bool vec = K % 8 == 0 && (((uintptr_t)X | (uintptr_t)g | (uintptr_t)Xn) & 15u) == 0;
-    if (vec)
+    if (vec && (K == 64 || K == 128 || K == 256 || K == 512) && M <= (1 << 24)) {
+      auto rows = [&](auto kernel, int lpr) {
+        const int64_t rpb = NORM_THREADS / lpr;
+        hipLaunchKernelGGL(kernel, dim3((unsigned)((M + rpb - 1) / rpb)), block, 0, stream,
+                           (const bf16_t*)X, (const bf16_t*)g, (bf16_t*)Xn, eps, M);
+      };
+      if (K == 64) rows(rmsnorm_rows_kernel<8>, 8);
+      else if (K == 128) rows(rmsnorm_rows_kernel<16>, 16);
+      else if (K == 256) rows(rmsnorm_rows_kernel<32>, 32);
+      else rows(rmsnorm_rows_kernel<64>, 64);
+    } else if (vec)
       hipLaunchKernelGGL((rmsnorm_kernel<bf16_t, true>), grid, block, 0, stream,
                          (const bf16_t*)X, (const bf16_t*)g, (bf16_t*)Xn, eps, M, K);
     else

@@ -132,3 +132,46 @@ def test_binding_workspace_per_layout(require_gpu):
     ref = oracle.qknorm_attention(inp.Q[heads], inp.K[heads], inp.V[heads], inp.gq, inp.gk,
                                   oracle.eps_as_passed(wl.eps))
     _check(o[torch.from_numpy(heads).cuda()], ref, "after a smaller call")
+
+
+# The unfused program the benchmark table compares against: RMSNorm of q
+# and of every key written to memory, then the attention step alone.
+
+@pytest.mark.parametrize("case", [(16, 1, 128), (16, 100, 64), (16, 1000, 128), (8, 4096, 64),
+                                  (3, 65, 128)], ids=lambda c: "x".join(map(str, c)))
+def test_attention_step_random(case, require_gpu):
+    BH, S, D = case
+    _log(f"attention step {case}")
+    inp = synth.make_attention_inputs(BH, S, D, seed=S + 1)
+    o = tpa.attention(_dev(inp, "Q"), _dev(inp, "K"), _dev(inp, "V"))
+    torch.cuda.synchronize()
+    _check(o, oracle.attention(inp.Q, inp.K, inp.V), f"step {case}")
+
+
+@pytest.mark.parametrize("case", [(16, 1000, 128), (8, 4096, 64)],
+                         ids=lambda c: "x".join(map(str, c)))
+def test_unfused_qknorm_program(case, require_gpu):
+    BH, S, D = case
+    eps = 1e-6
+    _log(f"unfused qknorm program {case}")
+    inp = synth.make_attention_inputs(BH, S, D, seed=S + 2)
+    qn = tpa.rmsnorm(_dev(inp, "Q"), _dev(inp, "gq"), eps)
+    kn = tpa.rmsnorm(_dev(inp, "K").view(BH * S, D), _dev(inp, "gk"), eps).view(BH, S, D)
+    o = tpa.attention(qn, kn, _dev(inp, "V"))
+    torch.cuda.synchronize()
+    e = oracle.eps_as_passed(eps)
+    _check(o, oracle.qknorm_attention(inp.Q, inp.K, inp.V, inp.gq, inp.gk, e), f"program {case}")
+
+
+def test_unfused_qknorm_workload_sampled(require_gpu):
+    wl = synth.get_workload("attn_bh256_s2048_d128")
+    _log("unfused qknorm program, benchmark workload")
+    inp = synth.make_attention_inputs(wl.BH, wl.S, wl.D)
+    qn = tpa.rmsnorm(_dev(inp, "Q"), _dev(inp, "gq"), wl.eps)
+    kn = tpa.rmsnorm(_dev(inp, "K").view(wl.BH * wl.S, wl.D), _dev(inp, "gk"), wl.eps)
+    o = tpa.attention(qn, kn.view(wl.BH, wl.S, wl.D), _dev(inp, "V"))
+    heads = np.unique(np.concatenate([[0, wl.BH - 1],
+                                      np.random.default_rng(5).choice(wl.BH, 20, replace=False)]))
+    ref = oracle.qknorm_attention(inp.Q[heads], inp.K[heads], inp.V[heads], inp.gq, inp.gk,
+                                  oracle.eps_as_passed(wl.eps))
+    _check(o[torch.from_numpy(heads).cuda()], ref, "unfused workload")

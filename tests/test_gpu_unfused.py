@@ -119,3 +119,21 @@ def test_unfused_program_matches_definition(name, require_gpu):
     else:
         ref = oracle.rmsnorm_matmul(inp.X, inp.g, inp.W1, e)
     assert_within_tol(y, ref, tol_for(wl.dtype), f"unfused {name}")
+
+
+@pytest.mark.parametrize("shape", [(1, 64), (33, 64), (31, 128), (1000, 128), (9, 256),
+                                   (300, 512), (65536, 128)], ids=lambda s: "x".join(map(str, s)))
+def test_rmsnorm_short_rows(shape, require_gpu):
+    # Rows of 64 .. 512 (many rows per workgroup, a ragged last workgroup):
+    # the per-key normalisation of the unfused QKNorm program.
+    M, K = shape
+    _log(f"rmsnorm short rows {shape}")
+    wl = synth.Workload("rows", "bf16", M, K, 8, 1e-6, False, None)
+    inp = synth.make_inputs(wl, weights=False)
+    x = to_device(inp, "X")
+    big = torch.full((M * K + 512,), 7.0, dtype=x.dtype, device="cuda")
+    out = big[256:256 + M * K].view(M, K)
+    xn = from_device(tpa.rmsnorm(x, to_device(inp, "g"), 1e-6, out=out))
+    ref = oracle.rmsnorm(inp.X, inp.g, oracle.eps_as_passed(1e-6))
+    _check_rows(xn, ref, "bf16", f"short rows {shape}")
+    assert torch.all(big[:256] == 7.0) and torch.all(big[256 + M * K:] == 7.0)

@@ -39,8 +39,9 @@
  * enqueue on `stream` (NULL = the default stream) and return; Y is valid once
  * the stream has reached that point.
  *
- * Workspace.  The decode (split-K) variant combines partial k-sums across
- * workgroups through a caller-owned workspace.  `ws` may be NULL: the library
+ * Workspace.  The split-K forms (the decode variant, the stream variant's
+ * split form, the prefill split for few output tiles) combine partial k-sums
+ * across workgroups through a caller-owned workspace.  `ws` may be NULL: the library
  * then picks a variant that needs none (correct, slower).  A non-NULL `ws` must
  * be zero-filled before its first use.  Every layout keeps its arrival
  * counters in the workspace's first 64 KiB and its partial sums after that;
@@ -50,7 +51,9 @@
  * long as each call runs to completion (a call forced to a split count
  * needing more than 16320 counters returns RMM_ERR_VARIANT).  One workspace
  * must not be used by two calls that may run at the same time.  ws_bytes
- * below rmm_workspace_bytes*() returns RMM_ERR_WORKSPACE.
+ * below rmm_workspace_bytes*() returns RMM_ERR_WORKSPACE, except where AUTO
+ * picks the prefill split: it then takes the best count that fits (down to
+ * no split).
  *
  * Errors.  Validation happens on the host before any HIP call, in this order:
  *   RMM_ERR_NULL      a NULL data pointer (when M*N > 0)
@@ -109,8 +112,15 @@ typedef enum {
  *             fp32: M <= 32 (16 rows per launch), not gated, no adapter,
  *             16-byte aligned pointers; the same split-K scheme with fp32 fused
  *             multiply-adds (no bf16 rounding).  Bandwidth-bound.
- *   PREFILL : not gated; LDS-tiled MFMA GEMM with the row sum of squares
- *             fused into its k-loop.  Matrix-core-bound shapes.
+ *   PREFILL : LDS-tiled MFMA GEMM with the row sum of squares fused into
+ *             its k-loop (gated: both products in one tile).  Matrix-core-
+ *             bound shapes.  Plain calls with few output tiles (at most 128
+ *             tiles of 256 x 256) and a workspace split K into ranges of
+ *             whole 64-deep steps: each workgroup writes its range's fp32
+ *             sums and row sums of squares to the workspace, and a second
+ *             kernel adds the ranges in order and applies 1/RMS.  AUTO
+ *             takes this form above 64 rows when a workspace is passed, with
+ *             a count whose partial sums fit in that workspace.
  *   STREAM  : gated: any M; plain: M <= 128, or M <= 256 with N <= 4096
  *             (above 64 rows: one launch per 64-row block); each
  *             workgroup streams 64-column strips of W (W1 and W3 when
@@ -140,7 +150,8 @@ rmm_status rmsnorm_matmul(const void* X, const void* g, const void* W, void* Y, 
  * GPU, held until the process ends; its device address is looked up once per
  * device on the first call there).  Validation and errors as rmsnorm_matmul,
  * plus RMM_ERR_SCRATCH when the call would need more than 16 MiB of scratch
- * (never for M <= 32, nor for the stream variant's split form); nothing is
+ * (never for M <= 32, nor for the stream variant's split form, nor for the
+ * prefill split, whose count is chosen to fit the array); nothing is
  * allocated or freed.  Every call on one GPU shares that array: calls that
  * may overlap on one GPU (different streams or threads) race and must be
  * serialised by the caller.  A call leaves the array's counters zeroed for
@@ -156,9 +167,12 @@ rmm_status rmsnorm_gated_mlp(const void* X, const void* g, const void* W1, const
                              rmm_dtype dtype, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* As above with a forced variant.  splits: number of K chunks the DECODE
- * variant combines across workgroups (0 = chosen by the library, 1 = no
- * cross-workgroup combine, so no workspace is needed); must be 0 for the
- * other variants. */
+ * variant, or the plain PREFILL variant, combines across workgroups (0 =
+ * chosen by the library, 1 = no cross-workgroup combine, so no workspace is
+ * needed; PREFILL rounds a forced count to whole, even ranges of 64-deep
+ * steps, so the count that runs, reported by rmm_plan, may be lower; above
+ * ceil(K / 64) or with partial sums above 2 GiB: RMM_ERR_VARIANT); must be
+ * 0 for the other variants and for gated PREFILL. */
 rmm_status rmsnorm_matmul_ex(const void* X, const void* g, const void* W, void* Y, float eps,
                              int64_t M, int64_t N, int64_t K, rmm_dtype dtype,
                              rmm_variant variant, int splits, void* ws, size_t ws_bytes,

@@ -86,13 +86,16 @@ int auto_decode_splits(int64_t N, int64_t K) {
 }
 
 // Shape/variant part of the plan; `aligned` says whether every pointer is
-// 16-byte aligned, `have_ws` whether a workspace was passed.
+// 16-byte aligned, `have_ws` whether a workspace was passed, `ws_avail` its
+// size (SIZE_MAX when only sizes are asked for): the library's choice of a
+// prefill split keeps its partial sums within it.
 rmm_status plan_shape(int64_t M, int64_t N, int64_t K, rmm_dtype dtype, int gated,
                       rmm_variant variant, int splits, bool aligned, bool have_ws, Plan* out,
-                      int64_t R = 0) {
+                      int64_t R = 0, size_t ws_avail = SIZE_MAX) {
   if (variant < RMM_VARIANT_AUTO || variant > RMM_VARIANT_STREAM) return RMM_ERR_VARIANT;
   if (splits < 0) return RMM_ERR_VARIANT;
-  if (splits != 0 && variant != RMM_VARIANT_DECODE) return RMM_ERR_VARIANT;
+  if (splits != 0 && variant != RMM_VARIANT_DECODE && !(variant == RMM_VARIANT_PREFILL && !gated))
+    return RMM_ERR_VARIANT;
   if (M == 0 || N == 0) {  // nothing to compute, nothing launched
     out->variant = variant == RMM_VARIANT_AUTO ? RMM_VARIANT_GENERIC : variant;
     out->splits = 1;
@@ -126,10 +129,12 @@ rmm_status plan_shape(int64_t M, int64_t N, int64_t K, rmm_dtype dtype, int gate
                                                  : RMM_VARIANT_GENERIC;
     else if (decode_ok)
       v = RMM_VARIANT_DECODE;
-    else if (stream_ok)  // M <= 64: far faster than one row of 256 x 256 prefill tiles
-      v = RMM_VARIANT_STREAM;
+    else if (stream_ok && (M <= kStreamRows || !have_ws))
+      v = RMM_VARIANT_STREAM;  // far faster than one row of unsplit 256 x 256 prefill tiles
+    else if (prefill_ok)       // above 64 rows with a workspace: the prefill split
+      v = RMM_VARIANT_PREFILL;
     else
-      v = prefill_ok ? RMM_VARIANT_PREFILL : RMM_VARIANT_GENERIC;
+      v = stream_ok ? RMM_VARIANT_STREAM : RMM_VARIANT_GENERIC;
   }
   if (v == RMM_VARIANT_DECODE && !decode_ok) return RMM_ERR_VARIANT;
   if (v == RMM_VARIANT_PREFILL && !prefill_ok) return RMM_ERR_VARIANT;
@@ -159,7 +164,12 @@ rmm_status plan_shape(int64_t M, int64_t N, int64_t K, rmm_dtype dtype, int gate
     out->splits = out->dec.splits;
     out->ws_bytes = out->dec.ws_bytes;
   } else if (v == RMM_VARIANT_PREFILL) {
-    rmm_prefill_plan(M, N, K, gated, &out->pre);
+    if (splits > (K + 63) / 64) return RMM_ERR_VARIANT;
+    if (splits > 1 && !have_ws) return RMM_ERR_WORKSPACE;  // a forced split count needs one
+    rmm_prefill_plan(M, N, K, gated, splits, have_ws ? ws_avail : 0, &out->pre);
+    if (out->pre.ws_bytes > (size_t)INT32_MAX) return RMM_ERR_VARIANT;
+    out->splits = out->pre.splits;
+    out->ws_bytes = out->pre.ws_bytes;
   } else if (v == RMM_VARIANT_STREAM) {
     rmm_stream_plan(N, K, gated, (int)kTargetWorkgroups, have_ws, &out->st);
     if (out->st.ws_bytes > (size_t)INT32_MAX) return RMM_ERR_VARIANT;  // 32-bit offsets
@@ -207,7 +217,8 @@ rmm_status plan_call(const void* X, const void* g, const void* W1, const void* W
                                  (!gated || aligned16(W3)) && aligned16(Y) &&
                                  (!lora || (aligned16(LA) && aligned16(LB))));
   rmm_status st =
-      plan_shape(M, N, K, dtype, gated, variant, splits, aligned, ws != nullptr, out, rank);
+      plan_shape(M, N, K, dtype, gated, variant, splits, aligned, ws != nullptr, out, rank,
+                 ws ? ws_bytes : 0);
   if (st != RMM_OK) return st;
   // 7. workspace
   if (ws && ws_bytes < out->ws_bytes) return RMM_ERR_WORKSPACE;
@@ -257,7 +268,7 @@ rmm_status run(const void* X, const void* g, const void* W1, const void* W3, voi
         }
       break;
     case RMM_VARIANT_PREFILL:
-      err = rmm_launch_prefill(a, plan.pre);
+      err = rmm_launch_prefill(a, plan.pre, plan.pre.splits > 1 ? ws : nullptr);
       break;
     case RMM_VARIANT_STREAM:
       // Row blocks of 64, in order on the stream (the split form's workspace
@@ -360,6 +371,18 @@ rmm_status chain_plan_call(const void* X0, const void* G, const void* W, const v
 }
 
 }  // namespace
+
+size_t rmm_workspace_bytes_within(int dtype, int64_t M, int64_t N, int64_t K, int gated,
+                                  size_t cap) {
+  if (M < 0 || N < 0 || K <= 0) return 0;
+  if (dtype != RMM_DTYPE_F32 && dtype != RMM_DTYPE_BF16) return 0;
+  Plan plan;
+  if (plan_shape(M, N, K, (rmm_dtype)dtype, gated ? 1 : 0, RMM_VARIANT_AUTO, 0, true, true, &plan,
+                 0, cap) !=
+      RMM_OK)
+    return 0;
+  return plan.ws_bytes;
+}
 
 extern "C" {
 
@@ -526,6 +549,7 @@ size_t rmm_workspace_bytes_ex(rmm_dtype dtype, int64_t M, int64_t N, int64_t K, 
 size_t rmm_workspace_bytes(rmm_dtype dtype, int64_t M, int64_t N, int64_t K, int gated) {
   return rmm_workspace_bytes_ex(dtype, M, N, K, gated, RMM_VARIANT_AUTO, 0);
 }
+
 
 size_t rmm_lora_workspace_bytes(rmm_dtype dtype, int64_t M, int64_t N, int64_t K, int64_t R,
                                 rmm_variant variant, int splits) {

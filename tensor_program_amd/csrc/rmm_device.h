@@ -151,9 +151,20 @@ struct PrefillPlan {
   int tiles_m, tiles_n;  // output tiles: 256 x 256, gated 128 x 128 (of each weight)
   int group_m;           // tile-rows walked together (L2 reuse)
   int xcd_remap;         // contiguous tile ranges per XCD
+  int splits;            // K ranges (plain tile only; > 1: partial sums + combine kernel)
+  int ksteps;            // 64-deep k-steps per range (even when splits > 1)
+  size_t ws_part_off, ws_bytes;
 };
-void rmm_prefill_plan(int64_t M, int64_t N, int64_t K, int gated, PrefillPlan* p);
-hipError_t rmm_launch_prefill(const RmmArgs& a, const PrefillPlan& p);
+// splits: 0 = chosen by the library (a split only if its partial sums fit
+// in ws_avail bytes of workspace), else the requested count (the count that
+// runs may be lower: whole, even ranges).
+void rmm_prefill_plan(int64_t M, int64_t N, int64_t K, int gated, int splits, size_t ws_avail,
+                      PrefillPlan* p);
+// Workspace bytes of an AUTO plain or gated call given a workspace of `cap`
+// bytes (the prefill split is chosen to fit), 0 for invalid arguments.
+size_t rmm_workspace_bytes_within(int dtype, int64_t M, int64_t N, int64_t K, int gated,
+                                  size_t cap);
+hipError_t rmm_launch_prefill(const RmmArgs& a, const PrefillPlan& p, void* ws);
 
 // Stream variant: one workgroup per 64-column strip, or (split form, with a
 // workspace, when there are fewer strips than workgroups wanted) `grid`

@@ -59,7 +59,7 @@ rmm_status rmsnorm_matmul_noalloc(const void* X, const void* g, const void* W, v
                                  0, nullptr, 0, nullptr, nullptr);
   if (st != RMM_OK) return st;
   if (M == 0 || N == 0) return RMM_OK;
-  const size_t need = rmm_workspace_bytes(dtype, M, N, K, 0);
+  const size_t need = rmm_workspace_bytes_within(dtype, M, N, K, 0, kScratchBytes);
   if (need > kScratchBytes) return RMM_ERR_SCRATCH;
   void* ws = nullptr;
   if (need > 0) {

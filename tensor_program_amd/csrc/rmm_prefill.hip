@@ -78,11 +78,13 @@ __device__ __forceinline__ u32x4 pf_load16(uint32_t voff, i32x4 rsrc) {
   return v;
 }
 
+// Columns at or past klim (K, or the end of this workgroup's K range) read
+// as zeros.
 template <bool GL>
 __device__ __forceinline__ void pf_load_a(PfA& st, i32x4 xr, i32x4 gr, int64_t m0, int64_t k0,
-                                          int64_t M, int64_t K, int tid) {
+                                          int64_t M, int64_t K, int64_t klim, int tid) {
   const int64_t ka = k0 + 8 * (tid & 7);
-  const bool ka_ok = ka < K;  // K % 8 == 0: a chunk is all in or all out
+  const bool ka_ok = ka < klim;  // klim % 8 == 0: a chunk is all in or all out
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t m = m0 + (tid >> 3) + 64 * i;
@@ -124,8 +126,9 @@ __device__ __forceinline__ void pf_lds_load16(uint32_t lds_addr, uint32_t voff, 
 // W block of step k0 into an LDS stage: wave w fills the four 1-KB blocks
 // 4w .. 4w+3 (two k-rows each); lane l of a block lands at byte 16 l of the
 // block, so it fetches the logical chunk the swizzle maps there.  The
-// resource starts at row k0, so rows past K fall outside it and read as
-// zeros; columns past N are given an out-of-range offset.
+// resource spans rows k0 .. klim - 1, so rows at or past klim (K, or the
+// end of this workgroup's K range) read as zeros; columns past N are given
+// an out-of-range offset.
 struct PfDma {
   uint32_t off[4];  // per-lane byte offsets from row k0 (step independent)
 };
@@ -142,8 +145,8 @@ __device__ __forceinline__ void pf_dma_setup(PfDma& d, int64_t n0, int64_t N, in
 }
 
 __device__ __forceinline__ void pf_dma_b(uint32_t b_lds, const PfDma& d, const bf16_t* W,
-                                         int64_t k0, int64_t N, int64_t K, int w) {
-  const int64_t rows = K - k0 > 0 ? K - k0 : 0;
+                                         int64_t k0, int64_t N, int64_t klim, int w) {
+  const int64_t rows = klim - k0 > 0 ? klim - k0 : 0;
   const i32x4 rsrc = pf_rsrc(W + k0 * N, (uint32_t)(rows * N * 2));
 #pragma unroll
   for (int q = 0; q < 4; ++q) pf_lds_load16(b_lds + (4 * w + q) * 1024, d.off[q], rsrc);
@@ -323,7 +326,8 @@ template <bool GATED, bool GL>
 __global__ __launch_bounds__(PF_THREADS, 2) void prefill_kernel(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ g, const bf16_t* __restrict__ W1,
     const bf16_t* __restrict__ W3, bf16_t* __restrict__ Y, float eps, int64_t M, int64_t N,
-    int64_t K, int tiles_m, int tiles_n, int group_m, int xcd_remap, int norm) {
+    int64_t K, int tiles_m, int tiles_n, int group_m, int xcd_remap, int norm, int splits,
+    int ksteps, float* __restrict__ part) {
   static_assert(!GATED, "the gated tile is prefill_gated_kernel");
   // Loads per thread per k-step outside the W transfers: 4 rows of X, and
   // the gain unless it sits in LDS.
@@ -339,12 +343,15 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_kernel(
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   // Tile order: with xcd_remap, XCD x (workgroups bid % 8 == x) takes a
-  // contiguous range of the tile sequence; the sequence walks groups of
-  // group_m tile-rows column by column, so concurrently resident workgroups
-  // of one XCD share A and B tiles in its L2.
+  // contiguous range of the sequence of (K range, tile) pairs, K range
+  // major; the tiles of one K range are walked in groups of group_m
+  // tile-rows, column by column, so concurrently resident workgroups of one
+  // XCD share A and B tiles in its L2.
   const int ntiles = tiles_m * tiles_n;
   int t = blockIdx.x;
-  if (xcd_remap) t = (t & 7) * (ntiles >> 3) + (t >> 3);
+  if (xcd_remap) t = (t & 7) * ((ntiles * splits) >> 3) + (t >> 3);
+  const int split = t / ntiles;
+  t -= split * ntiles;
   const int group = group_m * tiles_n;
   const int gid = t / group, first_m = gid * group_m;
   const int gm = (tiles_m - first_m < group_m) ? (tiles_m - first_m) : group_m;
@@ -377,7 +384,13 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_kernel(
   const int bk = 8 * (bG >> 1) + (bi >> 2);
   const int bn = wn * 64 + 16 * (bG & 1) + 4 * (bi & 3);
   const int bo0 = pf_b_off(bk, bn), bo1 = pf_b_off(bk, bn + 32);
+  // This workgroup's k-steps kt0 .. kt1 - 1 (all of K without a split; a
+  // split's ksteps is even, so only the last range can end on an odd step);
+  // every load at or past klim reads zeros.
   const int nk = (int)((K + PF_BK - 1) / PF_BK);
+  const int kt0 = split * ksteps;
+  const int kt1 = kt0 + ksteps < nk ? kt0 + ksteps : nk;
+  const int64_t klim = (int64_t)kt1 * PF_BK < K ? (int64_t)kt1 * PF_BK : K;
 
   // Pipeline, with LDS stage kt&1 holding step kt at the top of iteration kt:
   // W of step kt+1 streams into the other W stage, X of step kt+1 (in
@@ -396,31 +409,34 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_kernel(
     __syncthreads();
   }
 
+  const int64_t kb0 = (int64_t)kt0 * PF_BK;
   PfA sa, sb;
-  pf_dma_b(b0a, dma, W1, 0, N, K, w);
-  pf_load_a<GL>(sa, xr, gr, m0, 0, M, K, tid);
-  pf_load_a<GL>(sb, xr, gr, m0, PF_BK, M, K, tid);
+  pf_dma_b(b0a, dma, W1, kb0, N, klim, w);
+  pf_load_a<GL>(sa, xr, gr, m0, kb0, M, K, klim, tid);
+  pf_load_a<GL>(sb, xr, gr, m0, kb0 + PF_BK, M, K, klim, tid);
   pf_wait_a<XL, GL>(sa);
-  pf_store_a<GL>(sa, a_s0, ss, tid, 0, norm, g_s, 0);
-  pf_store_a<GL>(sa, a_s0, ss, tid, 2, norm, g_s, 0);
+  pf_store_a<GL>(sa, a_s0, ss, tid, 0, norm, g_s, kb0);
+  pf_store_a<GL>(sa, a_s0, ss, tid, 2, norm, g_s, kb0);
   PF_WAIT_VMCNT(0);
   __syncthreads();
 
   // Whole pairs of steps: with an odd step count the last one multiplies
-  // zeros (every operand past K reads as zero), which leaves the sums as
+  // zeros (every operand past klim reads as zero), which leaves the sums as
   // they are and keeps the accumulators in one place.
-  for (int kt = 0; kt < nk; kt += 2) {
+  for (int kt = kt0; kt < kt1; kt += 2) {
     pf_step<XL + 4, GL>(a_s0, b0s, a_s1, sb, acc, ss, a_base, bo0, bo1, tid, norm, g_s,
                         (int64_t)(kt + 1) * PF_BK, [&] {
-                          pf_dma_b(b1a, dma, W1, (int64_t)(kt + 1) * PF_BK, N, K, w);
-                          pf_load_a<GL>(sa, xr, gr, m0, (int64_t)(kt + 2) * PF_BK, M, K, tid);
+                          pf_dma_b(b1a, dma, W1, (int64_t)(kt + 1) * PF_BK, N, klim, w);
+                          pf_load_a<GL>(sa, xr, gr, m0, (int64_t)(kt + 2) * PF_BK, M, K, klim,
+                                        tid);
                         });
     PF_WAIT_VMCNT(XL);
     __syncthreads();
     pf_step<XL + 4, GL>(a_s1, b1s, a_s0, sa, acc, ss, a_base, bo0, bo1, tid, norm, g_s,
                         (int64_t)(kt + 2) * PF_BK, [&] {
-                          pf_dma_b(b0a, dma, W1, (int64_t)(kt + 2) * PF_BK, N, K, w);
-                          pf_load_a<GL>(sb, xr, gr, m0, (int64_t)(kt + 3) * PF_BK, M, K, tid);
+                          pf_dma_b(b0a, dma, W1, (int64_t)(kt + 2) * PF_BK, N, klim, w);
+                          pf_load_a<GL>(sb, xr, gr, m0, (int64_t)(kt + 3) * PF_BK, M, K, klim,
+                                        tid);
                         });
     PF_WAIT_VMCNT(XL);
     __syncthreads();
@@ -434,6 +450,37 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_kernel(
   PF_WAIT_VMCNT(0);
 
   // Row sums of squares: the 8 lanes tid&7 = 0..7 share rows (tid>>3) + 64 i.
+  if (splits > 1) {
+    // A K range of a split call: the raw sums go to the workspace, [split]
+    // [M][N] fp32, then the row sums of squares, [split][M] (written by the
+    // first tile-column; every tile-column computes the same values); the
+    // combine kernel adds the ranges in order and applies 1/RMS.
+    float* ssp = part + (int64_t)splits * M * N;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = ss[i];
+      v += __shfl_xor(v, 1);
+      v += __shfl_xor(v, 2);
+      v += __shfl_xor(v, 4);
+      const int64_t m = m0 + (tid >> 3) + 64 * i;
+      if (tn == 0 && (tid & 7) == 0 && m < M) ssp[(int64_t)split * M + m] = v;
+    }
+    float* pp = part + (int64_t)split * M * N;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int64_t n = n0 + wn * 64 + 32 * j + (l & 31);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int64_t m = m0 + wm * 128 + 32 * i + 8 * jj + 4 * (l >> 5) + r;
+            if (m < M && n < N) pp[m * N + n] = acc[i][j][4 * jj + r];
+          }
+      }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float v = ss[i];
@@ -808,29 +855,127 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_gated_kernel(
   }
 }
 
+// Second kernel of a split call (a split of K over workgroups, for shapes
+// with too few output tiles to fill the chip): Y = (sum of the K ranges' raw
+// sums) / RMS, the row's sum of squares likewise added over the ranges; both
+// sums in range order, so the result does not depend on which workgroup
+// finished first.  8 consecutive columns per thread (N % 8 == 0).
+constexpr int PC_THREADS = 256;
+
+__global__ __launch_bounds__(PC_THREADS) void prefill_combine_kernel(
+    const float* __restrict__ part, bf16_t* __restrict__ Y, float eps, int64_t M, int64_t N,
+    int64_t K, int splits, int norm) {
+  const int64_t n8 = N >> 3;
+  const int64_t idx = (int64_t)blockIdx.x * PC_THREADS + threadIdx.x;
+  if (idx >= M * n8) return;
+  const int64_t m = idx / n8, n = (idx - m * n8) * 8;
+  const float* ssp = part + (int64_t)splits * M * N;
+  float ss = 0.f, y[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) y[c] = 0.f;
+  for (int s = 0; s < splits; ++s) {
+    ss += ssp[(int64_t)s * M + m];
+    const float4* p = (const float4*)(part + ((int64_t)s * M + m) * N + n);
+    const float4 a = p[0], b = p[1];
+    y[0] += a.x; y[1] += a.y; y[2] += a.z; y[3] += a.w;
+    y[4] += b.x; y[5] += b.y; y[6] += b.z; y[7] += b.w;
+  }
+  const float inv = norm ? inv_rms(ss, K, eps) : 1.0f;
+  u32x4 o;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) o[d] = pack_bf16x2(y[2 * d] * inv, y[2 * d + 1] * inv);
+  *(u32x4*)(Y + m * N + n) = o;
+}
+
 }  // namespace rmm
 
-void rmm_prefill_plan(int64_t M, int64_t N, int64_t K, int gated, PrefillPlan* p) {
+// Split of K for the plain tile.  Without a forced count, with a workspace
+// and at most 128 output tiles (half the CUs), the count minimises a model
+// fitted to timings on this part (M = 129 .. 2048, N = 4096 and 14336,
+// K = 4096 and 14336): about 1.5 us per 64-deep k-step of a range, plus
+// about 0.4 us per MB of fp32 partial sums (written once, read back by the
+// combine kernel), with at most one workgroup per CU; ranges are whole,
+// even numbers of steps.  The partial sums must fit in ws_avail.
+namespace {
+struct SplitShape {
+  int64_t splits, ksteps;
+};
+SplitShape prefill_split_shape(int64_t nk, int64_t s) {
+  int64_t q = (nk + s - 1) / s;
+  q += q & 1;
+  return {(nk + q - 1) / q, q};
+}
+size_t prefill_split_bytes(int64_t M, int64_t N, int64_t S) {
+  return kWsCounterBytes + (size_t)(S * (M * N + M)) * 4;
+}
+}  // namespace
+
+void rmm_prefill_plan(int64_t M, int64_t N, int64_t K, int gated, int splits, size_t ws_avail,
+                      PrefillPlan* p) {
   using namespace rmm;
   const int bm = gated ? PG_BM : PF_BM, bn = gated ? PG_BNW : PF_BN;
   p->tiles_m = (int)((M + bm - 1) / bm);
   p->tiles_n = (int)((N + bn - 1) / bn);
   p->group_m = 4;
-  p->xcd_remap = ((int64_t)p->tiles_m * p->tiles_n) % 8 == 0;
+  const int64_t nk = (K + PF_BK - 1) / PF_BK;
+  const int64_t tiles = (int64_t)p->tiles_m * p->tiles_n;
+  p->splits = 1;
+  p->ksteps = (int)nk;
+  p->ws_part_off = 0;
+  p->ws_bytes = 0;
+  SplitShape best{1, nk};
+  if (!gated && splits > 1) {
+    best = prefill_split_shape(nk, splits);
+  } else if (!gated && splits == 0 && ws_avail > 0 && 2 * tiles <= 256 && nk >= 4) {
+    double best_us = 1.5 * nk;
+    for (int64_t s = 2; s * tiles <= 256 && s <= nk / 2; ++s) {
+      const SplitShape c = prefill_split_shape(nk, s);
+      if (prefill_split_bytes(M, N, c.splits) > ws_avail) break;
+      const double us = 1.5 * c.ksteps + 0.4e-6 * (double)(c.splits * M * N * 4);
+      if (us < best_us) {
+        best_us = us;
+        best = c;
+      }
+    }
+  }
+  if (best.splits > 1) {
+    p->splits = (int)best.splits;
+    p->ksteps = (int)best.ksteps;
+    p->ws_part_off = kWsCounterBytes;
+    p->ws_bytes = prefill_split_bytes(M, N, best.splits);
+  }
+  p->xcd_remap = (tiles * p->splits) % 8 == 0;
 }
 
-hipError_t rmm_launch_prefill(const RmmArgs& a, const PrefillPlan& p) {
+hipError_t rmm_launch_prefill(const RmmArgs& a, const PrefillPlan& p, void* ws) {
   using namespace rmm;
-  const unsigned grid = (unsigned)((int64_t)p.tiles_m * p.tiles_n);
+  const unsigned grid = (unsigned)((int64_t)p.tiles_m * p.tiles_n * p.splits);
+  float* part = p.splits > 1 ? (float*)((char*)ws + p.ws_part_off) : nullptr;
+  if (p.splits > 1 && !ws) return hipErrorInvalidValue;
   auto launch = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(PF_THREADS), 0, a.stream, (const bf16_t*)a.X,
                        (const bf16_t*)a.g, (const bf16_t*)a.W1, (const bf16_t*)a.W3, (bf16_t*)a.Y, a.eps,
                        a.M, a.N, a.K, p.tiles_m, p.tiles_n, p.group_m, p.xcd_remap, a.norm);
   };
+  auto launch_plain = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(PF_THREADS), 0, a.stream, (const bf16_t*)a.X,
+                       (const bf16_t*)a.g, (const bf16_t*)a.W1, (const bf16_t*)a.W3, (bf16_t*)a.Y, a.eps,
+                       a.M, a.N, a.K, p.tiles_m, p.tiles_n, p.group_m, p.xcd_remap, a.norm,
+                       p.splits, p.ksteps, part);
+  };
   const bool gl = a.K <= PF_G_LDS_MAX;
-  if (a.gated)
+  if (a.gated) {
     gl ? launch(prefill_gated_kernel<true>) : launch(prefill_gated_kernel<false>);
-  else
-    gl ? launch(prefill_kernel<false, true>) : launch(prefill_kernel<false, false>);
+    return hipGetLastError();
+  }
+  gl ? launch_plain(prefill_kernel<false, true>) : launch_plain(prefill_kernel<false, false>);
+  if (p.splits > 1) {
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int64_t threads = a.M * (a.N >> 3);
+    hipLaunchKernelGGL(prefill_combine_kernel, dim3((unsigned)((threads + PC_THREADS - 1) / PC_THREADS)),
+                       dim3(PC_THREADS), 0, a.stream, (const float*)part, (bf16_t*)a.Y, a.eps, a.M,
+                       a.N, a.K, p.splits, a.norm);
+  }
   return hipGetLastError();
 }

@@ -280,9 +280,29 @@ def test_variant_selection():
     assert tpa.plan(4096, 4096, 4096)[1:] == ("prefill", 1)
     assert tpa.plan(8192, 28672, 8192)[1] == "prefill"
     assert tpa.plan(33, 520, 1000)[1] == "stream"
-    assert tpa.plan(65, 520, 1000)[1] == "stream"    # two 64-row launches
-    assert tpa.plan(129, 520, 1000)[1] == "stream"    # N <= 4096: up to 256 rows
-    assert tpa.plan(257, 520, 1000)[1] == "prefill"
+    # above 64 rows with a workspace: the prefill tile with K split into
+    # ranges (256 x 4096 x 4096: 31 us against 89 us for four 64-row stream
+    # launches); without one, 64-row stream launches up to 128 rows (256
+    # when N <= 4096)
+    assert tpa.plan(65, 520, 1000)[1] == "prefill"
+    assert tpa.plan(65, 520, 1000, with_workspace=False)[1] == "stream"
+    assert tpa.plan(129, 520, 1000, with_workspace=False)[1] == "stream"
+    assert tpa.plan(257, 520, 1000, with_workspace=False)[1] == "prefill"
+    assert tpa.plan(256, 4096, 4096)[1:] == ("prefill", 8)
+    assert tpa.plan(129, 4096, 4096)[1:] == ("prefill", 11)
+    assert tpa.plan(512, 14336, 4096)[1:] == ("prefill", 2)
+    assert tpa.plan(1024, 14336, 4096)[1:] == ("prefill", 1)   # 224 tiles: no split
+    assert tpa.plan(256, 4096, 4096, with_workspace=False)[1] == "stream"
+    assert tpa.plan(512, 4096, 4096, with_workspace=False)[1:] == ("prefill", 1)
+    # forced counts: whole, even ranges of 64-deep steps (K = 1000: 16 steps)
+    assert tpa.plan(300, 264, 1000, variant="prefill", splits=5)[1:] == ("prefill", 4)
+    assert tpa.plan(300, 264, 1000, variant="prefill", splits=3)[1:] == ("prefill", 3)
+    assert tpa.plan(300, 264, 1000, variant="prefill", splits=16)[1:] == ("prefill", 8)
+    assert tpa.plan(300, 264, 1000, variant="prefill", splits=17)[0] == VARIANT
+    assert tpa.plan(300, 264, 1000, variant="prefill", splits=2,
+                    with_workspace=False)[0] == WORKSPACE
+    assert tpa.plan(300, 264, 1000, gated=True, variant="prefill", splits=2)[0] == VARIANT
+    assert tpa.plan(300, 264, 1000, variant="stream", splits=2)[0] == VARIANT
     assert tpa.plan(129, 4104, 1000)[1] == "prefill"
     assert tpa.plan(4096, 4096, 4095)[1] == "generic"   # K % 8 != 0
     assert tpa.plan(4096, 4096, 4096, variant="prefill", dtype=torch.float32)[0] == VARIANT
@@ -425,7 +445,10 @@ def test_forced_splits_beyond_the_counter_region(lib):
 
 def test_noalloc_validates_and_fits_its_scratch(lib):
     """rmsnorm_matmul_noalloc validates like rmsnorm_matmul (no HIP call on
-    these failures), and every plain call's workspace fits its 16 MiB array."""
+    these failures), and every plain call's workspace fits its 16 MiB array:
+    up to 64 rows the library's own choice needs no more; above, the prefill
+    split is chosen to fit the workspace passed, which a plan with 16 MiB
+    shows."""
     def na(X=A[0], g=A[1], W=A[2], Y=A[3], eps=1e-6, M=16, N=64, K=64, dtype=BF16):
         return lib.rmsnorm_matmul_noalloc(X, g, W, Y, eps, M, N, K, dtype, None)
     assert na(X=None) == NULL
@@ -435,9 +458,16 @@ def test_noalloc_validates_and_fits_its_scratch(lib):
     assert na(Y=A[0]) == ALIAS
     assert na(M=0) == OK and na(N=0, W=None) == OK and na(N=0) == OK  # empty: NULL allowed
     worst = 0
+    split = 0
     for dtype in (BF16, F32):
-        for M in (1, 8, 16, 17, 32, 33, 64, 100, 128, 200, 256):
+        for M in (1, 8, 16, 17, 32, 33, 64, 100, 128, 200, 256, 1024):
             for K in (64, 1024, 4096, 8192):
                 for N in (8, 128, 1024, 4096, 6144, 8192, 16384, 28672):
-                    worst = max(worst, lib.rmm_workspace_bytes(dtype, M, N, K, 0))
+                    if M <= 64:
+                        worst = max(worst, lib.rmm_workspace_bytes(dtype, M, N, K, 0))
+                    st, v, sp = _binding.plan(A[0], A[1], A[2], None, A[3], 1e-6, M, N, K,
+                                              dtype, False, ws=A[4], ws_bytes=16 << 20)
+                    assert st == OK, (M, N, K, dtype, st)
+                    split += v == "prefill" and sp > 1
     assert 0 < worst <= 16 << 20, worst
+    assert split > 0

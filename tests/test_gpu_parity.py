@@ -61,6 +61,15 @@ EXACT_CASES = [
     (40, 4096, 2048, "bf16", "prefill", 0),
     (4096, 4096, 4096, "bf16", "prefill", 0),
     (1024, 8192, 28672, "bf16", "prefill", 0),
+    # prefill with K split into ranges (few output tiles): forced counts,
+    # ragged ranges, a last range ending inside a step, an odd last range
+    (256, 4096, 4096, "bf16", "prefill", 1),
+    (256, 4096, 4096, "bf16", "prefill", 16),
+    (129, 1000, 520, "bf16", "prefill", 5),
+    (300, 1032, 264, "bf16", "prefill", 3),
+    (513, 200, 1032, "bf16", "prefill", 2),
+    (200, 2048, 1032, "bf16", "prefill", 8),
+    (384, 4096, 4096, "bf16", "prefill", 0),
     (64, 4096, 14336, "bf16", "stream", 0),
     (33, 1000, 520, "bf16", "stream", 0),
     (1, 8, 8, "bf16", "stream", 0),
@@ -198,6 +207,23 @@ def test_gated_prefill_shapes(M, K, N, require_gpu):
     inp = synth.make_inputs(wl, seed=13)
     y = from_device(run_gpu(inp, wl.eps, variant="prefill"))
     worst = assert_within_tol(y, run_oracle(inp, wl.eps), 1e-2, "gated_prefill")
+    _log(f"  worst err/tol {worst:.3f}")
+
+
+@pytest.mark.parametrize("M,K,N,splits", [(384, 4096, 4096, 0), (256, 4096, 4096, 8),
+                                          (129, 14336, 4096, 0), (1000, 1032, 2056, 0),
+                                          (512, 4096, 4096, 7)])
+def test_prefill_split_shapes(M, K, N, splits, require_gpu):
+    """Plain prefill with K split into ranges (few output tiles), on the
+    prefill workload's value recipe with rows scaled by 100, at the
+    elementwise bound on every output."""
+    wl = synth.Workload("prefill_split", "bf16", M, K, N, 1e-6, False, "pick_x100")
+    st, variant, s = tpa.plan(M, N, K, variant="prefill", splits=splits)
+    assert st == 0 and s > 1, (st, variant, s)
+    _log(f"prefill split M={M} K={K} N={N} splits {splits} -> {s}")
+    inp = synth.make_inputs(wl, seed=17)
+    y = from_device(run_gpu(inp, wl.eps, variant="prefill", splits=splits))
+    worst = assert_within_tol(y, run_oracle(inp, wl.eps), tol_for("bf16"), "prefill_split")
     _log(f"  worst err/tol {worst:.3f}")
 
 

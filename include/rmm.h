@@ -221,12 +221,18 @@ rmm_status rmm_gated_matmul(const void* X, const void* W1, const void* W3, void*
  * row-major (B[r*N + n]); both in the call's dtype, 1 <= R <= 64
  * (RMM_LORA_MAX_RANK, else RMM_ERR_SHAPE).  The down-projection T = Act A^T
  * is summed in fp32 from the same operand the weight product uses (bf16:
- * X*g rounded once), kept in fp32 (never rounded to the storage type), and
- * T B is added to the k-sum before the 1/RMS scale, so one rounding produces
- * Y.  Not combined with the gate.  Variants: DECODE (bf16, M <= 32, R <= 32;
- * the down-projection partials travel with the split-K partials) and
- * GENERIC (everything else); forcing PREFILL or STREAM returns
- * RMM_ERR_VARIANT.  NULL checks cover A and B; Y must not overlap them.
+ * X*g carried exactly as two bf16 parts, see the top of this file), kept in
+ * fp32 (never rounded to the storage type), and T B is added to the k-sum
+ * before the 1/RMS scale, so one rounding produces Y.  Not combined with
+ * the gate.  Variants: DECODE (bf16, M <= 128 as one launch per 32-row
+ * block, R <= 32; the down-projection partials travel with the split-K
+ * partials), PREFILL (bf16, any M, R <= 64, a workspace required: a first
+ * kernel writes T to it, then a tile of 128 rows x 256 columns carries X g
+ * as two bf16 parts and adds T B, T likewise in two parts, as one more
+ * k-step of the same accumulators; AUTO takes it above 128 rows when a
+ * workspace is passed) and GENERIC (everything else); forcing STREAM
+ * returns RMM_ERR_VARIANT.  NULL checks cover A and B; Y must not overlap
+ * them.
  * Workspace rules are those of rmsnorm_matmul, sized by
  * rmm_lora_workspace_bytes (variant = RMM_VARIANT_AUTO, splits = 0 for the
  * plain entry points). */

@@ -113,14 +113,20 @@ rmm_status plan_shape(int64_t M, int64_t N, int64_t K, rmm_dtype dtype, int gate
   const bool decode_ok = (fast_layout && lora_ok &&
                           M <= (gated ? kDecodeMaxMGated : (R > 0 ? kDecodeMaxMLora : kDecodeMaxM))) ||
                          decode32_ok;
-  const bool prefill_ok = fast_layout && R == 0;
+  // The adapter's prefill tile: T = (X g) A^T goes through the workspace;
+  // A's and B's rows are addressed with 32-bit offsets.
+  const bool lora_prefill_ok = R > 0 && !gated && R <= RMM_LORA_MAX_RANK &&
+                               R * K * 2 <= (int64_t)INT32_MAX && R * N * 2 <= (int64_t)INT32_MAX;
+  const bool prefill_ok = fast_layout && (R == 0 || lora_prefill_ok);
   const bool stream_ok = fast_layout && R == 0 &&
                          (gated || M <= kStreamMaxM || (M <= 256 && N <= 4096)) &&
                          rmm_stream_fits(M < kStreamRows ? M : kStreamRows, N, K);
   rmm_variant v = variant;
   if (v == RMM_VARIANT_AUTO) {
     if (R > 0)
-      v = decode_ok ? RMM_VARIANT_DECODE : RMM_VARIANT_GENERIC;
+      v = decode_ok                 ? RMM_VARIANT_DECODE
+          : (prefill_ok && have_ws) ? RMM_VARIANT_PREFILL
+                                    : RMM_VARIANT_GENERIC;
     else if (gated)  // decode (split-K over every CU) only with a workspace for its partials
       v = (decode_ok && have_ws)                 ? RMM_VARIANT_DECODE
           : (stream_ok && M <= kGatedStreamMaxM) ? RMM_VARIANT_STREAM
@@ -164,9 +170,10 @@ rmm_status plan_shape(int64_t M, int64_t N, int64_t K, rmm_dtype dtype, int gate
     out->splits = out->dec.splits;
     out->ws_bytes = out->dec.ws_bytes;
   } else if (v == RMM_VARIANT_PREFILL) {
-    if (splits > (K + 63) / 64) return RMM_ERR_VARIANT;
-    if (splits > 1 && !have_ws) return RMM_ERR_WORKSPACE;  // a forced split count needs one
-    rmm_prefill_plan(M, N, K, gated, splits, have_ws ? ws_avail : 0, &out->pre);
+    if (splits > (K + 63) / 64 || (R > 0 && splits > 1)) return RMM_ERR_VARIANT;
+    // a forced split count, and the adapter's T, need one
+    if ((splits > 1 || R > 0) && !have_ws) return RMM_ERR_WORKSPACE;
+    rmm_prefill_plan(M, N, K, gated, splits, have_ws ? ws_avail : 0, &out->pre, R);
     if (out->pre.ws_bytes > (size_t)INT32_MAX) return RMM_ERR_VARIANT;
     out->splits = out->pre.splits;
     out->ws_bytes = out->pre.ws_bytes;
@@ -268,7 +275,7 @@ rmm_status run(const void* X, const void* g, const void* W1, const void* W3, voi
         }
       break;
     case RMM_VARIANT_PREFILL:
-      err = rmm_launch_prefill(a, plan.pre, plan.pre.splits > 1 ? ws : nullptr);
+      err = rmm_launch_prefill(a, plan.pre, plan.pre.ws_bytes > 0 ? ws : nullptr);
       break;
     case RMM_VARIANT_STREAM:
       // Row blocks of 64, in order on the stream (the split form's workspace

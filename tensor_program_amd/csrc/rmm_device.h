@@ -153,13 +153,15 @@ struct PrefillPlan {
   int xcd_remap;         // contiguous tile ranges per XCD
   int splits;            // K ranges (plain tile only; > 1: partial sums + combine kernel)
   int ksteps;            // 64-deep k-steps per range (even when splits > 1)
-  size_t ws_part_off, ws_bytes;
+  int rb;                // adapter: 16-wide rank blocks of T (0: no adapter)
+  size_t ws_part_off, ws_t_off, ws_bytes;
 };
 // splits: 0 = chosen by the library (a split only if its partial sums fit
 // in ws_avail bytes of workspace), else the requested count (the count that
 // runs may be lower: whole, even ranges).
+// R > 0: the adapter tile (plain product, T = (X g) A^T in the workspace).
 void rmm_prefill_plan(int64_t M, int64_t N, int64_t K, int gated, int splits, size_t ws_avail,
-                      PrefillPlan* p);
+                      PrefillPlan* p, int64_t R = 0);
 // Workspace bytes of an AUTO plain or gated call given a workspace of `cap`
 // bytes (the prefill split is chosen to fit), 0 for invalid arguments.
 size_t rmm_workspace_bytes_within(int dtype, int64_t M, int64_t N, int64_t K, int gated,

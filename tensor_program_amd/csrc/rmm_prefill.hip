@@ -618,7 +618,7 @@ __device__ __forceinline__ void pg_gain(float (&g_f)[8], const u32x4& gsrc, int 
 // MFMAs over the 64 x 64 wave tile, fragments from set s & 1, each followed
 // by a fragment read of sub-step s + 1 and, in sub-steps 1 and 2, a share
 // of the forming of the next step's A stages.
-template <int VM, bool GL, typename Issue>
+template <int VM, bool GL, typename Issue, bool STAGE = true>
 __device__ __forceinline__ void pg_step(const char* ah_cur, const char* al_cur, const lds_char* b_cur,
                                         char* ah_nxt, char* al_nxt, PgA& st, floatx16 (&acc)[2][2],
                                         float (&ss)[2], int a_base, int b0, int b1, int tid, int norm,
@@ -661,7 +661,7 @@ __device__ __forceinline__ void pg_step(const char* ah_cur, const char* al_cur, 
 #define PG_SLOT_END __builtin_amdgcn_sched_barrier(0)
 #pragma unroll
   for (int q = 0; q < 8; ++q) read_q(0, q);
-  if (GL) gsrc = *(const u32x4*)(g_lds + 2 * (k_nxt + 8 * (tid & 7)));
+  if (STAGE && GL) gsrc = *(const u32x4*)(g_lds + 2 * (k_nxt + 8 * (tid & 7)));
   issue();
   PG_SLOT_END;
 #pragma unroll
@@ -670,22 +670,24 @@ __device__ __forceinline__ void pg_step(const char* ah_cur, const char* al_cur, 
     read_q(1, q);
     PG_SLOT_END;
   }
-  pg_wait_a<VM, GL>(st);
-  if (!GL) gsrc = st.g;
-  pg_gain<GL>(g_f, gsrc, norm);
+  if (STAGE) {
+    pg_wait_a<VM, GL>(st);
+    if (!GL) gsrc = st.g;
+    pg_gain<GL>(g_f, gsrc, norm);
+  }
   PG_SLOT_END;
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
     mfma_q(1, q);
     read_q(2, q);
-    if (q < 4) unit(q);
+    if (STAGE && q < 4) unit(q);
     PG_SLOT_END;
   }
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
     mfma_q(2, q);
     read_q(3, q);
-    if (q < 4) unit(4 + q);
+    if (STAGE && q < 4) unit(4 + q);
     PG_SLOT_END;
   }
 #pragma unroll
@@ -696,11 +698,19 @@ __device__ __forceinline__ void pg_step(const char* ah_cur, const char* al_cur, 
 #undef PG_SLOT_END
 }
 
-template <bool GL>
+// LORA: the same two-part tile for the plain product with the low-rank
+// adapter (Y = Nrm W + (Nrm A^T) B, the LoRA row of the same benchmark
+// table): the two weight slots are the two 128-column halves of a 256-column
+// tile of W, and after the k-loop one more k-step multiplies T = (X g) A^T
+// (fp32, from lora_down_kernel, split into two bf16 parts like X g) by the
+// tile's columns of B (R <= 64 rows, zero past R), into the same
+// accumulators, before 1/RMS: no rounding between the two products.
+template <bool GL, bool LORA>
 __global__ __launch_bounds__(PF_THREADS, 1) void prefill_gated_kernel(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ g, const bf16_t* __restrict__ W1,
     const bf16_t* __restrict__ W3, bf16_t* __restrict__ Y, float eps, int64_t M, int64_t N,
-    int64_t K, int tiles_m, int tiles_n, int group_m, int xcd_remap, int norm) {
+    int64_t K, int tiles_m, int tiles_n, int group_m, int xcd_remap, int norm,
+    const float* __restrict__ T, int rp, const bf16_t* __restrict__ LB, int R) {
   constexpr int XL = GL ? 2 : 3;  // X (and g) loads per thread per k-step
   __shared__ __attribute__((aligned(16))) char ah_s0[PG_A_BYTES];
   __shared__ __attribute__((aligned(16))) char ah_s1[PG_A_BYTES];
@@ -720,7 +730,9 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_gated_kernel(
   const int gm = (tiles_m - first_m < group_m) ? (tiles_m - first_m) : group_m;
   const int tm = first_m + (t % group) % gm;
   const int tn = (t % group) / gm;
-  const int64_t m0 = (int64_t)tm * PG_BM, n0 = (int64_t)tn * PG_BNW;
+  // Gated: 128 columns of each weight; LORA: 256 columns of W, the upper
+  // half in the second weight slot.
+  const int64_t m0 = (int64_t)tm * PG_BM, n0 = (int64_t)tn * (LORA ? 2 * PG_BNW : PG_BNW);
 
   const i32x4 xr = pf_rsrc(X, (uint32_t)(M * K * 2));
   const i32x4 gr = pf_rsrc(g, (uint32_t)(K * 2));
@@ -728,7 +740,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_gated_kernel(
   lds_char* b1s = (lds_char*)b_s1;
   const uint32_t b0a = (uint32_t)(uintptr_t)b0s, b1a = (uint32_t)(uintptr_t)b1s;
   PgDma dma;
-  pg_dma_setup(dma, n0, N, w, l);
+  pg_dma_setup(dma, n0 + (LORA && (w >> 2) ? PG_BNW : 0), N, w, l);
 
   floatx16 acc[2][2];
 #pragma unroll
@@ -811,6 +823,54 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_gated_kernel(
   }
   __syncthreads();
 
+  if (LORA) {
+    // The adapter step: T rows m0 .. m0 + 127 (rp columns, zero past R) as
+    // hi and lo A stages, B rows 0 .. R - 1 of the tile's columns in a W
+    // stage (rows past R read as zeros), then one k-step of MFMAs.
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = (tid >> 3) + 64 * i, c = tid & 7;
+      const int64_t m = m0 + row;
+      u32x4 hv = {0u, 0u, 0u, 0u}, lv = {0u, 0u, 0u, 0u};
+      if (m < M && 8 * c < rp) {
+        const float4* tp = (const float4*)(T + m * rp + 8 * c);
+        const float4 t0 = tp[0], t1 = tp[1];
+        const float tv[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const u32x2 hl = split_bf16x2(tv[2 * d], tv[2 * d + 1]);
+          hv[d] = hl[0];
+          lv[d] = hl[1];
+        }
+      }
+      const int off = row * PF_A_ROW + 16 * c;
+      *(u32x4*)(ah_s0 + off) = hv;
+      *(u32x4*)(al_s0 + off) = lv;
+    }
+    pg_dma_b(b0a, dma, LB, LB, 0, N, R, w);
+    PF_WAIT_VMCNT(0);
+    __syncthreads();
+    auto no_issue = [] {};
+    pg_step<0, GL, decltype(no_issue), false>(ah_s0, al_s0, b0s, ah_s1, al_s1, sa, acc, ss, a_base,
+                                              bo0, bo1, tid, norm, g_s, 0, no_issue);
+    // Y: each wave stores its own 64 x 64 block.
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int64_t n = n0 + wv * PG_BNW + wh * 64 + 32 * j + (l & 31);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int lr = wm * 64 + 32 * i + 8 * jj + 4 * (l >> 5) + rr;
+            const int64_t m = m0 + lr;
+            if (m < M && n < N) Y[m * N + n] = f32_to_bf16(acc[i][j][4 * jj + rr] * inv_s[lr]);
+          }
+      }
+    return;
+  }
+
   // Epilogue, one 64-row half at a time: the W3 waves of rows 64 r .. +63
   // put their sums in a W stage as [column half][row][col] fp32, the W1
   // waves of those rows read them back at the positions of their own sums.
@@ -852,6 +912,82 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_gated_kernel(
         }
     }
     __syncthreads();
+  }
+}
+
+// Down-projection of the adapter for the prefill tile: T = (X g) A^T, M x R
+// in fp32, row stride rp = 16 RB (columns R .. rp - 1 are zero).  As in the
+// decode kernel's adapter, X g is formed exactly in fp32 and split into two
+// bf16 parts, both multiplied into the sum, and A's R x K layout gives the
+// k-contiguous B fragments of v_mfma_f32_16x16x32_bf16 directly: lane l
+// holds row (rank) l % 16 and k chunk l / 16 of a 32-deep block for both
+// operands.  A workgroup takes 16 rows; its 4 waves take every 4th 32-deep
+// block of K and their sums are added in wave order.
+constexpr int LD_THREADS = 256;
+
+template <int RB>
+__global__ __launch_bounds__(LD_THREADS) void lora_down_kernel(
+    const bf16_t* __restrict__ X, const bf16_t* __restrict__ g, const bf16_t* __restrict__ A,
+    float* __restrict__ T, int64_t M, int64_t K, int R, int norm) {
+  __shared__ floatx4 red[4][RB][64];
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int64_t m0 = (int64_t)blockIdx.x * 16;
+  const int r16 = l & 15, kc = l >> 4;
+  const int64_t m = m0 + r16;
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc((void*)X, 0, (int)(M * K * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t gr = __builtin_amdgcn_make_buffer_rsrc((void*)g, 0, (int)(K * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc((void*)A, 0, (int)(R * K * 2), 0x00020000);
+  floatx4 acc[RB];
+#pragma unroll
+  for (int b = 0; b < RB; ++b) acc[b] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int64_t kb = 32 * w; kb < K; kb += 128) {
+    const int64_t k = kb + 8 * kc;
+    const bool kok = k < K;  // K % 8 == 0: a chunk is all in or all out
+    const u32x4 xv = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                   xr,
+                   (kok && m < M) ? (uint32_t)((m * K + k) * 2) : kPfOutOfRange, 0, 0));
+    const u32x4 gv = norm ? __builtin_bit_cast(
+                                u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           gr,
+                                           kok ? (uint32_t)(k * 2) : kPfOutOfRange, 0, 0))
+                          : u32x4{kBf16OnePair, kBf16OnePair, kBf16OnePair, kBf16OnePair};
+    u32x4 hi, lo;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const u32x2 hl = split_bf16x2(bf16_lo(xv[d]) * bf16_lo(gv[d]), bf16_hi(xv[d]) * bf16_hi(gv[d]));
+      hi[d] = hl[0];
+      lo[d] = hl[1];
+    }
+#pragma unroll
+    for (int b = 0; b < RB; ++b) {
+      const int r = 16 * b + r16;
+      const u32x4 av = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                     ar,
+                     (kok && r < R) ? (uint32_t)(((int64_t)r * K + k) * 2) : kPfOutOfRange, 0, 0));
+      acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, hi),
+                                                       __builtin_bit_cast(bf16x8, av), acc[b], 0, 0, 0);
+      acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, lo),
+                                                       __builtin_bit_cast(bf16x8, av), acc[b], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < RB; ++b) red[w][b][l] = acc[b];
+  __syncthreads();
+  // 16 x 16 accumulator layout: lane l holds column l % 16, rows 4 (l / 16) + i.
+  if (w == 0) {
+#pragma unroll
+    for (int b = 0; b < RB; ++b) {
+      floatx4 v = red[0][b][l];
+#pragma unroll
+      for (int q = 1; q < 4; ++q) v += red[q][b][l];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t mm = m0 + 4 * (l >> 4) + i;
+        if (mm < M) T[mm * (16 * RB) + 16 * b + (l & 15)] = v[i];
+      }
+    }
   }
 }
 
@@ -911,8 +1047,23 @@ size_t prefill_split_bytes(int64_t M, int64_t N, int64_t S) {
 }  // namespace
 
 void rmm_prefill_plan(int64_t M, int64_t N, int64_t K, int gated, int splits, size_t ws_avail,
-                      PrefillPlan* p) {
+                      PrefillPlan* p, int64_t R) {
   using namespace rmm;
+  p->rb = 0;
+  p->ws_t_off = 0;
+  if (R > 0) {  // the two-part tile, 128 rows x 256 columns, and T in the workspace
+    p->tiles_m = (int)((M + PG_BM - 1) / PG_BM);
+    p->tiles_n = (int)((N + 2 * PG_BNW - 1) / (2 * PG_BNW));
+    p->group_m = 4;
+    p->splits = 1;
+    p->ksteps = (int)((K + PF_BK - 1) / PF_BK);
+    p->rb = (int)((R + 15) / 16);
+    p->ws_part_off = 0;
+    p->ws_t_off = kWsCounterBytes;
+    p->ws_bytes = kWsCounterBytes + (size_t)(M * 16 * p->rb) * 4;
+    p->xcd_remap = ((int64_t)p->tiles_m * p->tiles_n) % 8 == 0;
+    return;
+  }
   const int bm = gated ? PG_BM : PF_BM, bn = gated ? PG_BNW : PF_BN;
   p->tiles_m = (int)((M + bm - 1) / bm);
   p->tiles_n = (int)((N + bn - 1) / bn);
@@ -955,7 +1106,8 @@ hipError_t rmm_launch_prefill(const RmmArgs& a, const PrefillPlan& p, void* ws) 
   auto launch = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(PF_THREADS), 0, a.stream, (const bf16_t*)a.X,
                        (const bf16_t*)a.g, (const bf16_t*)a.W1, (const bf16_t*)a.W3, (bf16_t*)a.Y, a.eps,
-                       a.M, a.N, a.K, p.tiles_m, p.tiles_n, p.group_m, p.xcd_remap, a.norm);
+                       a.M, a.N, a.K, p.tiles_m, p.tiles_n, p.group_m, p.xcd_remap, a.norm,
+                       (const float*)nullptr, 0, (const bf16_t*)nullptr, 0);
   };
   auto launch_plain = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(PF_THREADS), 0, a.stream, (const bf16_t*)a.X,
@@ -964,8 +1116,31 @@ hipError_t rmm_launch_prefill(const RmmArgs& a, const PrefillPlan& p, void* ws) 
                        p.splits, p.ksteps, part);
   };
   const bool gl = a.K <= PF_G_LDS_MAX;
+  if (a.R > 0) {
+    if (!ws || p.rb < 1 || p.rb > 4) return hipErrorInvalidValue;
+    float* T = (float*)((char*)ws + p.ws_t_off);
+    const dim3 dgrid((unsigned)((a.M + 15) / 16)), dblock(LD_THREADS);
+    auto down = [&](auto kernel) {
+      hipLaunchKernelGGL(kernel, dgrid, dblock, 0, a.stream, (const bf16_t*)a.X, (const bf16_t*)a.g,
+                         (const bf16_t*)a.LA, T, a.M, a.K, (int)a.R, a.norm);
+    };
+    if (p.rb == 1) down(lora_down_kernel<1>);
+    else if (p.rb == 2) down(lora_down_kernel<2>);
+    else if (p.rb == 3) down(lora_down_kernel<3>);
+    else down(lora_down_kernel<4>);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    auto tile = [&](auto kernel) {
+      hipLaunchKernelGGL(kernel, dim3(grid), dim3(PF_THREADS), 0, a.stream, (const bf16_t*)a.X,
+                         (const bf16_t*)a.g, (const bf16_t*)a.W1, (const bf16_t*)a.W1, (bf16_t*)a.Y,
+                         a.eps, a.M, a.N, a.K, p.tiles_m, p.tiles_n, p.group_m, p.xcd_remap, a.norm,
+                         (const float*)T, 16 * p.rb, (const bf16_t*)a.LB, (int)a.R);
+    };
+    gl ? tile(prefill_gated_kernel<true, true>) : tile(prefill_gated_kernel<false, true>);
+    return hipGetLastError();
+  }
   if (a.gated) {
-    gl ? launch(prefill_gated_kernel<true>) : launch(prefill_gated_kernel<false>);
+    gl ? launch(prefill_gated_kernel<true, false>) : launch(prefill_gated_kernel<false, false>);
     return hipGetLastError();
   }
   gl ? launch_plain(prefill_kernel<false, true>) : launch_plain(prefill_kernel<false, false>);

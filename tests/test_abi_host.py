@@ -142,7 +142,12 @@ def test_lora_entry_points_validate(lib):
     assert lo(dtype=7, Y=A[5]) == DTYPE
     assert lo(Y=A[5] + 16) == ALIAS                 # Y overlapping A
     assert lo(Y=A[6] - 64) == ALIAS                 # Y overlapping B
-    assert lo(variant=3) == VARIANT                 # no adapter prefill tile
+    assert lo(variant=3) == WORKSPACE               # the adapter tile keeps T in the workspace
+    # (a call that validates would launch: only the host-only plan takes these)
+    assert _binding.plan_lora(A[0], A[1], A[2], A[5], A[6], A[3], 1e-6, 16, 64, 64, 16, BF16,
+                              "prefill", 0, A[7], 1 << 30) == (OK, "prefill", 1)
+    assert lo(variant=3, splits=2, ws=A[7], ws_bytes=1 << 30) == VARIANT   # no split with T
+    assert lo(variant=3, ws=A[7], ws_bytes=1000) == WORKSPACE
     assert lo(variant=4) == VARIANT
     assert lo(M=129, variant=2) == VARIANT          # decode with the adapter: M <= 128 (32-row launches)
     assert lo(R=33, variant=2) == VARIANT           # decode: R <= 32
@@ -163,16 +168,22 @@ def test_lora_plans():
     assert tpa.plan_lora(16, 6144, 4096, 32)[1:] == ("decode", 4)
     assert tpa.plan_lora(16, 6144, 4096, 1)[1] == "decode"
     assert tpa.plan_lora(32, 6144, 4096, 16)[1] == "decode"
-    assert tpa.plan_lora(16, 6144, 4096, 33)[1] == "generic"
-    assert tpa.plan_lora(16, 6144, 4096, 64)[1] == "generic"
+    assert tpa.plan_lora(16, 6144, 4096, 33)[1] == "prefill"   # decode carries R <= 32
+    assert tpa.plan_lora(16, 6144, 4096, 64)[1] == "prefill"
+    assert tpa.plan_lora(16, 6144, 4096, 64, with_workspace=False)[1] == "generic"
     assert tpa.plan_lora(33, 6144, 4096, 16)[1] == "decode"    # 32-row launches
     assert tpa.plan_lora(128, 6144, 4096, 16)[1] == "decode"
-    assert tpa.plan_lora(129, 6144, 4096, 16)[1] == "generic"
-    assert tpa.plan_lora(4096, 4096, 4096, 16)[1] == "generic"
+    assert tpa.plan_lora(129, 6144, 4096, 16)[1:] == ("prefill", 1)
+    assert tpa.plan_lora(4096, 4096, 4096, 16)[1] == "prefill"
+    assert tpa.plan_lora(4096, 4096, 4096, 16, with_workspace=False)[1] == "generic"
+    assert tpa.plan_lora(4096, 4100, 4096, 16)[1] == "generic"    # N % 8 != 0
     assert tpa.plan_lora(8, 1024, 1024, 16, dtype=torch.float32)[1] == "generic"
     assert tpa.plan_lora(16, 6144, 4096, 16, with_workspace=False)[1:] == ("decode", 1)
     assert tpa.plan_lora(16, 6144, 4096, 16, variant="decode", splits=3)[1:] == ("decode", 3)
-    assert tpa.plan_lora(16, 6144, 4096, 16, variant="prefill")[0] == VARIANT
+    assert tpa.plan_lora(16, 6144, 4096, 16, variant="prefill")[1] == "prefill"
+    assert tpa.plan_lora(16, 6144, 4096, 16, variant="prefill", with_workspace=False)[0] == \
+        WORKSPACE
+    assert tpa.plan_lora(16, 6144, 4096, 16, variant="prefill", splits=2)[0] == VARIANT
     assert tpa.plan_lora(16, 6144, 4096, 65)[0] == SHAPE
 
 
@@ -183,7 +194,10 @@ def test_lora_workspace_sizes(lib):
     assert plain < lora16 < lora32   # the down-projection partials ride along
     # 4 splits x 48 tiles x (8 + 1) blocks of 16 x 16 fp32 beyond the plain partials' 8
     assert lora16 - plain == 4 * 48 * 1 * 256 * 4
-    assert lib.rmm_lora_workspace_bytes(BF16, 16, 6144, 4096, 48, 0, 0) == 0  # generic: none
+    # R = 48: the prefill tile (decode carries R <= 32): T, 16 rows x 48 ranks
+    assert lib.rmm_lora_workspace_bytes(BF16, 16, 6144, 4096, 48, 0, 0) == 65536 + 16 * 48 * 4
+    assert lib.rmm_lora_workspace_bytes(BF16, 16, 6144, 4096, 40, 0, 0) == 65536 + 16 * 48 * 4
+    assert lib.rmm_lora_workspace_bytes(F32, 16, 6144, 4096, 48, 0, 0) == 0   # generic: none
     assert lib.rmm_lora_workspace_bytes(BF16, 16, 6144, 4096, 0, 0, 0) == 0   # invalid rank
     assert lib.rmm_lora_workspace_bytes(BF16, 16, 6144, 4096, 16, 2, 1) == 0
 

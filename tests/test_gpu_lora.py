@@ -7,7 +7,9 @@ rmsnorm_lora computes Nrm W + (Nrm A^T) B and lora_matmul X W + (X A^T) B
   decode kernel at every split count (the down-projection partials ride the
   split-K combine), ranks below, at and between its 16-wide blocks, ragged
   N and K, both 16-row blocks, and several 32-row launches (M up to 128);
-  the generic kernel for larger ranks, more rows and fp32;
+  the prefill tile (T = (X g) A^T from its own kernel, then one more k-step
+  of the two-part tile) for more rows and ranks above 32; the generic kernel
+  for fp32;
 * the adapter workload within tolerance, and B = 0 against the plain fused
   call on the same kernels.
 """
@@ -55,7 +57,16 @@ LORA_EXACT = [
     (5, 40, 24, 3, "f32", "generic", 0),
     (64, 1024, 2048, 16, "bf16", "auto", 0),    # M > 32: two 32-row decode launches
     (100, 520, 1032, 16, "bf16", "decode", 3),  # four launches, ragged last block
-    (129, 200, 136, 8, "bf16", "generic", 0),   # above 128 rows: the generic kernel
+    (129, 200, 136, 8, "bf16", "generic", 0),   # the generic kernel above 128 rows
+    # the prefill tile: ragged rows, columns and last k-step, every rank
+    # block count, zero-padded ranks, K past the in-LDS gain
+    (129, 200, 136, 8, "bf16", "auto", 0),
+    (300, 1032, 520, 16, "bf16", "prefill", 0),
+    (256, 4096, 1024, 64, "bf16", "prefill", 0),
+    (130, 520, 264, 40, "bf16", "auto", 0),
+    (16, 1024, 1032, 48, "bf16", "auto", 0),    # R > 32 at decode size: the prefill tile
+    (200, 136, 16392, 1, "bf16", "prefill", 0),
+    (129, 10248, 264, 16, "bf16", "prefill", 0),
 ]
 
 
@@ -76,7 +87,8 @@ def test_lora_exact_bitwise(case, seed, require_gpu):
 
 
 @pytest.mark.parametrize("case", [(16, 4096, 6144, 16, "bf16"), (7, 100, 36, 5, "bf16"),
-                                  (8, 1024, 1024, 16, "f32")], ids=lambda c: "x".join(map(str, c)))
+                                  (8, 1024, 1024, 16, "f32"), (200, 1000, 520, 16, "bf16")],
+                         ids=lambda c: "x".join(map(str, c)))
 def test_lora_matmul_exact(case, require_gpu):
     M, K, N, R, dtype = case
     _log(f"lora_matmul exact {case}")
@@ -99,6 +111,22 @@ def test_lora_workload(variant, splits, require_gpu):
     # the elementwise bound tol (|Y_ref| + 1), also where the frozen product
     # and the adapter term cancel
     worst = assert_within_tol(y, ref, tol_for(wl.dtype), f"lora/{variant}")
+    _log(f"  worst err/tol {worst:.3f}")
+
+
+@pytest.mark.parametrize("M", [512, 1000])
+def test_lora_prefill_workload_recipe(M, require_gpu):
+    """The adapter workload's shape and value recipe with more rows (the
+    prefill tile), on every output at the elementwise bound."""
+    base = synth.get_workload("lora_m16_k4096_n6144_r16")
+    wl = synth.Workload("lora_prefill", base.dtype, M, base.K, base.N, base.eps, False, None,
+                        base.lora)
+    assert tpa.plan_lora(M, wl.N, wl.K, wl.lora)[1] == "prefill"
+    _log(f"lora prefill workload recipe M={M}")
+    inp = synth.make_inputs(wl)
+    y = from_device(_lora_gpu(inp, wl.eps))
+    ref = oracle.rmsnorm_lora(inp.X, inp.g, inp.W1, inp.LA, inp.LB, oracle.eps_as_passed(wl.eps))
+    worst = assert_within_tol(y, ref, tol_for(wl.dtype), "lora/prefill")
     _log(f"  worst err/tol {worst:.3f}")
 
 

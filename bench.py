@@ -145,7 +145,8 @@ def cpu_baseline(wl, inp, budget_s: float):
     eps = oracle.eps_as_passed(wl.eps)
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     attn = isinstance(wl, synth_attn_type())
-    total = wl.BH if attn else wl.M  # independent rows (batch-heads for attention)
+    # independent rows (key/value heads with their G queries for attention)
+    total = wl.BH if attn else wl.M
     # Probe on a small block of rows, then size the sample to the budget.
     rows = min(total, max(1, threads))
     X = inp.Q[:rows] if attn else inp.X[:rows]
@@ -153,8 +154,12 @@ def cpu_baseline(wl, inp, budget_s: float):
     def once(Xs):
         t0 = time.perf_counter()
         if attn:
+            # the oracle takes one key/value head per query row: each head's
+            # keys and values repeated for its G queries
             n = Xs.shape[0]
-            oracle.qknorm_attention(Xs, inp.K[:n], inp.V[:n], inp.gq, inp.gk, eps)
+            G = wl.G
+            oracle.qknorm_attention(inp.Q[:n * G], np.repeat(inp.K[:n], G, axis=0),
+                                    np.repeat(inp.V[:n], G, axis=0), inp.gq, inp.gk, eps)
         elif wl.gated:
             oracle.rmsnorm_gated_mlp(Xs, inp.g, inp.W1, inp.W3, eps)
         elif wl.lora:
@@ -164,7 +169,7 @@ def cpu_baseline(wl, inp, budget_s: float):
         return time.perf_counter() - t0
 
     full = inp.Q if attn else inp.X
-    unit_name = "batch-heads" if attn else "rows"
+    unit_name = "key/value heads" if attn else "rows"
     t_probe = once(X)
     per_row = t_probe / rows
     rows_budget = int(budget_s / max(per_row, 1e-9))
@@ -355,7 +360,7 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     log(f"workload {wl.name}: generating inputs")
-    inp = synth.make_attention_inputs(wl.BH, wl.S, wl.D) if attn else synth.make_inputs(wl)
+    inp = synth.make_attention_inputs(wl.BH, wl.S, wl.D, G=wl.G) if attn else synth.make_inputs(wl)
 
     def dev_tensor(name):
         a = inp.device_array(name)
@@ -375,11 +380,11 @@ def main():
     sets = []
     for r in range(R):
         s = {n: (t if r == 0 else t.clone()) for n, t in base.items()}
-        s["Y"] = torch.empty((wl.BH, wl.D) if attn else (wl.M, wl.N), dtype=torch.bfloat16
+        s["Y"] = torch.empty((wl.BH * wl.G, wl.D) if attn else (wl.M, wl.N), dtype=torch.bfloat16
                              if wl.dtype == "bf16" else torch.float32, device=dev)
         sets.append(s)
     if attn:
-        st, splits, _ = tpa.plan_attention(wl.BH, wl.S, wl.D, splits=args.splits)
+        st, splits, _ = tpa.plan_attention(wl.BH, wl.S, wl.D, splits=args.splits, G=wl.G)
         variant = "attention"
     elif wl.lora:
         st, variant, splits = tpa.plan_lora(wl.M, wl.N, wl.K, wl.lora, dtype=sets[0]["Y"].dtype,
@@ -394,7 +399,8 @@ def main():
     stream = torch.cuda.Stream(dev)
     dcode = tpa._DTYPES[sets[0]["Y"].dtype]
     if attn:
-        nbytes = tpa._binding.attention_workspace_bytes(dcode, wl.BH, wl.S, wl.D, args.splits)
+        nbytes = tpa._binding.attention_gqa_workspace_bytes(dcode, wl.BH, wl.G, wl.S, wl.D,
+                                                            args.splits)
     elif wl.lora:
         nbytes = tpa._binding.lora_workspace_bytes(dcode, wl.M, wl.N, wl.K, wl.lora, args.variant,
                                                    args.splits)
@@ -405,7 +411,10 @@ def main():
     torch.cuda.synchronize()
 
     def call(s):
-        if attn:
+        if attn and wl.G > 1:
+            tpa.qknorm_attention_gqa(s["Q"], s["K"], s["V"], s["gq"], s["gk"], wl.eps,
+                                     out=s["Y"], splits=args.splits, workspace=ws)
+        elif attn:
             tpa.qknorm_attention(s["Q"], s["K"], s["V"], s["gq"], s["gk"], wl.eps, out=s["Y"],
                                  splits=args.splits, workspace=ws)
         elif wl.gated:
@@ -527,7 +536,7 @@ def main():
                     "with the adapter, three products) reads it back"}
         log(f"unfused: {ms_u / steps * 1e3:.2f} us/step (ours), {ms_v / steps * 1e3:.2f} us/step "
             f"(vendor GEMM); fused {ms / steps * 1e3:.2f}")
-    elif not args.no_unfused:
+    elif not args.no_unfused and wl.G == 1:
         # QKNorm: RMSNorm of q and of every cached key written to memory, then
         # the attention step alone on the normalised copies.
         qn = [torch.empty_like(s["Q"]) for s in sets]
@@ -589,7 +598,7 @@ def main():
         "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": steps,
         "warmup": warm, "ms_per_step": ms / steps, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
-        "config": ({"workload": wl.name, "BH": wl.BH, "S": wl.S, "D": wl.D} if attn else
+        "config": ({"workload": wl.name, "BH": wl.BH, "G": wl.G, "S": wl.S, "D": wl.D} if attn else
                    {"workload": wl.name, "M": wl.M, "K": wl.K, "N": wl.N, "gated": wl.gated,
                     "lora_rank": wl.lora}) | {
                    "eps": wl.eps, "variant": variant, "splits": splits,

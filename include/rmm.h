@@ -287,6 +287,29 @@ rmm_status rmm_plan_attention(const void* Q, const void* K, const void* V, const
                               int64_t D, rmm_dtype dtype, int splits, const void* ws,
                               size_t ws_bytes, int* chunks_out, int64_t* keys_per_chunk_out);
 
+/* Grouped-query form of qknorm_attention (several query heads per cached
+ * key/value head, the layout of grouped-query attention; same reading of the
+ * QKNorm + Attention row, "五、实验结果"): BH counts key/value heads, G in 1..8
+ * query heads share each (RMM_ERR_SHAPE otherwise).  Q and O are (BH G) x D,
+ * query row h G + g belonging to key/value head h; K and V are BH x S x D as
+ * above.  One workgroup reads each key and value row once for the whole group
+ * (every query's dot product, the key's sum of squares once).  Other rules,
+ * including the workspace (sized by rmm_attention_gqa_workspace_bytes) and
+ * splits, are those of qknorm_attention_ex; G = 1 is qknorm_attention_ex. */
+rmm_status qknorm_attention_gqa(const void* Q, const void* K, const void* V, const void* gq,
+                                const void* gk, void* O, float eps, int64_t BH, int64_t G,
+                                int64_t S, int64_t D, rmm_dtype dtype, int splits, void* ws,
+                                size_t ws_bytes, hipStream_t stream);
+size_t rmm_attention_gqa_workspace_bytes(rmm_dtype dtype, int64_t BH, int64_t G, int64_t S,
+                                         int64_t D, int splits);
+/* Host-only: validates like qknorm_attention_gqa and reports the chunk count
+ * and keys per chunk that would run (either output may be NULL). */
+rmm_status rmm_plan_attention_gqa(const void* Q, const void* K, const void* V, const void* gq,
+                                  const void* gk, const void* O, float eps, int64_t BH, int64_t G,
+                                  int64_t S, int64_t D, rmm_dtype dtype, int splits,
+                                  const void* ws, size_t ws_bytes, int* chunks_out,
+                                  int64_t* keys_per_chunk_out);
+
 /* The attention step alone (the second kernel of the unfused QKNorm +
  * Attention program the same page's benchmark table compares against,
  * "五、实验结果"): Q and K arrive already normalised (rmsnorm over rows of

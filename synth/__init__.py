@@ -218,8 +218,9 @@ class AttnInputs:
         return self.bits[name]
 
 
-def make_attention_inputs(BH: int, S: int, D: int, seed: int = 0) -> AttnInputs:
-    Q = normals(seed, STREAM_Q, BH, D)
+def make_attention_inputs(BH: int, S: int, D: int, seed: int = 0, G: int = 1) -> AttnInputs:
+    """BH key/value heads; Q has BH * G rows (G query heads per key/value head)."""
+    Q = normals(seed, STREAM_Q, BH * G, D)
     K = normals(seed, STREAM_K, BH * S, D).reshape(BH, S, D)
     V = normals(seed, STREAM_V, BH * S, D).reshape(BH, S, D)
     gq = normals(seed, STREAM_GQ, 1, D, mul=0.1, add=1.0).reshape(D)
@@ -227,16 +228,20 @@ def make_attention_inputs(BH: int, S: int, D: int, seed: int = 0) -> AttnInputs:
     return AttnInputs(Q, K, V, gq, gk)
 
 
-def make_attention_onehot(BH: int, S: int, D: int, seed: int = 0):
+def make_attention_onehot(BH: int, S: int, D: int, seed: int = 0, G: int = 1):
     """Inputs whose softmax is exactly one-hot in fp32: gains of 40 and, per
-    batch-head, one key equal to q / 2 (exact in bf16), picked by the hash;
-    that key's score exceeds every other by thousands, so its weight is 1
-    and the others' are 0, and the output is that key's value row.
-    Returns (inputs, picked key index per batch-head)."""
-    inp = make_attention_inputs(BH, S, D, seed)
-    pick = (hashes(seed, STREAM_PICK, 0, BH, 0) % np.uint64(S)).astype(np.int64)
+    query, one key of its key/value head equal to q / 2 (exact in bf16),
+    picked by the hash (the G queries of a head pick keys S // G apart, so
+    they differ; needs S >= G); that key's score exceeds every other by
+    thousands, so its weight is 1 and the others' are 0, and the output is
+    that key's value row.  Returns (inputs, picked key index per query row,
+    shape [BH * G])."""
+    assert S >= G
+    inp = make_attention_inputs(BH, S, D, seed, G=G)
+    base = (hashes(seed, STREAM_PICK, 0, BH, 0) % np.uint64(S)).astype(np.int64)
+    pick = (base[:, None] + np.arange(G)[None, :] * (S // G)) % S
     Q = inp.Q.copy()
     K = inp.K.copy()
-    K[np.arange(BH), pick] = 0.5 * Q
+    K[np.repeat(np.arange(BH), G), pick.reshape(-1)] = 0.5 * Q
     g = np.full(D, 40.0, np.float32)
-    return AttnInputs(Q, K, inp.V, g, g), pick
+    return AttnInputs(Q, K, inp.V, g, g), pick.reshape(-1)

@@ -61,32 +61,37 @@ ORDER = list(WORKLOADS)
 
 @dataclass(frozen=True)
 class AttnWorkload:
-    """QKNorm + attention, one query per batch-head: Q [BH, D], K and V
-    [BH, S, D], gains [D], all bf16.  Q, K, V ~ N(0,1); gains ~ 1 + 0.1 N(0,1)."""
+    """QKNorm + attention, one query per query head: Q [BH * G, D], K and V
+    [BH, S, D] (BH key/value heads, G query heads sharing each), gains [D],
+    all bf16.  Q, K, V ~ N(0,1); gains ~ 1 + 0.1 N(0,1)."""
     name: str
     BH: int
     S: int
     D: int
     eps: float
     dtype: str = "bf16"
+    G: int = 1
 
     @property
     def elem_bytes(self) -> int:
         return 2
 
     def flops(self) -> int:
-        """Algorithmic flops: q.k and p.v, 2 * D each per key."""
-        return 4 * self.BH * self.S * self.D
+        """Algorithmic flops: q.k and p.v, 2 * D each per key and query."""
+        return 4 * self.BH * self.G * self.S * self.D
 
     def algo_bytes(self) -> int:
         """Every input once and O once."""
-        return (2 * self.BH * self.S * self.D + 2 * self.BH * self.D + 2 * self.D) * 2
+        return (2 * self.BH * self.S * self.D + 2 * self.BH * self.G * self.D + 2 * self.D) * 2
 
 
 ATTN_WORKLOADS = {
     w.name: w for w in (
         # 8 sequences x 32 heads attending over a 2048-token cache, head dim 128
         AttnWorkload("attn_bh256_s2048_d128", 256, 2048, 128, 1e-6),
+        # the same 256 query heads with grouped-query caches: 8 query heads per
+        # key/value head (32 key/value heads)
+        AttnWorkload("attn_gqa_bh32_g8_s2048_d128", 32, 2048, 128, 1e-6, G=8),
     )
 }
 

@@ -28,7 +28,8 @@ from . import _binding
 from ._binding import RmmError, load_library  # noqa: F401
 
 __all__ = ["rmsnorm_matmul", "rmsnorm_gated_mlp", "rmsnorm", "matmul", "gated_matmul",
-           "rmsnorm_lora", "lora_matmul", "qknorm_attention", "attention", "rmsnorm_matmul_chain",
+           "rmsnorm_lora", "lora_matmul", "qknorm_attention", "qknorm_attention_gqa", "attention",
+           "rmsnorm_matmul_chain",
            "RmmError", "load_library", "Workspace"]
 
 _DTYPES = {torch.float32: _binding.DTYPE_F32, torch.bfloat16: _binding.DTYPE_BF16}
@@ -288,6 +289,40 @@ def qknorm_attention(q, k, v, gq, gk, eps: float, out=None, splits: int = 0,
     return out
 
 
+def qknorm_attention_gqa(q, k, v, gq, gk, eps: float, out=None, splits: int = 0,
+                         workspace: Workspace | None = None):
+    """Grouped-query QKNorm + attention (bf16): q: [BH * G, D] with query row
+    h * G + g attending to key/value head h; k, v: [BH, S, D]; G = 1 .. 8."""
+    _check_operands([q, k, v, gq, gk], ["q", "k", "v", "gq", "gk"])
+    if q.dim() != 2 or k.dim() != 3 or gq.dim() != 1 or gk.dim() != 1:
+        raise ValueError("expected q: [BH * G, D], k, v: [BH, S, D], gq, gk: [D]")
+    BH, S, D = k.shape
+    if BH == 0 or q.shape[0] % BH != 0:
+        raise ValueError(f"q has {q.shape[0]} rows, not a multiple of {BH} key heads")
+    G = q.shape[0] // BH
+    if q.shape[1] != D or tuple(v.shape) != (BH, S, D) or gq.shape[0] != D or gk.shape[0] != D:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, "
+                         f"v {tuple(v.shape)}")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_operands([q, out], ["q", "out"])
+        if tuple(out.shape) != tuple(q.shape):
+            raise ValueError(f"out has shape {tuple(out.shape)}, expected {tuple(q.shape)}")
+    dtype = _DTYPES[q.dtype]
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    lib = load_library()
+    need = _binding.attention_gqa_workspace_bytes(dtype, BH, G, S, D, splits)
+    if workspace is None and need > 0:
+        workspace = _workspace_for(q.device, stream, need)
+    ws_ptr = workspace.ptr if workspace is not None else None
+    ws_bytes = workspace.nbytes if workspace is not None else 0
+    _binding.check(lib.qknorm_attention_gqa(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), gq.data_ptr(), gk.data_ptr(), out.data_ptr(),
+        float(eps), BH, G, S, D, dtype, splits, ws_ptr, ws_bytes, stream))
+    return out
+
+
 def attention(q, k, v, out=None, workspace: Workspace | None = None):
     """o = softmax(q . k^T / sqrt(D)) v per batch-head, the attention step alone
     (q and k already normalised; bf16; q: [BH, D], k, v: [BH, S, D], D = 64 or 128)."""
@@ -369,16 +404,18 @@ def chain_wait_flag(workspace: Workspace, M: int, K: int, L: int) -> int:
     return int(workspace.tensor[off:off + 4].view(torch.int32).item())
 
 
-def plan_attention(BH, S, D, splits=0, with_workspace=True):
-    """Chunks per batch-head and keys per chunk an attention call would run (host only)."""
+def plan_attention(BH, S, D, splits=0, with_workspace=True, G=1):
+    """Chunks per key/value head and keys per chunk an attention call would run
+    (host only); G query heads per key/value head."""
     base = 1 << 40
     span = 1 << 36
     ptrs = [base + i * span for i in range(7)]
     d = _binding.DTYPE_BF16
     ws = ptrs[6] if with_workspace else None
-    nb = _binding.attention_workspace_bytes(d, BH, S, D, splits) if with_workspace else 0
+    nb = (_binding.attention_gqa_workspace_bytes(d, BH, G, S, D, splits)
+          if with_workspace else 0)
     return _binding.plan_attention(ptrs[0], ptrs[1], ptrs[2], ptrs[3], ptrs[4], ptrs[5], 1e-6, BH,
-                                   S, D, d, splits, ws, nb)
+                                   S, D, d, splits, ws, nb, G=G)
 
 
 def plan(M, N, K, dtype=torch.bfloat16, gated=False, variant="auto", splits=0,

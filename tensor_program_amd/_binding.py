@@ -27,7 +27,8 @@ SYMBOLS = ("rmsnorm_matmul", "rmsnorm_gated_mlp", "rmsnorm_matmul_ex", "rmsnorm_
            "rmm_abi_version", "rmsnorm_lora", "rmsnorm_lora_ex", "rmm_lora_matmul",
            "rmm_lora_workspace_bytes", "rmm_plan_lora", "qknorm_attention",
            "qknorm_attention_ex", "rmm_attention_workspace_bytes", "rmm_plan_attention",
-           "rmm_attention",
+           "rmm_attention", "qknorm_attention_gqa", "rmm_attention_gqa_workspace_bytes",
+           "rmm_plan_attention_gqa",
            "rmsnorm_matmul_chain", "rmm_chain_workspace_bytes", "rmm_chain_flag_offset",
            "rmm_probe_hbm_read", "rmm_probe_mfma_bf16", "rmm_probe_mfma_flops",
            "rmsnorm_matmul_noalloc")
@@ -84,6 +85,14 @@ def load_library(path: str = LIB_PATH):
     lib.qknorm_attention_ex.restype = i32
     lib.rmm_attention.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, vp, sz, vp]
     lib.rmm_attention.restype = i32
+    lib.qknorm_attention_gqa.argtypes = [vp, vp, vp, vp, vp, vp, f32, i64, i64, i64, i64, i32, i32,
+                                         vp, sz, vp]
+    lib.qknorm_attention_gqa.restype = i32
+    lib.rmm_attention_gqa_workspace_bytes.argtypes = [i32, i64, i64, i64, i64, i32]
+    lib.rmm_attention_gqa_workspace_bytes.restype = sz
+    lib.rmm_plan_attention_gqa.argtypes = [vp, vp, vp, vp, vp, vp, f32, i64, i64, i64, i64, i32, i32,
+                                           vp, sz, ctypes.POINTER(i32), ctypes.POINTER(i64)]
+    lib.rmm_plan_attention_gqa.restype = i32
     lib.rmm_attention_workspace_bytes.argtypes = [i32, i64, i64, i64, i32]
     lib.rmm_attention_workspace_bytes.restype = sz
     lib.rmm_plan_attention.argtypes = [vp, vp, vp, vp, vp, vp, f32, i64, i64, i64, i32, i32, vp, sz,
@@ -176,10 +185,22 @@ def attention_workspace_bytes(dtype: int, BH: int, S: int, D: int, splits: int =
     return int(load_library().rmm_attention_workspace_bytes(dtype, BH, S, D, splits))
 
 
-def plan_attention(Q, K, V, gq, gk, O, eps, BH, S, D, dtype, splits=0, ws=None, ws_bytes=0):
-    """Host-only planning through rmm_plan_attention: (status, chunks, keys per chunk)."""
+def plan_attention(Q, K, V, gq, gk, O, eps, BH, S, D, dtype, splits=0, ws=None, ws_bytes=0,
+                   G=1):
+    """Host-only planning through rmm_plan_attention (rmm_plan_attention_gqa
+    for G > 1): (status, chunks, keys per chunk)."""
     c = ctypes.c_int(-1)
     kc = ctypes.c_int64(-1)
-    st = load_library().rmm_plan_attention(Q, K, V, gq, gk, O, eps, BH, S, D, dtype, splits, ws,
-                                           ws_bytes, ctypes.byref(c), ctypes.byref(kc))
+    lib = load_library()
+    if G == 1:
+        st = lib.rmm_plan_attention(Q, K, V, gq, gk, O, eps, BH, S, D, dtype, splits, ws,
+                                    ws_bytes, ctypes.byref(c), ctypes.byref(kc))
+    else:
+        st = lib.rmm_plan_attention_gqa(Q, K, V, gq, gk, O, eps, BH, G, S, D, dtype, splits, ws,
+                                        ws_bytes, ctypes.byref(c), ctypes.byref(kc))
     return st, c.value, kc.value
+
+
+def attention_gqa_workspace_bytes(dtype: int, BH: int, G: int, S: int, D: int,
+                                  splits: int = 0) -> int:
+    return int(load_library().rmm_attention_gqa_workspace_bytes(dtype, BH, G, S, D, splits))

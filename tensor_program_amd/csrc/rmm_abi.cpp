@@ -299,17 +299,19 @@ rmm_status run(const void* X, const void* g, const void* W1, const void* W3, voi
 }
 
 // QKNorm + attention: validation in the documented order, then the plan.
+// G: query heads per key/value head (BH counts key/value heads).
 rmm_status attn_plan_call(const void* Q, const void* K, const void* V, const void* gq,
                           const void* gk, const void* O, float eps, int64_t BH, int64_t S,
                           int64_t D, rmm_dtype dtype, int splits, const void* ws, size_t ws_bytes,
-                          AttnPlan* plan) {
+                          AttnPlan* plan, int64_t G = 1) {
   // 1. pointers
   if (BH > 0 && (!Q || !K || !V || !gq || !gk || !O)) return RMM_ERR_NULL;
-  // 2. shape: head dimension 64 or 128, at least one key
-  if (BH < 0 || S < 1 || (D != 64 && D != 128)) return RMM_ERR_SHAPE;
+  // 2. shape: head dimension 64 or 128, at least one key, 1..8 queries per head
+  if (BH < 0 || S < 1 || (D != 64 && D != 128) || G < 1 || G > 8) return RMM_ERR_SHAPE;
   int64_t sd, bhsd, tmp;
   if (__builtin_mul_overflow(S, D, &sd) || __builtin_mul_overflow(BH, sd, &bhsd) ||
-      __builtin_mul_overflow(bhsd, (int64_t)2, &tmp))
+      __builtin_mul_overflow(bhsd, (int64_t)2, &tmp) ||
+      __builtin_mul_overflow(BH * G * D, (int64_t)2, &tmp))
     return RMM_ERR_SHAPE;
   // 3. eps
   if (!isfinite(eps) || eps < 0.0f) return RMM_ERR_EPS;
@@ -322,7 +324,7 @@ rmm_status attn_plan_call(const void* Q, const void* K, const void* V, const voi
     return RMM_OK;
   }
   // 5. aliasing of the output
-  const size_t ob = (size_t)(BH * D) * 2;
+  const size_t ob = (size_t)(BH * G * D) * 2;
   if (overlaps(O, ob, Q, ob) || overlaps(O, ob, K, (size_t)bhsd * 2) ||
       overlaps(O, ob, V, (size_t)bhsd * 2) || overlaps(O, ob, gq, (size_t)D * 2) ||
       overlaps(O, ob, gk, (size_t)D * 2) || overlaps(O, ob, ws, ws ? ws_bytes : 0))
@@ -335,7 +337,7 @@ rmm_status attn_plan_call(const void* Q, const void* K, const void* V, const voi
   if (sd * 2 > (int64_t)INT32_MAX || splits < 0 || splits > S) return RMM_ERR_VARIANT;
   const int s = splits == 0 ? (ws ? 0 : 1) : splits;
   if (s > 1 && !ws) return RMM_ERR_WORKSPACE;
-  rmm_attention_plan(BH, S, D, s, plan);
+  rmm_attention_plan(BH, S, D, s, plan, G);
   if ((int64_t)plan->chunks * BH > (int64_t)INT32_MAX || plan->ws_bytes > (size_t)INT32_MAX)
     return RMM_ERR_VARIANT;
   // one arrival counter per batch-head, all in the workspace's counter region
@@ -464,7 +466,7 @@ rmm_status qknorm_attention_ex(const void* Q, const void* K, const void* V, cons
   const rmm_status st =
       attn_plan_call(Q, K, V, gq, gk, O, eps, BH, S, D, dtype, splits, ws, ws_bytes, &plan);
   if (st != RMM_OK || BH == 0) return st;
-  const AttnArgs a{Q, K, V, gq, gk, O, eps, BH, S, D, stream, 1};
+  const AttnArgs a{Q, K, V, gq, gk, O, eps, BH, S, D, stream, 1, 1};
   const hipError_t err = rmm_launch_attention(a, plan, plan.chunks > 1 ? ws : nullptr);
   if (err != hipSuccess) {
     g_last_hip_error = (int)err;
@@ -488,13 +490,40 @@ rmm_status rmm_attention(const void* Q, const void* K, const void* V, void* O, i
   const rmm_status st =
       attn_plan_call(Q, K, V, Q, Q, O, 0.0f, BH, S, D, dtype, 0, ws, ws_bytes, &plan);
   if (st != RMM_OK || BH == 0) return st;
-  const AttnArgs a{Q, K, V, Q, Q, O, 0.0f, BH, S, D, stream, 0};
+  const AttnArgs a{Q, K, V, Q, Q, O, 0.0f, BH, S, D, stream, 0, 1};
   const hipError_t err = rmm_launch_attention(a, plan, plan.chunks > 1 ? ws : nullptr);
   if (err != hipSuccess) {
     g_last_hip_error = (int)err;
     return RMM_ERR_HIP;
   }
   return RMM_OK;
+}
+
+rmm_status qknorm_attention_gqa(const void* Q, const void* K, const void* V, const void* gq,
+                                const void* gk, void* O, float eps, int64_t BH, int64_t G,
+                                int64_t S, int64_t D, rmm_dtype dtype, int splits, void* ws,
+                                size_t ws_bytes, hipStream_t stream) {
+  AttnPlan plan;
+  const rmm_status st =
+      attn_plan_call(Q, K, V, gq, gk, O, eps, BH, S, D, dtype, splits, ws, ws_bytes, &plan, G);
+  if (st != RMM_OK || BH == 0) return st;
+  const AttnArgs a{Q, K, V, gq, gk, O, eps, BH, S, D, stream, 1, G};
+  const hipError_t err = rmm_launch_attention(a, plan, plan.chunks > 1 ? ws : nullptr);
+  if (err != hipSuccess) {
+    g_last_hip_error = (int)err;
+    return RMM_ERR_HIP;
+  }
+  return RMM_OK;
+}
+
+size_t rmm_attention_gqa_workspace_bytes(rmm_dtype dtype, int64_t BH, int64_t G, int64_t S,
+                                         int64_t D, int splits) {
+  if (dtype != RMM_DTYPE_BF16 || BH <= 0 || S < 1 || (D != 64 && D != 128) || splits < 0 ||
+      splits > S || G < 1 || G > 8)
+    return 0;
+  AttnPlan plan;
+  rmm_attention_plan(BH, S, D, splits, &plan, G);
+  return plan.ws_bytes;
 }
 
 size_t rmm_attention_workspace_bytes(rmm_dtype dtype, int64_t BH, int64_t S, int64_t D,
@@ -505,6 +534,21 @@ size_t rmm_attention_workspace_bytes(rmm_dtype dtype, int64_t BH, int64_t S, int
   AttnPlan plan;
   rmm_attention_plan(BH, S, D, splits, &plan);
   return plan.ws_bytes;
+}
+
+rmm_status rmm_plan_attention_gqa(const void* Q, const void* K, const void* V, const void* gq,
+                                  const void* gk, const void* O, float eps, int64_t BH, int64_t G,
+                                  int64_t S, int64_t D, rmm_dtype dtype, int splits,
+                                  const void* ws, size_t ws_bytes, int* chunks_out,
+                                  int64_t* keys_per_chunk_out) {
+  AttnPlan plan;
+  const rmm_status st =
+      attn_plan_call(Q, K, V, gq, gk, O, eps, BH, S, D, dtype, splits, ws, ws_bytes, &plan, G);
+  if (st == RMM_OK) {
+    if (chunks_out) *chunks_out = plan.chunks;
+    if (keys_per_chunk_out) *keys_per_chunk_out = plan.kchunk;
+  }
+  return st;
 }
 
 rmm_status rmm_plan_attention(const void* Q, const void* K, const void* V, const void* gq,

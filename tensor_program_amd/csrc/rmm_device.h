@@ -184,25 +184,29 @@ hipError_t rmm_launch_stream(const RmmArgs& a, const StreamPlan& p, void* ws);
 // 32-bit buffer offsets.
 bool rmm_stream_fits(int64_t M, int64_t N, int64_t K);
 
-// QKNorm + attention, one query per batch-head (bf16, D = 64 or 128).
+// QKNorm + attention, one query per query head (bf16, D = 64 or 128); G
+// query heads share each key/value head.
 struct AttnArgs {
-  const void* Q;   // BH x D
+  const void* Q;   // (BH G) x D
   const void* K;   // BH x S x D
   const void* V;   // BH x S x D
   const void* gq;  // D
   const void* gk;  // D
-  void* O;         // BH x D
+  void* O;         // (BH G) x D
   float eps;
   int64_t BH, S, D;
   hipStream_t stream;
-  int norm;  // 1: QKNorm + attention; 0: attention on q and k as given (gains unused)
+  int norm;    // 1: QKNorm + attention; 0: attention on q and k as given (gains unused)
+  int64_t G;   // query heads per key/value head (1..8); Q and O hold BH * G rows
 };
 struct AttnPlan {
-  int64_t kchunk;  // keys per workgroup (a multiple of the workgroup's 64- or 128-key round)
-  int chunks;      // key chunks per batch-head, merged by the last arriving workgroup
+  int64_t kchunk;  // keys per workgroup (a multiple of the workgroup's key round)
+  int chunks;      // key chunks per key/value head, merged by the last arriving workgroup
   size_t ws_cnt_off, ws_part_off, ws_bytes;
 };
-void rmm_attention_plan(int64_t BH, int64_t S, int64_t D, int splits, AttnPlan* p);
+// BH: key/value heads; G: query heads per key/value head.
+void rmm_attention_plan(int64_t BH, int64_t S, int64_t D, int splits, AttnPlan* p,
+                        int64_t G = 1);
 hipError_t rmm_launch_attention(const AttnArgs& a, const AttnPlan& p, void* ws);
 
 // Unfused baseline, first kernel: Xn = bf16/f32(X * g / RMS) written out.

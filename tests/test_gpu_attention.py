@@ -175,3 +175,74 @@ def test_unfused_qknorm_workload_sampled(require_gpu):
     ref = oracle.qknorm_attention(inp.Q[heads], inp.K[heads], inp.V[heads], inp.gq, inp.gk,
                                   oracle.eps_as_passed(wl.eps))
     _check(o[torch.from_numpy(heads).cuda()], ref, "unfused workload")
+
+
+# Grouped queries: G query heads per key/value head, each key row read once
+# for the group.
+
+def _run_gqa(inp, eps, splits=0):
+    o = tpa.qknorm_attention_gqa(_dev(inp, "Q"), _dev(inp, "K"), _dev(inp, "V"), _dev(inp, "gq"),
+                                 _dev(inp, "gk"), eps, splits=splits)
+    torch.cuda.synchronize()
+    return o
+
+
+def _oracle_gqa(inp, G, eps, heads=None):
+    # the definition per query row: its key/value head's keys and values
+    K, V = np.repeat(inp.K, G, axis=0), np.repeat(inp.V, G, axis=0)
+    Q = inp.Q
+    if heads is not None:
+        rows = (heads[:, None] * G + np.arange(G)[None, :]).reshape(-1)
+        Q, K, V = Q[rows], K[rows], V[rows]
+    return oracle.qknorm_attention(Q, K, V, inp.gq, inp.gk, oracle.eps_as_passed(eps))
+
+
+GQA_ONEHOT = [
+    # (BH, G, S, D, splits)
+    (4, 2, 100, 128, 0), (3, 4, 64, 64, 0), (5, 7, 300, 128, 3), (2, 8, 129, 128, 0),
+    (6, 8, 1000, 64, 4), (4, 3, 8, 128, 0), (2, 5, 4096, 128, 0),
+]
+
+
+@pytest.mark.parametrize("case", GQA_ONEHOT, ids=lambda c: "x".join(map(str, c)))
+def test_attention_gqa_onehot_bitwise(case, require_gpu):
+    BH, G, S, D, splits = case
+    _log(f"gqa one-hot {case}")
+    inp, pick = synth.make_attention_onehot(BH, S, D, seed=BH + S + G, G=G)
+    o = _run_gqa(inp, 0.0, splits=splits)
+    heads = np.repeat(np.arange(BH), G)
+    want = synth.to_bf16_bits(inp.V[heads, pick])
+    got = _bits(o)
+    mism = np.argwhere(got != want)
+    assert mism.size == 0, f"{len(mism)} mismatches, first at {tuple(mism[0])}"
+
+
+@pytest.mark.parametrize("case", [(8, 2, 1000, 128, 0), (4, 3, 777, 64, 0), (4, 4, 4096, 128, 0),
+                                  (2, 8, 2048, 128, 5), (3, 6, 129, 64, 0), (16, 1, 1000, 128, 7)],
+                         ids=lambda c: "x".join(map(str, c)))
+@pytest.mark.parametrize("eps", [1e-6, 0.5])
+def test_attention_gqa_random(case, eps, require_gpu):
+    BH, G, S, D, splits = case
+    _log(f"gqa random {case} eps {eps}")
+    inp = synth.make_attention_inputs(BH, S, D, seed=S + G, G=G)
+    o = _run_gqa(inp, eps, splits=splits)
+    _check(o, _oracle_gqa(inp, G, eps), f"gqa {case}")
+
+
+def test_attention_gqa_g1_is_qknorm_attention(require_gpu):
+    inp = synth.make_attention_inputs(12, 1500, 128, seed=9)
+    a = _bits(_run_gqa(inp, 1e-6))
+    b = _bits(_run(inp, 1e-6))
+    assert np.array_equal(a, b)
+
+
+def test_attention_gqa_workload_sampled(require_gpu):
+    wl = synth.get_workload("attn_gqa_bh32_g8_s2048_d128")
+    _log("gqa workload, sampled heads")
+    inp = synth.make_attention_inputs(wl.BH, wl.S, wl.D, G=wl.G)
+    o = _run_gqa(inp, wl.eps)
+    heads = np.unique(np.concatenate([[0, wl.BH - 1],
+                                      np.random.default_rng(4).choice(wl.BH, 8, replace=False)]))
+    rows = (heads[:, None] * wl.G + np.arange(wl.G)[None, :]).reshape(-1)
+    _check(o[torch.from_numpy(rows).cuda()], _oracle_gqa(inp, wl.G, wl.eps, heads=heads),
+           "gqa workload")

@@ -289,11 +289,13 @@ rmm_status rmm_plan_attention(const void* Q, const void* K, const void* V, const
 
 /* Grouped-query form of qknorm_attention (several query heads per cached
  * key/value head, the layout of grouped-query attention; same reading of the
- * QKNorm + Attention row, "五、实验结果"): BH counts key/value heads, G in 1..8
+ * QKNorm + Attention row, "五、实验结果"): BH counts key/value heads, G in 1..16
  * query heads share each (RMM_ERR_SHAPE otherwise).  Q and O are (BH G) x D,
  * query row h G + g belonging to key/value head h; K and V are BH x S x D as
  * above.  One workgroup reads each key and value row once for the whole group
- * (every query's dot product, the key's sum of squares once).  Other rules,
+ * (every query's dot product, the key's sum of squares once); from G = 3 both
+ * products run on the matrix cores, with q gq gk and the softmax weights each
+ * carried as two bf16 parts (16 significant bits).  Other rules,
  * including the workspace (sized by rmm_attention_gqa_workspace_bytes) and
  * splits, are those of qknorm_attention_ex; G = 1 is qknorm_attention_ex. */
 rmm_status qknorm_attention_gqa(const void* Q, const void* K, const void* V, const void* gq,

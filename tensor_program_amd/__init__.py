@@ -279,8 +279,8 @@ def qknorm_attention(q, k, v, gq, gk, eps: float, out=None, splits: int = 0,
     dtype = _DTYPES[q.dtype]
     stream = torch.cuda.current_stream(q.device).cuda_stream
     need = _binding.attention_workspace_bytes(dtype, BH, S, D, splits)
-    if workspace is None and need > 0:
-        workspace = _workspace_for(q.device, stream, need)
+    if workspace is None and (need > 0 or splits > 1):  # a forced count needs one
+        workspace = _workspace_for(q.device, stream, max(need, 256))
     ws_ptr = workspace.ptr if workspace is not None else None
     ws_bytes = workspace.nbytes if workspace is not None else 0
     _binding.check(load_library().qknorm_attention_ex(
@@ -292,7 +292,7 @@ def qknorm_attention(q, k, v, gq, gk, eps: float, out=None, splits: int = 0,
 def qknorm_attention_gqa(q, k, v, gq, gk, eps: float, out=None, splits: int = 0,
                          workspace: Workspace | None = None):
     """Grouped-query QKNorm + attention (bf16): q: [BH * G, D] with query row
-    h * G + g attending to key/value head h; k, v: [BH, S, D]; G = 1 .. 8."""
+    h * G + g attending to key/value head h; k, v: [BH, S, D]; G = 1 .. 16."""
     _check_operands([q, k, v, gq, gk], ["q", "k", "v", "gq", "gk"])
     if q.dim() != 2 or k.dim() != 3 or gq.dim() != 1 or gk.dim() != 1:
         raise ValueError("expected q: [BH * G, D], k, v: [BH, S, D], gq, gk: [D]")
@@ -313,8 +313,8 @@ def qknorm_attention_gqa(q, k, v, gq, gk, eps: float, out=None, splits: int = 0,
     stream = torch.cuda.current_stream(q.device).cuda_stream
     lib = load_library()
     need = _binding.attention_gqa_workspace_bytes(dtype, BH, G, S, D, splits)
-    if workspace is None and need > 0:
-        workspace = _workspace_for(q.device, stream, need)
+    if workspace is None and (need > 0 or splits > 1):  # a forced count needs one
+        workspace = _workspace_for(q.device, stream, max(need, 256))
     ws_ptr = workspace.ptr if workspace is not None else None
     ws_bytes = workspace.nbytes if workspace is not None else 0
     _binding.check(lib.qknorm_attention_gqa(

@@ -306,8 +306,8 @@ rmm_status attn_plan_call(const void* Q, const void* K, const void* V, const voi
                           AttnPlan* plan, int64_t G = 1) {
   // 1. pointers
   if (BH > 0 && (!Q || !K || !V || !gq || !gk || !O)) return RMM_ERR_NULL;
-  // 2. shape: head dimension 64 or 128, at least one key, 1..8 queries per head
-  if (BH < 0 || S < 1 || (D != 64 && D != 128) || G < 1 || G > 8) return RMM_ERR_SHAPE;
+  // 2. shape: head dimension 64 or 128, at least one key, 1..16 queries per head
+  if (BH < 0 || S < 1 || (D != 64 && D != 128) || G < 1 || G > 16) return RMM_ERR_SHAPE;
   int64_t sd, bhsd, tmp;
   if (__builtin_mul_overflow(S, D, &sd) || __builtin_mul_overflow(BH, sd, &bhsd) ||
       __builtin_mul_overflow(bhsd, (int64_t)2, &tmp) ||
@@ -519,7 +519,7 @@ rmm_status qknorm_attention_gqa(const void* Q, const void* K, const void* V, con
 size_t rmm_attention_gqa_workspace_bytes(rmm_dtype dtype, int64_t BH, int64_t G, int64_t S,
                                          int64_t D, int splits) {
   if (dtype != RMM_DTYPE_BF16 || BH <= 0 || S < 1 || (D != 64 && D != 128) || splits < 0 ||
-      splits > S || G < 1 || G > 8)
+      splits > S || G < 1 || G > 16)
     return 0;
   AttnPlan plan;
   rmm_attention_plan(BH, S, D, splits, &plan, G);

@@ -333,6 +333,347 @@ __global__ __launch_bounds__(AT_THREADS) void qknorm_attention_kernel(
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Grouped queries on the matrix cores (G = 3 .. 16 query heads per key/value
+// head).  The VALU form above spends every query's dot product and value
+// update on the vector ALUs, which for G >= 4 costs more than streaming the
+// keys; here both products are 16 x 16 x 32 bf16 MFMAs over a block of up
+// to 16 queries:
+//   * scores, transposed: S^T (16 keys x 16 queries) = K (keys x 32 d) .
+//     U^T, with U = q gq gk (fp32) carried as two bf16 parts (16 significant
+//     bits of its 24: within 2^-17 of U); the K fragments are the key rows as
+//     loaded (lane l: key l % 16, 8 dims);
+//   * each lane then holds 4 keys of one query (column l % 16): the key's
+//     1/RMS (its sum of squares from the same K fragments, reduced over the
+//     4 lanes holding that key) and the query's scale give the score; the
+//     online softmax runs per query column over 32 keys per tile (2 x 16);
+//   * values: O (16 queries x 16 d) += P (queries x 32 keys) . V (keys x 16
+//     d), P (in [0, 1]) as two bf16 parts; P's A fragments are the score
+//     registers as they lie (lane l: query l % 16, keys 4 (l / 16) + i of
+//     both halves), and the matching V fragments come from the wave's V tile
+//     in LDS through two transposing reads (ds_read_b64_tr_b16: rows = keys
+//     4 (l / 16) .. +3 and 16 + 4 (l / 16) .. +3, column = d).
+// A workgroup (4 waves) owns one key/value head and a chunk of its keys;
+// wave w takes 32-key tiles w, w + 4, ...; each wave's tile loads for the
+// next tile are in flight while it multiplies the current one.  The waves'
+// (o, max, sum) merge through LDS, the chunks through the workspace as in
+// the VALU form.
+constexpr int AQ_THREADS = 256;
+typedef short at_i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) at_i16x4 at_lds_i16x4;
+typedef __attribute__((address_space(3))) char at_lds_char;
+
+template <int D>
+__device__ __forceinline__ int aq_v_off(int key, int n) {
+  // V tile row `key` (2 D bytes), 16-byte chunk c stored at c ^ 2 (key & 3):
+  // the 4 rows x 32 bytes of one transposing read hit 8 different chunks.
+  return key * (2 * D) + (((n >> 3) ^ (2 * (key & 3))) << 4) + ((n & 7) << 1);
+}
+
+template <int D, bool NORM>
+__global__ __launch_bounds__(AQ_THREADS) void gqa_mfma_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc,
+    const bf16_t* __restrict__ gq, const bf16_t* __restrict__ gk, bf16_t* __restrict__ O,
+    float eps, int64_t S, int64_t kchunk, int C, int G, unsigned* __restrict__ cnt,
+    float* __restrict__ part) {
+  constexpr int NDB = D / 32;       // 32-deep d blocks of the score products
+  constexpr int NOB = D / 16;       // 16-wide d blocks of O
+  constexpr int CPR = D / 8;        // 16-byte chunks per key row
+  constexpr int NV = 32 * CPR / 64; // V tile chunks per lane
+  constexpr int NWV = AQ_THREADS / 64;
+  __shared__ __attribute__((aligned(16))) char v_s[NWV][2][32 * 2 * D];
+  __shared__ float mo_s[NWV][16][D];
+  __shared__ float mm_s[NWV][16], ml_s[NWV][16];
+  __shared__ int last;
+
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lq = l & 15, lg = l >> 4;
+  const int64_t bh = blockIdx.x / C;
+  const int chunk = (int)(blockIdx.x % C);
+  const int64_t s_lo = (int64_t)chunk * kchunk;
+  const int64_t s_hi = (s_lo + kchunk < S) ? (s_lo + kchunk) : S;
+
+  // U^T fragments (query lq, dims 32 db + 8 lg .. +7) and the query's scale.
+  u32x4 uh[NDB], ul[NDB];
+  float cq;
+  {
+    float qss = 0.f;
+    constexpr u32x4 ones{kBf16OnePair, kBf16OnePair, kBf16OnePair, kBf16OnePair};
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int d0 = 32 * db + 8 * lg;
+      const u32x4 qv = lq < G ? *(const u32x4*)(Q + (bh * G + lq) * D + d0) : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 a = NORM ? *(const u32x4*)(gq + d0) : ones;
+      const u32x4 b = NORM ? *(const u32x4*)(gk + d0) : ones;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const float q0 = bf16_lo(qv[d]), q1 = bf16_hi(qv[d]);
+        const float u0 = q0 * bf16_lo(a[d]) * bf16_lo(b[d]);
+        const float u1 = q1 * bf16_hi(a[d]) * bf16_hi(b[d]);
+        const uint32_t hi = pack_bf16x2(u0, u1);
+        uh[db][d] = hi;
+        ul[db][d] = pack_bf16x2(u0 - bf16_lo(hi), u1 - bf16_hi(hi));
+        qss += q0 * q0 + q1 * q1;
+      }
+    }
+    qss += __shfl_xor(qss, 16);
+    qss += __shfl_xor(qss, 32);
+    cq = lq >= G ? 0.f
+         : NORM ? 1.0f / (__fsqrt_rn(__fdiv_rn(qss, (float)D) + eps) * __fsqrt_rn((float)D))
+                : 1.0f / __fsqrt_rn((float)D);
+  }
+
+  const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(Kc + bh * S * D), 0, (int)(S * D * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(Vc + bh * S * D), 0, (int)(S * D * 2), 0x00020000);
+  const int64_t ntile = (s_hi - s_lo + 31) / 32;
+  // Tile loads: K fragments (key 16 h + lq, dims 32 db + 8 lg) and the V
+  // tile's chunks (key j (64 / CPR) + l / CPR, chunk l % CPR).
+  auto load = [&](int64_t t, u32x4 (&kk)[2][NDB], u32x4 (&vv)[NV]) {
+    const int64_t k0 = s_lo + 32 * t;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int64_t key = k0 + 16 * h + lq;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        kk[h][db] = __builtin_amdgcn_raw_buffer_load_b128(
+            kr, key < s_hi ? (uint32_t)((key * D + 32 * db + 8 * lg) * 2) : kAtOutOfRange, 0, 0);
+    }
+#pragma unroll
+    for (int jv = 0; jv < NV; ++jv) {
+      const int64_t key = k0 + jv * (64 / CPR) + l / CPR;
+      vv[jv] = __builtin_amdgcn_raw_buffer_load_b128(
+          vr, key < s_hi ? (uint32_t)((key * D + 8 * (l % CPR)) * 2) : kAtOutOfRange, 0, 0);
+    }
+  };
+
+  float m = kAtNone, lpart = 0.f;
+  floatx4 o[NOB];
+#pragma unroll
+  for (int ob = 0; ob < NOB; ++ob) o[ob] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  auto consume = [&](int64_t t, int buf, const u32x4 (&kk)[2][NDB], const u32x4 (&vv)[NV]) {
+    // V tile into this wave's LDS buffer (the wave's own LDS operations
+    // complete in order, so its reads below see these writes).
+    char* vt = v_s[w][buf];
+#pragma unroll
+    for (int jv = 0; jv < NV; ++jv)
+      *(u32x4*)(vt + aq_v_off<D>(jv * (64 / CPR) + l / CPR, 8 * (l % CPR))) = vv[jv];
+    // Scores S^T and the keys' sums of squares.
+    floatx4 sc[2];
+    float rk[2][4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      sc[h] = floatx4{0.f, 0.f, 0.f, 0.f};
+      float ss = 0.f;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        sc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kk[h][db]),
+                                                        __builtin_bit_cast(bf16x8, uh[db]), sc[h],
+                                                        0, 0, 0);
+        sc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kk[h][db]),
+                                                        __builtin_bit_cast(bf16x8, ul[db]), sc[h],
+                                                        0, 0, 0);
+        if (NORM) {
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const float k0 = bf16_lo(kk[h][db][d]), k1 = bf16_hi(kk[h][db][d]);
+            ss += k0 * k0 + k1 * k1;
+          }
+        }
+      }
+      if (NORM) {
+        ss += __shfl_xor(ss, 16);
+        ss += __shfl_xor(ss, 32);
+        // 1/D is a power of two (exact); v_rsq_f32 for the key's 1/RMS.
+        const float r = __builtin_amdgcn_rsqf(ss * (1.0f / D) + eps);
+        // this lane's score rows are keys 4 lg + i of the half: their 1/RMS
+        // sits on the lanes whose key column lq is 4 lg + i
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rk[h][i] = __shfl(r, 4 * lg + i);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rk[h][i] = 1.0f;
+      }
+    }
+    // Online softmax per query column lq over the tile's 32 keys.
+    const int64_t k0 = s_lo + 32 * t;
+    float p[2][4];
+    float mb = kAtNone;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[h][i] = sc[h][i] * cq * rk[h][i];
+        if (k0 + 16 * h + 4 * lg + i < s_hi) mb = fmaxf(mb, p[h][i]);
+      }
+    mb = fmaxf(mb, __shfl_xor(mb, 16));
+    mb = fmaxf(mb, __shfl_xor(mb, 32));
+    const float mn = fmaxf(m, mb);
+    const float alpha = __expf(m - mn);
+    lpart *= alpha;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[h][i] = (k0 + 16 * h + 4 * lg + i < s_hi) ? __expf(p[h][i] - mn) : 0.f;
+        lpart += p[h][i];
+      }
+    m = mn;
+    // O rows are queries 4 lg + i: their alpha sits on lanes lq = 4 lg + i.
+    float ar[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * lg + i);
+    u32x4 ph, pl;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; i += 2) {
+        const uint32_t hi = pack_bf16x2(p[h][i], p[h][i + 1]);
+        ph[2 * h + i / 2] = hi;
+        pl[2 * h + i / 2] = pack_bf16x2(p[h][i] - bf16_lo(hi), p[h][i + 1] - bf16_hi(hi));
+      }
+    const at_lds_char* vl = (const at_lds_char*)vt;
+#pragma unroll
+    for (int ob = 0; ob < NOB; ++ob) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[ob][i] *= ar[i];
+      const int col = 16 * ob + 4 * (lq & 3), row = 4 * lg + (lq >> 2);
+      const u32x2 v0 = __builtin_bit_cast(
+          u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((at_lds_i16x4*)(vl + aq_v_off<D>(row, col))));
+      const u32x2 v1 = __builtin_bit_cast(
+          u32x2,
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((at_lds_i16x4*)(vl + aq_v_off<D>(row + 16, col))));
+      const u32x4 vb = {v0[0], v0[1], v1[0], v1[1]};
+      o[ob] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ph),
+                                                      __builtin_bit_cast(bf16x8, vb), o[ob], 0, 0,
+                                                      0);
+      o[ob] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pl),
+                                                      __builtin_bit_cast(bf16x8, vb), o[ob], 0, 0,
+                                                      0);
+    }
+  };
+
+  u32x4 ka[2][NDB], va[NV], kb[2][NDB], vb[NV];
+  load(w, ka, va);
+  load(w + NWV, kb, vb);
+  int64_t t = w;
+  for (; t + NWV < ntile; t += 2 * NWV) {
+    consume(t, 0, ka, va);
+    load(t + 2 * NWV, ka, va);
+    consume(t + NWV, 1, kb, vb);
+    load(t + 3 * NWV, kb, vb);
+  }
+  if (t < ntile) consume(t, 0, ka, va);
+
+  // This wave's (o, max, sum) per query into LDS.
+  lpart += __shfl_xor(lpart, 16);
+  lpart += __shfl_xor(lpart, 32);
+  if (lg == 0) {
+    mm_s[w][lq] = m;
+    ml_s[w][lq] = lpart;
+  }
+#pragma unroll
+  for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mo_s[w][4 * lg + i][16 * ob + lq] = o[ob][i];
+  __syncthreads();
+
+  // Thread t merges the waves for (query t / D, dim t % D), t < G D.
+  constexpr int PER = 16 * D / AQ_THREADS;
+  float od[PER], ld[PER], md[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int tt = tid + AQ_THREADS * e, g = tt / D, d = tt % D;
+    od[e] = 0.f;
+    ld[e] = 0.f;
+    md[e] = kAtNone;
+    if (g < G) {
+#pragma unroll
+      for (int ww = 0; ww < NWV; ++ww) md[e] = fmaxf(md[e], mm_s[ww][g]);
+#pragma unroll
+      for (int ww = 0; ww < NWV; ++ww) {
+        const float a = __expf(mm_s[ww][g] - md[e]);
+        od[e] += mo_s[ww][g][d] * a;
+        ld[e] += ml_s[ww][g] * a;
+      }
+    }
+  }
+  if (C > 1) {
+    const int64_t slot = bh * C + chunk;
+    const __amdgpu_buffer_rsrc_t pr =
+        __builtin_amdgcn_make_buffer_rsrc(part, 0, 0x7fffffff, 0x00020000);
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int tt = tid + AQ_THREADS * e, g = tt / D, d = tt % D;
+      if (g < G) {
+        const int64_t base = (slot * G + g) * (D + 2);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(od[e]), pr, (int)((base + d) * 4),
+                                              0, kAtCoherentDevice);
+        if (d == 0) {
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(md[e]), pr,
+                                                (int)((base + D) * 4), 0, kAtCoherentDevice);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ld[e]), pr,
+                                                (int)((base + D + 1) * 4), 0, kAtCoherentDevice);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0)
+      last = (__hip_atomic_fetch_add(&cnt[bh], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+              (unsigned)(C - 1));
+    __syncthreads();
+    if (!last) return;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int tt = tid + AQ_THREADS * e, g = tt / D, d = tt % D;
+      if (g < G) {
+        md[e] = kAtNone;
+        od[e] = 0.f;
+        ld[e] = 0.f;
+        for (int c0 = 0; c0 < C; c0 += 8) {
+          float oc[8], mc[8], lc[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const int64_t base = ((bh * C + c0 + q) * G + g) * (D + 2);
+            const bool in = c0 + q < C;
+            oc[q] = in ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                             pr, (int)((base + d) * 4), 0, kAtCoherentDevice))
+                       : 0.f;
+            mc[q] = in ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                             pr, (int)((base + D) * 4), 0, kAtCoherentDevice))
+                       : kAtNone;
+            lc[q] = in ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                             pr, (int)((base + D + 1) * 4), 0, kAtCoherentDevice))
+                       : 0.f;
+          }
+          float mn = md[e];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) mn = fmaxf(mn, mc[q]);
+          const float r = __expf(md[e] - mn);
+          od[e] *= r;
+          ld[e] *= r;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const float a = __expf(mc[q] - mn);
+            od[e] += oc[q] * a;
+            ld[e] += lc[q] * a;
+          }
+          md[e] = mn;
+        }
+      }
+    }
+    if (tid == 0) __hip_atomic_store(&cnt[bh], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int tt = tid + AQ_THREADS * e, g = tt / D, d = tt % D;
+    if (g < G) O[(bh * G + g) * D + d] = f32_to_bf16(__fdiv_rn(od[e], ld[e]));
+  }
+}
+
 }  // namespace rmm
 
 static size_t at_align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -341,12 +682,17 @@ static size_t at_align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // the combine costs more than the extra loads in flight buy), at least 256
 // keys per chunk, a whole number of the workgroup's key rounds.
 static int attn_group_template(int64_t G) { return G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8; }
+// Query groups from this size run on the matrix cores (gqa_mfma_kernel).
+constexpr int64_t kAttnMfmaMinG = 3;
 
 void rmm_attention_plan(int64_t BH, int64_t S, int64_t D, int splits, AttnPlan* p, int64_t G) {
   using namespace rmm;
   const int gt = attn_group_template(G);
   const int uu = gt == 1 ? AtCfg<1>::U : gt == 2 ? AtCfg<2>::U : gt == 4 ? AtCfg<4>::U : AtCfg<8>::U;
-  const int64_t round = (int64_t)(AT_THREADS / 64) * uu * (64 / (D / 8));  // keys per WG round
+  // keys per workgroup round: the VALU form's blocks, or the MFMA form's
+  // 32-key tiles over 4 waves
+  const int64_t round = G >= kAttnMfmaMinG ? (int64_t)(AQ_THREADS / 64) * 32
+                                          : (int64_t)(AT_THREADS / 64) * uu * (64 / (D / 8));
   int64_t C = splits;
   if (C <= 0) {
     const int64_t want = BH > 0 ? (256 + BH - 1) / BH : 1;
@@ -386,7 +732,14 @@ hipError_t rmm_launch_attention(const AttnArgs& a, const AttnPlan& p, void* ws) 
       a.norm ? launch(qknorm_attention_kernel<64, true, GT>)
              : launch(qknorm_attention_kernel<64, false, GT>);
   };
-  if ((a.D != 64 && a.D != 128) || a.G < 1 || a.G > 8) return hipErrorInvalidValue;
+  if ((a.D != 64 && a.D != 128) || a.G < 1 || a.G > 16) return hipErrorInvalidValue;
+  if (a.G >= kAttnMfmaMinG) {
+    if (a.D == 128)
+      a.norm ? launch(gqa_mfma_kernel<128, true>) : launch(gqa_mfma_kernel<128, false>);
+    else
+      a.norm ? launch(gqa_mfma_kernel<64, true>) : launch(gqa_mfma_kernel<64, false>);
+    return hipGetLastError();
+  }
   switch (attn_group_template(a.G)) {
     case 1: by_dim(std::integral_constant<int, 1>{}); break;
     case 2: by_dim(std::integral_constant<int, 2>{}); break;

@@ -178,7 +178,7 @@ def test_unfused_qknorm_workload_sampled(require_gpu):
 
 
 # Grouped queries: G query heads per key/value head, each key row read once
-# for the group.
+# for the group (G <= 2 on the vector ALUs, G >= 3 on the matrix cores).
 
 def _run_gqa(inp, eps, splits=0):
     o = tpa.qknorm_attention_gqa(_dev(inp, "Q"), _dev(inp, "K"), _dev(inp, "V"), _dev(inp, "gq"),
@@ -201,6 +201,7 @@ GQA_ONEHOT = [
     # (BH, G, S, D, splits)
     (4, 2, 100, 128, 0), (3, 4, 64, 64, 0), (5, 7, 300, 128, 3), (2, 8, 129, 128, 0),
     (6, 8, 1000, 64, 4), (4, 3, 8, 128, 0), (2, 5, 4096, 128, 0),
+    (2, 16, 300, 128, 0), (3, 12, 64, 64, 2), (5, 16, 33, 64, 0),
 ]
 
 
@@ -218,7 +219,8 @@ def test_attention_gqa_onehot_bitwise(case, require_gpu):
 
 
 @pytest.mark.parametrize("case", [(8, 2, 1000, 128, 0), (4, 3, 777, 64, 0), (4, 4, 4096, 128, 0),
-                                  (2, 8, 2048, 128, 5), (3, 6, 129, 64, 0), (16, 1, 1000, 128, 7)],
+                                  (2, 8, 2048, 128, 5), (3, 6, 129, 64, 0), (16, 1, 1000, 128, 7),
+                                  (4, 16, 1000, 128, 0), (2, 11, 3000, 64, 3)],
                          ids=lambda c: "x".join(map(str, c)))
 @pytest.mark.parametrize("eps", [1e-6, 0.5])
 def test_attention_gqa_random(case, eps, require_gpu):

@@ -54,6 +54,9 @@ def load(path: str = _LIB):
     lib.rmm_oracle_qknorm_attention_f64.restype = ctypes.c_int
     lib.rmm_oracle_attention_f64.argtypes = [vp, vp, vp, i64, i64, i64, vp]
     lib.rmm_oracle_attention_f64.restype = ctypes.c_int
+    lib.rmm_oracle_qknorm_attention_prefill_f64.argtypes = [vp, vp, vp, vp, vp, dbl, i64, i64,
+                                                            i64, i64, i64, ctypes.c_int, vp]
+    lib.rmm_oracle_qknorm_attention_prefill_f64.restype = ctypes.c_int
     return lib
 
 
@@ -189,6 +192,25 @@ def qknorm_attention(Q, K, V, gq, gk, eps, lib=None) -> np.ndarray:
     O = np.empty((BH, D), np.float64)
     rc = lib.rmm_oracle_qknorm_attention_f64(_p(Q), _p(K), _p(V), _p(gq), _p(gk), float(eps), BH,
                                              S, D, _p(O))
+    if rc != 0:
+        raise ValueError(f"oracle error {rc}")
+    return O
+
+
+def qknorm_attention_prefill(Q, K, V, gq, gk, eps, causal=True, lib=None) -> np.ndarray:
+    """QKNorm + attention for many queries per head, in fp64.  Q: [BH * G, Sq, D]
+    (query head h * G + g reads key/value head h), K and V: [BH, Skv, D]; causal:
+    query i sees keys 0 .. i + Skv - Sq.  -> O: [BH * G, Sq, D]."""
+    lib = lib or _default()
+    Q, K, V, gq, gk = _d(Q), _d(K), _d(V), _d(gq), _d(gk)
+    BHq, Sq, D = Q.shape
+    BH, Skv = K.shape[0], K.shape[1]
+    assert BH > 0 and BHq % BH == 0 and K.shape == (BH, Skv, D) and V.shape == K.shape
+    assert gq.shape == (D,) and gk.shape == (D,)
+    O = np.empty((BHq, Sq, D), np.float64)
+    rc = lib.rmm_oracle_qknorm_attention_prefill_f64(_p(Q), _p(K), _p(V), _p(gq), _p(gk),
+                                                     float(eps), BH, BHq // BH, Sq, Skv, D,
+                                                     int(bool(causal)), _p(O))
     if rc != 0:
         raise ValueError(f"oracle error {rc}")
     return O

@@ -46,6 +46,12 @@
  * (rmm_oracle_qknorm_attention_f64; the normalised vectors are materialised.)
  * The attention step alone, on given (already normalised) vectors, is
  * rmm_oracle_attention_f64: the second kernel of the unfused program.
+ * Many queries per head (prefill): every query row of a head attends, with
+ * the same normalisations, to its key/value head's keys; G query heads may
+ * share one key/value head (query head h G + g reads key head h), and with
+ * the causal mask query position i of Sq sees keys 0 .. i + Skv - Sq (the
+ * queries are the last Sq positions of the Skv cached ones)
+ * (rmm_oracle_qknorm_attention_prefill_f64).
  *
  * The steps are also exported one by one (rmm_oracle_rmsnorm_f64: steps 1-2,
  * rmm_oracle_matmul_f64: step 3, rmm_oracle_gated_matmul_f64: the two
@@ -306,6 +312,50 @@ int rmm_oracle_qknorm_attention_f64(const double* Q, const double* K, const doub
       normalise(k, gk, &rk, 1, D, kn + s * D);
     }
     attend(qn, kn, V + h * S * D, S, D, sc, O + h * D);
+    free(qn);
+    free(kn);
+    free(sc);
+  }
+  return rc;
+}
+
+/* QKNorm + attention for many queries per head.  Q and O: (BH G) x Sq x D,
+ * K and V: BH x Skv x D; query head qh reads key/value head qh / G; causal:
+ * query i attends to keys 0 .. i + Skv - Sq (needs Skv >= Sq), else to all. */
+int rmm_oracle_qknorm_attention_prefill_f64(const double* Q, const double* K, const double* V,
+                                            const double* gq, const double* gk, double eps,
+                                            int64_t BH, int64_t G, int64_t Sq, int64_t Skv,
+                                            int64_t D, int causal, double* O) {
+  if (BH < 0 || G < 1 || Sq <= 0 || Skv <= 0 || D <= 0 || (causal && Skv < Sq)) return 1;
+  int rc = 0;
+#pragma omp parallel for schedule(static)
+  for (int64_t qh = 0; qh < BH * G; ++qh) {
+    const int64_t h = qh / G;
+    double* qn = (double*)malloc(sizeof(double) * (size_t)D);
+    double* kn = (double*)malloc(sizeof(double) * (size_t)(Skv * D));
+    double* sc = (double*)malloc(sizeof(double) * (size_t)Skv);
+    if (!qn || !kn || !sc) {
+      free(qn);
+      free(kn);
+      free(sc);
+#pragma omp atomic write
+      rc = 2;
+      continue;
+    }
+    for (int64_t s = 0; s < Skv; ++s) {
+      const double* key = K + (h * Skv + s) * D;
+      double rkey;
+      row_rms(key, 1, D, eps, &rkey);
+      normalise(key, gk, &rkey, 1, D, kn + s * D);
+    }
+    for (int64_t i = 0; i < Sq; ++i) {
+      const double* q = Q + (qh * Sq + i) * D;
+      double rq;
+      row_rms(q, 1, D, eps, &rq);
+      normalise(q, gq, &rq, 1, D, qn);
+      const int64_t nk = causal ? i + Skv - Sq + 1 : Skv;
+      attend(qn, kn, V + h * Skv * D, nk, D, sc, O + (qh * Sq + i) * D);
+    }
     free(qn);
     free(kn);
     free(sc);

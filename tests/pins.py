@@ -456,7 +456,58 @@ def pin_attention(lib):
                               oracle.qknorm_attention(Q, K, V, gq, gk, eps, lib=lib))
 
 
+def _brute_prefill(Q, K, V, gq, gk, eps, causal):
+    # every query row of every query head, written out per the definition:
+    # its key/value head's keys (the first i + Skv - Sq + 1 under the mask)
+    BHq, Sq, Dd = Q.shape
+    BH, Skv = K.shape[0], K.shape[1]
+    G = BHq // BH
+    out = np.empty(Q.shape)
+    for qh in range(BHq):
+        for i in range(Sq):
+            n = i + Skv - Sq + 1 if causal else Skv
+            out[qh, i] = _brute_attention(Q[qh, i][None], K[qh // G, :n][None],
+                                          V[qh // G, :n][None], gq, gk, eps)[0]
+    return out
+
+
+def pin_qknorm_attention_prefill(lib):
+    """Many queries per head, grouped heads, the causal mask."""
+    rng = np.random.default_rng(47)
+    pre = lambda *a, **k: oracle.qknorm_attention_prefill(*a, lib=lib, **k)
+    for (BH, G, Sq, Skv, D) in ((2, 1, 3, 3, 4), (1, 3, 2, 5, 8), (2, 2, 4, 6, 4)):
+        Q = rng.normal(size=(BH * G, Sq, D))
+        K = rng.normal(size=(BH, Skv, D))
+        V = rng.normal(size=(BH, Skv, D))
+        gq = rng.normal(1.0, 0.3, size=D)
+        gk = rng.normal(1.0, 0.3, size=D)
+        eps = 0.125
+        for causal in (True, False):
+            ref = pre(Q, K, V, gq, gk, eps, causal=causal)
+            # brute force at 50 digits, query row by query row
+            _close(ref, _brute_prefill(Q, K, V, gq, gk, eps, causal), rtol=1e-12, atol=1e-13)
+        causal_ref = pre(Q, K, V, gq, gk, eps, causal=True)
+        full_ref = pre(Q, K, V, gq, gk, eps, causal=False)
+        Gh = np.repeat(np.arange(BH), G)
+        # without the mask each query row is the single-query call on its head
+        single = _attn(lib, Q.reshape(BH * G * Sq, D), np.repeat(K[Gh], Sq, axis=0),
+                       np.repeat(V[Gh], Sq, axis=0), gq, gk, eps)
+        assert np.array_equal(full_ref.reshape(-1, D), single)
+        # the last query sees every key: mask and no mask agree there
+        assert np.array_equal(causal_ref[:, -1], full_ref[:, -1])
+        # under the mask, query i ignores the keys after i + Skv - Sq: changing them
+        # (and their values) leaves it as it was
+        K2, V2 = K.copy(), V.copy()
+        K2[:, Skv - Sq + 1:] = rng.normal(size=K2[:, Skv - Sq + 1:].shape)
+        V2[:, Skv - Sq + 1:] = rng.normal(size=V2[:, Skv - Sq + 1:].shape)
+        assert np.array_equal(pre(Q, K2, V2, gq, gk, eps, causal=True)[:, 0], causal_ref[:, 0])
+        # with one visible key the first query's output is that key's value
+        if Skv == Sq:
+            for qh in range(BH * G):
+                assert np.array_equal(causal_ref[qh, 0], V[qh // G, 0])
+
+
 ALL_PINS = [pin_worked_example, pin_library_matmul, pin_identity_weight, pin_constant_row,
             pin_scale_law, pin_gain_fold, pin_structure, pin_zero_row, pin_brute_force,
             pin_gated_closed_forms, pin_unfused_steps, pin_lora, pin_qknorm_attention,
-            pin_attention]
+            pin_attention, pin_qknorm_attention_prefill]

@@ -45,6 +45,11 @@ MUTANTS = {
     "attn_values_reversed": ("const double* v = Vh + s * D;",
                              "const double* v = Vh + (S - 1 - s) * D;"),
     "attn_unnormalised_weights": ("const double p = sc[s] / den;", "const double p = sc[s];"),
+    "prefill_mask_ignored": ("const int64_t nk = causal ? i + Skv - Sq + 1 : Skv;",
+                             "const int64_t nk = causal ? Skv : Skv;"),
+    "prefill_head_of_query": ("const int64_t h = qh / G;", "const int64_t h = qh % BH;"),
+    "prefill_key_gain_is_query_gain": ("normalise(key, gk, &rkey, 1, D, kn + s * D);",
+                                       "normalise(key, gq, &rkey, 1, D, kn + s * D);"),
     "lora_last_rank_skipped": ("for (int64_t r = 0; r < R; ++r) {\n      double t = 0.0;",
                                "for (int64_t r = 0; r < R - 1; ++r) {\n      double t = 0.0;"),
 }

@@ -312,6 +312,25 @@ rmm_status rmm_plan_attention_gqa(const void* Q, const void* K, const void* V, c
                                   const void* ws, size_t ws_bytes, int* chunks_out,
                                   int64_t* keys_per_chunk_out);
 
+/* QKNorm + attention for many queries per head (prefill; same reading of the
+ * QKNorm + Attention row, "五、实验结果"): every query row is normalised and
+ * attends to its key/value head's normalised keys as in qknorm_attention.
+ * Layouts (row-major, packed, bf16 only): Q and O: (BH G) x Sq x D (query
+ * head h G + g, position i at ((h G + g) Sq + i) D), K and V: BH x Skv x D,
+ * gq, gk: D.  causal != 0: query position i attends to keys 0 .. i + Skv -
+ * Sq (the queries are the last Sq of the Skv positions; needs Skv >= Sq),
+ * else to all Skv keys.  Both products run on the matrix cores, with q gq gk
+ * and the softmax weights each carried as two bf16 parts (16 significant
+ * bits); no workspace.  Errors: RMM_ERR_NULL, RMM_ERR_SHAPE (BH < 0, G < 1,
+ * Sq or Skv < 1, D not 64 or 128, causal with Skv < Sq, element counts
+ * overflowing), RMM_ERR_EPS, RMM_ERR_DTYPE (bf16 only), RMM_ERR_ALIAS (O
+ * against any input), RMM_ERR_VARIANT (a pointer not 16-byte aligned, Skv D 2
+ * >= 2^31).  BH == 0 is a no-op. */
+rmm_status qknorm_attention_prefill(const void* Q, const void* K, const void* V, const void* gq,
+                                    const void* gk, void* O, float eps, int64_t BH, int64_t G,
+                                    int64_t Sq, int64_t Skv, int64_t D, int causal,
+                                    rmm_dtype dtype, hipStream_t stream);
+
 /* The attention step alone (the second kernel of the unfused QKNorm +
  * Attention program the same page's benchmark table compares against,
  * "五、实验结果"): Q and K arrive already normalised (rmsnorm over rows of

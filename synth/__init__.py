@@ -228,6 +228,18 @@ def make_attention_inputs(BH: int, S: int, D: int, seed: int = 0, G: int = 1) ->
     return AttnInputs(Q, K, V, gq, gk)
 
 
+def make_attention_prefill_inputs(BH: int, G: int, Sq: int, Skv: int, D: int,
+                                  seed: int = 0) -> AttnInputs:
+    """Many queries per head: Q [BH * G, Sq, D], K and V [BH, Skv, D], gains [D]
+    (the same distributions as make_attention_inputs)."""
+    Q = normals(seed, STREAM_Q, BH * G * Sq, D).reshape(BH * G, Sq, D)
+    K = normals(seed, STREAM_K, BH * Skv, D).reshape(BH, Skv, D)
+    V = normals(seed, STREAM_V, BH * Skv, D).reshape(BH, Skv, D)
+    gq = normals(seed, STREAM_GQ, 1, D, mul=0.1, add=1.0).reshape(D)
+    gk = normals(seed, STREAM_GK, 1, D, mul=0.1, add=1.0).reshape(D)
+    return AttnInputs(Q, K, V, gq, gk)
+
+
 def make_attention_onehot(BH: int, S: int, D: int, seed: int = 0, G: int = 1):
     """Inputs whose softmax is exactly one-hot in fp32: gains of 40 and, per
     query, one key of its key/value head equal to q / 2 (exact in bf16),

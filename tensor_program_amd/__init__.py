@@ -28,7 +28,8 @@ from . import _binding
 from ._binding import RmmError, load_library  # noqa: F401
 
 __all__ = ["rmsnorm_matmul", "rmsnorm_gated_mlp", "rmsnorm", "matmul", "gated_matmul",
-           "rmsnorm_lora", "lora_matmul", "qknorm_attention", "qknorm_attention_gqa", "attention",
+           "rmsnorm_lora", "lora_matmul", "qknorm_attention", "qknorm_attention_gqa",
+           "qknorm_attention_prefill", "attention",
            "rmsnorm_matmul_chain",
            "RmmError", "load_library", "Workspace"]
 
@@ -320,6 +321,34 @@ def qknorm_attention_gqa(q, k, v, gq, gk, eps: float, out=None, splits: int = 0,
     _binding.check(lib.qknorm_attention_gqa(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), gq.data_ptr(), gk.data_ptr(), out.data_ptr(),
         float(eps), BH, G, S, D, dtype, splits, ws_ptr, ws_bytes, stream))
+    return out
+
+
+def qknorm_attention_prefill(q, k, v, gq, gk, eps: float, causal: bool = True, out=None):
+    """QKNorm + attention for many queries per head (bf16): q: [BH * G, Sq, D]
+    (query head h * G + g reads key/value head h), k, v: [BH, Skv, D]; causal:
+    query position i sees keys 0 .. i + Skv - Sq."""
+    _check_operands([q, k, v, gq, gk], ["q", "k", "v", "gq", "gk"])
+    if q.dim() != 3 or k.dim() != 3 or gq.dim() != 1 or gk.dim() != 1:
+        raise ValueError("expected q: [BH * G, Sq, D], k, v: [BH, Skv, D], gq, gk: [D]")
+    BH, Skv, D = k.shape
+    BHq, Sq = q.shape[0], q.shape[1]
+    if BH == 0 or BHq % BH != 0:
+        raise ValueError(f"q has {BHq} heads, not a multiple of {BH} key heads")
+    if q.shape[2] != D or tuple(v.shape) != (BH, Skv, D) or gq.shape[0] != D or \
+            gk.shape[0] != D:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, "
+                         f"v {tuple(v.shape)}")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_operands([q, out], ["q", "out"])
+        if tuple(out.shape) != tuple(q.shape):
+            raise ValueError(f"out has shape {tuple(out.shape)}, expected {tuple(q.shape)}")
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    _binding.check(load_library().qknorm_attention_prefill(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), gq.data_ptr(), gk.data_ptr(), out.data_ptr(),
+        float(eps), BH, BHq // BH, Sq, Skv, D, int(bool(causal)), _DTYPES[q.dtype], stream))
     return out
 
 

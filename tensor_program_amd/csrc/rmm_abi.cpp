@@ -516,6 +516,49 @@ rmm_status qknorm_attention_gqa(const void* Q, const void* K, const void* V, con
   return RMM_OK;
 }
 
+rmm_status qknorm_attention_prefill(const void* Q, const void* K, const void* V, const void* gq,
+                                    const void* gk, void* O, float eps, int64_t BH, int64_t G,
+                                    int64_t Sq, int64_t Skv, int64_t D, int causal,
+                                    rmm_dtype dtype, hipStream_t stream) {
+  // 1. pointers
+  if (BH > 0 && (!Q || !K || !V || !gq || !gk || !O)) return RMM_ERR_NULL;
+  // 2. shape
+  if (BH < 0 || G < 1 || Sq < 1 || Skv < 1 || (D != 64 && D != 128) || (causal && Skv < Sq))
+    return RMM_ERR_SHAPE;
+  int64_t bhg, qn, kn, tmp;
+  if (__builtin_mul_overflow(BH, G, &bhg) || __builtin_mul_overflow(bhg, Sq * D, &qn) ||
+      __builtin_mul_overflow(Sq, D, &tmp) || __builtin_mul_overflow(BH, Skv * D, &kn) ||
+      __builtin_mul_overflow(Skv, D, &tmp) || __builtin_mul_overflow(qn, (int64_t)2, &tmp) ||
+      __builtin_mul_overflow(kn, (int64_t)2, &tmp))
+    return RMM_ERR_SHAPE;
+  // 3. eps
+  if (!isfinite(eps) || eps < 0.0f) return RMM_ERR_EPS;
+  // 4. dtype
+  if (dtype != RMM_DTYPE_BF16) return RMM_ERR_DTYPE;
+  if (BH == 0) return RMM_OK;
+  // 5. aliasing of the output
+  const size_t ob = (size_t)qn * 2;
+  if (overlaps(O, ob, Q, ob) || overlaps(O, ob, K, (size_t)kn * 2) ||
+      overlaps(O, ob, V, (size_t)kn * 2) || overlaps(O, ob, gq, (size_t)D * 2) ||
+      overlaps(O, ob, gk, (size_t)D * 2))
+    return RMM_ERR_ALIAS;
+  // 6. what the kernel can run: 16-byte aligned operands, 32-bit offsets
+  // within one head's keys, one workgroup per 64 positions of a query head
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(gq) || !aligned16(gk) ||
+      !aligned16(O))
+    return RMM_ERR_VARIANT;
+  if (Skv * D * 2 > (int64_t)INT32_MAX || bhg * ((Sq + 63) / 64) > (int64_t)INT32_MAX ||
+      G > (int64_t)INT32_MAX)
+    return RMM_ERR_VARIANT;
+  AttnArgs a{Q, K, V, gq, gk, O, eps, BH, Skv, D, stream, 1, G};
+  const hipError_t err = rmm_launch_attention_prefill(a, Sq, Skv, causal ? 1 : 0);
+  if (err != hipSuccess) {
+    g_last_hip_error = (int)err;
+    return RMM_ERR_HIP;
+  }
+  return RMM_OK;
+}
+
 size_t rmm_attention_gqa_workspace_bytes(rmm_dtype dtype, int64_t BH, int64_t G, int64_t S,
                                          int64_t D, int splits) {
   if (dtype != RMM_DTYPE_BF16 || BH <= 0 || S < 1 || (D != 64 && D != 128) || splits < 0 ||

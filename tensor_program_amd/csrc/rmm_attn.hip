@@ -674,6 +674,252 @@ __global__ __launch_bounds__(AQ_THREADS) void gqa_mfma_kernel(
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Many queries per head (prefill): Q and O are (BH G) x Sq x D, K and V are
+// BH x Skv x D (query head qh reads key/value head qh / G); with the causal
+// mask query i sees keys 0 .. i + Skv - Sq.  The same two matrix-core
+// products as gqa_mfma_kernel, on blocks of 16 query positions:
+//   * a workgroup (4 waves) owns 64 consecutive positions of one query
+//     head, wave w the 16 rows 16 w ..; each 32-key tile of K and V is loaded
+//     once per workgroup into LDS (double-buffered, one barrier per tile; the
+//     next tile travels in registers meanwhile) and read by all four waves;
+//   * K rows as the A fragments of the transposed scores come from LDS with
+//     16-byte reads (chunk c of key row j stored at c ^ (j mod D/8), so the
+//     16 keys of one read hit 16 different chunks); V as in gqa_mfma_kernel;
+//   * every wave keeps its own queries' softmax state over all the keys its
+//     block needs, so nothing is combined across workgroups: o / sum is
+//     stored directly.  Workgroups are ordered so that an XCD takes a
+//     contiguous range of (head, block) pairs, the heads' longest (latest)
+//     blocks first.
+constexpr int AP_THREADS = 256;
+constexpr int AP_QB = 64;  // query positions per workgroup
+
+template <int D>
+__device__ __forceinline__ int ap_k_off(int key, int c) {
+  return key * (2 * D) + ((c ^ (key & (D / 8 - 1))) << 4);
+}
+
+template <int D, bool NORM, bool CAUSAL>
+__global__ __launch_bounds__(AP_THREADS) void attn_prefill_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc,
+    const bf16_t* __restrict__ gq, const bf16_t* __restrict__ gk, bf16_t* __restrict__ O,
+    float eps, int64_t Sq, int64_t Skv, int G, int nblk, int xcd_remap) {
+  constexpr int NDB = D / 32;
+  constexpr int NOB = D / 16;
+  constexpr int CPR = D / 8;
+  constexpr int NL = 32 * CPR / AP_THREADS;  // K (and V) tile chunks per thread
+  __shared__ __attribute__((aligned(16))) char k_s[2][32 * 2 * D];
+  __shared__ __attribute__((aligned(16))) char v_s[2][32 * 2 * D];
+
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lq = l & 15, lg = l >> 4;
+  const int64_t total = (int64_t)gridDim.x;
+  int64_t t = blockIdx.x;
+  if (xcd_remap) t = (t & 7) * (total >> 3) + (t >> 3);
+  const int64_t qh = t / nblk;
+  const int64_t blk = nblk - 1 - t % nblk;
+  const int64_t h = qh / G;
+  const int64_t p0 = blk * AP_QB + 16 * w;   // this wave's first query position
+  const int64_t off = Skv - Sq;              // causal horizon of position p: p + off
+
+  // U^T fragments of this wave's 16 queries and their scales.
+  u32x4 uh[NDB], ul[NDB];
+  float cq;
+  {
+    const int64_t p = p0 + lq;
+    const bool qok = p < Sq;
+    float qss = 0.f;
+    constexpr u32x4 ones{kBf16OnePair, kBf16OnePair, kBf16OnePair, kBf16OnePair};
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int d0 = 32 * db + 8 * lg;
+      const u32x4 qv = qok ? *(const u32x4*)(Q + (qh * Sq + p) * D + d0) : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 a = NORM ? *(const u32x4*)(gq + d0) : ones;
+      const u32x4 b = NORM ? *(const u32x4*)(gk + d0) : ones;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const float q0 = bf16_lo(qv[d]), q1 = bf16_hi(qv[d]);
+        const float u0 = q0 * bf16_lo(a[d]) * bf16_lo(b[d]);
+        const float u1 = q1 * bf16_hi(a[d]) * bf16_hi(b[d]);
+        const uint32_t hi = pack_bf16x2(u0, u1);
+        uh[db][d] = hi;
+        ul[db][d] = pack_bf16x2(u0 - bf16_lo(hi), u1 - bf16_hi(hi));
+        qss += q0 * q0 + q1 * q1;
+      }
+    }
+    qss += __shfl_xor(qss, 16);
+    qss += __shfl_xor(qss, 32);
+    cq = !qok ? 0.f
+         : NORM ? 1.0f / (__fsqrt_rn(__fdiv_rn(qss, (float)D) + eps) * __fsqrt_rn((float)D))
+                : 1.0f / __fsqrt_rn((float)D);
+  }
+
+  // Keys the block needs: up to the horizon of its last position.
+  int64_t kend = Skv;
+  if (CAUSAL) {
+    const int64_t last = (blk + 1) * AP_QB - 1 < Sq - 1 ? (blk + 1) * AP_QB - 1 : Sq - 1;
+    kend = last + off + 1;
+  }
+  const int64_t ntile = (kend + 31) / 32;
+  const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(Kc + h * Skv * D), 0, (int)(Skv * D * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(Vc + h * Skv * D), 0, (int)(Skv * D * 2), 0x00020000);
+  // Tile loads into registers: chunk e = tid + 256 j is key e / CPR, chunk e % CPR.
+  auto load = [&](int64_t tt, u32x4 (&kk)[NL], u32x4 (&vv)[NL]) {
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      const int e = tid + AP_THREADS * j;
+      const int64_t key = 32 * tt + e / CPR;
+      const uint32_t o = (tt < ntile && key < kend) ? (uint32_t)((key * D + 8 * (e % CPR)) * 2)
+                                                    : kAtOutOfRange;
+      kk[j] = __builtin_amdgcn_raw_buffer_load_b128(kr, o, 0, 0);
+      vv[j] = __builtin_amdgcn_raw_buffer_load_b128(vr, o, 0, 0);
+    }
+  };
+  auto store = [&](int stage, const u32x4 (&kk)[NL], const u32x4 (&vv)[NL]) {
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      const int e = tid + AP_THREADS * j, key = e / CPR, c = e % CPR;
+      *(u32x4*)(k_s[stage] + ap_k_off<D>(key, c)) = kk[j];
+      *(u32x4*)(v_s[stage] + aq_v_off<D>(key, 8 * c)) = vv[j];
+    }
+  };
+
+  float m = kAtNone, lpart = 0.f;
+  floatx4 o[NOB];
+#pragma unroll
+  for (int ob = 0; ob < NOB; ++ob) o[ob] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int64_t tt, int stage) {
+    const char* ks = k_s[stage];
+    const int64_t k0 = 32 * tt;
+    floatx4 sc[2];
+    float rk[2][4];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      sc[hh] = floatx4{0.f, 0.f, 0.f, 0.f};
+      float ss = 0.f;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const u32x4 kf = *(const u32x4*)(ks + ap_k_off<D>(16 * hh + lq, 4 * db + lg));
+        sc[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf),
+                                                         __builtin_bit_cast(bf16x8, uh[db]),
+                                                         sc[hh], 0, 0, 0);
+        sc[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf),
+                                                         __builtin_bit_cast(bf16x8, ul[db]),
+                                                         sc[hh], 0, 0, 0);
+        if (NORM) {
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const float a0 = bf16_lo(kf[d]), a1 = bf16_hi(kf[d]);
+            ss += a0 * a0 + a1 * a1;
+          }
+        }
+      }
+      if (NORM) {
+        ss += __shfl_xor(ss, 16);
+        ss += __shfl_xor(ss, 32);
+        const float r = __builtin_amdgcn_rsqf(ss * (1.0f / D) + eps);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rk[hh][i] = __shfl(r, 4 * lg + i);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rk[hh][i] = 1.0f;
+      }
+    }
+    // Visible keys of query column lq: below kend and, causal, within its horizon.
+    const int64_t horizon = CAUSAL ? p0 + lq + off : kend - 1;
+    float p[2][4];
+    bool ok[2][4];
+    float mb = kAtNone;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t key = k0 + 16 * hh + 4 * lg + i;
+        ok[hh][i] = key < kend && key <= horizon;
+        p[hh][i] = sc[hh][i] * cq * rk[hh][i];
+        if (ok[hh][i]) mb = fmaxf(mb, p[hh][i]);
+      }
+    mb = fmaxf(mb, __shfl_xor(mb, 16));
+    mb = fmaxf(mb, __shfl_xor(mb, 32));
+    const float mn = fmaxf(m, mb);
+    const float alpha = __expf(m - mn);
+    lpart *= alpha;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[hh][i] = ok[hh][i] ? __expf(p[hh][i] - mn) : 0.f;
+        lpart += p[hh][i];
+      }
+    m = mn;
+    float ar[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * lg + i);
+    u32x4 ph, pl;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int i = 0; i < 4; i += 2) {
+        const uint32_t hi = pack_bf16x2(p[hh][i], p[hh][i + 1]);
+        ph[2 * hh + i / 2] = hi;
+        pl[2 * hh + i / 2] = pack_bf16x2(p[hh][i] - bf16_lo(hi), p[hh][i + 1] - bf16_hi(hi));
+      }
+    const at_lds_char* vl = (const at_lds_char*)v_s[stage];
+#pragma unroll
+    for (int ob = 0; ob < NOB; ++ob) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[ob][i] *= ar[i];
+      const int col = 16 * ob + 4 * (lq & 3), row = 4 * lg + (lq >> 2);
+      const u32x2 v0 = __builtin_bit_cast(
+          u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((at_lds_i16x4*)(vl + aq_v_off<D>(row, col))));
+      const u32x2 v1 = __builtin_bit_cast(
+          u32x2,
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((at_lds_i16x4*)(vl + aq_v_off<D>(row + 16, col))));
+      const u32x4 vb = {v0[0], v0[1], v1[0], v1[1]};
+      o[ob] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ph),
+                                                      __builtin_bit_cast(bf16x8, vb), o[ob], 0, 0,
+                                                      0);
+      o[ob] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pl),
+                                                      __builtin_bit_cast(bf16x8, vb), o[ob], 0, 0,
+                                                      0);
+    }
+  };
+
+  // Pipeline: at the top of iteration tt stage tt & 1 holds tile tt (the
+  // barrier publishes it, and every wave is done with the other stage);
+  // tile tt + 1 goes from registers into the other stage, tile tt + 2 is
+  // loaded into registers, tile tt is multiplied.
+  u32x4 kk[NL], vv[NL];
+  load(0, kk, vv);
+  store(0, kk, vv);
+  load(1, kk, vv);
+  for (int64_t tt = 0; tt < ntile; ++tt) {
+    __syncthreads();
+    if (tt + 1 < ntile) store((int)((tt + 1) & 1), kk, vv);
+    load(tt + 2, kk, vv);
+    compute(tt, (int)(tt & 1));
+  }
+
+  // o / sum for this wave's rows (queries 4 lg + i of its block of 16).
+  lpart += __shfl_xor(lpart, 16);
+  lpart += __shfl_xor(lpart, 32);
+  float lr[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lr[i] = __shfl(lpart, 4 * lg + i);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t p = p0 + 4 * lg + i;
+    if (p < Sq) {
+#pragma unroll
+      for (int ob = 0; ob < NOB; ++ob)
+        O[(qh * Sq + p) * D + 16 * ob + lq] = f32_to_bf16(__fdiv_rn(o[ob][i], lr[i]));
+    }
+  }
+}
+
 }  // namespace rmm
 
 static size_t at_align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -745,6 +991,33 @@ hipError_t rmm_launch_attention(const AttnArgs& a, const AttnPlan& p, void* ws) 
     case 2: by_dim(std::integral_constant<int, 2>{}); break;
     case 4: by_dim(std::integral_constant<int, 4>{}); break;
     default: by_dim(std::integral_constant<int, 8>{}); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t rmm_launch_attention_prefill(const AttnArgs& a, int64_t Sq, int64_t Skv, int causal) {
+  using namespace rmm;
+  const int64_t nblk = (Sq + AP_QB - 1) / AP_QB;
+  const int64_t grid = a.BH * a.G * nblk;
+  const int remap = grid % 8 == 0;
+  auto launch = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(AP_THREADS), 0, a.stream,
+                       (const bf16_t*)a.Q, (const bf16_t*)a.K, (const bf16_t*)a.V,
+                       (const bf16_t*)a.gq, (const bf16_t*)a.gk, (bf16_t*)a.O, a.eps, Sq, Skv,
+                       (int)a.G, (int)nblk, remap);
+  };
+  if (a.D == 128) {
+    if (a.norm)
+      causal ? launch(attn_prefill_kernel<128, true, true>) : launch(attn_prefill_kernel<128, true, false>);
+    else
+      causal ? launch(attn_prefill_kernel<128, false, true>) : launch(attn_prefill_kernel<128, false, false>);
+  } else if (a.D == 64) {
+    if (a.norm)
+      causal ? launch(attn_prefill_kernel<64, true, true>) : launch(attn_prefill_kernel<64, true, false>);
+    else
+      causal ? launch(attn_prefill_kernel<64, false, true>) : launch(attn_prefill_kernel<64, false, false>);
+  } else {
+    return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

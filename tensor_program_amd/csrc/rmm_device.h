@@ -208,6 +208,9 @@ struct AttnPlan {
 void rmm_attention_plan(int64_t BH, int64_t S, int64_t D, int splits, AttnPlan* p,
                         int64_t G = 1);
 hipError_t rmm_launch_attention(const AttnArgs& a, const AttnPlan& p, void* ws);
+// Many queries per head: Q and O (BH G) x Sq x D, K and V BH x Skv x D (a.S
+// unused); causal: query i sees keys 0 .. i + Skv - Sq.
+hipError_t rmm_launch_attention_prefill(const AttnArgs& a, int64_t Sq, int64_t Skv, int causal);
 
 // Unfused baseline, first kernel: Xn = bf16/f32(X * g / RMS) written out.
 hipError_t rmm_launch_rmsnorm(const void* X, const void* g, void* Xn, float eps, int64_t M,

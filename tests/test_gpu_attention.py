@@ -248,3 +248,65 @@ def test_attention_gqa_workload_sampled(require_gpu):
     rows = (heads[:, None] * wl.G + np.arange(wl.G)[None, :]).reshape(-1)
     _check(o[torch.from_numpy(rows).cuda()], _oracle_gqa(inp, wl.G, wl.eps, heads=heads),
            "gqa workload")
+
+
+# Many queries per head (prefill): blocks of 64 positions per workgroup, the
+# causal mask, grouped heads.
+
+def _run_prefill(inp, eps, causal):
+    o = tpa.qknorm_attention_prefill(_dev(inp, "Q"), _dev(inp, "K"), _dev(inp, "V"),
+                                     _dev(inp, "gq"), _dev(inp, "gk"), eps, causal=causal)
+    torch.cuda.synchronize()
+    return o
+
+
+@pytest.mark.parametrize("case", [(2, 2, 100, 128, True), (2, 2, 100, 128, False),
+                                  (1, 3, 70, 64, True), (3, 1, 129, 128, True)],
+                         ids=lambda c: "x".join(map(str, c)))
+def test_attention_prefill_onehot_bitwise(case, require_gpu):
+    # Query (g, i) of a head finds its own key at position g Sq + i (within its
+    # horizon i + Skv - Sq when Skv = G Sq), equal to q / 2, gains of 40: the
+    # softmax is exactly one-hot and the output is that key's value row.
+    BH, G, Sq, D, causal = case
+    Skv = G * Sq
+    _log(f"prefill one-hot {case}")
+    inp = synth.make_attention_prefill_inputs(BH, G, Sq, Skv, D, seed=Sq + G)
+    Q, K = inp.Q.copy(), inp.K.copy()
+    for qh in range(BH * G):
+        K[qh // G, (qh % G) * Sq + np.arange(Sq)] = 0.5 * Q[qh]
+    g40 = np.full(D, 40.0, np.float32)
+    inp = synth.AttnInputs(Q, K, inp.V, g40, g40)
+    o = _run_prefill(inp, 0.0, causal)
+    want = np.stack([inp.V[qh // G, (qh % G) * Sq + np.arange(Sq)] for qh in range(BH * G)])
+    got = _bits(o)
+    mism = np.argwhere(got != synth.to_bf16_bits(want))
+    assert mism.size == 0, f"{len(mism)} mismatches, first at {tuple(mism[0])}"
+
+
+@pytest.mark.parametrize("case", [(2, 1, 200, 200, 128, True), (2, 4, 130, 300, 64, True),
+                                  (1, 2, 64, 1000, 128, False), (3, 1, 1, 50, 128, True),
+                                  (1, 8, 257, 257, 128, True), (2, 3, 65, 90, 64, False)],
+                         ids=lambda c: "x".join(map(str, c)))
+@pytest.mark.parametrize("eps", [1e-6, 0.5])
+def test_attention_prefill_random(case, eps, require_gpu):
+    BH, G, Sq, Skv, D, causal = case
+    _log(f"prefill random {case} eps {eps}")
+    inp = synth.make_attention_prefill_inputs(BH, G, Sq, Skv, D, seed=Sq + Skv)
+    o = _run_prefill(inp, eps, causal)
+    ref = oracle.qknorm_attention_prefill(inp.Q, inp.K, inp.V, inp.gq, inp.gk,
+                                          oracle.eps_as_passed(eps), causal=causal)
+    _check(o.reshape(-1, D), ref.reshape(-1, D), f"prefill {case}")
+
+
+def test_attention_prefill_long_sampled(require_gpu):
+    # 8 key/value heads x 4 queries each, 2048 positions, causal: two query
+    # heads checked in full (every position against all its visible keys)
+    BH, G, S, D = 8, 4, 2048, 128
+    _log("prefill 8 x 4 heads x 2048, sampled heads")
+    inp = synth.make_attention_prefill_inputs(BH, G, S, S, D)
+    o = _run_prefill(inp, 1e-6, True)
+    for qh in (0, BH * G - 1):
+        ref = oracle.qknorm_attention_prefill(inp.Q[qh:qh + 1], inp.K[qh // G:qh // G + 1],
+                                              inp.V[qh // G:qh // G + 1], inp.gq, inp.gk,
+                                              oracle.eps_as_passed(1e-6), causal=True)
+        _check(o[qh], ref[0], f"prefill head {qh}")

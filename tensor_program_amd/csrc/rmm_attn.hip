@@ -535,10 +535,15 @@ __global__ __launch_bounds__(AQ_THREADS) void gqa_mfma_kernel(
         pl[2 * h + i / 2] = pack_bf16x2(p[h][i] - bf16_lo(hi), p[h][i + 1] - bf16_hi(hi));
       }
     const at_lds_char* vl = (const at_lds_char*)vt;
+    // Rescale O only when some query's maximum moved.
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+      for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[ob][i] *= ar[i];
+    }
 #pragma unroll
     for (int ob = 0; ob < NOB; ++ob) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[ob][i] *= ar[i];
       const int col = 16 * ob + 4 * (lq & 3), row = 4 * lg + (lq >> 2);
       const u32x2 v0 = __builtin_bit_cast(
           u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((at_lds_i16x4*)(vl + aq_v_off<D>(row, col))));
@@ -711,6 +716,7 @@ __global__ __launch_bounds__(AP_THREADS) void attn_prefill_kernel(
   constexpr int NL = 32 * CPR / AP_THREADS;  // K (and V) tile chunks per thread
   __shared__ __attribute__((aligned(16))) char k_s[2][32 * 2 * D];
   __shared__ __attribute__((aligned(16))) char v_s[2][32 * 2 * D];
+  __shared__ __attribute__((aligned(16))) float rk_s[2][32];  // the tile's keys' 1/RMS
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lq = l & 15, lg = l >> 4;
   const int64_t total = (int64_t)gridDim.x;
@@ -777,12 +783,26 @@ __global__ __launch_bounds__(AP_THREADS) void attn_prefill_kernel(
       vv[j] = __builtin_amdgcn_raw_buffer_load_b128(vr, o, 0, 0);
     }
   };
+  // Stores a tile into a stage; with the norm, the CPR threads holding a key
+  // row (adjacent lanes) also add its squares and one of them stores the
+  // key's 1/RMS (v_rsq_f32; 1/D is a power of two).
   auto store = [&](int stage, const u32x4 (&kk)[NL], const u32x4 (&vv)[NL]) {
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
       const int e = tid + AP_THREADS * j, key = e / CPR, c = e % CPR;
       *(u32x4*)(k_s[stage] + ap_k_off<D>(key, c)) = kk[j];
       *(u32x4*)(v_s[stage] + aq_v_off<D>(key, 8 * c)) = vv[j];
+      if (NORM) {
+        float ss = 0.f;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const float a0 = bf16_lo(kk[j][d]), a1 = bf16_hi(kk[j][d]);
+          ss += a0 * a0 + a1 * a1;
+        }
+#pragma unroll
+        for (int x = 1; x < CPR; x <<= 1) ss += __shfl_xor(ss, x);
+        if (c == 0) rk_s[stage][key] = __builtin_amdgcn_rsqf(ss * (1.0f / D) + eps);
+      }
     }
   };
 
@@ -799,7 +819,6 @@ __global__ __launch_bounds__(AP_THREADS) void attn_prefill_kernel(
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       sc[hh] = floatx4{0.f, 0.f, 0.f, 0.f};
-      float ss = 0.f;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         const u32x4 kf = *(const u32x4*)(ks + ap_k_off<D>(16 * hh + lq, 4 * db + lg));
@@ -809,24 +828,12 @@ __global__ __launch_bounds__(AP_THREADS) void attn_prefill_kernel(
         sc[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf),
                                                          __builtin_bit_cast(bf16x8, ul[db]),
                                                          sc[hh], 0, 0, 0);
-        if (NORM) {
-#pragma unroll
-          for (int d = 0; d < 4; ++d) {
-            const float a0 = bf16_lo(kf[d]), a1 = bf16_hi(kf[d]);
-            ss += a0 * a0 + a1 * a1;
-          }
-        }
       }
-      if (NORM) {
-        ss += __shfl_xor(ss, 16);
-        ss += __shfl_xor(ss, 32);
-        const float r = __builtin_amdgcn_rsqf(ss * (1.0f / D) + eps);
+      // this lane's score rows are keys 16 hh + 4 lg + i
+      const floatx4 r4 = NORM ? *(const floatx4*)(&rk_s[stage][16 * hh + 4 * lg])
+                              : floatx4{1.f, 1.f, 1.f, 1.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) rk[hh][i] = __shfl(r, 4 * lg + i);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) rk[hh][i] = 1.0f;
-      }
+      for (int i = 0; i < 4; ++i) rk[hh][i] = r4[i];
     }
     // Visible keys of query column lq: below kend and, causal, within its horizon.
     const int64_t horizon = CAUSAL ? p0 + lq + off : kend - 1;
@@ -868,10 +875,16 @@ __global__ __launch_bounds__(AP_THREADS) void attn_prefill_kernel(
         pl[2 * hh + i / 2] = pack_bf16x2(p[hh][i] - bf16_lo(hi), p[hh][i + 1] - bf16_hi(hi));
       }
     const at_lds_char* vl = (const at_lds_char*)v_s[stage];
+    // Rescale O only when some query's maximum moved (once the running
+    // maxima settle, most tiles skip it).
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+      for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[ob][i] *= ar[i];
+    }
 #pragma unroll
     for (int ob = 0; ob < NOB; ++ob) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[ob][i] *= ar[i];
       const int col = 16 * ob + 4 * (lq & 3), row = 4 * lg + (lq >> 2);
       const u32x2 v0 = __builtin_bit_cast(
           u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((at_lds_i16x4*)(vl + aq_v_off<D>(row, col))));

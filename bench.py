@@ -307,6 +307,109 @@ def bench_chain(args, name):
     print(json.dumps(out), flush=True)
 
 
+def bench_attn_prefill(args, name):
+    """QKNorm + attention for many queries per head on `attn_prefill_bh{BH}_g{G}_s{S}_d{D}`:
+    BH key/value heads, G query heads each, S positions (Sq = Skv = S), causal.
+    `value` is algorithmic TFLOP/s: 4 D flops (q.k and p.v) per visible
+    (query, key) pair; rotating input sets replayed from a HIP graph."""
+    import re
+    import numpy as np
+    import torch
+
+    import oracle
+    import synth
+    import tensor_program_amd as tpa
+
+    m = re.fullmatch(r"attn_prefill_bh(\d+)_g(\d+)_s(\d+)_d(\d+)", name)
+    if not m:
+        raise SystemExit(f"unknown workload {name}")
+    BH, G, S, D = (int(v) for v in m.groups())
+    eps = 1e-6
+    dev = torch.device("cuda", 0)
+    log(f"workload {name}: generating inputs")
+    inp = synth.make_attention_prefill_inputs(BH, G, S, S, D)
+
+    def d(nm):
+        return torch.from_numpy(np.ascontiguousarray(inp.device_array(nm)).view(np.int16)).to(
+            dev).view(torch.bfloat16)
+
+    base = {nm: d(nm) for nm in ("Q", "K", "V", "gq", "gk")}
+    per_set = (2 * BH * G * S * D + 2 * BH * S * D + 2 * D) * 2
+    pairs = BH * G * S * (S + 1) // 2
+    flops = 4 * D * pairs
+    R = max(1, min(8, math.ceil(ROTATE_BYTES / per_set)))
+    sets = []
+    for r in range(R):
+        st = {nm: (t if r == 0 else t.clone()) for nm, t in base.items()}
+        st["O"] = torch.empty_like(st["Q"])
+        sets.append(st)
+    stream = torch.cuda.Stream(dev)
+
+    def call(st):
+        tpa.qknorm_attention_prefill(st["Q"], st["K"], st["V"], st["gq"], st["gk"], eps,
+                                     causal=True, out=st["O"])
+    with torch.cuda.stream(stream):
+        for st in sets:
+            call(st)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for st in sets:
+                call(st)
+        torch.cuda.synchronize()
+        t0 = time.time()
+        while time.time() - t0 < args.settle_ms / 1e3:
+            graph.replay()
+
+        def run(n):  # exactly n calls: whole rotations from the graph, the rest eager
+            for _ in range(n // R):
+                graph.replay()
+            for i in range(n % R):
+                call(sets[i])
+        n_warm, n_steps = max(0, args.warmup), max(1, args.steps)
+        run(n_warm)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        stream.synchronize()
+        e0.record(stream)
+        run(n_steps)
+        e1.record(stream)
+        e1.synchronize()
+    ms = e0.elapsed_time(e1) / n_steps
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"{ms * 1e3:.1f} us per call, {tflops:.1f} TFLOP/s")
+    cpu = None
+    if not args.no_cpu_baseline:
+        # the oracle on the first query heads, as many as fit the budget
+        # (heads are independent), extrapolated to all of them
+        t0 = time.time()
+        n = 0
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        while n < BH * G and time.time() - t0 < args.cpu_budget:
+            k = min(threads, BH * G - n)
+            hs = np.arange(n, n + k)
+            oracle.qknorm_attention_prefill(inp.Q[hs], np.stack([inp.K[h // G] for h in hs]),
+                                            np.stack([inp.V[h // G] for h in hs]), inp.gq,
+                                            inp.gk, oracle.eps_as_passed(eps), causal=True)
+            n += k
+        sec = (time.time() - t0) * (BH * G) / n
+        cpu = {"value": flops / sec / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+               "sample": f"first {n} of {BH * G} query heads (fp64), extrapolated "
+                         f"x{BH * G / n:.1f}"} | host_cpu()
+    out = {"metric": METRIC, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": n_steps,
+           "warmup": n_warm, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": name, "BH": BH, "G": G, "Sq": S, "Skv": S, "D": D,
+                      "causal": True, "eps": eps, "rotating_input_sets": R, "hip_graph": True},
+           "roofline": {"bound": "mfma", "achieved": tflops, "peak": BF16_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": tflops / BF16_PEAK_TFLOPS, "traffic": None,
+                        "kernel": "attn_prefill_kernel", "algorithmic_flops_per_launch": flops,
+                        "note": "both products carry two bf16 parts: the matrix cores run "
+                                "twice the algorithmic flops"},
+           "cpu_baseline": cpu}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -355,6 +458,8 @@ def main():
         return
     if args.workload.startswith("chain_"):
         return bench_chain(args, args.workload)
+    if args.workload.startswith("attn_prefill_"):
+        return bench_attn_prefill(args, args.workload)
     wl = synth.get_workload(args.workload)
     attn = isinstance(wl, synth.AttnWorkload)
     dev = torch.device("cuda", 0)

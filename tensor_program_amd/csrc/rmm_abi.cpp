@@ -66,11 +66,15 @@ constexpr int64_t kGatedStreamMaxM = 128;
 // to two 16-wide rank blocks, every other shape runs the generic kernel.
 constexpr int64_t kLoraDecodeMaxRank = 32;
 
-// fp32 decode: about one workgroup per CU over 32-column tiles, each K range
-// at least 64 rows.
-int auto_decode32_splits(int64_t N, int64_t K) {
-  const int64_t tiles = (N + 31) / 32;
-  int64_t s = kTargetWorkgroups / (tiles > 0 ? tiles : 1);
+// fp32 decode: 128-column tiles, each K range at least 64 rows, about as
+// many workgroups as fit at once (two per CU with 8-row blocks, one with
+// 16: the accumulators of 16 rows leave room for one per SIMD).  Measured:
+// 8 x 14336 x 4096 57 us with 4 ranges (448 workgroups) against 86 us with
+// 2; 16 x 4096 x 4096 36 us with 8 ranges against 48 us with 16.
+int auto_decode32_splits(int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = (N + 127) / 128;
+  const int64_t target = M <= 8 ? 2 * kTargetWorkgroups : kTargetWorkgroups;
+  int64_t s = target / (tiles > 0 ? tiles : 1);
   const int64_t smax = (K + 63) / 64;
   if (s > smax) s = smax;
   return (int)(s < 1 ? 1 : s);
@@ -109,7 +113,7 @@ rmm_status plan_shape(int64_t M, int64_t N, int64_t K, rmm_dtype dtype, int gate
   const bool lora_ok = R == 0 || (R <= kLoraDecodeMaxRank && kLoraDecodeMaxRank * K * 2 <= (int64_t)INT32_MAX &&
                                   R * N * 2 <= (int64_t)INT32_MAX);
   const bool f32 = dtype == RMM_DTYPE_F32;
-  const bool decode32_ok = f32 && aligned && !gated && R == 0 && M <= kDecodeMaxMF32;
+  const bool decode32_ok = f32 && aligned && N % 4 == 0 && !gated && R == 0 && M <= kDecodeMaxMF32;
   const bool decode_ok = (fast_layout && lora_ok &&
                           M <= (gated ? kDecodeMaxMGated : (R > 0 ? kDecodeMaxMLora : kDecodeMaxM))) ||
                          decode32_ok;
@@ -150,7 +154,8 @@ rmm_status plan_shape(int64_t M, int64_t N, int64_t K, rmm_dtype dtype, int gate
   out->ws_bytes = 0;
   if (v == RMM_VARIANT_DECODE && f32) {
     int s = splits;
-    if (s == 0) s = have_ws ? auto_decode32_splits(N, K) : 1;
+    const int64_t rows = M < kDecodeRowsF32 ? M : kDecodeRowsF32;  // rows per launch
+    if (s == 0) s = have_ws ? auto_decode32_splits(rows, N, K) : 1;
     if (s > (K + 63) / 64 && s > 1) return RMM_ERR_VARIANT;
     if (s > 1 && !have_ws) return RMM_ERR_WORKSPACE;  // a forced split count needs one
     rmm_decode32_plan(M, N, K, s, &out->d32);

@@ -121,14 +121,14 @@ void rmm_decode_plan(int64_t M, int64_t N, int64_t K, int gated, int splits, int
                      DecodePlan* p);
 hipError_t rmm_launch_decode(const RmmArgs& a, const DecodePlan& p, void* ws);
 
-// fp32 decode (M <= 16, not gated, no adapter): 32-column tiles, K split
-// into `splits` ranges of `krange` rows walked in chunks of `kc` rows.
+// fp32 decode (M <= 16, not gated, no adapter): 128-column tiles, K split
+// into `splits` ranges of `krange` rows walked in chunks of `kc` (64) rows.
 struct Decode32Plan {
   int mr;          // rows computed per workgroup (8 or 16)
   int splits;      // K ranges combined across workgroups
-  int64_t kc;      // k rows per chunk (64, 128 or 256)
+  int64_t kc;      // k rows per chunk (64)
   int64_t krange;  // K per range (multiple of kc)
-  int64_t tiles;   // 32-column tiles
+  int64_t tiles;   // 128-column tiles
   size_t ws_cnt_off, ws_ssq_off, ws_part_off, ws_bytes;
 };
 void rmm_decode32_plan(int64_t M, int64_t N, int64_t K, int splits, Decode32Plan* p);

@@ -284,7 +284,7 @@ def test_variant_selection():
     assert tpa.plan(129, 4104, 4096, variant="stream")[0] == VARIANT
     assert tpa.plan(257, 4096, 4096, variant="stream")[0] == VARIANT
     f32 = torch.float32
-    assert tpa.plan(8, 1024, 1024, dtype=f32)[1:] == ("decode", 8)   # 32 tiles x 8 = 256
+    assert tpa.plan(8, 1024, 1024, dtype=f32)[1:] == ("decode", 16)  # 8 tiles x 16 ranges of 64
     assert tpa.plan(8, 1024, 1024, dtype=f32, with_workspace=False)[1:] == ("decode", 1)
     assert tpa.plan(16, 64, 100, dtype=f32)[1:] == ("decode", 2)     # K ranges of >= 64 rows
     assert tpa.plan(32, 1024, 1024, dtype=f32)[1] == "decode"    # two 16-row launches
@@ -337,7 +337,9 @@ def test_workspace_sizes(lib):
     assert lib.rmm_workspace_bytes_ex(BF16, 16, 6144, 4096, 0, 2, 1) == 0
     # fp32 decode at 8 x 1024 x 1024: 32 tiles x 8 splits; the counter region,
     # 8-row sums of squares, 8 x 32 fp32 partials per tile and split
-    assert lib.rmm_workspace_bytes(F32, 8, 1024, 1024, 0) == CNT + 8 * 32 * 8 * 4 + 8 * 32 * 8 * 32 * 4
+    # 16 K ranges x 8 tiles of 128 columns x 8 rows: sums of squares, then partials
+    assert lib.rmm_workspace_bytes(F32, 8, 1024, 1024, 0) == \
+        CNT + 16 * 8 * 8 * 4 + 16 * 8 * 8 * 128 * 4
     assert lib.rmm_workspace_bytes(F32, 8, 1024, 1024, 1) == 0   # gated fp32: generic kernel
     assert lib.rmm_workspace_bytes(BF16, 16, 6144, 0, 0) == 0  # invalid -> 0
 

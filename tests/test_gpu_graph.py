@@ -55,7 +55,7 @@ def test_graph_decode_f32_split_k(require_gpu):
     wl = synth.get_workload("f32_m8_k1024_n1024")
     inp = synth.make_inputs(wl)
     x, g, w = to_device(inp, "X"), to_device(inp, "g"), to_device(inp, "W1")
-    assert tpa.plan(wl.M, wl.N, wl.K, dtype=torch.float32)[1:] == ("decode", 8)
+    assert tpa.plan(wl.M, wl.N, wl.K, dtype=torch.float32)[1:] == ("decode", 16)
     out = torch.empty((wl.M, wl.N), dtype=torch.float32, device="cuda")
     ws = tpa.Workspace(tpa._binding.workspace_bytes(tpa._binding.DTYPE_F32, wl.M, wl.N, wl.K,
                                                     False), "cuda")

@@ -402,7 +402,8 @@ def bench_attn_prefill(args, name):
            "config": {"workload": name, "BH": BH, "G": G, "Sq": S, "Skv": S, "D": D,
                       "causal": True, "eps": eps, "rotating_input_sets": R, "hip_graph": True},
            "roofline": {"bound": "mfma", "achieved": tflops, "peak": BF16_PEAK_TFLOPS,
-                        "unit": "TFLOP/s", "frac": tflops / BF16_PEAK_TFLOPS, "traffic": None,
+                        "unit": "TFLOP/s", "frac": tflops / BF16_PEAK_TFLOPS,
+                        "traffic": stored_traffic(name, "attention"),
                         "kernel": "attn_prefill_kernel", "algorithmic_flops_per_launch": flops,
                         "note": "both products carry two bf16 parts: the matrix cores run "
                                 "twice the algorithmic flops"},
@@ -690,7 +691,8 @@ def main():
         if ach:
             roof["achievable_peak"] = ach
             roof["frac_of_achievable"] = roof["achieved"] / ach
-    roof["kernel"] = "qknorm_attention_kernel" if attn else f"{kvar}_kernel"
+    roof["kernel"] = (("gqa_mfma_kernel" if wl.G >= 3 else "qknorm_attention_kernel") if attn
+                      else f"{kvar}_kernel")
     roof["algorithmic_bytes_per_launch"] = per_set
     roof["algorithmic_flops_per_launch"] = wl.flops()
 

@@ -114,12 +114,14 @@ typedef enum {
  *             multiply-adds (no bf16 rounding).  Bandwidth-bound.
  *   PREFILL : LDS-tiled MFMA GEMM with the row sum of squares fused into
  *             its k-loop (gated: both products in one tile).  Matrix-core-
- *             bound shapes.  Plain calls with few output tiles (at most 128
- *             tiles of 256 x 256) and a workspace split K into ranges of
- *             whole 64-deep steps: each workgroup writes its range's fp32
- *             sums and row sums of squares to the workspace, and a second
- *             kernel adds the ranges in order and applies 1/RMS.  AUTO
- *             takes this form above 64 rows when a workspace is passed, with
+ *             bound shapes.  Calls with few output tiles (at most 128 tiles:
+ *             256 x 256 plain, 128 rows x 128 columns of each weight gated)
+ *             and a workspace split K into ranges of whole 64-deep steps:
+ *             each workgroup writes its range's fp32 sums (both products'
+ *             when gated) and row sums of squares to the workspace, and a
+ *             second kernel adds the ranges in order, applies 1/RMS (and the
+ *             gate).  AUTO takes this form for plain calls above 64 rows and
+ *             for gated ones above 128 rows when a workspace is passed, with
  *             a count whose partial sums fit in that workspace.
  *   STREAM  : gated: any M; plain: M <= 128, or M <= 256 with N <= 4096
  *             (above 64 rows: one launch per 64-row block); each
@@ -167,12 +169,12 @@ rmm_status rmsnorm_gated_mlp(const void* X, const void* g, const void* W1, const
                              rmm_dtype dtype, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* As above with a forced variant.  splits: number of K chunks the DECODE
- * variant, or the plain PREFILL variant, combines across workgroups (0 =
- * chosen by the library, 1 = no cross-workgroup combine, so no workspace is
- * needed; PREFILL rounds a forced count to whole, even ranges of 64-deep
- * steps, so the count that runs, reported by rmm_plan, may be lower; above
- * ceil(K / 64) or with partial sums above 2 GiB: RMM_ERR_VARIANT); must be
- * 0 for the other variants and for gated PREFILL. */
+ * or PREFILL variant combines across workgroups (0 = chosen by the library,
+ * 1 = no cross-workgroup combine, so no workspace is needed; PREFILL rounds
+ * a forced count to whole, even ranges of 64-deep steps, so the count that
+ * runs, reported by rmm_plan, may be lower; above ceil(K / 64) or with
+ * partial sums above 2 GiB: RMM_ERR_VARIANT); must be 0 for the other
+ * variants. */
 rmm_status rmsnorm_matmul_ex(const void* X, const void* g, const void* W, void* Y, float eps,
                              int64_t M, int64_t N, int64_t K, rmm_dtype dtype,
                              rmm_variant variant, int splits, void* ws, size_t ws_bytes,
@@ -229,8 +231,9 @@ rmm_status rmm_gated_matmul(const void* X, const void* W1, const void* W3, void*
  * partials), PREFILL (bf16, any M, R <= 64, a workspace required: a first
  * kernel writes T to it, then a tile of 128 rows x 256 columns carries X g
  * as two bf16 parts and adds T B, T likewise in two parts, as one more
- * k-step of the same accumulators; AUTO takes it above 128 rows when a
- * workspace is passed) and GENERIC (everything else); forcing STREAM
+ * k-step of the same accumulators; with at most 128 tiles the K split of
+ * the plain PREFILL variant, T B added by the last range; AUTO takes it
+ * above 128 rows when a workspace is passed) and GENERIC (everything else); forcing STREAM
  * returns RMM_ERR_VARIANT.  NULL checks cover A and B; Y must not overlap
  * them.
  * Workspace rules are those of rmsnorm_matmul, sized by

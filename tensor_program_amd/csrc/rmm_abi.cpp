@@ -98,7 +98,7 @@ rmm_status plan_shape(int64_t M, int64_t N, int64_t K, rmm_dtype dtype, int gate
                       int64_t R = 0, size_t ws_avail = SIZE_MAX) {
   if (variant < RMM_VARIANT_AUTO || variant > RMM_VARIANT_STREAM) return RMM_ERR_VARIANT;
   if (splits < 0) return RMM_ERR_VARIANT;
-  if (splits != 0 && variant != RMM_VARIANT_DECODE && !(variant == RMM_VARIANT_PREFILL && !gated))
+  if (splits != 0 && variant != RMM_VARIANT_DECODE && variant != RMM_VARIANT_PREFILL)
     return RMM_ERR_VARIANT;
   if (M == 0 || N == 0) {  // nothing to compute, nothing launched
     out->variant = variant == RMM_VARIANT_AUTO ? RMM_VARIANT_GENERIC : variant;
@@ -175,7 +175,7 @@ rmm_status plan_shape(int64_t M, int64_t N, int64_t K, rmm_dtype dtype, int gate
     out->splits = out->dec.splits;
     out->ws_bytes = out->dec.ws_bytes;
   } else if (v == RMM_VARIANT_PREFILL) {
-    if (splits > (K + 63) / 64 || (R > 0 && splits > 1)) return RMM_ERR_VARIANT;
+    if (splits > (K + 63) / 64) return RMM_ERR_VARIANT;
     // a forced split count, and the adapter's T, need one
     if ((splits > 1 || R > 0) && !have_ws) return RMM_ERR_WORKSPACE;
     rmm_prefill_plan(M, N, K, gated, splits, have_ws ? ws_avail : 0, &out->pre, R);

@@ -545,11 +545,13 @@ struct PgA {
   u32x4 g;
 };
 
+// Columns at or past klim (K, or the end of this workgroup's K range) read
+// as zeros.
 template <bool GL>
 __device__ __forceinline__ void pg_load_a(PgA& st, i32x4 xr, i32x4 gr, int64_t m0, int64_t k0,
-                                          int64_t M, int64_t K, int tid) {
+                                          int64_t M, int64_t K, int64_t klim, int tid) {
   const int64_t ka = k0 + 8 * (tid & 7);
-  const bool ka_ok = ka < K;
+  const bool ka_ok = ka < klim;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int64_t m = m0 + (tid >> 3) + 64 * i;
@@ -584,8 +586,9 @@ __device__ __forceinline__ void pg_dma_setup(PgDma& d, int64_t n0, int64_t N, in
 }
 
 __device__ __forceinline__ void pg_dma_b(uint32_t b_lds, const PgDma& d, const bf16_t* W1,
-                                         const bf16_t* W3, int64_t k0, int64_t N, int64_t K, int w) {
-  const int64_t rows = K - k0 > 0 ? K - k0 : 0;
+                                         const bf16_t* W3, int64_t k0, int64_t N, int64_t klim,
+                                         int w) {
+  const int64_t rows = klim - k0 > 0 ? klim - k0 : 0;
   const bf16_t* Wv = (w >> 2) ? W3 : W1;
   const i32x4 rsrc = pf_rsrc(Wv + k0 * N, (uint32_t)(rows * N * 2));
 #pragma unroll
@@ -710,7 +713,8 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_gated_kernel(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ g, const bf16_t* __restrict__ W1,
     const bf16_t* __restrict__ W3, bf16_t* __restrict__ Y, float eps, int64_t M, int64_t N,
     int64_t K, int tiles_m, int tiles_n, int group_m, int xcd_remap, int norm,
-    const float* __restrict__ T, int rp, const bf16_t* __restrict__ LB, int R) {
+    const float* __restrict__ T, int rp, const bf16_t* __restrict__ LB, int R, int splits,
+    int ksteps, float* __restrict__ part) {
   constexpr int XL = GL ? 2 : 3;  // X (and g) loads per thread per k-step
   __shared__ __attribute__((aligned(16))) char ah_s0[PG_A_BYTES];
   __shared__ __attribute__((aligned(16))) char ah_s1[PG_A_BYTES];
@@ -723,8 +727,11 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_gated_kernel(
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int ntiles = tiles_m * tiles_n;
+  // (K range, tile) pairs, K range major, as in prefill_kernel.
   int t = blockIdx.x;
-  if (xcd_remap) t = (t & 7) * (ntiles >> 3) + (t >> 3);
+  if (xcd_remap) t = (t & 7) * ((ntiles * splits) >> 3) + (t >> 3);
+  const int split = t / ntiles;
+  t -= split * ntiles;
   const int group = group_m * tiles_n;
   const int gid = t / group, first_m = gid * group_m;
   const int gm = (tiles_m - first_m < group_m) ? (tiles_m - first_m) : group_m;
@@ -757,7 +764,12 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_gated_kernel(
   const int bk = 8 * (bG >> 1) + (bi >> 2);
   const int bn = wh * 64 + 16 * (bG & 1) + 4 * (bi & 3);
   const int bo0 = wv * PG_W_BYTES + pg_b_off(bk, bn), bo1 = wv * PG_W_BYTES + pg_b_off(bk, bn + 32);
+  // This workgroup's k-steps kt0 .. kt1 - 1, as in prefill_kernel.
   const int nk = (int)((K + PF_BK - 1) / PF_BK);
+  const int kt0 = split * ksteps;
+  const int kt1 = kt0 + ksteps < nk ? kt0 + ksteps : nk;
+  const int64_t klim = (int64_t)kt1 * PF_BK < K ? (int64_t)kt1 * PF_BK : K;
+  const int64_t kb0 = (int64_t)kt0 * PF_BK;
 
   if (GL) {
     for (int c = tid; c < (PF_G_LDS_MAX + 2 * PF_BK) / 8; c += PF_THREADS)
@@ -769,13 +781,13 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_gated_kernel(
   // iteration kt, W of step kt+1 streams into the other stage, X of step
   // kt+1 is formed into the other A stages, X of step kt+2 is in flight.
   PgA sa, sb;
-  pg_dma_b(b0a, dma, W1, W3, 0, N, K, w);
-  pg_load_a<GL>(sa, xr, gr, m0, 0, M, K, tid);
-  pg_load_a<GL>(sb, xr, gr, m0, PF_BK, M, K, tid);
+  pg_dma_b(b0a, dma, W1, W3, kb0, N, klim, w);
+  pg_load_a<GL>(sa, xr, gr, m0, kb0, M, K, klim, tid);
+  pg_load_a<GL>(sb, xr, gr, m0, kb0 + PF_BK, M, K, klim, tid);
   pg_wait_a<XL, GL>(sa);
   {
     float g_f[8];
-    const u32x4 gsrc = GL ? *(const u32x4*)(g_s + 16 * (tid & 7)) : sa.g;
+    const u32x4 gsrc = GL ? *(const u32x4*)(g_s + 2 * kb0 + 16 * (tid & 7)) : sa.g;
     pg_gain<GL>(g_f, gsrc, norm);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -790,18 +802,18 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_gated_kernel(
   PF_WAIT_VMCNT(0);
   __syncthreads();
 
-  for (int kt = 0; kt < nk; kt += 2) {
+  for (int kt = kt0; kt < kt1; kt += 2) {
     pg_step<XL + 4, GL>(ah_s0, al_s0, b0s, ah_s1, al_s1, sb, acc, ss, a_base, bo0, bo1, tid, norm, g_s,
                         (int64_t)(kt + 1) * PF_BK, [&] {
-                          pg_dma_b(b1a, dma, W1, W3, (int64_t)(kt + 1) * PF_BK, N, K, w);
-                          pg_load_a<GL>(sa, xr, gr, m0, (int64_t)(kt + 2) * PF_BK, M, K, tid);
+                          pg_dma_b(b1a, dma, W1, W3, (int64_t)(kt + 1) * PF_BK, N, klim, w);
+                          pg_load_a<GL>(sa, xr, gr, m0, (int64_t)(kt + 2) * PF_BK, M, K, klim, tid);
                         });
     PF_WAIT_VMCNT(XL);
     __syncthreads();
     pg_step<XL + 4, GL>(ah_s1, al_s1, b1s, ah_s0, al_s0, sa, acc, ss, a_base, bo0, bo1, tid, norm, g_s,
                         (int64_t)(kt + 2) * PF_BK, [&] {
-                          pg_dma_b(b0a, dma, W1, W3, (int64_t)(kt + 2) * PF_BK, N, K, w);
-                          pg_load_a<GL>(sb, xr, gr, m0, (int64_t)(kt + 3) * PF_BK, M, K, tid);
+                          pg_dma_b(b0a, dma, W1, W3, (int64_t)(kt + 2) * PF_BK, N, klim, w);
+                          pg_load_a<GL>(sb, xr, gr, m0, (int64_t)(kt + 3) * PF_BK, M, K, klim, tid);
                         });
     PF_WAIT_VMCNT(XL);
     __syncthreads();
@@ -813,20 +825,51 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_gated_kernel(
   PF_WAIT_VMCNT(0);
 
   // Row sums of squares: the 8 lanes tid&7 share rows (tid>>3) and +64.
+  // A K range of a split call stores them raw ([split][M], from the first
+  // tile-column) and applies no scale; the combine kernel does.
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     float v = ss[i];
     v += __shfl_xor(v, 1);
     v += __shfl_xor(v, 2);
     v += __shfl_xor(v, 4);
-    if ((tid & 7) == 0) inv_s[(tid >> 3) + 64 * i] = norm ? inv_rms(v, K, eps) : 1.0f;
+    const int row = (tid >> 3) + 64 * i;
+    if (splits > 1) {
+      float* ssp = part + (int64_t)splits * (LORA ? 1 : 2) * M * N;
+      if (tn == 0 && (tid & 7) == 0 && m0 + row < M) ssp[(int64_t)split * M + m0 + row] = v;
+      if ((tid & 7) == 0) inv_s[row] = 1.0f;
+    } else if ((tid & 7) == 0) {
+      inv_s[row] = norm ? inv_rms(v, K, eps) : 1.0f;
+    }
   }
   __syncthreads();
+  // A split call's gated tile stores both products' raw sums,
+  // [split][weight][M][N]; the adapter's go on below (its last range adds
+  // T B first).
+  if (!LORA && splits > 1) {
+    float* pp = part + ((int64_t)split * 2 + wv) * M * N;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int64_t n = n0 + wh * 64 + 32 * j + (l & 31);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int64_t m = m0 + wm * 64 + 32 * i + 8 * jj + 4 * (l >> 5) + rr;
+            if (m < M && n < N) pp[m * N + n] = acc[i][j][4 * jj + rr];
+          }
+      }
+    return;
+  }
 
   if (LORA) {
-    // The adapter step: T rows m0 .. m0 + 127 (rp columns, zero past R) as
-    // hi and lo A stages, B rows 0 .. R - 1 of the tile's columns in a W
-    // stage (rows past R read as zeros), then one k-step of MFMAs.
+    // The adapter step (in a split call, by the last K range only): T rows
+    // m0 .. m0 + 127 (rp columns, zero past R) as hi and lo A stages, B rows
+    // 0 .. R - 1 of the tile's columns in a W stage (rows past R read as
+    // zeros), then one k-step of MFMAs.
+    if (split == splits - 1) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int row = (tid >> 3) + 64 * i, c = tid & 7;
@@ -853,7 +896,10 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_gated_kernel(
     auto no_issue = [] {};
     pg_step<0, GL, decltype(no_issue), false>(ah_s0, al_s0, b0s, ah_s1, al_s1, sa, acc, ss, a_base,
                                               bo0, bo1, tid, norm, g_s, 0, no_issue);
-    // Y: each wave stores its own 64 x 64 block.
+    }
+    // Y (or, in a split call, the range's raw sums [split][M][N]): each wave
+    // stores its own 64 x 64 block.
+    float* pp = splits > 1 ? part + (int64_t)split * M * N : nullptr;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -865,7 +911,12 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_gated_kernel(
           for (int rr = 0; rr < 4; ++rr) {
             const int lr = wm * 64 + 32 * i + 8 * jj + 4 * (l >> 5) + rr;
             const int64_t m = m0 + lr;
-            if (m < M && n < N) Y[m * N + n] = f32_to_bf16(acc[i][j][4 * jj + rr] * inv_s[lr]);
+            if (m < M && n < N) {
+              if (splits > 1)
+                pp[m * N + n] = acc[i][j][4 * jj + rr];
+              else
+                Y[m * N + n] = f32_to_bf16(acc[i][j][4 * jj + rr] * inv_s[lr]);
+            }
           }
       }
     return;
@@ -1023,6 +1074,40 @@ __global__ __launch_bounds__(PC_THREADS) void prefill_combine_kernel(
   *(u32x4*)(Y + m * N + n) = o;
 }
 
+// The gated form: both products' ranges, [split][weight][M][N], then the
+// gate on the scaled sums (1/RMS before the SiLU).
+__global__ __launch_bounds__(PC_THREADS) void prefill_gated_combine_kernel(
+    const float* __restrict__ part, bf16_t* __restrict__ Y, float eps, int64_t M, int64_t N,
+    int64_t K, int splits, int norm) {
+  const int64_t n8 = N >> 3;
+  const int64_t idx = (int64_t)blockIdx.x * PC_THREADS + threadIdx.x;
+  if (idx >= M * n8) return;
+  const int64_t m = idx / n8, n = (idx - m * n8) * 8;
+  const float* ssp = part + (int64_t)splits * 2 * M * N;
+  float ss = 0.f, z[2][8];
+#pragma unroll
+  for (int v = 0; v < 2; ++v)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) z[v][c] = 0.f;
+  for (int s = 0; s < splits; ++s) {
+    ss += ssp[(int64_t)s * M + m];
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      const float4* p = (const float4*)(part + (((int64_t)s * 2 + v) * M + m) * N + n);
+      const float4 a = p[0], b = p[1];
+      z[v][0] += a.x; z[v][1] += a.y; z[v][2] += a.z; z[v][3] += a.w;
+      z[v][4] += b.x; z[v][5] += b.y; z[v][6] += b.z; z[v][7] += b.w;
+    }
+  }
+  const float inv = norm ? inv_rms(ss, K, eps) : 1.0f;
+  u32x4 o;
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+    o[d] = pack_bf16x2(silu_gate(z[0][2 * d] * inv, z[1][2 * d] * inv),
+                       silu_gate(z[0][2 * d + 1] * inv, z[1][2 * d + 1] * inv));
+  *(u32x4*)(Y + m * N + n) = o;
+}
+
 }  // namespace rmm
 
 // Split of K for the plain tile.  Without a forced count, with a workspace
@@ -1041,30 +1126,19 @@ SplitShape prefill_split_shape(int64_t nk, int64_t s) {
   q += q & 1;
   return {(nk + q - 1) / q, q};
 }
-size_t prefill_split_bytes(int64_t M, int64_t N, int64_t S) {
-  return kWsCounterBytes + (size_t)(S * (M * N + M)) * 4;
+// [split][product][M][N] sums, then [split][M] sums of squares
+size_t prefill_part_bytes(int64_t M, int64_t N, int64_t S, int64_t nsum) {
+  return (size_t)(S * (nsum * M * N + M)) * 4;
 }
 }  // namespace
 
 void rmm_prefill_plan(int64_t M, int64_t N, int64_t K, int gated, int splits, size_t ws_avail,
                       PrefillPlan* p, int64_t R) {
   using namespace rmm;
-  p->rb = 0;
-  p->ws_t_off = 0;
-  if (R > 0) {  // the two-part tile, 128 rows x 256 columns, and T in the workspace
-    p->tiles_m = (int)((M + PG_BM - 1) / PG_BM);
-    p->tiles_n = (int)((N + 2 * PG_BNW - 1) / (2 * PG_BNW));
-    p->group_m = 4;
-    p->splits = 1;
-    p->ksteps = (int)((K + PF_BK - 1) / PF_BK);
-    p->rb = (int)((R + 15) / 16);
-    p->ws_part_off = 0;
-    p->ws_t_off = kWsCounterBytes;
-    p->ws_bytes = kWsCounterBytes + (size_t)(M * 16 * p->rb) * 4;
-    p->xcd_remap = ((int64_t)p->tiles_m * p->tiles_n) % 8 == 0;
-    return;
-  }
-  const int bm = gated ? PG_BM : PF_BM, bn = gated ? PG_BNW : PF_BN;
+  // Tiles: plain 256 x 256; gated 128 rows x 128 columns of each weight;
+  // with the adapter 128 x 256 (the two-part tile over two column halves).
+  const bool two = gated || R > 0;
+  const int bm = two ? PG_BM : PF_BM, bn = (gated ? PG_BNW : PF_BN);
   p->tiles_m = (int)((M + bm - 1) / bm);
   p->tiles_n = (int)((N + bn - 1) / bn);
   p->group_m = 4;
@@ -1072,17 +1146,24 @@ void rmm_prefill_plan(int64_t M, int64_t N, int64_t K, int gated, int splits, si
   const int64_t tiles = (int64_t)p->tiles_m * p->tiles_n;
   p->splits = 1;
   p->ksteps = (int)nk;
-  p->ws_part_off = 0;
-  p->ws_bytes = 0;
+  p->rb = R > 0 ? (int)((R + 15) / 16) : 0;
+  // Workspace: the counter region, the adapter's T (M x 16 rb fp32), then
+  // the partial sums of a split call.
+  p->ws_t_off = kWsCounterBytes;
+  const size_t t_bytes = R > 0 ? (size_t)(M * 16 * p->rb) * 4 : 0;
+  p->ws_part_off = kWsCounterBytes + ((t_bytes + 255) & ~(size_t)255);
+  const size_t fixed = R > 0 ? p->ws_part_off : 0;
+  const int64_t nsum = gated ? 2 : 1;  // products summed per output
+  p->ws_bytes = fixed;
   SplitShape best{1, nk};
-  if (!gated && splits > 1) {
+  if (splits > 1) {
     best = prefill_split_shape(nk, splits);
-  } else if (!gated && splits == 0 && ws_avail > 0 && 2 * tiles <= 256 && nk >= 4) {
+  } else if (splits == 0 && ws_avail > fixed && 2 * tiles <= 256 && nk >= 4) {
     double best_us = 1.5 * nk;
     for (int64_t s = 2; s * tiles <= 256 && s <= nk / 2; ++s) {
       const SplitShape c = prefill_split_shape(nk, s);
-      if (prefill_split_bytes(M, N, c.splits) > ws_avail) break;
-      const double us = 1.5 * c.ksteps + 0.4e-6 * (double)(c.splits * M * N * 4);
+      if (p->ws_part_off + prefill_part_bytes(M, N, c.splits, nsum) > ws_avail) break;
+      const double us = 1.5 * c.ksteps + 0.4e-6 * (double)(c.splits * nsum * M * N * 4);
       if (us < best_us) {
         best_us = us;
         best = c;
@@ -1092,8 +1173,7 @@ void rmm_prefill_plan(int64_t M, int64_t N, int64_t K, int gated, int splits, si
   if (best.splits > 1) {
     p->splits = (int)best.splits;
     p->ksteps = (int)best.ksteps;
-    p->ws_part_off = kWsCounterBytes;
-    p->ws_bytes = prefill_split_bytes(M, N, best.splits);
+    p->ws_bytes = p->ws_part_off + prefill_part_bytes(M, N, best.splits, nsum);
   }
   p->xcd_remap = (tiles * p->splits) % 8 == 0;
 }
@@ -1107,7 +1187,7 @@ hipError_t rmm_launch_prefill(const RmmArgs& a, const PrefillPlan& p, void* ws) 
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(PF_THREADS), 0, a.stream, (const bf16_t*)a.X,
                        (const bf16_t*)a.g, (const bf16_t*)a.W1, (const bf16_t*)a.W3, (bf16_t*)a.Y, a.eps,
                        a.M, a.N, a.K, p.tiles_m, p.tiles_n, p.group_m, p.xcd_remap, a.norm,
-                       (const float*)nullptr, 0, (const bf16_t*)nullptr, 0);
+                       (const float*)nullptr, 0, (const bf16_t*)nullptr, 0, p.splits, p.ksteps, part);
   };
   auto launch_plain = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(PF_THREADS), 0, a.stream, (const bf16_t*)a.X,
@@ -1134,23 +1214,26 @@ hipError_t rmm_launch_prefill(const RmmArgs& a, const PrefillPlan& p, void* ws) 
       hipLaunchKernelGGL(kernel, dim3(grid), dim3(PF_THREADS), 0, a.stream, (const bf16_t*)a.X,
                          (const bf16_t*)a.g, (const bf16_t*)a.W1, (const bf16_t*)a.W1, (bf16_t*)a.Y,
                          a.eps, a.M, a.N, a.K, p.tiles_m, p.tiles_n, p.group_m, p.xcd_remap, a.norm,
-                         (const float*)T, 16 * p.rb, (const bf16_t*)a.LB, (int)a.R);
+                         (const float*)T, 16 * p.rb, (const bf16_t*)a.LB, (int)a.R, p.splits,
+                         p.ksteps, part);
     };
     gl ? tile(prefill_gated_kernel<true, true>) : tile(prefill_gated_kernel<false, true>);
-    return hipGetLastError();
-  }
-  if (a.gated) {
+  } else if (a.gated) {
     gl ? launch(prefill_gated_kernel<true, false>) : launch(prefill_gated_kernel<false, false>);
-    return hipGetLastError();
+  } else {
+    gl ? launch_plain(prefill_kernel<false, true>) : launch_plain(prefill_kernel<false, false>);
   }
-  gl ? launch_plain(prefill_kernel<false, true>) : launch_plain(prefill_kernel<false, false>);
   if (p.splits > 1) {
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int64_t threads = a.M * (a.N >> 3);
-    hipLaunchKernelGGL(prefill_combine_kernel, dim3((unsigned)((threads + PC_THREADS - 1) / PC_THREADS)),
-                       dim3(PC_THREADS), 0, a.stream, (const float*)part, (bf16_t*)a.Y, a.eps, a.M,
-                       a.N, a.K, p.splits, a.norm);
+    const dim3 cgrid((unsigned)((threads + PC_THREADS - 1) / PC_THREADS));
+    if (a.gated && a.R == 0)
+      hipLaunchKernelGGL(prefill_gated_combine_kernel, cgrid, dim3(PC_THREADS), 0, a.stream,
+                         (const float*)part, (bf16_t*)a.Y, a.eps, a.M, a.N, a.K, p.splits, a.norm);
+    else
+      hipLaunchKernelGGL(prefill_combine_kernel, cgrid, dim3(PC_THREADS), 0, a.stream,
+                         (const float*)part, (bf16_t*)a.Y, a.eps, a.M, a.N, a.K, p.splits, a.norm);
   }
   return hipGetLastError();
 }

@@ -67,6 +67,12 @@ LORA_EXACT = [
     (16, 1024, 1032, 48, "bf16", "auto", 0),    # R > 32 at decode size: the prefill tile
     (200, 136, 16392, 1, "bf16", "prefill", 0),
     (129, 10248, 264, 16, "bf16", "prefill", 0),
+    # the prefill tile with K split into ranges (T B added by the last one)
+    (300, 1032, 520, 16, "bf16", "prefill", 4),
+    (256, 4096, 1024, 64, "bf16", "prefill", 8),
+    (129, 10248, 264, 16, "bf16", "prefill", 7),
+    (200, 136, 16392, 1, "bf16", "prefill", 2),
+    (130, 520, 264, 40, "bf16", "prefill", 3),
 ]
 
 
@@ -114,7 +120,7 @@ def test_lora_workload(variant, splits, require_gpu):
     _log(f"  worst err/tol {worst:.3f}")
 
 
-@pytest.mark.parametrize("M", [512, 1000])
+@pytest.mark.parametrize("M", [256, 512, 1000])
 def test_lora_prefill_workload_recipe(M, require_gpu):
     """The adapter workload's shape and value recipe with more rows (the
     prefill tile), on every output at the elementwise bound."""

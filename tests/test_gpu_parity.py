@@ -227,6 +227,21 @@ def test_prefill_split_shapes(M, K, N, splits, require_gpu):
     _log(f"  worst err/tol {worst:.3f}")
 
 
+@pytest.mark.parametrize("M,K,N,splits", [(256, 4096, 14336, 2), (512, 4096, 4096, 0),
+                                          (129, 14336, 4096, 0), (300, 1032, 2056, 7)])
+def test_gated_prefill_split_shapes(M, K, N, splits, require_gpu):
+    """The gated tile with K split into ranges, on the gated workload's value
+    recipe, at the elementwise bound on every output."""
+    wl = synth.Workload("gated_split", "bf16", M, K, N, 1e-6, True, None)
+    st, variant, s = tpa.plan(M, N, K, gated=True, variant="prefill", splits=splits)
+    assert st == 0 and s > 1, (st, variant, s)
+    _log(f"gated prefill split M={M} K={K} N={N} splits {splits} -> {s}")
+    inp = synth.make_inputs(wl, seed=19)
+    y = from_device(run_gpu(inp, wl.eps, variant="prefill", splits=splits))
+    worst = assert_within_tol(y, run_oracle(inp, wl.eps), tol_for("bf16"), "gated_split")
+    _log(f"  worst err/tol {worst:.3f}")
+
+
 def test_large_m8192_k8192_n28672_sampled(require_gpu):
     wl = synth.get_workload("large_m8192_k8192_n28672")
     _check_workload(wl.name, rows=_sample_rows(wl, n_random=24))
@@ -363,6 +378,7 @@ def test_one_workspace_for_every_layout(require_gpu):
     seq = [(16, 4096, 1024, "bf16", False, "decode", 4), (16, 1024, 9216, "bf16", False, "decode", 2),
            (33, 1000, 520, "bf16", False, "stream", 0), (8, 1024, 1024, "f32", False, "decode", 0),
            (16, 4096, 6144, "bf16", False, "decode", 8), (13, 1000, 520, "bf16", True, "decode", 3),
+           (200, 264, 1032, "bf16", True, "prefill", 3), (256, 1024, 1024, "bf16", False, "prefill", 4),
            (16, 4096, 1024, "bf16", False, "decode", 4)]
     for i, (M, K, N, dtype, gated, variant, splits) in enumerate(seq):
         _log(f"shared workspace call {i}: {M}x{K}x{N} {dtype} gated={gated} {variant} {splits}")
@@ -397,6 +413,14 @@ GATED_EXACT = [
     (13, 1000, 520, "generic", 0),
     (200, 264, 1032, "prefill", 0),   # gated tile: 2 x 9 tiles, ragged
     (256, 4096, 512, "prefill", 0),
+    # the gated tile with K split into ranges: a last range of one step, an
+    # odd count rounded down, K past the in-LDS gain, the library's count
+    (200, 264, 1032, "prefill", 3),
+    (256, 4096, 512, "prefill", 8),
+    (129, 1000, 520, "prefill", 5),
+    (136, 10248, 136, "prefill", 6),
+    (300, 1032, 264, "prefill", 0),
+    (256, 4096, 4096, "prefill", 0),
 ]
 
 

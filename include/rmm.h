@@ -99,9 +99,9 @@ typedef enum {
   RMM_ERR_SCRATCH = 9
 } rmm_status;
 
-/* Kernel variants.  AUTO picks by shape (gated M <= 16 takes DECODE only
- * when a workspace is passed, STREAM otherwise); the others force one
- * (tests, bench).
+/* Kernel variants.  AUTO picks by shape (gated: DECODE for M <= 16 when a
+ * workspace is passed, STREAM up to 64 rows with a workspace and up to 128
+ * without, PREFILL above); the others force one (tests, bench).
  * The fast variants need bf16, K % 8 == 0, N % 8 == 0, 16-byte aligned
  * pointers, and X and each weight below 2 GiB (except fp32 DECODE, below).
  *   GENERIC : any shape, alignment and dtype; VALU fp32 products.
@@ -120,9 +120,9 @@ typedef enum {
  *             each workgroup writes its range's fp32 sums (both products'
  *             when gated) and row sums of squares to the workspace, and a
  *             second kernel adds the ranges in order, applies 1/RMS (and the
- *             gate).  AUTO takes this form for plain calls above 64 rows and
- *             for gated ones above 128 rows when a workspace is passed, with
- *             a count whose partial sums fit in that workspace.
+ *             gate).  AUTO takes this form above 64 rows when a workspace
+ *             is passed, with a count whose partial sums fit in that
+ *             workspace.
  *   STREAM  : gated: any M; plain: M <= 128, or M <= 256 with N <= 4096
  *             (above 64 rows: one launch per 64-row block); each
  *             workgroup streams 64-column strips of W (W1 and W3 when
@@ -233,7 +233,7 @@ rmm_status rmm_gated_matmul(const void* X, const void* W1, const void* W3, void*
  * as two bf16 parts and adds T B, T likewise in two parts, as one more
  * k-step of the same accumulators; with at most 128 tiles the K split of
  * the plain PREFILL variant, T B added by the last range; AUTO takes it
- * above 128 rows when a workspace is passed) and GENERIC (everything else); forcing STREAM
+ * above 64 rows when a workspace is passed) and GENERIC (everything else); forcing STREAM
  * returns RMM_ERR_VARIANT.  NULL checks cover A and B; Y must not overlap
  * them.
  * Workspace rules are those of rmsnorm_matmul, sized by

@@ -59,9 +59,18 @@ constexpr int64_t kTargetWorkgroups = 256;
 // N = 2048 69.6 us, N = 4096 85.0 us, against 111-112 us).
 constexpr int64_t kStreamRows = 64;
 constexpr int64_t kStreamMaxM = 128;
-// Gated calls: 64-row stream launches up to this many rows, the gated
-// prefill tile above.
+// Gated calls: 64-row stream launches up to 64 rows with a workspace (to
+// 128 without one), the gated prefill tile above (with a workspace, its K
+// split).  Measured, 96 and 128 rows: K = 4096, N = 14336 70-75 us against
+// 98; N = 4096 34-39 against 55; K = 14336, N = 4096 69-75 against 121-127.
+// At 32-64 rows the two are within a few percent, the stream kernel ahead at
+// N = 14336 (55.5 against 68.5 us at 64 rows).
 constexpr int64_t kGatedStreamMaxM = 128;
+constexpr int64_t kGatedStreamMaxMWs = 64;
+// Adapter calls with a workspace: the decode kernel (32-row launches) up to
+// 64 rows, the prefill tile's K split above (6144 x 4096, R = 16: 96 rows
+// 46 against 64 us, 128 rows 47 against 85; 64 rows 44.5 against 43).
+constexpr int64_t kLoraDecodeMaxMWs = 64;
 // Low-rank adapter: ranks 1..RMM_LORA_MAX_RANK; the decode kernel carries up
 // to two 16-wide rank blocks, every other shape runs the generic kernel.
 constexpr int64_t kLoraDecodeMaxRank = 32;
@@ -128,15 +137,17 @@ rmm_status plan_shape(int64_t M, int64_t N, int64_t K, rmm_dtype dtype, int gate
   rmm_variant v = variant;
   if (v == RMM_VARIANT_AUTO) {
     if (R > 0)
-      v = decode_ok                 ? RMM_VARIANT_DECODE
-          : (prefill_ok && have_ws) ? RMM_VARIANT_PREFILL
-                                    : RMM_VARIANT_GENERIC;
+      v = (decode_ok && (M <= kLoraDecodeMaxMWs || !have_ws)) ? RMM_VARIANT_DECODE
+          : (prefill_ok && have_ws)                           ? RMM_VARIANT_PREFILL
+          : decode_ok                                         ? RMM_VARIANT_DECODE
+                                                              : RMM_VARIANT_GENERIC;
     else if (gated)  // decode (split-K over every CU) only with a workspace for its partials
-      v = (decode_ok && have_ws)                 ? RMM_VARIANT_DECODE
-          : (stream_ok && M <= kGatedStreamMaxM) ? RMM_VARIANT_STREAM
-          : prefill_ok                           ? RMM_VARIANT_PREFILL
-          : stream_ok                            ? RMM_VARIANT_STREAM
-                                                 : RMM_VARIANT_GENERIC;
+      v = (decode_ok && have_ws) ? RMM_VARIANT_DECODE
+          : (stream_ok && M <= (have_ws ? kGatedStreamMaxMWs : kGatedStreamMaxM))
+              ? RMM_VARIANT_STREAM
+          : prefill_ok ? RMM_VARIANT_PREFILL
+          : stream_ok  ? RMM_VARIANT_STREAM
+                       : RMM_VARIANT_GENERIC;
     else if (decode_ok)
       v = RMM_VARIANT_DECODE;
     else if (stream_ok && (M <= kStreamRows || !have_ws))

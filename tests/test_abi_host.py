@@ -172,8 +172,14 @@ def test_lora_plans():
     assert tpa.plan_lora(16, 6144, 4096, 64)[1] == "prefill"
     assert tpa.plan_lora(16, 6144, 4096, 64, with_workspace=False)[1] == "generic"
     assert tpa.plan_lora(33, 6144, 4096, 16)[1] == "decode"    # 32-row launches
-    assert tpa.plan_lora(128, 6144, 4096, 16)[1] == "decode"
-    assert tpa.plan_lora(129, 6144, 4096, 16)[1:] == ("prefill", 1)
+    assert tpa.plan_lora(64, 6144, 4096, 16)[1] == "decode"
+    # above 64 rows with a workspace the prefill tile with K split into
+    # ranges (128 x 6144 x 4096: 47 us against 85 us for four 32-row decode
+    # launches); without one, decode up to 128 rows
+    assert tpa.plan_lora(65, 6144, 4096, 16)[1] == "prefill"
+    assert tpa.plan_lora(128, 6144, 4096, 16, with_workspace=False)[1:] == ("decode", 1)
+    assert tpa.plan_lora(129, 6144, 4096, 16)[1:] == ("prefill", 5)
+    assert tpa.plan_lora(1000, 6144, 4096, 16)[1:] == ("prefill", 1)   # 192 tiles: no split
     assert tpa.plan_lora(4096, 4096, 4096, 16)[1] == "prefill"
     assert tpa.plan_lora(4096, 4096, 4096, 16, with_workspace=False)[1] == "generic"
     assert tpa.plan_lora(4096, 4100, 4096, 16)[1] == "generic"    # N % 8 != 0
@@ -183,7 +189,10 @@ def test_lora_plans():
     assert tpa.plan_lora(16, 6144, 4096, 16, variant="prefill")[1] == "prefill"
     assert tpa.plan_lora(16, 6144, 4096, 16, variant="prefill", with_workspace=False)[0] == \
         WORKSPACE
-    assert tpa.plan_lora(16, 6144, 4096, 16, variant="prefill", splits=2)[0] == VARIANT
+    assert tpa.plan_lora(16, 6144, 4096, 16, variant="prefill", splits=2)[1:] == ("prefill", 2)
+    assert tpa.plan_lora(16, 6144, 4096, 16, variant="prefill", splits=2,
+                         with_workspace=False)[0] == WORKSPACE
+    assert tpa.plan_lora(16, 6144, 4096, 16, variant="prefill", splits=65)[0] == VARIANT
     assert tpa.plan_lora(16, 6144, 4096, 65)[0] == SHAPE
 
 
@@ -195,8 +204,18 @@ def test_lora_workspace_sizes(lib):
     # 4 splits x 48 tiles x (8 + 1) blocks of 16 x 16 fp32 beyond the plain partials' 8
     assert lora16 - plain == 4 * 48 * 1 * 256 * 4
     # R = 48: the prefill tile (decode carries R <= 32): T, 16 rows x 48 ranks
-    assert lib.rmm_lora_workspace_bytes(BF16, 16, 6144, 4096, 48, 0, 0) == 65536 + 16 * 48 * 4
-    assert lib.rmm_lora_workspace_bytes(BF16, 16, 6144, 4096, 40, 0, 0) == 65536 + 16 * 48 * 4
+    # (3072 bytes, a multiple of 256), then the split's partial sums and row
+    # sums of squares, S x (16 x 6144 + 16) fp32
+    S = tpa.plan_lora(16, 6144, 4096, 48)[2]
+    assert S > 1
+    want = 65536 + 16 * 48 * 4 + S * (16 * 6144 + 16) * 4
+    assert lib.rmm_lora_workspace_bytes(BF16, 16, 6144, 4096, 48, 0, 0) == want
+    assert lib.rmm_lora_workspace_bytes(BF16, 16, 6144, 4096, 40, 0, 0) == want
+    # unsplit: T alone
+    assert lib.rmm_lora_workspace_bytes(BF16, 16, 6144, 4096, 48, 3, 1) == 65536 + 16 * 48 * 4
+    # T not a multiple of 256 bytes: the partial sums start at the next one
+    assert lib.rmm_lora_workspace_bytes(BF16, 3, 6144, 4096, 16, 3, 2) == \
+        65536 + 256 + 2 * (3 * 6144 + 3) * 4
     assert lib.rmm_lora_workspace_bytes(F32, 16, 6144, 4096, 48, 0, 0) == 0   # generic: none
     assert lib.rmm_lora_workspace_bytes(BF16, 16, 6144, 4096, 0, 0, 0) == 0   # invalid rank
     assert lib.rmm_lora_workspace_bytes(BF16, 16, 6144, 4096, 16, 2, 1) == 0
@@ -274,8 +293,14 @@ def test_variant_selection():
     assert tpa.plan(16, 14336, 4096, gated=True)[1] == "decode"
     assert tpa.plan(16, 14336, 4096, gated=True, with_workspace=False)[1] == "stream"
     assert tpa.plan(17, 14336, 4096, gated=True)[1] == "stream"
-    assert tpa.plan(128, 14336, 4096, gated=True)[1] == "stream"
-    assert tpa.plan(1024, 14336, 4096, gated=True)[1] == "prefill"  # gated: the 128-row tile above 128 rows
+    # gated above 64 rows with a workspace: the 128-row tile with K split into
+    # ranges (128 x 14336 x 4096: 75 us against 98 us for two 64-row stream
+    # launches); without one, stream launches up to 128 rows
+    assert tpa.plan(65, 14336, 4096, gated=True)[1:] == ("prefill", 2)
+    assert tpa.plan(128, 14336, 4096, gated=True, with_workspace=False)[1] == "stream"
+    assert tpa.plan(129, 14336, 4096, gated=True, with_workspace=False)[1:] == ("prefill", 1)
+    assert tpa.plan(256, 4096, 4096, gated=True)[1:] == ("prefill", 4)
+    assert tpa.plan(1024, 14336, 4096, gated=True)[1:] == ("prefill", 1)   # 896 tiles
     assert tpa.plan(129, 14336, 4100, gated=True)[1] == "generic"   # K % 8 != 0
     assert tpa.plan(48, 14336, 4096)[1] == "stream"
     # M <= 64 takes the stream kernel at any width (48 x 4096 x 4096: 21 us
@@ -315,14 +340,15 @@ def test_variant_selection():
     assert tpa.plan(300, 264, 1000, variant="prefill", splits=17)[0] == VARIANT
     assert tpa.plan(300, 264, 1000, variant="prefill", splits=2,
                     with_workspace=False)[0] == WORKSPACE
-    assert tpa.plan(300, 264, 1000, gated=True, variant="prefill", splits=2)[0] == VARIANT
+    assert tpa.plan(300, 264, 1000, gated=True, variant="prefill", splits=5)[1:] == ("prefill", 4)
+    assert tpa.plan(300, 264, 1000, gated=True, variant="prefill", splits=17)[0] == VARIANT
     assert tpa.plan(300, 264, 1000, variant="stream", splits=2)[0] == VARIANT
     assert tpa.plan(129, 4104, 1000)[1] == "prefill"
     assert tpa.plan(4096, 4096, 4095)[1] == "generic"   # K % 8 != 0
     assert tpa.plan(4096, 4096, 4096, variant="prefill", dtype=torch.float32)[0] == VARIANT
     assert tpa.plan(128, 256, 64, gated=True, variant="prefill")[1] == "prefill"
     assert tpa.plan(4096, 14336, 4096, gated=True)[1] == "prefill"
-    assert tpa.plan(128, 14336, 4096, gated=True)[1] == "stream"
+    assert tpa.plan(64, 14336, 4096, gated=True)[1] == "stream"
     assert tpa.plan(16, 6144, 4096, variant="decode", splits=3)[1:] == ("decode", 3)
     # split counts that do not divide K evenly are rounded to 128-deep chunks
     st, v, s = tpa.plan(17, 520, 1000, variant="decode", splits=4)

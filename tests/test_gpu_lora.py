@@ -73,6 +73,7 @@ LORA_EXACT = [
     (129, 10248, 264, 16, "bf16", "prefill", 7),
     (200, 136, 16392, 1, "bf16", "prefill", 2),
     (130, 520, 264, 40, "bf16", "prefill", 3),
+    (100, 1032, 1032, 16, "bf16", "auto", 0),   # above 64 rows with a workspace: the split tile
 ]
 
 

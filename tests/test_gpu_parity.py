@@ -421,6 +421,7 @@ GATED_EXACT = [
     (136, 10248, 136, "prefill", 6),
     (300, 1032, 264, "prefill", 0),
     (256, 4096, 4096, "prefill", 0),
+    (100, 1032, 520, "auto", 0),      # above 64 rows with a workspace: the split tile
 ]
 
 

@@ -261,7 +261,9 @@ def _run_prefill(inp, eps, causal):
 
 
 @pytest.mark.parametrize("case", [(2, 2, 100, 128, True), (2, 2, 100, 128, False),
-                                  (1, 3, 70, 64, True), (3, 1, 129, 128, True)],
+                                  (1, 3, 70, 64, True), (3, 1, 129, 128, True),
+                                  # enough heads for two 16-row query blocks per wave
+                                  (128, 2, 100, 128, False), (256, 4, 130, 64, True)],
                          ids=lambda c: "x".join(map(str, c)))
 def test_attention_prefill_onehot_bitwise(case, require_gpu):
     # Query (g, i) of a head finds its own key at position g Sq + i (within its
@@ -285,7 +287,10 @@ def test_attention_prefill_onehot_bitwise(case, require_gpu):
 
 @pytest.mark.parametrize("case", [(2, 1, 200, 200, 128, True), (2, 4, 130, 300, 64, True),
                                   (1, 2, 64, 1000, 128, False), (3, 1, 1, 50, 128, True),
-                                  (1, 8, 257, 257, 128, True), (2, 3, 65, 90, 64, False)],
+                                  (1, 8, 257, 257, 128, True), (2, 3, 65, 90, 64, False),
+                                  # two 16-row query blocks per wave (128-position
+                                  # workgroups), a ragged last block
+                                  (64, 4, 130, 200, 128, False), (128, 4, 200, 300, 64, True)],
                          ids=lambda c: "x".join(map(str, c)))
 @pytest.mark.parametrize("eps", [1e-6, 0.5])
 def test_attention_prefill_random(case, eps, require_gpu):

@@ -685,18 +685,19 @@ __global__ __launch_bounds__(AQ_THREADS) void gqa_mfma_kernel(
 // BH x Skv x D (query head qh reads key/value head qh / G); with the causal
 // mask query i sees keys 0 .. i + Skv - Sq.  The same two matrix-core
 // products as gqa_mfma_kernel, on blocks of 16 query positions:
-//   * a workgroup (4 waves) owns 64 consecutive positions of one query
-//     head, wave w the 16 rows 16 w ..; each 32-key tile of K and V is loaded
-//     once per workgroup into LDS (double-buffered, one barrier per tile; the
-//     next tile travels in registers meanwhile) and read by all four waves;
+//   * a workgroup (4 waves) owns 64 QW consecutive positions of one query
+//     head, wave w the 16 QW rows from 16 QW w (QW = 1 or 2 blocks of 16);
+//     each 32-key tile of K and V is loaded once per workgroup into LDS
+//     (double-buffered, one barrier per tile; the next tile travels in
+//     registers meanwhile) and read by all four waves;
 //   * K rows as the A fragments of the transposed scores come from LDS with
 //     16-byte reads (chunk c of key row j stored at c ^ (j mod D/8), so the
 //     16 keys of one read hit 16 different chunks); V as in gqa_mfma_kernel;
 //   * every wave keeps its own queries' softmax state over all the keys its
 //     block needs, so nothing is combined across workgroups: o / sum is
-//     stored directly.  Workgroups are ordered so that an XCD takes a
-//     contiguous range of (head, block) pairs, the heads' longest (latest)
-//     blocks first.
+//     stored directly.  Causal workgroups are ordered by their number of
+//     key tiles (see the kernel), the others so that an XCD takes a
+//     contiguous range of (head, block) pairs.
 constexpr int AP_THREADS = 256;
 constexpr int AP_QB = 64;  // query positions per workgroup per 16-row block of each wave
 

@@ -34,6 +34,7 @@ constexpr int AT_THREADS = 256;
 constexpr uint32_t kAtOutOfRange = 0x80000000u;  // past every buffer this path accepts
 constexpr int kAtCoherentDevice = 16;            // SC1: device-scope coherence
 constexpr float kAtNone = -1.0e30f;              // running max before any valid key
+constexpr float kLog2e = 1.44269504088896341f;
 
 // Sum over aligned groups of LPK (8 or 16) lanes with DPP moves: swaps
 // within quads, then the mirrored half-row and row.  Every lane of a group
@@ -701,6 +702,17 @@ __global__ __launch_bounds__(AQ_THREADS) void gqa_mfma_kernel(
 constexpr int AP_THREADS = 256;
 constexpr int AP_QB = 64;  // query positions per workgroup per 16-row block of each wave
 
+// Max over lanes l, l ^ 16, l ^ 32 and l ^ 48 of a wave, with gfx950's
+// permlane swaps (VALU, no LDS round trip): with both operands v, the
+// 16-lane swap returns rows (0, 0, 2, 2) and (1, 1, 3, 3) of v, the 32-lane
+// swap halves (0, 0) and (1, 1).
+__device__ __forceinline__ float max_xor16_32(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 template <int D>
 __device__ __forceinline__ int ap_k_off(int key, int c) {
   return key * (2 * D) + ((c ^ (key & (D / 8 - 1))) << 4);
@@ -749,38 +761,46 @@ __global__ __launch_bounds__(AP_THREADS, 2) void attn_prefill_kernel(
   const int64_t p0 = blk * QB + 16 * QW * w;  // this wave's first query position
   const int64_t off = Skv - Sq;                // causal horizon of position p: p + off
 
-  // U^T fragments of this wave's queries (block b: positions p0 + 16 b ..)
-  // and their scales.
+  // U^T fragments of this wave's queries (block b: positions p0 + 16 b ..):
+  // u = q gq gk c, with the query's scale c = log2(e) / (rms(q) sqrt(D))
+  // folded in (scores come out in base-2 units, so each softmax weight is
+  // one v_exp_f32 of a difference), as two bf16 parts.
   u32x4 uh[QW][NDB], ul[QW][NDB];
-  float cq[QW];
 #pragma unroll
   for (int b = 0; b < QW; ++b) {
     const int64_t p = p0 + 16 * b + lq;
     const bool qok = p < Sq;
+    u32x4 qv[NDB];
     float qss = 0.f;
-    constexpr u32x4 ones{kBf16OnePair, kBf16OnePair, kBf16OnePair, kBf16OnePair};
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const int d0 = 32 * db + 8 * lg;
-      const u32x4 qv = qok ? *(const u32x4*)(Q + (qh * Sq + p) * D + d0) : u32x4{0u, 0u, 0u, 0u};
-      const u32x4 a = NORM ? *(const u32x4*)(gq + d0) : ones;
-      const u32x4 c = NORM ? *(const u32x4*)(gk + d0) : ones;
+      qv[db] = qok ? *(const u32x4*)(Q + (qh * Sq + p) * D + 32 * db + 8 * lg) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        const float q0 = bf16_lo(qv[d]), q1 = bf16_hi(qv[d]);
-        const float u0 = q0 * bf16_lo(a[d]) * bf16_lo(c[d]);
-        const float u1 = q1 * bf16_hi(a[d]) * bf16_hi(c[d]);
-        const uint32_t hi = pack_bf16x2(u0, u1);
-        uh[b][db][d] = hi;
-        ul[b][db][d] = pack_bf16x2(u0 - bf16_lo(hi), u1 - bf16_hi(hi));
+        const float q0 = bf16_lo(qv[db][d]), q1 = bf16_hi(qv[db][d]);
         qss += q0 * q0 + q1 * q1;
       }
     }
     qss += __shfl_xor(qss, 16);
     qss += __shfl_xor(qss, 32);
-    cq[b] = !qok ? 0.f
-            : NORM ? 1.0f / (__fsqrt_rn(__fdiv_rn(qss, (float)D) + eps) * __fsqrt_rn((float)D))
-                   : 1.0f / __fsqrt_rn((float)D);
+    const float cq = !qok ? 0.f
+                     : NORM ? kLog2e / (__fsqrt_rn(__fdiv_rn(qss, (float)D) + eps) * __fsqrt_rn((float)D))
+                            : kLog2e / __fsqrt_rn((float)D);
+    constexpr u32x4 ones{kBf16OnePair, kBf16OnePair, kBf16OnePair, kBf16OnePair};
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int d0 = 32 * db + 8 * lg;
+      const u32x4 ga = NORM ? *(const u32x4*)(gq + d0) : ones;
+      const u32x4 gb = NORM ? *(const u32x4*)(gk + d0) : ones;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const float u0 = bf16_lo(qv[db][d]) * bf16_lo(ga[d]) * bf16_lo(gb[d]) * cq;
+        const float u1 = bf16_hi(qv[db][d]) * bf16_hi(ga[d]) * bf16_hi(gb[d]) * cq;
+        const uint32_t hi = pack_bf16x2(u0, u1);
+        uh[b][db][d] = hi;
+        ul[b][db][d] = pack_bf16x2(u0 - bf16_lo(hi), u1 - bf16_hi(hi));
+      }
+    }
   }
 
   // Keys the block needs: up to the horizon of its last position.
@@ -866,33 +886,47 @@ __global__ __launch_bounds__(AP_THREADS, 2) void attn_prefill_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) rk[hh][i] = r4[i];
     }
+    // Every key of the tile visible to every query of the wave (the tile
+    // ends before kend and, causal, at or before the wave's first horizon):
+    // no mask.  Key and position indices fit in 32 bits (Skv D 2 < 2^31).
+    const int kt = (int)k0;
+    const bool full = kt + 31 < (int)kend && (!CAUSAL || kt + 31 <= (int)(p0 + off));
     u32x4 ph[QW], pl[QW];
 #pragma unroll
     for (int b = 0; b < QW; ++b) {
-      // Visible keys of query column lq: below kend and, causal, within its horizon.
-      const int64_t horizon = CAUSAL ? p0 + 16 * b + lq + off : kend - 1;
       float p[2][4];
-      bool ok[2][4];
       float mb = kAtNone;
+      if (full) {
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
+        for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int64_t key = k0 + 16 * hh + 4 * lg + i;
-          ok[hh][i] = key < kend && key <= horizon;
-          p[hh][i] = sc[b][hh][i] * cq[b] * rk[hh][i];
-          if (ok[hh][i]) mb = fmaxf(mb, p[hh][i]);
-        }
-      mb = fmaxf(mb, __shfl_xor(mb, 16));
-      mb = fmaxf(mb, __shfl_xor(mb, 32));
+          for (int i = 0; i < 4; ++i) {
+            p[hh][i] = sc[b][hh][i] * rk[hh][i];
+            mb = fmaxf(mb, p[hh][i]);
+          }
+      } else {
+        // Visible keys of query column lq: below kend and, causal, within its horizon.
+        const int horizon = CAUSAL ? (int)(p0 + off) + 16 * b + lq : (int)kend - 1;
+        const int kv = horizon < (int)kend - 1 ? horizon : (int)kend - 1;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float v = sc[b][hh][i] * rk[hh][i];
+            p[hh][i] = kt + 16 * hh + 4 * lg + i <= kv ? v : -__builtin_inff();
+            mb = fmaxf(mb, p[hh][i]);
+          }
+      }
+      mb = max_xor16_32(mb);
       const float mn = fmaxf(m[b], mb);
-      const float alpha = __expf(m[b] - mn);
+      const float alpha = __builtin_amdgcn_exp2f(m[b] - mn);
       lpart[b] *= alpha;
+      // A masked key's score is -inf: its weight 2^(-inf - mn) is 0.
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          p[hh][i] = ok[hh][i] ? __expf(p[hh][i] - mn) : 0.f;
+          p[hh][i] = __builtin_amdgcn_exp2f(p[hh][i] - mn);
           lpart[b] += p[hh][i];
         }
       m[b] = mn;

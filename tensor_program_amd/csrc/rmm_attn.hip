@@ -842,8 +842,7 @@ __global__ __launch_bounds__(AP_THREADS, 2) void attn_prefill_kernel(
           const float a0 = bf16_lo(kk[j][d]), a1 = bf16_hi(kk[j][d]);
           ss += a0 * a0 + a1 * a1;
         }
-#pragma unroll
-        for (int x = 1; x < CPR; x <<= 1) ss += __shfl_xor(ss, x);
+        ss = group_sum<CPR>(ss);
         if (c == 0) rk_s[stage][key] = __builtin_amdgcn_rsqf(ss * (1.0f / D) + eps);
       }
     }

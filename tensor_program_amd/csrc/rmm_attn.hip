@@ -688,7 +688,7 @@ __global__ __launch_bounds__(AQ_THREADS) void gqa_mfma_kernel(
 // products as gqa_mfma_kernel, on blocks of 16 query positions:
 //   * a workgroup (4 waves) owns 64 QW consecutive positions of one query
 //     head, wave w the 16 QW rows from 16 QW w (QW = 1 or 2 blocks of 16);
-//     each 32-key tile of K and V is loaded once per workgroup into LDS
+//     each tile of 32 or 64 keys of K and V is loaded once per workgroup into LDS
 //     (double-buffered, one barrier per tile; the next tile travels in
 //     registers meanwhile) and read by all four waves;
 //   * K rows as the A fragments of the transposed scores come from LDS with
@@ -701,6 +701,7 @@ __global__ __launch_bounds__(AQ_THREADS) void gqa_mfma_kernel(
 //     contiguous range of (head, block) pairs.
 constexpr int AP_THREADS = 256;
 constexpr int AP_QB = 64;  // query positions per workgroup per 16-row block of each wave
+
 
 // Max over lanes l, l ^ 16, l ^ 32 and l ^ 48 of a wave, with gfx950's
 // permlane swaps (VALU, no LDS round trip): with both operands v, the
@@ -721,8 +722,9 @@ __device__ __forceinline__ int ap_k_off(int key, int c) {
 // QW: 16-row query blocks per wave (1 or 2); with two, each K and V
 // fragment read from LDS feeds both blocks' MFMAs, halving the LDS reads
 // per query.  The workgroup then owns 64 QW positions, wave w rows
-// 16 QW w .. +16 QW - 1.
-template <int D, bool NORM, bool CAUSAL, int QW>
+// 16 QW w .. +16 QW - 1.  KT: keys per tile (32 or 64), NH blocks of 16 in
+// the scores, NP steps of 32 in the value product.
+template <int D, bool NORM, bool CAUSAL, int QW, int KT>
 __global__ __launch_bounds__(AP_THREADS, 2) void attn_prefill_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc,
     const bf16_t* __restrict__ gq, const bf16_t* __restrict__ gk, bf16_t* __restrict__ O,
@@ -730,11 +732,12 @@ __global__ __launch_bounds__(AP_THREADS, 2) void attn_prefill_kernel(
   constexpr int NDB = D / 32;
   constexpr int NOB = D / 16;
   constexpr int CPR = D / 8;
-  constexpr int NL = 32 * CPR / AP_THREADS;  // K (and V) tile chunks per thread
+  constexpr int NL = KT * CPR / AP_THREADS;  // K (and V) tile chunks per thread
   constexpr int QB = AP_QB * QW;             // query positions per workgroup
-  __shared__ __attribute__((aligned(16))) char k_s[2][32 * 2 * D];
-  __shared__ __attribute__((aligned(16))) char v_s[2][32 * 2 * D];
-  __shared__ __attribute__((aligned(16))) float rk_s[2][32];  // the tile's keys' 1/RMS
+  constexpr int NH = KT / 16, NP = KT / 32;  // 16-key score blocks, 32-key value steps
+  __shared__ __attribute__((aligned(16))) char k_s[2][KT * 2 * D];
+  __shared__ __attribute__((aligned(16))) char v_s[2][KT * 2 * D];
+  __shared__ __attribute__((aligned(16))) float rk_s[2][KT];  // the tile's keys' 1/RMS
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lq = l & 15, lg = l >> 4;
   // Order of the (query head, block) pairs.  order 1 (causal, blocks of
@@ -809,7 +812,7 @@ __global__ __launch_bounds__(AP_THREADS, 2) void attn_prefill_kernel(
     const int64_t last = (blk + 1) * QB - 1 < Sq - 1 ? (blk + 1) * QB - 1 : Sq - 1;
     kend = last + off + 1;
   }
-  const int64_t ntile = (kend + 31) / 32;
+  const int64_t ntile = (kend + KT - 1) / KT;
   const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(Kc + h * Skv * D), 0, (int)(Skv * D * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
@@ -819,7 +822,7 @@ __global__ __launch_bounds__(AP_THREADS, 2) void attn_prefill_kernel(
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
       const int e = tid + AP_THREADS * j;
-      const int64_t key = 32 * tt + e / CPR;
+      const int64_t key = KT * tt + e / CPR;
       const uint32_t o = (tt < ntile && key < kend) ? (uint32_t)((key * D + 8 * (e % CPR)) * 2)
                                                     : kAtOutOfRange;
       kk[j] = __builtin_amdgcn_raw_buffer_load_b128(kr, o, 0, 0);
@@ -860,11 +863,11 @@ __global__ __launch_bounds__(AP_THREADS, 2) void attn_prefill_kernel(
 
   auto compute = [&](int64_t tt, int stage) {
     const char* ks = k_s[stage];
-    const int64_t k0 = 32 * tt;
-    floatx4 sc[QW][2];
-    float rk[2][4];
+    const int64_t k0 = KT * tt;
+    floatx4 sc[QW][NH];
+    float rk[NH][4];
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
+    for (int hh = 0; hh < NH; ++hh) {
 #pragma unroll
       for (int b = 0; b < QW; ++b) sc[b][hh] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -889,15 +892,15 @@ __global__ __launch_bounds__(AP_THREADS, 2) void attn_prefill_kernel(
     // ends before kend and, causal, at or before the wave's first horizon):
     // no mask.  Key and position indices fit in 32 bits (Skv D 2 < 2^31).
     const int kt = (int)k0;
-    const bool full = kt + 31 < (int)kend && (!CAUSAL || kt + 31 <= (int)(p0 + off));
-    u32x4 ph[QW], pl[QW];
+    const bool full = kt + KT - 1 < (int)kend && (!CAUSAL || kt + KT - 1 <= (int)(p0 + off));
+    u32x4 ph[QW][NP], pl[QW][NP];
 #pragma unroll
     for (int b = 0; b < QW; ++b) {
-      float p[2][4];
+      float p[NH][4];
       float mb = kAtNone;
       if (full) {
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
+        for (int hh = 0; hh < NH; ++hh)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             p[hh][i] = sc[b][hh][i] * rk[hh][i];
@@ -908,7 +911,7 @@ __global__ __launch_bounds__(AP_THREADS, 2) void attn_prefill_kernel(
         const int horizon = CAUSAL ? (int)(p0 + off) + 16 * b + lq : (int)kend - 1;
         const int kv = horizon < (int)kend - 1 ? horizon : (int)kend - 1;
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
+        for (int hh = 0; hh < NH; ++hh)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float v = sc[b][hh][i] * rk[hh][i];
@@ -922,20 +925,23 @@ __global__ __launch_bounds__(AP_THREADS, 2) void attn_prefill_kernel(
       lpart[b] *= alpha;
       // A masked key's score is -inf: its weight 2^(-inf - mn) is 0.
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
+      for (int hh = 0; hh < NH; ++hh)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           p[hh][i] = __builtin_amdgcn_exp2f(p[hh][i] - mn);
           lpart[b] += p[hh][i];
         }
       m[b] = mn;
+      // P fragments of value step hp: keys 32 hp + 4 lg .. +3 and
+      // 32 hp + 16 + 4 lg .. +3 of query column lq.
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
+      for (int hh = 0; hh < NH; ++hh)
 #pragma unroll
         for (int i = 0; i < 4; i += 2) {
           const uint32_t hi = pack_bf16x2(p[hh][i], p[hh][i + 1]);
-          ph[b][2 * hh + i / 2] = hi;
-          pl[b][2 * hh + i / 2] = pack_bf16x2(p[hh][i] - bf16_lo(hi), p[hh][i + 1] - bf16_hi(hi));
+          ph[b][hh >> 1][2 * (hh & 1) + i / 2] = hi;
+          pl[b][hh >> 1][2 * (hh & 1) + i / 2] =
+              pack_bf16x2(p[hh][i] - bf16_lo(hi), p[hh][i + 1] - bf16_hi(hi));
         }
       // Rescale O only when some query's maximum moved (once the running
       // maxima settle, most tiles skip it).
@@ -951,23 +957,25 @@ __global__ __launch_bounds__(AP_THREADS, 2) void attn_prefill_kernel(
     }
     const at_lds_char* vl = (const at_lds_char*)v_s[stage];
 #pragma unroll
-    for (int ob = 0; ob < NOB; ++ob) {
-      const int col = 16 * ob + 4 * (lq & 3), row = 4 * lg + (lq >> 2);
-      const u32x2 v0 = __builtin_bit_cast(
-          u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((at_lds_i16x4*)(vl + aq_v_off<D>(row, col))));
-      const u32x2 v1 = __builtin_bit_cast(
-          u32x2,
-          __builtin_amdgcn_ds_read_tr16_b64_v4i16((at_lds_i16x4*)(vl + aq_v_off<D>(row + 16, col))));
-      const u32x4 vb4 = {v0[0], v0[1], v1[0], v1[1]};
-      const bf16x8 vb = __builtin_bit_cast(bf16x8, vb4);
+    for (int hp = 0; hp < NP; ++hp)
 #pragma unroll
-      for (int b = 0; b < QW; ++b) {
-        o[b][ob] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ph[b]), vb,
-                                                           o[b][ob], 0, 0, 0);
-        o[b][ob] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pl[b]), vb,
-                                                           o[b][ob], 0, 0, 0);
+      for (int ob = 0; ob < NOB; ++ob) {
+        const int col = 16 * ob + 4 * (lq & 3), row = 32 * hp + 4 * lg + (lq >> 2);
+        const u32x2 v0 = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((at_lds_i16x4*)(vl + aq_v_off<D>(row, col))));
+        const u32x2 v1 = __builtin_bit_cast(
+            u32x2,
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((at_lds_i16x4*)(vl + aq_v_off<D>(row + 16, col))));
+        const u32x4 vb4 = {v0[0], v0[1], v1[0], v1[1]};
+        const bf16x8 vb = __builtin_bit_cast(bf16x8, vb4);
+#pragma unroll
+        for (int b = 0; b < QW; ++b) {
+          o[b][ob] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ph[b][hp]),
+                                                             vb, o[b][ob], 0, 0, 0);
+          o[b][ob] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pl[b][hp]),
+                                                             vb, o[b][ob], 0, 0, 0);
+        }
       }
-    }
   };
 
   // Pipeline: at the top of iteration tt stage tt & 1 holds tile tt (the
@@ -1094,6 +1102,12 @@ hipError_t rmm_launch_attention_prefill(const AttnArgs& a, int64_t Sq, int64_t S
   const int qw = wg2 >= (causal ? 4 * 256 : 256) ? 2 : 1;
   const int64_t nblk = (Sq + qw * AP_QB - 1) / (qw * AP_QB);
   const int64_t grid = a.BH * a.G * nblk;
+  // 64-key tiles (half the barriers and softmax rounds per key; 221 VGPRs
+  // and 64 KB of LDS: two workgroups per CU instead of three) when the grid
+  // holds at most one workgroup per CU anyway.  Measured: 8 x 4 heads, 512
+  // queries over 8192 keys 276.6 -> 237.5 us; 32 heads x 2048 causal
+  // (1024 workgroups) 116.4 -> 120.6 us.
+  const int kt = qw == 1 && grid <= 256 ? 64 : 32;
   const int order = causal ? 1 : (grid % 8 == 0 ? 0 : 2);
   auto launch = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(AP_THREADS), 0, a.stream,
@@ -1104,8 +1118,12 @@ hipError_t rmm_launch_attention_prefill(const AttnArgs& a, int64_t Sq, int64_t S
   auto by_qw = [&](auto d, auto norm, auto cz) {
     constexpr int D = decltype(d)::value;
     constexpr bool NORM = decltype(norm)::value, CAUSAL = decltype(cz)::value;
-    qw == 2 ? launch(attn_prefill_kernel<D, NORM, CAUSAL, 2>)
-            : launch(attn_prefill_kernel<D, NORM, CAUSAL, 1>);
+    if (qw == 2)
+      launch(attn_prefill_kernel<D, NORM, CAUSAL, 2, 32>);
+    else if (kt == 64)
+      launch(attn_prefill_kernel<D, NORM, CAUSAL, 1, 64>);
+    else
+      launch(attn_prefill_kernel<D, NORM, CAUSAL, 1, 32>);
   };
   auto by_mask = [&](auto d, auto norm) {
     causal ? by_qw(d, norm, std::true_type{}) : by_qw(d, norm, std::false_type{});

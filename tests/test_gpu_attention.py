@@ -290,7 +290,10 @@ def test_attention_prefill_onehot_bitwise(case, require_gpu):
                                   (1, 8, 257, 257, 128, True), (2, 3, 65, 90, 64, False),
                                   # two 16-row query blocks per wave (128-position
                                   # workgroups), a ragged last block
-                                  (64, 4, 130, 200, 128, False), (128, 4, 200, 300, 64, True)],
+                                  (64, 4, 130, 200, 128, False), (128, 4, 200, 300, 64, True),
+                                  # one block per wave with 32-key tiles (more than 256
+                                  # workgroups; the smaller grids above take 64-key tiles)
+                                  (50, 2, 256, 300, 64, False), (32, 4, 200, 260, 64, True)],
                          ids=lambda c: "x".join(map(str, c)))
 @pytest.mark.parametrize("eps", [1e-6, 0.5])
 def test_attention_prefill_random(case, eps, require_gpu):

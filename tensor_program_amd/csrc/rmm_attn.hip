@@ -384,7 +384,7 @@ __global__ __launch_bounds__(AQ_THREADS) void gqa_mfma_kernel(
   constexpr int NV = 32 * CPR / 64; // V tile chunks per lane
   constexpr int NWV = AQ_THREADS / 64;
   __shared__ __attribute__((aligned(16))) char v_s[NWV][2][32 * 2 * D];
-  __shared__ float mo_s[NWV][16][D];
+  __shared__ __attribute__((aligned(16))) float mo_s[NWV][16][D];
   __shared__ float mm_s[NWV][16], ml_s[NWV][16];
   __shared__ int last;
 
@@ -394,36 +394,8 @@ __global__ __launch_bounds__(AQ_THREADS) void gqa_mfma_kernel(
   const int64_t s_lo = (int64_t)chunk * kchunk;
   const int64_t s_hi = (s_lo + kchunk < S) ? (s_lo + kchunk) : S;
 
-  // U^T fragments (query lq, dims 32 db + 8 lg .. +7) and the query's scale.
-  u32x4 uh[NDB], ul[NDB];
+  u32x4 uh[NDB], ul[NDB];  // U^T fragments, formed below behind the first tile loads
   float cq;
-  {
-    float qss = 0.f;
-    constexpr u32x4 ones{kBf16OnePair, kBf16OnePair, kBf16OnePair, kBf16OnePair};
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const int d0 = 32 * db + 8 * lg;
-      const u32x4 qv = lq < G ? *(const u32x4*)(Q + (bh * G + lq) * D + d0) : u32x4{0u, 0u, 0u, 0u};
-      const u32x4 a = NORM ? *(const u32x4*)(gq + d0) : ones;
-      const u32x4 b = NORM ? *(const u32x4*)(gk + d0) : ones;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const float q0 = bf16_lo(qv[d]), q1 = bf16_hi(qv[d]);
-        const float u0 = q0 * bf16_lo(a[d]) * bf16_lo(b[d]);
-        const float u1 = q1 * bf16_hi(a[d]) * bf16_hi(b[d]);
-        const uint32_t hi = pack_bf16x2(u0, u1);
-        uh[db][d] = hi;
-        ul[db][d] = pack_bf16x2(u0 - bf16_lo(hi), u1 - bf16_hi(hi));
-        qss += q0 * q0 + q1 * q1;
-      }
-    }
-    qss += __shfl_xor(qss, 16);
-    qss += __shfl_xor(qss, 32);
-    cq = lq >= G ? 0.f
-         : NORM ? 1.0f / (__fsqrt_rn(__fdiv_rn(qss, (float)D) + eps) * __fsqrt_rn((float)D))
-                : 1.0f / __fsqrt_rn((float)D);
-  }
-
   const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(Kc + bh * S * D), 0, (int)(S * D * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
@@ -561,9 +533,46 @@ __global__ __launch_bounds__(AQ_THREADS) void gqa_mfma_kernel(
     }
   };
 
+  // The query and the gains are loaded first, the first two tiles right
+  // behind them, and U is formed while the tiles are in flight (HBM is
+  // busy from the start; the wait for the query's loads does not cover the
+  // tiles').
+  constexpr u32x4 ones{kBf16OnePair, kBf16OnePair, kBf16OnePair, kBf16OnePair};
+  u32x4 qv[NDB], ga[NDB], gb[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const int d0 = 32 * db + 8 * lg;
+    qv[db] = lq < G ? *(const u32x4*)(Q + (bh * G + lq) * D + d0) : u32x4{0u, 0u, 0u, 0u};
+    ga[db] = NORM ? *(const u32x4*)(gq + d0) : ones;
+    gb[db] = NORM ? *(const u32x4*)(gk + d0) : ones;
+  }
   u32x4 ka[2][NDB], va[NV], kb[2][NDB], vb[NV];
   load(w, ka, va);
   load(w + NWV, kb, vb);
+
+  // U^T fragments (query lq, dims 32 db + 8 lg .. +7) and the query's scale.
+  {
+    float qss = 0.f;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const float q0 = bf16_lo(qv[db][d]), q1 = bf16_hi(qv[db][d]);
+        const float u0 = q0 * bf16_lo(ga[db][d]) * bf16_lo(gb[db][d]);
+        const float u1 = q1 * bf16_hi(ga[db][d]) * bf16_hi(gb[db][d]);
+        const uint32_t hi = pack_bf16x2(u0, u1);
+        uh[db][d] = hi;
+        ul[db][d] = pack_bf16x2(u0 - bf16_lo(hi), u1 - bf16_hi(hi));
+        qss += q0 * q0 + q1 * q1;
+      }
+    }
+    qss += __shfl_xor(qss, 16);
+    qss += __shfl_xor(qss, 32);
+    cq = lq >= G ? 0.f
+         : NORM ? 1.0f / (__fsqrt_rn(__fdiv_rn(qss, (float)D) + eps) * __fsqrt_rn((float)D))
+                : 1.0f / __fsqrt_rn((float)D);
+  }
+
   int64_t t = w;
   for (; t + NWV < ntile; t += 2 * NWV) {
     consume(t, 0, ka, va);
@@ -586,13 +595,16 @@ __global__ __launch_bounds__(AQ_THREADS) void gqa_mfma_kernel(
     for (int i = 0; i < 4; ++i) mo_s[w][4 * lg + i][16 * ob + lq] = o[ob][i];
   __syncthreads();
 
-  // Thread t merges the waves for (query t / D, dim t % D), t < G D.
-  constexpr int PER = 16 * D / AQ_THREADS;
-  float od[PER], ld[PER], md[PER];
+  // Thread t merges the waves for (query p / (D/4), dims 4 (p % (D/4)) ..
+  // +3), p = t + 256 e (float4 in LDS and in the workspace).
+  constexpr int D4 = D / 4;
+  constexpr int PER = 16 * D4 / AQ_THREADS;
+  floatx4 od[PER];
+  float ld[PER], md[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
-    const int tt = tid + AQ_THREADS * e, g = tt / D, d = tt % D;
-    od[e] = 0.f;
+    const int pp = tid + AQ_THREADS * e, g = pp / D4, d0 = 4 * (pp % D4);
+    od[e] = floatx4{0.f, 0.f, 0.f, 0.f};
     ld[e] = 0.f;
     md[e] = kAtNone;
     if (g < G) {
@@ -601,27 +613,35 @@ __global__ __launch_bounds__(AQ_THREADS) void gqa_mfma_kernel(
 #pragma unroll
       for (int ww = 0; ww < NWV; ++ww) {
         const float a = __expf(mm_s[ww][g] - md[e]);
-        od[e] += mo_s[ww][g][d] * a;
+        const floatx4 v = *(const floatx4*)&mo_s[ww][g][d0];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) od[e][i] += v[i] * a;
         ld[e] += ml_s[ww][g] * a;
       }
     }
   }
   if (C > 1) {
-    const int64_t slot = bh * C + chunk;
+    // Workspace: o as [slot][query][D], then m and l as [slot][query]; slot =
+    // key/value head * C + chunk.  Device-coherent (SC1) stores and loads:
+    // the chunks of a head run on any XCD.
+    const int64_t nslot = (int64_t)gridDim.x, slot = bh * C + chunk;
+    const int64_t m_off = nslot * G * D, l_off = nslot * G * (D + 1);
     const __amdgpu_buffer_rsrc_t pr =
         __builtin_amdgcn_make_buffer_rsrc(part, 0, 0x7fffffff, 0x00020000);
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
-      const int tt = tid + AQ_THREADS * e, g = tt / D, d = tt % D;
+      const int pp = tid + AQ_THREADS * e, g = pp / D4, d0 = 4 * (pp % D4);
       if (g < G) {
-        const int64_t base = (slot * G + g) * (D + 2);
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(od[e]), pr, (int)((base + d) * 4),
-                                              0, kAtCoherentDevice);
-        if (d == 0) {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, od[e]), pr,
+                                               (int)(((slot * G + g) * D + d0) * 4), 0,
+                                               kAtCoherentDevice);
+        if (d0 == 0) {
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(md[e]), pr,
-                                                (int)((base + D) * 4), 0, kAtCoherentDevice);
+                                                (int)((m_off + slot * G + g) * 4), 0,
+                                                kAtCoherentDevice);
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ld[e]), pr,
-                                                (int)((base + D + 1) * 4), 0, kAtCoherentDevice);
+                                                (int)((l_off + slot * G + g) * 4), 0,
+                                                kAtCoherentDevice);
         }
       }
     }
@@ -632,51 +652,65 @@ __global__ __launch_bounds__(AQ_THREADS) void gqa_mfma_kernel(
               (unsigned)(C - 1));
     __syncthreads();
     if (!last) return;
+    // The last arrival adds the chunks in order, 8 at a time, every load of
+    // a batch issued before any is used.
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
-      const int tt = tid + AQ_THREADS * e, g = tt / D, d = tt % D;
-      if (g < G) {
-        md[e] = kAtNone;
-        od[e] = 0.f;
-        ld[e] = 0.f;
-        for (int c0 = 0; c0 < C; c0 += 8) {
-          float oc[8], mc[8], lc[8];
+      md[e] = kAtNone;
+      od[e] = floatx4{0.f, 0.f, 0.f, 0.f};
+      ld[e] = 0.f;
+    }
+    for (int c0 = 0; c0 < C; c0 += 8) {
+      floatx4 oc[PER][8];
+      float mc[PER][8], lc[PER][8];
 #pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            const int64_t base = ((bh * C + c0 + q) * G + g) * (D + 2);
-            const bool in = c0 + q < C;
-            oc[q] = in ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                             pr, (int)((base + d) * 4), 0, kAtCoherentDevice))
-                       : 0.f;
-            mc[q] = in ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                             pr, (int)((base + D) * 4), 0, kAtCoherentDevice))
-                       : kAtNone;
-            lc[q] = in ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                             pr, (int)((base + D + 1) * 4), 0, kAtCoherentDevice))
-                       : 0.f;
-          }
-          float mn = md[e];
+      for (int e = 0; e < PER; ++e) {
+        const int pp = tid + AQ_THREADS * e, g = pp / D4, d0 = 4 * (pp % D4);
 #pragma unroll
-          for (int q = 0; q < 8; ++q) mn = fmaxf(mn, mc[q]);
-          const float r = __expf(md[e] - mn);
-          od[e] *= r;
-          ld[e] *= r;
-#pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            const float a = __expf(mc[q] - mn);
-            od[e] += oc[q] * a;
-            ld[e] += lc[q] * a;
-          }
-          md[e] = mn;
+        for (int q = 0; q < 8; ++q) {
+          const int64_t sl = bh * C + c0 + q;
+          const bool in = g < G && c0 + q < C;
+          oc[e][q] = in ? __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                          pr, (int)(((sl * G + g) * D + d0) * 4), 0,
+                                                          kAtCoherentDevice))
+                        : floatx4{0.f, 0.f, 0.f, 0.f};
+          mc[e][q] = in ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                              pr, (int)((m_off + sl * G + g) * 4), 0, kAtCoherentDevice))
+                        : kAtNone;
+          lc[e][q] = in ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                              pr, (int)((l_off + sl * G + g) * 4), 0, kAtCoherentDevice))
+                        : 0.f;
         }
+      }
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        float mn = md[e];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) mn = fmaxf(mn, mc[e][q]);
+        const float r = __expf(md[e] - mn);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) od[e][i] *= r;
+        ld[e] *= r;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const float a = __expf(mc[e][q] - mn);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) od[e][i] += oc[e][q][i] * a;
+          ld[e] += lc[e][q] * a;
+        }
+        md[e] = mn;
       }
     }
     if (tid == 0) __hip_atomic_store(&cnt[bh], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
-    const int tt = tid + AQ_THREADS * e, g = tt / D, d = tt % D;
-    if (g < G) O[(bh * G + g) * D + d] = f32_to_bf16(__fdiv_rn(od[e], ld[e]));
+    const int pp = tid + AQ_THREADS * e, g = pp / D4, d0 = 4 * (pp % D4);
+    if (g < G) {
+      const uint32_t lo = pack_bf16x2(__fdiv_rn(od[e][0], ld[e]), __fdiv_rn(od[e][1], ld[e]));
+      const uint32_t hi = pack_bf16x2(__fdiv_rn(od[e][2], ld[e]), __fdiv_rn(od[e][3], ld[e]));
+      *(u32x2*)(O + (bh * G + g) * D + d0) = u32x2{lo, hi};
+    }
   }
 }
 

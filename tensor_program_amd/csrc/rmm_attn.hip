@@ -36,6 +36,23 @@ constexpr int kAtCoherentDevice = 16;            // SC1: device-scope coherence
 constexpr float kAtNone = -1.0e30f;              // running max before any valid key
 constexpr float kLog2e = 1.44269504088896341f;
 
+// Max and sum over lanes l, l ^ 16, l ^ 32 and l ^ 48 of a wave, with
+// gfx950's permlane swaps (VALU, no LDS round trip): with both operands v,
+// the 16-lane swap returns rows (0, 0, 2, 2) and (1, 1, 3, 3) of v, the
+// 32-lane swap halves (0, 0) and (1, 1); every lane gets the same bits.
+__device__ __forceinline__ float max_xor16_32(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_xor16_32(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Sum over aligned groups of LPK (8 or 16) lanes with DPP moves: swaps
 // within quads, then the mirrored half-row and row.  Every lane of a group
 // ends with the same bits (each step adds two operands in either order),
@@ -386,6 +403,7 @@ __global__ __launch_bounds__(AQ_THREADS) void gqa_mfma_kernel(
   __shared__ __attribute__((aligned(16))) char v_s[NWV][2][32 * 2 * D];
   __shared__ __attribute__((aligned(16))) float mo_s[NWV][16][D];
   __shared__ float mm_s[NWV][16], ml_s[NWV][16];
+  __shared__ __attribute__((aligned(16))) float rk_w[NWV][2][16];  // keys' 1/RMS, per wave
   __shared__ int last;
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lq = l & 15, lg = l >> 4;
@@ -457,14 +475,16 @@ __global__ __launch_bounds__(AQ_THREADS) void gqa_mfma_kernel(
         }
       }
       if (NORM) {
-        ss += __shfl_xor(ss, 16);
-        ss += __shfl_xor(ss, 32);
+        ss = sum_xor16_32(ss);
         // 1/D is a power of two (exact); v_rsq_f32 for the key's 1/RMS.
         const float r = __builtin_amdgcn_rsqf(ss * (1.0f / D) + eps);
         // this lane's score rows are keys 4 lg + i of the half: their 1/RMS
-        // sits on the lanes whose key column lq is 4 lg + i
+        // sits on the lanes whose key column lq is 4 lg + i; passed through
+        // the wave's LDS slots (its own LDS operations complete in order)
+        if (lg == 0) rk_w[w][h][lq] = r;
+        const floatx4 r4 = *(const floatx4*)&rk_w[w][h][4 * lg];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) rk[h][i] = __shfl(r, 4 * lg + i);
+        for (int i = 0; i < 4; ++i) rk[h][i] = r4[i];
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) rk[h][i] = 1.0f;
@@ -481,23 +501,18 @@ __global__ __launch_bounds__(AQ_THREADS) void gqa_mfma_kernel(
         p[h][i] = sc[h][i] * cq * rk[h][i];
         if (k0 + 16 * h + 4 * lg + i < s_hi) mb = fmaxf(mb, p[h][i]);
       }
-    mb = fmaxf(mb, __shfl_xor(mb, 16));
-    mb = fmaxf(mb, __shfl_xor(mb, 32));
+    mb = max_xor16_32(mb);
     const float mn = fmaxf(m, mb);
-    const float alpha = __expf(m - mn);
+    const float alpha = __builtin_amdgcn_exp2f(m - mn);
     lpart *= alpha;
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        p[h][i] = (k0 + 16 * h + 4 * lg + i < s_hi) ? __expf(p[h][i] - mn) : 0.f;
+        p[h][i] = (k0 + 16 * h + 4 * lg + i < s_hi) ? __builtin_amdgcn_exp2f(p[h][i] - mn) : 0.f;
         lpart += p[h][i];
       }
     m = mn;
-    // O rows are queries 4 lg + i: their alpha sits on lanes lq = 4 lg + i.
-    float ar[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * lg + i);
     u32x4 ph, pl;
 #pragma unroll
     for (int h = 0; h < 2; ++h)
@@ -508,8 +523,12 @@ __global__ __launch_bounds__(AQ_THREADS) void gqa_mfma_kernel(
         pl[2 * h + i / 2] = pack_bf16x2(p[h][i] - bf16_lo(hi), p[h][i + 1] - bf16_hi(hi));
       }
     const at_lds_char* vl = (const at_lds_char*)vt;
-    // Rescale O only when some query's maximum moved.
+    // Rescale O only when some query's maximum moved.  O rows are queries
+    // 4 lg + i: their alpha sits on lanes lq = 4 lg + i.
     if (__any(alpha != 1.0f)) {
+      float ar[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * lg + i);
 #pragma unroll
       for (int ob = 0; ob < NOB; ++ob)
 #pragma unroll
@@ -568,9 +587,10 @@ __global__ __launch_bounds__(AQ_THREADS) void gqa_mfma_kernel(
     }
     qss += __shfl_xor(qss, 16);
     qss += __shfl_xor(qss, 32);
+    // log2(e) folded in: scores in base-2 units, one v_exp_f32 per weight
     cq = lq >= G ? 0.f
-         : NORM ? 1.0f / (__fsqrt_rn(__fdiv_rn(qss, (float)D) + eps) * __fsqrt_rn((float)D))
-                : 1.0f / __fsqrt_rn((float)D);
+         : NORM ? kLog2e / (__fsqrt_rn(__fdiv_rn(qss, (float)D) + eps) * __fsqrt_rn((float)D))
+                : kLog2e / __fsqrt_rn((float)D);
   }
 
   int64_t t = w;
@@ -596,7 +616,8 @@ __global__ __launch_bounds__(AQ_THREADS) void gqa_mfma_kernel(
   __syncthreads();
 
   // Thread t merges the waves for (query p / (D/4), dims 4 (p % (D/4)) ..
-  // +3), p = t + 256 e (float4 in LDS and in the workspace).
+  // +3), p = t + 256 e (float4 in LDS and in the workspace); the maxima are
+  // in base-2 units.
   constexpr int D4 = D / 4;
   constexpr int PER = 16 * D4 / AQ_THREADS;
   floatx4 od[PER];
@@ -612,7 +633,7 @@ __global__ __launch_bounds__(AQ_THREADS) void gqa_mfma_kernel(
       for (int ww = 0; ww < NWV; ++ww) md[e] = fmaxf(md[e], mm_s[ww][g]);
 #pragma unroll
       for (int ww = 0; ww < NWV; ++ww) {
-        const float a = __expf(mm_s[ww][g] - md[e]);
+        const float a = __builtin_amdgcn_exp2f(mm_s[ww][g] - md[e]);
         const floatx4 v = *(const floatx4*)&mo_s[ww][g][d0];
 #pragma unroll
         for (int i = 0; i < 4; ++i) od[e][i] += v[i] * a;
@@ -687,13 +708,13 @@ __global__ __launch_bounds__(AQ_THREADS) void gqa_mfma_kernel(
         float mn = md[e];
 #pragma unroll
         for (int q = 0; q < 8; ++q) mn = fmaxf(mn, mc[e][q]);
-        const float r = __expf(md[e] - mn);
+        const float r = __builtin_amdgcn_exp2f(md[e] - mn);
 #pragma unroll
         for (int i = 0; i < 4; ++i) od[e][i] *= r;
         ld[e] *= r;
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-          const float a = __expf(mc[e][q] - mn);
+          const float a = __builtin_amdgcn_exp2f(mc[e][q] - mn);
 #pragma unroll
           for (int i = 0; i < 4; ++i) od[e][i] += oc[e][q][i] * a;
           ld[e] += lc[e][q] * a;
@@ -736,17 +757,6 @@ __global__ __launch_bounds__(AQ_THREADS) void gqa_mfma_kernel(
 constexpr int AP_THREADS = 256;
 constexpr int AP_QB = 64;  // query positions per workgroup per 16-row block of each wave
 
-
-// Max over lanes l, l ^ 16, l ^ 32 and l ^ 48 of a wave, with gfx950's
-// permlane swaps (VALU, no LDS round trip): with both operands v, the
-// 16-lane swap returns rows (0, 0, 2, 2) and (1, 1, 3, 3) of v, the 32-lane
-// swap halves (0, 0) and (1, 1).
-__device__ __forceinline__ float max_xor16_32(float v) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
 
 template <int D>
 __device__ __forceinline__ int ap_k_off(int key, int c) {

@@ -166,7 +166,7 @@ __device__ __forceinline__ void pf_store_a(const PfA& st, char* a_lds, float (&s
     u32x4 v;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      const uint32_t gd = norm ? gsrc[d] : kBf16OnePair;
+      const uint32_t gd = (GL || norm) ? gsrc[d] : kBf16OnePair;
       const float x0 = __uint_as_float(st.a[i][d] << 16), x1 = __uint_as_float(st.a[i][d] & 0xffff0000u);
       v[d] = pack_bf16x2(x0 * __uint_as_float(gd << 16), x1 * __uint_as_float(gd & 0xffff0000u));
       ss[i] = __builtin_fmaf(x1, x1, __builtin_fmaf(x0, x0, ss[i]));
@@ -266,7 +266,7 @@ __device__ __forceinline__ void pf_step(const char* a_cur, const lds_char* b_cur
     if (!GL) gsrc = st.g;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      const uint32_t gd = norm ? gsrc[d] : kBf16OnePair;
+      const uint32_t gd = (GL || norm) ? gsrc[d] : kBf16OnePair;
       g_f[2 * d] = __uint_as_float(gd << 16);
       g_f[2 * d + 1] = __uint_as_float(gd & 0xffff0000u);
     }
@@ -319,7 +319,8 @@ __device__ __forceinline__ void pf_step(const char* a_cur, const lds_char* b_cur
 
 // Largest K whose gain vector is held in LDS for the whole call (20 KB, the
 // room left beside the A and W stages); the k-steps past K (up to one more
-// step) read zeros from the padding.
+// step) read zeros from the padding.  Without the norm the LDS copy holds
+// ones, so the k-loop forms X g with no select on the norm flag.
 constexpr int PF_G_LDS_MAX = 10240;
 
 template <bool GATED, bool GL>
@@ -405,7 +406,9 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_kernel(
   // sees none of these loads.
   if (GL) {  // the whole gain vector, zero past K
     for (int c = tid; c < (PF_G_LDS_MAX + 2 * PF_BK) / 8; c += PF_THREADS)
-      *(u32x4*)(g_s + 16 * c) = 8 * c < K ? *(const u32x4*)(g + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+      *(u32x4*)(g_s + 16 * c) = 8 * c >= K ? u32x4{0u, 0u, 0u, 0u}
+                                : norm     ? *(const u32x4*)(g + 8 * c)
+                                           : u32x4{kBf16OnePair, kBf16OnePair, kBf16OnePair, kBf16OnePair};
     __syncthreads();
   }
 
@@ -611,7 +614,7 @@ template <bool GL>
 __device__ __forceinline__ void pg_gain(float (&g_f)[8], const u32x4& gsrc, int norm) {
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
-    const uint32_t gd = norm ? gsrc[d] : kBf16OnePair;
+    const uint32_t gd = (GL || norm) ? gsrc[d] : kBf16OnePair;
     g_f[2 * d] = __uint_as_float(gd << 16);
     g_f[2 * d + 1] = __uint_as_float(gd & 0xffff0000u);
   }
@@ -773,7 +776,9 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_gated_kernel(
 
   if (GL) {
     for (int c = tid; c < (PF_G_LDS_MAX + 2 * PF_BK) / 8; c += PF_THREADS)
-      *(u32x4*)(g_s + 16 * c) = 8 * c < K ? *(const u32x4*)(g + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+      *(u32x4*)(g_s + 16 * c) = 8 * c >= K ? u32x4{0u, 0u, 0u, 0u}
+                                : norm     ? *(const u32x4*)(g + 8 * c)
+                                           : u32x4{kBf16OnePair, kBf16OnePair, kBf16OnePair, kBf16OnePair};
     __syncthreads();
   }
 

@@ -50,10 +50,11 @@
  * entry point, shape, dtype, variant or split count -- without clearing, as
  * long as each call runs to completion (a call forced to a split count
  * needing more than 16320 counters returns RMM_ERR_VARIANT).  One workspace
- * must not be used by two calls that may run at the same time.  ws_bytes
- * below rmm_workspace_bytes*() returns RMM_ERR_WORKSPACE, except where AUTO
- * picks the prefill split: it then takes the best count that fits (down to
- * no split).
+ * must not be used by two calls that may run at the same time.  A non-NULL
+ * `ws` must be 16-byte aligned (hipMalloc's are), else RMM_ERR_WORKSPACE.
+ * ws_bytes below rmm_workspace_bytes*() returns RMM_ERR_WORKSPACE, except
+ * where AUTO picks the prefill split: it then takes the best count that fits
+ * (down to no split).
  *
  * Errors.  Validation happens on the host before any HIP call, in this order:
  *   RMM_ERR_NULL      a NULL data pointer (when M*N > 0)
@@ -64,7 +65,7 @@
  *   RMM_ERR_DTYPE     unknown dtype
  *   RMM_ERR_ALIAS     Y's byte range overlaps an input or the workspace
  *   RMM_ERR_VARIANT   a forced variant/split count cannot run this call
- *   RMM_ERR_WORKSPACE ws non-NULL and ws_bytes too small
+ *   RMM_ERR_WORKSPACE ws non-NULL and ws_bytes too small or ws not 16-byte aligned
  * M == 0 or N == 0 is a no-op returning RMM_OK.  A failed launch returns
  * RMM_ERR_HIP; rmm_last_hip_error() gives the hipError_t (thread local).
  * Input values are not checked: NaN/Inf propagate (with eps = 0 an all-zero

@@ -243,8 +243,8 @@ rmm_status plan_call(const void* X, const void* g, const void* W1, const void* W
       plan_shape(M, N, K, dtype, gated, variant, splits, aligned, ws != nullptr, out, rank,
                  ws ? ws_bytes : 0);
   if (st != RMM_OK) return st;
-  // 7. workspace
-  if (ws && ws_bytes < out->ws_bytes) return RMM_ERR_WORKSPACE;
+  // 7. workspace (its partial sums are read and written 16 bytes at a time)
+  if (ws && (ws_bytes < out->ws_bytes || !aligned16(ws))) return RMM_ERR_WORKSPACE;
   return RMM_OK;
 }
 
@@ -358,8 +358,8 @@ rmm_status attn_plan_call(const void* Q, const void* K, const void* V, const voi
     return RMM_ERR_VARIANT;
   // one arrival counter per batch-head, all in the workspace's counter region
   if (plan->chunks > 1 && BH > kWsMaxCounters) return RMM_ERR_VARIANT;
-  // 7. workspace
-  if (ws && ws_bytes < plan->ws_bytes) return RMM_ERR_WORKSPACE;
+  // 7. workspace (its partial sums are read and written 16 bytes at a time)
+  if (ws && (ws_bytes < plan->ws_bytes || !aligned16(ws))) return RMM_ERR_WORKSPACE;
   return RMM_OK;
 }
 
@@ -391,7 +391,7 @@ rmm_status chain_plan_call(const void* X0, const void* G, const void* W, const v
       !(aligned16(X0) && aligned16(G) && aligned16(W) && aligned16(Xs)))
     return RMM_ERR_VARIANT;
   if (rmm_chain_plan(M, K, L, plan) != 0) return RMM_ERR_VARIANT;  // not one workgroup per CU
-  if (!ws || ws_bytes < plan->ws_bytes) return RMM_ERR_WORKSPACE;
+  if (!ws || ws_bytes < plan->ws_bytes || !aligned16(ws)) return RMM_ERR_WORKSPACE;
   return RMM_OK;
 }
 
@@ -707,7 +707,7 @@ const char* rmm_status_string(rmm_status s) {
     case RMM_ERR_EPS: return "RMM_ERR_EPS: eps must be finite and >= 0";
     case RMM_ERR_DTYPE: return "RMM_ERR_DTYPE: unknown dtype";
     case RMM_ERR_ALIAS: return "RMM_ERR_ALIAS: Y overlaps an input or the workspace";
-    case RMM_ERR_WORKSPACE: return "RMM_ERR_WORKSPACE: workspace too small";
+    case RMM_ERR_WORKSPACE: return "RMM_ERR_WORKSPACE: workspace too small or not 16-byte aligned";
     case RMM_ERR_HIP: return "RMM_ERR_HIP: kernel launch failed";
     case RMM_ERR_VARIANT: return "RMM_ERR_VARIANT: variant/splits cannot run this call";
     case RMM_ERR_SCRATCH:

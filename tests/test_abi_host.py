@@ -93,6 +93,8 @@ def test_validation_order(lib):
     need = lib.rmm_workspace_bytes_ex(BF16, 16, 6144, 4096, 0, 2, 8)
     assert need > 0
     assert call(lib, variant=2, K=4096, N=6144, splits=8, ws=A[6], ws_bytes=need - 1) == WORKSPACE
+    # a workspace must be 16-byte aligned (its partial sums move 16 bytes at a time)
+    assert call(lib, variant=2, K=4096, N=6144, splits=8, ws=A[6] + 8, ws_bytes=need) == WORKSPACE
 
 
 def test_unfused_entry_points_validate(lib):
@@ -244,6 +246,7 @@ def test_attention_entry_points_validate(lib):
     assert at(splits=513) == VARIANT                     # more chunks than keys
     assert at(splits=2) == WORKSPACE                     # forced chunks without a workspace
     assert at(splits=2, ws=A[6], ws_bytes=16) == WORKSPACE
+    assert at(splits=2, ws=A[6] + 4, ws_bytes=1 << 24) == WORKSPACE   # not 16-byte aligned
     assert at(Q=None, K=None, V=None, gq=None, gk=None, O=None, BH=0) == OK
 
 
@@ -391,6 +394,7 @@ def test_chain_validation_and_workspace(lib):
     assert chain(ws=None) == WORKSPACE
     need = lib.rmm_chain_workspace_bytes(16, 1024, 4)
     assert need > 0 and chain(ws_bytes=need - 1) == WORKSPACE
+    assert chain(ws=A[6] + 4) == WORKSPACE        # not 16-byte aligned
     assert chain(M=0, ws=None) == OK              # nothing to do, nothing launched
     # 8 tiles x 8 chunks of 128: the counter region (tile counters first, the
     # done + flag words in its last 256 bytes), 16-row sums, 8 x 64 floatx4 partials

@@ -87,7 +87,7 @@ def test_matmul_exact(case, require_gpu):
     assert mism.size == 0, f"{len(mism)} mismatches, first at {tuple(mism[0])}"
 
 
-@pytest.mark.parametrize("shape", [(13, 520, 392), (64, 1024, 14336)])
+@pytest.mark.parametrize("shape", [(13, 520, 392), (64, 1024, 14336), (200, 1032, 1032)])
 def test_gated_matmul(shape, require_gpu):
     M, K, N = shape
     wl = synth.Workload("gated_plain", "bf16", M, K, N, 1e-6, True, None)

@@ -25,8 +25,10 @@
 //     and written to LDS with 144-byte rows (128 + 16 padding), which makes
 //     both the staging writes and the fragment reads bank-conflict-free.
 // W tile layout: [64 k][256 n] bf16, 512-byte rows; 16-byte chunk c of row k
-// sits at chunk c ^ 2(k & 3), so the 4 rows x 32 bytes that one 16-lane group
-// reads land on 8 different bank groups.
+// sits at chunk c ^ 4(k & 3), so the 4 rows x 64 bytes that the two 16-lane
+// groups of a half-wave read (columns 32 j .. +31 of rows k .. k+3) land on
+// 16 different bank groups (with c ^ 2(k & 3) the two groups' reads fell on
+// the same 8: two cycles of bank conflict per transposing read).
 #include "rmm_device.h"
 
 namespace rmm {
@@ -46,7 +48,7 @@ __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t v) { return __builtin_bit_c
 
 // Byte offset of element n (a multiple of 4) of row k in a W stage.
 __device__ __forceinline__ int pf_b_off(int k, int n) {
-  return k * 512 + (((n >> 3) ^ (2 * (k & 3))) << 4) + ((n & 7) << 1);
+  return k * 512 + (((n >> 3) ^ (4 * (k & 3))) << 4) + ((n & 7) << 1);
 }
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -138,7 +140,7 @@ __device__ __forceinline__ void pf_dma_setup(PfDma& d, int64_t n0, int64_t N, in
   for (int q = 0; q < 4; ++q) {
     const int blk = 4 * w + q;
     const int kl = 2 * blk + (l >> 5);
-    const int c = (l & 31) ^ (2 * (kl & 3));
+    const int c = (l & 31) ^ (4 * (kl & 3));
     const int64_t nn = n0 + 8 * c;
     d.off[q] = nn < N ? (uint32_t)((kl * N + nn) * 2) : kPfOutOfRange;
   }
@@ -524,7 +526,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_kernel(
 // same accumulator.  Tile 128 rows x 128 columns of each weight x 64 k:
 //   * A: two stages (hi, lo), double-buffered, 144-byte rows as above;
 //   * W: one stage holds the 64 x 128 blocks of W1 and W3 ([weight][k][n],
-//     256-byte rows, chunk c of row k at c ^ 2(k & 3)); each 1 KB
+//     256-byte rows, chunk c of row k at c ^ 4(k & 3)); each 1 KB
 //     LDS-direct transfer reads 4 rows of one weight;
 //   * wave w: rows 64 (w >> 2) .. +63, weight (w >> 1) & 1, columns
 //     64 (w & 1) .. +63 of that weight: 2 x 2 v_mfma_f32_32x32x16_bf16
@@ -539,7 +541,7 @@ constexpr int PG_W_BYTES = PF_BK * PG_BNW * 2;        // one weight's block, 16 
 
 // Byte offset of element n (a multiple of 4) of row k in one weight's block.
 __device__ __forceinline__ int pg_b_off(int k, int n) {
-  return k * 256 + (((n >> 3) ^ (2 * (k & 3))) << 4) + ((n & 7) << 1);
+  return k * 256 + (((n >> 3) ^ (4 * (k & 3))) << 4) + ((n & 7) << 1);
 }
 
 // X of one k-step for this thread: rows (t>>3) and (t>>3) + 64, chunk t&7.
@@ -582,7 +584,7 @@ __device__ __forceinline__ void pg_dma_setup(PgDma& d, int64_t n0, int64_t N, in
   for (int q = 0; q < 4; ++q) {
     const int blk = (4 * w + q) & 15;
     const int kl = 4 * blk + (l >> 4);
-    const int c = (l & 15) ^ (2 * (kl & 3));
+    const int c = (l & 15) ^ (4 * (kl & 3));
     const int64_t nn = n0 + 8 * c;
     d.off[q] = nn < N ? (uint32_t)((kl * N + nn) * 2) : kPfOutOfRange;
   }

@@ -384,9 +384,12 @@ typedef __attribute__((address_space(3))) char at_lds_char;
 
 template <int D>
 __device__ __forceinline__ int aq_v_off(int key, int n) {
-  // V tile row `key` (2 D bytes), 16-byte chunk c stored at c ^ 2 (key & 3):
-  // the 4 rows x 32 bytes of one transposing read hit 8 different chunks.
-  return key * (2 * D) + (((n >> 3) ^ (2 * (key & 3))) << 4) + ((n & 7) << 1);
+  // V tile row `key` (2 D bytes), 16-byte chunk c stored at c ^ f(key): a
+  // half-wave's transposing reads (rows 8 i .. 8 i + 7, 32 bytes of each)
+  // then cover all 16 bank groups.  D = 128 (256-byte rows): f = 2 (key & 7);
+  // D = 64 (128-byte rows, odd rows on the other 8 groups): f = 2 ((key >> 1) & 3).
+  const int f = D == 128 ? 2 * (key & 7) : 2 * ((key >> 1) & 3);
+  return key * (2 * D) + (((n >> 3) ^ f) << 4) + ((n & 7) << 1);
 }
 
 template <int D, bool NORM>

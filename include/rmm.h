@@ -329,11 +329,31 @@ rmm_status rmm_plan_attention_gqa(const void* Q, const void* K, const void* V, c
  * Sq or Skv < 1, D not 64 or 128, causal with Skv < Sq, element counts
  * overflowing), RMM_ERR_EPS, RMM_ERR_DTYPE (bf16 only), RMM_ERR_ALIAS (O
  * against any input), RMM_ERR_VARIANT (a pointer not 16-byte aligned, Skv D 2
- * >= 2^31).  BH == 0 is a no-op. */
+ * >= 2^31).  BH == 0 is a no-op.  No split of the keys (see _ex). */
 rmm_status qknorm_attention_prefill(const void* Q, const void* K, const void* V, const void* gq,
                                     const void* gk, void* O, float eps, int64_t BH, int64_t G,
                                     int64_t Sq, int64_t Skv, int64_t D, int causal,
                                     rmm_dtype dtype, hipStream_t stream);
+
+/* As qknorm_attention_prefill with a split of the keys: splits spans of whole
+ * 64-key tiles, each workgroup taking one span of one block of queries and
+ * storing its raw (o, max, sum) in the workspace, a second kernel combining
+ * the spans in order per query row (the log-sum-exp merge of the decode
+ * form).  splits: 0 = chosen by the library (with a workspace: spans of at
+ * least 512 keys, up to three workgroups per CU, when the query blocks alone
+ * leave CUs idle; without one, no split), 1 = no split (no workspace), n > 1
+ * forced (rounded to whole 64-key tiles, so the count that runs may be lower;
+ * above ceil(Skv / 64): RMM_ERR_VARIANT; without a workspace:
+ * RMM_ERR_WORKSPACE).  Workspace rules are those of rmsnorm_matmul, sized by
+ * rmm_attention_prefill_workspace_bytes (same splits; 0 when no split runs);
+ * O must not overlap it (RMM_ERR_ALIAS). */
+rmm_status qknorm_attention_prefill_ex(const void* Q, const void* K, const void* V,
+                                       const void* gq, const void* gk, void* O, float eps,
+                                       int64_t BH, int64_t G, int64_t Sq, int64_t Skv, int64_t D,
+                                       int causal, rmm_dtype dtype, int splits, void* ws,
+                                       size_t ws_bytes, hipStream_t stream);
+size_t rmm_attention_prefill_workspace_bytes(int64_t BH, int64_t G, int64_t Sq, int64_t Skv,
+                                             int64_t D, int causal, int splits);
 
 /* The attention step alone (the second kernel of the unfused QKNorm +
  * Attention program the same page's benchmark table compares against,

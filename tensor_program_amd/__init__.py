@@ -324,10 +324,12 @@ def qknorm_attention_gqa(q, k, v, gq, gk, eps: float, out=None, splits: int = 0,
     return out
 
 
-def qknorm_attention_prefill(q, k, v, gq, gk, eps: float, causal: bool = True, out=None):
+def qknorm_attention_prefill(q, k, v, gq, gk, eps: float, causal: bool = True, out=None,
+                             splits: int = 0, workspace: Workspace | None = None):
     """QKNorm + attention for many queries per head (bf16): q: [BH * G, Sq, D]
     (query head h * G + g reads key/value head h), k, v: [BH, Skv, D]; causal:
-    query position i sees keys 0 .. i + Skv - Sq."""
+    query position i sees keys 0 .. i + Skv - Sq.  splits: spans of the keys
+    combined by a second kernel (0: the library's choice, 1: none)."""
     _check_operands([q, k, v, gq, gk], ["q", "k", "v", "gq", "gk"])
     if q.dim() != 3 or k.dim() != 3 or gq.dim() != 1 or gk.dim() != 1:
         raise ValueError("expected q: [BH * G, Sq, D], k, v: [BH, Skv, D], gq, gk: [D]")
@@ -346,9 +348,17 @@ def qknorm_attention_prefill(q, k, v, gq, gk, eps: float, causal: bool = True, o
         if tuple(out.shape) != tuple(q.shape):
             raise ValueError(f"out has shape {tuple(out.shape)}, expected {tuple(q.shape)}")
     stream = torch.cuda.current_stream(q.device).cuda_stream
-    _binding.check(load_library().qknorm_attention_prefill(
+    lib = load_library()
+    G = BHq // BH
+    need = lib.rmm_attention_prefill_workspace_bytes(BH, G, Sq, Skv, D, int(bool(causal)), splits)
+    if workspace is None and (need > 0 or splits > 1):  # a forced count needs one
+        workspace = _workspace_for(q.device, stream, max(need, 256))
+    ws_ptr = workspace.ptr if workspace is not None else None
+    ws_bytes = workspace.nbytes if workspace is not None else 0
+    _binding.check(lib.qknorm_attention_prefill_ex(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), gq.data_ptr(), gk.data_ptr(), out.data_ptr(),
-        float(eps), BH, BHq // BH, Sq, Skv, D, int(bool(causal)), _DTYPES[q.dtype], stream))
+        float(eps), BH, G, Sq, Skv, D, int(bool(causal)), _DTYPES[q.dtype], splits, ws_ptr,
+        ws_bytes, stream))
     return out
 
 

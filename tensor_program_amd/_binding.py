@@ -28,7 +28,8 @@ SYMBOLS = ("rmsnorm_matmul", "rmsnorm_gated_mlp", "rmsnorm_matmul_ex", "rmsnorm_
            "rmm_lora_workspace_bytes", "rmm_plan_lora", "qknorm_attention",
            "qknorm_attention_ex", "rmm_attention_workspace_bytes", "rmm_plan_attention",
            "rmm_attention", "qknorm_attention_gqa", "rmm_attention_gqa_workspace_bytes",
-           "rmm_plan_attention_gqa", "qknorm_attention_prefill",
+           "rmm_plan_attention_gqa", "qknorm_attention_prefill", "qknorm_attention_prefill_ex",
+           "rmm_attention_prefill_workspace_bytes",
            "rmsnorm_matmul_chain", "rmm_chain_workspace_bytes", "rmm_chain_flag_offset",
            "rmm_probe_hbm_read", "rmm_probe_mfma_bf16", "rmm_probe_mfma_flops",
            "rmsnorm_matmul_noalloc")
@@ -96,6 +97,11 @@ def load_library(path: str = LIB_PATH):
     lib.qknorm_attention_prefill.argtypes = [vp, vp, vp, vp, vp, vp, f32, i64, i64, i64, i64, i64,
                                              i32, i32, vp]
     lib.qknorm_attention_prefill.restype = i32
+    lib.qknorm_attention_prefill_ex.argtypes = [vp, vp, vp, vp, vp, vp, f32, i64, i64, i64, i64,
+                                                i64, i32, i32, i32, vp, sz, vp]
+    lib.qknorm_attention_prefill_ex.restype = i32
+    lib.rmm_attention_prefill_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32, i32]
+    lib.rmm_attention_prefill_workspace_bytes.restype = sz
     lib.rmm_attention_workspace_bytes.argtypes = [i32, i64, i64, i64, i32]
     lib.rmm_attention_workspace_bytes.restype = sz
     lib.rmm_plan_attention.argtypes = [vp, vp, vp, vp, vp, vp, f32, i64, i64, i64, i32, i32, vp, sz,

@@ -395,6 +395,52 @@ rmm_status chain_plan_call(const void* X0, const void* G, const void* W, const v
   return RMM_OK;
 }
 
+// qknorm_attention_prefill(_ex): validation in the documented order, then
+// the plan (query blocks per wave, key tiles, the split of the keys).
+rmm_status prefill_attn_plan_call(const void* Q, const void* K, const void* V, const void* gq,
+                                  const void* gk, const void* O, float eps, int64_t BH,
+                                  int64_t G, int64_t Sq, int64_t Skv, int64_t D, int causal,
+                                  rmm_dtype dtype, int splits, const void* ws, size_t ws_bytes,
+                                  AttnPrefillPlan* plan) {
+  // 1. pointers
+  if (BH > 0 && (!Q || !K || !V || !gq || !gk || !O)) return RMM_ERR_NULL;
+  // 2. shape
+  if (BH < 0 || G < 1 || Sq < 1 || Skv < 1 || (D != 64 && D != 128) || (causal && Skv < Sq))
+    return RMM_ERR_SHAPE;
+  int64_t bhg, qn, kn, tmp;
+  if (__builtin_mul_overflow(BH, G, &bhg) || __builtin_mul_overflow(bhg, Sq * D, &qn) ||
+      __builtin_mul_overflow(Sq, D, &tmp) || __builtin_mul_overflow(BH, Skv * D, &kn) ||
+      __builtin_mul_overflow(Skv, D, &tmp) || __builtin_mul_overflow(qn, (int64_t)2, &tmp) ||
+      __builtin_mul_overflow(kn, (int64_t)2, &tmp))
+    return RMM_ERR_SHAPE;
+  // 3. eps
+  if (!isfinite(eps) || eps < 0.0f) return RMM_ERR_EPS;
+  // 4. dtype
+  if (dtype != RMM_DTYPE_BF16) return RMM_ERR_DTYPE;
+  if (BH == 0) return RMM_OK;
+  // 5. aliasing of the output
+  const size_t ob = (size_t)qn * 2;
+  if (overlaps(O, ob, Q, ob) || overlaps(O, ob, K, (size_t)kn * 2) ||
+      overlaps(O, ob, V, (size_t)kn * 2) || overlaps(O, ob, gq, (size_t)D * 2) ||
+      overlaps(O, ob, gk, (size_t)D * 2) || overlaps(O, ob, ws, ws ? ws_bytes : 0))
+    return RMM_ERR_ALIAS;
+  // 6. what the kernel can run: 16-byte aligned operands, 32-bit offsets
+  // within one head's keys, one workgroup per 64 positions of a query head
+  // and key span, spans of whole 64-key tiles
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(gq) || !aligned16(gk) ||
+      !aligned16(O))
+    return RMM_ERR_VARIANT;
+  if (Skv * D * 2 > (int64_t)INT32_MAX || G > (int64_t)INT32_MAX || splits < 0 ||
+      splits > (Skv + 63) / 64)
+    return RMM_ERR_VARIANT;
+  rmm_attention_prefill_plan(bhg, Sq, Skv, D, causal ? 1 : 0, splits, ws != nullptr, plan);
+  if (bhg * plan->nblk * plan->splits > (int64_t)INT32_MAX) return RMM_ERR_VARIANT;
+  // 7. workspace
+  if (plan->splits > 1 && !ws) return RMM_ERR_WORKSPACE;  // a forced split count needs one
+  if (ws && (ws_bytes < plan->ws_bytes || !aligned16(ws))) return RMM_ERR_WORKSPACE;
+  return RMM_OK;
+}
+
 }  // namespace
 
 size_t rmm_workspace_bytes_within(int dtype, int64_t M, int64_t N, int64_t K, int gated,
@@ -532,47 +578,42 @@ rmm_status qknorm_attention_gqa(const void* Q, const void* K, const void* V, con
   return RMM_OK;
 }
 
-rmm_status qknorm_attention_prefill(const void* Q, const void* K, const void* V, const void* gq,
-                                    const void* gk, void* O, float eps, int64_t BH, int64_t G,
-                                    int64_t Sq, int64_t Skv, int64_t D, int causal,
-                                    rmm_dtype dtype, hipStream_t stream) {
-  // 1. pointers
-  if (BH > 0 && (!Q || !K || !V || !gq || !gk || !O)) return RMM_ERR_NULL;
-  // 2. shape
-  if (BH < 0 || G < 1 || Sq < 1 || Skv < 1 || (D != 64 && D != 128) || (causal && Skv < Sq))
-    return RMM_ERR_SHAPE;
-  int64_t bhg, qn, kn, tmp;
-  if (__builtin_mul_overflow(BH, G, &bhg) || __builtin_mul_overflow(bhg, Sq * D, &qn) ||
-      __builtin_mul_overflow(Sq, D, &tmp) || __builtin_mul_overflow(BH, Skv * D, &kn) ||
-      __builtin_mul_overflow(Skv, D, &tmp) || __builtin_mul_overflow(qn, (int64_t)2, &tmp) ||
-      __builtin_mul_overflow(kn, (int64_t)2, &tmp))
-    return RMM_ERR_SHAPE;
-  // 3. eps
-  if (!isfinite(eps) || eps < 0.0f) return RMM_ERR_EPS;
-  // 4. dtype
-  if (dtype != RMM_DTYPE_BF16) return RMM_ERR_DTYPE;
-  if (BH == 0) return RMM_OK;
-  // 5. aliasing of the output
-  const size_t ob = (size_t)qn * 2;
-  if (overlaps(O, ob, Q, ob) || overlaps(O, ob, K, (size_t)kn * 2) ||
-      overlaps(O, ob, V, (size_t)kn * 2) || overlaps(O, ob, gq, (size_t)D * 2) ||
-      overlaps(O, ob, gk, (size_t)D * 2))
-    return RMM_ERR_ALIAS;
-  // 6. what the kernel can run: 16-byte aligned operands, 32-bit offsets
-  // within one head's keys, one workgroup per 64 positions of a query head
-  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(gq) || !aligned16(gk) ||
-      !aligned16(O))
-    return RMM_ERR_VARIANT;
-  if (Skv * D * 2 > (int64_t)INT32_MAX || bhg * ((Sq + 63) / 64) > (int64_t)INT32_MAX ||
-      G > (int64_t)INT32_MAX)
-    return RMM_ERR_VARIANT;
+rmm_status qknorm_attention_prefill_ex(const void* Q, const void* K, const void* V,
+                                       const void* gq, const void* gk, void* O, float eps,
+                                       int64_t BH, int64_t G, int64_t Sq, int64_t Skv, int64_t D,
+                                       int causal, rmm_dtype dtype, int splits, void* ws,
+                                       size_t ws_bytes, hipStream_t stream) {
+  AttnPrefillPlan plan;
+  const rmm_status st = prefill_attn_plan_call(Q, K, V, gq, gk, O, eps, BH, G, Sq, Skv, D, causal,
+                                               dtype, splits, ws, ws_bytes, &plan);
+  if (st != RMM_OK || BH == 0) return st;
   AttnArgs a{Q, K, V, gq, gk, O, eps, BH, Skv, D, stream, 1, G};
-  const hipError_t err = rmm_launch_attention_prefill(a, Sq, Skv, causal ? 1 : 0);
+  const hipError_t err = rmm_launch_attention_prefill(a, Sq, Skv, causal ? 1 : 0, plan, ws);
   if (err != hipSuccess) {
     g_last_hip_error = (int)err;
     return RMM_ERR_HIP;
   }
   return RMM_OK;
+}
+
+rmm_status qknorm_attention_prefill(const void* Q, const void* K, const void* V, const void* gq,
+                                    const void* gk, void* O, float eps, int64_t BH, int64_t G,
+                                    int64_t Sq, int64_t Skv, int64_t D, int causal,
+                                    rmm_dtype dtype, hipStream_t stream) {
+  return qknorm_attention_prefill_ex(Q, K, V, gq, gk, O, eps, BH, G, Sq, Skv, D, causal, dtype, 1,
+                                     nullptr, 0, stream);
+}
+
+size_t rmm_attention_prefill_workspace_bytes(int64_t BH, int64_t G, int64_t Sq, int64_t Skv,
+                                             int64_t D, int causal, int splits) {
+  if (BH < 1 || G < 1 || Sq < 1 || Skv < 1 || (D != 64 && D != 128) || (causal && Skv < Sq) ||
+      splits < 0 || splits > (Skv + 63) / 64)
+    return 0;
+  int64_t bhg;
+  if (__builtin_mul_overflow(BH, G, &bhg)) return 0;
+  AttnPrefillPlan plan;
+  rmm_attention_prefill_plan(bhg, Sq, Skv, D, causal ? 1 : 0, splits, true, &plan);
+  return plan.ws_bytes;
 }
 
 size_t rmm_attention_gqa_workspace_bytes(rmm_dtype dtype, int64_t BH, int64_t G, int64_t S,

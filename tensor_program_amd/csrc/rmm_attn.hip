@@ -775,7 +775,8 @@ template <int D, bool NORM, bool CAUSAL, int QW, int KT>
 __global__ __launch_bounds__(AP_THREADS, 2) void attn_prefill_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc,
     const bf16_t* __restrict__ gq, const bf16_t* __restrict__ gk, bf16_t* __restrict__ O,
-    float eps, int64_t Sq, int64_t Skv, int G, int nblk, int order) {
+    float eps, int64_t Sq, int64_t Skv, int G, int nblk, int order, int splits, int kspan,
+    float* __restrict__ part) {
   constexpr int NDB = D / 32;
   constexpr int NOB = D / 16;
   constexpr int CPR = D / 8;
@@ -793,16 +794,20 @@ __global__ __launch_bounds__(AP_THREADS, 2) void attn_prefill_kernel(
   // gets about the same number of key tiles as every other CU.  Order 0:
   // an XCD (workgroups b % 8) takes a contiguous range of pairs, latest
   // blocks of a head first; 2: as 0 without the XCD remap.
-  const int64_t total = (int64_t)gridDim.x;
+  // With the keys split into `splits` spans of kspan keys, workgroup b takes
+  // span b / (grid / splits) of pair b % (grid / splits).
+  const int64_t total = (int64_t)gridDim.x / splits;
+  const int split = (int)(blockIdx.x / total);
+  const int64_t bidx = (int64_t)blockIdx.x - (int64_t)split * total;
   int64_t qh, blk;
   if (order == 1) {
-    const int64_t half = (total + 1) / 2, b = blockIdx.x;
+    const int64_t half = (total + 1) / 2, b = bidx;
     const int64_t r = b < half ? b : total - 1 - (b - half);
     const int64_t nh = total / nblk;
     blk = nblk - 1 - r / nh;
     qh = r % nh;
   } else {
-    int64_t t = blockIdx.x;
+    int64_t t = bidx;
     if (order == 0) t = (t & 7) * (total >> 3) + (t >> 3);
     qh = t / nblk;
     blk = nblk - 1 - t % nblk;
@@ -853,13 +858,16 @@ __global__ __launch_bounds__(AP_THREADS, 2) void attn_prefill_kernel(
     }
   }
 
-  // Keys the block needs: up to the horizon of its last position.
+  // Keys the block needs: up to the horizon of its last position, within
+  // this workgroup's span [kbeg, kbeg + kspan) (all of them without a split).
   int64_t kend = Skv;
   if (CAUSAL) {
     const int64_t last = (blk + 1) * QB - 1 < Sq - 1 ? (blk + 1) * QB - 1 : Sq - 1;
     kend = last + off + 1;
   }
-  const int64_t ntile = (kend + KT - 1) / KT;
+  const int64_t kbeg = (int64_t)split * kspan;
+  if (splits > 1 && kbeg + kspan < kend) kend = kbeg + kspan;
+  const int64_t ntile = kend > kbeg ? (kend - kbeg + KT - 1) / KT : 0;
   const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(Kc + h * Skv * D), 0, (int)(Skv * D * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
@@ -869,7 +877,7 @@ __global__ __launch_bounds__(AP_THREADS, 2) void attn_prefill_kernel(
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
       const int e = tid + AP_THREADS * j;
-      const int64_t key = KT * tt + e / CPR;
+      const int64_t key = kbeg + KT * tt + e / CPR;
       const uint32_t o = (tt < ntile && key < kend) ? (uint32_t)((key * D + 8 * (e % CPR)) * 2)
                                                     : kAtOutOfRange;
       kk[j] = __builtin_amdgcn_raw_buffer_load_b128(kr, o, 0, 0);
@@ -910,7 +918,7 @@ __global__ __launch_bounds__(AP_THREADS, 2) void attn_prefill_kernel(
 
   auto compute = [&](int64_t tt, int stage) {
     const char* ks = k_s[stage];
-    const int64_t k0 = KT * tt;
+    const int64_t k0 = kbeg + KT * tt;
     floatx4 sc[QW][NH];
     float rk[NH][4];
 #pragma unroll
@@ -1040,6 +1048,38 @@ __global__ __launch_bounds__(AP_THREADS, 2) void attn_prefill_kernel(
     compute(tt, (int)(tt & 1));
   }
 
+  // A span of a split call: the raw (o, max, sum) of its keys per query to
+  // the workspace -- o as [span][query head][position][D] fp32, then the
+  // maxima (base 2) and the sums as [span][query head][position] -- for
+  // the combine kernel.  A span past the block's keys stores (0, -1e30, 0).
+  if (splits > 1) {
+    const int64_t rows = (int64_t)splits * total / nblk * Sq;  // spans x query heads x Sq
+    float* po = part;
+    float* pm = part + rows * D;
+    float* pl = pm + rows;
+    const int64_t row0 = ((int64_t)split * (total / nblk) + qh) * Sq;
+#pragma unroll
+    for (int b = 0; b < QW; ++b) {
+      float ls = lpart[b];
+      ls += __shfl_xor(ls, 16);
+      ls += __shfl_xor(ls, 32);
+      const int64_t pc = p0 + 16 * b + lq;  // this lane's query column
+      if (lg == 0 && pc < Sq) {
+        pm[row0 + pc] = m[b];
+        pl[row0 + pc] = ls;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t p = p0 + 16 * b + 4 * lg + i;
+        if (p < Sq) {
+#pragma unroll
+          for (int ob = 0; ob < NOB; ++ob) po[(row0 + p) * D + 16 * ob + lq] = o[b][ob][i];
+        }
+      }
+    }
+    return;
+  }
+
   // o / sum for this wave's rows (block b: queries 4 lg + i of its 16).
 #pragma unroll
   for (int b = 0; b < QW; ++b) {
@@ -1059,6 +1099,36 @@ __global__ __launch_bounds__(AP_THREADS, 2) void attn_prefill_kernel(
       }
     }
   }
+}
+
+// Spans of a split prefill call: per query row, O = sum_s o_s 2^(m_s - M) /
+// sum_s l_s 2^(m_s - M), M = max_s m_s, the spans added in order; 4 dims per
+// thread.
+constexpr int AC_THREADS = 256;
+
+template <int D>
+__global__ __launch_bounds__(AC_THREADS) void attn_prefill_combine_kernel(
+    const float* __restrict__ part, bf16_t* __restrict__ O, int64_t rows, int splits) {
+  const int64_t idx = (int64_t)blockIdx.x * AC_THREADS + threadIdx.x;
+  if (idx >= rows * (D / 4)) return;
+  const int64_t r = idx / (D / 4);
+  const int d0 = 4 * (int)(idx % (D / 4));
+  const float* pm = part + (int64_t)splits * rows * D;
+  const float* pl = pm + (int64_t)splits * rows;
+  float mx = kAtNone;
+  for (int sp = 0; sp < splits; ++sp) mx = fmaxf(mx, pm[(int64_t)sp * rows + r]);
+  float l = 0.f, o[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int sp = 0; sp < splits; ++sp) {
+    const int64_t rr = (int64_t)sp * rows + r;
+    const float wgt = __builtin_amdgcn_exp2f(pm[rr] - mx);
+    const floatx4 v = *(const floatx4*)(part + rr * D + d0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] += v[i] * wgt;
+    l += pl[rr] * wgt;
+  }
+  const uint32_t lo = pack_bf16x2(__fdiv_rn(o[0], l), __fdiv_rn(o[1], l));
+  const uint32_t hi = pack_bf16x2(__fdiv_rn(o[2], l), __fdiv_rn(o[3], l));
+  *(u32x2*)(O + r * D + d0) = u32x2{lo, hi};
 }
 
 }  // namespace rmm
@@ -1136,7 +1206,8 @@ hipError_t rmm_launch_attention(const AttnArgs& a, const AttnPlan& p, void* ws) 
   return hipGetLastError();
 }
 
-hipError_t rmm_launch_attention_prefill(const AttnArgs& a, int64_t Sq, int64_t Skv, int causal) {
+void rmm_attention_prefill_plan(int64_t BHG, int64_t Sq, int64_t Skv, int64_t D, int causal,
+                                int splits, bool have_ws, AttnPrefillPlan* p) {
   using namespace rmm;
   // Two 16-row query blocks per wave when the 128-position workgroups
   // number at least one per CU (blocks of equal length) or, causal, two
@@ -1145,22 +1216,60 @@ hipError_t rmm_launch_attention_prefill(const AttnArgs& a, int64_t Sq, int64_t S
   // causal, D = 128: 32 heads x 2048 129.6 us (one block per wave) against
   // 149.0 (two); 32 x 4096 426.1 against 415.6; non-causal 32 x 2048 218.8
   // against 167.3.
-  const int64_t wg2 = a.BH * a.G * ((Sq + 2 * AP_QB - 1) / (2 * AP_QB));
-  const int qw = wg2 >= (causal ? 4 * 256 : 256) ? 2 : 1;
-  const int64_t nblk = (Sq + qw * AP_QB - 1) / (qw * AP_QB);
-  const int64_t grid = a.BH * a.G * nblk;
+  const int64_t wg2 = BHG * ((Sq + 2 * AP_QB - 1) / (2 * AP_QB));
+  p->qw = wg2 >= (causal ? 4 * 256 : 256) ? 2 : 1;
+  p->nblk = (Sq + p->qw * AP_QB - 1) / (p->qw * AP_QB);
+  const int64_t grid = BHG * p->nblk;
+  // Split of the keys into spans (a whole number of 64-key tiles each),
+  // combined by a second kernel: with a workspace and no forced count, when
+  // the query blocks alone make one workgroup per CU or fewer, up to three
+  // workgroups per CU with spans of at least 512 keys.  Measured (causal
+  // unless noted, D = 128): 8 x 4 heads, 512 queries over 8192 keys 261 ->
+  // 176 us (3 spans); 256 queries 231 -> 98 us (6); 128 over 16384 keys 450
+  // -> 103 us (8); 16 x 4 heads, 512 over 8192, D = 64, non-causal 272 ->
+  // 177 us (3).
+  int64_t s = splits;
+  if (s == 0) {
+    s = 1;
+    if (have_ws && grid <= 256) {
+      s = 768 / (grid > 0 ? grid : 1);
+      if (s > Skv / 512) s = Skv / 512;
+      if (s > 8) s = 8;
+      if (s < 1) s = 1;
+    }
+  }
+  int64_t span = (Skv + s - 1) / s;
+  span = (span + 63) / 64 * 64;
+  p->kspan = span;
+  p->splits = (int)((Skv + span - 1) / span);
   // 64-key tiles (half the barriers and softmax rounds per key; 221 VGPRs
   // and 64 KB of LDS: two workgroups per CU instead of three) when the grid
   // holds at most one workgroup per CU anyway.  Measured: 8 x 4 heads, 512
   // queries over 8192 keys 276.6 -> 237.5 us; 32 heads x 2048 causal
   // (1024 workgroups) 116.4 -> 120.6 us.
-  const int kt = qw == 1 && grid <= 256 ? 64 : 32;
-  const int order = causal ? 1 : (grid % 8 == 0 ? 0 : 2);
+  p->kt = p->qw == 1 && grid * p->splits <= 256 ? 64 : 32;
+  // Workspace (split calls): the counter region stays unused, then o
+  // ([span][row][D]) and the spans' maxima and sums ([span][row]), fp32.
+  p->ws_part_off = kWsCounterBytes;
+  p->ws_bytes = p->splits > 1
+                    ? kWsCounterBytes + (size_t)p->splits * (size_t)(BHG * Sq) * (size_t)(D + 2) * 4
+                    : 0;
+}
+
+hipError_t rmm_launch_attention_prefill(const AttnArgs& a, int64_t Sq, int64_t Skv, int causal,
+                                        const AttnPrefillPlan& p, void* ws) {
+  using namespace rmm;
+  const int qw = p.qw, kt = p.kt, splits = p.splits;
+  const int64_t nblk = p.nblk;
+  const int64_t grid = a.BH * a.G * nblk * splits;
+  if (splits > 1 && !ws) return hipErrorInvalidValue;
+  float* part = splits > 1 ? (float*)((char*)ws + p.ws_part_off) : nullptr;
+  const int order = causal ? 1 : ((grid / splits) % 8 == 0 ? 0 : 2);
   auto launch = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(AP_THREADS), 0, a.stream,
                        (const bf16_t*)a.Q, (const bf16_t*)a.K, (const bf16_t*)a.V,
                        (const bf16_t*)a.gq, (const bf16_t*)a.gk, (bf16_t*)a.O, a.eps, Sq, Skv,
-                       (int)a.G, (int)nblk, order);
+                       (int)a.G, (int)nblk, order, splits, (int)p.kspan, part);
   };
   auto by_qw = [&](auto d, auto norm, auto cz) {
     constexpr int D = decltype(d)::value;
@@ -1184,5 +1293,17 @@ hipError_t rmm_launch_attention_prefill(const AttnArgs& a, int64_t Sq, int64_t S
     by_norm(std::integral_constant<int, 64>{});
   else
     return hipErrorInvalidValue;
+  if (splits > 1) {
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int64_t rows = a.BH * a.G * Sq;
+    const dim3 cgrid((unsigned)((rows * (a.D / 4) + AC_THREADS - 1) / AC_THREADS));
+    if (a.D == 128)
+      hipLaunchKernelGGL(attn_prefill_combine_kernel<128>, cgrid, dim3(AC_THREADS), 0, a.stream,
+                         (const float*)part, (bf16_t*)a.O, rows, splits);
+    else
+      hipLaunchKernelGGL(attn_prefill_combine_kernel<64>, cgrid, dim3(AC_THREADS), 0, a.stream,
+                         (const float*)part, (bf16_t*)a.O, rows, splits);
+  }
   return hipGetLastError();
 }

@@ -210,7 +210,18 @@ void rmm_attention_plan(int64_t BH, int64_t S, int64_t D, int splits, AttnPlan* 
 hipError_t rmm_launch_attention(const AttnArgs& a, const AttnPlan& p, void* ws);
 // Many queries per head: Q and O (BH G) x Sq x D, K and V BH x Skv x D (a.S
 // unused); causal: query i sees keys 0 .. i + Skv - Sq.
-hipError_t rmm_launch_attention_prefill(const AttnArgs& a, int64_t Sq, int64_t Skv, int causal);
+// Many queries per head: query blocks per wave (qw), key-tile length (kt),
+// blocks per query head, and the split of the keys into spans of kspan
+// (splits > 1: partials in the workspace, a second kernel combines them).
+struct AttnPrefillPlan {
+  int qw, kt, splits;
+  int64_t nblk, kspan;
+  size_t ws_part_off, ws_bytes;
+};
+void rmm_attention_prefill_plan(int64_t BHG, int64_t Sq, int64_t Skv, int64_t D, int causal,
+                                int splits, bool have_ws, AttnPrefillPlan* p);
+hipError_t rmm_launch_attention_prefill(const AttnArgs& a, int64_t Sq, int64_t Skv, int causal,
+                                        const AttnPrefillPlan& p, void* ws);
 
 // Unfused baseline, first kernel: Xn = bf16/f32(X * g / RMS) written out.
 hipError_t rmm_launch_rmsnorm(const void* X, const void* g, void* Xn, float eps, int64_t M,

@@ -517,3 +517,51 @@ def test_noalloc_validates_and_fits_its_scratch(lib):
                     split += v == "prefill" and sp > 1
     assert 0 < worst <= 16 << 20, worst
     assert split > 0
+
+
+def test_attention_prefill_validation(lib):
+    # qknorm_attention_prefill(_ex): NULL, SHAPE, EPS, DTYPE, ALIAS, VARIANT,
+    # WORKSPACE, in that order; every call here fails before any launch.
+    def at(Q=A[0], K=A[1], V=A[2], gq=A[3], gk=A[4], O=A[5], eps=1e-6, BH=2, G=2, Sq=100,
+           Skv=1000, D=128, causal=1, dtype=BF16, splits=2, ws=None, ws_bytes=0):
+        return lib.qknorm_attention_prefill_ex(Q, K, V, gq, gk, O, eps, BH, G, Sq, Skv, D, causal,
+                                               dtype, splits, ws, ws_bytes, None)
+    assert at(Q=None) == NULL
+    assert at(G=0) == SHAPE
+    assert at(D=96) == SHAPE
+    assert at(Sq=1001) == SHAPE                           # causal needs Skv >= Sq
+    assert at(eps=-1.0) == EPS
+    assert at(dtype=F32) == DTYPE
+    assert at(O=A[0]) == ALIAS                            # O on Q
+    assert at(O=A[6] + 64, ws=A[6], ws_bytes=1 << 30) == ALIAS   # O inside the workspace
+    assert at(Q=A[0] + 8) == VARIANT                      # not 16-byte aligned
+    assert at(splits=17) == VARIANT                       # more spans than 64-key tiles
+    assert at(splits=-1) == VARIANT
+    assert at() == WORKSPACE                              # a forced split needs a workspace
+    assert at(ws=A[6], ws_bytes=16) == WORKSPACE
+    assert at(ws=A[6] + 4, ws_bytes=1 << 30) == WORKSPACE  # not 16-byte aligned
+    assert at(Q=None, K=None, V=None, gq=None, gk=None, O=None, BH=0) == OK
+    # the plain entry point: the same rules, no split
+    assert lib.qknorm_attention_prefill(A[0], A[1], A[2], A[3], A[4], A[0], 1e-6, 2, 2, 100, 1000,
+                                        128, 1, BF16, None) == ALIAS
+
+
+def test_attention_prefill_workspace_sizes(lib):
+    # 8 key/value heads x 4 queries, 512 positions over 8192 keys: 256
+    # workgroups of 64 positions, so the library splits the keys in three
+    # (spans of 2752 keys); the counter region, then 3 spans x 32 heads x 512
+    # rows x (128 + 2) fp32
+    assert lib.rmm_attention_prefill_workspace_bytes(8, 4, 512, 8192, 128, 1, 0) == \
+        CNT + 3 * 32 * 512 * 130 * 4
+    assert lib.rmm_attention_prefill_workspace_bytes(8, 4, 512, 8192, 128, 1, 3) == \
+        CNT + 3 * 32 * 512 * 130 * 4
+    assert lib.rmm_attention_prefill_workspace_bytes(8, 4, 512, 8192, 128, 1, 1) == 0
+    # 2048 positions: 1024 workgroups already, no split
+    assert lib.rmm_attention_prefill_workspace_bytes(8, 4, 2048, 2048, 128, 1, 0) == 0
+    # 5 spans of 1000 keys round to 4 of 256 (whole 64-key tiles)
+    assert lib.rmm_attention_prefill_workspace_bytes(1, 1, 64, 1000, 64, 0, 5) == \
+        CNT + 4 * 64 * 66 * 4
+    assert lib.rmm_attention_prefill_workspace_bytes(8, 4, 512, 8192, 128, 1, 200) == 0  # invalid
+    # two query blocks per wave (256 workgroups of 128 positions), not causal: 3 spans
+    assert lib.rmm_attention_prefill_workspace_bytes(16, 4, 512, 8192, 64, 0, 0) == \
+        CNT + 3 * 64 * 512 * 66 * 4

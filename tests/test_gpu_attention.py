@@ -318,3 +318,74 @@ def test_attention_prefill_long_sampled(require_gpu):
                                               inp.V[qh // G:qh // G + 1], inp.gq, inp.gk,
                                               oracle.eps_as_passed(1e-6), causal=True)
         _check(o[qh], ref[0], f"prefill head {qh}")
+
+
+# The keys split into spans (whole 64-key tiles), combined per query row by a
+# second kernel: forced counts, spans past a causal block's keys (stored
+# empty), the library's own choice for few query blocks over many keys.
+def _run_prefill_split(inp, eps, causal, splits):
+    o = tpa.qknorm_attention_prefill(_dev(inp, "Q"), _dev(inp, "K"), _dev(inp, "V"),
+                                     _dev(inp, "gq"), _dev(inp, "gk"), eps, causal=causal,
+                                     splits=splits)
+    torch.cuda.synchronize()
+    return o
+
+
+@pytest.mark.parametrize("case", [(2, 4, 130, 1000, 128, True, 3), (1, 2, 64, 1000, 64, False, 5),
+                                  (2, 1, 200, 200, 128, True, 2), (1, 8, 70, 3000, 128, True, 0),
+                                  (2, 2, 33, 700, 64, True, 11),
+                                  # two query blocks per wave, the library's split
+                                  (64, 4, 100, 2000, 64, False, 0)],
+                         ids=lambda c: "x".join(map(str, c)))
+@pytest.mark.parametrize("eps", [1e-6, 0.5])
+def test_attention_prefill_split_random(case, eps, require_gpu):
+    BH, G, Sq, Skv, D, causal, splits = case
+    lib = tpa.load_library()
+    need = lib.rmm_attention_prefill_workspace_bytes(BH, G, Sq, Skv, D, int(causal), splits)
+    assert need > 0, "the case must run split"
+    _log(f"prefill split {case} eps {eps}")
+    inp = synth.make_attention_prefill_inputs(BH, G, Sq, Skv, D, seed=Sq + Skv + splits)
+    o = _run_prefill_split(inp, eps, causal, splits)
+    ref = oracle.qknorm_attention_prefill(inp.Q, inp.K, inp.V, inp.gq, inp.gk,
+                                          oracle.eps_as_passed(eps), causal=causal)
+    _check(o.reshape(-1, D), ref.reshape(-1, D), f"prefill split {case}")
+
+
+@pytest.mark.parametrize("case", [(2, 2, 100, 128, True, 2), (1, 3, 70, 64, False, 3)],
+                         ids=lambda c: "x".join(map(str, c)))
+def test_attention_prefill_split_onehot_bitwise(case, require_gpu):
+    # as test_attention_prefill_onehot_bitwise, with the keys in spans: the
+    # span holding a query's own key gives o = v, every other span's weight
+    # underflows to zero in the combine
+    BH, G, Sq, D, causal, splits = case
+    Skv = G * Sq
+    _log(f"prefill split one-hot {case}")
+    inp = synth.make_attention_prefill_inputs(BH, G, Sq, Skv, D, seed=Sq + G + 7)
+    Q, K = inp.Q.copy(), inp.K.copy()
+    for qh in range(BH * G):
+        K[qh // G, (qh % G) * Sq + np.arange(Sq)] = 0.5 * Q[qh]
+    g40 = np.full(D, 40.0, np.float32)
+    inp = synth.AttnInputs(Q, K, inp.V, g40, g40)
+    o = _run_prefill_split(inp, 0.0, causal, splits)
+    want = np.stack([inp.V[qh // G, (qh % G) * Sq + np.arange(Sq)] for qh in range(BH * G)])
+    got = _bits(o)
+    mism = np.argwhere(got != synth.to_bf16_bits(want))
+    assert mism.size == 0, f"{len(mism)} mismatches, first at {tuple(mism[0])}"
+
+
+def test_attention_prefill_split_matches_unsplit_workload(require_gpu):
+    # 8 key/value heads x 4 queries, 512 positions over 8192 keys (the library
+    # splits the keys in three): two query heads against the oracle, every
+    # head against the unsplit call at the elementwise bound
+    BH, G, Sq, Skv, D = 8, 4, 512, 8192, 128
+    assert tpa.load_library().rmm_attention_prefill_workspace_bytes(BH, G, Sq, Skv, D, 1, 0) > 0
+    _log("prefill split 8 x 4 heads, 512 over 8192 keys")
+    inp = synth.make_attention_prefill_inputs(BH, G, Sq, Skv, D, seed=3)
+    o = _run_prefill_split(inp, 1e-6, True, 0)
+    o1 = _run_prefill_split(inp, 1e-6, True, 1)
+    _check(o.reshape(-1, D), o1.float().cpu().numpy().reshape(-1, D), "split against unsplit")
+    for qh in (0, BH * G - 1):
+        ref = oracle.qknorm_attention_prefill(inp.Q[qh:qh + 1], inp.K[qh // G:qh // G + 1],
+                                              inp.V[qh // G:qh // G + 1], inp.gq, inp.gk,
+                                              oracle.eps_as_passed(1e-6), causal=True)
+        _check(o[qh], ref[0], f"prefill split head {qh}")
